@@ -1,0 +1,629 @@
+"""Plain, slow fp64 CPU oracle of one DeepSeek-V4-style compressed-KV attention layer.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, the smoke check and the
+benchmark's CPU-baseline leg; never by the product path.  It shares no code
+with the HIP library: its number codecs, rotation, pooling, normalisation,
+scoring, selection and attention are written here from the pages alone.
+
+Sources (cited by page title and section):
+
+* P1 = "【#3】ds4.c を読み解く" (Metal graph + compressed KV, DwarfStar ds4)
+* P4 = "vLLM DeepSeek V4 サポート: 効率的な長文コンテキスト注意機構"
+
+What it computes, per layer of compression ratio r (0, 4 or 128):
+
+1. compressor (P1 s4, s5; P4 "KV Cache Compression"): for every token t,
+   kappa_t = W_kv x_t and sigma_t = W_gate x_t.  Compressed row i pools the
+   window of W tokens (W = 8 at stride 4 for c4a, 128 at stride 128 for
+   c128a) channel by channel with a softmax over the window of
+   sigma + APE[slot]; then RMS normalisation, RoPE on the last n_rot
+   channels at position i*r, and the cast into the cache format.  Ratio-4
+   layers run a second, narrower compressor of the same form for the indexer
+   (P1 s6).
+2. raw sliding window (P1 s2, s7; P4 "Short Sliding Window"): the last
+   min(128, p+1) tokens' rows u_t, RoPE'd at t.
+3. indexer (P1 s6; P4 "DSA"), ratio 4 only: score every visible compressed
+   row, keep the top k.
+4. attention (P1 s7; P4 "Shared Key and Value"): one softmax over the raw
+   window plus the selected (r=4) or all visible (r=128) compressed rows, the
+   same row serving as key and value, then inverse RoPE on the output tail.
+5. chunked prefill (P1 s3) is defined as the sequence of decode steps.
+
+Readings taken where the pages are silent (each also listed in the design
+notes): APE row = the token's slot in the window being pooled; a compressed
+row sits at position i*r; RoPE rotates adjacent channel pairs of the tail
+with theta_j = base^(-2j/n_rot); one RoPE base per layer; RMSNorm eps 1e-6;
+logit scale 1/sqrt(d); indexer score = sum_h w_h * relu(qI_h . kI_s) with the
+rotated indexer query cast to the indexer-cache format; top-k ties go to the
+lower index, output ascending with -1 padding; an fp8 row keeps its RoPE tail
+in bf16 and scales its other channels by max|z|/448.
+
+Parity pins for every function live in tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+F64 = np.float64
+
+# ===========================================================================
+# number formats (own codecs; textbook definitions)
+# ===========================================================================
+
+
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> values: the pattern is the top half of a float32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(F64)
+
+
+def _round_to_quantum(x: np.ndarray, mant_bits: int, min_exp: int) -> np.ndarray:
+    """Round-to-nearest-even onto a binary grid with ``mant_bits`` significant
+    bits and smallest quantum 2**min_exp (covers normal and subnormal ranges)."""
+    x = np.asarray(x, dtype=F64)
+    out = np.array(x, dtype=F64, copy=True)  # zeros keep their sign; inf / nan pass
+    nz = (x != 0) & np.isfinite(x)
+    _, e = np.frexp(x[nz])                   # x = m * 2**e with 0.5 <= |m| < 1
+    qexp = np.maximum(e - mant_bits, min_exp)
+    scaled = np.ldexp(x[nz], -qexp)          # exact (power-of-two scaling)
+    out[nz] = np.ldexp(np.rint(scaled), qexp)  # np.rint rounds half to even
+    return out
+
+
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """fp64 -> nearest bfloat16 value (8 significant bits, RNE, overflow to inf)."""
+    y = _round_to_quantum(x, 8, -133)
+    return np.where(np.abs(y) > BF16_MAX, np.copysign(np.inf, y), y)
+
+
+def bf16_encode(x: np.ndarray) -> np.ndarray:
+    """fp64 -> bfloat16 bit patterns (RNE)."""
+    v = bf16_round(x).astype(np.float32)     # exact: bf16 values are float32 values
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3FN code -> value.  Exponent bias 7, 3 mantissa bits, no
+    infinities; S.1111.111 is NaN; exponent field 0 holds subnormals m * 2^-9."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return s * val
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """fp64 -> nearest E4M3 value (4 significant bits, smallest quantum 2^-9,
+    RNE), saturated to +-448."""
+    y = _round_to_quantum(x, 4, -9)
+    return np.clip(y, -E4M3_MAX, E4M3_MAX)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """fp64 -> E4M3 code of ``e4m3_round(x)``."""
+    y = e4m3_round(x)
+    sign = (np.signbit(y)).astype(np.int64) << 7
+    a = np.abs(y)
+    code = np.zeros(a.shape, np.int64)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.int64)
+    nrm = ~sub
+    if np.any(nrm):
+        _, e = np.frexp(a[nrm])              # a = f * 2**e, f in [0.5, 1)
+        ef = e - 1 + 7                        # unbiased exponent e-1
+        m = np.rint((a[nrm] / np.ldexp(1.0, e - 1) - 1.0) * 8).astype(np.int64)
+        code[nrm] = (ef << 3) | m
+    return (code | sign).astype(np.uint8)
+
+
+def f32_round(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, F64).astype(np.float32).astype(F64)
+
+
+# ---------------------------------------------------------------------------
+# stored-row formats
+# ---------------------------------------------------------------------------
+
+def stored_row_bytes(fmt: str, d: int, n_rot: int) -> int:
+    """Size of one stored K=V row: f32 4d, bf16 2d; an fp8 row keeps
+    d - n_rot E4M3 codes, the n_rot RoPE channels in bf16 and one fp32 scale,
+    padded to a multiple of 128 bytes."""
+    if fmt == "f32":
+        return 4 * d
+    if fmt == "bf16":
+        return 2 * d
+    raw = (d - n_rot) + 2 * n_rot + 4
+    return (raw + 127) // 128 * 128
+
+
+def decode_values(a: np.ndarray, fmt: str) -> np.ndarray:
+    if fmt == "f32":
+        return np.asarray(a, np.float32).astype(F64)
+    if fmt == "bf16":
+        return bf16_decode(a)
+    raise ValueError(fmt)
+
+
+def cast_values(z: np.ndarray, fmt: str) -> np.ndarray:
+    """Value after storing ``z`` in format ``fmt`` (f32 or bf16, RNE)."""
+    if fmt == "f32":
+        return f32_round(z)
+    if fmt == "bf16":
+        return bf16_round(z)
+    raise ValueError(fmt)
+
+
+def decode_rows(rec: np.ndarray, fmt: str, d: int, n_rot: int) -> np.ndarray:
+    """Stored row records [..., rb] uint8 -> row values [..., d] fp64."""
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    shp = rec.shape[:-1]
+    if fmt == "f32":
+        return rec[..., :4 * d].copy().view(np.float32).reshape(shp + (d,)).astype(F64)
+    if fmt == "bf16":
+        return bf16_decode(rec[..., :2 * d].copy().view(np.uint16).reshape(shp + (d,)))
+    dn = d - n_rot
+    codes = rec[..., :dn]
+    tail = rec[..., dn:dn + 2 * n_rot].copy().view(np.uint16).reshape(shp + (n_rot,))
+    scale = rec[..., dn + 2 * n_rot:dn + 2 * n_rot + 4].copy().view(np.float32).reshape(shp)
+    out = np.empty(shp + (d,), F64)
+    out[..., :dn] = e4m3_decode(codes) * scale.astype(F64)[..., None]
+    out[..., dn:] = bf16_decode(tail)
+    return out
+
+
+def encode_row(z: np.ndarray, fmt: str, d: int, n_rot: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Store one row ``z`` [d]: returns (record bytes, stored value fp64).
+
+    fp8 rows (P1 s9: the FP8 round trip covers the non-RoPE part only): the
+    tail is kept as bf16; the other channels use the row scale
+    s = max|z_c| / 448 (1 when the row is all zero), kept as fp32, and the
+    codes RNE(z_c / s) saturated to +-448.
+    """
+    z = np.asarray(z, F64)
+    rb = stored_row_bytes(fmt, d, n_rot)
+    rec = np.zeros(rb, np.uint8)
+    if fmt == "f32":
+        v = z.astype(np.float32)
+        rec[:4 * d] = v.view(np.uint8)
+        return rec, v.astype(F64)
+    if fmt == "bf16":
+        bits = bf16_encode(z)
+        rec[:2 * d] = bits.view(np.uint8)
+        return rec, bf16_decode(bits)
+    dn = d - n_rot
+    amax = float(np.max(np.abs(z[:dn]))) if dn else 0.0
+    s32 = np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+    codes = e4m3_encode(z[:dn] / F64(s32))
+    tail = bf16_encode(z[dn:])
+    rec[:dn] = codes
+    rec[dn:dn + 2 * n_rot] = tail.view(np.uint8)
+    rec[dn + 2 * n_rot:dn + 2 * n_rot + 4] = np.array([s32], np.float32).view(np.uint8)
+    val = np.concatenate([e4m3_decode(codes) * F64(s32), bf16_decode(tail)])
+    return rec, val
+
+
+# ===========================================================================
+# method steps
+# ===========================================================================
+
+
+def rope_theta(base: float, n_rot: int) -> np.ndarray:
+    """theta_j = base^(-2j/n_rot), j = 0 .. n_rot/2 - 1."""
+    j = np.arange(n_rot // 2, dtype=F64)
+    return np.power(F64(base), -2.0 * j / n_rot)
+
+
+def rope_tail(x: np.ndarray, pos, base: float, n_rot: int) -> np.ndarray:
+    """Rotate only the last n_rot channels of each vector (P1 s8: the head's
+    first d - n_rot channels are left alone).  Channel pair
+    (d - n_rot + 2j, d - n_rot + 2j + 1) turns by the angle pos * theta_j;
+    a negative ``pos`` undoes the rotation at -pos.  ``pos`` may be an array
+    broadcasting against x[..., 0]."""
+    x = np.array(x, dtype=F64, copy=True)
+    d = x.shape[-1]
+    dn = d - n_rot
+    ang = np.multiply.outer(np.asarray(pos, F64), rope_theta(base, n_rot))  # [..., n_rot/2]
+    c, s = np.cos(ang), np.sin(ang)
+    a = x[..., dn + 0::2].copy()
+    b = x[..., dn + 1::2].copy()
+    # broadcast the angle over the head axis when x has one more axis than pos
+    while c.ndim < a.ndim:
+        c = c[..., None, :]
+        s = s[..., None, :]
+    x[..., dn + 0::2] = a * c - b * s
+    x[..., dn + 1::2] = a * s + b * c
+    return x
+
+
+def rmsnorm(y: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """z = gamma * y / sqrt(mean(y^2) + eps) (P1 s4 step 6)."""
+    y = np.asarray(y, F64)
+    return np.asarray(gamma, F64) * y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
+
+
+def window_positions(i: int, ratio: int) -> np.ndarray:
+    """Token position held by each slot j of compressed row i's window.
+
+    c4a: 8 tokens at stride 4, row i pooling the previous stride block (slots
+    0-3) and its own (slots 4-7): t_j = 4i - 4 + j (P1 s5, P4 c4a).
+    c128a: 128 tokens at stride 128: t_j = 128 i + j (P4 c128a)."""
+    if ratio == 4:
+        return 4 * i - 4 + np.arange(8)
+    if ratio == 128:
+        return 128 * i + np.arange(128)
+    raise ValueError(ratio)
+
+
+def softmax_pool(kappa: np.ndarray, score: np.ndarray) -> np.ndarray:
+    """Per-channel softmax-weighted pooling over the window axis (P1 s4):
+    for each channel, m = max_j score, w_j = exp(score_j - m),
+    y = sum_j w_j kappa_j / sum_j w_j (0 when the sum is 0).  Slots with score
+    -inf get weight 0."""
+    kappa = np.asarray(kappa, F64)
+    score = np.asarray(score, F64)
+    m = np.max(score, axis=0)
+    m = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(score - m)
+    w = np.where(np.isfinite(score), w, 0.0)
+    den = np.sum(w, axis=0)
+    num = np.sum(w * np.where(np.isfinite(score), kappa, 0.0), axis=0)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), 0.0)
+
+
+def pool_window(kappa_win: np.ndarray, sigma_win: np.ndarray, ape: np.ndarray,
+                valid: np.ndarray) -> np.ndarray:
+    """Pool one window: slot j scores sigma_j + APE[j] (P1 s4 step 3); slots
+    before token 0 are empty and carry no weight."""
+    e = np.asarray(sigma_win, F64) + np.asarray(ape, F64)
+    e = np.where(np.asarray(valid)[:, None], e, -np.inf)
+    return softmax_pool(kappa_win, e)
+
+
+def indexer_scores(qhat: np.ndarray, w: np.ndarray, rows: np.ndarray, relu: bool = True) -> np.ndarray:
+    """I(s) = sum_h w_h * relu(qhat_h . k_s) for every row s (P1 s6: the
+    narrow indexer representation scores every compressed row)."""
+    dots = np.asarray(rows, F64) @ np.asarray(qhat, F64).T       # [V, H_I]
+    if relu:
+        dots = np.maximum(dots, 0.0)
+    return dots @ np.asarray(w, F64)
+
+
+def topk_select(scores: np.ndarray, k: int) -> np.ndarray:
+    """The k largest scores' indices (ties to the lower index), listed in
+    ascending index order, -1-padded to length k; every index when there are
+    at most k scores (P1 s6, s7: negative entries are skipped by the
+    consumer)."""
+    V = len(scores)
+    out = np.full(k, -1, np.int32)
+    if V <= k:
+        out[:V] = np.arange(V)
+        return out
+    order = sorted(range(V), key=lambda s: (-float(scores[s]), s))
+    out[:] = np.sort(np.array(order[:k], np.int32))
+    return out
+
+
+def attention(qhat: np.ndarray, rows: np.ndarray, scale: float) -> np.ndarray:
+    """Shared-K=V attention (P4 "Shared Key and Value"): logits
+    l_hj = scale * qhat_h . k_j, a = softmax_j(l), o_h = sum_j a_hj k_j.
+    Two-pass softmax over the explicit row set."""
+    rows = np.asarray(rows, F64)
+    l = scale * (np.asarray(qhat, F64) @ rows.T)                  # [H, S]
+    l = l - np.max(l, axis=1, keepdims=True)
+    a = np.exp(l)
+    a = a / np.sum(a, axis=1, keepdims=True)
+    return a @ rows
+
+
+# ===========================================================================
+# one layer, history based
+# ===========================================================================
+
+
+@dataclass
+class OracleLayer:
+    """Layer parameters (fp64 copies of the stored weights)."""
+    ratio: int
+    head_dim: int
+    n_heads: int
+    idx_heads: int
+    idx_dim: int
+    top_k: int
+    n_rot: int
+    swa: int
+    rope_base: float
+    norm_eps: float
+    kv_fmt: str
+    idx_fmt: str
+    act_fmt: str
+    wkv: Optional[np.ndarray] = None
+    wgate: Optional[np.ndarray] = None
+    ape: Optional[np.ndarray] = None
+    gamma: Optional[np.ndarray] = None
+    idx_wkv: Optional[np.ndarray] = None
+    idx_wgate: Optional[np.ndarray] = None
+    idx_ape: Optional[np.ndarray] = None
+    idx_gamma: Optional[np.ndarray] = None
+    relu: bool = True
+
+    @property
+    def window(self) -> int:
+        return {4: 8, 128: 128}.get(self.ratio, 0)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+def layer_from(cfg, weights) -> OracleLayer:
+    """Build an OracleLayer from a workload shape and its stored weights."""
+    def w(a, fmt):
+        return None if a is None else decode_values(a, fmt)
+    L = OracleLayer(ratio=cfg.ratio, head_dim=cfg.head_dim, n_heads=cfg.n_heads,
+                    idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim, top_k=cfg.top_k,
+                    n_rot=cfg.n_rot, swa=cfg.swa, rope_base=cfg.rope_base,
+                    norm_eps=cfg.norm_eps, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt,
+                    act_fmt=cfg.act_fmt)
+    if weights is not None:
+        L.wkv = w(weights.wkv, cfg.w_fmt)
+        L.wgate = w(weights.wgate, cfg.w_fmt)
+        L.ape = weights.ape.astype(F64)
+        L.gamma = weights.gamma.astype(F64)
+        if weights.idx_wkv is not None:
+            L.idx_wkv = w(weights.idx_wkv, cfg.w_fmt)
+            L.idx_wgate = w(weights.idx_wgate, cfg.w_fmt)
+            L.idx_ape = weights.idx_ape.astype(F64)
+            L.idx_gamma = weights.idx_gamma.astype(F64)
+    return L
+
+
+class OracleSequence:
+    """One sequence's token history and the cache it implies.
+
+    Tokens fed through :meth:`feed` are live: their projections and raw rows
+    are computed here.  Everything from before the first live token comes
+    from the drawn cache bytes: compressed rows whose window ends before it,
+    raw rows, and the pending compressor window values (kappa, sigma) of the
+    tokens just before it.
+    """
+
+    def __init__(self, L: OracleLayer, raw_rec=None, comp_rec=None, idx_vals=None,
+                 st_kv=None, st_sc=None, ist_kv=None, ist_sc=None, first_live: int = 0):
+        self.L = L
+        self.first_live = int(first_live)
+        self.raw_rec = raw_rec          # [swa, rb] uint8 (ring, slot t mod swa)
+        self.comp_rec = comp_rec        # [cap, rb] uint8
+        self.idx_vals = idx_vals        # [cap, D_I] stored f32 / bf16 bits
+        self.kap: Dict[int, np.ndarray] = {}
+        self.sig: Dict[int, np.ndarray] = {}
+        self.ikap: Dict[int, np.ndarray] = {}
+        self.isig: Dict[int, np.ndarray] = {}
+        self.u: Dict[int, np.ndarray] = {}
+        self._row_cache: Dict[Tuple[str, int], Tuple[np.ndarray, np.ndarray, np.ndarray]] = {}
+        W = L.window
+        if W and st_kv is not None:
+            for t in range(max(0, first_live - W), first_live):
+                self.kap[t] = np.asarray(st_kv[t % W], F64)
+                self.sig[t] = np.asarray(st_sc[t % W], F64)
+        if L.ratio == 4 and ist_kv is not None:
+            for t in range(max(0, first_live - 8), first_live):
+                self.ikap[t] = np.asarray(ist_kv[t % 8], F64)
+                self.isig[t] = np.asarray(ist_sc[t % 8], F64)
+
+    # -- tokens ------------------------------------------------------------
+    def feed(self, t0: int, x: np.ndarray, u: np.ndarray) -> None:
+        """Make tokens t0 .. t0+len(x)-1 live: kappa = W_kv x, sigma = W_gate x
+        for the attention lane and (ratio 4) the indexer lane (P1 s4 steps 1-2)."""
+        L = self.L
+        X = decode_values(x, L.act_fmt).reshape(len(x), -1)
+        U = decode_values(u, L.act_fmt).reshape(len(u), -1)
+        if L.ratio:
+            K, S = X @ L.wkv.T, X @ L.wgate.T
+            has_idx = L.ratio == 4 and L.idx_wkv is not None
+            if has_idx:
+                KI, SI = X @ L.idx_wkv.T, X @ L.idx_wgate.T
+        for n in range(len(X)):
+            t = t0 + n
+            self.u[t] = U[n]
+            if L.ratio:
+                self.kap[t], self.sig[t] = K[n], S[n]
+                if has_idx:
+                    self.ikap[t], self.isig[t] = KI[n], SI[n]
+            for key in [k for k in self._row_cache if k[1] >= (t // max(L.ratio, 1)) - 1]:
+                del self._row_cache[key]
+
+    def is_live(self, t: int) -> bool:
+        return t in self.u
+
+    # -- compressed rows -----------------------------------------------------
+    def pooled(self, i: int, lane: str = "attn") -> np.ndarray:
+        """Row i's window pooled channel by channel, before normalisation."""
+        L = self.L
+        ts = window_positions(i, L.ratio)
+        kap, sig = (self.kap, self.sig) if lane == "attn" else (self.ikap, self.isig)
+        ape = L.ape if lane == "attn" else L.idx_ape
+        width = ape.shape[1]
+        valid = ts >= 0
+        kw = np.zeros((len(ts), width))
+        sw = np.zeros((len(ts), width))
+        for j, t in enumerate(ts):
+            if t >= 0:
+                kw[j], sw[j] = kap[int(t)], sig[int(t)]
+        return pool_window(kw, sw, ape, valid)
+
+    def _pool_row(self, i: int, lane: str) -> np.ndarray:
+        """Pool, RMS-normalise, then rotate the tail at the row position i*r
+        (P1 s4 steps 5-7)."""
+        L = self.L
+        y = self.pooled(i, lane)
+        gamma = L.gamma if lane == "attn" else L.idx_gamma
+        z = rmsnorm(y, gamma, L.norm_eps)
+        n_rot = min(L.n_rot, len(z))
+        return rope_tail(z, i * L.ratio, L.rope_base, n_rot)
+
+    def _row_is_computed(self, i: int) -> bool:
+        """Row i is computed from history when its last window token is live."""
+        last = i * self.L.ratio + self.L.ratio - 1
+        return self.is_live(last)
+
+    def comp_row(self, i: int) -> Tuple[np.ndarray, Optional[np.ndarray], np.ndarray]:
+        """(pre-cast value, stored record or None, stored value) of attention row i."""
+        key = ("attn", i)
+        if key not in self._row_cache:
+            L = self.L
+            if self._row_is_computed(i):
+                z = self._pool_row(i, "attn")
+                rec, val = encode_row(z, L.kv_fmt, L.head_dim, L.n_rot)
+                self._row_cache[key] = (z, rec, val)
+            else:
+                val = decode_rows(self.comp_rec[i], L.kv_fmt, L.head_dim, L.n_rot)
+                self._row_cache[key] = (val, None, val)
+        return self._row_cache[key]
+
+    def idx_row(self, i: int) -> Tuple[np.ndarray, np.ndarray]:
+        """(pre-cast value, stored value) of indexer row i."""
+        key = ("idx", i)
+        if key not in self._row_cache:
+            L = self.L
+            if self._row_is_computed(i):
+                z = self._pool_row(i, "idx")
+                self._row_cache[key] = (z, cast_values(z, L.idx_fmt), None)
+            else:
+                v = decode_values(self.idx_vals[i], L.idx_fmt)
+                self._row_cache[key] = (v, v, None)
+        return self._row_cache[key][:2]
+
+    # -- raw window ----------------------------------------------------------
+    def raw_row(self, t: int) -> Tuple[np.ndarray, Optional[np.ndarray], np.ndarray]:
+        """(pre-cast, record, stored value) of the raw row of token t: u_t RoPE'd
+        at t (P4: the SWA rows carry their position)."""
+        L = self.L
+        if self.is_live(t):
+            z = rope_tail(self.u[t], t, L.rope_base, L.n_rot)
+            rec, val = encode_row(z, L.kv_fmt, L.head_dim, L.n_rot)
+            return z, rec, val
+        val = decode_rows(self.raw_rec[t % L.swa], L.kv_fmt, L.head_dim, L.n_rot)
+        return val, None, val
+
+    # -- one query -------------------------------------------------------------
+    def visible_rows(self, p: int) -> int:
+        """V_p = floor((p+1)/r): rows whose window has closed by token p."""
+        return (p + 1) // self.L.ratio if self.L.ratio else 0
+
+    def raw_window(self, p: int) -> range:
+        """Raw positions max(0, p-swa+1) .. p (P1 s7 window rule)."""
+        return range(max(0, p + 1 - self.L.swa), p + 1)
+
+    def index_scores(self, p: int, qI: np.ndarray, w: np.ndarray) -> np.ndarray:
+        """Indexer scores of every visible row for query p.  The indexer query
+        gets the tail RoPE at p and is cast to the indexer-cache format."""
+        L = self.L
+        V = self.visible_rows(p)
+        qh = rope_tail(decode_values(qI, L.act_fmt), p, L.rope_base, min(L.n_rot, L.idx_dim))
+        qh = cast_values(qh, L.idx_fmt)
+        rows = np.stack([self.idx_row(i)[1] for i in range(V)]) if V else np.zeros((0, L.idx_dim))
+        return indexer_scores(qh, np.asarray(w, F64), rows, relu=L.relu)
+
+    def attend(self, p: int, q: np.ndarray, topk: Optional[np.ndarray]) -> np.ndarray:
+        """Output o [H, d] (pre-cast) for query p over raw window + compressed set."""
+        L = self.L
+        rows = [self.raw_row(t)[2] for t in self.raw_window(p)]
+        V = self.visible_rows(p)
+        if L.ratio == 4:
+            for i in topk:
+                if i < 0:
+                    continue
+                if i >= V:
+                    break
+                rows.append(self.comp_row(int(i))[2])
+        elif L.ratio == 128:
+            rows += [self.comp_row(i)[2] for i in range(V)]
+        qh = rope_tail(decode_values(q, L.act_fmt), p, L.rope_base, L.n_rot)
+        o = attention(qh, np.stack(rows), L.scale)
+        return rope_tail(o, -p, L.rope_base, L.n_rot)   # inverse RoPE (P4)
+
+    def step(self, p: int, x, u, q, qI=None, w=None, topk_override=None) -> dict:
+        """One decode step at token p: make p live, then index, select, attend."""
+        self.feed(p, np.asarray(x)[None], np.asarray(u)[None])
+        return self.query(p, q, qI, w, topk_override)
+
+    def query(self, p: int, q, qI=None, w=None, topk_override=None) -> dict:
+        L = self.L
+        res = {"p": p, "V": self.visible_rows(p)}
+        topk = None
+        if L.ratio == 4:
+            sc = self.index_scores(p, qI, w)
+            res["scores"] = sc
+            topk = topk_select(sc, L.top_k)
+            res["topk"] = topk
+            if topk_override is not None:
+                topk = np.asarray(topk_override)
+        o = self.attend(p, q, topk)
+        res["out_f64"] = o
+        res["out"] = cast_values(o, L.act_fmt)
+        return res
+
+
+def prefill(seq: OracleSequence, pos0: int, x, u, q, qI=None, w=None, queries=None) -> Dict[int, dict]:
+    """Chunked prefill, defined as the run of decode steps pos0 .. pos0+T-1
+    (P1 s3: the chunking keeps absolute compressor and indexer boundaries).
+    ``queries`` limits which positions' outputs are computed (all by default);
+    every token is made live regardless."""
+    T = len(x)
+    seq.feed(pos0, np.asarray(x), np.asarray(u))
+    want = range(pos0, pos0 + T) if queries is None else queries
+    out = {}
+    for p in want:
+        n = p - pos0
+        out[p] = seq.query(p, q[n], None if qI is None else qI[n], None if w is None else w[n])
+    return out
+
+
+# ===========================================================================
+# closed forms used as pins
+# ===========================================================================
+
+
+def flash_ratio(il: int) -> int:
+    """Flash layer schedule (P1 s1): layers 0-1 uncompressed, then even
+    layers ratio 4 and odd layers ratio 128."""
+    if il < 2:
+        return 0
+    return 4 if il % 2 == 0 else 128
+
+
+def pro_ratio(il: int) -> int:
+    """Pro layer schedule (P1 s1): layers 0-1 ratio 128, then alternating 4 / 128."""
+    if il < 2:
+        return 128
+    return 4 if il % 2 == 0 else 128
+
+
+def kv_bytes_per_sequence(n_tokens: int, ratios: Sequence[int], head_dim: int = 512,
+                          idx_dim: int = 128, swa: int = 128, attn_bytes_per_row: float = 1024,
+                          idx_bytes_per_row: float = 256) -> float:
+    """Bytes of KV cache one sequence of ``n_tokens`` needs over a stack with
+    the given per-layer ratios: c4a layers keep n/4 attention rows plus n/4
+    indexer rows, c128a layers n/128 attention rows, and every layer its
+    sliding window of ``swa`` raw rows (P4 "KV Cache Compression" and the
+    9.62 GiB figure)."""
+    total = 0.0
+    for r in ratios:
+        total += swa * attn_bytes_per_row
+        if r == 4:
+            total += n_tokens / 4 * (attn_bytes_per_row + idx_bytes_per_row)
+        elif r == 128:
+            total += n_tokens / 128 * attn_bytes_per_row
+    return total

@@ -1,0 +1,436 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+None of these compare the oracle with itself: each checks a closed form, an
+invariant, a library routine (torch's own bf16 / fp8 casts), a printed figure
+or a brute-force count on tiny inputs, chosen so that a dropped term, a wrong
+sign or index, or a transposed operand in the oracle fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import get_config, flash_ratio as wl_flash_ratio
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def test_bf16_round_matches_torch_rne():
+    x32 = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 20000).astype(np.float32),
+        np.array([1e-40, -3e-39, 3.3e38, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1 + 2 ** -8)], np.float32),
+    ])
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    got = O.bf16_round(x32.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+    # encode / decode round trip on the bit level
+    bits = O.bf16_encode(x32.astype(np.float64))
+    np.testing.assert_array_equal(O.bf16_decode(bits), ref)
+
+
+def test_bf16_round_is_single_rounding_from_fp64():
+    # 1 + 2^-8 + 2^-30 is just above the bf16 midpoint; rounding through
+    # float32 first would land on the midpoint and round to even (1.0).
+    x = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert O.bf16_round(np.array([x]))[0] == 1.0 + 2.0 ** -7
+    assert O.bf16_round(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+
+
+def test_e4m3_table_against_ocp_fixture():
+    g = json.load(open(os.path.join(GOLD, "e4m3_ocp_codes.json")))
+    for code, val in g["codes"].items():
+        v = O.e4m3_decode(np.array([int(code, 16)], np.uint8))[0]
+        assert v == val and math.copysign(1, v) == math.copysign(1, val), code
+    for code in g["nan_codes"]:
+        assert np.isnan(O.e4m3_decode(np.array([int(code, 16)], np.uint8))[0])
+    for x, code, why in g["rne_cases"]:
+        assert O.e4m3_encode(np.array([x]))[0] == int(code, 16), why
+
+
+def test_e4m3_all_codes_round_trip_and_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.e4m3_decode(codes)
+    finite = ~np.isnan(vals)
+    assert finite.sum() == 254
+    np.testing.assert_array_equal(O.e4m3_encode(vals[finite]), codes[finite])
+    tv = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    np.testing.assert_array_equal(vals[finite], tv[finite].astype(np.float64))
+    assert np.nanmax(vals) == 448.0
+    # random in-range values: encode agrees with torch's RNE cast
+    x = (rng.standard_normal(50000) * 10.0 ** rng.uniform(-3, 2.6, 50000)).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.e4m3_encode(x.astype(np.float64)), ref)
+
+
+def test_fp8_row_record_layout_and_scale():
+    d, n_rot = 512, 64
+    z = rng.standard_normal(d) * 3
+    rec, val = O.encode_row(z, "e4m3", d, n_rot)
+    assert rec.size == 640
+    dn = d - n_rot
+    s = rec[dn + 128:dn + 132].copy().view(np.float32)[0]
+    assert s == np.float32(np.max(np.abs(z[:dn])) / 448.0)
+    # the largest non-RoPE channel lands on the top code
+    j = int(np.argmax(np.abs(z[:dn])))
+    assert rec[j] & 0x7F == 0x7E
+    # tail is the bf16 value of the input, untouched by the scale
+    np.testing.assert_array_equal(val[dn:], O.bf16_round(z[dn:]))
+    assert np.max(np.abs(val[:dn] - z[:dn]) / np.max(np.abs(z[:dn]))) <= 2.0 ** -4
+    np.testing.assert_array_equal(O.decode_rows(rec, "e4m3", d, n_rot), val)
+    # all-zero non-RoPE part -> scale 1
+    rec0, _ = O.encode_row(np.zeros(d), "e4m3", d, n_rot)
+    assert rec0[dn + 128:dn + 132].copy().view(np.float32)[0] == 1.0
+
+
+# ---------------------------------------------------------------------------
+# RoPE on the tail only
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,n_rot,base", [(512, 64, 160000.0), (128, 64, 10000.0), (64, 64, 160000.0)])
+def test_rope_tail_invariants(d, n_rot, base):
+    x = rng.standard_normal((5, d))
+    p = 123457
+    y = O.rope_tail(x, p, base, n_rot)
+    dn = d - n_rot
+    np.testing.assert_array_equal(y[:, :dn], x[:, :dn])                  # head untouched
+    n_x = x[:, dn:].reshape(5, -1, 2)
+    n_y = y[:, dn:].reshape(5, -1, 2)
+    np.testing.assert_allclose(np.hypot(n_y[..., 0], n_y[..., 1]),
+                               np.hypot(n_x[..., 0], n_x[..., 1]), rtol=1e-13)
+    np.testing.assert_array_equal(O.rope_tail(x, 0, base, n_rot), x)      # position 0
+    np.testing.assert_allclose(O.rope_tail(O.rope_tail(x, 777, base, n_rot), 1234, base, n_rot),
+                               O.rope_tail(x, 2011, base, n_rot), atol=1e-12)
+    np.testing.assert_allclose(O.rope_tail(y, -p, base, n_rot), x, atol=1e-10)
+    # relative position: <R(p) a, R(s) b> depends on p - s only
+    a, b = rng.standard_normal(d), rng.standard_normal(d)
+    s1 = O.rope_tail(a, 1000, base, n_rot) @ O.rope_tail(b, 937, base, n_rot)
+    s2 = O.rope_tail(a, 5063, base, n_rot) @ O.rope_tail(b, 5000, base, n_rot)
+    assert abs(s1 - s2) < 1e-9
+
+
+def test_rope_pair_rotation_closed_form():
+    # pair j = 0 turns by exactly pos radians; the last pair by pos * base^(-(n_rot-2)/n_rot)
+    d, n_rot, base = 128, 64, 10000.0
+    for j, theta in ((0, 1.0), (n_rot // 2 - 1, base ** (-(n_rot - 2) / n_rot)), (16, base ** -0.5)):
+        x = np.zeros(d)
+        x[d - n_rot + 2 * j] = 1.0
+        y = O.rope_tail(x, 3, base, n_rot)
+        assert abs(y[d - n_rot + 2 * j] - math.cos(3 * theta)) < 1e-13
+        assert abs(y[d - n_rot + 2 * j + 1] - math.sin(3 * theta)) < 1e-13
+        assert np.count_nonzero(y) <= 2
+
+
+# ---------------------------------------------------------------------------
+# compressor pooling and norm
+# ---------------------------------------------------------------------------
+
+def _linear_history_layer(ratio, width=8, relu=True):
+    """Layer whose kappa_t = (t + 1) * v and sigma_t = 0 (hidden size 1)."""
+    v = np.linspace(-1.0, 2.0, width)
+    L = O.OracleLayer(ratio=ratio, head_dim=width, n_heads=1, idx_heads=0, idx_dim=0, top_k=0,
+                      n_rot=2, swa=128, rope_base=10000.0, norm_eps=1e-6, kv_fmt="f32",
+                      idx_fmt="f32", act_fmt="f32")
+    L.wkv = v[:, None].copy()
+    L.wgate = np.zeros((width, 1))
+    L.ape = np.zeros((L.window, width))
+    L.gamma = np.ones(width)
+    return L, v
+
+
+@pytest.mark.parametrize("ratio", [4, 128])
+def test_uniform_scores_reduce_pooling_to_mean(ratio):
+    L, v = _linear_history_layer(ratio)
+    seq = O.OracleSequence(L)
+    n = 3 * ratio + 5
+    seq.feed(0, np.arange(1, n + 1, dtype=np.float32)[:, None], np.zeros((n, 8), np.float32))
+    for i in range((n) // ratio):
+        y = seq.pooled(i)
+        if ratio == 4:
+            mean = 2.5 if i == 0 else 4 * i + 0.5
+        else:
+            mean = 128 * i + 64.5
+        np.testing.assert_allclose(y, mean * v, rtol=1e-12, atol=1e-12)
+
+
+def test_ape_slot_order_picks_window_ends():
+    # a dominant APE bias on one slot makes the row that slot's token
+    L, v = _linear_history_layer(4)
+    seq = O.OracleSequence(L)
+    seq.feed(0, np.arange(1, 33, dtype=np.float32)[:, None], np.zeros((32, 8), np.float32))
+    for slot, tok_of_row in ((7, lambda i: 4 * i + 3), (0, lambda i: 4 * i - 4), (4, lambda i: 4 * i)):
+        L.ape = np.zeros((8, 8))
+        L.ape[slot] = 60.0
+        for i in (1, 2, 5):
+            np.testing.assert_allclose(seq.pooled(i), (tok_of_row(i) + 1) * v, rtol=1e-12)
+    # row 0: slots 0-3 hold no token; a bias there must not select anything
+    L.ape = np.zeros((8, 8))
+    L.ape[0] = 60.0
+    np.testing.assert_allclose(seq.pooled(0), 2.5 * v, rtol=1e-12)
+
+
+def test_pooling_invariants():
+    W, c = 8, 16
+    kap = rng.standard_normal((W, c))
+    sc = rng.standard_normal((W, c)) * 3
+    y = O.softmax_pool(kap, sc)
+    # shift of the scores per channel does not matter
+    np.testing.assert_allclose(O.softmax_pool(kap, sc + rng.standard_normal(c) * 50), y, rtol=1e-11, atol=1e-12)
+    # convex combination per channel
+    assert np.all(y <= kap.max(0) + 1e-12) and np.all(y >= kap.min(0) - 1e-12)
+    # two-slot closed form: weight sigmoid(s0 - s1)
+    k2 = np.array([[1.0], [3.0]])
+    s2 = np.array([[0.7], [-0.4]])
+    w0 = 1 / (1 + math.exp(-(0.7 + 0.4)))
+    assert abs(O.softmax_pool(k2, s2)[0] - (w0 * 1 + (1 - w0) * 3)) < 1e-14
+
+
+def test_rmsnorm_closed_form():
+    y = rng.standard_normal((4, 64)) * rng.uniform(0.01, 10, (4, 1))
+    gamma = rng.uniform(0.5, 1.5, 64)
+    eps = 1e-6
+    z = O.rmsnorm(y, gamma, eps)
+    rms = np.sqrt(np.mean((z / gamma) ** 2, axis=1))
+    np.testing.assert_allclose(rms, (1 + eps / np.mean(y * y, axis=1)) ** -0.5, rtol=1e-12)
+    # direction preserved channel-wise: z / gamma is a positive multiple of y
+    ratio = (z / gamma) / y
+    np.testing.assert_allclose(ratio, ratio[:, :1] * np.ones_like(ratio), rtol=1e-12)
+
+
+def _small_layer(ratio, d=16, D=12, DI=8, n_rot=4, fmt="f32", seed=0):
+    r = np.random.default_rng(seed)
+    W = {4: 8, 128: 128}.get(ratio, 0)
+    L = O.OracleLayer(ratio=ratio, head_dim=d, n_heads=3, idx_heads=2, idx_dim=DI, top_k=4,
+                      n_rot=n_rot, swa=128, rope_base=10000.0, norm_eps=1e-6, kv_fmt=fmt,
+                      idx_fmt=fmt, act_fmt="f32")
+    if ratio:
+        L.wkv, L.wgate = r.standard_normal((d, D)) * 0.3, r.standard_normal((d, D)) * 0.3
+        L.ape, L.gamma = r.standard_normal((W, d)) * 0.2, np.ones(d)
+        if ratio == 4:
+            L.idx_wkv, L.idx_wgate = r.standard_normal((DI, D)) * 0.3, r.standard_normal((DI, D)) * 0.3
+            L.idx_ape, L.idx_gamma = r.standard_normal((8, DI)) * 0.2, np.ones(DI)
+    return L
+
+
+@pytest.mark.parametrize("ratio", [4, 128])
+def test_window_membership_by_perturbation(ratio):
+    L = _small_layer(ratio)
+    n = 4 * ratio + (3 if ratio == 4 else 0)
+    X = rng.standard_normal((n, 12)).astype(np.float32)
+    U = rng.standard_normal((n, 16)).astype(np.float32)
+    base = O.OracleSequence(L)
+    base.feed(0, X, U)
+    V = n // ratio
+    rows0 = [base.comp_row(i)[0] for i in range(V)]
+    for t in (0, 3, 4, 5, 9, n - 1) if ratio == 4 else (0, 127, 128, 300, n - 1):
+        X2 = X.copy()
+        X2[t] += 1.0
+        s2 = O.OracleSequence(L)
+        s2.feed(0, X2, U)
+        changed = {i for i in range(V) if not np.array_equal(s2.comp_row(i)[0], rows0[i])}
+        expect = {t // 4, t // 4 + 1} if ratio == 4 else {t // 128}
+        assert changed == {i for i in expect if i < V}, (t, changed)
+
+
+def test_row_counts_and_swa_cap():
+    # V = floor(n / r): 256, 16384, 8192, 32768, 1024 rows
+    L4 = _small_layer(4)
+    L128 = _small_layer(128)
+    s4, s128 = O.OracleSequence(L4), O.OracleSequence(L128)
+    assert s4.visible_rows(1023) == 256
+    assert s4.visible_rows(65535) == 16384
+    assert s128.visible_rows((1 << 20) - 1) == 8192
+    assert s4.visible_rows(131071) == 32768 and s128.visible_rows(131071) == 1024
+    # a 256-token block holds 64 c4a rows and 2 c128a rows (vLLM page)
+    assert s4.visible_rows(256 * 7 - 1) - s4.visible_rows(256 * 6 - 1) == 64
+    assert s128.visible_rows(256 * 7 - 1) - s128.visible_rows(256 * 6 - 1) == 2
+    # 1M tokens -> 262144 c4a rows ("250k")
+    assert s4.visible_rows((1 << 20) - 1) == 262144
+    # emission: row i appears exactly when token i*r + r - 1 is seen
+    for p in range(0, 40):
+        assert s4.visible_rows(p) == (p + 1) // 4
+    for p in (0, 5, 127, 128, 300):
+        assert len(s4.raw_window(p)) == min(128, p + 1)
+        assert s4.raw_window(p)[-1] == p
+
+
+# ---------------------------------------------------------------------------
+# indexer and top-k
+# ---------------------------------------------------------------------------
+
+def _brute_topk(scores, k):
+    """Row s is selected iff fewer than k rows beat it (higher score, or equal
+    score at a lower index)."""
+    V = len(scores)
+    sel = []
+    for s in range(V):
+        beats = sum(1 for t in range(V) if scores[t] > scores[s] or (scores[t] == scores[s] and t < s))
+        if beats < k:
+            sel.append(s)
+    return sel
+
+
+def test_topk_against_brute_force_tiny_exhaustive():
+    for V in range(0, 65, 3):
+        for k in (1, 2, 5, 8):
+            for trial in range(3):
+                if trial == 0:
+                    sc = rng.integers(0, 4, V).astype(np.float64)   # forced ties
+                else:
+                    sc = rng.standard_normal(V)
+                got = O.topk_select(sc, k)
+                ref = _brute_topk(sc, k)
+                assert list(got[got >= 0]) == ref
+                assert np.all(got[len(ref):] == -1) and len(got) == k
+                assert list(got[:len(ref)]) == sorted(got[:len(ref)])
+
+
+def test_indexer_score_closed_form_and_relu():
+    qh = np.array([[1.0, 0.0, 0.0], [0.0, 2.0, 0.0]])
+    w = np.array([0.5, 0.25])
+    rows = np.array([[2.0, 1.0, 9.0], [-3.0, 4.0, 0.0], [-1.0, -1.0, 5.0]])
+    # row0: 0.5*2 + 0.25*2 = 1.5; row1: 0.5*0 + 0.25*8 = 2; row2: 0
+    np.testing.assert_allclose(O.indexer_scores(qh, w, rows), [1.5, 2.0, 0.0])
+    np.testing.assert_allclose(O.indexer_scores(qh, w, rows, relu=False), [1.5, 0.5, -1.0])
+
+
+def test_topk_invariant_under_positive_head_weight_scale():
+    qh = rng.standard_normal((4, 16))
+    w = rng.uniform(0, 1, 4)
+    rows = rng.standard_normal((200, 16))
+    a = O.topk_select(O.indexer_scores(qh, w, rows), 20)
+    b = O.topk_select(O.indexer_scores(qh, 7.5 * w, rows), 20)
+    np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def test_attention_special_cases():
+    rows = rng.standard_normal((7, 32))
+    np.testing.assert_allclose(O.attention(np.zeros((3, 32)), rows, 0.17), np.tile(rows.mean(0), (3, 1)), rtol=1e-13)
+    np.testing.assert_allclose(O.attention(rng.standard_normal((2, 32)), rows[:1], 1.0), np.tile(rows[0], (2, 1)), rtol=1e-14)
+    # two rows with logits l0, l1 -> weight sigmoid(l0 - l1)
+    r2 = np.array([[1.0, 0.0], [0.0, 1.0]])
+    q = np.array([[2.0, -1.0]])
+    a0 = 1 / (1 + math.exp(-(0.5 * 2.0 - 0.5 * -1.0)))
+    np.testing.assert_allclose(O.attention(q, r2, 0.5), [[a0, 1 - a0]], rtol=1e-14)
+    # permutation of the row set does not matter
+    perm = rng.permutation(7)
+    qq = rng.standard_normal((4, 32))
+    np.testing.assert_allclose(O.attention(qq, rows[perm], 0.2), O.attention(qq, rows, 0.2), rtol=1e-12)
+
+
+def test_attention_translation_invariance_with_inverse_rope():
+    # same un-rotated rows and query; every position shifted by delta ->
+    # identical output once the output tail is rotated back (vLLM page: the
+    # inverse RoPE keeps shared K=V attention translation invariant)
+    d, n_rot, base = 64, 16, 160000.0
+    R = rng.standard_normal((20, d))
+    q = rng.standard_normal((3, d))
+    t = np.sort(rng.choice(5000, 20, replace=False))
+    p = 5000
+
+    def out(shift):
+        rows = O.rope_tail(R, t + shift, base, n_rot)
+        qh = O.rope_tail(q, p + shift, base, n_rot)
+        return O.rope_tail(O.attention(qh, rows, d ** -0.5), -(p + shift), base, n_rot)
+
+    np.testing.assert_allclose(out(0), out(4 * 12345), atol=1e-9)
+    # without the inverse rotation the tails differ
+    rows0 = O.rope_tail(R, t, base, n_rot)
+    o_plain = O.attention(O.rope_tail(q, p, base, n_rot), rows0, d ** -0.5)
+    assert not np.allclose(o_plain[:, -n_rot:], out(0)[:, -n_rot:], atol=1e-6)
+
+
+def test_swa_only_layer_first_token_returns_its_row():
+    # ratio 0, p = 0: the only visible row is u_0, so every head returns u_0
+    L = _small_layer(0)
+    seq = O.OracleSequence(L)
+    u0 = rng.standard_normal(16).astype(np.float32)
+    res = seq.step(0, np.zeros(12, np.float32), u0, rng.standard_normal((3, 16)).astype(np.float32))
+    np.testing.assert_allclose(res["out_f64"], np.tile(u0.astype(np.float64), (3, 1)), rtol=1e-12, atol=1e-12)
+
+
+def test_zero_query_gives_mean_of_attended_rows():
+    L = _small_layer(4)
+    seq = O.OracleSequence(L)
+    n = 60
+    X = rng.standard_normal((n, 12)).astype(np.float32)
+    U = rng.standard_normal((n, 16)).astype(np.float32)
+    seq.feed(0, X, U)
+    p = n - 1
+    topk = np.array([3, 7, 11, -1], np.int32)
+    res = seq.query(p, np.zeros((3, 16), np.float32), rng.standard_normal((2, 8)).astype(np.float32),
+                    rng.uniform(0, 1, 2), topk_override=topk)
+    rows = [seq.raw_row(t)[2] for t in range(0, p + 1)] + [seq.comp_row(i)[2] for i in (3, 7, 11)]
+    mean = O.rope_tail(np.mean(rows, axis=0), -p, L.rope_base, L.n_rot)
+    np.testing.assert_allclose(res["out_f64"], np.tile(mean, (3, 1)), rtol=1e-11, atol=1e-12)
+    # -1 entries and any order of the list give the same output
+    qx = rng.standard_normal((3, 16)).astype(np.float32)
+    a = seq.query(p, qx, np.zeros((2, 8), np.float32), np.ones(2), topk_override=[11, -1, 3, 7])["out_f64"]
+    b = seq.query(p, qx, np.zeros((2, 8), np.float32), np.ones(2), topk_override=[3, 7, 11, -1])["out_f64"]
+    np.testing.assert_allclose(a, b, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# prefill vs decode, schedule, cache sizes
+# ---------------------------------------------------------------------------
+
+def test_prefill_equals_sequential_decode():
+    L = _small_layer(4)
+    n = 45
+    X = rng.standard_normal((n, 12)).astype(np.float32)
+    U = rng.standard_normal((n, 16)).astype(np.float32)
+    Q = rng.standard_normal((n, 3, 16)).astype(np.float32)
+    QI = rng.standard_normal((n, 2, 8)).astype(np.float32)
+    Wt = rng.uniform(0, 1, (n, 2))
+    dec = O.OracleSequence(L)
+    outs = [dec.step(p, X[p], U[p], Q[p], QI[p], Wt[p])["out_f64"] for p in range(n)]
+    chk = O.OracleSequence(L)
+    p0 = 0
+    res = {}
+    for T in (37, 1, 7):
+        res.update(O.prefill(chk, p0, X[p0:p0 + T], U[p0:p0 + T], Q[p0:p0 + T], QI[p0:p0 + T], Wt[p0:p0 + T]))
+        p0 += T
+    for p in range(n):
+        np.testing.assert_array_equal(res[p]["out_f64"], outs[p])
+
+
+def test_flash_schedule():
+    r = [O.flash_ratio(i) for i in range(43)]
+    assert r[:2] == [0, 0] and r.count(4) == 21 and r.count(128) == 20
+    assert r == [wl_flash_ratio(i) for i in range(43)]
+    rp = [O.pro_ratio(i) for i in range(61)]
+    assert rp.count(4) == 30 and rp.count(128) == 31
+
+
+def test_kv_cache_size_figures_of_the_vllm_page():
+    g = json.load(open(os.path.join(GOLD, "kv_cache_sizes.json")))
+    n = g["n_tokens"]
+    pro = [O.pro_ratio(i) for i in range(g["pro_layers"])]
+    v4 = O.kv_bytes_per_sequence(n, pro) / 2 ** 30
+    # V3.2-style: every layer keeps every token (576-wide MLA latent + 128 indexer, bf16)
+    v32 = g["pro_layers"] * n * (576 + 128) * 2 / 2 ** 30
+    tol = g["print_precision"]
+    assert abs(v4 - g["v4_bf16_gib"]) <= tol["v4_bf16_gib"]
+    assert abs(v32 - g["v32_bf16_gib"]) <= tol["v32_bf16_gib"]
+    assert abs(v32 / v4 - g["ratio"]) <= tol["ratio"]
+    fp = O.kv_bytes_per_sequence(n, pro, attn_bytes_per_row=448 + 128, idx_bytes_per_row=64) / 2 ** 30
+    assert abs(fp / v4 - g["fp8_fp4_factor"]) <= tol["fp8_fp4_factor"]
+
+
+def test_workload_row_counts():
+    assert get_config("c2").comp_cap == 16384
+    assert get_config("c5").comp_cap == 32768 and get_config("c5_c128a").comp_cap == 1024
+    assert get_config("c3").comp_cap == 8192
