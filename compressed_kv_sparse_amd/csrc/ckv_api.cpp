@@ -1,0 +1,202 @@
+// C ABI entry points of libckv: argument checks on the host, then kernel
+// enqueues on the caller's stream.  Nothing here synchronises or allocates.
+#include <stdint.h>
+
+#include "ckv_internal.h"
+
+using namespace ckv;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_ptr(const void* p) { return (p && aligned16(p)) ? CKV_OK : CKV_E_INVAL; }
+
+Weights to_weights(const ckv_layer_weights* w) {
+  Weights x;
+  x.wkv = w->wkv;
+  x.wgate = w->wgate;
+  x.ape = w->ape;
+  x.gamma = w->gamma;
+  x.idx_wkv = w->idx_wkv;
+  x.idx_wgate = w->idx_wgate;
+  x.idx_ape = w->idx_ape;
+  x.idx_gamma = w->idx_gamma;
+  return x;
+}
+
+Cache to_cache(const ckv_layer_cache* c) {
+  Cache x;
+  x.raw = (uint8_t*)c->raw;
+  x.comp = (uint8_t*)c->comp;
+  x.idx = c->idx;
+  x.st_kv = c->st_kv;
+  x.st_sc = c->st_sc;
+  x.ist_kv = c->ist_kv;
+  x.ist_sc = c->ist_sc;
+  x.stage = (uint8_t*)c->raw_stage;
+  x.stage_rows = c->stage_rows;
+  x.status = c->status;
+  return x;
+}
+
+// Common prologue: validate the description and the cache pointers a layer of
+// this ratio uses.
+int prologue(const ckv_layer_desc* d, const ckv_layer_cache* c, LayerParams* P) {
+  int rc = ckv_validate(d);
+  if (rc) return rc;
+  if (!c) return CKV_E_INVAL;
+  make_params(d, P);
+  if (check_ptr(c->raw)) return CKV_E_INVAL;
+  if (P->ratio) {
+    if (check_ptr(c->comp) || check_ptr(c->st_kv) || check_ptr(c->st_sc)) return CKV_E_INVAL;
+  }
+  if (P->ratio == 4) {
+    if (check_ptr(c->idx) || check_ptr(c->ist_kv) || check_ptr(c->ist_sc)) return CKV_E_INVAL;
+  }
+  return CKV_OK;
+}
+
+int check_ws(const LayerParams& P, int mode, int n, void* ws, size_t ws_bytes, WsLayout* L) {
+  *L = ws_layout(P, mode, n);
+  if (!ws || !aligned16(ws) || ws_bytes < L->total) return CKV_E_WORKSPACE;
+  return CKV_OK;
+}
+
+int weights_ok(const LayerParams& P, const ckv_layer_weights* w) {
+  if (P.ratio == 0) return CKV_OK;
+  if (!w) return CKV_E_INVAL;
+  if (check_ptr(w->wkv) || check_ptr(w->wgate) || check_ptr(w->ape) || check_ptr(w->gamma))
+    return CKV_E_INVAL;
+  if (P.ratio == 4 && (check_ptr(w->idx_wkv) || check_ptr(w->idx_wgate) || check_ptr(w->idx_ape) ||
+                       check_ptr(w->idx_gamma)))
+    return CKV_E_INVAL;
+  return CKV_OK;
+}
+
+int prefill_range_ok(const LayerParams& P, const ckv_layer_cache* c, int32_t seq, int32_t pos0,
+                     int32_t T) {
+  if (T < 1 || pos0 < 0 || seq < 0) return CKV_E_INVAL;
+  if (T > CKV_MAX_CHUNK || seq >= P.batch) return CKV_E_CAPACITY;
+  if ((long long)pos0 + T > (1ll << 30)) return CKV_E_CAPACITY;
+  if (P.ratio && (pos0 + T) / P.ratio > P.cap) return CKV_E_CAPACITY;
+  if (!c->raw_stage || !aligned16(c->raw_stage)) return CKV_E_INVAL;
+  if (c->stage_rows < T + P.swa - 1) return CKV_E_CAPACITY;
+  return CKV_OK;
+}
+
+int launched(int hip_rc) { return hip_rc ? CKV_E_HIP : CKV_OK; }
+
+}  // namespace
+
+extern "C" int ckv_compress_append_decode(const ckv_layer_desc* desc, const ckv_layer_weights* w,
+                                          const ckv_layer_cache* cache, const void* x, const void* u,
+                                          const int32_t* pos, int32_t B, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  LayerParams P;
+  int rc = prologue(desc, cache, &P);
+  if (rc) return rc;
+  if (B < 1) return CKV_E_INVAL;
+  if (B > P.batch) return CKV_E_CAPACITY;
+  if ((rc = weights_ok(P, w))) return rc;
+  if (check_ptr(u) || check_ptr(pos) || (P.ratio && check_ptr(x))) return CKV_E_INVAL;
+  WsLayout L;
+  if ((rc = check_ws(P, CKV_MODE_DECODE, B, ws, ws_bytes, &L))) return rc;
+  const Weights W = P.ratio ? to_weights(w) : Weights{};
+  const Cache C = to_cache(cache);
+  float* part = (float*)((uint8_t*)ws + L.proj);
+  if (P.ratio) {
+    if ((rc = launch_proj(P, W, x, B, part, L.proj_splits, stream))) return launched(rc);
+  }
+  return launched(launch_compress_decode(P, W, C, u, pos, B, part, L.proj_splits, stream));
+}
+
+extern "C" int ckv_compress_append_prefill(const ckv_layer_desc* desc, const ckv_layer_weights* w,
+                                           const ckv_layer_cache* cache, const void* x, const void* u,
+                                           int32_t seq, int32_t pos0, int32_t T, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  LayerParams P;
+  int rc = prologue(desc, cache, &P);
+  if (rc) return rc;
+  if ((rc = prefill_range_ok(P, cache, seq, pos0, T))) return rc;
+  if ((rc = weights_ok(P, w))) return rc;
+  if (check_ptr(u) || (P.ratio && check_ptr(x))) return CKV_E_INVAL;
+  WsLayout L;
+  if ((rc = check_ws(P, CKV_MODE_PREFILL, T, ws, ws_bytes, &L))) return rc;
+  const Weights W = P.ratio ? to_weights(w) : Weights{};
+  const Cache C = to_cache(cache);
+  float* part = (float*)((uint8_t*)ws + L.proj);
+  if (P.ratio) {
+    if ((rc = launch_proj(P, W, x, T, part, 1, stream))) return launched(rc);
+  }
+  return launched(launch_compress_prefill(P, W, C, u, seq, pos0, T, part, stream));
+}
+
+extern "C" int ckv_indexer_topk_decode(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
+                                       const void* qI, const float* w, const int32_t* pos, int32_t B,
+                                       int32_t* topk, void* ws, size_t ws_bytes, void* stream) {
+  LayerParams P;
+  int rc = prologue(desc, cache, &P);
+  if (rc) return rc;
+  if (P.ratio != 4) return CKV_E_UNSUPPORTED;
+  if (B < 1) return CKV_E_INVAL;
+  if (B > P.batch) return CKV_E_CAPACITY;
+  if (check_ptr(qI) || check_ptr(w) || check_ptr(pos) || check_ptr(topk)) return CKV_E_INVAL;
+  WsLayout L;
+  if ((rc = check_ws(P, CKV_MODE_DECODE, B, ws, ws_bytes, &L))) return rc;
+  uint8_t* wb = (uint8_t*)ws;
+  return launched(launch_indexer(P, to_cache(cache), qI, w, pos, 0, 0, B, (uint32_t*)(wb + L.keys),
+                                 (uint32_t*)(wb + L.hist), topk, stream));
+}
+
+extern "C" int ckv_indexer_topk_prefill(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
+                                        const void* qI, const float* w, int32_t seq, int32_t pos0,
+                                        int32_t T, int32_t* topk, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  LayerParams P;
+  int rc = prologue(desc, cache, &P);
+  if (rc) return rc;
+  if (P.ratio != 4) return CKV_E_UNSUPPORTED;
+  if (T < 1 || pos0 < 0 || seq < 0) return CKV_E_INVAL;
+  if (T > CKV_MAX_CHUNK || seq >= P.batch || (pos0 + T) / 4 > P.cap) return CKV_E_CAPACITY;
+  if (check_ptr(qI) || check_ptr(w) || check_ptr(topk)) return CKV_E_INVAL;
+  WsLayout L;
+  if ((rc = check_ws(P, CKV_MODE_PREFILL, T, ws, ws_bytes, &L))) return rc;
+  uint8_t* wb = (uint8_t*)ws;
+  return launched(launch_indexer(P, to_cache(cache), qI, w, nullptr, seq, pos0, T,
+                                 (uint32_t*)(wb + L.keys), (uint32_t*)(wb + L.hist), topk, stream));
+}
+
+extern "C" int ckv_sparse_swa_attn_decode(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
+                                          const void* q, const int32_t* pos, const int32_t* topk,
+                                          int32_t B, void* out, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  LayerParams P;
+  int rc = prologue(desc, cache, &P);
+  if (rc) return rc;
+  if (B < 1) return CKV_E_INVAL;
+  if (B > P.batch) return CKV_E_CAPACITY;
+  if (check_ptr(q) || check_ptr(pos) || check_ptr(out)) return CKV_E_INVAL;
+  if ((P.ratio == 4) != (topk != nullptr)) return CKV_E_INVAL;
+  if (topk && !aligned16(topk)) return CKV_E_INVAL;
+  WsLayout L;
+  if ((rc = check_ws(P, CKV_MODE_DECODE, B, ws, ws_bytes, &L))) return rc;
+  return launched(launch_attn(P, to_cache(cache), q, pos, 0, 0, B, topk, out, L, (uint8_t*)ws, stream));
+}
+
+extern "C" int ckv_sparse_swa_attn_prefill(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
+                                           const void* q, int32_t seq, int32_t pos0, int32_t T,
+                                           const int32_t* topk, void* out, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  LayerParams P;
+  int rc = prologue(desc, cache, &P);
+  if (rc) return rc;
+  if ((rc = prefill_range_ok(P, cache, seq, pos0, T))) return rc;
+  if (check_ptr(q) || check_ptr(out)) return CKV_E_INVAL;
+  if ((P.ratio == 4) != (topk != nullptr)) return CKV_E_INVAL;
+  if (topk && !aligned16(topk)) return CKV_E_INVAL;
+  WsLayout L;
+  if ((rc = check_ws(P, CKV_MODE_PREFILL, T, ws, ws_bytes, &L))) return rc;
+  return launched(
+      launch_attn(P, to_cache(cache), q, nullptr, seq, pos0, T, topk, out, L, (uint8_t*)ws, stream));
+}

@@ -1,0 +1,147 @@
+// Device helpers shared by the CDNA4 (gfx950) kernels of libckv.
+//
+// Number formats: bfloat16 (round to nearest even) and OCP FP8 E4M3FN with a
+// float32 row scale (the attention-cache format of "ds4.c を読み解く (#3)",
+// section 9: the non-RoPE channels go through FP8, the RoPE tail does not).
+// Both codecs are written from the format definitions with integer bit
+// arithmetic, so their rounding does not depend on the hardware converters.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ckv_internal.h"
+
+namespace ckv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bfloat16
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float32 -> bfloat16 bits, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- E4M3FN
+
+// code -> value.  Exponent field 0 holds subnormals m * 2^-9; otherwise the
+// value is (1 + m/8) * 2^(e-7).  The NaN pattern is never stored.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -v : v;
+}
+
+// value -> code, round to nearest even on the E4M3 grid, saturated to +-448.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
+  const float a = fabsf(f);
+  if (!(a < 448.0f)) return sign | 0x7eu;           // also catches values that round past 448
+  if (a < 0.015625f) {                               // below 2^-6: quantum 2^-9
+    const float m = __builtin_rintf(a * 512.0f);     // exact scaling, RNE
+    return sign | (uint32_t)m;                        // m == 8 encodes 2^-6 itself
+  }
+  uint32_t u = __float_as_uint(a);
+  u += 0x7ffffu + ((u >> 20) & 1u);                  // RNE to 3 mantissa bits
+  const uint32_t e = (u >> 23) - 120u;               // E4M3 exponent field
+  const uint32_t m = (u >> 20) & 7u;
+  if (e > 15u || (e == 15u && m == 7u)) return sign | 0x7eu;
+  return sign | (e << 3) | m;
+}
+
+// ---------------------------------------------------------------- RoPE
+
+// cos / sin of pos * base^(-2j/n_rot), the angle formed and reduced in fp64 so
+// that positions near 2^20 keep full float accuracy.
+__device__ __forceinline__ void rope_cs(double base, int n_rot, int j, double pos, float* c,
+                                        float* s) {
+  const double theta = pow(base, -2.0 * (double)j / (double)n_rot);
+  double sn, cs;
+  sincos(pos * theta, &sn, &cs);
+  *c = (float)cs;
+  *s = (float)sn;
+}
+
+// ---------------------------------------------------------------- MFMA
+
+// D = A(16x32) * B(32x16) + C on bf16 inputs with fp32 accumulation.
+// Lane l holds A[l%16][8(l/16) .. 8(l/16)+7], B[8(l/16) .. +7][l%16] and
+// returns D[4(l/16) + i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum; `red` is LDS scratch of at least blockDim.x/64 floats.
+// Every thread returns the total.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = -INFINITY;
+  for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+// ---------------------------------------------------------------- format IO
+
+template <int FMT>
+__device__ __forceinline__ float load_val(const void* p, long i) {
+  if constexpr (FMT == CKV_F32) return ((const float*)p)[i];
+  else return bf16_to_f32(((const uint16_t*)p)[i]);
+}
+
+template <int FMT>
+__device__ __forceinline__ void store_val(void* p, long i, float v) {
+  if constexpr (FMT == CKV_F32) ((float*)p)[i] = v;
+  else ((uint16_t*)p)[i] = (uint16_t)f32_to_bf16(v);
+}
+
+// float key that orders like the float (larger float -> larger key); -0 is
+// first folded onto +0 so the two compare equal.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace ckv

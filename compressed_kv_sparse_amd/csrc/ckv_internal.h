@@ -1,0 +1,88 @@
+// Internal declarations of libckv: the normalised layer parameters the kernels
+// take, the workspace layout, and the kernel launchers the C ABI dispatches to.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ckv.h"
+
+namespace ckv {
+
+constexpr int kHistBins = 4096;   // first-level top-k histogram: top 12 key bits
+constexpr int kMaxD = 512;
+constexpr int kMaxDI = 128;
+
+// Layer parameters as the kernels see them (built from ckv_layer_desc after
+// validation; plain values, passed by value to every kernel).
+struct LayerParams {
+  int ratio, hidden, d, n_rot, H, swa, HI, DI, topk, cap, batch;
+  int kv_fmt, idx_fmt, act_fmt, w_fmt;
+  unsigned flags;
+  double base;
+  float eps, scale;
+  int W;          // compressor window: 8 (ratio 4), 128 (ratio 128), 0
+  int row_bytes;  // stored K=V row size
+  int ncol;       // projection columns: 2d (+ 2 DI on ratio 4)
+  int idx_rot;    // RoPE channels of indexer rows / queries: min(n_rot, DI)
+};
+
+struct Weights {
+  const void* wkv;
+  const void* wgate;
+  const float* ape;
+  const float* gamma;
+  const void* idx_wkv;
+  const void* idx_wgate;
+  const float* idx_ape;
+  const float* idx_gamma;
+};
+
+struct Cache {
+  uint8_t* raw;
+  uint8_t* comp;
+  void* idx;
+  float* st_kv;
+  float* st_sc;
+  float* ist_kv;
+  float* ist_sc;
+  uint8_t* stage;
+  int stage_rows;
+  uint32_t* status;
+};
+
+// Workspace carve-up (all offsets 256-byte aligned).
+struct WsLayout {
+  size_t proj;      // float [proj_splits][n][ncol]
+  size_t keys;      // uint32 [n][cap]   indexer keys
+  size_t hist;      // uint32 [n][kHistBins]
+  size_t part_o;    // float [n][splits][H][d]  attention partial outputs
+  size_t part_ml;   // float [n][splits][H][2]  attention partial (max, sum)
+  size_t total;
+  int proj_splits;
+  int attn_splits;
+  int attn_rows_per_split;
+};
+
+bool make_params(const ckv_layer_desc* desc, LayerParams* P);
+WsLayout ws_layout(const LayerParams& P, int mode, int n);
+int attn_max_rows(const LayerParams& P);
+
+// ---- launchers (return 0 or a hipError_t value) ----------------------------
+// projection: part[s][m][c] for columns c of the concatenated weights
+int launch_proj(const LayerParams& P, const Weights& w, const void* x, int M, float* part,
+                int splits, void* stream);
+int launch_compress_decode(const LayerParams& P, const Weights& w, const Cache& c, const void* u,
+                           const int32_t* pos, int B, const float* part, int splits, void* stream);
+int launch_compress_prefill(const LayerParams& P, const Weights& w, const Cache& c, const void* u,
+                            int seq, int pos0, int T, const float* part, void* stream);
+// indexer: decode (pos != NULL, query b of sequence b) or prefill (pos == NULL,
+// query n of sequence seq at position pos0 + n)
+int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
+                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
+                   int32_t* topk, void* stream);
+int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32_t* pos, int seq,
+                int pos0, int nq, const int32_t* topk, void* out, const WsLayout& L, uint8_t* ws,
+                void* stream);
+
+}  // namespace ckv

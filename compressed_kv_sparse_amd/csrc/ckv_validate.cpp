@@ -1,0 +1,150 @@
+// Host-only, HIP-free part of libckv: layer-description checks, row sizes,
+// workspace sizing and error strings.  Compiles with a plain C++ compiler so
+// that its checks can be exercised on a machine without a GPU.
+//
+// The engine described in "ds4.c を読み解く (#3)" (section 1) refuses a model
+// whose layout differs from the one it was built for instead of guessing;
+// ckv_validate applies the same rule to a layer description.
+#include <math.h>
+#include <string.h>
+
+#include "ckv_internal.h"
+
+namespace ckv {
+
+static bool fmt_ok(int f, bool allow_e4m3) {
+  return f == CKV_F32 || f == CKV_BF16 || (allow_e4m3 && f == CKV_E4M3);
+}
+
+bool make_params(const ckv_layer_desc* d, LayerParams* P) {
+  memset(P, 0, sizeof(*P));
+  P->ratio = d->ratio;
+  P->hidden = d->hidden;
+  P->d = d->head_dim;
+  P->n_rot = d->n_rot;
+  P->H = d->n_heads;
+  P->swa = d->swa;
+  P->HI = d->ratio == 4 ? d->idx_heads : 0;
+  P->DI = d->ratio == 4 ? d->idx_dim : 0;
+  P->topk = d->ratio == 4 ? d->top_k : 0;
+  P->cap = d->ratio ? d->comp_cap : 0;
+  P->batch = d->batch;
+  P->kv_fmt = d->kv_fmt;
+  P->idx_fmt = d->idx_fmt;
+  P->act_fmt = d->act_fmt;
+  P->w_fmt = d->w_fmt;
+  P->flags = d->flags;
+  P->base = d->rope_base;
+  P->eps = d->norm_eps;
+  P->scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / sqrt((double)d->head_dim));
+  P->W = d->ratio == 4 ? 8 : d->ratio == 128 ? 128 : 0;
+  P->row_bytes = (int)ckv_row_bytes(d->kv_fmt, d->head_dim, d->n_rot);
+  P->ncol = d->ratio == 0 ? 0 : 2 * d->head_dim + (d->ratio == 4 ? 2 * d->idx_dim : 0);
+  P->idx_rot = d->ratio == 4 ? (d->idx_dim < d->n_rot ? d->idx_dim : d->n_rot) : 0;
+  return true;
+}
+
+int attn_max_rows(const LayerParams& P) {
+  return P.swa + (P.ratio == 4 ? P.topk : P.ratio == 128 ? P.cap : 0);
+}
+
+static bool attn_is_mfma(const LayerParams& P) {
+  return P.act_fmt == CKV_BF16 && P.kv_fmt != CKV_F32 && P.H % 64 == 0 &&
+         (P.d == 512 || P.d == 128) && P.n_rot == 64;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const LayerParams& P, int mode, int n) {
+  WsLayout L;
+  memset(&L, 0, sizeof(L));
+  const bool prefill = mode == CKV_MODE_PREFILL;
+  const bool proj_mfma = P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16;
+  L.proj_splits = (!prefill && proj_mfma) ? (P.hidden >= 1024 ? P.hidden / 512 : 1) : 1;
+  const int rows = attn_max_rows(P);
+  int rps;
+  if (attn_is_mfma(P)) {
+    if (prefill) rps = rows;
+    else rps = P.ratio == 4 ? 64 : P.ratio == 128 ? 256 : 32;
+  } else {
+    rps = 32;
+  }
+  rps = (rps + 31) / 32 * 32;
+  L.attn_rows_per_split = rps;
+  L.attn_splits = (rows + rps - 1) / rps;
+  size_t off = 0;
+  L.proj = off;
+  off += align256((size_t)L.proj_splits * n * P.ncol * sizeof(float));
+  L.keys = off;
+  if (P.ratio == 4) off += align256((size_t)n * P.cap * sizeof(uint32_t));
+  L.hist = off;
+  if (P.ratio == 4) off += align256((size_t)n * kHistBins * sizeof(uint32_t));
+  const bool need_part = !(attn_is_mfma(P) && L.attn_splits == 1);
+  L.part_o = off;
+  if (need_part) off += align256((size_t)n * L.attn_splits * P.H * P.d * sizeof(float));
+  L.part_ml = off;
+  if (need_part) off += align256((size_t)n * L.attn_splits * P.H * 2 * sizeof(float));
+  L.total = off ? off : 256;
+  return L;
+}
+
+}  // namespace ckv
+
+using namespace ckv;
+
+extern "C" size_t ckv_row_bytes(int32_t fmt, int32_t head_dim, int32_t n_rot) {
+  if (head_dim <= 0 || n_rot < 0 || n_rot > head_dim) return 0;
+  if (fmt == CKV_F32) return (size_t)4 * head_dim;
+  if (fmt == CKV_BF16) return (size_t)2 * head_dim;
+  if (fmt == CKV_E4M3) {
+    const size_t raw = (size_t)(head_dim - n_rot) + 2 * (size_t)n_rot + 4;
+    return (raw + 127) / 128 * 128;
+  }
+  return 0;
+}
+
+extern "C" int ckv_validate(const ckv_layer_desc* d) {
+  if (!d) return CKV_E_INVAL;
+  if (d->batch <= 0 || d->hidden <= 0 || d->head_dim <= 0 || d->n_heads <= 0) return CKV_E_INVAL;
+  if (!(d->rope_base > 0.0) || !(d->norm_eps >= 0.f) || !(d->softmax_scale >= 0.f)) return CKV_E_INVAL;
+  if (d->ratio != 0 && d->ratio != 4 && d->ratio != 128) return CKV_E_UNSUPPORTED;
+  if (d->n_rot != 64 || d->swa != 128) return CKV_E_UNSUPPORTED;
+  if (d->head_dim < 64 || d->head_dim > kMaxD || d->head_dim % 32) return CKV_E_UNSUPPORTED;
+  if (d->n_heads % 16 || d->n_heads > 128) return CKV_E_UNSUPPORTED;
+  if (d->hidden % 64 || d->hidden > 65536) return CKV_E_UNSUPPORTED;
+  if (!fmt_ok(d->kv_fmt, true) || !fmt_ok(d->act_fmt, false) || !fmt_ok(d->w_fmt, false))
+    return CKV_E_UNSUPPORTED;
+  if (d->kv_fmt == CKV_E4M3 && d->head_dim <= d->n_rot) return CKV_E_UNSUPPORTED;
+  if (d->flags & ~(CKV_FLAG_NO_INV_ROPE | CKV_FLAG_IDX_NO_RELU)) return CKV_E_UNSUPPORTED;
+  if (d->ratio != 0) {
+    if (d->comp_cap <= 0) return CKV_E_INVAL;
+    if ((long long)d->comp_cap * d->ratio > (1ll << 30)) return CKV_E_UNSUPPORTED;
+  }
+  if (d->ratio == 4) {
+    if (!fmt_ok(d->idx_fmt, false)) return CKV_E_UNSUPPORTED;
+    if (d->idx_dim != 64 && d->idx_dim != 128) return CKV_E_UNSUPPORTED;
+    if (d->idx_heads < 1 || d->idx_heads > 64) return CKV_E_UNSUPPORTED;
+    if (d->top_k < 1 || d->top_k > 4096) return CKV_E_UNSUPPORTED;
+  }
+  return CKV_OK;
+}
+
+extern "C" const char* ckv_strerror(int code) {
+  switch (code) {
+    case CKV_OK: return "ok";
+    case CKV_E_INVAL: return "invalid argument (NULL pointer, bad size or misaligned pointer)";
+    case CKV_E_UNSUPPORTED: return "unsupported layer shape, format or ratio";
+    case CKV_E_CAPACITY: return "capacity exceeded (batch, chunk, compressed rows or stage)";
+    case CKV_E_WORKSPACE: return "workspace missing or too small";
+    case CKV_E_HIP: return "HIP kernel launch failed";
+    default: return "unknown error";
+  }
+}
+
+extern "C" size_t ckv_workspace_bytes(const ckv_layer_desc* d, int32_t mode, int32_t n) {
+  if (ckv_validate(d) != CKV_OK || n <= 0) return 0;
+  if (mode != CKV_MODE_DECODE && mode != CKV_MODE_PREFILL) return 0;
+  LayerParams P;
+  make_params(d, &P);
+  return ws_layout(P, mode, n).total;
+}

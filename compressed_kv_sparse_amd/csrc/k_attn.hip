@@ -1,0 +1,448 @@
+// Sliding-window + sparse compressed attention with shared K = V
+// ("ds4.c を読み解く (#3)", section 7: one online softmax over the raw window
+// rows and the selected compressed rows; vLLM DeepSeek V4 page: the same
+// vector is key and value, and the output tail is rotated back by -p).
+//
+// Row list of a query at p: raw positions max(0, p-swa+1) .. p, then
+//   ratio 4   : the top-k list (entries < 0 skipped, the list ends at the first
+//               entry >= V),
+//   ratio 128 : rows 0 .. V-1,
+//   ratio 0   : nothing.
+// The list is cut into splits; each block runs the online softmax over its
+// split and either finishes the output (one split) or leaves (max, sum,
+// unnormalised output) for the merge kernel.
+#include "ckv_device.h"
+
+namespace ckv {
+
+struct AttnQuery {
+  int seq, p, V, n_raw, n_list;
+};
+
+__device__ __forceinline__ AttnQuery attn_query(const LayerParams& P, const int32_t* pos, int seq_fixed,
+                                                int pos0, int qn) {
+  AttnQuery a;
+  a.seq = pos ? qn : seq_fixed;
+  a.p = pos ? pos[qn] : pos0 + qn;
+  if (a.p < 0) {
+    a.V = a.n_raw = a.n_list = 0;
+    return a;
+  }
+  a.V = P.ratio ? min((a.p + 1) / P.ratio, P.cap) : 0;
+  a.n_raw = min(P.swa, a.p + 1);
+  a.n_list = a.n_raw + (P.ratio == 4 ? P.topk : P.ratio == 128 ? a.V : 0);
+  return a;
+}
+
+// Pointer to list entry j's stored row, or NULL when the entry is skipped.
+__device__ __forceinline__ const uint8_t* attn_row(const LayerParams& P, const Cache& c, const AttnQuery& a,
+                                                   bool decode, int pos0, const int32_t* tk, int tk_end,
+                                                   int j) {
+  if (j < a.n_raw) {
+    const int t = a.p - a.n_raw + 1 + j;
+    if (decode) return c.raw + ((size_t)a.seq * P.swa + t % P.swa) * P.row_bytes;
+    return c.stage + (size_t)(t - pos0 + P.swa - 1) * P.row_bytes;
+  }
+  const int jj = j - a.n_raw;
+  int row;
+  if (P.ratio == 4) {
+    if (jj >= tk_end) return nullptr;
+    row = tk[jj];
+    if (row < 0) return nullptr;
+  } else {
+    row = jj;
+  }
+  return c.comp + ((size_t)a.seq * P.cap + row) * P.row_bytes;
+}
+
+// First index of the top-k list holding a row >= V (the list ends there).
+__device__ __forceinline__ int topk_end(const int32_t* tk, int k, int V, int* smem) {
+  if (threadIdx.x == 0) *smem = k;
+  __syncthreads();
+  for (int j = threadIdx.x; j < k; j += blockDim.x)
+    if (tk[j] >= V) atomicMin(smem, j);
+  __syncthreads();
+  return *smem;
+}
+
+// ----------------------------------------------------------------- MFMA
+// bf16 activations; rows bf16 or E4M3 (+ bf16 tail, fp32 scale).  Block of 4
+// waves, each owning 16 heads; grid (queries, splits, H / 64).  The K = V row
+// tile sits in LDS twice: row-major for the QK^T operand and channel-major for
+// the PV operand.  An E4M3 row enters the products exactly (codes are exact in
+// bf16); its scale multiplies the non-RoPE logit part and the non-RoPE
+// probability operand.
+template <int KVF, int D>
+__global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, const uint16_t* __restrict__ q,
+                                                   const int32_t* __restrict__ pos, int seq_fixed, int pos0,
+                                                   const int32_t* __restrict__ topk, int rows_per_split,
+                                                   int nsplit, float* __restrict__ part_o,
+                                                   float* __restrict__ part_ml, uint16_t* __restrict__ out) {
+  constexpr int R = 32;          // rows per tile
+  constexpr int KP = D + 8;      // K row stride (bf16 elements)
+  constexpr int VP = R + 8;      // Vt channel stride
+  constexpr int KS = D / 32;     // k-steps of QK^T
+  constexpr int NO = D / 16;     // output channel tiles
+  constexpr int DN = D - 64;     // non-RoPE channels
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[R * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16 * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps1[4][16 * VP];
+  __shared__ const uint8_t* rptr[R];
+  __shared__ float rsc[R];
+  __shared__ float cs_[32], sn_[32];
+  __shared__ int tk_lim;
+
+  const int qn = blockIdx.x, split = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int H = P.H;
+  const int h0 = blockIdx.z * 64 + wave * 16;
+  const bool decode = pos != nullptr;
+  const AttnQuery A = attn_query(P, pos, seq_fixed, pos0, qn);
+  const int j0 = split * rows_per_split;
+  const int j1 = min(A.n_list, j0 + rows_per_split);
+  const int32_t* tk = (P.ratio == 4 && topk) ? topk + (size_t)qn * P.topk : nullptr;
+  int tk_end = 0;
+  if (tk) tk_end = topk_end(tk, P.topk, A.V, &tk_lim);
+  if (tid < 32) rope_cs(P.base, 64, tid, (double)A.p, &cs_[tid], &sn_[tid]);
+  __syncthreads();
+
+  // rotated query of head h0 + r as the A operand, one bf16x8 per k-step
+  u32x4 Aq[KS];
+  {
+    const uint16_t* qr = q + ((size_t)qn * H + h0 + r) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c0 = 32 * ks + 8 * g;
+      u32x4 v = *(const u32x4*)(qr + c0);
+      if (c0 >= DN) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = bf16_to_f32(v[e] & 0xffffu), b = bf16_to_f32(v[e] >> 16);
+          const int jp = (c0 - DN) / 2 + e;
+          v[e] = pack_bf16x2(a * cs_[jp] - b * sn_[jp], a * sn_[jp] + b * cs_[jp]);
+        }
+      }
+      Aq[ks] = v;
+    }
+  }
+
+  float m_i[4], l_i[4];
+  f32x4 O[NO];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m_i[i] = -INFINITY;
+    l_i[i] = 0.f;
+  }
+#pragma unroll
+  for (int n = 0; n < NO; ++n) O[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const float scale = P.scale;
+
+  for (int jt = j0; jt < j1; jt += R) {
+    __syncthreads();
+    if (tid < R) {
+      const int j = jt + tid;
+      const uint8_t* rp = j < j1 ? attn_row(P, cc, A, decode, pos0, tk, tk_end, j) : nullptr;
+      rptr[tid] = rp;
+      float s = 0.f;
+      if (rp) s = KVF == CKV_E4M3 ? *(const float*)(rp + DN + 128) : 1.f;
+      rsc[tid] = rp ? s : -1.f;  // < 0 marks an empty slot
+    }
+    __syncthreads();
+    // stage: thread handles row pair (2*pr, 2*pr+1), 8 channels at 8*cc8
+    for (int it = tid; it < (R / 2) * (D / 8); it += 256) {
+      const int pr = it / (D / 8), c8 = it % (D / 8);
+      u32x4 v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint8_t* rp = rptr[2 * pr + h];
+        if (!rp) {
+          v[h] = (u32x4){0u, 0u, 0u, 0u};
+        } else if (KVF == CKV_BF16 || 8 * c8 >= DN) {
+          const uint8_t* src = KVF == CKV_BF16 ? rp + 16 * c8 : rp + DN + 16 * (c8 - DN / 8);
+          v[h] = *(const u32x4*)src;
+        } else {
+          const u32x2 cw = *(const u32x2*)(rp + 8 * c8);
+          u32x4 t;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+              const uint32_t b0 = (cw[e] >> (16 * f)) & 0xffu, b1 = (cw[e] >> (16 * f + 8)) & 0xffu;
+              t[2 * e + f] = (__float_as_uint(e4m3_to_f32(b0)) >> 16) |
+                             (__float_as_uint(e4m3_to_f32(b1)) & 0xffff0000u);
+            }
+          }
+          v[h] = t;
+        }
+        *(u32x4*)&Ks[(2 * pr + h) * KP + 8 * c8] = v[h];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (v[0][e] & 0xffffu) | (v[1][e] << 16);
+        const uint32_t hi = (v[0][e] >> 16) | (v[1][e] & 0xffff0000u);
+        *(uint32_t*)&Vt[(8 * c8 + 2 * e) * VP + 2 * pr] = lo;
+        *(uint32_t*)&Vt[(8 * c8 + 2 * e + 1) * VP + 2 * pr] = hi;
+      }
+    }
+    __syncthreads();
+
+    // logits for 2 row tiles of 16
+    float S[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 b = *(const u32x4*)&Ks[(16 * nt + r) * KP + 32 * ks + 8 * g];
+        if (32 * ks < DN) a1 = mfma16x16x32(as_bf16x8(Aq[ks]), as_bf16x8(b), a1);
+        else a2 = mfma16x16x32(as_bf16x8(Aq[ks]), as_bf16x8(b), a2);
+      }
+      const float rs = rsc[16 * nt + r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[nt][i] = rs < 0.f ? -INFINITY : (a1[i] * rs + a2[i]) * scale;
+    }
+    // online softmax per head 4g+i (rows spread over the 16 lanes of group g)
+    float alpha[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = fmaxf(S[0][i], S[1][i]);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const float mn = fmaxf(m_i[i], mx);
+      const bool none = mn == -INFINITY;
+      alpha[i] = none ? 1.f : __expf(m_i[i] - mn);
+      float ps = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float pv = none ? 0.f : __expf(S[nt][i] - mn);
+        S[nt][i] = pv;
+        ps += pv;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o, 64);
+      l_i[i] = l_i[i] * alpha[i] + ps;
+      m_i[i] = mn;
+    }
+#pragma unroll
+    for (int n = 0; n < NO; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[n][i] *= alpha[i];
+    // probabilities -> LDS as the A operand [16 heads][32 rows]
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float rs = rsc[16 * nt + r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Ps[wave][(4 * g + i) * VP + 16 * nt + r] = (uint16_t)f32_to_bf16(S[nt][i]);
+        if (KVF == CKV_E4M3) Ps1[wave][(4 * g + i) * VP + 16 * nt + r] = (uint16_t)f32_to_bf16(S[nt][i] * fmaxf(rs, 0.f));
+      }
+    }
+    __syncthreads();
+    const u32x4 ap = *(const u32x4*)&Ps[wave][r * VP + 8 * g];
+    const u32x4 ap1 = KVF == CKV_E4M3 ? *(const u32x4*)&Ps1[wave][r * VP + 8 * g] : ap;
+#pragma unroll
+    for (int n = 0; n < NO; ++n) {
+      const u32x4 b = *(const u32x4*)&Vt[(16 * n + r) * VP + 8 * g];
+      O[n] = mfma16x16x32(as_bf16x8(16 * n < DN ? ap1 : ap), as_bf16x8(b), O[n]);
+    }
+  }
+
+  if (nsplit == 1) {
+    // finish: normalise, rotate the tail back by -p, store bf16
+#pragma unroll
+    for (int n = 0; n < NO; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float inv = l_i[i] > 0.f ? 1.f / l_i[i] : 0.f;
+        float v = O[n][i] * inv;
+        const int ch = 16 * n + r;
+        if (ch >= DN && !(P.flags & CKV_FLAG_NO_INV_ROPE)) {
+          const float other = __shfl_xor(v, 1, 64);
+          const int jp = (ch - DN) >> 1;
+          // rotation by -p: (a, b) -> (a cos + b sin, -a sin + b cos)
+          v = (ch & 1) ? (-other * sn_[jp] + v * cs_[jp]) : (v * cs_[jp] + other * sn_[jp]);
+        }
+        out[((size_t)qn * H + h0 + 4 * g + i) * D + ch] = (uint16_t)f32_to_bf16(v);
+      }
+    }
+    return;
+  }
+  const size_t pb = ((size_t)qn * nsplit + split) * H;
+#pragma unroll
+  for (int n = 0; n < NO; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part_o[(pb + h0 + 4 * g + i) * D + 16 * n + r] = O[n][i];
+  if (r == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      part_ml[(pb + h0 + 4 * g + i) * 2] = m_i[i];
+      part_ml[(pb + h0 + 4 * g + i) * 2 + 1] = l_i[i];
+    }
+  }
+}
+
+// ----------------------------------------------------------------- vector
+// Any formats.  Block of 256 = 16 heads x 16 lanes; lane `sub` owns channels
+// [sub*dpt, (sub+1)*dpt).  grid (queries, splits, H / 16).
+template <int KVF, int ACTF>
+__global__ __launch_bounds__(256) void k_attn_vec(LayerParams P, Cache cc, const void* __restrict__ q,
+                                                  const int32_t* __restrict__ pos, int seq_fixed, int pos0,
+                                                  const int32_t* __restrict__ topk, int rows_per_split,
+                                                  int nsplit, float* __restrict__ part_o,
+                                                  float* __restrict__ part_ml) {
+  __shared__ int tk_lim;
+  const int qn = blockIdx.x, split = blockIdx.y;
+  const int tid = threadIdx.x, hl = tid >> 4, sub = tid & 15;
+  const int d = P.d, H = P.H, h = blockIdx.z * 16 + hl;
+  const int dpt = d / 16, dn = d - P.n_rot;
+  const bool decode = pos != nullptr;
+  const AttnQuery A = attn_query(P, pos, seq_fixed, pos0, qn);
+  const int j0 = split * rows_per_split, j1 = min(A.n_list, j0 + rows_per_split);
+  const int32_t* tk = (P.ratio == 4 && topk) ? topk + (size_t)qn * P.topk : nullptr;
+  int tk_end = 0;
+  if (tk) tk_end = topk_end(tk, P.topk, A.V, &tk_lim);
+
+  float qv[32], acc[32];
+  const int c0 = sub * dpt;
+  for (int e = 0; e < dpt; e += 2) {
+    const size_t o = ((size_t)qn * H + h) * d + c0 + e;
+    float a = load_val<ACTF>(q, o), b = load_val<ACTF>(q, o + 1);
+    if (c0 + e >= dn) {
+      float cs, sn;
+      rope_cs(P.base, P.n_rot, (c0 + e - dn) / 2, (double)A.p, &cs, &sn);
+      const float x = a * cs - b * sn, y = a * sn + b * cs;
+      a = x;
+      b = y;
+    }
+    qv[e] = a * P.scale;
+    qv[e + 1] = b * P.scale;
+    acc[e] = acc[e + 1] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int j = j0; j < j1; ++j) {
+    const uint8_t* rp = attn_row(P, cc, A, decode, pos0, tk, tk_end, j);
+    if (!rp) continue;
+    float rv[32];
+    float dot = 0.f;
+    for (int e = 0; e < dpt; ++e) {
+      const int ch = c0 + e;
+      float v;
+      if (KVF == CKV_F32) v = ((const float*)rp)[ch];
+      else if (KVF == CKV_BF16) v = bf16_to_f32(((const uint16_t*)rp)[ch]);
+      else v = ch < dn ? e4m3_to_f32(rp[ch]) * *(const float*)(rp + dn + 2 * P.n_rot)
+                       : bf16_to_f32(((const uint16_t*)(rp + dn))[ch - dn]);
+      rv[e] = v;
+      dot += qv[e] * v;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) dot += __shfl_xor(dot, o, 64);
+    const float mn = fmaxf(m, dot);
+    const float f = __expf(m - mn), pw = __expf(dot - mn);
+    l = l * f + pw;
+    for (int e = 0; e < dpt; ++e) acc[e] = acc[e] * f + pw * rv[e];
+    m = mn;
+  }
+  const size_t pb = ((size_t)qn * nsplit + split) * H + h;
+  for (int e = 0; e < dpt; ++e) part_o[pb * d + c0 + e] = acc[e];
+  if (sub == 0) {
+    part_ml[pb * 2] = m;
+    part_ml[pb * 2 + 1] = l;
+  }
+}
+
+// ----------------------------------------------------------------- merge
+// grid (queries, H); block d/2 threads, each two adjacent channels.
+template <int ACTF>
+__global__ __launch_bounds__(256) void k_attn_merge(LayerParams P, const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml,
+                                                    const int32_t* __restrict__ pos, int pos0, int nsplit,
+                                                    void* __restrict__ out) {
+  const int qn = blockIdx.x, h = blockIdx.y, H = P.H, d = P.d;
+  const int c = 2 * threadIdx.x;
+  if (c >= d) return;
+  const int p = pos ? pos[qn] : pos0 + qn;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) {
+    const size_t b = ((size_t)qn * nsplit + s) * H + h;
+    if (part_ml[b * 2 + 1] > 0.f) M = fmaxf(M, part_ml[b * 2]);
+  }
+  float L = 0.f, a = 0.f, bb = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const size_t b = ((size_t)qn * nsplit + s) * H + h;
+    const float l = part_ml[b * 2 + 1];
+    if (!(l > 0.f)) continue;
+    const float wgt = __expf(part_ml[b * 2] - M);
+    L += l * wgt;
+    a += part_o[b * d + c] * wgt;
+    bb += part_o[b * d + c + 1] * wgt;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  a *= inv;
+  bb *= inv;
+  const int dn = d - P.n_rot;
+  if (c >= dn && !(P.flags & CKV_FLAG_NO_INV_ROPE) && p >= 0) {
+    float cs, sn;
+    rope_cs(P.base, P.n_rot, (c - dn) / 2, (double)p, &cs, &sn);
+    const float x = a * cs + bb * sn, y = -a * sn + bb * cs;
+    a = x;
+    bb = y;
+  }
+  const size_t o = ((size_t)qn * H + h) * d + c;
+  store_val<ACTF>(out, o, a);
+  store_val<ACTF>(out, o + 1, bb);
+}
+
+// ----------------------------------------------------------------- launcher
+
+int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32_t* pos, int seq,
+                int pos0, int nq, const int32_t* topk, void* out, const WsLayout& L, uint8_t* ws,
+                void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  float* po = (float*)(ws + L.part_o);
+  float* pml = (float*)(ws + L.part_ml);
+  const int ns = L.attn_splits, rps = L.attn_rows_per_split;
+  const bool mf = P.act_fmt == CKV_BF16 && P.kv_fmt != CKV_F32 && P.H % 64 == 0 &&
+                  (P.d == 512 || P.d == 128) && P.n_rot == 64;
+  if (mf) {
+    dim3 grid(nq, ns, P.H / 64);
+    const uint16_t* qq = (const uint16_t*)q;
+    uint16_t* oo = (uint16_t*)out;
+#define CKV_AM(KF, DD)                                                                              \
+  hipLaunchKernelGGL((k_attn_mfma<KF, DD>), grid, dim3(256), 0, st, P, c, qq, pos, seq, pos0, topk, rps, \
+                     ns, po, pml, oo)
+    if (P.kv_fmt == CKV_BF16) {
+      if (P.d == 512) CKV_AM(CKV_BF16, 512);
+      else CKV_AM(CKV_BF16, 128);
+    } else {
+      if (P.d == 512) CKV_AM(CKV_E4M3, 512);
+      else CKV_AM(CKV_E4M3, 128);
+    }
+#undef CKV_AM
+    if (ns == 1) return (int)hipGetLastError();
+  } else {
+    dim3 grid(nq, ns, P.H / 16);
+#define CKV_AV(KF, AF)                                                                                  \
+  hipLaunchKernelGGL((k_attn_vec<KF, AF>), grid, dim3(256), 0, st, P, c, q, pos, seq, pos0, topk, rps, ns, \
+                     po, pml)
+    if (P.act_fmt == CKV_F32) {
+      if (P.kv_fmt == CKV_F32) CKV_AV(CKV_F32, CKV_F32);
+      else if (P.kv_fmt == CKV_BF16) CKV_AV(CKV_BF16, CKV_F32);
+      else CKV_AV(CKV_E4M3, CKV_F32);
+    } else {
+      if (P.kv_fmt == CKV_F32) CKV_AV(CKV_F32, CKV_BF16);
+      else if (P.kv_fmt == CKV_BF16) CKV_AV(CKV_BF16, CKV_BF16);
+      else CKV_AV(CKV_E4M3, CKV_BF16);
+    }
+#undef CKV_AV
+  }
+  dim3 mg(nq, P.H);
+  if (P.act_fmt == CKV_F32)
+    hipLaunchKernelGGL(k_attn_merge<CKV_F32>, mg, dim3(P.d / 2), 0, st, P, po, pml, pos, pos0, ns, out);
+  else
+    hipLaunchKernelGGL(k_attn_merge<CKV_BF16>, mg, dim3(P.d / 2), 0, st, P, po, pml, pos, pos0, ns, out);
+  return (int)hipGetLastError();
+}
+
+}  // namespace ckv

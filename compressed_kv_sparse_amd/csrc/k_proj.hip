@@ -1,0 +1,136 @@
+// Compressor projections kappa = W_kv x, sigma = W_gate x (and the indexer
+// lane's pair on ratio-4 layers) -- steps 1-2 of the per-token compressor of
+// "ds4.c を読み解く (#3)", section 4.
+//
+// The four weight matrices are treated as one [ncol, hidden] matrix whose row
+// blocks are wkv | wgate | idx_wkv | idx_wgate.  The result goes to
+// part[split][m][col] in fp32; split-K partials are summed, in split order, by
+// the compress kernels that consume them.
+#include "ckv_device.h"
+
+namespace ckv {
+
+struct WCat {
+  const void* p[4];
+  int start[5];  // column ranges of the four blocks
+};
+
+__device__ __forceinline__ const void* wcat_row(const WCat& wc, int col, int K, int esz,
+                                                int* local) {
+  int s = 0;
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if (col >= wc.start[i]) s = i;
+  *local = col - wc.start[s];
+  return (const char*)wc.p[s] + (size_t)(*local) * K * esz;
+}
+
+// bf16 activations x bf16 weights on MFMA.  One wave computes a 32 x 16 tile
+// (two 16-row blocks of x against 16 weight rows) over one K range.
+// grid: x = ncol / 64 (4 waves of 16 columns), y = splits, z = ceil(M / 32).
+__global__ __launch_bounds__(256) void k_proj_mfma(const uint16_t* __restrict__ X, int M, int K,
+                                                   WCat wc, int ncol, int klen,
+                                                   float* __restrict__ part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col0 = blockIdx.x * 64 + wave * 16;
+  if (col0 >= ncol) return;
+  const int m0 = blockIdx.z * 32;
+  const int k0 = blockIdx.y * klen, k1 = min(K, k0 + klen);
+  const int r = lane & 15, g = lane >> 4;
+
+  int local;
+  const uint16_t* wrow = (const uint16_t*)wcat_row(wc, col0 + r, K, 2, &local);
+  const bool ok0 = (m0 + r) < M, ok1 = (m0 + 16 + r) < M;
+  const uint16_t* x0 = X + (size_t)(ok0 ? m0 + r : 0) * K;
+  const uint16_t* x1 = X + (size_t)(ok1 ? m0 + 16 + r : 0) * K;
+
+  f32x4 c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0};
+  const u32x4 zero = {0, 0, 0, 0};
+  int k = k0;
+  for (; k + 128 <= k1; k += 128) {
+    u32x4 a0[4], a1[4], b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kk = k + 32 * s + 8 * g;
+      b[s] = *(const u32x4*)(wrow + kk);
+      a0[s] = ok0 ? *(const u32x4*)(x0 + kk) : zero;
+      a1[s] = ok1 ? *(const u32x4*)(x1 + kk) : zero;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      c0 = mfma16x16x32(as_bf16x8(a0[s]), as_bf16x8(b[s]), c0);
+      c1 = mfma16x16x32(as_bf16x8(a1[s]), as_bf16x8(b[s]), c1);
+    }
+  }
+  for (; k < k1; k += 32) {
+    const int kk = k + 8 * g;
+    const u32x4 b = *(const u32x4*)(wrow + kk);
+    const u32x4 a0 = ok0 ? *(const u32x4*)(x0 + kk) : zero;
+    const u32x4 a1 = ok1 ? *(const u32x4*)(x1 + kk) : zero;
+    c0 = mfma16x16x32(as_bf16x8(a0), as_bf16x8(b), c0);
+    c1 = mfma16x16x32(as_bf16x8(a1), as_bf16x8(b), c1);
+  }
+  float* out = part + (size_t)blockIdx.y * M * ncol;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ma = m0 + 4 * g + i, mb = m0 + 16 + 4 * g + i;
+    if (ma < M) out[(size_t)ma * ncol + col0 + r] = c0[i];
+    if (mb < M) out[(size_t)mb * ncol + col0 + r] = c1[i];
+  }
+}
+
+// Any formats, vector ALU: one wave per (column, 4 rows), lanes stride K.
+// grid: x = ncol, y = ceil(M / 4).  Writes split 0.
+template <int XF, int WF>
+__global__ __launch_bounds__(64) void k_proj_vec(const void* __restrict__ X, int M, int K, WCat wc,
+                                                 int ncol, float* __restrict__ part) {
+  const int col = blockIdx.x, m0 = blockIdx.y * 4, lane = threadIdx.x;
+  int local;
+  const void* wrow = wcat_row(wc, col, K, WF == CKV_F32 ? 4 : 2, &local);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = lane; k < K; k += 64) {
+    const float wv = load_val<WF>(wrow, k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (m0 + i < M) acc[i] += wv * load_val<XF>(X, (long)(m0 + i) * K + k);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float s = wave_sum(acc[i]);
+    if (lane == 0 && m0 + i < M) part[(size_t)(m0 + i) * ncol + col] = s;
+  }
+}
+
+int launch_proj(const LayerParams& P, const Weights& w, const void* x, int M, float* part,
+                int splits, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  WCat wc;
+  wc.p[0] = w.wkv;
+  wc.p[1] = w.wgate;
+  wc.p[2] = w.idx_wkv;
+  wc.p[3] = w.idx_wgate;
+  wc.start[0] = 0;
+  wc.start[1] = P.d;
+  wc.start[2] = 2 * P.d;
+  wc.start[3] = P.ratio == 4 ? 2 * P.d + P.DI : 1 << 30;
+  wc.start[4] = P.ncol;
+  if (P.ratio != 4) wc.start[2] = wc.start[3] = 1 << 30;
+  const int K = P.hidden;
+  if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16) {
+    const int klen = ((K / splits) + 31) / 32 * 32;
+    dim3 grid((P.ncol + 63) / 64, splits, (M + 31) / 32);
+    hipLaunchKernelGGL(k_proj_mfma, grid, dim3(256), 0, st, (const uint16_t*)x, M, K, wc, P.ncol,
+                       klen, part);
+  } else {
+    dim3 grid(P.ncol, (M + 3) / 4);
+#define CKV_PV(XF, WF)                                                                     \
+  hipLaunchKernelGGL((k_proj_vec<XF, WF>), grid, dim3(64), 0, st, x, M, K, wc, P.ncol, part)
+    if (P.act_fmt == CKV_F32 && P.w_fmt == CKV_F32) CKV_PV(CKV_F32, CKV_F32);
+    else if (P.act_fmt == CKV_F32) CKV_PV(CKV_F32, CKV_BF16);
+    else CKV_PV(CKV_BF16, CKV_F32);
+#undef CKV_PV
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace ckv

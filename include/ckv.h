@@ -1,0 +1,263 @@
+/*
+ * ckv.h -- C ABI of the MI355X compressed-KV sparse attention library (libckv.so).
+ *
+ * One attention layer of the DeepSeek-V4 design described in
+ *   [P1] "【#3】ds4.c を読み解く" (compressor s4-s5, indexer s6, mixed attention
+ *        s7, tail-only RoPE s8, FP8 cache s9, prefill chunks s3), and
+ *   [P4] "vLLM DeepSeek V4 サポート" (shared K=V with inverse RoPE, c4a / c128a,
+ *        DSA top-k, sliding window of 128, fused cache insertion).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer is a DEVICE pointer unless its comment says "host".
+ * - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *   Every call only enqueues work on that stream and returns; nothing
+ *   synchronises.  The caller keeps every buffer alive until that work ends.
+ * - The caller owns every buffer.  The library allocates no device memory,
+ *   keeps no pointer after a call returns and has no mutable global state, so
+ *   calls on different streams over disjoint caches may overlap.
+ * - Errors: each call returns CKV_OK (0) or a negative CKV_E_* code.  All
+ *   argument, shape, capacity and workspace checks run on the host BEFORE any
+ *   work is enqueued, so a failed call leaves every buffer untouched.
+ *   Conditions only the device can see (a per-sequence position beyond the
+ *   cache capacity, a negative position) skip that sequence and OR a bit into
+ *   cache->status[b] (when status is non-NULL); the caller reads it at its own
+ *   synchronisation point.  No call aborts, prints or throws.
+ * - A layer is described by ckv_layer_desc; ckv_validate() checks it.  The
+ *   compiled kernels support: ratio 0, 4 or 128; n_rot 64; swa 128;
+ *   head_dim 128 or 512 (a multiple of 64, at most 512); idx_dim 64 or 128;
+ *   n_heads a multiple of 16, at most 128; idx_heads 1..64; top_k 1..2048;
+ *   hidden a multiple of 64.
+ *
+ * Stored row formats (one K=V row of head_dim channels)
+ * -----------------------------------------------------
+ *   CKV_F32  : head_dim float32                          (4*head_dim bytes)
+ *   CKV_BF16 : head_dim bfloat16                         (2*head_dim bytes)
+ *   CKV_E4M3 : head_dim-n_rot OCP E4M3FN codes of z_c/s, then the n_rot RoPE
+ *              channels as bfloat16, then the float32 row scale
+ *              s = max|z_c|/448 over the non-RoPE channels (1 if all zero),
+ *              padded to a multiple of 128 bytes (640 bytes at head_dim 512).
+ *              The FP8 round trip covers the non-RoPE part only [P1 s9].
+ * ckv_row_bytes() returns the size.  Indexer rows are idx_dim values in
+ * idx_fmt (F32 or BF16).
+ */
+#ifndef CKV_H
+#define CKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------ */
+#define CKV_OK 0
+#define CKV_E_INVAL (-1)       /* NULL pointer, bad size, misaligned pointer   */
+#define CKV_E_UNSUPPORTED (-2) /* shape / format / ratio not built, or indexer on r != 4 */
+#define CKV_E_CAPACITY (-3)    /* B > batch, T > chunk cap, rows beyond comp_cap, stage too small */
+#define CKV_E_WORKSPACE (-4)   /* ws NULL or ws_bytes < ckv_workspace_bytes()  */
+#define CKV_E_HIP (-5)         /* a kernel launch failed                       */
+
+/* ---- cache->status bits (device-detected, sticky) ------------------------ */
+#define CKV_STATUS_BAD_POS 1u   /* pos < 0                                      */
+#define CKV_STATUS_CAPACITY 2u  /* the row a token closes lies beyond comp_cap  */
+
+/* ---- formats -------------------------------------------------------------- */
+#define CKV_F32 0
+#define CKV_BF16 1
+#define CKV_E4M3 2
+
+/* ---- desc.flags ------------------------------------------------------------ */
+#define CKV_FLAG_NO_INV_ROPE 1u  /* skip the inverse RoPE on the output [P4]   */
+#define CKV_FLAG_IDX_NO_RELU 2u  /* indexer sums raw dots instead of relu(dots) */
+
+/* ---- modes for ckv_workspace_bytes ---------------------------------------- */
+#define CKV_MODE_DECODE 0
+#define CKV_MODE_PREFILL 1
+
+/* Largest chunk one prefill call accepts [P1 s3: prompts are prefilled in
+ * chunks of at most 4096 tokens]. */
+#define CKV_MAX_CHUNK 4096
+
+/* Layer description (host memory).
+ *   ratio       0 (sliding window only), 4 (c4a: rows pool 8 tokens at stride
+ *               4, with indexer) or 128 (c128a: 128 tokens at stride 128, every
+ *               visible row attended) [P4 "KV Cache Compression"; P1 s1]
+ *   hidden      D, width of the compressor input x
+ *   head_dim    d, width of q, of the shared K=V rows and of the output
+ *   n_rot       RoPE channels at the end of each head (64) [P1 s8]
+ *   n_heads     H query heads sharing one K=V head [P4]
+ *   swa         raw sliding-window rows (128) [P1 s2; P4]
+ *   idx_heads, idx_dim, top_k   indexer shape (ratio 4 only) [P1 s6]
+ *   comp_cap    compressed rows per sequence the cache holds
+ *   batch       sequences the cache holds
+ *   kv_fmt      CKV_F32 / CKV_BF16 / CKV_E4M3 for raw and compressed rows
+ *   idx_fmt     CKV_F32 / CKV_BF16 for indexer rows
+ *   act_fmt     CKV_F32 / CKV_BF16 for x, u, q, qI and out
+ *   w_fmt       CKV_F32 / CKV_BF16 for wkv / wgate / idx_wkv / idx_wgate
+ *   rope_base   the layer's RoPE base; one base serves the query, raw rows,
+ *               compressed rows and indexer of the layer [P1 s8]
+ *   norm_eps    RMSNorm epsilon of the compressor [P1 s4 step 6]
+ *   softmax_scale  logit scale; 0 means 1/sqrt(head_dim)
+ *   flags       CKV_FLAG_* */
+typedef struct ckv_layer_desc {
+  int32_t ratio;
+  int32_t hidden;
+  int32_t head_dim;
+  int32_t n_rot;
+  int32_t n_heads;
+  int32_t swa;
+  int32_t idx_heads;
+  int32_t idx_dim;
+  int32_t top_k;
+  int32_t comp_cap;
+  int32_t batch;
+  int32_t kv_fmt;
+  int32_t idx_fmt;
+  int32_t act_fmt;
+  int32_t w_fmt;
+  uint32_t flags;
+  double rope_base;
+  float norm_eps;
+  float softmax_scale;
+} ckv_layer_desc;
+
+/* Compressor weights (device pointers, read only).
+ *   wkv, wgate          [head_dim, hidden] row-major, w_fmt   [P1 s4 steps 1-2]
+ *   ape                 [W, head_dim] float32, W = 8 (r=4) / 128 (r=128): the
+ *                       learned position bias added to the score of window slot j
+ *   gamma               [head_dim] float32 RMSNorm weight
+ *   idx_wkv, idx_wgate  [idx_dim, hidden] (ratio 4 only)   [P1 s6]
+ *   idx_ape             [8, idx_dim] float32
+ *   idx_gamma           [idx_dim] float32 */
+typedef struct ckv_layer_weights {
+  const void* wkv;
+  const void* wgate;
+  const float* ape;
+  const float* gamma;
+  const void* idx_wkv;
+  const void* idx_wgate;
+  const float* idx_ape;
+  const float* idx_gamma;
+} ckv_layer_weights;
+
+/* Per-layer cache (device pointers; the struct itself is host memory).
+ *   raw        [batch, swa, row_bytes]      raw rows, token t in slot t % swa,
+ *                                           stored RoPE'd at t      [P1 s2, s7]
+ *   comp       [batch, comp_cap, row_bytes] compressed row i at index i
+ *   idx        [batch, comp_cap, idx_dim]   indexer rows (ratio 4)
+ *   st_kv, st_sc   [batch, W, head_dim] float32: compressor window state,
+ *                  token t's (kappa, sigma) in slot t % W          [P1 s5; P4]
+ *   ist_kv, ist_sc [batch, 8, idx_dim] float32: indexer compressor state
+ *   raw_stage  [stage_rows, row_bytes]: prefill staging of the raw rows of
+ *              positions pos0-swa+1 .. pos0+T-1 (stage_rows >= T + swa - 1)
+ *   status     [batch] uint32 sticky device error bits, or NULL
+ * Pointers a layer does not use (comp/state for ratio 0, idx/ist_* unless
+ * ratio 4, raw_stage for decode) may be NULL. */
+typedef struct ckv_layer_cache {
+  void* raw;
+  void* comp;
+  void* idx;
+  float* st_kv;
+  float* st_sc;
+  float* ist_kv;
+  float* ist_sc;
+  void* raw_stage;
+  int32_t stage_rows;
+  uint32_t* status;
+} ckv_layer_cache;
+
+/* ---- utilities (host only, never touch the GPU) --------------------------- */
+
+/* Bytes of one stored K=V row in format fmt; 0 for an unknown format. */
+size_t ckv_row_bytes(int32_t fmt, int32_t head_dim, int32_t n_rot);
+
+/* Fail-fast check of a layer description against what the library is built
+ * for [P1 s1: the engine refuses a layout it was not built for rather than
+ * guessing].  Returns CKV_OK, CKV_E_INVAL or CKV_E_UNSUPPORTED. */
+int ckv_validate(const ckv_layer_desc* desc);
+
+/* Static string for a return code. */
+const char* ckv_strerror(int code);
+
+/* Workspace bytes a call of `mode` with n = B (decode) or T (prefill) tokens
+ * needs; the same figure serves all three entry points of that mode.
+ * 0 when desc is invalid. */
+size_t ckv_workspace_bytes(const ckv_layer_desc* desc, int32_t mode, int32_t n);
+
+/* ---- compress_append: compressor + cache insertion [P1 s4-s5, s8-s9; P4 fused
+ * compressor + RMSNorm + RoPE + cache insertion] ----------------------------
+ *
+ * Decode: one token per sequence b < B at position pos[b] (device int32).
+ *   - kappa = wkv.x, sigma = wgate.x (and the indexer lane on ratio 4) are
+ *     stored in state slot pos % W;
+ *   - u[b] is RoPE'd at pos (tail only) and stored in raw slot pos % swa;
+ *   - when (pos+1) % ratio == 0 the window of row i = (pos+1)/ratio - 1
+ *     (tokens 4i-4..4i+3 for c4a, 128i..128i+127 for c128a) is pooled per
+ *     channel with softmax(sigma + ape[slot]), RMS-normalised, RoPE'd at i*ratio
+ *     and stored as comp row i (and idx row i).
+ * x [B, hidden] act_fmt, u [B, head_dim] act_fmt.
+ * ratio 0 stores the raw row only (weights may be NULL).
+ * Re-running a step at the same positions rewrites identical values. */
+int ckv_compress_append_decode(const ckv_layer_desc* desc, const ckv_layer_weights* w,
+                               const ckv_layer_cache* cache, const void* x, const void* u,
+                               const int32_t* pos, int32_t B, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Prefill: tokens pos0 .. pos0+T-1 of sequence `seq` (host ints), 1 <= T <=
+ * CKV_MAX_CHUNK; x [T, hidden], u [T, head_dim].  Equivalent to T decode
+ * steps; compressor windows that straddle pos0 take their earlier tokens from
+ * the state, so boundaries stay at absolute positions [P1 s3].  Also fills
+ * cache->raw_stage with the raw rows of pos0-swa+1 .. pos0+T-1 (stage row
+ * t - pos0 + swa - 1) for the prefill attention, then refreshes the raw ring. */
+int ckv_compress_append_prefill(const ckv_layer_desc* desc, const ckv_layer_weights* w,
+                                const ckv_layer_cache* cache, const void* x, const void* u,
+                                int32_t seq, int32_t pos0, int32_t T, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* ---- indexer_topk: score every visible compressed row, keep the top k
+ * [P1 s6; P4 DSA] (ratio 4 only, else CKV_E_UNSUPPORTED) ------------------------
+ *
+ * For query position p, V = (p+1)/4 rows are visible.  The indexer query
+ * qI[h] is RoPE'd at p (tail) and cast to idx_fmt; row s scores
+ * I(s) = sum_h w[h] * relu(qI[h] . idx[s]).  topk[0..k) receives the k best
+ * rows (ties to the lower index) in ascending index order, -1 padded; when
+ * V <= k it receives 0..V-1 then -1s.
+ * Decode: qI [B, idx_heads, idx_dim] act_fmt, w [B, idx_heads] float32,
+ *         pos [B] device, topk [B, top_k] int32.
+ * Prefill: qI [T, ...], w [T, ...], topk [T, top_k] for queries pos0..pos0+T-1
+ *         of sequence seq (run after compress_append_prefill of the chunk). */
+int ckv_indexer_topk_decode(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
+                            const void* qI, const float* w, const int32_t* pos, int32_t B,
+                            int32_t* topk, void* ws, size_t ws_bytes, void* stream);
+int ckv_indexer_topk_prefill(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
+                             const void* qI, const float* w, int32_t seq, int32_t pos0, int32_t T,
+                             int32_t* topk, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- sparse_swa_attn: one softmax over the raw window and the compressed rows,
+ * shared K=V, inverse RoPE on the output [P1 s7; P4] -------------------------
+ *
+ * For query p, head h: q[h] RoPE'd at p; rows = raw positions
+ * max(0, p-swa+1)..p, plus topk rows (ratio 4; entries < 0 skipped, entries
+ * >= V end the list) or rows 0..V-1 (ratio 128) or none (ratio 0);
+ * l_j = scale * q.row_j, o = sum_j softmax(l)_j row_j, then the output tail is
+ * rotated by -p, and o is cast to act_fmt.
+ * Decode: q [B, n_heads, head_dim], pos [B] device, topk [B, top_k] (ratio 4,
+ *         else NULL), out [B, n_heads, head_dim].
+ * Prefill: q [T, ...], topk [T, top_k] or NULL, out [T, ...] for queries
+ *         pos0..pos0+T-1 of sequence seq; reads cache->raw_stage written by
+ *         compress_append_prefill of the same chunk. */
+int ckv_sparse_swa_attn_decode(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
+                               const void* q, const int32_t* pos, const int32_t* topk, int32_t B,
+                               void* out, void* ws, size_t ws_bytes, void* stream);
+int ckv_sparse_swa_attn_prefill(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
+                                const void* q, int32_t seq, int32_t pos0, int32_t T,
+                                const int32_t* topk, void* out, void* ws, size_t ws_bytes,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CKV_H */

@@ -526,6 +526,41 @@ class OracleSequence:
         """Raw positions max(0, p-swa+1) .. p (P1 s7 window rule)."""
         return range(max(0, p + 1 - self.L.swa), p + 1)
 
+    def computed_rows(self, V: int):
+        """Indices < V of the rows whose window closes at a live token."""
+        r = self.L.ratio
+        return sorted({(t + 1) // r - 1 for t in self.u if (t + 1) % r == 0 and (t + 1) // r - 1 < V})
+
+    def idx_matrix(self, V: int) -> np.ndarray:
+        """Stored values of indexer rows 0..V-1 (drawn rows decoded in bulk,
+        computed rows from the history)."""
+        L = self.L
+        if V == 0:
+            return np.zeros((0, L.idx_dim))
+        if self.idx_vals is not None:
+            rows = decode_values(self.idx_vals[:V], L.idx_fmt)
+        else:
+            rows = np.zeros((V, L.idx_dim))
+        for i in self.computed_rows(V):
+            rows[i] = self.idx_row(i)[1]
+        return rows
+
+    def comp_matrix(self, idx: Sequence[int]) -> np.ndarray:
+        """Stored values of attention rows ``idx``."""
+        L = self.L
+        idx = np.asarray(idx, np.int64)
+        if len(idx) == 0:
+            return np.zeros((0, L.head_dim))
+        comp = set(self.computed_rows(int(idx.max()) + 1))
+        if self.comp_rec is not None:
+            rows = decode_rows(self.comp_rec[idx], L.kv_fmt, L.head_dim, L.n_rot)
+        else:
+            rows = np.zeros((len(idx), L.head_dim))
+        for n, i in enumerate(idx):
+            if int(i) in comp:
+                rows[n] = self.comp_row(int(i))[2]
+        return rows
+
     def index_scores(self, p: int, qI: np.ndarray, w: np.ndarray) -> np.ndarray:
         """Indexer scores of every visible row for query p.  The indexer query
         gets the tail RoPE at p and is cast to the indexer-cache format."""
@@ -533,25 +568,26 @@ class OracleSequence:
         V = self.visible_rows(p)
         qh = rope_tail(decode_values(qI, L.act_fmt), p, L.rope_base, min(L.n_rot, L.idx_dim))
         qh = cast_values(qh, L.idx_fmt)
-        rows = np.stack([self.idx_row(i)[1] for i in range(V)]) if V else np.zeros((0, L.idx_dim))
-        return indexer_scores(qh, np.asarray(w, F64), rows, relu=L.relu)
+        return indexer_scores(qh, np.asarray(w, F64), self.idx_matrix(V), relu=L.relu)
 
     def attend(self, p: int, q: np.ndarray, topk: Optional[np.ndarray]) -> np.ndarray:
         """Output o [H, d] (pre-cast) for query p over raw window + compressed set."""
         L = self.L
         rows = [self.raw_row(t)[2] for t in self.raw_window(p)]
         V = self.visible_rows(p)
+        sel = []
         if L.ratio == 4:
             for i in topk:
                 if i < 0:
                     continue
                 if i >= V:
                     break
-                rows.append(self.comp_row(int(i))[2])
+                sel.append(int(i))
         elif L.ratio == 128:
-            rows += [self.comp_row(i)[2] for i in range(V)]
+            sel = list(range(V))
+        allrows = np.concatenate([np.stack(rows), self.comp_matrix(sel)]) if sel else np.stack(rows)
         qh = rope_tail(decode_values(q, L.act_fmt), p, L.rope_base, L.n_rot)
-        o = attention(qh, np.stack(rows), L.scale)
+        o = attention(qh, allrows, L.scale)
         return rope_tail(o, -p, L.rope_base, L.n_rot)   # inverse RoPE (P4)
 
     def step(self, p: int, x, u, q, qI=None, w=None, topk_override=None) -> dict:

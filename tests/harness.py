@@ -1,0 +1,121 @@
+"""Shared test plumbing: upload seeded workloads to a DeviceLayer and build
+oracle sequences over the same bytes.  Test infrastructure only."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+from workloads import gen as G
+from workloads.configs import LayerShape
+
+BF16_TOL = (2e-2, 1e-3)   # (rtol, atol) for bf16 / fp32 outputs
+FP8_TOL = (5e-2, 1e-3)    # when the K=V cache is fp8
+
+
+def device_layer(cfg: LayerShape, weights, cache: G.CacheInit = None, max_chunk: int = 0, batch=None):
+    from compressed_kv_sparse_amd import DeviceLayer
+    dl = DeviceLayer(ratio=cfg.ratio, hidden=cfg.hidden, head_dim=cfg.head_dim, n_heads=cfg.n_heads,
+                     batch=cfg.batch if batch is None else batch, idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim,
+                     top_k=cfg.top_k, comp_cap=cfg.comp_cap, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt,
+                     act_fmt=cfg.act_fmt, w_fmt=cfg.w_fmt, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps,
+                     n_rot=cfg.n_rot, swa=cfg.swa, max_chunk=max_chunk)
+    if weights is not None:
+        dl.set_weights(wkv=weights.wkv, wgate=weights.wgate, ape=weights.ape, gamma=weights.gamma,
+                       idx_wkv=weights.idx_wkv, idx_wgate=weights.idx_wgate, idx_ape=weights.idx_ape,
+                       idx_gamma=weights.idx_gamma)
+    if cache is not None:
+        dl.load_cache(raw=cache.raw, comp=cache.comp, idx=cache.idx, st_kv=cache.st_kv, st_sc=cache.st_sc,
+                      ist_kv=cache.ist_kv, ist_sc=cache.ist_sc)
+    return dl
+
+
+def dev(a, device="cuda"):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def oracle_layer(cfg, weights):
+    return O.layer_from(cfg, weights)
+
+
+def oracle_seq_from_init(L, cache: G.CacheInit, b: int) -> O.OracleSequence:
+    """Oracle sequence b starting from the drawn cache (tokens before
+    first_live come from the drawn bytes)."""
+    return O.OracleSequence(
+        L, raw_rec=cache.raw[b], comp_rec=None if cache.comp is None else cache.comp[b],
+        idx_vals=None if cache.idx is None else cache.idx[b],
+        st_kv=None if cache.st_kv is None else cache.st_kv[b], st_sc=None if cache.st_sc is None else cache.st_sc[b],
+        ist_kv=None if cache.ist_kv is None else cache.ist_kv[b],
+        ist_sc=None if cache.ist_sc is None else cache.ist_sc[b], first_live=int(cache.first_live[b]))
+
+
+def oracle_seq_from_bytes(L, raw, comp, idx, live_from: int) -> O.OracleSequence:
+    """Oracle sequence that reads every row from the given stored bytes
+    (nothing is computed: no token is live before ``live_from``)."""
+    return O.OracleSequence(L, raw_rec=raw, comp_rec=comp, idx_vals=idx, first_live=live_from)
+
+
+def close(gpu, ref, tol, what=""):
+    """|g - o| <= atol + rtol |o| element-wise; returns (ok, max_abs, max_rel)."""
+    rtol, atol = tol
+    g = np.asarray(gpu, np.float64)
+    o = np.asarray(ref, np.float64)
+    err = np.abs(g - o)
+    ok = bool(np.all(err <= atol + rtol * np.abs(o)))
+    rel = float(np.max(err / np.maximum(np.abs(o), 1e-30))) if err.size else 0.0
+    return ok, float(err.max() if err.size else 0.0), rel
+
+
+def assert_close(gpu, ref, tol, what=""):
+    ok, ma, mr = close(gpu, ref, tol)
+    if not ok:
+        g = np.asarray(gpu, np.float64)
+        o = np.asarray(ref, np.float64)
+        bad = np.abs(g - o) > tol[1] + tol[0] * np.abs(o)
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} outside tol {tol}; max abs {ma:.3g}; "
+                             f"first {idx.tolist()} gpu {g[bad][:5]} ref {o[bad][:5]}")
+
+
+def e4m3_ordinal(c):
+    c = np.asarray(c).astype(np.int64)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def compare_rows(gpu_rec, ref_z, fmt, d, n_rot, what):
+    """Stored row(s) from the GPU vs the oracle's pre-cast values.  f32 / bf16:
+    tolerance on values.  e4m3: codes within one step of the oracle's own
+    encoding, tail within tolerance, scale within 1e-5."""
+    gpu_rec = np.asarray(gpu_rec, np.uint8)
+    ref_z = np.atleast_2d(np.asarray(ref_z, np.float64))
+    gpu_rec = gpu_rec.reshape(ref_z.shape[0], -1)
+    if fmt in ("f32", "bf16"):
+        assert_close(O.decode_rows(gpu_rec, fmt, d, n_rot), ref_z, BF16_TOL, what)
+        return
+    dn = d - n_rot
+    for n in range(ref_z.shape[0]):
+        rec, _ = O.encode_row(ref_z[n], "e4m3", d, n_rot)
+        dist = np.abs(e4m3_ordinal(gpu_rec[n, :dn]) - e4m3_ordinal(rec[:dn]))
+        assert dist.max() <= 1, f"{what} row {n}: fp8 code distance {dist.max()}"
+        gs = gpu_rec[n, dn + 2 * n_rot:dn + 2 * n_rot + 4].copy().view(np.float32)[0]
+        rs = rec[dn + 2 * n_rot:dn + 2 * n_rot + 4].copy().view(np.float32)[0]
+        assert abs(gs - rs) <= 1e-5 * abs(rs), f"{what} row {n}: scale {gs} vs {rs}"
+        gt = O.bf16_decode(gpu_rec[n, dn:dn + 2 * n_rot].copy().view(np.uint16))
+        assert_close(gt, ref_z[n, dn:], BF16_TOL, f"{what} row {n} tail")
+
+
+def topk_margin(scores: np.ndarray, k: int) -> float:
+    """Gap between the k-th and (k+1)-th largest score, relative to max|s|
+    (inf when every row is selected)."""
+    if len(scores) <= k:
+        return np.inf
+    s = np.sort(scores)[::-1]
+    return float((s[k - 1] - s[k]) / max(np.max(np.abs(s)), 1e-30))
+
+
+def sets_equal(gpu_topk: np.ndarray, ref_topk: np.ndarray) -> bool:
+    return np.array_equal(np.sort(gpu_topk), np.sort(ref_topk))

@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/ckv.h declares, and rejects bad arguments before any
+work is enqueued.  Every call here fails validation on the host, so no
+kernel is ever launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ckv = pytest.importorskip("compressed_kv_sparse_amd", reason="libckv.so not built")
+from compressed_kv_sparse_amd import _lib as L  # noqa: E402
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "ckv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ckv_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 10, names
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(L.EXPORTS) == names
+
+
+def desc(**kw):
+    base = dict(ratio=4, hidden=4096, head_dim=512, n_rot=64, n_heads=64, swa=128, idx_heads=64, idx_dim=128,
+                top_k=512, comp_cap=32768, batch=16, kv_fmt=L.CKV_E4M3, idx_fmt=L.CKV_BF16, act_fmt=L.CKV_BF16,
+                w_fmt=L.CKV_BF16, flags=0, rope_base=160000.0, norm_eps=1e-6, softmax_scale=0.0)
+    base.update(kw)
+    return L.LayerDesc(**base)
+
+
+def test_validate_accepts_the_workload_shapes():
+    assert L.validate(desc()) == 0
+    assert L.validate(desc(ratio=128, comp_cap=8192, kv_fmt=L.CKV_BF16)) == 0
+    assert L.validate(desc(ratio=0, comp_cap=0)) == 0
+    assert L.validate(desc(hidden=1024, head_dim=128, n_heads=16, idx_heads=4, idx_dim=64, top_k=32,
+                           comp_cap=256, batch=1, kv_fmt=0, idx_fmt=0, act_fmt=0, w_fmt=0)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ratio=3), L.CKV_E_UNSUPPORTED), (dict(n_rot=32), L.CKV_E_UNSUPPORTED),
+    (dict(swa=64), L.CKV_E_UNSUPPORTED), (dict(head_dim=1024), L.CKV_E_UNSUPPORTED),
+    (dict(head_dim=500), L.CKV_E_UNSUPPORTED), (dict(n_heads=24), L.CKV_E_UNSUPPORTED),
+    (dict(idx_dim=96), L.CKV_E_UNSUPPORTED), (dict(idx_heads=65), L.CKV_E_UNSUPPORTED),
+    (dict(top_k=0), L.CKV_E_UNSUPPORTED), (dict(kv_fmt=7), L.CKV_E_UNSUPPORTED),
+    (dict(act_fmt=L.CKV_E4M3), L.CKV_E_UNSUPPORTED), (dict(comp_cap=0), L.CKV_E_INVAL),
+    (dict(batch=0), L.CKV_E_INVAL), (dict(rope_base=0.0), L.CKV_E_INVAL),
+    (dict(flags=0x80), L.CKV_E_UNSUPPORTED), (dict(hidden=100), L.CKV_E_UNSUPPORTED),
+])
+def test_validate_rejects(kw, code):
+    assert L.validate(desc(**kw)) == code
+
+
+def test_row_bytes_and_workspace():
+    assert L.row_bytes(L.CKV_E4M3, 512) == 640
+    assert L.row_bytes(L.CKV_BF16, 512) == 1024
+    assert L.row_bytes(L.CKV_F32, 128) == 512
+    assert L.row_bytes(9, 128) == 0
+    d = desc()
+    ws = L.workspace_bytes(d, L.CKV_MODE_DECODE, 16)
+    assert ws >= 16 * 32768 * 4 + 16 * 4096 * 4   # keys + histogram
+    assert L.workspace_bytes(d, 7, 16) == 0
+    assert L.workspace_bytes(desc(ratio=9), L.CKV_MODE_DECODE, 16) == 0
+    assert L.strerror(L.CKV_E_CAPACITY).startswith("capacity")
+
+
+FAKE = 1 << 40          # aligned, never dereferenced: every call below fails first
+MIS = FAKE + 4          # misaligned
+
+
+def cache(**kw):
+    c = dict(raw=FAKE, comp=FAKE, idx=FAKE, st_kv=FAKE, st_sc=FAKE, ist_kv=FAKE, ist_sc=FAKE, raw_stage=FAKE,
+             stage_rows=4096 + 127, status=None)
+    c.update(kw)
+    return L.LayerCache(**c)
+
+
+def weights(**kw):
+    w = {n: FAKE for n in ("wkv", "wgate", "ape", "gamma", "idx_wkv", "idx_wgate", "idx_ape", "idx_gamma")}
+    w.update(kw)
+    return L.LayerWeights(**w)
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="fake device addresses are only passed where no GPU exists")
+def test_host_errors_before_any_enqueue():
+    d = desc()
+    ws = L.workspace_bytes(d, L.CKV_MODE_DECODE, 16)
+    c, w = cache(), weights()
+    # batch beyond the cache
+    assert L.compress_append_decode(d, w, c, FAKE, FAKE, FAKE, 17, FAKE, ws) == L.CKV_E_CAPACITY
+    assert L.compress_append_decode(d, w, c, FAKE, FAKE, FAKE, 0, FAKE, ws) == L.CKV_E_INVAL
+    # workspace too small / missing / misaligned
+    assert L.compress_append_decode(d, w, c, FAKE, FAKE, FAKE, 16, FAKE, ws - 1) == L.CKV_E_WORKSPACE
+    assert L.indexer_topk_decode(d, c, FAKE, FAKE, FAKE, 16, FAKE, None, ws) == L.CKV_E_WORKSPACE
+    assert L.indexer_topk_decode(d, c, FAKE, FAKE, FAKE, 16, FAKE, MIS, ws) == L.CKV_E_WORKSPACE
+    # NULL / misaligned pointers
+    assert L.compress_append_decode(d, w, c, None, FAKE, FAKE, 16, FAKE, ws) == L.CKV_E_INVAL
+    assert L.compress_append_decode(d, weights(ape=MIS), c, FAKE, FAKE, FAKE, 16, FAKE, ws) == L.CKV_E_INVAL
+    assert L.compress_append_decode(d, w, cache(comp=None), FAKE, FAKE, FAKE, 16, FAKE, ws) == L.CKV_E_INVAL
+    assert L.sparse_swa_attn_decode(d, c, FAKE, FAKE, None, 16, FAKE, FAKE, ws) == L.CKV_E_INVAL  # r=4 needs topk
+    assert L.sparse_swa_attn_decode(d, c, MIS, FAKE, FAKE, 16, FAKE, FAKE, ws) == L.CKV_E_INVAL
+    # indexer on a ratio-128 layer
+    d128 = desc(ratio=128, comp_cap=1024)
+    assert L.indexer_topk_decode(d128, c, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 1 << 30) == L.CKV_E_UNSUPPORTED
+    assert L.sparse_swa_attn_decode(d128, c, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 1 << 30) == L.CKV_E_INVAL
+    # prefill limits
+    wp = L.workspace_bytes(d, L.CKV_MODE_PREFILL, 4096)
+    assert L.compress_append_prefill(d, w, c, FAKE, FAKE, 0, 0, 4097, FAKE, 1 << 40) == L.CKV_E_CAPACITY
+    assert L.compress_append_prefill(d, w, c, FAKE, FAKE, 16, 0, 16, FAKE, wp) == L.CKV_E_CAPACITY
+    assert L.compress_append_prefill(d, w, c, FAKE, FAKE, 0, -1, 16, FAKE, wp) == L.CKV_E_INVAL
+    assert L.compress_append_prefill(d, w, c, FAKE, FAKE, 0, 4 * 32768 - 8, 16, FAKE, wp) == L.CKV_E_CAPACITY
+    assert L.compress_append_prefill(d, w, cache(stage_rows=100), FAKE, FAKE, 0, 0, 16, FAKE, wp) == L.CKV_E_CAPACITY
+    assert L.compress_append_prefill(d, w, cache(raw_stage=None), FAKE, FAKE, 0, 0, 16, FAKE, wp) == L.CKV_E_INVAL
+    assert L.indexer_topk_prefill(d, c, FAKE, FAKE, 0, 0, 5000, FAKE, FAKE, wp) == L.CKV_E_CAPACITY
+    assert L.sparse_swa_attn_prefill(d, c, FAKE, 0, 0, 16, FAKE, FAKE, FAKE, 16) == L.CKV_E_WORKSPACE
+    # invalid description
+    assert L.compress_append_decode(desc(ratio=5), w, c, FAKE, FAKE, FAKE, 1, FAKE, ws) == L.CKV_E_UNSUPPORTED
+    assert L.lib.ckv_validate(None) == L.CKV_E_INVAL

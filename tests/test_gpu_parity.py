@@ -1,0 +1,297 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Each stage is checked in isolation on identical bytes (the oracle reads the
+cache the GPU wrote, and is fed the GPU's own top-k list for the attention),
+and the chained runs (C1 from token 0) compare whole histories.  Bars:
+top-k sets bit-exact on tie-free inputs; rows and outputs within
+2e-2 rel + 1e-3 abs (5e-2 rel when the K=V cache is fp8); fp8 codes within one
+step of the oracle's encoding.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from harness import (BF16_TOL, FP8_TOL, assert_close, compare_rows, dev, device_layer, oracle_layer,
+                     oracle_seq_from_bytes, oracle_seq_from_init, sets_equal, topk_margin)
+from workloads import get_config, make_decode_inputs, make_layer_weights, make_prefill_inputs
+from workloads import gen as G
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+MARGIN = 1e-4   # tie-free rule: gap between k-th and (k+1)-th score > MARGIN * max|s|
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import compressed_kv_sparse_amd  # noqa: F401  (fails loudly if libckv.so is missing)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def cpu(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def out_values(t, fmt):
+    a = cpu(t)
+    return O.decode_values(a, fmt)
+
+
+def tie_free_queries(cfg, seqs, pos, qI, w, attempts=40):
+    """Redraw q^I / w of any query whose oracle score gap at the k boundary is
+    below MARGIN (same generator, sub-seed per query and attempt)."""
+    qI, w = qI.copy(), w.copy()
+    for b, seq in enumerate(seqs):
+        for a in range(attempts):
+            sc = seq.index_scores(int(pos[b]), qI[b], w[b])
+            if topk_margin(sc, cfg.top_k) > MARGIN:
+                break
+            nq, nw = G.draw_query_index(cfg, 1, sub=b, attempt=a + 1)
+            qI[b], w[b] = nq[0], nw[0]
+        else:
+            raise AssertionError(f"no tie-free indexer query for sequence {b}")
+    return qI, w
+
+
+def run_decode_stage_checks(cfg, inp, wts, tol):
+    """One decode step at full size: compressor, indexer and attention each
+    compared with the oracle on the bytes the GPU holds."""
+    B, d = cfg.batch, cfg.head_dim
+    log(f"[decode] {cfg.name} B={B} p={inp.pos[:4]}")
+    dl = device_layer(cfg, wts, inp.cache)
+    pos_d = dev(inp.pos)
+    x, u, q = dev(inp.x), dev(inp.u), dev(inp.q)
+    dl.compress_decode(x, u, pos_d)
+    torch.cuda.synchronize()
+    assert int(dl.status.abs().sum()) == 0
+    L = oracle_layer(cfg, wts)
+    raw_g = cpu(dl.raw)
+    comp_g = cpu(dl.comp) if dl.comp is not None else None
+    idx_g = cpu(dl.idx) if dl.idx is not None else None
+
+    # --- compressor + raw insertion vs the oracle run from the drawn state
+    for b in range(B):
+        p = int(inp.pos[b])
+        seq = oracle_seq_from_init(L, inp.cache, b)
+        seq.feed(p, inp.x[b][None], inp.u[b][None])
+        z, _, _ = seq.raw_row(p)
+        compare_rows(raw_g[b, p % cfg.swa], z, cfg.kv_fmt, d, cfg.n_rot, f"raw row b={b}")
+        if cfg.ratio and (p + 1) % cfg.ratio == 0:
+            i = (p + 1) // cfg.ratio - 1
+            compare_rows(comp_g[b, i], seq.comp_row(i)[0], cfg.kv_fmt, d, cfg.n_rot, f"comp row {i} b={b}")
+            if cfg.ratio == 4:
+                gi = O.decode_values(idx_g[b, i], cfg.idx_fmt)
+                assert_close(gi, seq.idx_row(i)[0], BF16_TOL, f"idx row {i} b={b}")
+        if cfg.ratio:
+            W = cfg.window
+            kap = seq.kap[p]
+            st = cpu(dl.st_kv)[b, p % W]
+            assert_close(st, kap, (1e-4, 1e-5), f"state kappa b={b}")
+
+    # --- indexer on the GPU's own cache bytes
+    topk_d = None
+    bseqs = [oracle_seq_from_bytes(L, raw_g[b], None if comp_g is None else comp_g[b],
+                                   None if idx_g is None else idx_g[b], int(inp.pos[b]) + 1) for b in range(B)]
+    if cfg.ratio == 4:
+        qI, w = tie_free_queries(cfg, bseqs, inp.pos, inp.qI, inp.w)
+        topk_d = torch.empty((B, cfg.top_k), dtype=torch.int32, device="cuda")
+        dl.indexer_decode(dev(qI), dev(w), pos_d, topk_d)
+        torch.cuda.synchronize()
+        tk = cpu(topk_d)
+        for b in range(B):
+            ref = O.topk_select(bseqs[b].index_scores(int(inp.pos[b]), qI[b], w[b]), cfg.top_k)
+            assert sets_equal(tk[b], ref), f"top-k set differs for sequence {b}"
+            n = int((tk[b] >= 0).sum())
+            assert np.all(tk[b][:n] == np.sort(tk[b][:n])) and np.all(tk[b][n:] == -1)
+    # --- attention with the GPU's top-k list
+    out = dl.new_out(B)
+    dl.attn_decode(q, pos_d, topk_d, out)
+    torch.cuda.synchronize()
+    og = out_values(out, cfg.act_fmt)
+    for b in range(B):
+        ref = bseqs[b].attend(int(inp.pos[b]), inp.q[b], None if topk_d is None else cpu(topk_d)[b])
+        assert_close(og[b], ref, tol, f"attention output b={b}")
+    return dl
+
+
+def test_c2_c4a_decode_full_size():
+    cfg = get_config("c2")
+    run_decode_stage_checks(cfg, make_decode_inputs(cfg), make_layer_weights(cfg), BF16_TOL)
+
+
+def test_c5_c4a_fp8_decode_full_size():
+    cfg = get_config("c5")
+    run_decode_stage_checks(cfg, make_decode_inputs(cfg), make_layer_weights(cfg), FP8_TOL)
+
+
+def test_c3_c128a_decode_full_size():
+    cfg = get_config("c3")
+    # force a few sequences onto a c128a boundary so the step emits a row
+    n = G.context_lengths(cfg)
+    n[:3] = (n[:3] // 128) * 128
+    inp = make_decode_inputs(cfg, n_ctx=n)
+    run_decode_stage_checks(cfg, inp, make_layer_weights(cfg), BF16_TOL)
+
+
+def test_c5_c128a_and_swa_layers_decode():
+    for name in ("c5_c128a", "c5_swa"):
+        cfg = get_config(name)
+        run_decode_stage_checks(cfg, make_decode_inputs(cfg), make_layer_weights(cfg), FP8_TOL)
+
+
+@pytest.mark.parametrize("ratio,fmt", [(4, "bf16"), (4, "e4m3"), (128, "bf16"), (0, "bf16")])
+def test_short_contexts_and_ragged_batch(ratio, fmt):
+    """Positions below the window and the top-k size (V <= k, raw window < 128,
+    row 0's empty slots), mixed per sequence."""
+    base = get_config("c2")
+    cfg = base.with_(ratio=ratio, batch=8, comp_cap={4: 512, 128: 64, 0: 0}[ratio], kv_fmt=fmt,
+                     idx_heads=8 if ratio == 4 else 0, idx_dim=128 if ratio == 4 else 0,
+                     top_k=64 if ratio == 4 else 0, seed=11, name=f"short_r{ratio}_{fmt}")
+    n = np.array([1, 4, 8, 100, 129, 260, 1024, 2047 if ratio != 128 else 8192], np.int64)
+    run_decode_stage_checks(cfg, make_decode_inputs(cfg, n_ctx=n), make_layer_weights(cfg),
+                            FP8_TOL if fmt == "e4m3" else BF16_TOL)
+
+
+def test_bad_position_sets_status_and_spares_others():
+    cfg = get_config("c2").with_(batch=4, comp_cap=64, top_k=16, seed=12, name="badpos")
+    inp = make_decode_inputs(cfg, n_ctx=np.array([20, 40, 60, 80]))
+    wts = make_layer_weights(cfg)
+    dl = device_layer(cfg, wts, inp.cache)
+    pos = inp.pos.copy()
+    pos[1] = -1            # invalid position
+    pos[2] = 64 * 4 + 3    # closes row 64: beyond comp_cap
+    raw_before = cpu(dl.raw).copy()
+    dl.compress_decode(dev(inp.x), dev(inp.u), dev(pos))
+    torch.cuda.synchronize()
+    st = cpu(dl.status)
+    assert st[0] == 0 and st[3] == 0
+    assert st[1] & 1 and st[2] & 2
+    raw_after = cpu(dl.raw)
+    np.testing.assert_array_equal(raw_after[1], raw_before[1])       # untouched
+    assert not np.array_equal(raw_after[0], raw_before[0])
+
+
+def test_c1_full_history_decode_chain():
+    """C1 from token 0: 1024 compress_append steps, then index + attend at 1023;
+    every stored row and the output compared with the oracle's history run."""
+    cfg = get_config("c1")
+    wts = make_layer_weights(cfg)
+    T = cfg.n_ctx
+    x, u, q, qI, w = G.make_token_stream(cfg, T)
+    dl = device_layer(cfg, wts)
+    L = oracle_layer(cfg, wts)
+    seq = O.OracleSequence(L)
+    seq.feed(0, x, u)
+    xd, ud = dev(x), dev(u)
+    for p in range(T):
+        dl.compress_decode(xd[p:p + 1], ud[p:p + 1], dev(np.array([p], np.int32)), B=1)
+    torch.cuda.synchronize()
+    log("[c1] compressed 1024 tokens")
+    comp_g, idx_g, raw_g = cpu(dl.comp)[0], cpu(dl.idx)[0], cpu(dl.raw)[0]
+    for i in range(T // 4):
+        compare_rows(comp_g[i], seq.comp_row(i)[0], "f32", cfg.head_dim, cfg.n_rot, f"comp row {i}")
+        assert_close(idx_g[i], seq.idx_row(i)[0], BF16_TOL, f"idx row {i}")
+    for t in range(T - 128, T):
+        compare_rows(raw_g[t % 128], seq.raw_row(t)[0], "f32", cfg.head_dim, cfg.n_rot, f"raw {t}")
+    p = T - 1
+    qI1, w1 = tie_free_queries(cfg, [seq], [p], qI[p:p + 1], w[p:p + 1])
+    pos_d = dev(np.array([p], np.int32))
+    topk_d = torch.empty((1, cfg.top_k), dtype=torch.int32, device="cuda")
+    dl.indexer_decode(dev(qI1), dev(w1), pos_d, topk_d, B=1)
+    out = dl.new_out(1)
+    dl.attn_decode(dev(q[p:p + 1]), pos_d, topk_d, out, B=1)
+    torch.cuda.synchronize()
+    ref = seq.query(p, q[p], qI1[0], w1[0])
+    assert sets_equal(cpu(topk_d)[0], ref["topk"])
+    assert_close(cpu(out)[0], ref["out_f64"], BF16_TOL, "c1 output")
+
+
+@pytest.mark.parametrize("chunks", [(1024,), (37, 1, 500, 486)])
+def test_c1_prefill_chunks_equal_sequential_decode(chunks):
+    """Chunked prefill from token 0 in chunks of varying size: stored rows and
+    every query's output against the oracle (prefill = sequential decode)."""
+    cfg = get_config("c1")
+    wts = make_layer_weights(cfg)
+    T = sum(chunks)
+    x, u, q, qI, w = G.make_token_stream(cfg, T)
+    L = oracle_layer(cfg, wts)
+    seq = O.OracleSequence(L)
+    seq.feed(0, x, u)
+    # tie-free per query: redraw q^I rows whose margin is too small
+    qI, w = qI.copy(), w.copy()
+    for p in range(T):
+        for a in range(40):
+            if topk_margin(seq.index_scores(p, qI[p], w[p]), cfg.top_k) > MARGIN:
+                break
+            nq, nw = G.draw_query_index(cfg, 1, sub=5000 + p, attempt=a + 1)
+            qI[p], w[p] = nq[0], nw[0]
+    dl = device_layer(cfg, wts, max_chunk=max(chunks))
+    outs, tks = [], []
+    p0 = 0
+    for c in chunks:
+        o, tk = dl.prefill(0, p0, dev(x[p0:p0 + c]), dev(u[p0:p0 + c]), dev(q[p0:p0 + c]), dev(qI[p0:p0 + c]),
+                           dev(w[p0:p0 + c]))
+        torch.cuda.synchronize()
+        outs.append(cpu(o))
+        tks.append(cpu(tk))
+        p0 += c
+    log(f"[c1 prefill] chunks {chunks} done")
+    outs, tks = np.concatenate(outs), np.concatenate(tks)
+    comp_g, idx_g = cpu(dl.comp)[0], cpu(dl.idx)[0]
+    for i in range(T // 4):
+        compare_rows(comp_g[i], seq.comp_row(i)[0], "f32", cfg.head_dim, cfg.n_rot, f"comp row {i}")
+        assert_close(idx_g[i], seq.idx_row(i)[0], BF16_TOL, f"idx row {i}")
+    st = cpu(dl.st_kv)[0]
+    for t in range(T - 8, T):
+        assert_close(st[t % 8], seq.kap[t], (1e-4, 1e-5), f"state {t}")
+    for p in range(T):
+        ref = seq.query(p, q[p], qI[p], w[p])
+        assert sets_equal(tks[p], ref["topk"]), f"top-k of query {p}"
+        assert_close(outs[p], ref["out_f64"], BF16_TOL, f"output of query {p}")
+
+
+def test_c4_prefill_chunk_sampled():
+    """4096-token chunk at 61440 (compressor windows straddle the chunk edge):
+    every emitted row, and sampled queries' top-k and outputs."""
+    cfg = get_config("c4")
+    wts = make_layer_weights(cfg)
+    inp = make_prefill_inputs(cfg)
+    L = oracle_layer(cfg, wts)
+    seq = oracle_seq_from_init(L, inp.cache, 0)
+    seq.feed(inp.pos0, inp.x, inp.u)
+    T, p0 = inp.T, inp.pos0
+    sample = sorted({0, 1, 2, 3, 4, 127, 128, 1000, 2047, 2048, 3001, T - 5, T - 2, T - 1})
+    qI, w = inp.qI.copy(), inp.w.copy()
+    for n in sample:
+        for a in range(40):
+            if topk_margin(seq.index_scores(p0 + n, qI[n], w[n]), cfg.top_k) > MARGIN:
+                break
+            nq, nw = G.draw_query_index(cfg, 1, sub=9000 + n, attempt=a + 1)
+            qI[n], w[n] = nq[0], nw[0]
+    dl = device_layer(cfg, wts, inp.cache, max_chunk=T)
+    out, tk = dl.prefill(0, p0, dev(inp.x), dev(inp.u), dev(inp.q), dev(qI), dev(w))
+    torch.cuda.synchronize()
+    log("[c4] prefill chunk done")
+    comp_g, idx_g = cpu(dl.comp)[0], cpu(dl.idx)[0]
+    for i in range(p0 // 4, (p0 + T) // 4, 37):
+        compare_rows(comp_g[i], seq.comp_row(i)[0], cfg.kv_fmt, cfg.head_dim, cfg.n_rot, f"comp row {i}")
+        assert_close(O.decode_values(idx_g[i], cfg.idx_fmt), seq.idx_row(i)[0], BF16_TOL, f"idx row {i}")
+    i = p0 // 4   # the row whose window straddles the chunk edge
+    compare_rows(comp_g[i], seq.comp_row(i)[0], cfg.kv_fmt, cfg.head_dim, cfg.n_rot, "edge row")
+    og, tkg = out_values(out, cfg.act_fmt), cpu(tk)
+    bseq = oracle_seq_from_bytes(L, None, comp_g, idx_g, 0)
+    for n in sample:
+        p = p0 + n
+        # raw rows and rows of the chunk from the oracle's history; top-k on the GPU's index bytes
+        sc = bseq.index_scores(p, qI[n], w[n])
+        assert sets_equal(tkg[n], O.topk_select(sc, cfg.top_k)), f"top-k of query {n}"
+        ref = seq.attend(p, inp.q[n], tkg[n])
+        assert_close(og[n], ref, BF16_TOL, f"output of query {n}")
