@@ -58,13 +58,20 @@ class LayerCache(ctypes.Structure):
 class CkvError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
-        super().__init__(f"{where}: {strerror(code)} ({code})")
+        extra = f" [{lib.ckv_last_hip_error().decode()}]" if code == CKV_E_HIP else ""
+        super().__init__(f"{where}: {strerror(code)} ({code}){extra}")
 
 
 def _load() -> ctypes.CDLL:
+    # PyTorch ships its own HIP runtime whose libraries ask for it by a file
+    # name that does not match an already-mapped /opt/rocm runtime, so loading
+    # libckv first would leave two HIP runtimes in the process (the second sees
+    # no device).  With torch loaded first, libckv's libamdhip64.so.7 and
+    # libhsa-runtime64.so.1 dependencies resolve to the copies torch mapped.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libckv.so is not built at {LIB_PATH}; run "
-                          "`python -m compressed_kv_sparse_amd.build` (hipcc, gfx950)")
+                          "`python compressed_kv_sparse_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
     D, Wt, C = P(LayerDesc), P(LayerWeights), P(LayerCache)
@@ -74,6 +81,8 @@ def _load() -> ctypes.CDLL:
     lib.ckv_validate.restype = ctypes.c_int
     lib.ckv_strerror.argtypes = [ctypes.c_int]
     lib.ckv_strerror.restype = ctypes.c_char_p
+    lib.ckv_last_hip_error.argtypes = []
+    lib.ckv_last_hip_error.restype = ctypes.c_char_p
     lib.ckv_workspace_bytes.argtypes = [D, I32, I32]
     lib.ckv_workspace_bytes.restype = SZ
     sig = {
@@ -93,7 +102,7 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 
-EXPORTS = ("ckv_row_bytes", "ckv_validate", "ckv_strerror", "ckv_workspace_bytes",
+EXPORTS = ("ckv_row_bytes", "ckv_validate", "ckv_strerror", "ckv_last_hip_error", "ckv_workspace_bytes",
            "ckv_compress_append_decode", "ckv_compress_append_prefill", "ckv_indexer_topk_decode",
            "ckv_indexer_topk_prefill", "ckv_sparse_swa_attn_decode", "ckv_sparse_swa_attn_prefill")
 

@@ -1,6 +1,7 @@
 """Build libckv.so (gfx950) in-tree with hipcc.
 
-    python -m compressed_kv_sparse_amd.build        # or build() from Python
+    python compressed_kv_sparse_amd/build.py     # (run as a file: importing the
+                                                 #  package would load the library)
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
 selection switched off, then linked into compressed_kv_sparse_amd/libckv.so.

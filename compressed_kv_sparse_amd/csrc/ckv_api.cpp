@@ -1,5 +1,6 @@
 // C ABI entry points of libckv: argument checks on the host, then kernel
 // enqueues on the caller's stream.  Nothing here synchronises or allocates.
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "ckv_internal.h"
@@ -85,7 +86,19 @@ int prefill_range_ok(const LayerParams& P, const ckv_layer_cache* c, int32_t seq
   return CKV_OK;
 }
 
-int launched(int hip_rc) { return hip_rc ? CKV_E_HIP : CKV_OK; }
+thread_local int t_last_hip = 0;
+
+// An error left behind by an earlier, unrelated runtime call would otherwise be
+// reported as this call's launch failure: read it off before enqueueing.
+void clear_stale() { (void)hipGetLastError(); }
+
+int launched(int hip_rc) {
+  if (hip_rc) {
+    t_last_hip = hip_rc;
+    return CKV_E_HIP;
+  }
+  return CKV_OK;
+}
 
 }  // namespace
 
@@ -102,6 +115,7 @@ extern "C" int ckv_compress_append_decode(const ckv_layer_desc* desc, const ckv_
   if (check_ptr(u) || check_ptr(pos) || (P.ratio && check_ptr(x))) return CKV_E_INVAL;
   WsLayout L;
   if ((rc = check_ws(P, CKV_MODE_DECODE, B, ws, ws_bytes, &L))) return rc;
+  clear_stale();
   const Weights W = P.ratio ? to_weights(w) : Weights{};
   const Cache C = to_cache(cache);
   float* part = (float*)((uint8_t*)ws + L.proj);
@@ -123,6 +137,7 @@ extern "C" int ckv_compress_append_prefill(const ckv_layer_desc* desc, const ckv
   if (check_ptr(u) || (P.ratio && check_ptr(x))) return CKV_E_INVAL;
   WsLayout L;
   if ((rc = check_ws(P, CKV_MODE_PREFILL, T, ws, ws_bytes, &L))) return rc;
+  clear_stale();
   const Weights W = P.ratio ? to_weights(w) : Weights{};
   const Cache C = to_cache(cache);
   float* part = (float*)((uint8_t*)ws + L.proj);
@@ -144,6 +159,7 @@ extern "C" int ckv_indexer_topk_decode(const ckv_layer_desc* desc, const ckv_lay
   if (check_ptr(qI) || check_ptr(w) || check_ptr(pos) || check_ptr(topk)) return CKV_E_INVAL;
   WsLayout L;
   if ((rc = check_ws(P, CKV_MODE_DECODE, B, ws, ws_bytes, &L))) return rc;
+  clear_stale();
   uint8_t* wb = (uint8_t*)ws;
   return launched(launch_indexer(P, to_cache(cache), qI, w, pos, 0, 0, B, (uint32_t*)(wb + L.keys),
                                  (uint32_t*)(wb + L.hist), topk, stream));
@@ -162,6 +178,7 @@ extern "C" int ckv_indexer_topk_prefill(const ckv_layer_desc* desc, const ckv_la
   if (check_ptr(qI) || check_ptr(w) || check_ptr(topk)) return CKV_E_INVAL;
   WsLayout L;
   if ((rc = check_ws(P, CKV_MODE_PREFILL, T, ws, ws_bytes, &L))) return rc;
+  clear_stale();
   uint8_t* wb = (uint8_t*)ws;
   return launched(launch_indexer(P, to_cache(cache), qI, w, nullptr, seq, pos0, T,
                                  (uint32_t*)(wb + L.keys), (uint32_t*)(wb + L.hist), topk, stream));
@@ -181,6 +198,7 @@ extern "C" int ckv_sparse_swa_attn_decode(const ckv_layer_desc* desc, const ckv_
   if (topk && !aligned16(topk)) return CKV_E_INVAL;
   WsLayout L;
   if ((rc = check_ws(P, CKV_MODE_DECODE, B, ws, ws_bytes, &L))) return rc;
+  clear_stale();
   return launched(launch_attn(P, to_cache(cache), q, pos, 0, 0, B, topk, out, L, (uint8_t*)ws, stream));
 }
 
@@ -197,6 +215,11 @@ extern "C" int ckv_sparse_swa_attn_prefill(const ckv_layer_desc* desc, const ckv
   if (topk && !aligned16(topk)) return CKV_E_INVAL;
   WsLayout L;
   if ((rc = check_ws(P, CKV_MODE_PREFILL, T, ws, ws_bytes, &L))) return rc;
+  clear_stale();
   return launched(
       launch_attn(P, to_cache(cache), q, nullptr, seq, pos0, T, topk, out, L, (uint8_t*)ws, stream));
+}
+
+extern "C" const char* ckv_last_hip_error(void) {
+  return t_last_hip ? hipGetErrorName((hipError_t)t_last_hip) : "none";
 }

@@ -71,7 +71,10 @@ __device__ __forceinline__ int topk_end(const int32_t* tk, int k, int V, int* sm
 // tile sits in LDS twice: row-major for the QK^T operand and channel-major for
 // the PV operand.  An E4M3 row enters the products exactly (codes are exact in
 // bf16); its scale multiplies the non-RoPE logit part and the non-RoPE
-// probability operand.
+// probability operand.  The rotated query and the probabilities are fp32
+// values split into a bf16 pair hi + lo, each product taking two MFMAs, so
+// both contractions run at close to fp32 operand precision; the rows
+// themselves are exact in bf16.
 template <int KVF, int D>
 __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, const uint16_t* __restrict__ q,
                                                    const int32_t* __restrict__ pos, int seq_fixed, int pos0,
@@ -86,8 +89,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, cons
   constexpr int DN = D - 64;     // non-RoPE channels
   __shared__ __attribute__((aligned(16))) uint16_t Ks[R * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16 * VP];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps1[4][16 * VP];
+  // per wave: probabilities hi / lo, and (E4M3) scaled probabilities hi / lo
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[4][4][16 * VP];
   __shared__ const uint8_t* rptr[R];
   __shared__ float rsc[R];
   __shared__ float cs_[32], sn_[32];
@@ -108,23 +111,28 @@ __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, cons
   if (tid < 32) rope_cs(P.base, 64, tid, (double)A.p, &cs_[tid], &sn_[tid]);
   __syncthreads();
 
-  // rotated query of head h0 + r as the A operand, one bf16x8 per k-step
-  u32x4 Aq[KS];
+  // rotated query of head h0 + r as the A operand (hi, lo), one bf16x8 per k-step;
+  // the non-RoPE channels are bf16 inputs, exact in hi with lo = 0
+  u32x4 Aq[KS], Aql[KS];
   {
     const uint16_t* qr = q + ((size_t)qn * H + h0 + r) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c0 = 32 * ks + 8 * g;
       u32x4 v = *(const u32x4*)(qr + c0);
+      u32x4 lo = {0u, 0u, 0u, 0u};
       if (c0 >= DN) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float a = bf16_to_f32(v[e] & 0xffffu), b = bf16_to_f32(v[e] >> 16);
           const int jp = (c0 - DN) / 2 + e;
-          v[e] = pack_bf16x2(a * cs_[jp] - b * sn_[jp], a * sn_[jp] + b * cs_[jp]);
+          const float x = a * cs_[jp] - b * sn_[jp], y = a * sn_[jp] + b * cs_[jp];
+          v[e] = pack_bf16x2(x, y);
+          lo[e] = pack_bf16x2(x - bf16_to_f32(v[e] & 0xffffu), y - bf16_to_f32(v[e] >> 16));
         }
       }
       Aq[ks] = v;
+      Aql[ks] = lo;
     }
   }
 
@@ -196,8 +204,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, cons
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4 b = *(const u32x4*)&Ks[(16 * nt + r) * KP + 32 * ks + 8 * g];
-        if (32 * ks < DN) a1 = mfma16x16x32(as_bf16x8(Aq[ks]), as_bf16x8(b), a1);
-        else a2 = mfma16x16x32(as_bf16x8(Aq[ks]), as_bf16x8(b), a2);
+        if (32 * ks < DN) {
+          a1 = mfma16x16x32(as_bf16x8(Aq[ks]), as_bf16x8(b), a1);
+        } else {
+          a2 = mfma16x16x32(as_bf16x8(Aq[ks]), as_bf16x8(b), a2);
+          a2 = mfma16x16x32(as_bf16x8(Aql[ks]), as_bf16x8(b), a2);
+        }
       }
       const float rs = rsc[16 * nt + r];
 #pragma unroll
@@ -229,23 +241,37 @@ __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, cons
     for (int n = 0; n < NO; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) O[n][i] *= alpha[i];
-    // probabilities -> LDS as the A operand [16 heads][32 rows]
+    // probabilities -> LDS as the A operand [16 heads][32 rows], split hi + lo
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const float rs = rsc[16 * nt + r];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Ps[wave][(4 * g + i) * VP + 16 * nt + r] = (uint16_t)f32_to_bf16(S[nt][i]);
-        if (KVF == CKV_E4M3) Ps1[wave][(4 * g + i) * VP + 16 * nt + r] = (uint16_t)f32_to_bf16(S[nt][i] * fmaxf(rs, 0.f));
+        const int o = (4 * g + i) * VP + 16 * nt + r;
+        const float pv = S[nt][i];
+        const uint32_t hb = f32_to_bf16(pv);
+        Ps[wave][0][o] = (uint16_t)hb;
+        Ps[wave][1][o] = (uint16_t)f32_to_bf16(pv - bf16_to_f32(hb));
+        if (KVF == CKV_E4M3) {
+          const float ps = pv * fmaxf(rs, 0.f);
+          const uint32_t hs = f32_to_bf16(ps);
+          Ps[wave][2][o] = (uint16_t)hs;
+          Ps[wave][3][o] = (uint16_t)f32_to_bf16(ps - bf16_to_f32(hs));
+        }
       }
     }
     __syncthreads();
-    const u32x4 ap = *(const u32x4*)&Ps[wave][r * VP + 8 * g];
-    const u32x4 ap1 = KVF == CKV_E4M3 ? *(const u32x4*)&Ps1[wave][r * VP + 8 * g] : ap;
+    const int pa = r * VP + 8 * g;
+    const u32x4 aph = *(const u32x4*)&Ps[wave][0][pa];
+    const u32x4 apl = *(const u32x4*)&Ps[wave][1][pa];
+    const u32x4 ash = KVF == CKV_E4M3 ? *(const u32x4*)&Ps[wave][2][pa] : aph;
+    const u32x4 asl = KVF == CKV_E4M3 ? *(const u32x4*)&Ps[wave][3][pa] : apl;
 #pragma unroll
     for (int n = 0; n < NO; ++n) {
       const u32x4 b = *(const u32x4*)&Vt[(16 * n + r) * VP + 8 * g];
-      O[n] = mfma16x16x32(as_bf16x8(16 * n < DN ? ap1 : ap), as_bf16x8(b), O[n]);
+      const bool nope = 16 * n < DN;
+      O[n] = mfma16x16x32(as_bf16x8(nope ? ash : aph), as_bf16x8(b), O[n]);
+      O[n] = mfma16x16x32(as_bf16x8(nope ? asl : apl), as_bf16x8(b), O[n]);
     }
   }
 

@@ -181,6 +181,10 @@ int ckv_validate(const ckv_layer_desc* desc);
 /* Static string for a return code. */
 const char* ckv_strerror(int code);
 
+/* Name of the HIP error behind the calling thread's most recent CKV_E_HIP
+ * ("none" if there was none).  Static string. */
+const char* ckv_last_hip_error(void);
+
 /* Workspace bytes a call of `mode` with n = B (decode) or T (prefill) tokens
  * needs; the same figure serves all three entry points of that mode.
  * 0 when desc is invalid. */
