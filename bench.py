@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the compressed-KV sparse attention hot path on one MI355X.
+
+A step is one decode step of one c4a layer at 128k context for a batch of 16
+sequences: compress_append -> indexer_topk -> sparse_swa_attn through the C
+ABI, inputs resident in HBM (fp8 E4M3 attention cache with fp32 row scales,
+bf16 indexer cache, 64 query heads x 512, top-k 512).  The timed loop replays
+a captured HIP graph of one step.  Alongside it the script reports:
+
+* roofline of the dominant kernel (the indexer score scan): algorithmic bytes
+  per launch / its average launch duration from HIP events around it;
+* the whole step's algorithmic bytes against HBM peak;
+* the 4096-token chunked prefill at position 61440 (tokens/s and the share of
+  bf16 MFMA peak of its algorithmic flops);
+* the CPU oracle timed on the host cores on the same inputs (a baseline).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
+ALGO_ROW_BYTES = {"f32": lambda d: 4 * d, "bf16": lambda d: 2 * d,
+                  "e4m3": lambda d: (d - 64) + 128 + 4}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- setup
+
+def make_layer(cfg, wts, cache, max_chunk=0):
+    from compressed_kv_sparse_amd import DeviceLayer
+    dl = DeviceLayer(ratio=cfg.ratio, hidden=cfg.hidden, head_dim=cfg.head_dim, n_heads=cfg.n_heads,
+                     batch=cfg.batch, idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim, top_k=cfg.top_k,
+                     comp_cap=cfg.comp_cap, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt, act_fmt=cfg.act_fmt,
+                     w_fmt=cfg.w_fmt, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps, max_chunk=max_chunk)
+    if wts is not None:
+        dl.set_weights(wkv=wts.wkv, wgate=wts.wgate, ape=wts.ape, gamma=wts.gamma, idx_wkv=wts.idx_wkv,
+                       idx_wgate=wts.idx_wgate, idx_ape=wts.idx_ape, idx_gamma=wts.idx_gamma)
+    dl.load_cache(raw=cache.raw, comp=cache.comp, idx=cache.idx, st_kv=cache.st_kv, st_sc=cache.st_sc,
+                  ist_kv=cache.ist_kv, ist_sc=cache.ist_sc)
+    return dl
+
+
+def dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+# --------------------------------------------------------------------------- algorithmic work
+
+def decode_step_bytes(cfg, n):
+    """Bytes one decode step must move (reads + writes), per the method."""
+    d, D, H, HI, DI, k, r = cfg.head_dim, cfg.hidden, cfg.n_heads, cfg.idx_heads, cfg.idx_dim, cfg.top_k, cfg.ratio
+    rho = ALGO_ROW_BYTES[cfg.kv_fmt](d)
+    s_i = 2 if cfg.idx_fmt == "bf16" else 4
+    s_a = 2 if cfg.act_fmt == "bf16" else 4
+    s_w = 2 if cfg.w_fmt == "bf16" else 4
+    W = cfg.window
+    total = 0.0
+    for nb in n:
+        p = nb - 1
+        V = (nb // r) if r else 0
+        C = min(k, V) if r == 4 else (V if r == 128 else 0)
+        b = 0.0
+        if r == 4:
+            b += V * DI * s_i + HI * (DI * s_a + 4) + 8 * k
+        b += (min(nb, 128) + C) * rho + H * d * 2 * s_a + d * s_a + rho
+        if r:
+            b += D * s_a + 8 * (d + (DI if r == 4 else 0))
+            if (p + 1) % r == 0:
+                b += W * 8 * (d + (DI if r == 4 else 0)) + rho + (DI * s_i if r == 4 else 0)
+        total += b
+    if r:
+        total += 2 * D * (d + (DI if r == 4 else 0)) * s_w + W * 4 * (d + (DI if r == 4 else 0))
+    return total
+
+
+def score_kernel_bytes(cfg, n):
+    """Bytes the indexer score kernel must move: every visible indexer row, the
+    queries and head weights, and one 4-byte key written per row."""
+    s_i = 2 if cfg.idx_fmt == "bf16" else 4
+    s_a = 2 if cfg.act_fmt == "bf16" else 4
+    tot = 0.0
+    for nb in n:
+        V = nb // 4
+        tot += V * cfg.idx_dim * s_i + V * 4 + cfg.idx_heads * (cfg.idx_dim * s_a + 4)
+    return tot
+
+
+def prefill_flops(cfg, pos0, T):
+    d, D, H, HI, DI, k = cfg.head_dim, cfg.hidden, cfg.n_heads, cfg.idx_heads, cfg.idx_dim, cfg.top_k
+    f = 2.0 * T * D * 2 * (d + DI)
+    for p in range(pos0, pos0 + T):
+        V = (p + 1) // 4
+        f += 2.0 * HI * DI * V + 4.0 * H * d * (min(128, p + 1) + min(k, V))
+    return f
+
+
+# --------------------------------------------------------------------------- decode
+
+def bench_decode(cfg, steps, warmup, with_kernel=True):
+    import torch
+    from workloads import make_decode_inputs, make_layer_weights
+    from workloads.gen import context_lengths
+    from compressed_kv_sparse_amd import _lib as L
+
+    t0 = time.time()
+    inp = make_decode_inputs(cfg)
+    wts = make_layer_weights(cfg)
+    n = context_lengths(cfg)
+    log(f"[bench] {cfg.name}: inputs drawn in {time.time() - t0:.1f}s")
+    dl = make_layer(cfg, wts, inp.cache)
+    x, u, q, pos = dev(inp.x), dev(inp.u), dev(inp.q), dev(inp.pos)
+    qI = dev(inp.qI) if inp.qI is not None else None
+    w = dev(inp.w) if inp.w is not None else None
+    B = cfg.batch
+    out = dl.new_out(B)
+    topk = torch.empty((B, cfg.top_k), dtype=torch.int32, device="cuda") if cfg.ratio == 4 else None
+
+    def step():
+        dl.decode(x, u, q, qI, w, pos, out=out, topk=topk)
+
+    step()
+    torch.cuda.synchronize()
+    assert int(dl.status.abs().sum()) == 0, "device status set"
+    ref_out = out.clone()
+    ref_tk = topk.clone() if topk is not None else None
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):          # replays interleaved with eager checks
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "graph replay differs"
+        if ref_tk is not None:
+            assert torch.equal(topk, ref_tk), "graph replay top-k differs"
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    res = {"ms_per_step": dt * 1e3, "tok_s": B / dt, "step_bytes": decode_step_bytes(cfg, n)}
+    res["step_gbs"] = res["step_bytes"] / dt / 1e9
+    res["step_hbm_frac"] = res["step_gbs"] / HBM_PEAK_GBS
+
+    if with_kernel and cfg.ratio == 4:
+        # the dominant kernel on its own: indexer score scan, events around each launch
+        keys = torch.empty((B, cfg.comp_cap), dtype=torch.int32, device="cuda")
+        hist = torch.zeros((B, 4096), dtype=torch.int32, device="cuda")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        stream = torch.cuda.current_stream().cuda_stream
+        for i in range(warmup + steps):
+            hist.zero_()
+            if i >= warmup:
+                evs[i - warmup][0].record()
+            rc = L.indexer_score_decode(dl.desc, dl.cache, qI, w, pos, B, keys, hist, stream)
+            if i >= warmup:
+                evs[i - warmup][1].record()
+            if rc:
+                raise L.CkvError(rc, "indexer_score_decode")
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        kb = score_kernel_bytes(cfg, n)
+        res["kernel"] = {"name": "k_idx_score_mfma", "avg_us": ms * 1e3, "bytes": kb,
+                         "gbs": kb / (ms * 1e-3) / 1e9}
+    res["_inp"] = inp
+    res["_wts"] = wts
+    return res
+
+
+# --------------------------------------------------------------------------- prefill
+
+def bench_prefill(cfg, steps, warmup):
+    import torch
+    from workloads import make_layer_weights, make_prefill_inputs
+
+    inp = make_prefill_inputs(cfg)
+    wts = make_layer_weights(cfg)
+    dl = make_layer(cfg.with_(batch=1), wts, inp.cache, max_chunk=inp.T)
+    x, u, q, qI, w = dev(inp.x), dev(inp.u), dev(inp.q), dev(inp.qI), dev(inp.w)
+    T = inp.T
+    out = dl.new_out(T)
+    topk = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+    # the chunk rewrites the raw ring and the compressor state; restoring them
+    # before each run keeps every run identical (a few hundred KiB of copies)
+    saved = [(t, t.clone()) for t in (dl.raw, dl.st_kv, dl.st_sc, dl.ist_kv, dl.ist_sc) if t is not None]
+
+    def run():
+        for t, c in saved:
+            t.copy_(c)
+        dl.prefill(0, inp.pos0, x, u, q, qI, w, out=out, topk=topk)
+
+    for _ in range(max(1, warmup)):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    fl = prefill_flops(cfg, inp.pos0, T)
+    return {"ms_per_chunk": dt * 1e3, "tok_s": T / dt, "tflops": fl / dt / 1e12,
+            "mfma_frac": fl / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS, "flops": fl}
+
+
+# --------------------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(cfg, inp, wts, budget_s=12.0):
+    """The oracle on the host cores, on the same inputs: whole decode steps
+    (compressor, indexer scores, full-sort top-k, attention) per sequence."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    L = O.layer_from(cfg, wts)
+    c = inp.cache
+    done, t0 = 0, time.perf_counter()
+    while True:
+        for b in range(cfg.batch):
+            seq = O.OracleSequence(L, raw_rec=c.raw[b], comp_rec=c.comp[b] if c.comp is not None else None,
+                                   idx_vals=c.idx[b] if c.idx is not None else None,
+                                   st_kv=c.st_kv[b] if c.st_kv is not None else None,
+                                   st_sc=c.st_sc[b] if c.st_sc is not None else None,
+                                   ist_kv=c.ist_kv[b] if c.ist_kv is not None else None,
+                                   ist_sc=c.ist_sc[b] if c.ist_sc is not None else None,
+                                   first_live=int(c.first_live[b]))
+            seq.step(int(inp.pos[b]), inp.x[b], inp.u[b], inp.q[b],
+                     None if inp.qI is None else inp.qI[b], None if inp.w is None else inp.w[b])
+            done += 1
+            if time.perf_counter() - t0 > budget_s and done >= 2:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} sequence decode steps of {cfg.name} (p={int(inp.pos[0])}), "
+                      f"{dt:.1f}s on the host, numpy fp64"}
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c5")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--extra", action="store_true", help="also time the other decode workloads")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(sequences shard across GPUs with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from workloads import get_config
+
+    cfg = get_config(args.workload)
+    r = bench_decode(cfg, args.steps, args.warmup)
+    log(f"[bench] decode {cfg.name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['tok_s']:.0f} tok/s, "
+        f"step {r['step_gbs']:.0f} GB/s ({100 * r['step_hbm_frac']:.1f}% of HBM)")
+    kern = r.get("kernel")
+    roof = None
+    if kern:
+        log(f"[bench] {kern['name']}: {kern['avg_us']:.1f} us, {kern['gbs']:.0f} GB/s")
+        roof = {"bound": "hbm", "kernel": kern["name"], "achieved": round(kern["gbs"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern["gbs"] / HBM_PEAK_GBS, 4),
+                "avg_us": round(kern["avg_us"], 2), "bytes_per_launch": int(kern["bytes"]), "traffic": None}
+    extra = {}
+    if args.extra:
+        for name in ("c2", "c3", "c5_c128a", "c5_swa"):
+            e = bench_decode(get_config(name), args.steps, args.warmup, with_kernel=False)
+            extra[name] = {k: round(v, 4) for k, v in e.items() if not k.startswith("_") and isinstance(v, float)}
+            log(f"[bench] decode {name}: {e['ms_per_step'] * 1e3:.1f} us/step, {e['tok_s']:.0f} tok/s, "
+                f"{100 * e['step_hbm_frac']:.1f}% HBM")
+    pre = None
+    if not args.no_prefill:
+        p = bench_prefill(get_config("c4"), args.prefill_steps, 1)
+        pre = {"workload": get_config("c4").name, "tok_s": round(p["tok_s"], 1),
+               "ms_per_chunk": round(p["ms_per_chunk"], 3), "tflops": round(p["tflops"], 2),
+               "mfma_frac": round(p["mfma_frac"], 4)}
+        log(f"[bench] prefill: {p['ms_per_chunk']:.2f} ms/chunk, {p['tok_s']:.0f} tok/s, "
+            f"{p['tflops']:.1f} TFLOP/s ({100 * p['mfma_frac']:.1f}% of bf16 MFMA)")
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, r["_inp"], r["_wts"])
+        log(f"[bench] cpu oracle: {cpu['value']:.2f} tok/s on {cpu['cores']} threads")
+    line = {
+        "metric": "decode tokens/s + HBM GB/s % peak, c4a sparse attn @128k ctx; prefill tok/s",
+        "value": round(r["tok_s"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16+fp8",
+        "data": "synthetic (seeded draws of the workload's shapes)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "context": cfg.n_ctx, "head_dim": cfg.head_dim,
+                   "heads": cfg.n_heads, "indexer": f"{cfg.idx_heads}x{cfg.idx_dim}", "top_k": cfg.top_k,
+                   "kv_cache": cfg.kv_fmt, "indexer_cache": cfg.idx_fmt, "parallelism": "1 GPU"},
+        "step_hbm": {"bytes": int(r["step_bytes"]), "achieved": round(r["step_gbs"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(r["step_hbm_frac"], 4)},
+        "roofline": roof,
+        "prefill": pre,
+        "cpu_baseline": cpu,
+    }
+    if extra:
+        line["extra"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -90,6 +90,7 @@ def _load() -> ctypes.CDLL:
         "ckv_compress_append_prefill": [D, Wt, C, VP, VP, I32, I32, I32, VP, SZ, VP],
         "ckv_indexer_topk_decode": [D, C, VP, VP, VP, I32, VP, VP, SZ, VP],
         "ckv_indexer_topk_prefill": [D, C, VP, VP, I32, I32, I32, VP, VP, SZ, VP],
+        "ckv_indexer_score_decode": [D, C, VP, VP, VP, I32, VP, VP, VP],
         "ckv_sparse_swa_attn_decode": [D, C, VP, VP, VP, I32, VP, VP, SZ, VP],
         "ckv_sparse_swa_attn_prefill": [D, C, VP, I32, I32, I32, VP, VP, VP, SZ, VP],
     }
@@ -104,7 +105,8 @@ lib = _load()
 
 EXPORTS = ("ckv_row_bytes", "ckv_validate", "ckv_strerror", "ckv_last_hip_error", "ckv_workspace_bytes",
            "ckv_compress_append_decode", "ckv_compress_append_prefill", "ckv_indexer_topk_decode",
-           "ckv_indexer_topk_prefill", "ckv_sparse_swa_attn_decode", "ckv_sparse_swa_attn_prefill")
+           "ckv_indexer_topk_prefill", "ckv_indexer_score_decode", "ckv_sparse_swa_attn_decode",
+           "ckv_sparse_swa_attn_prefill")
 
 
 def strerror(code: int) -> str:
@@ -149,6 +151,11 @@ def compress_append_prefill(desc, weights, cache, x, u, seq, pos0, T, ws, ws_byt
 def indexer_topk_decode(desc, cache, qI, w, pos, B, topk, ws, ws_bytes, stream=None) -> int:
     return lib.ckv_indexer_topk_decode(_ref(desc), _ref(cache), _p(qI), _p(w), _p(pos), int(B), _p(topk),
                                        _p(ws), int(ws_bytes), stream)
+
+
+def indexer_score_decode(desc, cache, qI, w, pos, B, keys, hist, stream=None) -> int:
+    return lib.ckv_indexer_score_decode(_ref(desc), _ref(cache), _p(qI), _p(w), _p(pos), int(B), _p(keys),
+                                        _p(hist), stream)
 
 
 def indexer_topk_prefill(desc, cache, qI, w, seq, pos0, T, topk, ws, ws_bytes, stream=None) -> int:

@@ -165,6 +165,21 @@ extern "C" int ckv_indexer_topk_decode(const ckv_layer_desc* desc, const ckv_lay
                                  (uint32_t*)(wb + L.hist), topk, stream));
 }
 
+extern "C" int ckv_indexer_score_decode(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
+                                        const void* qI, const float* w, const int32_t* pos, int32_t B,
+                                        uint32_t* keys, uint32_t* hist, void* stream) {
+  LayerParams P;
+  int rc = prologue(desc, cache, &P);
+  if (rc) return rc;
+  if (P.ratio != 4) return CKV_E_UNSUPPORTED;
+  if (B < 1) return CKV_E_INVAL;
+  if (B > P.batch) return CKV_E_CAPACITY;
+  if (check_ptr(qI) || check_ptr(w) || check_ptr(pos) || check_ptr(keys) || check_ptr(hist))
+    return CKV_E_INVAL;
+  clear_stale();
+  return launched(launch_idx_score(P, to_cache(cache), qI, w, pos, 0, 0, B, keys, hist, stream));
+}
+
 extern "C" int ckv_indexer_topk_prefill(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
                                         const void* qI, const float* w, int32_t seq, int32_t pos0,
                                         int32_t T, int32_t* topk, void* ws, size_t ws_bytes,

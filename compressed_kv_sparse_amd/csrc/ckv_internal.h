@@ -81,6 +81,9 @@ int launch_compress_prefill(const LayerParams& P, const Weights& w, const Cache&
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
                    const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
                    int32_t* topk, void* stream);
+int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const float* w,
+                     const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
+                     void* stream);
 int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32_t* pos, int seq,
                 int pos0, int nq, const int32_t* topk, void* out, const WsLayout& L, uint8_t* ws,
                 void* stream);

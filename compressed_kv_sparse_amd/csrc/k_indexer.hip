@@ -341,6 +341,15 @@ int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const f
   const size_t nh = (size_t)nq * kHistBins;
   const size_t fb = (nh + 255) / 256;
   hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)(fb < 1024 ? fb : 1024)), dim3(256), 0, st, hist, nh, 0u);
+  launch_idx_score(P, c, qI, w, pos, seq, pos0, nq, keys, hist, stream);
+  hipLaunchKernelGGL(k_topk_select, dim3(nq), dim3(1024), 0, st, P, keys, hist, pos, pos0, topk);
+  return (int)hipGetLastError();
+}
+
+int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const float* w,
+                     const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
+                     void* stream) {
+  hipStream_t st = (hipStream_t)stream;
   // rows to cover: decode -> the whole capacity; prefill -> rows visible to the last query
   const int vlast = (pos0 + nq) / 4;
   const int vmax = pos ? P.cap : (vlast < P.cap ? vlast : P.cap);
@@ -374,7 +383,6 @@ int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const f
     else CKV_IV(CKV_BF16, CKV_BF16);
 #undef CKV_IV
   }
-  hipLaunchKernelGGL(k_topk_select, dim3(nq), dim3(1024), 0, st, P, keys, hist, pos, pos0, topk);
   return (int)hipGetLastError();
 }
 
