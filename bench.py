@@ -172,14 +172,12 @@ def bench_decode(cfg, steps, warmup, with_kernel=True):
     if with_kernel and cfg.ratio == 4:
         # the dominant kernel on its own: indexer score scan, events around each launch
         keys = torch.empty((B, cfg.comp_cap), dtype=torch.int32, device="cuda")
-        hist = torch.zeros((B, 4096), dtype=torch.int32, device="cuda")
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         stream = torch.cuda.current_stream().cuda_stream
         for i in range(warmup + steps):
-            hist.zero_()
             if i >= warmup:
                 evs[i - warmup][0].record()
-            rc = L.indexer_score_decode(dl.desc, dl.cache, qI, w, pos, B, keys, hist, stream)
+            rc = L.indexer_score_decode(dl.desc, dl.cache, qI, w, pos, B, keys, stream)
             if i >= warmup:
                 evs[i - warmup][1].record()
             if rc:
@@ -274,6 +272,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--extra", action="store_true", help="also time the other decode workloads")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run 3 plain device copies of MIB MiB (a known-size reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -285,6 +285,14 @@ def main():
         sys.exit(1)
     from workloads import get_config
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     cfg = get_config(args.workload)
     r = bench_decode(cfg, args.steps, args.warmup)
     log(f"[bench] decode {cfg.name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['tok_s']:.0f} tok/s, "

@@ -90,7 +90,7 @@ def _load() -> ctypes.CDLL:
         "ckv_compress_append_prefill": [D, Wt, C, VP, VP, I32, I32, I32, VP, SZ, VP],
         "ckv_indexer_topk_decode": [D, C, VP, VP, VP, I32, VP, VP, SZ, VP],
         "ckv_indexer_topk_prefill": [D, C, VP, VP, I32, I32, I32, VP, VP, SZ, VP],
-        "ckv_indexer_score_decode": [D, C, VP, VP, VP, I32, VP, VP, VP],
+        "ckv_indexer_score_decode": [D, C, VP, VP, VP, I32, VP, VP],
         "ckv_sparse_swa_attn_decode": [D, C, VP, VP, VP, I32, VP, VP, SZ, VP],
         "ckv_sparse_swa_attn_prefill": [D, C, VP, I32, I32, I32, VP, VP, VP, SZ, VP],
     }
@@ -153,9 +153,9 @@ def indexer_topk_decode(desc, cache, qI, w, pos, B, topk, ws, ws_bytes, stream=N
                                        _p(ws), int(ws_bytes), stream)
 
 
-def indexer_score_decode(desc, cache, qI, w, pos, B, keys, hist, stream=None) -> int:
+def indexer_score_decode(desc, cache, qI, w, pos, B, keys, stream=None) -> int:
     return lib.ckv_indexer_score_decode(_ref(desc), _ref(cache), _p(qI), _p(w), _p(pos), int(B), _p(keys),
-                                        _p(hist), stream)
+                                        stream)
 
 
 def indexer_topk_prefill(desc, cache, qI, w, seq, pos0, T, topk, ws, ws_bytes, stream=None) -> int:

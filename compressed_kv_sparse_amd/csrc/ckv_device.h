@@ -64,15 +64,17 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
 
 // ---------------------------------------------------------------- RoPE
 
-// cos / sin of pos * base^(-2j/n_rot), the angle formed and reduced in fp64 so
-// that positions near 2^20 keep full float accuracy.
-__device__ __forceinline__ void rope_cs(double base, int n_rot, int j, double pos, float* c,
-                                        float* s) {
-  const double theta = pow(base, -2.0 * (double)j / (double)n_rot);
-  double sn, cs;
-  sincos(pos * theta, &sn, &cs);
-  *c = (float)cs;
-  *s = (float)sn;
+// cos / sin of pos * theta_j.  The angle is formed in fp64 and reduced to
+// [-pi, pi] with a two-part 2*pi (error ~1e-11 rad at positions near 2^20);
+// the reduced angle then goes through float sincos.  theta_j comes from the
+// host (LayerParams::theta, base^(-2j/n_rot) in fp64).  All RoPE tails here
+// have n_rot = 64, so pair j of every tail uses theta_j.
+__device__ __forceinline__ void rope_cs(const LayerParams& P, int j, double pos, float* c, float* s) {
+  const double a = pos * P.theta[j];
+  const double k = rint(a * 0.15915494309189535);      // a / (2 pi)
+  double r = fma(-k, 6.283185307179586, a);            // 2 pi, high part
+  r = fma(-k, 2.4492935982947064e-16, r);              // 2 pi, low part
+  sincosf((float)r, s, c);
 }
 
 // ---------------------------------------------------------------- MFMA

@@ -9,8 +9,8 @@
 
 namespace ckv {
 
-constexpr int kHistBins = 4096;   // first-level top-k histogram: top 12 key bits
 constexpr int kMaxD = 512;
+constexpr int kMaxSplits = 256;   // attention partial results merged per query
 constexpr int kMaxDI = 128;
 
 // Layer parameters as the kernels see them (built from ckv_layer_desc after
@@ -25,6 +25,7 @@ struct LayerParams {
   int row_bytes;  // stored K=V row size
   int ncol;       // projection columns: 2d (+ 2 DI on ratio 4)
   int idx_rot;    // RoPE channels of indexer rows / queries: min(n_rot, DI)
+  double theta[32];  // RoPE frequencies base^(-2j/n_rot), j < n_rot/2
 };
 
 struct Weights {
@@ -55,7 +56,6 @@ struct Cache {
 struct WsLayout {
   size_t proj;      // float [proj_splits][n][ncol]
   size_t keys;      // uint32 [n][cap]   indexer keys
-  size_t hist;      // uint32 [n][kHistBins]
   size_t part_o;    // float [n][splits][H][d]  attention partial outputs
   size_t part_ml;   // float [n][splits][H][2]  attention partial (max, sum)
   size_t total;
@@ -79,11 +79,10 @@ int launch_compress_prefill(const LayerParams& P, const Weights& w, const Cache&
 // indexer: decode (pos != NULL, query b of sequence b) or prefill (pos == NULL,
 // query n of sequence seq at position pos0 + n)
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
-                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
-                   int32_t* topk, void* stream);
+                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, int32_t* topk,
+                   void* stream);
 int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const float* w,
-                     const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
-                     void* stream);
+                     const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, void* stream);
 int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32_t* pos, int seq,
                 int pos0, int nq, const int32_t* topk, void* out, const WsLayout& L, uint8_t* ws,
                 void* stream);

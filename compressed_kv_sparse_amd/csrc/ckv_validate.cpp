@@ -6,6 +6,7 @@
 // whose layout differs from the one it was built for instead of guessing;
 // ckv_validate applies the same rule to a layer description.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "ckv_internal.h"
@@ -41,6 +42,8 @@ bool make_params(const ckv_layer_desc* d, LayerParams* P) {
   P->row_bytes = (int)ckv_row_bytes(d->kv_fmt, d->head_dim, d->n_rot);
   P->ncol = d->ratio == 0 ? 0 : 2 * d->head_dim + (d->ratio == 4 ? 2 * d->idx_dim : 0);
   P->idx_rot = d->ratio == 4 ? (d->idx_dim < d->n_rot ? d->idx_dim : d->n_rot) : 0;
+  for (int j = 0; j < 32; ++j)
+    P->theta[j] = 2 * j < d->n_rot ? pow(d->rope_base, -2.0 * j / (double)d->n_rot) : 0.0;
   return true;
 }
 
@@ -64,12 +67,21 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   const int rows = attn_max_rows(P);
   int rps;
   if (attn_is_mfma(P)) {
-    if (prefill) rps = rows;
-    else rps = P.ratio == 4 ? 64 : P.ratio == 128 ? 256 : 32;
+    if (prefill) {
+      rps = rows;
+    } else {
+      rps = P.ratio == 4 ? 64 : P.ratio == 128 ? 256 : 32;
+      // tuning knob: rows of the row list one decode block handles (multiple of 32)
+      const char* e = getenv("CKV_ATTN_ROWS_PER_SPLIT");
+      if (e && atoi(e) >= 32) rps = atoi(e);
+    }
   } else {
     rps = 32;
   }
   rps = (rps + 31) / 32 * 32;
+  // the merge kernel combines at most kMaxSplits partial results per query
+  const int min_rps = ((rows + kMaxSplits - 1) / kMaxSplits + 31) / 32 * 32;
+  if (rps < min_rps) rps = min_rps;
   L.attn_rows_per_split = rps;
   L.attn_splits = (rows + rps - 1) / rps;
   size_t off = 0;
@@ -77,8 +89,6 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   off += align256((size_t)L.proj_splits * n * P.ncol * sizeof(float));
   L.keys = off;
   if (P.ratio == 4) off += align256((size_t)n * P.cap * sizeof(uint32_t));
-  L.hist = off;
-  if (P.ratio == 4) off += align256((size_t)n * kHistBins * sizeof(uint32_t));
   const bool need_part = !(attn_is_mfma(P) && L.attn_splits == 1);
   L.part_o = off;
   if (need_part) off += align256((size_t)n * L.attn_splits * P.H * P.d * sizeof(float));

@@ -87,11 +87,14 @@ __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, cons
   constexpr int KS = D / 32;     // k-steps of QK^T
   constexpr int NO = D / 16;     // output channel tiles
   constexpr int DN = D - 64;     // non-RoPE channels
+  constexpr int C8 = D / 8;      // 8-channel chunks per row
+  constexpr int IT = (R / 2) * C8 / 256;  // staging items per thread per tile
+  constexpr int MAXK = 4096;     // top-k list held in LDS
   __shared__ __attribute__((aligned(16))) uint16_t Ks[R * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
   // per wave: probabilities hi / lo, and (E4M3) scaled probabilities hi / lo
   __shared__ __attribute__((aligned(16))) uint16_t Ps[4][4][16 * VP];
-  __shared__ const uint8_t* rptr[R];
+  __shared__ int32_t tks[MAXK];
   __shared__ float rsc[R];
   __shared__ float cs_[32], sn_[32];
   __shared__ int tk_lim;
@@ -105,11 +108,103 @@ __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, cons
   const AttnQuery A = attn_query(P, pos, seq_fixed, pos0, qn);
   const int j0 = split * rows_per_split;
   const int j1 = min(A.n_list, j0 + rows_per_split);
-  const int32_t* tk = (P.ratio == 4 && topk) ? topk + (size_t)qn * P.topk : nullptr;
-  int tk_end = 0;
-  if (tk) tk_end = topk_end(tk, P.topk, A.V, &tk_lim);
-  if (tid < 32) rope_cs(P.base, 64, tid, (double)A.p, &cs_[tid], &sn_[tid]);
+  const int32_t* tkg = (P.ratio == 4 && topk) ? topk + (size_t)qn * P.topk : nullptr;
+  // top-k list into LDS; the list ends at its first entry >= V
+  if (tid == 0) tk_lim = tkg ? P.topk : 0;
   __syncthreads();
+  if (tkg) {
+    for (int j = tid; j < P.topk; j += 256) {
+      const int v = tkg[j];
+      tks[j] = v;
+      if (v >= A.V) atomicMin(&tk_lim, j);
+    }
+  }
+  if (tid < 32) rope_cs(P, tid, (double)A.p, &cs_[tid], &sn_[tid]);
+  __syncthreads();
+  const int tk_end = tk_lim;
+
+  // address of list entry j's stored row (NULL: skipped entry or past the split)
+  auto row_ptr = [&](int j) -> const uint8_t* {
+    if (j >= j1) return nullptr;
+    if (j < A.n_raw) {
+      const int t = A.p - A.n_raw + 1 + j;
+      if (decode) return cc.raw + ((size_t)A.seq * P.swa + t % P.swa) * P.row_bytes;
+      return cc.stage + (size_t)(t - pos0 + P.swa - 1) * P.row_bytes;
+    }
+    const int jj = j - A.n_raw;
+    int row = jj;
+    if (P.ratio == 4) {
+      if (jj >= tk_end) return nullptr;
+      row = tks[jj];
+      if (row < 0) return nullptr;
+    }
+    return cc.comp + ((size_t)A.seq * P.cap + row) * P.row_bytes;
+  };
+
+  // staged global loads of one tile: item e covers rows (2pr, 2pr+1), channels
+  // 8*c8..; the row pair varies fastest across lanes so that the channel-major
+  // Vt stores of 16 lanes land in 16 consecutive LDS words
+  u32x4 stg[IT][2];
+  float ssc[IT][2];
+  auto issue = [&](int jt) {
+#pragma unroll
+    for (int e = 0; e < IT; ++e) {
+      const int it = tid + 256 * e, pr = it & 15, c8 = it >> 4;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint8_t* rp = row_ptr(jt + 2 * pr + h);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        float sc = -1.f;
+        if (rp) {
+          if (KVF == CKV_BF16) {
+            v = *(const u32x4*)(rp + 16 * c8);
+          } else if (8 * c8 >= DN) {
+            v = *(const u32x4*)(rp + DN + 16 * (c8 - DN / 8));
+          } else {
+            const u32x2 cw = *(const u32x2*)(rp + 8 * c8);
+            v[0] = cw[0];
+            v[1] = cw[1];
+          }
+          if (c8 == 0) sc = KVF == CKV_E4M3 ? *(const float*)(rp + DN + 128) : 1.f;
+        }
+        stg[e][h] = v;
+        ssc[e][h] = sc;
+      }
+    }
+  };
+  // staged registers -> LDS (row-major K, channel-major V); E4M3 codes become
+  // their exact bf16 values
+  auto commit = [&]() {
+#pragma unroll
+    for (int e = 0; e < IT; ++e) {
+      const int it = tid + 256 * e, pr = it & 15, c8 = it >> 4;
+      u32x4 v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v[h] = stg[e][h];
+        if (KVF == CKV_E4M3 && 8 * c8 < DN) {
+          const uint32_t w0 = v[h][0], w1 = v[h][1];
+          u32x4 t;
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const uint32_t word = f < 2 ? w0 : w1;
+            const uint32_t b0 = (word >> (16 * (f & 1))) & 0xffu, b1 = (word >> (16 * (f & 1) + 8)) & 0xffu;
+            t[f] = (__float_as_uint(e4m3_to_f32(b0)) >> 16) | (__float_as_uint(e4m3_to_f32(b1)) & 0xffff0000u);
+          }
+          v[h] = t;
+        }
+        *(u32x4*)&Ks[(2 * pr + h) * KP + 8 * c8] = v[h];
+        if (c8 == 0) rsc[2 * pr + h] = ssc[e][h];
+      }
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        *(uint32_t*)&Vt[(8 * c8 + 2 * f) * VP + 2 * pr] = (v[0][f] & 0xffffu) | (v[1][f] << 16);
+        *(uint32_t*)&Vt[(8 * c8 + 2 * f + 1) * VP + 2 * pr] = (v[0][f] >> 16) | (v[1][f] & 0xffff0000u);
+      }
+    }
+  };
+
+  if (j0 < j1) issue(j0);
 
   // rotated query of head h0 + r as the A operand (hi, lo), one bf16x8 per k-step;
   // the non-RoPE channels are bf16 inputs, exact in hi with lo = 0
@@ -148,53 +243,10 @@ __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, cons
   const float scale = P.scale;
 
   for (int jt = j0; jt < j1; jt += R) {
+    __syncthreads();              // the previous tile's readers are done
+    commit();
     __syncthreads();
-    if (tid < R) {
-      const int j = jt + tid;
-      const uint8_t* rp = j < j1 ? attn_row(P, cc, A, decode, pos0, tk, tk_end, j) : nullptr;
-      rptr[tid] = rp;
-      float s = 0.f;
-      if (rp) s = KVF == CKV_E4M3 ? *(const float*)(rp + DN + 128) : 1.f;
-      rsc[tid] = rp ? s : -1.f;  // < 0 marks an empty slot
-    }
-    __syncthreads();
-    // stage: thread handles row pair (2*pr, 2*pr+1), 8 channels at 8*cc8
-    for (int it = tid; it < (R / 2) * (D / 8); it += 256) {
-      const int pr = it / (D / 8), c8 = it % (D / 8);
-      u32x4 v[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint8_t* rp = rptr[2 * pr + h];
-        if (!rp) {
-          v[h] = (u32x4){0u, 0u, 0u, 0u};
-        } else if (KVF == CKV_BF16 || 8 * c8 >= DN) {
-          const uint8_t* src = KVF == CKV_BF16 ? rp + 16 * c8 : rp + DN + 16 * (c8 - DN / 8);
-          v[h] = *(const u32x4*)src;
-        } else {
-          const u32x2 cw = *(const u32x2*)(rp + 8 * c8);
-          u32x4 t;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-#pragma unroll
-            for (int f = 0; f < 2; ++f) {
-              const uint32_t b0 = (cw[e] >> (16 * f)) & 0xffu, b1 = (cw[e] >> (16 * f + 8)) & 0xffu;
-              t[2 * e + f] = (__float_as_uint(e4m3_to_f32(b0)) >> 16) |
-                             (__float_as_uint(e4m3_to_f32(b1)) & 0xffff0000u);
-            }
-          }
-          v[h] = t;
-        }
-        *(u32x4*)&Ks[(2 * pr + h) * KP + 8 * c8] = v[h];
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (v[0][e] & 0xffffu) | (v[1][e] << 16);
-        const uint32_t hi = (v[0][e] >> 16) | (v[1][e] & 0xffff0000u);
-        *(uint32_t*)&Vt[(8 * c8 + 2 * e) * VP + 2 * pr] = lo;
-        *(uint32_t*)&Vt[(8 * c8 + 2 * e + 1) * VP + 2 * pr] = hi;
-      }
-    }
-    __syncthreads();
+    if (jt + R < j1) issue(jt + R);   // next tile's loads fly during this tile's math
 
     // logits for 2 row tiles of 16
     float S[2][4];
@@ -337,7 +389,7 @@ __global__ __launch_bounds__(256) void k_attn_vec(LayerParams P, Cache cc, const
     float a = load_val<ACTF>(q, o), b = load_val<ACTF>(q, o + 1);
     if (c0 + e >= dn) {
       float cs, sn;
-      rope_cs(P.base, P.n_rot, (c0 + e - dn) / 2, (double)A.p, &cs, &sn);
+      rope_cs(P, (c0 + e - dn) / 2, (double)A.p, &cs, &sn);
       const float x = a * cs - b * sn, y = a * sn + b * cs;
       a = x;
       b = y;
@@ -379,45 +431,75 @@ __global__ __launch_bounds__(256) void k_attn_vec(LayerParams P, Cache cc, const
 }
 
 // ----------------------------------------------------------------- merge
-// grid (queries, H); block d/2 threads, each two adjacent channels.
+// grid (queries, H); block d/4 threads, each four adjacent channels.  The
+// splits' (max, sum) pairs are read once into LDS.
 template <int ACTF>
-__global__ __launch_bounds__(256) void k_attn_merge(LayerParams P, const float* __restrict__ part_o,
+__global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     const int32_t* __restrict__ pos, int pos0, int nsplit,
                                                     void* __restrict__ out) {
+  __shared__ float wsh[kMaxSplits];
+  __shared__ float Lsh;
   const int qn = blockIdx.x, h = blockIdx.y, H = P.H, d = P.d;
-  const int c = 2 * threadIdx.x;
-  if (c >= d) return;
+  const int c = 4 * threadIdx.x;
   const int p = pos ? pos[qn] : pos0 + qn;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) {
-    const size_t b = ((size_t)qn * nsplit + s) * H + h;
-    if (part_ml[b * 2 + 1] > 0.f) M = fmaxf(M, part_ml[b * 2]);
+  const size_t b0 = (size_t)qn * nsplit * H + h;
+  if (threadIdx.x < 64) {
+    // max over splits with rows, then each split's weight exp(m_s - M)
+    float m[4], l[4];
+    float M = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int sidx = threadIdx.x + 64 * e;
+      m[e] = -INFINITY;
+      l[e] = 0.f;
+      if (sidx < nsplit) {
+        const float2 ml = *(const float2*)(part_ml + (b0 + (size_t)sidx * H) * 2);
+        m[e] = ml.x;
+        l[e] = ml.y;
+        if (l[e] > 0.f) M = fmaxf(M, m[e]);
+      }
+    }
+    M = wave_max(M);
+    float L = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int sidx = threadIdx.x + 64 * e;
+      const float wgt = l[e] > 0.f ? __expf(m[e] - M) : 0.f;
+      if (sidx < nsplit) wsh[sidx] = wgt;
+      L += l[e] * wgt;
+    }
+    L = wave_sum(L);
+    if (threadIdx.x == 0) Lsh = L;
   }
-  float L = 0.f, a = 0.f, bb = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const size_t b = ((size_t)qn * nsplit + s) * H + h;
-    const float l = part_ml[b * 2 + 1];
-    if (!(l > 0.f)) continue;
-    const float wgt = __expf(part_ml[b * 2] - M);
-    L += l * wgt;
-    a += part_o[b * d + c] * wgt;
-    bb += part_o[b * d + c + 1] * wgt;
+  __syncthreads();
+  if (c >= d) return;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sidx = 0; sidx < nsplit; ++sidx) {
+    const float wgt = wsh[sidx];
+    if (wgt == 0.f) continue;
+    const float4 v = *(const float4*)(part_o + (b0 + (size_t)sidx * H) * d + c);
+    a.x += v.x * wgt;
+    a.y += v.y * wgt;
+    a.z += v.z * wgt;
+    a.w += v.w * wgt;
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  a *= inv;
-  bb *= inv;
+  const float inv = Lsh > 0.f ? 1.f / Lsh : 0.f;
+  float o[4] = {a.x * inv, a.y * inv, a.z * inv, a.w * inv};
   const int dn = d - P.n_rot;
   if (c >= dn && !(P.flags & CKV_FLAG_NO_INV_ROPE) && p >= 0) {
-    float cs, sn;
-    rope_cs(P.base, P.n_rot, (c - dn) / 2, (double)p, &cs, &sn);
-    const float x = a * cs + bb * sn, y = -a * sn + bb * cs;
-    a = x;
-    bb = y;
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      float cs, sn;
+      rope_cs(P, (c + e - dn) / 2, (double)p, &cs, &sn);
+      const float x = o[e] * cs + o[e + 1] * sn, y = -o[e] * sn + o[e + 1] * cs;
+      o[e] = x;
+      o[e + 1] = y;
+    }
   }
-  const size_t o = ((size_t)qn * H + h) * d + c;
-  store_val<ACTF>(out, o, a);
-  store_val<ACTF>(out, o + 1, bb);
+  const size_t oo = ((size_t)qn * H + h) * d + c;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) store_val<ACTF>(out, oo + e, o[e]);
 }
 
 // ----------------------------------------------------------------- launcher
@@ -465,9 +547,9 @@ int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32
   }
   dim3 mg(nq, P.H);
   if (P.act_fmt == CKV_F32)
-    hipLaunchKernelGGL(k_attn_merge<CKV_F32>, mg, dim3(P.d / 2), 0, st, P, po, pml, pos, pos0, ns, out);
+    hipLaunchKernelGGL(k_attn_merge<CKV_F32>, mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
   else
-    hipLaunchKernelGGL(k_attn_merge<CKV_BF16>, mg, dim3(P.d / 2), 0, st, P, po, pml, pos, pos0, ns, out);
+    hipLaunchKernelGGL(k_attn_merge<CKV_BF16>, mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
   return (int)hipGetLastError();
 }
 

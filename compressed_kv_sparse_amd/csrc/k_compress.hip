@@ -19,11 +19,11 @@ namespace ckv {
 
 // Rotate the last `nrot` entries of z[0..width) (LDS) at position `pos`.
 // Caller synchronises before and after.
-__device__ __forceinline__ void rope_lds(float* z, int width, int nrot, double base, double pos) {
+__device__ __forceinline__ void rope_lds(const LayerParams& P, float* z, int width, int nrot, double pos) {
   const int dn = width - nrot;
   for (int j = threadIdx.x; j < nrot / 2; j += blockDim.x) {
     float c, s;
-    rope_cs(base, nrot, j, pos, &c, &s);
+    rope_cs(P, j, pos, &c, &s);
     const float a = z[dn + 2 * j], b = z[dn + 2 * j + 1];
     z[dn + 2 * j] = a * c - b * s;
     z[dn + 2 * j + 1] = a * s + b * c;
@@ -87,15 +87,88 @@ struct PoolAcc {
 
 // ------------------------------------------------------------ decode
 
-// One block per sequence.  part: projection partials [splits][B][ncol].
+template <int F>
+__device__ __forceinline__ float2 load2(const void* p, long i) {  // i even
+  if constexpr (F == CKV_F32) return *(const float2*)((const float*)p + i);
+  else {
+    const uint32_t w = *(const uint32_t*)((const uint16_t*)p + i);
+    return make_float2(bf16_to_f32(w & 0xffffu), bf16_to_f32(w >> 16));
+  }
+}
+
+__device__ __forceinline__ float2 ld2(const float* p) { return *(const float2*)p; }
+
+// Store one row from per-thread channel pairs (c, c+1) in format KVF.  Every
+// thread of the block calls (the E4M3 row scale is a block-wide max).
+template <int KVF>
+__device__ __forceinline__ void store_row2(uint8_t* dst, float2 z, int c, bool act, int d, int n_rot,
+                                           float* red) {
+  if constexpr (KVF == CKV_F32) {
+    if (act) *(float2*)(dst + 4 * c) = z;
+  } else if constexpr (KVF == CKV_BF16) {
+    if (act) *(uint32_t*)(dst + 2 * c) = pack_bf16x2(z.x, z.y);
+  } else {
+    const int dn = d - n_rot;
+    const float amax = block_max(act && c < dn ? fmaxf(fabsf(z.x), fabsf(z.y)) : 0.f, red);
+    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (act) {
+      if (c < dn) *(uint16_t*)(dst + c) = (uint16_t)(f32_to_e4m3(z.x / s) | (f32_to_e4m3(z.y / s) << 8));
+      else *(uint32_t*)(dst + dn + 2 * (c - dn)) = pack_bf16x2(z.x, z.y);
+    }
+    if (threadIdx.x == 0) *(float*)(dst + dn + 2 * n_rot) = s;
+  }
+}
+
+// Rotate the pair (c, c+1) if it lies in the last n_rot channels of `width`.
+__device__ __forceinline__ float2 rope2(const LayerParams& P, float2 z, int c, int width, int nrot, double pos) {
+  const int dn = width - nrot;
+  if (c < dn) return z;
+  float cs, sn;
+  rope_cs(P, (c - dn) >> 1, pos, &cs, &sn);
+  return make_float2(z.x * cs - z.y * sn, z.x * sn + z.y * cs);
+}
+
+// Pool channels (c, c+1) of row i over its window.  Token p's own values come
+// from registers; the other W-1 tokens from the state ring.  Loads go out in
+// groups of 8 slots before the group is accumulated.
+__device__ __forceinline__ float2 pool2(const float* skv, const float* ssc, const float* ape, int width, int W,
+                                        int r, int i, int p, float2 kcur, float2 scur, int c) {
+  PoolAcc a0, a1;
+  const int t0 = i * r - (W - r);
+  for (int j0 = 0; j0 < W; j0 += 8) {
+    float2 kv[8], sc[8], ap[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int t = t0 + j0 + jj;
+      kv[jj] = sc[jj] = make_float2(0.f, 0.f);
+      if (t >= 0 && t != p) {
+        kv[jj] = ld2(skv + (size_t)(t % W) * width + c);
+        sc[jj] = ld2(ssc + (size_t)(t % W) * width + c);
+      }
+      ap[jj] = ld2(ape + (size_t)(j0 + jj) * width + c);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int t = t0 + j0 + jj;
+      if (t < 0) continue;
+      const float2 k = t == p ? kcur : kv[jj];
+      const float2 e = t == p ? scur : sc[jj];
+      a0.add(e.x + ap[jj].x, k.x);
+      a1.add(e.y + ap[jj].y, k.y);
+    }
+  }
+  return make_float2(a0.value(), a1.value());
+}
+
+// One block per sequence; thread t owns channels (2t, 2t+1) of the attention
+// lane and, on ratio 4, of the indexer lane.  part: projection partials
+// [splits][B][ncol], summed here in split order.
 template <int KVF, int IDXF, int ACTF>
 __global__ __launch_bounds__(256) void k_compress_decode(LayerParams P, Weights w, Cache cc,
                                                          const void* __restrict__ u,
                                                          const int32_t* __restrict__ pos,
                                                          const float* __restrict__ part,
                                                          int splits, int B) {
-  __shared__ float zs[kMaxD];
-  __shared__ float zi[kMaxDI];
   __shared__ float red[16];
   const int b = blockIdx.x;
   const int p = pos[b];
@@ -103,114 +176,83 @@ __global__ __launch_bounds__(256) void k_compress_decode(LayerParams P, Weights 
     if (threadIdx.x == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_BAD_POS);
     return;
   }
-  const int d = P.d, r = P.ratio;
+  const int d = P.d, r = P.ratio, W = P.W, DI = P.DI;
+  const int c = 2 * threadIdx.x;
+  const bool act = c < d;
+  const bool iact = r == 4 && c < DI;
+  const bool emit = r != 0 && (p + 1) % r == 0;
+  const int i = emit ? (p + 1) / r - 1 : 0;
+  if (emit && i >= P.cap && threadIdx.x == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_CAPACITY);
+  const bool pool = emit && i < P.cap;
 
-  // raw sliding-window row: u rotated at p, stored in slot p % swa
-  for (int c = threadIdx.x; c < d; c += blockDim.x) zs[c] = load_val<ACTF>(u, (long)b * d + c);
-  __syncthreads();
-  rope_lds(zs, d, P.n_rot, P.base, (double)p);
-  __syncthreads();
-  store_row<KVF>(cc.raw + ((size_t)b * P.swa + p % P.swa) * P.row_bytes, zs, d, P.n_rot, red);
-  if (r == 0) return;
-
-  // this token's projections -> window state slot p % W
-  const int W = P.W;
+  // this token's inputs
+  const float2 uu = act ? load2<ACTF>(u, (long)b * d + c) : make_float2(0.f, 0.f);
+  float2 ka = make_float2(0.f, 0.f), sa = ka, kia = ka, sia = ka;
   const size_t pstride = (size_t)B * P.ncol;
   const float* pb = part + (size_t)b * P.ncol;
-  float kap[2] = {0.f, 0.f}, sig[2] = {0.f, 0.f};
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int c = threadIdx.x + n * blockDim.x;
-    if (c < d) {
-      float a = 0.f, g = 0.f;
-      for (int s = 0; s < splits; ++s) {
-        a += pb[s * pstride + c];
-        g += pb[s * pstride + d + c];
-      }
-      kap[n] = a;
-      sig[n] = g;
-      const size_t o = ((size_t)b * W + p % W) * d + c;
-      cc.st_kv[o] = a;
-      cc.st_sc[o] = g;
-    }
-  }
-  float kapi = 0.f, sigi = 0.f;
-  const int DI = P.DI;
-  if (r == 4 && (int)threadIdx.x < DI) {
-    const int c = threadIdx.x;
+  if (r && act) {
     for (int s = 0; s < splits; ++s) {
-      kapi += pb[s * pstride + 2 * d + c];
-      sigi += pb[s * pstride + 2 * d + DI + c];
+      const float2 a = ld2(pb + s * pstride + c), g = ld2(pb + s * pstride + d + c);
+      ka.x += a.x; ka.y += a.y;
+      sa.x += g.x; sa.y += g.y;
     }
+  }
+  if (iact) {
+    for (int s = 0; s < splits; ++s) {
+      const float2 a = ld2(pb + s * pstride + 2 * d + c), g = ld2(pb + s * pstride + 2 * d + DI + c);
+      kia.x += a.x; kia.y += a.y;
+      sia.x += g.x; sia.y += g.y;
+    }
+  }
+
+  // raw sliding-window row: u rotated at p, slot p % swa
+  store_row2<KVF>(cc.raw + ((size_t)b * P.swa + p % P.swa) * P.row_bytes, rope2(P, uu, c, d, P.n_rot, p), c,
+                  act, d, P.n_rot, red);
+  if (r == 0) return;
+
+  float2 y, yi;
+  if (pool) {
+    if (act)
+      y = pool2(cc.st_kv + (size_t)b * W * d, cc.st_sc + (size_t)b * W * d, w.ape, d, W, r, i, p, ka, sa, c);
+    if (iact)
+      yi = pool2(cc.ist_kv + (size_t)b * 8 * DI, cc.ist_sc + (size_t)b * 8 * DI, w.idx_ape, DI, 8, 4, i, p, kia,
+                 sia, c);
+  }
+  // this token's projections -> state slot p % W (slots the pooling read are other tokens')
+  if (act) {
+    const size_t o = ((size_t)b * W + p % W) * d + c;
+    *(float2*)(cc.st_kv + o) = ka;
+    *(float2*)(cc.st_sc + o) = sa;
+  }
+  if (iact) {
     const size_t o = ((size_t)b * 8 + p % 8) * DI + c;
-    cc.ist_kv[o] = kapi;
-    cc.ist_sc[o] = sigi;
+    *(float2*)(cc.ist_kv + o) = kia;
+    *(float2*)(cc.ist_sc + o) = sia;
   }
-  if ((p + 1) % r != 0) return;
-  const int i = (p + 1) / r - 1;
-  if (i >= P.cap) {
-    if (threadIdx.x == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_CAPACITY);
-    return;
-  }
+  if (!pool) return;
 
-  // pool row i of the attention lane
-  const int t0 = i * r - (W - r);
-  const float* skv = cc.st_kv + (size_t)b * W * d;
-  const float* ssc = cc.st_sc + (size_t)b * W * d;
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int c = threadIdx.x + n * blockDim.x;
-    if (c < d) {
-      PoolAcc pa;
-      for (int j = 0; j < W; ++j) {
-        const int t = t0 + j;
-        if (t < 0) continue;
-        float kv, sc;
-        if (t == p) {
-          kv = kap[n];
-          sc = sig[n];
-        } else {
-          kv = skv[(t % W) * d + c];
-          sc = ssc[(t % W) * d + c];
-        }
-        pa.add(sc + w.ape[j * d + c], kv);
-      }
-      zs[c] = pa.value();
+  // attention lane: RMSNorm, tail RoPE at i*r, store row i
+  {
+    const float ss = block_sum(act ? y.x * y.x + y.y * y.y : 0.f, red);
+    const float inv = 1.0f / sqrtf(ss / (float)d + P.eps);
+    float2 z = make_float2(0.f, 0.f);
+    if (act) {
+      const float2 gm = ld2(w.gamma + c);
+      z = rope2(P, make_float2(gm.x * (y.x * inv), gm.y * (y.y * inv)), c, d, P.n_rot, (double)i * r);
     }
+    store_row2<KVF>(cc.comp + ((size_t)b * P.cap + i) * P.row_bytes, z, c, act, d, P.n_rot, red);
   }
-  rmsnorm_lds(zs, d, w.gamma, P.eps, red);
-  __syncthreads();
-  rope_lds(zs, d, P.n_rot, P.base, (double)i * r);
-  __syncthreads();
-  store_row<KVF>(cc.comp + ((size_t)b * P.cap + i) * P.row_bytes, zs, d, P.n_rot, red);
-
   if (r == 4) {  // indexer lane: its own compressor of the same form
-    const float* ikv = cc.ist_kv + (size_t)b * 8 * DI;
-    const float* isc = cc.ist_sc + (size_t)b * 8 * DI;
-    const int c = threadIdx.x;
-    if (c < DI) {
-      PoolAcc pa;
-      for (int j = 0; j < 8; ++j) {
-        const int t = t0 + j;
-        if (t < 0) continue;
-        float kv, sc;
-        if (t == p) {
-          kv = kapi;
-          sc = sigi;
-        } else {
-          kv = ikv[(t % 8) * DI + c];
-          sc = isc[(t % 8) * DI + c];
-        }
-        pa.add(sc + w.idx_ape[j * DI + c], kv);
-      }
-      zi[c] = pa.value();
+    const float ss = block_sum(iact ? yi.x * yi.x + yi.y * yi.y : 0.f, red);
+    const float inv = 1.0f / sqrtf(ss / (float)DI + P.eps);
+    if (iact) {
+      const float2 gm = ld2(w.idx_gamma + c);
+      const float2 z = rope2(P, make_float2(gm.x * (yi.x * inv), gm.y * (yi.y * inv)), c, DI, P.idx_rot,
+                             (double)i * r);
+      uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * DI * (IDXF == CKV_F32 ? 4 : 2);
+      if (IDXF == CKV_F32) *(float2*)(dst + 4 * c) = z;
+      else *(uint32_t*)(dst + 2 * c) = pack_bf16x2(z.x, z.y);
     }
-    rmsnorm_lds(zi, DI, w.idx_gamma, P.eps, red);
-    __syncthreads();
-    rope_lds(zi, DI, P.idx_rot, P.base, (double)i * r);
-    __syncthreads();
-    uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * DI * (IDXF == CKV_F32 ? 4 : 2);
-    store_vals<IDXF>(dst, zi, DI);
   }
 }
 
@@ -236,7 +278,7 @@ __global__ __launch_bounds__(256) void k_stage_raw(LayerParams P, Cache cc, cons
   const int d = P.d;
   for (int c = threadIdx.x; c < d; c += blockDim.x) zs[c] = load_val<ACTF>(u, (long)(t - pos0) * d + c);
   __syncthreads();
-  rope_lds(zs, d, P.n_rot, P.base, (double)t);
+  rope_lds(P, zs, d, P.n_rot, (double)t);
   __syncthreads();
   store_row<KVF>(dst, zs, d, P.n_rot, red);
 }
@@ -276,7 +318,7 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
   }
   rmsnorm_lds(zs, d, w.gamma, P.eps, red);
   __syncthreads();
-  rope_lds(zs, d, P.n_rot, P.base, (double)i * r);
+  rope_lds(P, zs, d, P.n_rot, (double)i * r);
   __syncthreads();
   store_row<KVF>(cc.comp + ((size_t)seq * P.cap + i) * P.row_bytes, zs, d, P.n_rot, red);
   if (r != 4) return;
@@ -302,7 +344,7 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
   }
   rmsnorm_lds(zi, DI, w.idx_gamma, P.eps, red);
   __syncthreads();
-  rope_lds(zi, DI, P.idx_rot, P.base, (double)i * r);
+  rope_lds(P, zi, DI, P.idx_rot, (double)i * r);
   __syncthreads();
   uint8_t* dst = (uint8_t*)cc.idx + ((size_t)seq * P.cap + i) * DI * (IDXF == CKV_F32 ? 4 : 2);
   store_vals<IDXF>(dst, zi, DI);

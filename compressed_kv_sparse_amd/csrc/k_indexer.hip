@@ -4,19 +4,18 @@
 // Score of row s for a query at position p:
 //   I(s) = sum_h w_h * relu(qI_h . kI_s),  qI rotated at p (tail) and cast to
 //   the indexer-cache format, s < V = (p+1)/4.
-// The score kernel writes an order-preserving 32-bit key per row and a
-// histogram of the keys' top 12 bits per query.  The select kernel then finds
-// the exact k-th largest key with two more histogram levels over the
-// candidates (bits 19..8, then 7..0) and emits, in ascending index order,
-// every row above it plus the lowest-index rows equal to it.
+// The score kernel writes an order-preserving 32-bit key per row.  The select
+// kernel works on d = M - key, M the largest key of the query, and finds the
+// k-th smallest d by radix levels of up to 10 bits, most significant first;
+// each level counts only the keys that share the bits chosen so far.  The
+// first level bins d >> 14 and counts only d < 2^24 (scores within about two
+// octaves of the maximum), so the top rows spread over narrow bins instead of
+// piling into a few; when fewer than k keys fall in that range it widens the
+// range and counts again.  Every row above the k-th key is emitted, plus the
+// lowest-index rows equal to it, in ascending index order.
 #include "ckv_device.h"
 
 namespace ckv {
-
-__global__ void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t v) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
 
 struct IdxQuery {
   int seq, p, V;
@@ -31,41 +30,49 @@ __device__ __forceinline__ IdxQuery idx_query(const LayerParams& P, const int32_
   return q;
 }
 
-// LDS histogram of the block's keys, flushed to the query's global histogram.
-__device__ __forceinline__ void hist_flush(uint32_t* lh, uint32_t* gh) {
-  __syncthreads();
-  for (int e = threadIdx.x; e < kHistBins; e += blockDim.x) {
-    const uint32_t v = lh[e];
-    if (v) atomicAdd(&gh[e], v);
-  }
-}
-
 // ---------------------------------------------------------------- MFMA score
 // bf16 indexer rows; MT = ceil(H_I / 16) head tiles, KS = D_I / 32 k-steps.
-// grid: x = row blocks of 256, y = queries.  Each wave scores 64 rows.
+// grid: x = row blocks of 256 * groups, y = queries.  Per group each wave
+// scores 64 rows; the next group's rows are loaded while the current one is
+// multiplied.  Heads are the MFMA M dimension, rows the N dimension, so the
+// weighted head sum is 4 in-lane adds per tile and two cross-lane adds.
 template <int MT, int KS, int QF>
 __global__ __launch_bounds__(256) void k_idx_score_mfma(LayerParams P, const uint16_t* __restrict__ idx,
                                                         const void* __restrict__ qI,
                                                         const float* __restrict__ wt,
                                                         const int32_t* __restrict__ pos, int seq_fixed,
-                                                        int pos0, uint32_t* __restrict__ keys,
-                                                        uint32_t* __restrict__ hist) {
+                                                        int pos0, int groups, uint32_t* __restrict__ keys) {
   constexpr int DI = KS * 32;
   constexpr int HP = MT * 16;
   __shared__ __attribute__((aligned(16))) uint16_t qh[HP * DI];
   __shared__ float wsh[HP];
   __shared__ float cs_[32], sn_[32];
-  __shared__ uint32_t lh[kHistBins];
   const int qn = blockIdx.y;
   const IdxQuery Q = idx_query(P, pos, seq_fixed, pos0, qn);
-  const int rb0 = blockIdx.x * 256;
+  const int rb0 = blockIdx.x * 256 * groups;
   if (rb0 >= Q.V) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int HI = P.HI, nrot = P.idx_rot, dn = DI - nrot;
+  const uint16_t* base = idx + (size_t)Q.seq * P.cap * DI;
+  const u32x4 zero = {0, 0, 0, 0};
 
-  if (tid < nrot / 2) rope_cs(P.base, nrot, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
-  for (int e = tid; e < kHistBins; e += 256) lh[e] = 0;
+  // rows of group gi for this wave -> B operands (issued first: the loads
+  // overlap the prologue)
+  auto load = [&](u32x4(&Bv)[4][KS], int gi) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = rb0 + 256 * gi + wave * 64 + 16 * t + r;
+      const bool ok = row < Q.V;
+      const uint16_t* rp = base + (size_t)(ok ? row : 0) * DI + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) Bv[t][ks] = ok ? *(const u32x4*)(rp + 32 * ks) : zero;
+    }
+  };
+  u32x4 B0[4][KS], B1[4][KS];
+  load(B0, 0);
+
+  if (tid < nrot / 2) rope_cs(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
   if (tid < HP) wsh[tid] = tid < HI ? wt[(size_t)qn * HI + tid] : 0.f;
   __syncthreads();
   for (int pe = tid; pe < HP * DI / 2; pe += 256) {
@@ -95,44 +102,39 @@ __global__ __launch_bounds__(256) void k_idx_score_mfma(LayerParams P, const uin
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[mt][i] = wsh[16 * mt + 4 * g + i];
   }
-
-  const int row0 = rb0 + wave * 64;
-  const uint16_t* base = idx + (size_t)Q.seq * P.cap * DI;
-  const u32x4 zero = {0, 0, 0, 0};
-  u32x4 Bv[4][KS];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int row = row0 + 16 * t + r;
-    const bool ok = row < Q.V;
-    const uint16_t* rp = base + (size_t)(ok ? row : 0) * DI + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) Bv[t][ks] = ok ? *(const u32x4*)(rp + 32 * ks) : zero;
-  }
   const bool relu = !(P.flags & CKV_FLAG_IDX_NO_RELU);
-  float sc[4];
+  uint32_t* kout = keys + (size_t)qn * P.cap;
+
+  auto score = [&](const u32x4(&Bv)[4][KS], int gi) {
+    float sc[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    float s = 0.f;
+    for (int t = 0; t < 4; ++t) {
+      float s = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = {0, 0, 0, 0};
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(as_bf16x8(A[mt][ks]), as_bf16x8(Bv[t][ks]), acc);
+        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(as_bf16x8(A[mt][ks]), as_bf16x8(Bv[t][ks]), acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s += wv[mt][i] * (relu ? fmaxf(acc[i], 0.f) : acc[i]);
+        for (int i = 0; i < 4; ++i) s += wv[mt][i] * (relu ? fmaxf(acc[i], 0.f) : acc[i]);
+      }
+      s += __shfl_xor(s, 16, 64);
+      s += __shfl_xor(s, 32, 64);
+      sc[t] = s;
     }
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
-    sc[t] = s;
+    const float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
+    const int row = rb0 + 256 * gi + wave * 64 + lane;
+    if (row < Q.V) kout[row] = float_key(mine);
+  };
+  for (int gi = 0; gi < groups; gi += 2) {
+    if (rb0 + 256 * gi >= Q.V) break;
+    const bool more = gi + 1 < groups && rb0 + 256 * (gi + 1) < Q.V;
+    if (more) load(B1, gi + 1);
+    score(B0, gi);
+    if (!more) break;
+    if (gi + 2 < groups && rb0 + 256 * (gi + 2) < Q.V) load(B0, gi + 2);
+    score(B1, gi + 1);
   }
-  const float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
-  const int row = row0 + lane;
-  if (row < Q.V) {
-    const uint32_t key = float_key(mine);
-    keys[(size_t)qn * P.cap + row] = key;
-    atomicAdd(&lh[key >> 20], 1u);
-  }
-  hist_flush(lh, hist + (size_t)qn * kHistBins);
 }
 
 // ---------------------------------------------------------------- vector score
@@ -142,20 +144,17 @@ __global__ __launch_bounds__(256) void k_idx_score_vec(LayerParams P, const void
                                                        const void* __restrict__ qI,
                                                        const float* __restrict__ wt,
                                                        const int32_t* __restrict__ pos, int seq_fixed,
-                                                       int pos0, uint32_t* __restrict__ keys,
-                                                       uint32_t* __restrict__ hist) {
+                                                       int pos0, uint32_t* __restrict__ keys) {
   __shared__ float qh[64 * kMaxDI];
   __shared__ float wsh[64];
   __shared__ float cs_[32], sn_[32];
-  __shared__ uint32_t lh[kHistBins];
   const int qn = blockIdx.y;
   const IdxQuery Q = idx_query(P, pos, seq_fixed, pos0, qn);
   const int rb0 = blockIdx.x * 256;
   if (rb0 >= Q.V) return;
   const int tid = threadIdx.x;
   const int HI = P.HI, DI = P.DI, nrot = P.idx_rot, dn = DI - nrot;
-  if (tid < nrot / 2) rope_cs(P.base, nrot, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
-  for (int e = tid; e < kHistBins; e += 256) lh[e] = 0;
+  if (tid < nrot / 2) rope_cs(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
   if (tid < HI) wsh[tid] = wt[(size_t)qn * HI + tid];
   __syncthreads();
   for (int pe = tid; pe < HI * DI / 2; pe += 256) {
@@ -186,11 +185,8 @@ __global__ __launch_bounds__(256) void k_idx_score_vec(LayerParams P, const void
       for (int c = 0; c < DI; ++c) dot += qh[h * DI + c] * load_val<IDXF>(idx, ro + c);
       s += wsh[h] * (relu ? fmaxf(dot, 0.f) : dot);
     }
-    const uint32_t key = float_key(s);
-    keys[(size_t)qn * P.cap + row] = key;
-    atomicAdd(&lh[key >> 20], 1u);
+    keys[(size_t)qn * P.cap + row] = float_key(s);
   }
-  hist_flush(lh, hist + (size_t)qn * kHistBins);
 }
 
 // ---------------------------------------------------------------- select
@@ -217,14 +213,26 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* wsum, uin
   return before + x - v;
 }
 
-// Histogram sh[0..nb) (nb a multiple of... any <= 4096): find the bin b where
-// the count of keys in bins above b is < need and reaches need including b.
-// Thread t owns the bins nb-(t+1)*per .. nb-t*per-1 (highest bins first).
-__device__ __forceinline__ void find_bin(const uint32_t* sh, int nb, uint32_t need, uint32_t* wsum,
-                                         uint32_t* bc) {
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* wsum) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if (lane == 0) wsum[wave] = v;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int w = 0; w < nw; ++w) t += wsum[w];
+  __syncthreads();
+  return t;
+}
+
+// Histogram sh[0..nb) ascending: find the bin b where the count of keys in
+// bins below b is < need and reaches need including b.  Thread t owns bins
+// t*per .. (t+1)*per-1.  bc[0] = b, bc[1] = count below b.
+__device__ __forceinline__ void find_bin_asc(const uint32_t* sh, int nb, uint32_t need, uint32_t* wsum,
+                                             uint32_t* bc) {
   const int per = (nb + blockDim.x - 1) / blockDim.x;
-  const int hi = nb - threadIdx.x * per;  // exclusive
-  const int lo = max(0, hi - per);
+  const int lo = min(nb, (int)threadIdx.x * per), hi = min(nb, lo + per);
   uint32_t local = 0;
   for (int b = lo; b < hi; ++b) local += sh[b];
   if (threadIdx.x == 0) {  // in-range fallback should the counts disagree
@@ -232,10 +240,10 @@ __device__ __forceinline__ void find_bin(const uint32_t* sh, int nb, uint32_t ne
     bc[1] = 0;
   }
   uint32_t tot;
-  const uint32_t above = block_exscan(local, wsum, &tot);
-  if (above < need && above + local >= need) {
-    uint32_t cum = above;
-    for (int b = hi - 1; b >= lo; --b) {
+  const uint32_t below = block_exscan(local, wsum, &tot);
+  if (below < need && below + local >= need) {
+    uint32_t cum = below;
+    for (int b = lo; b < hi; ++b) {
       if (cum + sh[b] >= need) {
         bc[0] = (uint32_t)b;
         bc[1] = cum;
@@ -247,60 +255,62 @@ __device__ __forceinline__ void find_bin(const uint32_t* sh, int nb, uint32_t ne
   __syncthreads();
 }
 
-// One block of 1024 threads per query.
-__global__ __launch_bounds__(1024) void k_topk_select(LayerParams P, const uint32_t* __restrict__ keys,
-                                                      const uint32_t* __restrict__ hist,
-                                                      const int32_t* __restrict__ pos, int pos0,
-                                                      int32_t* __restrict__ out) {
-  __shared__ uint32_t sh[kHistBins];
-  __shared__ uint32_t wsum[16], wgt[16], weq[16];
-  __shared__ uint32_t bc[2];
-  const int qn = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int k = P.topk;
-  const IdxQuery Q = idx_query(P, pos, 0, pos0, qn);
-  const int V = Q.V;
-  int32_t* o = out + (size_t)qn * k;
-  if (V <= k) {
-    for (int j = tid; j < k; j += blockDim.x) o[j] = j < V ? j : -1;
-    return;
-  }
-  const uint32_t* kq = keys + (size_t)qn * P.cap;
-
-  // level 1: top 12 bits, histogram built by the score kernel
-  for (int e = tid; e < kHistBins; e += blockDim.x) sh[e] = hist[(size_t)qn * kHistBins + e];
-  __syncthreads();
-  uint32_t need = (uint32_t)k;
-  find_bin(sh, kHistBins, need, wsum, bc);
-  uint32_t prefix = bc[0] << 20, mask = 0xfff00000u;
-  need -= bc[1];
-  // levels 2 and 3 over the keys that share the prefix
-#pragma unroll 1
-  for (int lvl = 0; lvl < 2; ++lvl) {
-    const int shift = lvl == 0 ? 8 : 0;
-    const int nb = lvl == 0 ? 4096 : 256;
-    __syncthreads();
-    for (int e = tid; e < nb; e += blockDim.x) sh[e] = 0;
-    __syncthreads();
-    for (int s = tid; s < V; s += blockDim.x) {
-      const uint32_t key = kq[s];
-      if ((key & mask) == prefix) atomicAdd(&sh[(key >> shift) & (nb - 1)], 1u);
+// Radix select over d = M - key.  count_level(shift, nbits, pfx, pmask, sh)
+// must histogram (d >> shift) & ((1 << nbits) - 1) into sh for the keys whose
+// d agrees with pfx on the bits in pmask.  Returns T (the k-th largest key) and
+// sets *need to the number of keys equal to T that are selected.
+template <typename CountLevel>
+__device__ __forceinline__ uint32_t radix_select(uint32_t M, uint32_t k, CountLevel count_level, uint32_t* sh,
+                                                 uint32_t* wsum, uint32_t* bc, uint32_t* need_out) {
+  uint32_t need = k;
+  // level 1: d >> s over d < 2^(s + 10); widen until at least k keys are in range
+  int shift = 14;
+  for (;;) {
+    count_level(shift, 10, 0u, shift + 10 >= 32 ? 0u : ~((1u << (shift + 10)) - 1u), sh);
+    uint32_t tot = 0;
+    {
+      uint32_t part = 0;
+      for (int e = threadIdx.x; e < 1024; e += blockDim.x) part += sh[e];
+      tot = (uint32_t)block_sum_u32(part, wsum);
     }
-    __syncthreads();
-    find_bin(sh, nb, need, wsum, bc);
-    prefix |= bc[0] << shift;
-    mask |= (uint32_t)(nb - 1) << shift;
+    if (tot >= need || shift >= 22) break;
+    shift += 8;
+  }
+  // bins are ascending in d: bin 0 holds the largest keys; find the bin where
+  // the running count (from bin 0 up) reaches `need`
+  find_bin_asc(sh, 1024, need, wsum, bc);
+  uint32_t pfx = bc[0] << shift;
+  uint32_t pmask = ~((1u << shift) - 1u);
+  need -= bc[1];
+  while (shift > 0) {
+    const int nbits = shift < 10 ? shift : 10;
+    shift -= nbits;
+    count_level(shift, nbits, pfx, pmask, sh);
+    find_bin_asc(sh, 1 << nbits, need, wsum, bc);
+    pfx |= bc[0] << shift;
+    pmask |= ((1u << nbits) - 1u) << shift;
     need -= bc[1];
   }
-  const uint32_t T = prefix;  // the k-th largest key; `need` keys equal to it are taken
+  *need_out = need;
+  return M - pfx;
+}
 
-  // ascending emission: each wave walks a contiguous chunk of indices
-  const int nw = blockDim.x >> 6;
-  const int CH = ((V + nw - 1) / nw + 63) / 64 * 64;
-  const int c0 = wave * CH, c1 = min(V, c0 + CH);
+// The selection once the k-th largest key T is known and `need` keys equal to
+// T are to be taken: wave w walks its contiguous chunk [c0, c1) in steps of
+// 64, so indices come out ascending.  key_at(j) returns the key of step j of
+// this lane (index c0 + 64 j + lane).  NS > 0 fixes the step count at compile
+// time (register-resident keys); NS == 0 walks the chunk at run time.
+template <int NS, typename KeyAt>
+__device__ __forceinline__ void emit_selected(KeyAt key_at, int c0, int c1, uint32_t T, uint32_t need,
+                                              int k, int32_t* o, uint32_t* wgt, uint32_t* weq) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nstep = NS > 0 ? NS : (c1 - c0 + 63) / 64;
   uint32_t ngt = 0, neq = 0;
-  for (int b0 = c0; b0 < c1; b0 += 64) {
-    const int s = b0 + lane;
-    const uint32_t key = s < c1 ? kq[s] : 0u;
+#pragma unroll
+  for (int j = 0; j < (NS > 0 ? NS : 1 << 30); ++j) {
+    if (NS == 0 && j >= nstep) break;
+    const int s = c0 + 64 * j + lane;
+    const uint32_t key = s < c1 ? key_at(j) : 0u;
     ngt += __popcll(__ballot(s < c1 && key > T));
     neq += __popcll(__ballot(s < c1 && key == T));
   }
@@ -317,9 +327,11 @@ __global__ __launch_bounds__(1024) void k_topk_select(LayerParams P, const uint3
   uint32_t eq_run = eq_before;
   uint32_t sel_run = gt_before + min(eq_before, need);
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int b0 = c0; b0 < c1; b0 += 64) {
-    const int s = b0 + lane;
-    const uint32_t key = s < c1 ? kq[s] : 0u;
+#pragma unroll
+  for (int j = 0; j < (NS > 0 ? NS : 1 << 30); ++j) {
+    if (NS == 0 && j >= nstep) break;
+    const int s = c0 + 64 * j + lane;
+    const uint32_t key = s < c1 ? key_at(j) : 0u;
     const bool gt = s < c1 && key > T, eq = s < c1 && key == T;
     const unsigned long long eqm = __ballot(eq);
     const uint32_t eq_rank = eq_run + (uint32_t)__popcll(eqm & lt);
@@ -332,23 +344,123 @@ __global__ __launch_bounds__(1024) void k_topk_select(LayerParams P, const uint3
   }
 }
 
-// ---------------------------------------------------------------- launcher
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* wsum) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, 64));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if (lane == 0) wsum[wave] = v;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int w = 0; w < nw; ++w) t = max(t, wsum[w]);
+  __syncthreads();
+  return t;
+}
+
+// Keys of one query held in registers: wave w owns indices [2048 w, 2048 w +
+// 2048), step j of lane l holding index 2048 w + 64 j + l.  V <= 32768.  One
+// block of 1024 threads per query.
+__global__ __launch_bounds__(1024) void k_topk_select_reg(LayerParams P, const uint32_t* __restrict__ keys,
+                                                          const int32_t* __restrict__ pos, int pos0,
+                                                          int32_t* __restrict__ out) {
+  constexpr int KPT = 32;
+  __shared__ uint32_t sh[1024];
+  __shared__ uint32_t wsum[16], wgt[16], weq[16];
+  __shared__ uint32_t bc[2];
+  const int qn = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = P.topk;
+  const IdxQuery Q = idx_query(P, pos, 0, pos0, qn);
+  const int V = Q.V;
+  int32_t* o = out + (size_t)qn * k;
+  if (V <= k) {
+    for (int j = tid; j < k; j += blockDim.x) o[j] = j < V ? j : -1;
+    return;
+  }
+  const uint32_t* kq = keys + (size_t)qn * P.cap;
+  const int c0 = wave * (KPT * 64);
+  uint32_t kr[KPT];
+  uint32_t mloc = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int s = c0 + 64 * j + lane;
+    kr[j] = s < V ? kq[s] : 0u;
+    mloc = max(mloc, kr[j]);
+  }
+  const uint32_t M = block_max_u32(mloc, wsum);
+  auto count_level = [&](int shift, int nbits, uint32_t pfx, uint32_t pmask, uint32_t* h) {
+    const uint32_t nb = 1u << nbits;
+    for (int e = tid; e < (int)nb; e += blockDim.x) h[e] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t d = M - kr[j];
+      if (c0 + 64 * j + lane < V && (d & pmask) == pfx) atomicAdd(&h[(d >> shift) & (nb - 1u)], 1u);
+    }
+    __syncthreads();
+  };
+  uint32_t need;
+  const uint32_t T = radix_select(M, (uint32_t)k, count_level, sh, wsum, bc, &need);
+  const int c1 = min(V, c0 + KPT * 64);
+  emit_selected<KPT>([&](int j) -> uint32_t { return kr[j]; }, c0, max(c0, c1), T, need, k, o, wgt, weq);
+}
+
+// Any V: the same selection streaming the keys from memory.  Wave w owns the
+// contiguous chunk [c0, c1).  One block of 1024 threads per query.
+__global__ __launch_bounds__(1024) void k_topk_select(LayerParams P, const uint32_t* __restrict__ keys,
+                                                      const int32_t* __restrict__ pos, int pos0,
+                                                      int32_t* __restrict__ out) {
+  __shared__ uint32_t sh[1024];
+  __shared__ uint32_t wsum[16], wgt[16], weq[16];
+  __shared__ uint32_t bc[2];
+  const int qn = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = P.topk;
+  const IdxQuery Q = idx_query(P, pos, 0, pos0, qn);
+  const int V = Q.V;
+  int32_t* o = out + (size_t)qn * k;
+  if (V <= k) {
+    for (int j = tid; j < k; j += blockDim.x) o[j] = j < V ? j : -1;
+    return;
+  }
+  const uint32_t* kq = keys + (size_t)qn * P.cap;
+  const int CH = ((V + 15) / 16 + 63) / 64 * 64;
+  const int c0 = min(V, wave * CH), c1 = min(V, c0 + CH);
+  uint32_t mloc = 0;
+  for (int s = c0 + lane; s < c1; s += 64) mloc = max(mloc, kq[s]);
+  const uint32_t M = block_max_u32(mloc, wsum);
+  auto count_level = [&](int shift, int nbits, uint32_t pfx, uint32_t pmask, uint32_t* h) {
+    const uint32_t nb = 1u << nbits;
+    for (int e = tid; e < (int)nb; e += blockDim.x) h[e] = 0;
+    __syncthreads();
+    for (int s = c0 + lane; s < c1; s += 64) {
+      const uint32_t d = M - kq[s];
+      if ((d & pmask) == pfx) atomicAdd(&h[(d >> shift) & (nb - 1u)], 1u);
+    }
+    __syncthreads();
+  };
+  uint32_t need;
+  const uint32_t T = radix_select(M, (uint32_t)k, count_level, sh, wsum, bc, &need);
+  emit_selected<0>([&](int j) -> uint32_t { return kq[c0 + 64 * j + lane]; }, c0, c1, T, need, k, o, wgt,
+                   weq);
+}
+
+// ---------------------------------------------------------------- launchers
 
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
-                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
-                   int32_t* topk, void* stream) {
+                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, int32_t* topk,
+                   void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  const size_t nh = (size_t)nq * kHistBins;
-  const size_t fb = (nh + 255) / 256;
-  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)(fb < 1024 ? fb : 1024)), dim3(256), 0, st, hist, nh, 0u);
-  launch_idx_score(P, c, qI, w, pos, seq, pos0, nq, keys, hist, stream);
-  hipLaunchKernelGGL(k_topk_select, dim3(nq), dim3(1024), 0, st, P, keys, hist, pos, pos0, topk);
+  launch_idx_score(P, c, qI, w, pos, seq, pos0, nq, keys, stream);
+  const int vlast = (pos0 + nq) / 4;
+  const int vmax = pos ? P.cap : (vlast < P.cap ? vlast : P.cap);
+  if (vmax <= 32768)
+    hipLaunchKernelGGL(k_topk_select_reg, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);
+  else
+    hipLaunchKernelGGL(k_topk_select, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);
   return (int)hipGetLastError();
 }
 
 int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const float* w,
-                     const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
-                     void* stream) {
+                     const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   // rows to cover: decode -> the whole capacity; prefill -> rows visible to the last query
   const int vlast = (pos0 + nq) / 4;
@@ -358,9 +470,11 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
   if (mf) {
     const uint16_t* ix = (const uint16_t*)c.idx;
     const int MT = (P.HI + 15) / 16;
-#define CKV_IS(MTV, QF)                                                                          \
-  hipLaunchKernelGGL((k_idx_score_mfma<MTV, 4, QF>), grid, dim3(256), 0, st, P, ix, qI, w, pos, seq, \
-                     pos0, keys, hist)
+    const int groups = 4;
+    dim3 mgrid((unsigned)(vmax > 0 ? (vmax + 256 * groups - 1) / (256 * groups) : 1), nq);
+#define CKV_IS(MTV, QF)                                                                           \
+  hipLaunchKernelGGL((k_idx_score_mfma<MTV, 4, QF>), mgrid, dim3(256), 0, st, P, ix, qI, w, pos, seq, \
+                     pos0, groups, keys)
     if (P.act_fmt == CKV_BF16) {
       if (MT == 1) CKV_IS(1, CKV_BF16);
       else if (MT == 2) CKV_IS(2, CKV_BF16);
@@ -374,9 +488,8 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
     }
 #undef CKV_IS
   } else {
-#define CKV_IV(IF, QF)                                                                               \
-  hipLaunchKernelGGL((k_idx_score_vec<IF, QF>), grid, dim3(256), 0, st, P, c.idx, qI, w, pos, seq, pos0, \
-                     keys, hist)
+#define CKV_IV(IF, QF) \
+  hipLaunchKernelGGL((k_idx_score_vec<IF, QF>), grid, dim3(256), 0, st, P, c.idx, qI, w, pos, seq, pos0, keys)
     if (P.idx_fmt == CKV_F32 && P.act_fmt == CKV_F32) CKV_IV(CKV_F32, CKV_F32);
     else if (P.idx_fmt == CKV_F32) CKV_IV(CKV_F32, CKV_BF16);
     else if (P.act_fmt == CKV_F32) CKV_IV(CKV_BF16, CKV_F32);

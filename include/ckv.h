@@ -239,13 +239,11 @@ int ckv_indexer_topk_decode(const ckv_layer_desc* desc, const ckv_layer_cache* c
  * s < V of sequence b, keys[b * comp_cap + s] receives the order-preserving
  * 32-bit image of I(s): a non-negative score's float bits with the top bit
  * set, a negative score's bits inverted (-0 counts as +0), so keys compare
- * like the scores.  hist [B, 4096] uint32 must hold zeros on entry and
- * receives, per sequence, the number of keys with each value of their top 12
- * bits.  keys [B, comp_cap] uint32; other arguments as for the decode call.
- * Rows >= V are left untouched. */
+ * like the scores.  keys [B, comp_cap] uint32; other arguments as for the
+ * decode call.  Rows >= V are left untouched. */
 int ckv_indexer_score_decode(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
                              const void* qI, const float* w, const int32_t* pos, int32_t B,
-                             uint32_t* keys, uint32_t* hist, void* stream);
+                             uint32_t* keys, void* stream);
 int ckv_indexer_topk_prefill(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
                              const void* qI, const float* w, int32_t seq, int32_t pos0, int32_t T,
                              int32_t* topk, void* ws, size_t ws_bytes, void* stream);

@@ -295,3 +295,29 @@ def test_c4_prefill_chunk_sampled():
         assert sets_equal(tkg[n], O.topk_select(sc, cfg.top_k)), f"top-k of query {n}"
         ref = seq.attend(p, inp.q[n], tkg[n])
         assert_close(og[n], ref, BF16_TOL, f"output of query {n}")
+
+
+def test_indexer_score_stage_keys():
+    """ckv_indexer_score_decode alone: keys decode to the oracle's scores."""
+    from compressed_kv_sparse_amd import _lib as L
+    cfg = get_config("c5").with_(batch=4, comp_cap=4096, seed=31, name="score_stage")
+    inp = make_decode_inputs(cfg, n_ctx=np.array([16384, 9001, 4100, 333]))
+    wts = make_layer_weights(cfg)
+    dl = device_layer(cfg, wts, inp.cache)
+    keys = torch.zeros((cfg.batch, cfg.comp_cap), dtype=torch.int32, device="cuda")
+    rc = L.indexer_score_decode(dl.desc, dl.cache, dev(inp.qI), dev(inp.w), dev(inp.pos), cfg.batch, keys,
+                                torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    kg = cpu(keys).view(np.uint32)
+    Lo = oracle_layer(cfg, wts)
+    for b in range(cfg.batch):
+        p = int(inp.pos[b])
+        V = (p + 1) // 4
+        k = kg[b, :V]
+        bits = np.where(k & 0x80000000, k & 0x7FFFFFFF, ~k).astype(np.uint32)
+        sc = bits.view(np.float32).astype(np.float64)
+        seq = oracle_seq_from_bytes(Lo, cpu(dl.raw)[b], cpu(dl.comp)[b], cpu(dl.idx)[b], p + 1)
+        ref = seq.index_scores(p, inp.qI[b], inp.w[b])
+        assert np.max(np.abs(sc - ref)) <= 1e-4 * np.max(np.abs(ref)), f"scores b={b}"
+        assert np.all(kg[b, V:] == 0)      # rows beyond V untouched
