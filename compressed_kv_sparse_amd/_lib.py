@@ -85,6 +85,8 @@ def _load() -> ctypes.CDLL:
     lib.ckv_last_hip_error.restype = ctypes.c_char_p
     lib.ckv_workspace_bytes.argtypes = [D, I32, I32]
     lib.ckv_workspace_bytes.restype = SZ
+    lib.ckv_workspace_sync_bytes.argtypes = [D, I32, I32]
+    lib.ckv_workspace_sync_bytes.restype = SZ
     sig = {
         "ckv_compress_append_decode": [D, Wt, C, VP, VP, VP, I32, VP, SZ, VP],
         "ckv_compress_append_prefill": [D, Wt, C, VP, VP, I32, I32, I32, VP, SZ, VP],
@@ -104,6 +106,7 @@ def _load() -> ctypes.CDLL:
 lib = _load()
 
 EXPORTS = ("ckv_row_bytes", "ckv_validate", "ckv_strerror", "ckv_last_hip_error", "ckv_workspace_bytes",
+           "ckv_workspace_sync_bytes",
            "ckv_compress_append_decode", "ckv_compress_append_prefill", "ckv_indexer_topk_decode",
            "ckv_indexer_topk_prefill", "ckv_indexer_score_decode", "ckv_sparse_swa_attn_decode",
            "ckv_sparse_swa_attn_prefill")
@@ -123,6 +126,10 @@ def validate(desc: LayerDesc) -> int:
 
 def workspace_bytes(desc: LayerDesc, mode: int, n: int) -> int:
     return int(lib.ckv_workspace_bytes(ctypes.byref(desc), mode, n))
+
+
+def workspace_sync_bytes(desc: LayerDesc, mode: int, n: int) -> int:
+    return int(lib.ckv_workspace_sync_bytes(ctypes.byref(desc), mode, n))
 
 
 def _p(x) -> int:

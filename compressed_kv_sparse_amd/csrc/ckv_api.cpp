@@ -161,8 +161,8 @@ extern "C" int ckv_indexer_topk_decode(const ckv_layer_desc* desc, const ckv_lay
   if ((rc = check_ws(P, CKV_MODE_DECODE, B, ws, ws_bytes, &L))) return rc;
   clear_stale();
   uint8_t* wb = (uint8_t*)ws;
-  return launched(launch_indexer(P, to_cache(cache), qI, w, pos, 0, 0, B, (uint32_t*)(wb + L.keys), topk,
-                                 stream));
+  return launched(launch_indexer(P, to_cache(cache), qI, w, pos, 0, 0, B, (uint32_t*)(wb + L.keys),
+                                 (uint32_t*)(wb + L.hist), topk, stream));
 }
 
 extern "C" int ckv_indexer_score_decode(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
@@ -176,7 +176,7 @@ extern "C" int ckv_indexer_score_decode(const ckv_layer_desc* desc, const ckv_la
   if (B > P.batch) return CKV_E_CAPACITY;
   if (check_ptr(qI) || check_ptr(w) || check_ptr(pos) || check_ptr(keys)) return CKV_E_INVAL;
   clear_stale();
-  return launched(launch_idx_score(P, to_cache(cache), qI, w, pos, 0, 0, B, keys, stream));
+  return launched(launch_idx_score(P, to_cache(cache), qI, w, pos, 0, 0, B, keys, nullptr, stream));
 }
 
 extern "C" int ckv_indexer_topk_prefill(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
@@ -195,7 +195,7 @@ extern "C" int ckv_indexer_topk_prefill(const ckv_layer_desc* desc, const ckv_la
   clear_stale();
   uint8_t* wb = (uint8_t*)ws;
   return launched(launch_indexer(P, to_cache(cache), qI, w, nullptr, seq, pos0, T,
-                                 (uint32_t*)(wb + L.keys), topk, stream));
+                                 (uint32_t*)(wb + L.keys), nullptr, topk, stream));
 }
 
 extern "C" int ckv_sparse_swa_attn_decode(const ckv_layer_desc* desc, const ckv_layer_cache* cache,

@@ -10,6 +10,7 @@
 namespace ckv {
 
 constexpr int kMaxD = 512;
+constexpr int kHistBins = 4096;   // top-k histogram of the keys' top 12 bits
 constexpr int kMaxSplits = 256;   // attention partial results merged per query
 constexpr int kMaxDI = 128;
 
@@ -52,8 +53,13 @@ struct Cache {
   uint32_t* status;
 };
 
-// Workspace carve-up (all offsets 256-byte aligned).
+// Workspace carve-up (all offsets 256-byte aligned).  The sync region comes
+// first in every mode: counters and histograms that must hold zeros before a
+// call and that every call leaves at zero.
 struct WsLayout {
+  size_t sync;      // zero-kept region: uint32 hist [n][kHistBins] (ratio 4)
+  size_t sync_bytes;
+  size_t hist;      // offset of the histograms inside the sync region
   size_t proj;      // float [proj_splits][n][ncol]
   size_t keys;      // uint32 [n][cap]   indexer keys
   size_t part_o;    // float [n][splits][H][d]  attention partial outputs
@@ -79,10 +85,12 @@ int launch_compress_prefill(const LayerParams& P, const Weights& w, const Cache&
 // indexer: decode (pos != NULL, query b of sequence b) or prefill (pos == NULL,
 // query n of sequence seq at position pos0 + n)
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
-                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, int32_t* topk,
-                   void* stream);
+                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
+                   int32_t* topk, void* stream);
+// hist may be NULL: scores only
 int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const float* w,
-                     const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, void* stream);
+                     const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
+                     void* stream);
 int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32_t* pos, int seq,
                 int pos0, int nq, const int32_t* topk, void* out, const WsLayout& L, uint8_t* ws,
                 void* stream);

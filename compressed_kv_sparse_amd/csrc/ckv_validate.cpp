@@ -63,7 +63,8 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   memset(&L, 0, sizeof(L));
   const bool prefill = mode == CKV_MODE_PREFILL;
   const bool proj_mfma = P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16;
-  L.proj_splits = (!prefill && proj_mfma) ? (P.hidden >= 1024 ? P.hidden / 512 : 1) : 1;
+  // decode projection: split K so each wave's loads (256 K-values) are in flight at once
+  L.proj_splits = (!prefill && proj_mfma) ? (P.hidden >= 512 ? P.hidden / 256 : 1) : 1;
   const int rows = attn_max_rows(P);
   int rps;
   if (attn_is_mfma(P)) {
@@ -85,6 +86,12 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   L.attn_rows_per_split = rps;
   L.attn_splits = (rows + rps - 1) / rps;
   size_t off = 0;
+  // sync region: per-sequence top-k histograms of decode calls, sized by the
+  // cache batch so that the same bytes are reserved in every mode
+  L.sync = 0;
+  L.hist = 0;
+  if (P.ratio == 4) off += align256((size_t)P.batch * kHistBins * sizeof(uint32_t));
+  L.sync_bytes = off;
   L.proj = off;
   off += align256((size_t)L.proj_splits * n * P.ncol * sizeof(float));
   L.keys = off;
@@ -149,6 +156,14 @@ extern "C" const char* ckv_strerror(int code) {
     case CKV_E_HIP: return "HIP kernel launch failed";
     default: return "unknown error";
   }
+}
+
+extern "C" size_t ckv_workspace_sync_bytes(const ckv_layer_desc* d, int32_t mode, int32_t n) {
+  if (ckv_validate(d) != CKV_OK || n <= 0) return 0;
+  if (mode != CKV_MODE_DECODE && mode != CKV_MODE_PREFILL) return 0;
+  LayerParams P;
+  make_params(d, &P);
+  return ws_layout(P, mode, n).sync_bytes;
 }
 
 extern "C" size_t ckv_workspace_bytes(const ckv_layer_desc* d, int32_t mode, int32_t n) {

@@ -113,10 +113,21 @@ __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, cons
   if (tid == 0) tk_lim = tkg ? P.topk : 0;
   __syncthreads();
   if (tkg) {
-    for (int j = tid; j < P.topk; j += 256) {
-      const int v = tkg[j];
-      tks[j] = v;
-      if (v >= A.V) atomicMin(&tk_lim, j);
+    for (int j0 = 0; j0 < P.topk; j0 += 256 * 4) {   // four loads per thread in flight
+      int v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + tid + 256 * e;
+        v[e] = j < P.topk ? tkg[j] : -1;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + tid + 256 * e;
+        if (j < P.topk) {
+          tks[j] = v[e];
+          if (v[e] >= A.V) atomicMin(&tk_lim, j);
+        }
+      }
     }
   }
   if (tid < 32) rope_cs(P, tid, (double)A.p, &cs_[tid], &sn_[tid]);
@@ -183,14 +194,13 @@ __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, cons
       for (int h = 0; h < 2; ++h) {
         v[h] = stg[e][h];
         if (KVF == CKV_E4M3 && 8 * c8 < DN) {
+          // OCP E4M3 codes -> their exact bf16 values, two per conversion
           const uint32_t w0 = v[h][0], w1 = v[h][1];
           u32x4 t;
-#pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            const uint32_t word = f < 2 ? w0 : w1;
-            const uint32_t b0 = (word >> (16 * (f & 1))) & 0xffu, b1 = (word >> (16 * (f & 1) + 8)) & 0xffu;
-            t[f] = (__float_as_uint(e4m3_to_f32(b0)) >> 16) | (__float_as_uint(e4m3_to_f32(b1)) & 0xffff0000u);
-          }
+          t[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+          t[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+          t[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+          t[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
           v[h] = t;
         }
         *(u32x4*)&Ks[(2 * pr + h) * KP + 8 * c8] = v[h];
@@ -267,16 +277,23 @@ __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, cons
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[nt][i] = rs < 0.f ? -INFINITY : (a1[i] * rs + a2[i]) * scale;
     }
-    // online softmax per head 4g+i (rows spread over the 16 lanes of group g)
+    // online softmax per head 4g+i (rows spread over the 16 lanes of group g).
+    // The reference max m_i moves only when a tile's max exceeds it by more
+    // than 8 (probabilities stay below e^8, safe in fp32 and bf16), so the
+    // rescale of the 128 accumulators is rare; the result does not depend on
+    // the reference chosen.
     float alpha[4];
+    bool moved = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float mx = fmaxf(S[0][i], S[1][i]);
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      const float mn = fmaxf(m_i[i], mx);
+      const bool move = mx > m_i[i] + 8.f;
+      const float mn = move ? mx : m_i[i];
       const bool none = mn == -INFINITY;
-      alpha[i] = none ? 1.f : __expf(m_i[i] - mn);
+      alpha[i] = (none || !move) ? 1.f : __expf(m_i[i] - mn);
+      moved |= move && !none;
       float ps = 0.f;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -289,10 +306,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, cons
       l_i[i] = l_i[i] * alpha[i] + ps;
       m_i[i] = mn;
     }
+    if (__ballot(moved)) {
 #pragma unroll
-    for (int n = 0; n < NO; ++n)
+      for (int n = 0; n < NO; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) O[n][i] *= alpha[i];
+        for (int i = 0; i < 4; ++i) O[n][i] *= alpha[i];
+    }
     // probabilities -> LDS as the A operand [16 heads][32 rows], split hi + lo
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -475,14 +494,21 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
   __syncthreads();
   if (c >= d) return;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sidx = 0; sidx < nsplit; ++sidx) {
-    const float wgt = wsh[sidx];
-    if (wgt == 0.f) continue;
-    const float4 v = *(const float4*)(part_o + (b0 + (size_t)sidx * H) * d + c);
-    a.x += v.x * wgt;
-    a.y += v.y * wgt;
-    a.z += v.z * wgt;
-    a.w += v.w * wgt;
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {   // eight splits' loads in flight at a time
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s0 + j < nsplit && wsh[s0 + j] != 0.f) v[j] = *(const float4*)(part_o + (b0 + (size_t)(s0 + j) * H) * d + c);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float wgt = s0 + j < nsplit ? wsh[s0 + j] : 0.f;
+      a.x += v[j].x * wgt;
+      a.y += v[j].y * wgt;
+      a.z += v[j].z * wgt;
+      a.w += v[j].w * wgt;
+    }
   }
   const float inv = Lsh > 0.f ? 1.f / Lsh : 0.f;
   float o[4] = {a.x * inv, a.y * inv, a.z * inv, a.w * inv};

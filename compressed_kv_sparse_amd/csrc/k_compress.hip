@@ -162,7 +162,9 @@ __device__ __forceinline__ float2 pool2(const float* skv, const float* ssc, cons
 
 // One block per sequence; thread t owns channels (2t, 2t+1) of the attention
 // lane and, on ratio 4, of the indexer lane.  part: projection partials
-// [splits][B][ncol], summed here in split order.
+// [splits][B][ncol], summed here in split order.  Every load is issued before
+// the first barrier: this token's inputs (independent of the position), then
+// the window ring, APE and gamma; the stores follow.
 template <int KVF, int IDXF, int ACTF>
 __global__ __launch_bounds__(256) void k_compress_decode(LayerParams P, Weights w, Cache cc,
                                                          const void* __restrict__ u,
@@ -171,37 +173,62 @@ __global__ __launch_bounds__(256) void k_compress_decode(LayerParams P, Weights 
                                                          int splits, int B) {
   __shared__ float red[16];
   const int b = blockIdx.x;
-  const int p = pos[b];
-  if (p < 0) {
-    if (threadIdx.x == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_BAD_POS);
-    return;
-  }
   const int d = P.d, r = P.ratio, W = P.W, DI = P.DI;
   const int c = 2 * threadIdx.x;
   const bool act = c < d;
   const bool iact = r == 4 && c < DI;
-  const bool emit = r != 0 && (p + 1) % r == 0;
-  const int i = emit ? (p + 1) / r - 1 : 0;
-  if (emit && i >= P.cap && threadIdx.x == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_CAPACITY);
-  const bool pool = emit && i < P.cap;
 
   // this token's inputs
   const float2 uu = act ? load2<ACTF>(u, (long)b * d + c) : make_float2(0.f, 0.f);
   float2 ka = make_float2(0.f, 0.f), sa = ka, kia = ka, sia = ka;
   const size_t pstride = (size_t)B * P.ncol;
   const float* pb = part + (size_t)b * P.ncol;
-  if (r && act) {
-    for (int s = 0; s < splits; ++s) {
-      const float2 a = ld2(pb + s * pstride + c), g = ld2(pb + s * pstride + d + c);
-      ka.x += a.x; ka.y += a.y;
-      sa.x += g.x; sa.y += g.y;
+  // split-K partials, eight splits' loads in flight at a time, summed in split order
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    float2 a[8], g[8], ai[8], gi[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool in = s0 + j < splits;
+      const float* q = pb + (size_t)(s0 + j) * pstride;
+      a[j] = g[j] = ai[j] = gi[j] = make_float2(0.f, 0.f);
+      if (in && r && act) {
+        a[j] = ld2(q + c);
+        g[j] = ld2(q + d + c);
+      }
+      if (in && iact) {
+        ai[j] = ld2(q + 2 * d + c);
+        gi[j] = ld2(q + 2 * d + DI + c);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ka.x += a[j].x; ka.y += a[j].y;
+      sa.x += g[j].x; sa.y += g[j].y;
+      kia.x += ai[j].x; kia.y += ai[j].y;
+      sia.x += gi[j].x; sia.y += gi[j].y;
     }
   }
-  if (iact) {
-    for (int s = 0; s < splits; ++s) {
-      const float2 a = ld2(pb + s * pstride + 2 * d + c), g = ld2(pb + s * pstride + 2 * d + DI + c);
-      kia.x += a.x; kia.y += a.y;
-      sia.x += g.x; sia.y += g.y;
+  const int p = pos[b];
+  if (p < 0) {
+    if (threadIdx.x == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_BAD_POS);
+    return;
+  }
+  const bool emit = r != 0 && (p + 1) % r == 0;
+  const int i = emit ? (p + 1) / r - 1 : 0;
+  if (emit && i >= P.cap && threadIdx.x == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_CAPACITY);
+  const bool pool = emit && i < P.cap;
+
+  // window pooling (reads only other tokens' ring slots) and the norm weights
+  float2 y = make_float2(0.f, 0.f), yi = y, gm = y, gmi = y;
+  if (pool) {
+    if (act) {
+      y = pool2(cc.st_kv + (size_t)b * W * d, cc.st_sc + (size_t)b * W * d, w.ape, d, W, r, i, p, ka, sa, c);
+      gm = ld2(w.gamma + c);
+    }
+    if (iact) {
+      yi = pool2(cc.ist_kv + (size_t)b * 8 * DI, cc.ist_sc + (size_t)b * 8 * DI, w.idx_ape, DI, 8, 4, i, p, kia,
+                 sia, c);
+      gmi = ld2(w.idx_gamma + c);
     }
   }
 
@@ -209,16 +236,7 @@ __global__ __launch_bounds__(256) void k_compress_decode(LayerParams P, Weights 
   store_row2<KVF>(cc.raw + ((size_t)b * P.swa + p % P.swa) * P.row_bytes, rope2(P, uu, c, d, P.n_rot, p), c,
                   act, d, P.n_rot, red);
   if (r == 0) return;
-
-  float2 y, yi;
-  if (pool) {
-    if (act)
-      y = pool2(cc.st_kv + (size_t)b * W * d, cc.st_sc + (size_t)b * W * d, w.ape, d, W, r, i, p, ka, sa, c);
-    if (iact)
-      yi = pool2(cc.ist_kv + (size_t)b * 8 * DI, cc.ist_sc + (size_t)b * 8 * DI, w.idx_ape, DI, 8, 4, i, p, kia,
-                 sia, c);
-  }
-  // this token's projections -> state slot p % W (slots the pooling read are other tokens')
+  // this token's projections -> state slot p % W
   if (act) {
     const size_t o = ((size_t)b * W + p % W) * d + c;
     *(float2*)(cc.st_kv + o) = ka;
@@ -236,18 +254,14 @@ __global__ __launch_bounds__(256) void k_compress_decode(LayerParams P, Weights 
     const float ss = block_sum(act ? y.x * y.x + y.y * y.y : 0.f, red);
     const float inv = 1.0f / sqrtf(ss / (float)d + P.eps);
     float2 z = make_float2(0.f, 0.f);
-    if (act) {
-      const float2 gm = ld2(w.gamma + c);
-      z = rope2(P, make_float2(gm.x * (y.x * inv), gm.y * (y.y * inv)), c, d, P.n_rot, (double)i * r);
-    }
+    if (act) z = rope2(P, make_float2(gm.x * (y.x * inv), gm.y * (y.y * inv)), c, d, P.n_rot, (double)i * r);
     store_row2<KVF>(cc.comp + ((size_t)b * P.cap + i) * P.row_bytes, z, c, act, d, P.n_rot, red);
   }
   if (r == 4) {  // indexer lane: its own compressor of the same form
     const float ss = block_sum(iact ? yi.x * yi.x + yi.y * yi.y : 0.f, red);
     const float inv = 1.0f / sqrtf(ss / (float)DI + P.eps);
     if (iact) {
-      const float2 gm = ld2(w.idx_gamma + c);
-      const float2 z = rope2(P, make_float2(gm.x * (yi.x * inv), gm.y * (yi.y * inv)), c, DI, P.idx_rot,
+      const float2 z = rope2(P, make_float2(gmi.x * (yi.x * inv), gmi.y * (yi.y * inv)), c, DI, P.idx_rot,
                              (double)i * r);
       uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * DI * (IDXF == CKV_F32 ? 4 : 2);
       if (IDXF == CKV_F32) *(float2*)(dst + 4 * c) = z;

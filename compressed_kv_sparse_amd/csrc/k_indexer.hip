@@ -41,12 +41,14 @@ __global__ __launch_bounds__(256) void k_idx_score_mfma(LayerParams P, const uin
                                                         const void* __restrict__ qI,
                                                         const float* __restrict__ wt,
                                                         const int32_t* __restrict__ pos, int seq_fixed,
-                                                        int pos0, int groups, uint32_t* __restrict__ keys) {
+                                                        int pos0, int groups, uint32_t* __restrict__ keys,
+                                                        uint32_t* __restrict__ hist) {
   constexpr int DI = KS * 32;
   constexpr int HP = MT * 16;
   __shared__ __attribute__((aligned(16))) uint16_t qh[HP * DI];
   __shared__ float wsh[HP];
   __shared__ float cs_[32], sn_[32];
+  __shared__ uint32_t lh[kHistBins];
   const int qn = blockIdx.y;
   const IdxQuery Q = idx_query(P, pos, seq_fixed, pos0, qn);
   const int rb0 = blockIdx.x * 256 * groups;
@@ -71,23 +73,35 @@ __global__ __launch_bounds__(256) void k_idx_score_mfma(LayerParams P, const uin
   };
   u32x4 B0[4][KS], B1[4][KS];
   load(B0, 0);
+  // this thread's share of the query, loaded together with the first rows
+  constexpr int NPAIR = HP * DI / 2 / 256;
+  float qa[NPAIR], qb[NPAIR];
+#pragma unroll
+  for (int e = 0; e < NPAIR; ++e) {
+    const int pe = tid + 256 * e, h = pe / (DI / 2), c = 2 * (pe % (DI / 2));
+    qa[e] = qb[e] = 0.f;
+    if (h < HI) {
+      const size_t o = ((size_t)qn * HI + h) * DI + c;
+      qa[e] = load_val<QF>(qI, o);
+      qb[e] = load_val<QF>(qI, o + 1);
+    }
+  }
 
   if (tid < nrot / 2) rope_cs(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
   if (tid < HP) wsh[tid] = tid < HI ? wt[(size_t)qn * HI + tid] : 0.f;
+  if (hist)
+    for (int e = tid; e < kHistBins; e += 256) lh[e] = 0;
   __syncthreads();
-  for (int pe = tid; pe < HP * DI / 2; pe += 256) {
-    const int h = pe / (DI / 2), c = 2 * (pe % (DI / 2));
-    float a = 0.f, b = 0.f;
-    if (h < HI) {
-      const size_t o = ((size_t)qn * HI + h) * DI + c;
-      a = load_val<QF>(qI, o);
-      b = load_val<QF>(qI, o + 1);
-      if (c >= dn) {
-        const int j = (c - dn) >> 1;
-        const float x = a * cs_[j] - b * sn_[j], y = a * sn_[j] + b * cs_[j];
-        a = x;
-        b = y;
-      }
+  // rotated query -> bf16 in LDS
+#pragma unroll
+  for (int e = 0; e < NPAIR; ++e) {
+    const int pe = tid + 256 * e, h = pe / (DI / 2), c = 2 * (pe % (DI / 2));
+    float a = qa[e], b = qb[e];
+    if (c >= dn) {
+      const int j = (c - dn) >> 1;
+      const float x = a * cs_[j] - b * sn_[j], y = a * sn_[j] + b * cs_[j];
+      a = x;
+      b = y;
     }
     ((uint32_t*)qh)[(h * DI + c) >> 1] = pack_bf16x2(a, b);
   }
@@ -124,7 +138,11 @@ __global__ __launch_bounds__(256) void k_idx_score_mfma(LayerParams P, const uin
     }
     const float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
     const int row = rb0 + 256 * gi + wave * 64 + lane;
-    if (row < Q.V) kout[row] = float_key(mine);
+    if (row < Q.V) {
+      const uint32_t key = float_key(mine);
+      kout[row] = key;
+      if (hist) atomicAdd(&lh[key >> 20], 1u);
+    }
   };
   for (int gi = 0; gi < groups; gi += 2) {
     if (rb0 + 256 * gi >= Q.V) break;
@@ -135,6 +153,14 @@ __global__ __launch_bounds__(256) void k_idx_score_mfma(LayerParams P, const uin
     if (gi + 2 < groups && rb0 + 256 * (gi + 2) < Q.V) load(B0, gi + 2);
     score(B1, gi + 1);
   }
+  if (hist) {  // this block's key histogram into the query's
+    __syncthreads();
+    uint32_t* gh = hist + (size_t)qn * kHistBins;
+    for (int e = tid; e < kHistBins; e += 256) {
+      const uint32_t v = lh[e];
+      if (v) atomicAdd(&gh[e], v);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- vector score
@@ -144,10 +170,12 @@ __global__ __launch_bounds__(256) void k_idx_score_vec(LayerParams P, const void
                                                        const void* __restrict__ qI,
                                                        const float* __restrict__ wt,
                                                        const int32_t* __restrict__ pos, int seq_fixed,
-                                                       int pos0, uint32_t* __restrict__ keys) {
+                                                       int pos0, uint32_t* __restrict__ keys,
+                                                       uint32_t* __restrict__ hist) {
   __shared__ float qh[64 * kMaxDI];
   __shared__ float wsh[64];
   __shared__ float cs_[32], sn_[32];
+  __shared__ uint32_t lh[kHistBins];
   const int qn = blockIdx.y;
   const IdxQuery Q = idx_query(P, pos, seq_fixed, pos0, qn);
   const int rb0 = blockIdx.x * 256;
@@ -156,6 +184,8 @@ __global__ __launch_bounds__(256) void k_idx_score_vec(LayerParams P, const void
   const int HI = P.HI, DI = P.DI, nrot = P.idx_rot, dn = DI - nrot;
   if (tid < nrot / 2) rope_cs(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
   if (tid < HI) wsh[tid] = wt[(size_t)qn * HI + tid];
+  if (hist)
+    for (int e = tid; e < kHistBins; e += 256) lh[e] = 0;
   __syncthreads();
   for (int pe = tid; pe < HI * DI / 2; pe += 256) {
     const int h = pe / (DI / 2), c = 2 * (pe % (DI / 2));
@@ -185,7 +215,17 @@ __global__ __launch_bounds__(256) void k_idx_score_vec(LayerParams P, const void
       for (int c = 0; c < DI; ++c) dot += qh[h * DI + c] * load_val<IDXF>(idx, ro + c);
       s += wsh[h] * (relu ? fmaxf(dot, 0.f) : dot);
     }
-    keys[(size_t)qn * P.cap + row] = float_key(s);
+    const uint32_t key = float_key(s);
+    keys[(size_t)qn * P.cap + row] = key;
+    if (hist) atomicAdd(&lh[key >> 20], 1u);
+  }
+  if (hist) {
+    __syncthreads();
+    uint32_t* gh = hist + (size_t)qn * kHistBins;
+    for (int e = tid; e < kHistBins; e += 256) {
+      const uint32_t v = lh[e];
+      if (v) atomicAdd(&gh[e], v);
+    }
   }
 }
 
@@ -443,16 +483,177 @@ __global__ __launch_bounds__(1024) void k_topk_select(LayerParams P, const uint3
                    weq);
 }
 
+// Decode selection driven by the score kernel's histogram of the keys' top 12
+// bits (V <= 32768, keys in registers as in k_topk_select_reg).  The bin
+// holding the k-th largest key is read off the histogram; its keys (a few
+// percent of V) are gathered into LDS, where two more levels (bits 19..8, then
+// 7..0) fix the k-th key exactly.  The histogram is zeroed again for the next
+// call.  If the bin holds more keys than the LDS list takes, the register
+// radix select runs instead.
+__global__ __launch_bounds__(1024) void k_topk_select_hist(LayerParams P, const uint32_t* __restrict__ keys,
+                                                           uint32_t* __restrict__ hist,
+                                                           const int32_t* __restrict__ pos,
+                                                           int32_t* __restrict__ out) {
+  constexpr int KPT = 32;
+  constexpr int CAP = 6144;          // candidate keys gathered into LDS
+  __shared__ uint32_t sh[kHistBins];
+  __shared__ uint32_t cand[CAP];
+  __shared__ uint32_t wsum[16], wgt[16], weq[16];
+  __shared__ uint32_t bc[2];
+  __shared__ uint32_t ncand;
+  const int qn = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = P.topk;
+  const IdxQuery Q = idx_query(P, pos, 0, 0, qn);
+  const int V = Q.V;
+  int32_t* o = out + (size_t)qn * k;
+  uint32_t* gh = hist + (size_t)qn * kHistBins;
+  // histogram -> LDS, and leave zeros behind
+  {
+    uint32_t hv[kHistBins / 1024];
+#pragma unroll
+    for (int e = 0; e < kHistBins / 1024; ++e) hv[e] = gh[tid + 1024 * e];
+#pragma unroll
+    for (int e = 0; e < kHistBins / 1024; ++e) {
+      sh[tid + 1024 * e] = hv[e];
+      gh[tid + 1024 * e] = 0u;
+    }
+  }
+  if (V <= k) {
+    for (int j = tid; j < k; j += blockDim.x) o[j] = j < V ? j : -1;
+    return;
+  }
+  const uint32_t* kq = keys + (size_t)qn * P.cap;
+  const int c0 = wave * (KPT * 64);
+  uint32_t kr[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int s = c0 + 64 * j + lane;
+    kr[j] = s < V ? kq[s] : 0u;
+  }
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  // level 1 from the histogram (bins ascending in key: search from the top)
+  {
+    const int per = kHistBins / 1024;
+    const int hi = kHistBins - tid * per, lo = hi - per;
+    uint32_t local = 0;
+    for (int b = lo; b < hi; ++b) local += sh[b];
+    if (tid == 0) {
+      bc[0] = 0;
+      bc[1] = 0;
+    }
+    uint32_t tot;
+    const uint32_t above = block_exscan(local, wsum, &tot);
+    if (above < (uint32_t)k && above + local >= (uint32_t)k) {
+      uint32_t cum = above;
+      for (int b = hi - 1; b >= lo; --b) {
+        if (cum + sh[b] >= (uint32_t)k) {
+          bc[0] = (uint32_t)b;
+          bc[1] = cum;
+          break;
+        }
+        cum += sh[b];
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t b1 = bc[0];
+  uint32_t need = (uint32_t)k - bc[1];
+  const uint32_t nb1 = sh[b1];
+  uint32_t T;
+  if (nb1 <= (uint32_t)CAP) {
+    // gather the keys of bin b1
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool in = c0 + 64 * j + lane < V && (kr[j] >> 20) == b1;
+      const unsigned long long m = __ballot(in);
+      if (m) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&ncand, (uint32_t)__popcll(m));
+        base = __shfl(base, 0, 64);
+        const uint32_t slot = base + (uint32_t)__popcll(m & lt);
+        if (in && slot < (uint32_t)CAP) cand[slot] = kr[j];
+      }
+    }
+    __syncthreads();
+    const int nc = (int)min(ncand, (uint32_t)CAP);
+    uint32_t prefix = b1 << 20, mask = 0xfff00000u;
+#pragma unroll 1
+    for (int lvl = 0; lvl < 2; ++lvl) {
+      const int shift = lvl == 0 ? 8 : 0;
+      const int nb = lvl == 0 ? 4096 : 256;
+      for (int e = tid; e < nb; e += blockDim.x) sh[e] = 0;
+      __syncthreads();
+      for (int i = tid; i < nc; i += blockDim.x) {
+        const uint32_t key = cand[i];
+        if ((key & mask) == prefix) atomicAdd(&sh[(key >> shift) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      // descending search within the level
+      const int per = (nb + 1023) / 1024;
+      const int hi = nb - tid * per, lo = max(0, hi - per);
+      uint32_t local = 0;
+      for (int b = lo; b < hi; ++b) local += sh[b];
+      if (tid == 0) {
+        bc[0] = 0;
+        bc[1] = 0;
+      }
+      uint32_t tot;
+      const uint32_t above = block_exscan(local, wsum, &tot);
+      if (above < need && above + local >= need) {
+        uint32_t cum = above;
+        for (int b = hi - 1; b >= lo; --b) {
+          if (cum + sh[b] >= need) {
+            bc[0] = (uint32_t)b;
+            bc[1] = cum;
+            break;
+          }
+          cum += sh[b];
+        }
+      }
+      __syncthreads();
+      prefix |= bc[0] << shift;
+      mask |= (uint32_t)(nb - 1) << shift;
+      need -= bc[1];
+    }
+    T = prefix;
+  } else {
+    uint32_t mloc = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) mloc = max(mloc, kr[j]);
+    const uint32_t M = block_max_u32(mloc, wsum);
+    auto count_level = [&](int shift, int nbits, uint32_t pfx, uint32_t pmask, uint32_t* h) {
+      const uint32_t nb = 1u << nbits;
+      for (int e = tid; e < (int)nb; e += blockDim.x) h[e] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const uint32_t d = M - kr[j];
+        if (c0 + 64 * j + lane < V && (d & pmask) == pfx) atomicAdd(&h[(d >> shift) & (nb - 1u)], 1u);
+      }
+      __syncthreads();
+    };
+    T = radix_select(M, (uint32_t)k, count_level, sh, wsum, bc, &need);
+  }
+  const int c1 = min(V, c0 + KPT * 64);
+  emit_selected<KPT>([&](int j) -> uint32_t { return kr[j]; }, c0, max(c0, c1), T, need, k, o, wgt, weq);
+}
+
 // ---------------------------------------------------------------- launchers
 
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
-                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, int32_t* topk,
-                   void* stream) {
+                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
+                   int32_t* topk, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  launch_idx_score(P, c, qI, w, pos, seq, pos0, nq, keys, stream);
   const int vlast = (pos0 + nq) / 4;
   const int vmax = pos ? P.cap : (vlast < P.cap ? vlast : P.cap);
-  if (vmax <= 32768)
+  // decode with the workspace histogram: the score kernel fills it, the select consumes and clears it
+  const bool use_hist = pos && hist && vmax <= 32768;
+  launch_idx_score(P, c, qI, w, pos, seq, pos0, nq, keys, use_hist ? hist : nullptr, stream);
+  if (use_hist)
+    hipLaunchKernelGGL(k_topk_select_hist, dim3(nq), dim3(1024), 0, st, P, keys, hist, pos, topk);
+  else if (vmax <= 32768)
     hipLaunchKernelGGL(k_topk_select_reg, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);
   else
     hipLaunchKernelGGL(k_topk_select, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);
@@ -460,7 +661,8 @@ int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const f
 }
 
 int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const float* w,
-                     const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, void* stream) {
+                     const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
+                     void* stream) {
   hipStream_t st = (hipStream_t)stream;
   // rows to cover: decode -> the whole capacity; prefill -> rows visible to the last query
   const int vlast = (pos0 + nq) / 4;
@@ -474,7 +676,7 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
     dim3 mgrid((unsigned)(vmax > 0 ? (vmax + 256 * groups - 1) / (256 * groups) : 1), nq);
 #define CKV_IS(MTV, QF)                                                                           \
   hipLaunchKernelGGL((k_idx_score_mfma<MTV, 4, QF>), mgrid, dim3(256), 0, st, P, ix, qI, w, pos, seq, \
-                     pos0, groups, keys)
+                     pos0, groups, keys, hist)
     if (P.act_fmt == CKV_BF16) {
       if (MT == 1) CKV_IS(1, CKV_BF16);
       else if (MT == 2) CKV_IS(2, CKV_BF16);
@@ -489,7 +691,8 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
 #undef CKV_IS
   } else {
 #define CKV_IV(IF, QF) \
-  hipLaunchKernelGGL((k_idx_score_vec<IF, QF>), grid, dim3(256), 0, st, P, c.idx, qI, w, pos, seq, pos0, keys)
+  hipLaunchKernelGGL((k_idx_score_vec<IF, QF>), grid, dim3(256), 0, st, P, c.idx, qI, w, pos, seq, pos0, keys, \
+                     hist)
     if (P.idx_fmt == CKV_F32 && P.act_fmt == CKV_F32) CKV_IV(CKV_F32, CKV_F32);
     else if (P.idx_fmt == CKV_F32) CKV_IV(CKV_F32, CKV_BF16);
     else if (P.act_fmt == CKV_F32) CKV_IV(CKV_BF16, CKV_F32);

@@ -47,17 +47,17 @@ __global__ __launch_bounds__(256) void k_proj_mfma(const uint16_t* __restrict__ 
   f32x4 c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0};
   const u32x4 zero = {0, 0, 0, 0};
   int k = k0;
-  for (; k + 128 <= k1; k += 128) {
-    u32x4 a0[4], a1[4], b[4];
+  for (; k + 256 <= k1; k += 256) {   // eight k-steps' loads in flight
+    u32x4 a0[8], a1[8], b[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 8; ++s) {
       const int kk = k + 32 * s + 8 * g;
       b[s] = *(const u32x4*)(wrow + kk);
       a0[s] = ok0 ? *(const u32x4*)(x0 + kk) : zero;
       a1[s] = ok1 ? *(const u32x4*)(x1 + kk) : zero;
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 8; ++s) {
       c0 = mfma16x16x32(as_bf16x8(a0[s]), as_bf16x8(b[s]), c0);
       c1 = mfma16x16x32(as_bf16x8(a1[s]), as_bf16x8(b[s]), c1);
     }

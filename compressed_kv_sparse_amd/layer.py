@@ -70,7 +70,7 @@ class DeviceLayer:
         self._wt = {}
         nb = max(L.workspace_bytes(self.desc, L.CKV_MODE_DECODE, batch),
                  L.workspace_bytes(self.desc, L.CKV_MODE_PREFILL, max_chunk) if max_chunk else 0)
-        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(nb, dtype=torch.uint8, device=dev)   # the sync region must start zeroed
         self.ws_bytes = nb
 
     @staticmethod

@@ -186,9 +186,17 @@ const char* ckv_strerror(int code);
 const char* ckv_last_hip_error(void);
 
 /* Workspace bytes a call of `mode` with n = B (decode) or T (prefill) tokens
- * needs; the same figure serves all three entry points of that mode.
- * 0 when desc is invalid. */
+ * needs; the same figure serves all entry points of that mode.
+ * 0 when desc is invalid.
+ *
+ * Workspace contract: the first ckv_workspace_sync_bytes(desc, mode, n) bytes
+ * of the workspace hold counters and histograms that kernels accumulate into.
+ * They must be zero before the workspace is first used (allocate it zeroed);
+ * every call that completes leaves them zero again, so a workspace can be
+ * reused across calls, modes and graph replays.  Calls sharing one workspace
+ * must not overlap. */
 size_t ckv_workspace_bytes(const ckv_layer_desc* desc, int32_t mode, int32_t n);
+size_t ckv_workspace_sync_bytes(const ckv_layer_desc* desc, int32_t mode, int32_t n);
 
 /* ---- compress_append: compressor + cache insertion [P1 s4-s5, s8-s9; P4 fused
  * compressor + RMSNorm + RoPE + cache insertion] ----------------------------
