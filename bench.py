@@ -12,6 +12,8 @@ a captured HIP graph of one step.  Alongside it the script reports:
 * the whole step's algorithmic bytes against HBM peak;
 * the 4096-token chunked prefill at position 61440 (tokens/s and the share of
   bf16 MFMA peak of its algorithmic flops);
+* the whole 43-layer Flash stack (2 window-only, 21 c4a, 20 c128a layers) at
+  the same batch and context, one graph per step;
 * the CPU oracle timed on the host cores on the same inputs (a baseline).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -192,6 +194,67 @@ def bench_decode(cfg, steps, warmup, with_kernel=True):
     return res
 
 
+# --------------------------------------------------------------------------- layer stack
+
+def bench_stack(steps, warmup):
+    """The 43-layer Flash stack at 128k context, batch 16: one decode step of
+    every layer (window-only, c4a and c128a per the schedule), replayed as one
+    captured HIP graph.  Caches, weights and inputs are seeded device-side draws."""
+    import torch
+    from compressed_kv_sparse_amd.stack import DeviceStack, StackShape
+    from workloads.configs import stack_layer
+    from workloads.device_gen import draw_step_inputs, draw_weights, fill_layer_cache
+    from workloads.gen import context_lengths
+
+    t0 = time.time()
+    stk = DeviceStack(StackShape())
+    inputs, nbytes = [], 0.0
+    for il, dl in enumerate(stk.layers):
+        cfg = stack_layer(il)
+        assert cfg.ratio == dl.ratio
+        fill_layer_cache(dl, cfg)
+        wts = draw_weights(cfg)
+        if wts:
+            dl.set_weights(**wts)
+        inputs.append(draw_step_inputs(cfg))
+        nbytes += decode_step_bytes(cfg, context_lengths(cfg))
+    outs, topks = stk.buffers()
+    torch.cuda.synchronize()
+    log(f"[bench] stack: {len(stk)} layers set up in {time.time() - t0:.1f}s")
+
+    def step():
+        stk.decode(inputs, outs, topks)
+
+    step()
+    torch.cuda.synchronize()
+    assert all(int(dl.status.abs().sum()) == 0 for dl in stk.layers), "device status set"
+    ref = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    assert all(torch.equal(o.view(torch.int16), r.view(torch.int16)) for o, r in zip(outs, ref)), \
+        "stack graph replay differs"
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    B = stk.shape.batch
+    return {"workload": "c5_flash_stack_43L_b16_ctx131072_fp8", "layers": len(stk),
+            "ms_per_step": round(dt * 1e3, 4), "tok_s": round(B / dt, 1), "bytes": int(nbytes),
+            "achieved_gbs": round(nbytes / dt / 1e9, 1), "frac": round(nbytes / dt / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 # --------------------------------------------------------------------------- prefill
 
 def bench_prefill(cfg, steps, warmup):
@@ -271,9 +334,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--part", choices=("all", "prefill", "stack"), default="all",
+                    help="time one part alone and print its own JSON line (for kernel profiles)")
+    ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--extra", action="store_true", help="also time the other decode workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="first run 3 plain device copies of MIB MiB (a known-size reference for HBM counters)")
+                    help="first run 3 elementwise copies (neg) of MIB MiB: a known-size reference for HBM counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -286,13 +353,23 @@ def main():
     from workloads import get_config
 
     if args.copy_calibration:
-        n = args.copy_calibration << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        # an elementwise kernel that reads MIB MiB and writes MIB MiB: the
+        # reference for what FETCH_SIZE / WRITE_SIZE read per byte moved
+        n = (args.copy_calibration << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
         b = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            torch.neg(a, out=b)
         torch.cuda.synchronize()
         del a, b
+    if args.part == "prefill":
+        p = bench_prefill(get_config("c4"), args.prefill_steps, 1)
+        print(json.dumps({"part": "prefill", "workload": get_config("c4").name,
+                          **{k: round(v, 4) for k, v in p.items()}}), flush=True)
+        return
+    if args.part == "stack":
+        print(json.dumps({"part": "stack", **bench_stack(args.stack_steps, 3)}), flush=True)
+        return
     cfg = get_config(args.workload)
     r = bench_decode(cfg, args.steps, args.warmup)
     log(f"[bench] decode {cfg.name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['tok_s']:.0f} tok/s, "
@@ -319,6 +396,11 @@ def main():
                "mfma_frac": round(p["mfma_frac"], 4)}
         log(f"[bench] prefill: {p['ms_per_chunk']:.2f} ms/chunk, {p['tok_s']:.0f} tok/s, "
             f"{p['tflops']:.1f} TFLOP/s ({100 * p['mfma_frac']:.1f}% of bf16 MFMA)")
+    stack = None
+    if not args.no_stack:
+        stack = bench_stack(args.stack_steps, 3)
+        log(f"[bench] stack {stack['layers']} layers: {stack['ms_per_step']:.3f} ms/step, {stack['tok_s']:.0f} tok/s, "
+            f"{100 * stack['frac']:.1f}% of HBM")
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, r["_inp"], r["_wts"])
@@ -336,6 +418,7 @@ def main():
                      "unit": "GB/s", "frac": round(r["step_hbm_frac"], 4)},
         "roofline": roof,
         "prefill": pre,
+        "stack": stack,
         "cpu_baseline": cpu,
     }
     if extra:

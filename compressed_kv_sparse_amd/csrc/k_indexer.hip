@@ -32,78 +32,119 @@ __device__ __forceinline__ IdxQuery idx_query(const LayerParams& P, const int32_
 
 // ---------------------------------------------------------------- MFMA score
 // bf16 indexer rows; MT = ceil(H_I / 16) head tiles, KS = D_I / 32 k-steps.
-// grid: x = row blocks of 256 * groups, y = queries.  Per group each wave
-// scores 64 rows; the next group's rows are loaded while the current one is
-// multiplied.  Heads are the MFMA M dimension, rows the N dimension, so the
+// grid: x = row blocks of 256 * kScoreGroups, y = queries.  Per group each
+// wave scores 64 rows; the next group's rows are loaded while the current one
+// is multiplied.  Heads are the MFMA M dimension, rows the N dimension, so the
 // weighted head sum is 4 in-lane adds per tile and two cross-lane adds.
-template <int MT, int KS, int QF>
-__global__ __launch_bounds__(256) void k_idx_score_mfma(LayerParams P, const uint16_t* __restrict__ idx,
+//
+// Every global load here is unconditional (indices clamped into range, the
+// value replaced afterwards), the key stores are branch-free, and the group
+// loop has a compile-time trip count: a load under a branch, or in a loop of
+// unknown length, makes the compiler wait for all outstanding loads right
+// after it, which turns the prefetch into a chain of full memory round trips.
+// Each wave keeps kScoreBufs row groups in registers: while group i is
+// multiplied, groups i+1 .. i+kScoreBufs-1 are in flight.  Two buffers and
+// the query fragments fill 256 registers (VGPRs + MFMA accumulators), so the
+// kernel runs two waves per SIMD -- two blocks per CU -- and four groups per
+// block give the 128k-context batch 512 blocks, all resident at once.  Left
+// to its default occupancy target the compiler reuses one buffer's
+// registers for the next and every wave's loads and multiplies serialise;
+// with more blocks than fit, a second round of blocks waits for the first.
+// (Measured on the 16 x 32768-row batch: 25.7 us here; 30.8 us with one
+// wave per SIMD and three buffers; 30.8 us with four waves and no prefetch.)
+constexpr int kScoreGroups = 4;
+constexpr int kScoreBufs = 2;
+
+// Destination of the key stores of rows at or past the cache capacity (the
+// last row block of a query can run past it); written, never read.
+__device__ uint32_t g_key_sink[64];
+
+template <int MT, int KS, int QF, bool HIST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_idx_score_mfma(LayerParams P, const uint16_t* idx,
                                                         const void* __restrict__ qI,
                                                         const float* __restrict__ wt,
                                                         const int32_t* __restrict__ pos, int seq_fixed,
-                                                        int pos0, int groups, uint32_t* __restrict__ keys,
+                                                        int pos0, uint32_t* __restrict__ keys,
                                                         uint32_t* __restrict__ hist) {
   constexpr int DI = KS * 32;
   constexpr int HP = MT * 16;
+  constexpr int RB = 256 * kScoreGroups;
   __shared__ __attribute__((aligned(16))) uint16_t qh[HP * DI];
   __shared__ float wsh[HP];
   __shared__ float cs_[32], sn_[32];
   __shared__ uint32_t lh[kHistBins];
   const int qn = blockIdx.y;
   const IdxQuery Q = idx_query(P, pos, seq_fixed, pos0, qn);
-  const int rb0 = blockIdx.x * 256 * groups;
+  const int rb0 = blockIdx.x * RB;
   if (rb0 >= Q.V) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int HI = P.HI, nrot = P.idx_rot, dn = DI - nrot;
   const uint16_t* base = idx + (size_t)Q.seq * P.cap * DI;
-  const u32x4 zero = {0, 0, 0, 0};
+  const int vlast = Q.V - 1;
 
-  // rows of group gi for this wave -> B operands (issued first: the loads
-  // overlap the prologue)
+  // rows of group gi for this wave -> B operands; rows past V re-read row V-1
   auto load = [&](u32x4(&Bv)[4][KS], int gi) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int row = rb0 + 256 * gi + wave * 64 + 16 * t + r;
-      const bool ok = row < Q.V;
-      const uint16_t* rp = base + (size_t)(ok ? row : 0) * DI + 8 * g;
+      const int row = min(rb0 + 256 * gi + wave * 64 + 16 * t + r, vlast);
+      const uint16_t* rp = base + (size_t)row * DI + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Bv[t][ks] = ok ? *(const u32x4*)(rp + 32 * ks) : zero;
+      for (int ks = 0; ks < KS; ++ks) Bv[t][ks] = *(const u32x4*)(rp + 32 * ks);
     }
   };
-  u32x4 B0[4][KS], B1[4][KS];
-  load(B0, 0);
-  // this thread's share of the query, loaded together with the first rows
-  constexpr int NPAIR = HP * DI / 2 / 256;
-  float qa[NPAIR], qb[NPAIR];
+  u32x4 Bq[kScoreBufs][4][KS];
+  constexpr int kAhead = kScoreBufs > 1 ? kScoreBufs - 1 : 1;   // groups issued before the prologue
 #pragma unroll
-  for (int e = 0; e < NPAIR; ++e) {
-    const int pe = tid + 256 * e, h = pe / (DI / 2), c = 2 * (pe % (DI / 2));
-    qa[e] = qb[e] = 0.f;
-    if (h < HI) {
-      const size_t o = ((size_t)qn * HI + h) * DI + c;
-      qa[e] = load_val<QF>(qI, o);
-      qb[e] = load_val<QF>(qI, o + 1);
+  for (int b = 0; b < kAhead && b < kScoreGroups; ++b) load(Bq[b % kScoreBufs], b);
+  // the query: MT chunks of 8 channels per thread (chunk ci = tid + 256 e is
+  // head ci / (DI/8), channels 8 (ci % (DI/8)) .. +7); heads past H_I read head
+  // H_I - 1 and are zeroed below
+  constexpr int CPH = DI / 8;
+  u32x4 qraw[MT][QF == CKV_F32 ? 2 : 1];
+#pragma unroll
+  for (int e = 0; e < MT; ++e) {
+    const int ci = tid + 256 * e, h = min(ci / CPH, HI - 1), c = 8 * (ci % CPH);
+    const size_t o = ((size_t)qn * HI + h) * DI + c;
+    if constexpr (QF == CKV_F32) {
+      qraw[e][0] = *(const u32x4*)((const float*)qI + o);
+      qraw[e][1] = *(const u32x4*)((const float*)qI + o + 4);
+    } else {
+      qraw[e][0] = *(const u32x4*)((const uint16_t*)qI + o);
     }
   }
+  const float wl = wt[(size_t)qn * HI + min(tid, HI - 1)];
 
   if (tid < nrot / 2) rope_cs(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
-  if (tid < HP) wsh[tid] = tid < HI ? wt[(size_t)qn * HI + tid] : 0.f;
-  if (hist)
+  if (tid < HP) wsh[tid] = tid < HI ? wl : 0.f;
+  if constexpr (HIST)
     for (int e = tid; e < kHistBins; e += 256) lh[e] = 0;
   __syncthreads();
   // rotated query -> bf16 in LDS
 #pragma unroll
-  for (int e = 0; e < NPAIR; ++e) {
-    const int pe = tid + 256 * e, h = pe / (DI / 2), c = 2 * (pe % (DI / 2));
-    float a = qa[e], b = qb[e];
-    if (c >= dn) {
-      const int j = (c - dn) >> 1;
-      const float x = a * cs_[j] - b * sn_[j], y = a * sn_[j] + b * cs_[j];
-      a = x;
-      b = y;
+  for (int e = 0; e < MT; ++e) {
+    const int ci = tid + 256 * e, h = ci / CPH, c = 8 * (ci % CPH);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (QF == CKV_F32) v[i] = __uint_as_float(qraw[e][i >> 2][i & 3]);
+      else v[i] = bf16_to_f32((qraw[e][0][i >> 1] >> (16 * (i & 1))) & 0xffffu);
+      if (h >= HI) v[i] = 0.f;
     }
-    ((uint32_t*)qh)[(h * DI + c) >> 1] = pack_bf16x2(a, b);
+    u32x4 packed;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float a = v[2 * i], b = v[2 * i + 1];
+      const int cc = c + 2 * i;
+      if (cc >= dn) {
+        const int j = (cc - dn) >> 1;
+        const float x = a * cs_[j] - b * sn_[j], y = a * sn_[j] + b * cs_[j];
+        a = x;
+        b = y;
+      }
+      packed[i] = pack_bf16x2(a, b);
+    }
+    *(u32x4*)&qh[h * DI + c] = packed;
   }
   __syncthreads();
 
@@ -138,22 +179,43 @@ __global__ __launch_bounds__(256) void k_idx_score_mfma(LayerParams P, const uin
     }
     const float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
     const int row = rb0 + 256 * gi + wave * 64 + lane;
-    if (row < Q.V) {
-      const uint32_t key = float_key(mine);
-      kout[row] = key;
-      if (hist) atomicAdd(&lh[key >> 20], 1u);
-    }
+    // branch-free: keys of rows in [V, cap) are written but never read; rows
+    // past the capacity go to the sink; only rows below V enter the histogram
+    *(row < P.cap ? kout + row : g_key_sink + lane) = float_key(mine);
   };
-  for (int gi = 0; gi < groups; gi += 2) {
-    if (rb0 + 256 * gi >= Q.V) break;
-    const bool more = gi + 1 < groups && rb0 + 256 * (gi + 1) < Q.V;
-    if (more) load(B1, gi + 1);
-    score(B0, gi);
-    if (!more) break;
-    if (gi + 2 < groups && rb0 + 256 * (gi + 2) < Q.V) load(B0, gi + 2);
-    score(B1, gi + 1);
+  // An empty asm that takes the buffer about to be multiplied as in/out
+  // operands and clobbers memory: the loads issued before it cannot sink
+  // below it, and the multiplies (which read its outputs) cannot rise above
+  // it.  Without it the compiler places each prefetch after the previous
+  // group's multiplies.  (idx is deliberately not __restrict__: with it the
+  // compiler may prove the clobber cannot touch the rows and move the loads
+  // anyway.)
+  auto pin = [&](u32x4(&Bv)[4][KS]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(Bv[t][ks]) : : "memory");
+  };
+#pragma unroll
+  for (int gi = 0; gi < kScoreGroups; ++gi) {
+    if constexpr (kScoreBufs > 1) {
+      if (gi + kAhead < kScoreGroups) load(Bq[(gi + kAhead) % kScoreBufs], gi + kAhead);
+    }
+    pin(Bq[gi % kScoreBufs]);
+    score(Bq[gi % kScoreBufs], gi);
+    if constexpr (kScoreBufs == 1) {
+      if (gi + 1 < kScoreGroups) load(Bq[0], gi + 1);
+    }
   }
-  if (hist) {  // this block's key histogram into the query's
+  if constexpr (HIST) {  // this block's key histogram into the query's
+    // each thread reads back the keys it wrote (kept out of the main loop,
+    // whose registers are full)
+#pragma unroll
+    for (int gi = 0; gi < kScoreGroups; ++gi) {
+      const int row = rb0 + 256 * gi + wave * 64 + lane;
+      const uint32_t key = kout[min(row, P.cap - 1)];
+      atomicAdd(&lh[key >> 20], row < Q.V ? 1u : 0u);
+    }
     __syncthreads();
     uint32_t* gh = hist + (size_t)qn * kHistBins;
     for (int e = tid; e < kHistBins; e += 256) {
@@ -672,11 +734,15 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
   if (mf) {
     const uint16_t* ix = (const uint16_t*)c.idx;
     const int MT = (P.HI + 15) / 16;
-    const int groups = 4;
-    dim3 mgrid((unsigned)(vmax > 0 ? (vmax + 256 * groups - 1) / (256 * groups) : 1), nq);
+    constexpr int RB = 256 * kScoreGroups;
+    dim3 mgrid((unsigned)(vmax > 0 ? (vmax + RB - 1) / RB : 1), nq);
 #define CKV_IS(MTV, QF)                                                                           \
-  hipLaunchKernelGGL((k_idx_score_mfma<MTV, 4, QF>), mgrid, dim3(256), 0, st, P, ix, qI, w, pos, seq, \
-                     pos0, groups, keys, hist)
+  if (hist)                                                                                       \
+    hipLaunchKernelGGL((k_idx_score_mfma<MTV, 4, QF, true>), mgrid, dim3(256), 0, st, P, ix, qI, w, pos, \
+                       seq, pos0, keys, hist);                                                          \
+  else                                                                                            \
+    hipLaunchKernelGGL((k_idx_score_mfma<MTV, 4, QF, false>), mgrid, dim3(256), 0, st, P, ix, qI, w, pos, \
+                       seq, pos0, keys, hist)
     if (P.act_fmt == CKV_BF16) {
       if (MT == 1) CKV_IS(1, CKV_BF16);
       else if (MT == 2) CKV_IS(2, CKV_BF16);

@@ -248,7 +248,8 @@ int ckv_indexer_topk_decode(const ckv_layer_desc* desc, const ckv_layer_cache* c
  * 32-bit image of I(s): a non-negative score's float bits with the top bit
  * set, a negative score's bits inverted (-0 counts as +0), so keys compare
  * like the scores.  keys [B, comp_cap] uint32; other arguments as for the
- * decode call.  Rows >= V are left untouched. */
+ * decode call.  Entries V <= s < comp_cap may receive unspecified values;
+ * nothing outside [B, comp_cap] is written. */
 int ckv_indexer_score_decode(const ckv_layer_desc* desc, const ckv_layer_cache* cache,
                              const void* qI, const float* w, const int32_t* pos, int32_t B,
                              uint32_t* keys, void* stream);

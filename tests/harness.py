@@ -119,3 +119,19 @@ def topk_margin(scores: np.ndarray, k: int) -> float:
 
 def sets_equal(gpu_topk: np.ndarray, ref_topk: np.ndarray) -> bool:
     return np.array_equal(np.sort(gpu_topk), np.sort(ref_topk))
+
+
+def tie_free_queries(cfg, seqs, pos, qI, w, attempts=40, margin=1e-4):
+    """Redraw q^I / w of any query whose oracle score gap at the k boundary is
+    below ``margin`` (same generator, sub-seed per query and attempt)."""
+    qI, w = qI.copy(), w.copy()
+    for b, seq in enumerate(seqs):
+        for a in range(attempts):
+            sc = seq.index_scores(int(pos[b]), qI[b], w[b])
+            if topk_margin(sc, cfg.top_k) > margin:
+                break
+            nq, nw = G.draw_query_index(cfg, 1, sub=b, attempt=a + 1)
+            qI[b], w[b] = nq[0], nw[0]
+        else:
+            raise AssertionError(f"no tie-free indexer query for sequence {b}")
+    return qI, w

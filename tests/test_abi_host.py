@@ -123,3 +123,14 @@ def test_host_errors_before_any_enqueue():
     # invalid description
     assert L.compress_append_decode(desc(ratio=5), w, c, FAKE, FAKE, FAKE, 1, FAKE, ws) == L.CKV_E_UNSUPPORTED
     assert L.lib.ckv_validate(None) == L.CKV_E_INVAL
+
+
+def test_stack_schedule_matches_the_oracle():
+    """The stack driver's per-layer ratio rule against the oracle's schedules."""
+    import oracle as O
+    from compressed_kv_sparse_amd.stack import layer_ratio
+    for il in range(61):
+        assert layer_ratio(il, "flash") == O.flash_ratio(il)
+        assert layer_ratio(il, "pro") == O.pro_ratio(il)
+    with pytest.raises(ValueError):
+        layer_ratio(0, "other")

@@ -12,7 +12,7 @@ import pytest
 
 import oracle as O
 from harness import (BF16_TOL, FP8_TOL, assert_close, compare_rows, dev, device_layer, oracle_layer,
-                     oracle_seq_from_bytes, oracle_seq_from_init, sets_equal, topk_margin)
+                     oracle_seq_from_bytes, oracle_seq_from_init, sets_equal, tie_free_queries, topk_margin)
 from workloads import get_config, make_decode_inputs, make_layer_weights, make_prefill_inputs
 from workloads import gen as G
 
@@ -43,22 +43,6 @@ def cpu(t):
 def out_values(t, fmt):
     a = cpu(t)
     return O.decode_values(a, fmt)
-
-
-def tie_free_queries(cfg, seqs, pos, qI, w, attempts=40):
-    """Redraw q^I / w of any query whose oracle score gap at the k boundary is
-    below MARGIN (same generator, sub-seed per query and attempt)."""
-    qI, w = qI.copy(), w.copy()
-    for b, seq in enumerate(seqs):
-        for a in range(attempts):
-            sc = seq.index_scores(int(pos[b]), qI[b], w[b])
-            if topk_margin(sc, cfg.top_k) > MARGIN:
-                break
-            nq, nw = G.draw_query_index(cfg, 1, sub=b, attempt=a + 1)
-            qI[b], w[b] = nq[0], nw[0]
-        else:
-            raise AssertionError(f"no tie-free indexer query for sequence {b}")
-    return qI, w
 
 
 def run_decode_stage_checks(cfg, inp, wts, tol):
@@ -304,7 +288,9 @@ def test_indexer_score_stage_keys():
     inp = make_decode_inputs(cfg, n_ctx=np.array([16384, 9001, 4100, 333]))
     wts = make_layer_weights(cfg)
     dl = device_layer(cfg, wts, inp.cache)
-    keys = torch.zeros((cfg.batch, cfg.comp_cap), dtype=torch.int32, device="cuda")
+    # one guard row after the batch's [B, comp_cap] keys must stay untouched
+    keys_g = torch.zeros((cfg.batch + 1, cfg.comp_cap), dtype=torch.int32, device="cuda")
+    keys = keys_g[:cfg.batch]
     rc = L.indexer_score_decode(dl.desc, dl.cache, dev(inp.qI), dev(inp.w), dev(inp.pos), cfg.batch, keys,
                                 torch.cuda.current_stream().cuda_stream)
     assert rc == 0
@@ -320,4 +306,4 @@ def test_indexer_score_stage_keys():
         seq = oracle_seq_from_bytes(Lo, cpu(dl.raw)[b], cpu(dl.comp)[b], cpu(dl.idx)[b], p + 1)
         ref = seq.index_scores(p, inp.qI[b], inp.w[b])
         assert np.max(np.abs(sc - ref)) <= 1e-4 * np.max(np.abs(ref)), f"scores b={b}"
-        assert np.all(kg[b, V:] == 0)      # rows beyond V untouched
+    assert np.all(cpu(keys_g[cfg.batch]) == 0), "keys written past the batch's rows"
