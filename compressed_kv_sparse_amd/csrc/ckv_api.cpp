@@ -161,8 +161,14 @@ extern "C" int ckv_indexer_topk_decode(const ckv_layer_desc* desc, const ckv_lay
   if ((rc = check_ws(P, CKV_MODE_DECODE, B, ws, ws_bytes, &L))) return rc;
   clear_stale();
   uint8_t* wb = (uint8_t*)ws;
-  return launched(launch_indexer(P, to_cache(cache), qI, w, pos, 0, 0, B, (uint32_t*)(wb + L.keys),
-                                 (uint32_t*)(wb + L.hist), topk, stream));
+  SelWs sel;
+  sel.hist = (uint32_t*)(wb + L.hist);
+  sel.ctr = (uint32_t*)(wb + L.ctr);
+  sel.sure = (uint32_t*)(wb + L.sure);
+  sel.cand_key = (uint32_t*)(wb + L.cand_key);
+  sel.cand_idx = (uint32_t*)(wb + L.cand_idx);
+  return launched(launch_indexer(P, to_cache(cache), qI, w, pos, 0, 0, B, (uint32_t*)(wb + L.keys), &sel,
+                                 topk, stream));
 }
 
 extern "C" int ckv_indexer_score_decode(const ckv_layer_desc* desc, const ckv_layer_cache* cache,

@@ -11,6 +11,7 @@ namespace ckv {
 
 constexpr int kMaxD = 512;
 constexpr int kHistBins = 4096;   // top-k histogram of the keys' top 12 bits
+constexpr int kCandCap = 4096;    // decode top-k: keys of the threshold bin resolved in LDS
 constexpr int kMaxSplits = 256;   // attention partial results merged per query
 constexpr int kMaxDI = 128;
 
@@ -56,10 +57,25 @@ struct Cache {
 // Workspace carve-up (all offsets 256-byte aligned).  The sync region comes
 // first in every mode: counters and histograms that must hold zeros before a
 // call and that every call leaves at zero.
+// Decode top-k scratch.  hist [n][kHistBins] and ctr [n][4] (finished
+// blocks, sure count, candidate count) live in the zero-kept sync region;
+// sure [n][top_k] and cand_key / cand_idx [n][kCandCap] are plain scratch.
+struct SelWs {
+  uint32_t* hist;
+  uint32_t* ctr;
+  uint32_t* sure;
+  uint32_t* cand_key;
+  uint32_t* cand_idx;
+};
+
 struct WsLayout {
-  size_t sync;      // zero-kept region: uint32 hist [n][kHistBins] (ratio 4)
+  size_t sync;      // zero-kept region: hist and ctr (ratio 4)
   size_t sync_bytes;
-  size_t hist;      // offset of the histograms inside the sync region
+  size_t hist;      // uint32 [batch][kHistBins]
+  size_t ctr;       // uint32 [batch][4]
+  size_t sure;      // uint32 [n][top_k]
+  size_t cand_key;  // uint32 [n][kCandCap]
+  size_t cand_idx;  // uint32 [n][kCandCap]
   size_t proj;      // float [proj_splits][n][ncol]
   size_t keys;      // uint32 [n][cap]   indexer keys
   size_t part_o;    // float [n][splits][H][d]  attention partial outputs
@@ -85,7 +101,7 @@ int launch_compress_prefill(const LayerParams& P, const Weights& w, const Cache&
 // indexer: decode (pos != NULL, query b of sequence b) or prefill (pos == NULL,
 // query n of sequence seq at position pos0 + n)
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
-                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
+                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, const SelWs* sel,
                    int32_t* topk, void* stream);
 // hist may be NULL: scores only
 int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const float* w,

@@ -91,7 +91,19 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   L.sync = 0;
   L.hist = 0;
   if (P.ratio == 4) off += align256((size_t)P.batch * kHistBins * sizeof(uint32_t));
+  L.ctr = off;
+  if (P.ratio == 4) off += align256((size_t)P.batch * 4 * sizeof(uint32_t));
   L.sync_bytes = off;
+  L.sure = off;
+  L.cand_key = off;
+  L.cand_idx = off;
+  if (P.ratio == 4 && !prefill) {
+    off += align256((size_t)n * P.topk * sizeof(uint32_t));
+    L.cand_key = off;
+    off += align256((size_t)n * kCandCap * sizeof(uint32_t));
+    L.cand_idx = off;
+    off += align256((size_t)n * kCandCap * sizeof(uint32_t));
+  }
   L.proj = off;
   off += align256((size_t)L.proj_splits * n * P.ncol * sizeof(float));
   L.keys = off;

@@ -545,177 +545,344 @@ __global__ __launch_bounds__(1024) void k_topk_select(LayerParams P, const uint3
                    weq);
 }
 
-// Decode selection driven by the score kernel's histogram of the keys' top 12
-// bits (V <= 32768, keys in registers as in k_topk_select_reg).  The bin
-// holding the k-th largest key is read off the histogram; its keys (a few
-// percent of V) are gathered into LDS, where two more levels (bits 19..8, then
-// 7..0) fix the k-th key exactly.  The histogram is zeroed again for the next
-// call.  If the bin holds more keys than the LDS list takes, the register
-// radix select runs instead.
-__global__ __launch_bounds__(1024) void k_topk_select_hist(LayerParams P, const uint32_t* __restrict__ keys,
-                                                           uint32_t* __restrict__ hist,
-                                                           const int32_t* __restrict__ pos,
-                                                           int32_t* __restrict__ out) {
-  constexpr int KPT = 32;
-  constexpr int CAP = 6144;          // candidate keys gathered into LDS
+// Decode selection spread over many blocks, driven by the score kernel's
+// histogram of the keys' top 12 bits, in two kernels.
+//
+// k_topk_classify (grid: x = chunks of kSelChunk keys, y = queries): every
+// block reads the query's histogram and finds the bin b1 holding the k-th
+// largest key (A keys lie in higher bins, A < k).  It classifies its chunk:
+// keys above b1 are selected outright and appended to the query's "sure"
+// list, keys in b1 are appended to its candidate list (offsets from atomics
+// on per-query counters).
+//
+// k_topk_finish (one block per query) resolves the candidates: two radix
+// levels over their low 20 bits give the k-th key T exactly and how many keys
+// equal to T are taken (the lowest-index ones); the k selected indices are
+// sorted ascending in LDS (bitonic) and written out, and the histogram and
+// counters are returned to zero.  Should the candidate bin hold more keys
+// than the list takes (heavily tied scores), it runs the exact streaming
+// radix select over all keys of the query instead.
+//
+// The lists cross from one kernel to the next: within one kernel, making one
+// block's stores visible to a block on another XCD takes a device-scope
+// fence, which writes back and invalidates the L2 (tens of microseconds when
+// every block issues one); the kernel boundary does it once.
+constexpr int kSelChunk = 2048;
+
+// bitonic sort of sh[0..n) ascending, n a power of two, all threads
+__device__ __forceinline__ void bitonic_sort_lds(uint32_t* sh, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (n >> 1); i += blockDim.x) {
+        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint32_t a = sh[lo], b = sh[hi];
+        if ((a > b) == up) {
+          sh[lo] = b;
+          sh[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// In a histogram of nb bins held as `per` consecutive bins per thread
+// (thread t: bins t*per .. t*per+per-1, values v[]), find the bin where the
+// count of keys in higher bins first reaches `need`: out[0] = bin, out[1] =
+// count in bins above it, out[2] = count in the bin.  All threads.
+template <int PER>
+__device__ __forceinline__ void find_from_top(const uint32_t (&v)[PER], uint32_t need, uint32_t* wsum,
+                                              uint32_t* out) {
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) local += v[i];
+  uint32_t tot;
+  const uint32_t before = block_exscan(local, wsum, &tot);   // bins below this thread's
+  const uint32_t above = tot - before - local;                // bins above this thread's
+  if (above < need && above + local >= need) {
+    uint32_t cum = above;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (cum < need && cum + v[i] >= need) {
+        out[0] = (uint32_t)(threadIdx.x * PER + i);
+        out[1] = cum;
+        out[2] = v[i];
+      }
+      cum += v[i];
+    }
+  }
+  __syncthreads();
+}
+
+// The query's histogram, 16 consecutive bins per thread -> b1 and A.
+__device__ __forceinline__ void hist_threshold(const uint32_t* gh, uint32_t k, uint32_t* wsum, uint32_t* res,
+                                               uint32_t (&hv)[16]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const u32x4 t4 = *(const u32x4*)(gh + 16 * threadIdx.x + 4 * e);
+    hv[4 * e] = t4.x;
+    hv[4 * e + 1] = t4.y;
+    hv[4 * e + 2] = t4.z;
+    hv[4 * e + 3] = t4.w;
+  }
+  if (threadIdx.x == 0) {
+    res[0] = 0;
+    res[1] = 0;
+  }
+  find_from_top<16>(hv, k, wsum, res);
+}
+
+__global__ __launch_bounds__(256) void k_topk_classify(LayerParams P, const uint32_t* __restrict__ keys,
+                                                       SelWs S, const int32_t* __restrict__ pos) {
+  constexpr int KPT = kSelChunk / 256;
+  __shared__ uint32_t wsum[8], res[4], wcnt[2][4], base[2];
+  const int qn = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = P.topk;
+  const IdxQuery Q = idx_query(P, pos, 0, 0, qn);
+  const int V = Q.V;
+  const int c0 = blockIdx.x * kSelChunk;
+  if (V <= k || c0 >= V) return;   // nothing to select, or no key of this query here
+  const uint32_t* gh = S.hist + (size_t)qn * kHistBins;
+  uint32_t* ctr = S.ctr + (size_t)qn * 4;
+  const uint32_t* kq = keys + (size_t)qn * P.cap;
+  // this block's keys (indices clamped, rows past V masked below), issued
+  // together with the histogram loads
+  uint32_t kr[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) kr[j] = kq[min(c0 + 256 * j + tid, V - 1)];
+  uint32_t hv[16];
+  hist_threshold(gh, (uint32_t)k, wsum, res, hv);
+  const uint32_t b1 = res[0];
+
+  // classify: counts per wave, one global append per list per block
+  uint32_t ns = 0, nc = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool ok = c0 + 256 * j + tid < V;
+    const uint32_t bin = kr[j] >> 20;
+    ns += __popcll(__ballot(ok && bin > b1));
+    nc += __popcll(__ballot(ok && bin == b1));
+  }
+  if (lane == 0) {
+    wcnt[0][wave] = ns;
+    wcnt[1][wave] = nc;
+  }
+  __syncthreads();
+  if (tid < 2) {   // the two appends' offsets, one thread each (in parallel)
+    const uint32_t t = wcnt[tid][0] + wcnt[tid][1] + wcnt[tid][2] + wcnt[tid][3];
+    base[tid] = t ? atomicAdd(&ctr[1 + tid], t) : 0u;
+  }
+  __syncthreads();
+  {
+    uint32_t os = base[0], oc = base[1];
+    for (int w = 0; w < wave; ++w) {
+      os += wcnt[0][w];
+      oc += wcnt[1][w];
+    }
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t* sure = S.sure + (size_t)qn * k;
+    uint32_t* cnk = S.cand_key + (size_t)qn * kCandCap;
+    uint32_t* cni = S.cand_idx + (size_t)qn * kCandCap;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int sidx = c0 + 256 * j + tid;
+      const bool ok = sidx < V;
+      const uint32_t bin = kr[j] >> 20;
+      const bool is_s = ok && bin > b1, is_c = ok && bin == b1;
+      const unsigned long long ms = __ballot(is_s), mc = __ballot(is_c);
+      const uint32_t ps = os + (uint32_t)__popcll(ms & lt), pc = oc + (uint32_t)__popcll(mc & lt);
+      if (is_s && ps < (uint32_t)k) sure[ps] = (uint32_t)sidx;
+      if (is_c && pc < (uint32_t)kCandCap) {
+        cnk[pc] = kr[j];
+        cni[pc] = (uint32_t)sidx;
+      }
+      os += (uint32_t)__popcll(ms);
+      oc += (uint32_t)__popcll(mc);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_topk_finish(LayerParams P, const uint32_t* __restrict__ keys,
+                                                     SelWs S, const int32_t* __restrict__ pos,
+                                                     int32_t* __restrict__ out) {
   __shared__ uint32_t sh[kHistBins];
-  __shared__ uint32_t cand[CAP];
-  __shared__ uint32_t wsum[16], wgt[16], weq[16];
-  __shared__ uint32_t bc[2];
-  __shared__ uint32_t ncand;
+  __shared__ uint32_t ck[kCandCap], ci[kCandCap];
+  __shared__ uint32_t fin[4096];
+  __shared__ uint32_t wsum[8], res[4], wcnt[2][4], nfin, neq;
   const int qn = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = P.topk;
   const IdxQuery Q = idx_query(P, pos, 0, 0, qn);
   const int V = Q.V;
   int32_t* o = out + (size_t)qn * k;
-  uint32_t* gh = hist + (size_t)qn * kHistBins;
-  // histogram -> LDS, and leave zeros behind
-  {
-    uint32_t hv[kHistBins / 1024];
-#pragma unroll
-    for (int e = 0; e < kHistBins / 1024; ++e) hv[e] = gh[tid + 1024 * e];
-#pragma unroll
-    for (int e = 0; e < kHistBins / 1024; ++e) {
-      sh[tid + 1024 * e] = hv[e];
-      gh[tid + 1024 * e] = 0u;
-    }
-  }
-  if (V <= k) {
-    for (int j = tid; j < k; j += blockDim.x) o[j] = j < V ? j : -1;
+  uint32_t* gh = S.hist + (size_t)qn * kHistBins;
+  uint32_t* ctr = S.ctr + (size_t)qn * 4;
+  if (V <= k) {   // every visible row is taken; the histogram is cleared all the same
+    for (int j = tid; j < k; j += 256) o[j] = j < V ? j : -1;
+    for (int e = tid; e < kHistBins; e += 256) gh[e] = 0;
     return;
   }
   const uint32_t* kq = keys + (size_t)qn * P.cap;
-  const int c0 = wave * (KPT * 64);
-  uint32_t kr[KPT];
+  // the whole candidate and sure lists are read together with the histogram
+  // (one memory round trip; their lengths are known only after it)
+  const uint32_t* cnk = S.cand_key + (size_t)qn * kCandCap;
+  const uint32_t* cni = S.cand_idx + (size_t)qn * kCandCap;
+  const uint32_t* sure = S.sure + (size_t)qn * k;
+  uint32_t rk[kCandCap / 256], ri[kCandCap / 256], rs[16];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int s = c0 + 64 * j + lane;
-    kr[j] = s < V ? kq[s] : 0u;
+  for (int e = 0; e < kCandCap / 256; ++e) {
+    rk[e] = cnk[tid + 256 * e];
+    ri[e] = cni[tid + 256 * e];
   }
-  if (tid == 0) ncand = 0;
-  __syncthreads();
-  // level 1 from the histogram (bins ascending in key: search from the top)
-  {
-    const int per = kHistBins / 1024;
-    const int hi = kHistBins - tid * per, lo = hi - per;
-    uint32_t local = 0;
-    for (int b = lo; b < hi; ++b) local += sh[b];
-    if (tid == 0) {
-      bc[0] = 0;
-      bc[1] = 0;
-    }
-    uint32_t tot;
-    const uint32_t above = block_exscan(local, wsum, &tot);
-    if (above < (uint32_t)k && above + local >= (uint32_t)k) {
-      uint32_t cum = above;
-      for (int b = hi - 1; b >= lo; --b) {
-        if (cum + sh[b] >= (uint32_t)k) {
-          bc[0] = (uint32_t)b;
-          bc[1] = cum;
-          break;
-        }
-        cum += sh[b];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) rs[e] = sure[min(tid + 256 * e, k - 1)];   // k <= 4096
+  uint32_t hv[16];
+  hist_threshold(gh, (uint32_t)k, wsum, res, hv);
+  const uint32_t b1 = res[0], A = res[1], nb1 = res[2];   // nb1: keys in b1 = candidates appended
+  if (nb1 <= (uint32_t)kCandCap) {
+    const uint32_t nc_all = nb1;
+#pragma unroll
+    for (int e = 0; e < kCandCap / 256; ++e) {
+      const int i = tid + 256 * e;
+      if (i < (int)nc_all) {
+        ck[i] = rk[e];
+        ci[i] = ri[e];
       }
     }
-    __syncthreads();
-  }
-  const uint32_t b1 = bc[0];
-  uint32_t need = (uint32_t)k - bc[1];
-  const uint32_t nb1 = sh[b1];
-  uint32_t T;
-  if (nb1 <= (uint32_t)CAP) {
-    // gather the keys of bin b1
-    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const bool in = c0 + 64 * j + lane < V && (kr[j] >> 20) == b1;
-      const unsigned long long m = __ballot(in);
-      if (m) {
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&ncand, (uint32_t)__popcll(m));
-        base = __shfl(base, 0, 64);
-        const uint32_t slot = base + (uint32_t)__popcll(m & lt);
-        if (in && slot < (uint32_t)CAP) cand[slot] = kr[j];
-      }
-    }
-    __syncthreads();
-    const int nc = (int)min(ncand, (uint32_t)CAP);
+    uint32_t need = (uint32_t)k - A;
     uint32_t prefix = b1 << 20, mask = 0xfff00000u;
+    // two levels over the candidates: bits 19..8 (4096 bins), then 7..0
 #pragma unroll 1
     for (int lvl = 0; lvl < 2; ++lvl) {
       const int shift = lvl == 0 ? 8 : 0;
       const int nb = lvl == 0 ? 4096 : 256;
-      for (int e = tid; e < nb; e += blockDim.x) sh[e] = 0;
+      for (int e = tid; e < kHistBins; e += 256) sh[e] = 0;
       __syncthreads();
-      for (int i = tid; i < nc; i += blockDim.x) {
-        const uint32_t key = cand[i];
+      for (int i = tid; i < (int)nc_all; i += 256) {
+        const uint32_t key = ck[i];
         if ((key & mask) == prefix) atomicAdd(&sh[(key >> shift) & (nb - 1)], 1u);
       }
       __syncthreads();
-      // descending search within the level
-      const int per = (nb + 1023) / 1024;
-      const int hi = nb - tid * per, lo = max(0, hi - per);
-      uint32_t local = 0;
-      for (int b = lo; b < hi; ++b) local += sh[b];
+      uint32_t v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = (lvl == 0 || tid < 16) ? sh[(16 * tid + i) & (kHistBins - 1)] : 0u;
       if (tid == 0) {
-        bc[0] = 0;
-        bc[1] = 0;
+        res[0] = 0;
+        res[1] = 0;
       }
+      find_from_top<16>(v, need, wsum, res);
+      prefix |= res[0] << shift;
+      mask |= (uint32_t)(nb - 1) << shift;
+      need -= res[1];
+    }
+    const uint32_t T = prefix;   // the k-th largest key; `need` keys equal to it are taken
+    // The selected rows, marked in a bitmap over [0, V): the sure list, the
+    // candidates above T and the `need` lowest-index candidates equal to T.
+    // (Rows beyond the bitmap's reach go through a bitonic sort instead.)
+    const bool use_bm = V <= 32 * 4096;
+    const int nw = (V + 31) / 32;
+    uint32_t* bm = fin;                 // bitmap words (V <= 131072)
+    uint32_t* eql = sh;                 // candidates equal to T (sh is free now)
+    if (use_bm)
+      for (int e = tid; e < nw; e += 256) bm[e] = 0;
+    if (tid == 0) {
+      nfin = 0;
+      neq = 0;
+    }
+    __syncthreads();
+    auto mark = [&](uint32_t idx) {
+      if (use_bm) atomicOr(&bm[idx >> 5], 1u << (idx & 31));
+      else fin[atomicAdd(&nfin, 1u)] = idx;
+    };
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (tid + 256 * e < (int)A) mark(rs[e]);
+    for (int i = tid; i < (int)nc_all; i += 256) {
+      const uint32_t key = ck[i];
+      if (key > T) mark(ci[i]);
+      else if (key == T) eql[atomicAdd(&neq, 1u)] = ci[i];
+    }
+    __syncthreads();
+    const int ne = (int)neq;
+    if (ne > (int)need) {   // more ties than taken: keep the lowest indices
+      int n2 = 1;
+      while (n2 < ne) n2 <<= 1;
+      for (int i = ne + tid; i < n2; i += 256) eql[i] = 0xffffffffu;
+      __syncthreads();
+      bitonic_sort_lds(eql, n2);
+    }
+    for (int i = tid; i < (int)need; i += 256) mark(eql[i]);
+    __syncthreads();
+    if (use_bm) {
+      // ascending emission: each thread owns a run of words; block prefix of
+      // their popcounts gives its first output slot
+      const int per = (nw + 255) / 256;
+      const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+      uint32_t cnt = 0;
+      for (int e = w0; e < w1; ++e) cnt += __popc(bm[e]);
       uint32_t tot;
-      const uint32_t above = block_exscan(local, wsum, &tot);
-      if (above < need && above + local >= need) {
-        uint32_t cum = above;
-        for (int b = hi - 1; b >= lo; --b) {
-          if (cum + sh[b] >= need) {
-            bc[0] = (uint32_t)b;
-            bc[1] = cum;
-            break;
-          }
-          cum += sh[b];
+      uint32_t slot = block_exscan(cnt, wsum, &tot);
+      for (int e = w0; e < w1; ++e) {
+        uint32_t bits = bm[e];
+        while (bits) {
+          const int b = __ffs(bits) - 1;
+          bits &= bits - 1;
+          if (slot < (uint32_t)k) o[slot] = 32 * e + b;
+          ++slot;
         }
       }
+    } else {
+      int n2 = 1;
+      while (n2 < k) n2 <<= 1;
+      for (int i = k + tid; i < n2; i += 256) fin[i] = 0xffffffffu;
       __syncthreads();
-      prefix |= bc[0] << shift;
-      mask |= (uint32_t)(nb - 1) << shift;
-      need -= bc[1];
+      bitonic_sort_lds(fin, n2);
+      for (int j = tid; j < k; j += 256) o[j] = (int32_t)fin[j];
     }
-    T = prefix;
   } else {
+    // heavily tied scores: exact streaming radix select over all V keys
+    const int CH = ((V + 3) / 4 + 63) / 64 * 64;
+    const int w0 = min(V, wave * CH), w1 = min(V, w0 + CH);
     uint32_t mloc = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) mloc = max(mloc, kr[j]);
+    for (int s = w0 + lane; s < w1; s += 64) mloc = max(mloc, kq[s]);
     const uint32_t M = block_max_u32(mloc, wsum);
     auto count_level = [&](int shift, int nbits, uint32_t pfx, uint32_t pmask, uint32_t* h) {
       const uint32_t nb = 1u << nbits;
-      for (int e = tid; e < (int)nb; e += blockDim.x) h[e] = 0;
+      for (int e = tid; e < (int)nb; e += 256) h[e] = 0;
       __syncthreads();
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const uint32_t d = M - kr[j];
-        if (c0 + 64 * j + lane < V && (d & pmask) == pfx) atomicAdd(&h[(d >> shift) & (nb - 1u)], 1u);
+      for (int s = w0 + lane; s < w1; s += 64) {
+        const uint32_t d = M - kq[s];
+        if ((d & pmask) == pfx) atomicAdd(&h[(d >> shift) & (nb - 1u)], 1u);
       }
       __syncthreads();
     };
-    T = radix_select(M, (uint32_t)k, count_level, sh, wsum, bc, &need);
+    uint32_t need;
+    const uint32_t T = radix_select(M, (uint32_t)k, count_level, sh, wsum, res, &need);
+    emit_selected<0>([&](int j) -> uint32_t { return kq[w0 + 64 * j + lane]; }, w0, w1, T, need, k, o,
+                     wcnt[0], wcnt[1]);
   }
-  const int c1 = min(V, c0 + KPT * 64);
-  emit_selected<KPT>([&](int j) -> uint32_t { return kr[j]; }, c0, max(c0, c1), T, need, k, o, wgt, weq);
+  // leave the histogram and counters zeroed for the next call
+  for (int e = tid; e < kHistBins; e += 256) gh[e] = 0;
+  if (tid < 4) ctr[tid] = 0;
 }
 
 // ---------------------------------------------------------------- launchers
 
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
-                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
+                   const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, const SelWs* sel,
                    int32_t* topk, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int vlast = (pos0 + nq) / 4;
   const int vmax = pos ? P.cap : (vlast < P.cap ? vlast : P.cap);
-  // decode with the workspace histogram: the score kernel fills it, the select consumes and clears it
-  const bool use_hist = pos && hist && vmax <= 32768;
-  launch_idx_score(P, c, qI, w, pos, seq, pos0, nq, keys, use_hist ? hist : nullptr, stream);
-  if (use_hist)
-    hipLaunchKernelGGL(k_topk_select_hist, dim3(nq), dim3(1024), 0, st, P, keys, hist, pos, topk);
-  else if (vmax <= 32768)
+  // decode: the score kernel fills the workspace histogram, the chunked
+  // select consumes it and leaves it (and its counters) zero
+  const bool use_hist = pos && sel;
+  launch_idx_score(P, c, qI, w, pos, seq, pos0, nq, keys, use_hist ? sel->hist : nullptr, stream);
+  if (use_hist) {
+    dim3 grid((unsigned)((vmax + kSelChunk - 1) / kSelChunk), nq);
+    hipLaunchKernelGGL(k_topk_classify, grid, dim3(256), 0, st, P, keys, *sel, pos);
+    hipLaunchKernelGGL(k_topk_finish, dim3(nq), dim3(256), 0, st, P, keys, *sel, pos, topk);
+  } else if (vmax <= 32768)
     hipLaunchKernelGGL(k_topk_select_reg, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);
   else
     hipLaunchKernelGGL(k_topk_select, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);

@@ -307,3 +307,55 @@ def test_indexer_score_stage_keys():
         ref = seq.index_scores(p, inp.qI[b], inp.w[b])
         assert np.max(np.abs(sc - ref)) <= 1e-4 * np.max(np.abs(ref)), f"scores b={b}"
     assert np.all(cpu(keys_g[cfg.batch]) == 0), "keys written past the batch's rows"
+
+
+@pytest.mark.parametrize("case", ["all_equal", "integer_ties"])
+def test_decode_topk_with_exact_ties(case):
+    """Top-k under exact score ties, where the lowest-index rule decides.
+    all_equal: zero head weights make every score 0 -- the threshold bin holds
+    every row (the exhaustive fallback select).  integer_ties: indexer rows and
+    queries with small-integer entries and integer weights make every score an
+    integer that fp32 and fp64 both hold exactly, with hundreds of rows per
+    value -- the candidate select must apply the index rule among the keys
+    equal to the k-th.  Compared bit-exactly with the oracle's full sort."""
+    cfg = get_config("c5").with_(batch=2, comp_cap=16384, kv_fmt="bf16", seed=41, name=f"ties_{case}")
+    n = np.array([65536, 40000])
+    inp = make_decode_inputs(cfg, n_ctx=n)
+    wts = make_layer_weights(cfg)
+    rng = np.random.default_rng(7)
+    c = inp.cache
+    qI = inp.qI.copy()
+    w = inp.w.copy()
+    if case == "all_equal":
+        w[:] = 0.0
+    else:
+        vals = np.array([-2.0, -1.0, 0.0, 1.0, 2.0], np.float32)
+        c.idx[:] = G.bf16_bits_of_draw(rng.choice(vals, size=c.idx.shape).astype(np.float32))
+        qI_f = rng.choice(vals, size=qI.shape).astype(np.float32)
+        qI_f[..., cfg.idx_dim - 64:] = 0.0      # the rotated tail would make scores non-integer
+        qI = G.bf16_bits_of_draw(qI_f)
+        w = rng.integers(0, 3, size=w.shape).astype(np.float32)
+    dl = device_layer(cfg, wts, c)
+    topk = torch.empty((cfg.batch, cfg.top_k), dtype=torch.int32, device="cuda")
+    L = oracle_layer(cfg, wts)
+    for rep in range(2):     # twice: the first call must leave the workspace counters zero
+        dl.indexer_decode(dev(qI), dev(w), dev(inp.pos), topk)
+        torch.cuda.synchronize()
+        tk = cpu(topk)
+        for b in range(cfg.batch):
+            p = int(inp.pos[b])
+            seq = oracle_seq_from_bytes(L, cpu(dl.raw)[b], cpu(dl.comp)[b], cpu(dl.idx)[b], p + 1)
+            sc = seq.index_scores(p, qI[b], w[b])
+            ref = O.topk_select(sc, cfg.top_k)
+            if case == "integer_ties":
+                assert np.all(sc == np.round(sc)), "scores are not exact integers"
+                kth = np.sort(sc)[::-1][cfg.top_k - 1]
+                assert int((sc == kth).sum()) > 1, "no tie at the k-th score"
+            assert np.array_equal(tk[b], np.sort(ref)), f"{case}: top-k differs for b={b} (rep {rep})"
+    ws = dl.ws[:L_sync_bytes(dl)]
+    assert int(ws.view(torch.int32).abs().sum()) == 0, "sync region not left zero"
+
+
+def L_sync_bytes(dl):
+    from compressed_kv_sparse_amd import _lib as L
+    return L.workspace_sync_bytes(dl.desc, L.CKV_MODE_DECODE, dl.batch)
