@@ -88,6 +88,19 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// ---------------------------------------------------------------- barriers
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also drains every
+// outstanding global memory operation (its release fence must cover global
+// stores, and on this architecture loads and stores share one counter), which
+// would stall prefetched loads at every barrier.  Use this one where the
+// barrier protects LDS data only.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- reductions
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -89,6 +89,9 @@ struct WsLayout {
 bool make_params(const ckv_layer_desc* desc, LayerParams* P);
 WsLayout ws_layout(const LayerParams& P, int mode, int n);
 int attn_max_rows(const LayerParams& P);
+// the tiled MFMA attention kernel serves this layer (bf16 activations, bf16 or
+// E4M3 rows, head_dim 512, heads a multiple of 64)
+bool attn_uses_tiles(const LayerParams& P);
 
 // ---- launchers (return 0 or a hipError_t value) ----------------------------
 // projection: part[s][m][c] for columns c of the concatenated weights

@@ -51,9 +51,8 @@ int attn_max_rows(const LayerParams& P) {
   return P.swa + (P.ratio == 4 ? P.topk : P.ratio == 128 ? P.cap : 0);
 }
 
-static bool attn_is_mfma(const LayerParams& P) {
-  return P.act_fmt == CKV_BF16 && P.kv_fmt != CKV_F32 && P.H % 64 == 0 &&
-         (P.d == 512 || P.d == 128) && P.n_rot == 64;
+bool attn_uses_tiles(const LayerParams& P) {
+  return P.act_fmt == CKV_BF16 && P.kv_fmt != CKV_F32 && P.H % 64 == 0 && P.d == 512 && P.n_rot == 64;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -63,15 +62,19 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   memset(&L, 0, sizeof(L));
   const bool prefill = mode == CKV_MODE_PREFILL;
   const bool proj_mfma = P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16;
-  // decode projection: split K so each wave's loads (256 K-values) are in flight at once
-  L.proj_splits = (!prefill && proj_mfma) ? (P.hidden >= 512 ? P.hidden / 256 : 1) : 1;
+  // the decode projection reduces its K range inside each block and writes
+  // final sums (one slice); the compressor still accepts up to 4 K slices
+  (void)proj_mfma;
+  L.proj_splits = 1;
   const int rows = attn_max_rows(P);
   int rps;
-  if (attn_is_mfma(P)) {
+  if (attn_uses_tiles(P)) {
     if (prefill) {
       rps = rows;
     } else {
-      rps = P.ratio == 4 ? 64 : P.ratio == 128 ? 256 : 32;
+      // about four splits per query, each 4 to 10 tiles of 32 rows
+      rps = (rows + 3) / 4;
+      rps = rps < 128 ? 128 : rps > 320 ? 320 : rps;
       // tuning knob: rows of the row list one decode block handles (multiple of 32)
       const char* e = getenv("CKV_ATTN_ROWS_PER_SPLIT");
       if (e && atoi(e) >= 32) rps = atoi(e);
@@ -108,7 +111,7 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   off += align256((size_t)L.proj_splits * n * P.ncol * sizeof(float));
   L.keys = off;
   if (P.ratio == 4) off += align256((size_t)n * P.cap * sizeof(uint32_t));
-  const bool need_part = !(attn_is_mfma(P) && L.attn_splits == 1);
+  const bool need_part = !(attn_uses_tiles(P) && L.attn_splits == 1);
   L.part_o = off;
   if (need_part) off += align256((size_t)n * L.attn_splits * P.H * P.d * sizeof(float));
   L.part_ml = off;

@@ -66,317 +66,411 @@ __device__ __forceinline__ int topk_end(const int32_t* tk, int k, int V, int* sm
 }
 
 // ----------------------------------------------------------------- MFMA
-// bf16 activations; rows bf16 or E4M3 (+ bf16 tail, fp32 scale).  Block of 4
-// waves, each owning 16 heads; grid (queries, splits, H / 64).  The K = V row
-// tile sits in LDS twice: row-major for the QK^T operand and channel-major for
-// the PV operand.  An E4M3 row enters the products exactly (codes are exact in
-// bf16); its scale multiplies the non-RoPE logit part and the non-RoPE
-// probability operand.  The rotated query and the probabilities are fp32
-// values split into a bf16 pair hi + lo, each product taking two MFMAs, so
-// both contractions run at close to fp32 operand precision; the rows
-// themselves are exact in bf16.
-template <int KVF, int D>
-__global__ __launch_bounds__(256) void k_attn_mfma(LayerParams P, Cache cc, const uint16_t* __restrict__ q,
+// bf16 activations, head_dim 512, rows bf16 or E4M3 (+ bf16 tail, fp32 row
+// scale).  One block of 8 waves per (query, split, 64 heads); grid x =
+// queries * splits (split fastest), y = H / 64.
+//
+// Wave (hg, cg) = (w & 3, w >> 2) owns heads 16 hg .. +15 and channels
+// 256 cg .. +255.  Both products are taken transposed, so that everything a
+// head needs sits in that head's lanes: lane (r, g) = (l & 15, l >> 4) works
+// for head 16 hg + r.
+//   * logits S^T = K Q^T: A = 16 rows of the tile (row-major copy in LDS),
+//     B = the rotated query; lane (r, g) receives rows 16 nt + 4 g + i.  Each
+//     wave covers its 256-channel half; the two halves of a head group are
+//     summed through LDS in a fixed order, so both waves hold identical logits
+//     and run identical online-softmax updates (one head, 8 rows per lane).
+//   * output O^T = V^T P^T: A = 16 channels x 32 rows, read from the same
+//     row-major tile with the LDS transpose read (ds_read_b64_tr_b16: within
+//     each 16-lane group, lane 4 a + e receives element e of the 8-byte rows
+//     addressed by lanes a, a + 4, a + 8, a + 12), so lane (r, g) gathers
+//     channel r of rows 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3 -- the
+//     order in which it holds its probabilities, which therefore go into PV
+//     straight from the registers as the B operand.  Lane (r, g) accumulates
+//     channels 16 n + 4 g + i of its head.
+// Operand precision: the tile, the rotated query and the probabilities are
+// fp16 (MFMA f16 x f16 -> fp32).  E4M3 codes are exact in fp16 and a row's
+// scale multiplies the non-RoPE logit part and, for PV, the probability
+// operand of the non-RoPE channels; bf16 values convert to fp16 with 2^-11
+// relative rounding (stored rows are RMS-normalised or activation-sized, far
+// inside the fp16 range).  Probabilities lie in [0, e^8].
+//
+// The block first lays out its split's row list in LDS as 64-bit row
+// addresses (bit 0 set: skipped entry, a valid dummy row stands in).  Staging
+// is coalesced: consecutive lanes load consecutive 16-byte chunks of one
+// stored row and convert them into the row-major tile.  The tile is
+// double-buffered: tile t is multiplied from one buffer while tile t + 1 is
+// written into the other, two barriers per tile.  Global loads are
+// unconditional and sit outside any branch, so the compiler waits only for
+// the tile being committed; two tiles' loads are in flight while a tile is
+// multiplied.  The wave index comes from readfirstlane, so branches on the
+// wave's role (around MFMAs) are scalar branches, and the barriers inside the
+// loop order LDS only (lds_barrier).
+namespace attn {
+constexpr int D = 512, DN = 448, R = 32;
+constexpr int NT = 512;     // threads per block
+constexpr int KP = D + 8;   // row-major row stride (16-bit elements)
+constexpr int MAXK = 4096;
+constexpr int MAXL = 128 + MAXK + 4 * R;   // row-list entries of one split (+ padding tiles)
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+// two floats -> packed fp16 pair (hardware conversion, round to nearest even)
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
+}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// 8 bf16 values -> 8 fp16 values
+__device__ __forceinline__ u32x4 bf16x8_to_f16(u32x4 v) {
+  u32x4 t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = pk_f16(lo_bf16(v[i]), hi_bf16(v[i]));
+  return t;
+}
+// 8 E4M3 codes -> their exact fp16 values
+__device__ __forceinline__ u32x4 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
+  u32x4 t;
+  t[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false));
+  t[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true));
+  t[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false));
+  t[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
+  return t;
+}
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+__device__ __forceinline__ u32x2 ds_tr16(const uint16_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) i16x4_t*)(p)));
+}
+}  // namespace attn
+
+template <int KVF>
+__global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, const uint16_t* __restrict__ q,
                                                    const int32_t* __restrict__ pos, int seq_fixed, int pos0,
                                                    const int32_t* __restrict__ topk, int rows_per_split,
                                                    int nsplit, float* __restrict__ part_o,
                                                    float* __restrict__ part_ml, uint16_t* __restrict__ out) {
-  constexpr int R = 32;          // rows per tile
-  constexpr int KP = D + 8;      // K row stride (bf16 elements)
-  constexpr int VP = R + 8;      // Vt channel stride
-  constexpr int KS = D / 32;     // k-steps of QK^T
-  constexpr int NO = D / 16;     // output channel tiles
-  constexpr int DN = D - 64;     // non-RoPE channels
-  constexpr int C8 = D / 8;      // 8-channel chunks per row
-  constexpr int IT = (R / 2) * C8 / 256;  // staging items per thread per tile
-  constexpr int MAXK = 4096;     // top-k list held in LDS
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[R * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
-  // per wave: probabilities hi / lo, and (E4M3) scaled probabilities hi / lo
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[4][4][16 * VP];
-  __shared__ int32_t tks[MAXK];
-  __shared__ float rsc[R];
+  using namespace attn;
+  constexpr bool F8 = KVF == CKV_E4M3;
+  // staging items per thread: bf16 rows are 64 chunks of 16 bytes; E4M3 rows
+  // 28 code chunks + 8 tail chunks
+  constexpr int CPR = F8 ? 36 : 64;                 // chunks per row
+  constexpr int IT = (R * CPR + NT - 1) / NT;       // 4 (bf16) or 3 (E4M3)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][R * KP];
+  __shared__ __attribute__((aligned(16))) float Sp[8][2][4][64];   // partial non-RoPE logits per wave
+  __shared__ __attribute__((aligned(16))) float St[4][2][4][64];   // RoPE-tail logits per head group
+  __shared__ uint64_t rtab[MAXL];                                  // row addresses of the split
+  __shared__ __attribute__((aligned(16))) float rsc[2][R];
   __shared__ float cs_[32], sn_[32];
   __shared__ int tk_lim;
 
-  const int qn = blockIdx.x, split = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qn = blockIdx.x / nsplit, split = blockIdx.x - qn * nsplit;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave & 3, cg = wave >> 2;
+  const bool tailw = cg == 1;   // this wave's half holds the RoPE tail (channels 448..511)
   const int r = lane & 15, g = lane >> 4;
   const int H = P.H;
-  const int h0 = blockIdx.z * 64 + wave * 16;
+  const int head = blockIdx.y * 64 + 16 * hg + r;
   const bool decode = pos != nullptr;
   const AttnQuery A = attn_query(P, pos, seq_fixed, pos0, qn);
   const int j0 = split * rows_per_split;
   const int j1 = min(A.n_list, j0 + rows_per_split);
-  const int32_t* tkg = (P.ratio == 4 && topk) ? topk + (size_t)qn * P.topk : nullptr;
-  // top-k list into LDS; the list ends at its first entry >= V
-  if (tid == 0) tk_lim = tkg ? P.topk : 0;
+  const int ntiles = j1 > j0 ? (j1 - j0 + R - 1) / R : 0;
+  const int nent = (ntiles + 4) * R;   // table entries incl. the padding tiles the loop issues
+  const int K = (P.ratio == 4 && topk) ? P.topk : 0;
+  const uint8_t* dummy = decode ? cc.raw + (size_t)A.seq * P.swa * P.row_bytes : cc.stage;
+
+  // ---- the split's row list -> rtab.  The top-k list ends at its first
+  // entry >= V; entries < 0 are skipped.
+  int tkv[MAXK / NT];
+  if (tid == 0) tk_lim = K;
   __syncthreads();
-  if (tkg) {
-    for (int j0 = 0; j0 < P.topk; j0 += 256 * 4) {   // four loads per thread in flight
-      int v[4];
+  if (K) {
+    const int32_t* tkg = topk + (size_t)qn * P.topk;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + tid + 256 * e;
-        v[e] = j < P.topk ? tkg[j] : -1;
-      }
+    for (int e = 0; e < MAXK / NT; ++e) tkv[e] = tkg[min(tid + NT * e, K - 1)];
+    int first = K;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + tid + 256 * e;
-        if (j < P.topk) {
-          tks[j] = v[e];
-          if (v[e] >= A.V) atomicMin(&tk_lim, j);
-        }
-      }
-    }
+    for (int e = 0; e < MAXK / NT; ++e)
+      if (tid + NT * e < K && tkv[e] >= A.V) first = min(first, tid + NT * e);
+    if (first < K) atomicMin(&tk_lim, first);
   }
-  if (tid < 32) rope_cs(P, tid, (double)A.p, &cs_[tid], &sn_[tid]);
+  if (tid < 32) rope_cs(P, tid, (double)max(A.p, 0), &cs_[tid], &sn_[tid]);
   __syncthreads();
   const int tk_end = tk_lim;
-
-  // address of list entry j's stored row (NULL: skipped entry or past the split)
-  auto row_ptr = [&](int j) -> const uint8_t* {
-    if (j >= j1) return nullptr;
-    if (j < A.n_raw) {
+  for (int x = tid; x < nent; x += NT) {   // raw window entries, padding
+    const int j = j0 + x;
+    uint64_t v = (uint64_t)dummy | 1u;
+    if (j < j1 && j < A.n_raw) {
       const int t = A.p - A.n_raw + 1 + j;
-      if (decode) return cc.raw + ((size_t)A.seq * P.swa + t % P.swa) * P.row_bytes;
-      return cc.stage + (size_t)(t - pos0 + P.swa - 1) * P.row_bytes;
+      v = (uint64_t)(decode ? cc.raw + ((size_t)A.seq * P.swa + (t & (P.swa - 1))) * P.row_bytes
+                            : cc.stage + (size_t)(t - pos0 + P.swa - 1) * P.row_bytes);
+    } else if (j < j1 && P.ratio == 128) {
+      v = (uint64_t)(cc.comp + ((size_t)A.seq * P.cap + (j - A.n_raw)) * P.row_bytes);
     }
-    const int jj = j - A.n_raw;
-    int row = jj;
-    if (P.ratio == 4) {
-      if (jj >= tk_end) return nullptr;
-      row = tks[jj];
-      if (row < 0) return nullptr;
+    if (!(j < j1 && j >= A.n_raw && P.ratio == 4)) rtab[x] = v;
+  }
+  if (K) {   // top-k entries of this split, from the registers that hold them
+#pragma unroll
+    for (int e = 0; e < MAXK / NT; ++e) {
+      const int jj = tid + NT * e;
+      const int x = A.n_raw + jj - j0;
+      if (jj < K && x >= 0 && A.n_raw + jj < j1) {
+        const int row = tkv[e];
+        const bool ok = jj < tk_end && row >= 0 && row < A.V;
+        rtab[x] = ok ? (uint64_t)(cc.comp + ((size_t)A.seq * P.cap + row) * P.row_bytes) : ((uint64_t)dummy | 1u);
+      }
     }
-    return cc.comp + ((size_t)A.seq * P.cap + row) * P.row_bytes;
-  };
+  }
+  __syncthreads();
 
-  // staged global loads of one tile: item e covers rows (2pr, 2pr+1), channels
-  // 8*c8..; the row pair varies fastest across lanes so that the channel-major
-  // Vt stores of 16 lanes land in 16 consecutive LDS words
-  u32x4 stg[IT][2];
-  float ssc[IT][2];
-  auto issue = [&](int jt) {
+  // staging: item e of this thread is chunk it % CPR of tile row it / CPR,
+  // it = tid + NT e; items past the tile read a dummy row and are dropped.
+  // Thread t < 32 also loads the scale of row t.
+  struct Stg {
+    u32x4 v[IT];
+    bool ok[IT];
+    float s;
+    bool sok;
+  };
+  auto issue = [&](Stg& S, int tile) {
 #pragma unroll
     for (int e = 0; e < IT; ++e) {
-      const int it = tid + 256 * e, pr = it & 15, c8 = it >> 4;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint8_t* rp = row_ptr(jt + 2 * pr + h);
-        u32x4 v = {0u, 0u, 0u, 0u};
-        float sc = -1.f;
-        if (rp) {
-          if (KVF == CKV_BF16) {
-            v = *(const u32x4*)(rp + 16 * c8);
-          } else if (8 * c8 >= DN) {
-            v = *(const u32x4*)(rp + DN + 16 * (c8 - DN / 8));
-          } else {
-            const u32x2 cw = *(const u32x2*)(rp + 8 * c8);
-            v[0] = cw[0];
-            v[1] = cw[1];
-          }
-          if (c8 == 0) sc = KVF == CKV_E4M3 ? *(const float*)(rp + DN + 128) : 1.f;
-        }
-        stg[e][h] = v;
-        ssc[e][h] = sc;
-      }
+      const int it = tid + NT * e;
+      const int row = min(it / CPR, R - 1), ch = it % CPR;
+      const uint64_t ra = rtab[tile * R + row];
+      S.ok[e] = !(ra & 1u) && it < R * CPR;
+      const int off = !F8 ? 16 * ch : (ch < 28 ? 16 * ch : DN + 16 * (ch - 28));
+      S.v[e] = *(const u32x4*)((const uint8_t*)(ra & ~(uint64_t)1) + off);
     }
+    const uint64_t rs = rtab[tile * R + (tid & 31)];
+    S.s = F8 ? *(const float*)((const uint8_t*)(rs & ~(uint64_t)1) + DN + 128) : 1.f;
+    S.sok = !(rs & 1u);
   };
-  // staged registers -> LDS (row-major K, channel-major V); E4M3 codes become
-  // their exact bf16 values
-  auto commit = [&]() {
+  auto pin = [&](Stg& S) {
+#pragma unroll
+    for (int e = 0; e < IT; ++e) asm volatile("" : "+v"(S.v[e]) : : "memory");
+    asm volatile("" : "+v"(S.s) : : "memory");
+  };
+  auto commit = [&](const Stg& S, int buf) {
+    uint16_t* kb = Ks[buf];
 #pragma unroll
     for (int e = 0; e < IT; ++e) {
-      const int it = tid + 256 * e, pr = it & 15, c8 = it >> 4;
-      u32x4 v[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        v[h] = stg[e][h];
-        if (KVF == CKV_E4M3 && 8 * c8 < DN) {
-          // OCP E4M3 codes -> their exact bf16 values, two per conversion
-          const uint32_t w0 = v[h][0], w1 = v[h][1];
-          u32x4 t;
-          t[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
-          t[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
-          t[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
-          t[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
-          v[h] = t;
+      const int it = tid + NT * e;
+      const int row = it / CPR, ch = it % CPR;
+      if (it < R * CPR) {
+        const u32x4 v = S.ok[e] ? S.v[e] : (u32x4){0u, 0u, 0u, 0u};
+        if (!F8) {
+          *(u32x4*)&kb[row * KP + 8 * ch] = bf16x8_to_f16(v);
+        } else if (ch < 28) {   // 16 codes -> 16 fp16 channels
+          *(u32x4*)&kb[row * KP + 16 * ch] = e4m3x8_to_f16(v[0], v[1]);
+          *(u32x4*)&kb[row * KP + 16 * ch + 8] = e4m3x8_to_f16(v[2], v[3]);
+        } else {                // 8 bf16 tail channels
+          *(u32x4*)&kb[row * KP + DN + 8 * (ch - 28)] = bf16x8_to_f16(v);
         }
-        *(u32x4*)&Ks[(2 * pr + h) * KP + 8 * c8] = v[h];
-        if (c8 == 0) rsc[2 * pr + h] = ssc[e][h];
-      }
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        *(uint32_t*)&Vt[(8 * c8 + 2 * f) * VP + 2 * pr] = (v[0][f] & 0xffffu) | (v[1][f] << 16);
-        *(uint32_t*)&Vt[(8 * c8 + 2 * f + 1) * VP + 2 * pr] = (v[0][f] >> 16) | (v[1][f] & 0xffff0000u);
       }
     }
+    if (tid < 32) rsc[buf][tid] = S.sok ? S.s : -1.f;
   };
 
-  if (j0 < j1) issue(j0);
-
-  // rotated query of head h0 + r as the A operand (hi, lo), one bf16x8 per k-step;
-  // the non-RoPE channels are bf16 inputs, exact in hi with lo = 0
-  u32x4 Aq[KS], Aql[KS];
+  // rotated query of this lane's head in fp16, channels 256 cg + 32 ks + 8 g
+  // .. +7 (B operand)
+  Stg S0, S1;
+  u32x4 Bq[8];
   {
-    const uint16_t* qr = q + ((size_t)qn * H + h0 + r) * D;
+    const uint16_t* qr = q + ((size_t)qn * H + head) * D + 256 * cg + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int c0 = 32 * ks + 8 * g;
-      u32x4 v = *(const u32x4*)(qr + c0);
-      u32x4 lo = {0u, 0u, 0u, 0u};
-      if (c0 >= DN) {
+    for (int ks = 0; ks < 8; ++ks) Bq[ks] = *(const u32x4*)(qr + 32 * ks);
+    // the first tiles' loads go out behind the query's
+    issue(S0, 0);
+    if (!F8) issue(S1, 1);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      u32x4 v = Bq[ks];
+      if (tailw && ks >= 6) {
+        const int jb = (32 * ks + 8 * g + 256 - DN) / 2;   // first pair index of this chunk
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float a = bf16_to_f32(v[e] & 0xffffu), b = bf16_to_f32(v[e] >> 16);
-          const int jp = (c0 - DN) / 2 + e;
-          const float x = a * cs_[jp] - b * sn_[jp], y = a * sn_[jp] + b * cs_[jp];
-          v[e] = pack_bf16x2(x, y);
-          lo[e] = pack_bf16x2(x - bf16_to_f32(v[e] & 0xffffu), y - bf16_to_f32(v[e] >> 16));
+          const float a = lo_bf16(v[e]), b = hi_bf16(v[e]);
+          v[e] = pk_f16(a * cs_[jb + e] - b * sn_[jb + e], a * sn_[jb + e] + b * cs_[jb + e]);
         }
+      } else {
+        v = bf16x8_to_f16(v);
       }
-      Aq[ks] = v;
-      Aql[ks] = lo;
+      Bq[ks] = v;
     }
   }
 
-  float m_i[4], l_i[4];
-  f32x4 O[NO];
+  float m_i = -INFINITY, l_i = 0.f;
+  f32x4 O[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m_i[i] = -INFINITY;
-    l_i[i] = 0.f;
-  }
-#pragma unroll
-  for (int n = 0; n < NO; ++n) O[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < 16; ++n) O[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float scale = P.scale;
+  // transpose-read addresses: lane 16 g + 4 j + a reads row base + j,
+  // channels ch0 + 4 a .. + 3 (base 4 g, then 16 + 4 g)
+  const int tr_row = 4 * g + ((lane & 15) >> 2), tr_col = 4 * (lane & 3);
 
-  for (int jt = j0; jt < j1; jt += R) {
-    __syncthreads();              // the previous tile's readers are done
-    commit();
-    __syncthreads();
-    if (jt + R < j1) issue(jt + R);   // next tile's loads fly during this tile's math
-
-    // logits for 2 row tiles of 16
-    float S[2][4];
+  auto tile_math = [&](int buf) {
+    const uint16_t* kb = Ks[buf];
+    // partial logits S^T over this wave's channel half: rows 16 nt + 4 g + i;
+    // the tail wave keeps its RoPE channels (k-steps 6, 7) apart
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+      f32x4 an = {0.f, 0.f, 0.f, 0.f}, at = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 b = *(const u32x4*)&Ks[(16 * nt + r) * KP + 32 * ks + 8 * g];
-        if (32 * ks < DN) {
-          a1 = mfma16x16x32(as_bf16x8(Aq[ks]), as_bf16x8(b), a1);
-        } else {
-          a2 = mfma16x16x32(as_bf16x8(Aq[ks]), as_bf16x8(b), a2);
-          a2 = mfma16x16x32(as_bf16x8(Aql[ks]), as_bf16x8(b), a2);
-        }
+      for (int ks = 0; ks < 6; ++ks) {
+        const u32x4 a = *(const u32x4*)&kb[(16 * nt + r) * KP + 256 * cg + 32 * ks + 8 * g];
+        an = mfma_f16(a, Bq[ks], an);
       }
-      const float rs = rsc[16 * nt + r];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[nt][i] = rs < 0.f ? -INFINITY : (a1[i] * rs + a2[i]) * scale;
+      const u32x4 a6 = *(const u32x4*)&kb[(16 * nt + r) * KP + 256 * cg + 192 + 8 * g];
+      const u32x4 a7 = *(const u32x4*)&kb[(16 * nt + r) * KP + 256 * cg + 224 + 8 * g];
+      if (tailw) {
+        at = mfma_f16(a6, Bq[6], at);
+        at = mfma_f16(a7, Bq[7], at);
+        *(f32x4*)&St[hg][nt][0][4 * lane] = at;
+      } else {
+        an = mfma_f16(a6, Bq[6], an);
+        an = mfma_f16(a7, Bq[7], an);
+      }
+      *(f32x4*)&Sp[wave][nt][0][4 * lane] = an;
     }
-    // online softmax per head 4g+i (rows spread over the 16 lanes of group g).
-    // The reference max m_i moves only when a tile's max exceeds it by more
-    // than 8 (probabilities stay below e^8, safe in fp32 and bf16), so the
-    // rescale of the 128 accumulators is rare; the result does not depend on
-    // the reference chosen.
-    float alpha[4];
-    bool moved = false;
+    lds_barrier();
+    // logits of this lane's head for its 8 rows; online softmax with one
+    // head per lane: the tile max and sum reduce 8 values in the lane and
+    // across the 4 lanes of the head (xor 16, xor 32).  The reference max
+    // moves only when a tile's max exceeds it by more than 8, so probabilities
+    // stay below e^8 and the rescale of the accumulators is rare.
+    float Sv[2][4];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = fmaxf(S[0][i], S[1][i]);
+    for (int nt = 0; nt < 2; ++nt) {
+      const f32x4 n0 = *(const f32x4*)&Sp[hg][nt][0][4 * lane];
+      const f32x4 n1 = *(const f32x4*)&Sp[hg + 4][nt][0][4 * lane];
+      const f32x4 tl = *(const f32x4*)&St[hg][nt][0][4 * lane];
+      const f32x4 sc = *(const f32x4*)&rsc[buf][16 * nt + 4 * g];
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      const bool move = mx > m_i[i] + 8.f;
-      const float mn = move ? mx : m_i[i];
-      const bool none = mn == -INFINITY;
-      alpha[i] = (none || !move) ? 1.f : __expf(m_i[i] - mn);
-      moved |= move && !none;
-      float ps = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        Sv[nt][i] = sc[i] < 0.f ? -INFINITY : ((n0[i] + n1[i]) * sc[i] + tl[i]) * scale;
+        mx = fmaxf(mx, Sv[nt][i]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool move = mx > m_i + 8.f;
+    const float mn = move ? mx : m_i;
+    const bool none = mn == -INFINITY;
+    const float alpha = (none || !move) ? 1.f : __expf(m_i - mn);
+    float ps = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float pv = none ? 0.f : __expf(S[nt][i] - mn);
-        S[nt][i] = pv;
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = none ? 0.f : __expf(Sv[nt][i] - mn);
+        Sv[nt][i] = pv;
         ps += pv;
       }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_i = l_i * alpha + ps;
+    m_i = mn;
+    if (__builtin_amdgcn_readfirstlane(__ballot(alpha != 1.f) != 0ull)) {
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o, 64);
-      l_i[i] = l_i[i] * alpha[i] + ps;
-      m_i[i] = mn;
+      for (int n = 0; n < 16; ++n) O[n] *= alpha;
     }
-    if (__ballot(moved)) {
+    // PV B operands: k = 8 g + e holds rows 4 g + e (e < 4) and 16 + 4 g + e - 4
+    // (e >= 4), i.e. Sv[0][e] and Sv[1][e - 4].  bpp: plain probabilities;
+    // bps (E4M3): times the row scale, for the non-RoPE channels
+    u32x4 bpp, bps;
 #pragma unroll
-      for (int n = 0; n < NO; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[n][i] *= alpha[i];
-    }
-    // probabilities -> LDS as the A operand [16 heads][32 rows], split hi + lo
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float rs = rsc[16 * nt + r];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = (4 * g + i) * VP + 16 * nt + r;
-        const float pv = S[nt][i];
-        const uint32_t hb = f32_to_bf16(pv);
-        Ps[wave][0][o] = (uint16_t)hb;
-        Ps[wave][1][o] = (uint16_t)f32_to_bf16(pv - bf16_to_f32(hb));
-        if (KVF == CKV_E4M3) {
-          const float ps = pv * fmaxf(rs, 0.f);
-          const uint32_t hs = f32_to_bf16(ps);
-          Ps[wave][2][o] = (uint16_t)hs;
-          Ps[wave][3][o] = (uint16_t)f32_to_bf16(ps - bf16_to_f32(hs));
-        }
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const int nt = e2 >> 1, i = 2 * (e2 & 1);
+      const float a = Sv[nt][i], b = Sv[nt][i + 1];
+      bpp[e2] = pk_f16(a, b);
+      if (F8) {
+        const f32x2_t sc = *(const f32x2_t*)&rsc[buf][16 * nt + 4 * g + i];
+        bps[e2] = pk_f16(a * fmaxf(sc[0], 0.f), b * fmaxf(sc[1], 0.f));
+      } else {
+        bps[e2] = bpp[e2];
       }
     }
-    __syncthreads();
-    const int pa = r * VP + 8 * g;
-    const u32x4 aph = *(const u32x4*)&Ps[wave][0][pa];
-    const u32x4 apl = *(const u32x4*)&Ps[wave][1][pa];
-    const u32x4 ash = KVF == CKV_E4M3 ? *(const u32x4*)&Ps[wave][2][pa] : aph;
-    const u32x4 asl = KVF == CKV_E4M3 ? *(const u32x4*)&Ps[wave][3][pa] : apl;
+    // channels 256 cg + 16 n + (0..15): n < 12 non-RoPE on both waves; n >= 12
+    // non-RoPE on cg 0, RoPE tail on the tail wave
+    const u32x4 bhi = tailw ? bpp : bps;
 #pragma unroll
-    for (int n = 0; n < NO; ++n) {
-      const u32x4 b = *(const u32x4*)&Vt[(16 * n + r) * VP + 8 * g];
-      const bool nope = 16 * n < DN;
-      O[n] = mfma16x16x32(as_bf16x8(nope ? ash : aph), as_bf16x8(b), O[n]);
-      O[n] = mfma16x16x32(as_bf16x8(nope ? asl : apl), as_bf16x8(b), O[n]);
+    for (int n = 0; n < 16; ++n) {
+      const uint16_t* tp = kb + tr_row * KP + 256 * cg + 16 * n + tr_col;
+      const u32x2 lo4 = ds_tr16(tp), hi4 = ds_tr16(tp + 16 * KP);
+      const u32x4 a = {lo4[0], lo4[1], hi4[0], hi4[1]};
+      O[n] = mfma_f16(a, n < 12 ? bps : bhi, O[n]);
     }
+  };
+
+  // tile loop in pairs, both halves always commit and issue (see above).
+  // Iteration t: tile t sits in LDS buffer 0 (committed earlier); multiply
+  // it, commit tile t + 1 into buffer 1 and issue the next loads; then the
+  // same with the buffers swapped.  Each tile_math has its own barrier (logit
+  // halves), and one barrier per tile publishes the next buffer.  bf16 rows
+  // keep two tiles' loads in flight in registers (S0, S1); E4M3 rows one
+  // (S0 only: with the conversion temporaries a second set would spill).
+  constexpr bool TWO = !F8;
+  pin(S0);
+  commit(S0, 0);
+  if (TWO) issue(S0, 2);
+  else issue(S0, 1);
+  lds_barrier();
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_math(0);
+    if (TWO) {
+      pin(S1);
+      commit(S1, 1);
+      issue(S1, t + 3);
+    } else {
+      pin(S0);
+      commit(S0, 1);
+      issue(S0, t + 2);
+    }
+    lds_barrier();
+    if (t + 1 < ntiles) tile_math(1);
+    pin(S0);
+    commit(S0, 0);
+    issue(S0, TWO ? t + 4 : t + 3);
+    lds_barrier();
   }
 
+  // lane (r, g) holds channels 256 cg + 16 n + 4 g + i of head `head`
   if (nsplit == 1) {
     // finish: normalise, rotate the tail back by -p, store bf16
+    const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
 #pragma unroll
-    for (int n = 0; n < NO; ++n) {
+    for (int n = 0; n < 16; ++n) {
+      const int ch = 256 * cg + 16 * n + 4 * g;
+      float v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float inv = l_i[i] > 0.f ? 1.f / l_i[i] : 0.f;
-        float v = O[n][i] * inv;
-        const int ch = 16 * n + r;
-        if (ch >= DN && !(P.flags & CKV_FLAG_NO_INV_ROPE)) {
-          const float other = __shfl_xor(v, 1, 64);
-          const int jp = (ch - DN) >> 1;
+      for (int i = 0; i < 4; ++i) v[i] = O[n][i] * inv;
+      if (tailw && n >= 12 && !(P.flags & CKV_FLAG_NO_INV_ROPE)) {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const int jp = (ch + i - DN) >> 1;
           // rotation by -p: (a, b) -> (a cos + b sin, -a sin + b cos)
-          v = (ch & 1) ? (-other * sn_[jp] + v * cs_[jp]) : (v * cs_[jp] + other * sn_[jp]);
+          const float x = v[i] * cs_[jp] + v[i + 1] * sn_[jp], y = -v[i] * sn_[jp] + v[i + 1] * cs_[jp];
+          v[i] = x;
+          v[i + 1] = y;
         }
-        out[((size_t)qn * H + h0 + 4 * g + i) * D + ch] = (uint16_t)f32_to_bf16(v);
       }
+      u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *(u32x2*)&out[((size_t)qn * H + head) * D + ch] = w;
     }
     return;
   }
-  const size_t pb = ((size_t)qn * nsplit + split) * H;
+  const size_t pb = ((size_t)qn * nsplit + split) * H + head;
 #pragma unroll
-  for (int n = 0; n < NO; ++n)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part_o[(pb + h0 + 4 * g + i) * D + 16 * n + r] = O[n][i];
-  if (r == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      part_ml[(pb + h0 + 4 * g + i) * 2] = m_i[i];
-      part_ml[(pb + h0 + 4 * g + i) * 2 + 1] = l_i[i];
-    }
+  for (int n = 0; n < 16; ++n) *(f32x4*)&part_o[pb * D + 256 * cg + 16 * n + 4 * g] = O[n];
+  if (g == 0 && cg == 0) {
+    part_ml[pb * 2] = m_i;
+    part_ml[pb * 2 + 1] = l_i;
   }
 }
 
@@ -468,16 +562,13 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
     float m[4], l[4];
     float M = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 4; ++e) {   // clamped, unconditional loads; splits past nsplit weigh 0
       const int sidx = threadIdx.x + 64 * e;
-      m[e] = -INFINITY;
-      l[e] = 0.f;
-      if (sidx < nsplit) {
-        const float2 ml = *(const float2*)(part_ml + (b0 + (size_t)sidx * H) * 2);
-        m[e] = ml.x;
-        l[e] = ml.y;
-        if (l[e] > 0.f) M = fmaxf(M, m[e]);
-      }
+      const float2 ml = *(const float2*)(part_ml + (b0 + (size_t)min(sidx, nsplit - 1) * H) * 2);
+      const bool in = sidx < nsplit;
+      m[e] = in ? ml.x : -INFINITY;
+      l[e] = in ? ml.y : 0.f;
+      if (l[e] > 0.f) M = fmaxf(M, m[e]);
     }
     M = wave_max(M);
     float L = 0.f;
@@ -498,8 +589,7 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
     float4 v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (s0 + j < nsplit && wsh[s0 + j] != 0.f) v[j] = *(const float4*)(part_o + (b0 + (size_t)(s0 + j) * H) * d + c);
+      v[j] = *(const float4*)(part_o + (b0 + (size_t)min(s0 + j, nsplit - 1) * H) * d + c);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -537,23 +627,16 @@ int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32
   float* po = (float*)(ws + L.part_o);
   float* pml = (float*)(ws + L.part_ml);
   const int ns = L.attn_splits, rps = L.attn_rows_per_split;
-  const bool mf = P.act_fmt == CKV_BF16 && P.kv_fmt != CKV_F32 && P.H % 64 == 0 &&
-                  (P.d == 512 || P.d == 128) && P.n_rot == 64;
-  if (mf) {
-    dim3 grid(nq, ns, P.H / 64);
+  if (attn_uses_tiles(P)) {
+    dim3 grid(nq * ns, P.H / 64);
     const uint16_t* qq = (const uint16_t*)q;
     uint16_t* oo = (uint16_t*)out;
-#define CKV_AM(KF, DD)                                                                              \
-  hipLaunchKernelGGL((k_attn_mfma<KF, DD>), grid, dim3(256), 0, st, P, c, qq, pos, seq, pos0, topk, rps, \
-                     ns, po, pml, oo)
-    if (P.kv_fmt == CKV_BF16) {
-      if (P.d == 512) CKV_AM(CKV_BF16, 512);
-      else CKV_AM(CKV_BF16, 128);
-    } else {
-      if (P.d == 512) CKV_AM(CKV_E4M3, 512);
-      else CKV_AM(CKV_E4M3, 128);
-    }
-#undef CKV_AM
+    if (P.kv_fmt == CKV_BF16)
+      hipLaunchKernelGGL(k_attn_tile<CKV_BF16>, grid, dim3(512), 0, st, P, c, qq, pos, seq, pos0, topk, rps, ns,
+                         po, pml, oo);
+    else
+      hipLaunchKernelGGL(k_attn_tile<CKV_E4M3>, grid, dim3(512), 0, st, P, c, qq, pos, seq, pos0, topk, rps, ns,
+                         po, pml, oo);
     if (ns == 1) return (int)hipGetLastError();
   } else {
     dim3 grid(nq, ns, P.H / 16);

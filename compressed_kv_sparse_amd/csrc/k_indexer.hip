@@ -866,6 +866,161 @@ __global__ __launch_bounds__(256) void k_topk_finish(LayerParams P, const uint32
   if (tid < 4) ctr[tid] = 0;
 }
 
+// Decode selection of one query in one block (1024 threads, V <= 32768).
+// Thread t holds the keys of rows t + 1024 e (e < 32) in registers.  The
+// score kernel's histogram of the keys' top 12 bits gives the bin b1 holding
+// the k-th largest key: rows in higher bins are selected outright; the rows
+// of bin b1 are candidates, resolved exactly with two more radix levels (bits
+// 19..8, then 7..0) in LDS, giving the k-th largest key T.  Rows above T are
+// selected, and of the rows equal to T the lowest-index ones, ranked through
+// a block scan of an equal-key bitmap.  The selection is a bitmap over the
+// rows, emitted in ascending order from a block scan of its word popcounts.
+// The histogram is returned to zero as it is read.  Should bin b1 hold more
+// keys than the candidate list takes (heavily tied scores), the threshold is
+// found by a radix select over all the keys instead.
+__global__ __launch_bounds__(1024) void k_topk_decode(LayerParams P, const uint32_t* __restrict__ keys, SelWs S,
+                                                      const int32_t* __restrict__ pos, int32_t* __restrict__ out) {
+  constexpr int KPT = 32;
+  __shared__ uint32_t bm[1024];    // selected rows
+  __shared__ uint32_t eqm[1024];   // rows whose key equals the threshold
+  __shared__ uint32_t sh[kHistBins];
+  __shared__ uint32_t ck[kCandCap], ci[kCandCap];
+  __shared__ uint32_t wsum[16], res[4], ncand;
+  const int qn = blockIdx.x, tid = threadIdx.x;
+  const int k = P.topk;
+  const IdxQuery Q = idx_query(P, pos, 0, 0, qn);
+  const int V = Q.V;
+  int32_t* o = out + (size_t)qn * k;
+  uint32_t* gh = S.hist + (size_t)qn * kHistBins;
+  // histogram bins 4 t .. 4 t + 3 and this thread's keys, one round of loads
+  const u32x4 h4 = *(const u32x4*)(gh + 4 * tid);
+  const uint32_t* kq = keys + (size_t)qn * P.cap;
+  uint32_t kr[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) kr[e] = kq[min(tid + 1024 * e, P.cap - 1)];
+  *(u32x4*)(gh + 4 * tid) = (u32x4){0u, 0u, 0u, 0u};
+  if (V <= k) {   // every visible row is taken
+    for (int j = tid; j < k; j += 1024) o[j] = j < V ? j : -1;
+    return;
+  }
+  bm[tid] = 0u;
+  eqm[tid] = 0u;
+  if (tid == 0) ncand = 0u;
+  uint32_t hv[4] = {h4[0], h4[1], h4[2], h4[3]};
+  if (tid == 0) {
+    res[0] = 0;
+    res[1] = 0;
+    res[2] = 0;
+  }
+  find_from_top<4>(hv, (uint32_t)k, wsum, res);   // ends with a barrier
+  const uint32_t b1 = res[0], A = res[1], nb1 = res[2];
+  uint32_t T, need_eq;
+  if (nb1 <= (uint32_t)kCandCap) {
+    // classify: above b1 -> selected; in b1 -> candidate
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+      const int x = tid + 1024 * e;
+      const uint32_t bin = kr[e] >> 20;
+      if (x < V && bin > b1) atomicOr(&bm[x >> 5], 1u << (x & 31));
+      if (x < V && bin == b1) {
+        const uint32_t sl = atomicAdd(&ncand, 1u);
+        if (sl < (uint32_t)kCandCap) {
+          ck[sl] = kr[e];
+          ci[sl] = (uint32_t)x;
+        }
+      }
+    }
+    __syncthreads();
+    const int nc = (int)min(ncand, (uint32_t)kCandCap);
+    uint32_t need = (uint32_t)k - A;
+    uint32_t prefix = b1 << 20, mask = 0xfff00000u;
+#pragma unroll 1
+    for (int lvl = 0; lvl < 2; ++lvl) {
+      const int shift = lvl == 0 ? 8 : 0;
+      const int nb = lvl == 0 ? 4096 : 256;
+      for (int e = tid; e < kHistBins; e += 1024) sh[e] = 0;
+      __syncthreads();
+      for (int c = tid; c < nc; c += 1024) {
+        const uint32_t key = ck[c];
+        if ((key & mask) == prefix) atomicAdd(&sh[(key >> shift) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      uint32_t v[4];
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) v[i2] = (4 * tid + i2 < nb) ? sh[4 * tid + i2] : 0u;
+      if (tid == 0) {
+        res[0] = 0;
+        res[1] = 0;
+      }
+      find_from_top<4>(v, need, wsum, res);
+      prefix |= res[0] << shift;
+      mask |= (uint32_t)(nb - 1) << shift;
+      need -= res[1];
+    }
+    T = prefix;
+    need_eq = need;
+    for (int c = tid; c < nc; c += 1024) {
+      const uint32_t key = ck[c], x = ci[c];
+      if (key > T) atomicOr(&bm[x >> 5], 1u << (x & 31));
+      else if (key == T) atomicOr(&eqm[x >> 5], 1u << (x & 31));
+    }
+  } else {
+    // heavily tied scores: radix select over all keys (d = M - key)
+    uint32_t mloc = 0;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) mloc = max(mloc, tid + 1024 * e < V ? kr[e] : 0u);
+    const uint32_t M = block_max_u32(mloc, wsum);
+    auto count_level = [&](int shift, int nbits, uint32_t pfx, uint32_t pmask, uint32_t* h) {
+      const uint32_t nbn = 1u << nbits;
+      for (int e = tid; e < (int)nbn; e += 1024) h[e] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < KPT; ++e) {
+        const uint32_t dd = M - kr[e];
+        if (tid + 1024 * e < V && (dd & pmask) == pfx) atomicAdd(&h[(dd >> shift) & (nbn - 1u)], 1u);
+      }
+      __syncthreads();
+    };
+    T = radix_select(M, (uint32_t)k, count_level, sh, wsum, res, &need_eq);
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+      const int x = tid + 1024 * e;
+      if (x < V && kr[e] > T) atomicOr(&bm[x >> 5], 1u << (x & 31));
+      else if (x < V && kr[e] == T) atomicOr(&eqm[x >> 5], 1u << (x & 31));
+    }
+  }
+  __syncthreads();
+  // the need_eq lowest-index rows equal to T join the selection
+  {
+    const uint32_t ew = eqm[tid];
+    uint32_t tot;
+    uint32_t rank = block_exscan((uint32_t)__popc(ew), wsum, &tot);
+    uint32_t keep = 0u, bits = ew;
+    while (bits && rank < need_eq) {
+      const uint32_t lowest = bits & (~bits + 1u);
+      keep |= lowest;
+      bits ^= lowest;
+      ++rank;
+    }
+    bm[tid] |= keep;
+  }
+  __syncthreads();
+  // ascending emission: word t covers rows 32 t .. 32 t + 31
+  {
+    const uint32_t wd = bm[tid];
+    uint32_t tot;
+    uint32_t slot = block_exscan((uint32_t)__popc(wd), wsum, &tot);
+    uint32_t bits = wd;
+    while (bits) {
+      const int bpos = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (slot < (uint32_t)k) o[slot] = 32 * tid + bpos;
+      ++slot;
+    }
+    for (int j = (int)tot + tid; j < k; j += 1024) o[j] = -1;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
@@ -878,7 +1033,9 @@ int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const f
   // select consumes it and leaves it (and its counters) zero
   const bool use_hist = pos && sel;
   launch_idx_score(P, c, qI, w, pos, seq, pos0, nq, keys, use_hist ? sel->hist : nullptr, stream);
-  if (use_hist) {
+  if (use_hist && P.cap <= 32768) {
+    hipLaunchKernelGGL(k_topk_decode, dim3(nq), dim3(1024), 0, st, P, keys, *sel, pos, topk);
+  } else if (use_hist) {
     dim3 grid((unsigned)((vmax + kSelChunk - 1) / kSelChunk), nq);
     hipLaunchKernelGGL(k_topk_classify, grid, dim3(256), 0, st, P, keys, *sel, pos);
     hipLaunchKernelGGL(k_topk_finish, dim3(nq), dim3(256), 0, st, P, keys, *sel, pos, topk);

@@ -79,6 +79,52 @@ __global__ __launch_bounds__(256) void k_proj_mfma(const uint16_t* __restrict__ 
   }
 }
 
+// Decode (few rows): bf16 x bf16 on MFMA, one block of 16 waves per 16
+// columns x 16 rows x one of gridDim.z slices of K.  Wave w takes the
+// slice's k-steps w, w + 16, ... (eight of them in flight per round, their
+// loads unconditional with the step index clamped); the 16 partial tiles are
+// summed through LDS in wave order, so the result is the same on every run.
+// Splitting K over blocks puts the weight stream on more compute units (a
+// unit keeps only a limited number of misses in flight).  grid: x = ncol / 16,
+// y = ceil(M / 16), z = K slices; writes part[slice][m][col].
+__global__ __launch_bounds__(1024) void k_proj_dec(const uint16_t* __restrict__ X, int M, int K, WCat wc, int ncol,
+                                                   float* __restrict__ part) {
+  __shared__ f32x4 red[16][64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int col0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+  const int ksl = K / (int)gridDim.z;   // K slice of this block (a multiple of 32)
+  int local;
+  const uint16_t* wrow = (const uint16_t*)wcat_row(wc, col0 + r, K, 2, &local) + (size_t)blockIdx.z * ksl;
+  const uint16_t* xrow = X + (size_t)min(m0 + r, M - 1) * K + (size_t)blockIdx.z * ksl;
+  const int nsteps = ksl / 32;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = wave; s0 < nsteps; s0 += 16 * 8) {
+    u32x4 a[8], b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = 32 * min(s0 + 16 * e, nsteps - 1) + 8 * g;
+      a[e] = *(const u32x4*)(xrow + k);
+      b[e] = *(const u32x4*)(wrow + k);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (s0 + 16 * e < nsteps) acc = mfma16x16x32(as_bf16x8(a[e]), as_bf16x8(b[e]), acc);
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 t = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) t += red[w][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 4 * g + i;
+      if (m < M) part[((size_t)blockIdx.z * M + m) * ncol + col0 + r] = t[i];
+    }
+  }
+}
+
 // Any formats, vector ALU: one wave per (column, 4 rows), lanes stride K.
 // grid: x = ncol, y = ceil(M / 4).  Writes split 0.
 template <int XF, int WF>
@@ -116,7 +162,10 @@ int launch_proj(const LayerParams& P, const Weights& w, const void* x, int M, fl
   wc.start[4] = P.ncol;
   if (P.ratio != 4) wc.start[2] = wc.start[3] = 1 << 30;
   const int K = P.hidden;
-  if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16) {
+  if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && M <= 64) {
+    dim3 grid(P.ncol / 16, (M + 15) / 16, splits);
+    hipLaunchKernelGGL(k_proj_dec, grid, dim3(1024), 0, st, (const uint16_t*)x, M, K, wc, P.ncol, part);
+  } else if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16) {
     const int klen = ((K / splits) + 31) / 32 * 32;
     dim3 grid((P.ncol + 63) / 64, splits, (M + 31) / 32);
     hipLaunchKernelGGL(k_proj_mfma, grid, dim3(256), 0, st, (const uint16_t*)x, M, K, wc, P.ncol,
