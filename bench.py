@@ -117,7 +117,7 @@ def prefill_flops(cfg, pos0, T):
 
 # --------------------------------------------------------------------------- decode
 
-def bench_decode(cfg, steps, warmup, with_kernel=True):
+def bench_decode(cfg, steps, warmup, with_kernel=True, api="step"):
     import torch
     from workloads import make_decode_inputs, make_layer_weights
     from workloads.gen import context_lengths
@@ -137,7 +137,10 @@ def bench_decode(cfg, steps, warmup, with_kernel=True):
     topk = torch.empty((B, cfg.top_k), dtype=torch.int32, device="cuda") if cfg.ratio == 4 else None
 
     def step():
-        dl.decode(x, u, q, qI, w, pos, out=out, topk=topk)
+        if api == "step":
+            dl.decode_step(x, u, q, qI, w, pos, out=out, topk=topk)
+        else:
+            dl.decode(x, u, q, qI, w, pos, out=out, topk=topk)
 
     step()
     torch.cuda.synchronize()
@@ -331,6 +334,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c5")
+    ap.add_argument("--api", choices=("step", "calls"), default="step",
+                    help="decode through the single decode-step entry point or the three stage calls")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=3)
@@ -371,7 +376,7 @@ def main():
         print(json.dumps({"part": "stack", **bench_stack(args.stack_steps, 3)}), flush=True)
         return
     cfg = get_config(args.workload)
-    r = bench_decode(cfg, args.steps, args.warmup)
+    r = bench_decode(cfg, args.steps, args.warmup, api=args.api)
     log(f"[bench] decode {cfg.name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['tok_s']:.0f} tok/s, "
         f"step {r['step_gbs']:.0f} GB/s ({100 * r['step_hbm_frac']:.1f}% of HBM)")
     kern = r.get("kernel")

@@ -95,6 +95,7 @@ def _load() -> ctypes.CDLL:
         "ckv_indexer_score_decode": [D, C, VP, VP, VP, I32, VP, VP],
         "ckv_sparse_swa_attn_decode": [D, C, VP, VP, VP, I32, VP, VP, SZ, VP],
         "ckv_sparse_swa_attn_prefill": [D, C, VP, I32, I32, I32, VP, VP, VP, SZ, VP],
+        "ckv_decode_step": [D, Wt, C, VP, VP, VP, VP, VP, VP, I32, VP, VP, VP, SZ, VP],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -109,7 +110,7 @@ EXPORTS = ("ckv_row_bytes", "ckv_validate", "ckv_strerror", "ckv_last_hip_error"
            "ckv_workspace_sync_bytes",
            "ckv_compress_append_decode", "ckv_compress_append_prefill", "ckv_indexer_topk_decode",
            "ckv_indexer_topk_prefill", "ckv_indexer_score_decode", "ckv_sparse_swa_attn_decode",
-           "ckv_sparse_swa_attn_prefill")
+           "ckv_sparse_swa_attn_prefill", "ckv_decode_step")
 
 
 def strerror(code: int) -> str:
@@ -178,3 +179,8 @@ def sparse_swa_attn_decode(desc, cache, q, pos, topk, B, out, ws, ws_bytes, stre
 def sparse_swa_attn_prefill(desc, cache, q, seq, pos0, T, topk, out, ws, ws_bytes, stream=None) -> int:
     return lib.ckv_sparse_swa_attn_prefill(_ref(desc), _ref(cache), _p(q), int(seq), int(pos0), int(T),
                                            _p(topk), _p(out), _p(ws), int(ws_bytes), stream)
+
+
+def decode_step(desc, weights, cache, x, u, q, qI, w, pos, B, topk, out, ws, ws_bytes, stream=None) -> int:
+    return lib.ckv_decode_step(_ref(desc), _ref(weights), _ref(cache), _p(x), _p(u), _p(q), _p(qI), _p(w),
+                               _p(pos), int(B), _p(topk), _p(out), _p(ws), int(ws_bytes), stream)

@@ -240,6 +240,43 @@ extern "C" int ckv_sparse_swa_attn_prefill(const ckv_layer_desc* desc, const ckv
       launch_attn(P, to_cache(cache), q, nullptr, seq, pos0, T, topk, out, L, (uint8_t*)ws, stream));
 }
 
+extern "C" int ckv_decode_step(const ckv_layer_desc* desc, const ckv_layer_weights* w,
+                               const ckv_layer_cache* cache, const void* x, const void* u, const void* q,
+                               const void* qI, const float* iw, const int32_t* pos, int32_t B, int32_t* topk,
+                               void* out, void* ws, size_t ws_bytes, void* stream) {
+  LayerParams P;
+  int rc = prologue(desc, cache, &P);
+  if (rc) return rc;
+  if (B < 1) return CKV_E_INVAL;
+  if (B > P.batch) return CKV_E_CAPACITY;
+  if ((rc = weights_ok(P, w))) return rc;
+  if (check_ptr(u) || check_ptr(q) || check_ptr(pos) || check_ptr(out) || (P.ratio && check_ptr(x)))
+    return CKV_E_INVAL;
+  if (P.ratio == 4 && (check_ptr(qI) || check_ptr(iw) || check_ptr(topk))) return CKV_E_INVAL;
+  WsLayout L;
+  if ((rc = check_ws(P, CKV_MODE_DECODE, B, ws, ws_bytes, &L))) return rc;
+  if (P.ratio != 4 || !step_fusable(P, B)) {
+    if ((rc = ckv_compress_append_decode(desc, w, cache, x, u, pos, B, ws, ws_bytes, stream))) return rc;
+    if (P.ratio == 4 && (rc = ckv_indexer_topk_decode(desc, cache, qI, iw, pos, B, topk, ws, ws_bytes, stream)))
+      return rc;
+    return ckv_sparse_swa_attn_decode(desc, cache, q, pos, P.ratio == 4 ? topk : nullptr, B, out, ws, ws_bytes,
+                                      stream);
+  }
+  clear_stale();
+  uint8_t* wb = (uint8_t*)ws;
+  SelWs sel;
+  sel.hist = (uint32_t*)(wb + L.hist);
+  sel.ctr = (uint32_t*)(wb + L.ctr);
+  sel.sure = (uint32_t*)(wb + L.sure);
+  sel.cand_key = (uint32_t*)(wb + L.cand_key);
+  sel.cand_idx = (uint32_t*)(wb + L.cand_idx);
+  const Cache C = to_cache(cache);
+  if ((rc = launch_step_scan_select(P, to_weights(w), C, x, u, qI, iw, pos, B, (float*)(wb + L.proj),
+                                    (uint32_t*)(wb + L.keys), sel, topk, stream)))
+    return launched(rc);
+  return launched(launch_attn(P, C, q, pos, 0, 0, B, topk, out, L, wb, stream));
+}
+
 extern "C" const char* ckv_last_hip_error(void) {
   return t_last_hip ? hipGetErrorName((hipError_t)t_last_hip) : "none";
 }

@@ -113,5 +113,11 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
 int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32_t* pos, int seq,
                 int pos0, int nq, const int32_t* topk, void* out, const WsLayout& L, uint8_t* ws,
                 void* stream);
+// fused decode step of a ratio-4 layer: projection + scan of the existing rows
+// in one launch, then per-sequence compressor + new-row score + selection
+bool step_fusable(const LayerParams& P, int B);
+int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache& c, const void* x,
+                            const void* u, const void* qI, const float* wt, const int32_t* pos, int B,
+                            float* proj, uint32_t* keys, const SelWs& sel, int32_t* topk, void* stream);
 
 }  // namespace ckv

@@ -1,0 +1,433 @@
+// Device code of the per-token compressor shared by the decode kernels:
+// row helpers, the online pooling accumulator and the per-sequence decode
+// body (state store, window pooling, RMSNorm, tail RoPE and cache insertion,
+// "ds4.c を読み解く (#3)" sections 4-5; fused the way the vLLM DeepSeek V4
+// page fuses compressor + RMSNorm + RoPE + cache insertion).
+#pragma once
+
+#include <type_traits>
+
+#include "ckv_device.h"
+
+namespace ckv {
+
+// ------------------------------------------------------------ row helpers
+
+// Rotate the last `nrot` entries of z[0..width) (LDS) at position `pos`.
+// Caller synchronises before and after.
+__device__ __forceinline__ void rope_lds(const LayerParams& P, float* z, int width, int nrot, double pos) {
+  const int dn = width - nrot;
+  for (int j = threadIdx.x; j < nrot / 2; j += blockDim.x) {
+    float c, s;
+    rope_cs(P, j, pos, &c, &s);
+    const float a = z[dn + 2 * j], b = z[dn + 2 * j + 1];
+    z[dn + 2 * j] = a * c - b * s;
+    z[dn + 2 * j + 1] = a * s + b * c;
+  }
+}
+
+// z <- gamma * z / sqrt(mean(z^2) + eps), channels owned as c = tid + k*blockDim.
+__device__ __forceinline__ void rmsnorm_lds(float* z, int width, const float* gamma, float eps,
+                                            float* red) {
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < width; c += blockDim.x) ss += z[c] * z[c];
+  ss = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)width + eps);
+  for (int c = threadIdx.x; c < width; c += blockDim.x) z[c] = gamma[c] * (z[c] * inv);
+}
+
+// Store z[0..d) (LDS) as one K=V row record of format KVF.  All threads call.
+template <int KVF>
+__device__ __forceinline__ void store_row(uint8_t* dst, const float* z, int d, int n_rot,
+                                          float* red) {
+  if constexpr (KVF == CKV_F32) {
+    for (int c = threadIdx.x; c < d; c += blockDim.x) ((float*)dst)[c] = z[c];
+  } else if constexpr (KVF == CKV_BF16) {
+    for (int c = threadIdx.x; c < d; c += blockDim.x) ((uint16_t*)dst)[c] = (uint16_t)f32_to_bf16(z[c]);
+  } else {
+    const int dn = d - n_rot;
+    float amax = 0.f;
+    for (int c = threadIdx.x; c < dn; c += blockDim.x) amax = fmaxf(amax, fabsf(z[c]));
+    amax = block_max(amax, red);
+    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    for (int c = threadIdx.x; c < dn; c += blockDim.x) dst[c] = (uint8_t)f32_to_e4m3(z[c] / s);
+    uint16_t* tail = (uint16_t*)(dst + dn);
+    for (int c = threadIdx.x; c < n_rot; c += blockDim.x) tail[c] = (uint16_t)f32_to_bf16(z[dn + c]);
+    if (threadIdx.x == 0) *(float*)(dst + dn + 2 * n_rot) = s;
+  }
+}
+
+template <int F>
+__device__ __forceinline__ void store_vals(void* dst, const float* z, int n) {
+  for (int c = threadIdx.x; c < n; c += blockDim.x) store_val<F>(dst, c, z[c]);
+}
+
+// Online per-channel softmax pooling over one window (same result as the
+// max / exp / normalise sequence of the pages, one pass).
+struct PoolAcc {
+  float m = -INFINITY, s = 0.f, acc = 0.f;
+  __device__ __forceinline__ void add(float e, float kv) {
+    if (e > m) {
+      const float f = expf(m - e);
+      s = s * f + 1.f;
+      acc = acc * f + kv;
+      m = e;
+    } else {
+      const float w = expf(e - m);
+      s += w;
+      acc += w * kv;
+    }
+  }
+  __device__ __forceinline__ float value() const { return s > 0.f ? acc / s : 0.f; }
+};
+
+// ------------------------------------------------------------ decode
+
+template <int F>
+__device__ __forceinline__ float2 load2(const void* p, long i) {  // i even
+  if constexpr (F == CKV_F32) return *(const float2*)((const float*)p + i);
+  else {
+    const uint32_t w = *(const uint32_t*)((const uint16_t*)p + i);
+    return make_float2(bf16_to_f32(w & 0xffffu), bf16_to_f32(w >> 16));
+  }
+}
+
+__device__ __forceinline__ float2 ld2(const float* p) { return *(const float2*)p; }
+
+// Store one row from per-thread channel pairs (c, c+1) in format KVF.  Every
+// thread of the block calls (the E4M3 row scale is a block-wide max).
+template <int KVF>
+__device__ __forceinline__ void store_row2(uint8_t* dst, float2 z, int c, bool act, int d, int n_rot,
+                                           float* red) {
+  if constexpr (KVF == CKV_F32) {
+    if (act) *(float2*)(dst + 4 * c) = z;
+  } else if constexpr (KVF == CKV_BF16) {
+    if (act) *(uint32_t*)(dst + 2 * c) = pack_bf16x2(z.x, z.y);
+  } else {
+    const int dn = d - n_rot;
+    const float amax = block_max(act && c < dn ? fmaxf(fabsf(z.x), fabsf(z.y)) : 0.f, red);
+    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (act) {
+      if (c < dn) *(uint16_t*)(dst + c) = (uint16_t)(f32_to_e4m3(z.x / s) | (f32_to_e4m3(z.y / s) << 8));
+      else *(uint32_t*)(dst + dn + 2 * (c - dn)) = pack_bf16x2(z.x, z.y);
+    }
+    if (threadIdx.x == 0) *(float*)(dst + dn + 2 * n_rot) = s;
+  }
+}
+
+// Rotate the pair (c, c+1) if it lies in the last n_rot channels of `width`.
+__device__ __forceinline__ float2 rope2(const LayerParams& P, float2 z, int c, int width, int nrot, double pos) {
+  const int dn = width - nrot;
+  if (c < dn) return z;
+  float cs, sn;
+  rope_cs(P, (c - dn) >> 1, pos, &cs, &sn);
+  return make_float2(z.x * cs - z.y * sn, z.x * sn + z.y * cs);
+}
+
+// Pool channels (c, c+1) of row i over its window.  Token p's own values come
+// from registers; the other W-1 tokens from the state ring.  Loads go out in
+// groups of 8 slots before the group is accumulated.
+__device__ __forceinline__ float2 pool2(const float* skv, const float* ssc, const float* ape, int width, int W,
+                                        int r, int i, int p, float2 kcur, float2 scur, int c) {
+  PoolAcc a0, a1;
+  const int t0 = i * r - (W - r);
+  for (int j0 = 0; j0 < W; j0 += 8) {
+    float2 kv[8], sc[8], ap[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int t = t0 + j0 + jj;
+      kv[jj] = sc[jj] = make_float2(0.f, 0.f);
+      if (t >= 0 && t != p) {
+        kv[jj] = ld2(skv + (size_t)(t % W) * width + c);
+        sc[jj] = ld2(ssc + (size_t)(t % W) * width + c);
+      }
+      ap[jj] = ld2(ape + (size_t)(j0 + jj) * width + c);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int t = t0 + j0 + jj;
+      if (t < 0) continue;
+      const float2 k = t == p ? kcur : kv[jj];
+      const float2 e = t == p ? scur : sc[jj];
+      a0.add(e.x + ap[jj].x, k.x);
+      a1.add(e.y + ap[jj].y, k.y);
+    }
+  }
+  return make_float2(a0.value(), a1.value());
+}
+
+// Decode: one block per sequence; thread t works on the channel pair
+// c = 2 (t % NP) (NP = d / 2 pairs) and, on ratio 4, on the indexer pair of
+// the same index (t % NP < D_I / 2).  TPC threads share a pair: part
+// t / NP pools W / TPC of the window's slots, and the parts' online-softmax
+// states are merged through LDS.
+//
+// The window state is a ring: token t sits in slot t % W, and the row closed
+// by token p = i r + r - 1 pools tokens t0 .. t0 + W - 1 with t0 = i r - (W - r),
+// i.e. every slot of the ring, token t0 + j in slot (t0 + j) % W.  So the ring
+// loads do not depend on p and go out together with this token's inputs; p
+// only decides which window position j (and APE row) each slot takes, which
+// slot is the current token (taken from registers, its ring slot still holds
+// token p - W), and which positions precede token 0 (no weight).
+//   c4a  (W 8,   r 4):   t0 % 8 is 0 or 4, so j = s ^ (t0 & 4)
+//   c128a (W 128, r 128): t0 % 128 = 0, so j = s
+// Every load is unconditional (clamped indices, values selected afterwards);
+// on c128a the ring is read only on a boundary step (a block-uniform branch),
+// in rounds of 8 slots per thread.  On c4a with TPC parts, part q holds slots
+// q + TPC e: flipping by 4 maps that set onto itself (slot q + TPC e takes the
+// APE row of local index e ^ (4 / TPC)), so its loads do not depend on p.
+namespace cmp {
+// block-wide sum and max (every thread returns the totals); red: 2 * 32 floats
+__device__ __forceinline__ float2 block_sum_max(float s, float m, float* red) {
+  s = wave_sum(s);
+  m = wave_max(m);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    red[w] = s;
+    red[32 + w] = m;
+  }
+  __syncthreads();
+  float ts = 0.f, tm = 0.f;
+  for (int i = 0; i < nw; ++i) {
+    ts += red[i];
+    tm = fmaxf(tm, red[32 + i]);
+  }
+  return make_float2(ts, tm);
+}
+}  // namespace cmp
+
+// The per-sequence body, called by every thread of a block of at least
+// TPC * d / 2 threads (threads past that take part in the reductions only).
+// Returns 1 when the token closed a row (on ratio 4 the indexer row's stored
+// values are left in idx_row[0 .. D_I) when idx_row is non-NULL), 0 when it
+// did not, -1 for a negative position.  red: 64 floats of LDS; mrg: the
+// parts' merge area (TPC > 1): TPC * d / 2 * 6 floats, plus TPC * D_I / 2 * 6
+// on c4a.
+template <int KVF, int IDXF, int ACTF, int W, int TPC, int MAXS = 4>
+__device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const Weights& w, const Cache& cc,
+                                                   const void* __restrict__ u, const int32_t* __restrict__ pos,
+                                                   const float* __restrict__ proj, int splits, int B, int b,
+                                                   float* red, float* mrg, float* idx_row) {
+  constexpr int SPT = W / TPC;                 // slots per thread
+  constexpr int RND = SPT < 8 ? SPT : 8;       // slots per load round
+  constexpr int r = W == 8 ? 4 : 128;
+  const int d = P.d, DI = P.DI, NP = d / 2;
+  const int tid = threadIdx.x;
+  const int pair = tid % NP, part = min(tid / NP, TPC);
+  const int c = 2 * pair;
+  const bool ilane = W == 8 && pair < DI / 2;  // indexer channels (ratio 4)
+  const int ci = 2 * min(pair, max(DI / 2 - 1, 0));
+
+  // this token's inputs and, on c4a, the whole ring: one round of loads
+  const int p = pos[b];
+  const float2 uu = load2<ACTF>(u, (long)b * d + c);
+  // projection partials (at most MAXS K slices), summed in slice order
+  float2 ka = make_float2(0.f, 0.f), sa = ka, kia = ka, sia = ka;
+  {
+    float2 pk[MAXS], psg[MAXS], pki[MAXS], psi[MAXS];
+#pragma unroll
+    for (int q = 0; q < MAXS; ++q) {
+      const float* pj = proj + ((size_t)min(q, splits - 1) * B + b) * P.ncol;
+      pk[q] = ld2(pj + c);
+      psg[q] = ld2(pj + d + c);
+      if (W == 8) {
+        pki[q] = ld2(pj + 2 * d + ci);
+        psi[q] = ld2(pj + 2 * d + DI + ci);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < MAXS; ++q) {
+      if (q < splits) {
+        ka.x += pk[q].x; ka.y += pk[q].y;
+        sa.x += psg[q].x; sa.y += psg[q].y;
+        if (W == 8) {
+          kia.x += pki[q].x; kia.y += pki[q].y;
+          sia.x += psi[q].x; sia.y += psi[q].y;
+        }
+      }
+    }
+  }
+  const float* skv = cc.st_kv + (size_t)b * W * d;
+  const float* ssc = cc.st_sc + (size_t)b * W * d;
+  static_assert(W != 8 || (TPC == 1 || TPC == 2 || TPC == 4), "c4a parts must divide the flip");
+  constexpr int S8 = W == 8 ? 8 / TPC : 1;   // c4a ring slots per thread
+  const int q8 = min(part, TPC - 1);         // threads past the parts mirror the last one's loads
+  float2 rk[S8], rs[S8], ap[S8], irk[S8], irs[S8], iap[S8];
+  float2 gm = make_float2(1.f, 1.f), gmi = gm;
+  if (W == 8) {
+    const float* ikv = cc.ist_kv + (size_t)b * 8 * DI;
+    const float* isc = cc.ist_sc + (size_t)b * 8 * DI;
+#pragma unroll
+    for (int e = 0; e < S8; ++e) {
+      const int sl = q8 + TPC * e;
+      rk[e] = ld2(skv + sl * d + c);
+      rs[e] = ld2(ssc + sl * d + c);
+      ap[e] = ld2(w.ape + sl * d + c);
+      irk[e] = ld2(ikv + sl * DI + ci);
+      irs[e] = ld2(isc + sl * DI + ci);
+      iap[e] = ld2(w.idx_ape + sl * DI + ci);
+    }
+    gm = ld2(w.gamma + c);
+    gmi = ld2(w.idx_gamma + ci);
+  }
+
+  if (p < 0) {
+    if (tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_BAD_POS);
+    return -1;
+  }
+  const bool emit = (p + 1) % r == 0;
+  const int i = (p + 1) / r - 1;
+  if (emit && i >= P.cap && tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_CAPACITY);
+  const bool pool = emit && i < P.cap;
+  const int t0 = i * r - (W - r);
+  const int cur = p & (W - 1);
+
+  // ---- pooling: online softmax per channel over this thread's slots
+  PoolAcc a0, a1, b0, b1;
+  if (pool) {
+    if (W == 8) {
+      // the flip (t0 & 4) is block-uniform; both forms are instantiated with
+      // compile-time slot indices so the register arrays stay in registers
+      auto pool8 = [&](auto flip) {
+        constexpr int F = decltype(flip)::value;
+        constexpr int FE = F / TPC;   // the flip in local slot indices
+#pragma unroll
+        for (int e = 0; e < S8; ++e) {
+          const int sl = q8 + TPC * e;
+          const int j = sl ^ F;
+          const bool valid = t0 + j >= 0 && part < TPC;
+          const bool self = sl == cur;
+          const float2 kk = self ? ka : rk[e], ss = self ? sa : rs[e];
+          const float2 ikk = self ? kia : irk[e], iss = self ? sia : irs[e];
+          if (valid) {
+            a0.add(ss.x + ap[e ^ FE].x, kk.x);
+            a1.add(ss.y + ap[e ^ FE].y, kk.y);
+            b0.add(iss.x + iap[e ^ FE].x, ikk.x);
+            b1.add(iss.y + iap[e ^ FE].y, ikk.y);
+          }
+        }
+      };
+      if (t0 & 4) pool8(std::integral_constant<int, 4>{});
+      else pool8(std::integral_constant<int, 0>{});
+    } else {
+      // c128a: j = slot; the window starts at t0 = 128 i >= 0
+#pragma unroll 1
+      for (int s0 = part * SPT; s0 < (part + 1) * SPT && part < TPC; s0 += RND) {
+        float2 kk[RND], ss[RND], aa[RND];
+#pragma unroll
+        for (int e = 0; e < RND; ++e) {
+          kk[e] = ld2(skv + (s0 + e) * d + c);
+          ss[e] = ld2(ssc + (s0 + e) * d + c);
+          aa[e] = ld2(w.ape + (s0 + e) * d + c);
+        }
+#pragma unroll
+        for (int e = 0; e < RND; ++e) {
+          const bool self = s0 + e == cur;
+          const float2 k2 = self ? ka : kk[e], s2 = self ? sa : ss[e];
+          a0.add(s2.x + aa[e].x, k2.x);
+          a1.add(s2.y + aa[e].y, k2.y);
+        }
+      }
+    }
+  }
+  float2 y = make_float2(a0.value(), a1.value());
+  float2 yi = make_float2(b0.value(), b1.value());
+  if (TPC > 1) {
+    // merge the parts' (max, sum, acc) per channel; part 0 ends with the row.
+    // mrg: attention pairs [TPC][NP][6], then (c4a) indexer pairs [TPC][DI/2][6]
+    float* mi = mrg + TPC * NP * 6;
+    if (pool && part < TPC) {
+      float* mm = mrg + (part * NP + pair) * 6;
+      mm[0] = a0.m; mm[1] = a0.s; mm[2] = a0.acc;
+      mm[3] = a1.m; mm[4] = a1.s; mm[5] = a1.acc;
+      if (W == 8 && ilane) {
+        float* mb = mi + (part * (DI / 2) + pair) * 6;
+        mb[0] = b0.m; mb[1] = b0.s; mb[2] = b0.acc;
+        mb[3] = b1.m; mb[4] = b1.s; mb[5] = b1.acc;
+      }
+    }
+    __syncthreads();
+    if (pool && part == 0) {
+      auto merge = [](PoolAcc& x, float m, float s, float acc) {
+        if (s == 0.f) return;
+        if (x.s == 0.f) { x.m = m; x.s = s; x.acc = acc; return; }
+        const float mx = fmaxf(x.m, m);
+        const float fa = expf(x.m - mx), fb = expf(m - mx);
+        x.s = x.s * fa + s * fb;
+        x.acc = x.acc * fa + acc * fb;
+        x.m = mx;
+      };
+      PoolAcc t0a = a0, t1a = a1;
+      for (int q = 1; q < TPC; ++q) {
+        const float* mm = mrg + (q * NP + pair) * 6;
+        merge(t0a, mm[0], mm[1], mm[2]);
+        merge(t1a, mm[3], mm[4], mm[5]);
+      }
+      y = make_float2(t0a.value(), t1a.value());
+      if (W == 8 && ilane) {
+        PoolAcc t0b = b0, t1b = b1;
+        for (int q = 1; q < TPC; ++q) {
+          const float* mb = mi + (q * (DI / 2) + pair) * 6;
+          merge(t0b, mb[0], mb[1], mb[2]);
+          merge(t1b, mb[3], mb[4], mb[5]);
+        }
+        yi = make_float2(t0b.value(), t1b.value());
+      }
+    }
+  }
+  const bool own = part == 0;   // the thread that stores this pair
+
+  // ---- raw sliding-window row: u rotated at p into slot p % swa
+  {
+    const float2 z = rope2(P, uu, c, d, P.n_rot, p);
+    store_row2<KVF>(cc.raw + ((size_t)b * P.swa + (p & (P.swa - 1))) * P.row_bytes, z, c, own, d, P.n_rot, red);
+  }
+  // ---- this token's projections -> state slot p % W
+  if (own) {
+    const size_t o = ((size_t)b * W + cur) * d + c;
+    *(float2*)(cc.st_kv + o) = ka;
+    *(float2*)(cc.st_sc + o) = sa;
+  }
+  if (W == 8 && own && ilane) {
+    const size_t o = ((size_t)b * 8 + cur) * DI + c;
+    *(float2*)(cc.ist_kv + o) = kia;
+    *(float2*)(cc.ist_sc + o) = sia;
+  }
+  if (!pool) return 0;
+  if (W == 128 && TPC > 1) gm = own ? ld2(w.gamma + c) : gm;
+
+  // ---- attention lane: RMSNorm, tail RoPE at i r, store row i
+  {
+    const float ss = cmp::block_sum_max(own ? y.x * y.x + y.y * y.y : 0.f, 0.f, red).x;
+    const float inv = 1.0f / sqrtf(ss / (float)d + P.eps);
+    const float2 z = rope2(P, make_float2(gm.x * (y.x * inv), gm.y * (y.y * inv)), c, d, P.n_rot, (double)i * r);
+    store_row2<KVF>(cc.comp + ((size_t)b * P.cap + i) * P.row_bytes, z, c, own, d, P.n_rot, red);
+  }
+  if (W == 8) {  // indexer lane: its own compressor of the same form
+    const float ss = cmp::block_sum_max(own && ilane ? yi.x * yi.x + yi.y * yi.y : 0.f, 0.f, red).x;
+    const float inv = 1.0f / sqrtf(ss / (float)DI + P.eps);
+    if (own && ilane) {
+      const float2 z = rope2(P, make_float2(gmi.x * (yi.x * inv), gmi.y * (yi.y * inv)), c, DI, P.idx_rot,
+                             (double)i * r);
+      uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * DI * (IDXF == CKV_F32 ? 4 : 2);
+      if (IDXF == CKV_F32) {
+        *(float2*)(dst + 4 * c) = z;
+        if (idx_row) {
+          idx_row[c] = z.x;
+          idx_row[c + 1] = z.y;
+        }
+      } else {
+        const uint32_t pz = pack_bf16x2(z.x, z.y);
+        *(uint32_t*)(dst + 2 * c) = pz;
+        if (idx_row) {
+          idx_row[c] = bf16_to_f32(pz & 0xffffu);
+          idx_row[c + 1] = bf16_to_f32(pz >> 16);
+        }
+      }
+    }
+  }
+  return 1;
+}
+
+}  // namespace ckv

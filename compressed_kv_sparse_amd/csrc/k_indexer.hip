@@ -13,7 +13,8 @@
 // piling into a few; when fewer than k keys fall in that range it widens the
 // range and counts again.  Every row above the k-th key is emitted, plus the
 // lowest-index rows equal to it, in ascending index order.
-#include "ckv_device.h"
+#include "compress_dec.h"
+#include "proj_dec.h"
 
 namespace ckv {
 
@@ -59,13 +60,15 @@ constexpr int kScoreBufs = 2;
 // last row block of a query can run past it); written, never read.
 __device__ uint32_t g_key_sink[64];
 
+// The body as a device function: block (bx, qn) of the grid above.
+// old_only: the rows of the query's cache except the row its own token
+// closes (a decode step whose compressor runs concurrently scores that row
+// separately).
 template <int MT, int KS, int QF, bool HIST>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_idx_score_mfma(LayerParams P, const uint16_t* idx,
-                                                        const void* __restrict__ qI,
-                                                        const float* __restrict__ wt,
-                                                        const int32_t* __restrict__ pos, int seq_fixed,
-                                                        int pos0, uint32_t* __restrict__ keys,
-                                                        uint32_t* __restrict__ hist) {
+__device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint16_t* idx, const void* __restrict__ qI,
+                                                const float* __restrict__ wt, const int32_t* __restrict__ pos,
+                                                int seq_fixed, int pos0, uint32_t* __restrict__ keys,
+                                                uint32_t* __restrict__ hist, int bx, int qn, bool old_only) {
   constexpr int DI = KS * 32;
   constexpr int HP = MT * 16;
   constexpr int RB = 256 * kScoreGroups;
@@ -73,9 +76,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float wsh[HP];
   __shared__ float cs_[32], sn_[32];
   __shared__ uint32_t lh[kHistBins];
-  const int qn = blockIdx.y;
-  const IdxQuery Q = idx_query(P, pos, seq_fixed, pos0, qn);
-  const int rb0 = blockIdx.x * RB;
+  IdxQuery Q = idx_query(P, pos, seq_fixed, pos0, qn);
+  if (old_only && Q.p >= 0 && (Q.p + 1) % 4 == 0 && (Q.p + 1) / 4 <= P.cap) Q.V -= 1;
+  const int rb0 = bx * RB;
   if (rb0 >= Q.V) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -223,6 +226,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (v) atomicAdd(&gh[e], v);
     }
   }
+}
+
+template <int MT, int KS, int QF, bool HIST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_idx_score_mfma(
+    LayerParams P, const uint16_t* idx, const void* __restrict__ qI, const float* __restrict__ wt,
+    const int32_t* __restrict__ pos, int seq_fixed, int pos0, uint32_t* __restrict__ keys,
+    uint32_t* __restrict__ hist) {
+  idx_score_block<MT, KS, QF, HIST>(P, idx, qI, wt, pos, seq_fixed, pos0, keys, hist, blockIdx.x, blockIdx.y, false);
 }
 
 // ---------------------------------------------------------------- vector score
@@ -878,35 +889,23 @@ __global__ __launch_bounds__(256) void k_topk_finish(LayerParams P, const uint32
 // The histogram is returned to zero as it is read.  Should bin b1 hold more
 // keys than the candidate list takes (heavily tied scores), the threshold is
 // found by a radix select over all the keys instead.
-__global__ __launch_bounds__(1024) void k_topk_decode(LayerParams P, const uint32_t* __restrict__ keys, SelWs S,
-                                                      const int32_t* __restrict__ pos, int32_t* __restrict__ out) {
-  constexpr int KPT = 32;
+constexpr int kSelKPT = 32;   // keys per thread of the one-block decode selection
+
+// The selection itself, from keys kr (row tid + 1024 e) and histogram bins
+// hv (bins 4 tid .. 4 tid + 3) held by the 1024 threads of the block.
+__device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, uint32_t (&kr)[kSelKPT],
+                                                   uint32_t (&hv)[4], int32_t* __restrict__ o) {
+  constexpr int KPT = kSelKPT;
   __shared__ uint32_t bm[1024];    // selected rows
   __shared__ uint32_t eqm[1024];   // rows whose key equals the threshold
   __shared__ uint32_t sh[kHistBins];
   __shared__ uint32_t ck[kCandCap], ci[kCandCap];
   __shared__ uint32_t wsum[16], res[4], ncand;
-  const int qn = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int k = P.topk;
-  const IdxQuery Q = idx_query(P, pos, 0, 0, qn);
-  const int V = Q.V;
-  int32_t* o = out + (size_t)qn * k;
-  uint32_t* gh = S.hist + (size_t)qn * kHistBins;
-  // histogram bins 4 t .. 4 t + 3 and this thread's keys, one round of loads
-  const u32x4 h4 = *(const u32x4*)(gh + 4 * tid);
-  const uint32_t* kq = keys + (size_t)qn * P.cap;
-  uint32_t kr[KPT];
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) kr[e] = kq[min(tid + 1024 * e, P.cap - 1)];
-  *(u32x4*)(gh + 4 * tid) = (u32x4){0u, 0u, 0u, 0u};
-  if (V <= k) {   // every visible row is taken
-    for (int j = tid; j < k; j += 1024) o[j] = j < V ? j : -1;
-    return;
-  }
   bm[tid] = 0u;
   eqm[tid] = 0u;
   if (tid == 0) ncand = 0u;
-  uint32_t hv[4] = {h4[0], h4[1], h4[2], h4[3]};
   if (tid == 0) {
     res[0] = 0;
     res[1] = 0;
@@ -1021,6 +1020,143 @@ __global__ __launch_bounds__(1024) void k_topk_decode(LayerParams P, const uint3
   }
 }
 
+__global__ __launch_bounds__(1024) void k_topk_decode(LayerParams P, const uint32_t* __restrict__ keys, SelWs S,
+                                                      const int32_t* __restrict__ pos, int32_t* __restrict__ out) {
+  const int qn = blockIdx.x, tid = threadIdx.x;
+  const int k = P.topk;
+  const IdxQuery Q = idx_query(P, pos, 0, 0, qn);
+  const int V = Q.V;
+  int32_t* o = out + (size_t)qn * k;
+  uint32_t* gh = S.hist + (size_t)qn * kHistBins;
+  // histogram bins 4 t .. 4 t + 3 and this thread's keys, one round of loads
+  const u32x4 h4 = *(const u32x4*)(gh + 4 * tid);
+  const uint32_t* kq = keys + (size_t)qn * P.cap;
+  uint32_t kr[kSelKPT];
+#pragma unroll
+  for (int e = 0; e < kSelKPT; ++e) kr[e] = kq[min(tid + 1024 * e, P.cap - 1)];
+  *(u32x4*)(gh + 4 * tid) = (u32x4){0u, 0u, 0u, 0u};
+  if (V <= k) {   // every visible row is taken
+    for (int j = tid; j < k; j += 1024) o[j] = j < V ? j : -1;
+    return;
+  }
+  uint32_t hv[4] = {h4[0], h4[1], h4[2], h4[3]};
+  topk_decode_select(P, V, kr, hv, o);
+}
+
+// ---------------------------------------------------------------- fused decode step
+// One decode step of a ratio-4 layer in three launches (plus the attention
+// merge): the compressor's projection runs inside the score scan's launch
+// (the rows the scan reads do not depend on it), and one block per sequence
+// then runs the compressor, scores the row its token closed and selects.
+//
+// k_step_scan: blocks [0, nproj) compute the projection tiles (16 columns x
+// 16 rows each, 4 waves over K); the others score the query's cache rows
+// except the row its own token closes, building the key histogram.
+template <int MT, int QF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_step_scan(
+    LayerParams P, const uint16_t* idx, const void* __restrict__ qI, const float* __restrict__ wt,
+    const int32_t* __restrict__ pos, uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
+    const uint16_t* __restrict__ X, int M, WCat wc, float* __restrict__ proj, int nproj, int nrb) {
+  const int bid = blockIdx.x;
+  if (bid < nproj) {
+    const int ncb = P.ncol / 16;
+    proj_tile<4>(X, M, P.hidden, wc, P.ncol, proj, 16 * (bid % ncb), 16 * (bid / ncb));
+    return;
+  }
+  const int i = bid - nproj;
+  idx_score_block<MT, 4, QF, true>(P, idx, qI, wt, pos, 0, 0, keys, hist, i % nrb, i / nrb, true);
+}
+
+// k_step_select: one block of 1024 threads per sequence.  The query's keys
+// and histogram are loaded first; the compressor (state store, raw row,
+// pooling, RMSNorm, RoPE, cache insertion) runs on the block; when the token
+// closed a row, its indexer score is computed here (the rotated query cast to
+// the indexer format, dotted with the row's stored values, relu, weighted head
+// sum) and joins the keys and the histogram; then the selection.
+template <int KVF, int IDXF, int ACTF>
+__global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, Cache cc, const void* __restrict__ u,
+                                                      const int32_t* __restrict__ pos, const float* __restrict__ proj,
+                                                      int B, const void* __restrict__ qI,
+                                                      const float* __restrict__ wt, const uint32_t* __restrict__ keys,
+                                                      SelWs S, int32_t* __restrict__ out) {
+  constexpr int TPC = 4;   // four threads per channel pair share the c4a window
+  __shared__ float red[64];
+  __shared__ float mrg[TPC * (kMaxD / 2 + kMaxDI / 2) * 6];
+  __shared__ float idx_row[kMaxDI];
+  __shared__ float hsum[64];
+  const int qn = blockIdx.x, tid = threadIdx.x;
+  const int k = P.topk;
+  const IdxQuery Q = idx_query(P, pos, 0, 0, qn);
+  const int V = Q.V;
+  int32_t* o = out + (size_t)qn * k;
+  uint32_t* gh = S.hist + (size_t)qn * kHistBins;
+  const u32x4 h4 = *(const u32x4*)(gh + 4 * tid);
+  const uint32_t* kq = keys + (size_t)qn * P.cap;
+  uint32_t kr[kSelKPT];
+#pragma unroll
+  for (int e = 0; e < kSelKPT; ++e) kr[e] = kq[min(tid + 1024 * e, P.cap - 1)];
+  // this thread's share of the indexer query (head tid / 16, DI / 16 channels)
+  const int HI = P.HI, DI = P.DI, cpt = DI / 16;
+  const int hh = min(tid >> 4, max(HI - 1, 0)), c0 = (tid & 15) * cpt;
+  static_assert(ACTF == CKV_BF16, "the fused step takes bf16 activations");
+  const u32x4 qraw = *(const u32x4*)((const uint16_t*)qI + ((size_t)qn * HI + hh) * DI + c0);
+  const float wv = wt[(size_t)qn * HI + hh];
+  *(u32x4*)(gh + 4 * tid) = (u32x4){0u, 0u, 0u, 0u};
+
+  const int st = compress_decode_seq<KVF, IDXF, ACTF, 8, TPC, 1>(P, w, cc, u, pos, proj, 1, B, qn, red, mrg, idx_row);
+  if (st < 0) {
+    for (int j = tid; j < k; j += 1024) o[j] = -1;
+    return;
+  }
+  if (V <= k) {
+    for (int j = tid; j < k; j += 1024) o[j] = j < V ? j : -1;
+    return;
+  }
+  uint32_t hv[4] = {h4[0], h4[1], h4[2], h4[3]};
+  if (st == 1 && Q.V == (Q.p + 1) / 4) {
+    // score of row V - 1: rotate the query tail at p, cast to the cache format
+    __syncthreads();   // idx_row complete
+    const int dn = DI - P.idx_rot;
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      if (e < cpt) {
+        float a = bf16_to_f32(qraw[e >> 1] & 0xffffu), b2 = bf16_to_f32(qraw[e >> 1] >> 16);
+        const int c = c0 + e;
+        if (c >= dn) {
+          float cs, sn;
+          rope_cs(P, (c - dn) >> 1, (double)Q.p, &cs, &sn);
+          const float x = a * cs - b2 * sn, y = a * sn + b2 * cs;
+          a = x;
+          b2 = y;
+        }
+        if (IDXF == CKV_BF16) {
+          a = bf16_to_f32(f32_to_bf16(a));
+          b2 = bf16_to_f32(f32_to_bf16(b2));
+        }
+        dot += a * idx_row[c] + b2 * idx_row[c + 1];
+      }
+    }
+#pragma unroll
+    for (int o2 = 1; o2 < 16; o2 <<= 1) dot += __shfl_xor(dot, o2, 64);
+    const bool relu = !(P.flags & CKV_FLAG_IDX_NO_RELU);
+    if ((tid & 15) == 0) hsum[tid >> 4] = (tid >> 4) < HI ? wv * (relu ? fmaxf(dot, 0.f) : dot) : 0.f;
+    __syncthreads();
+    float sc = 0.f;
+    for (int h = 0; h < HI; ++h) sc += hsum[h];
+    const uint32_t key = float_key(sc);
+    const int x = V - 1;
+#pragma unroll
+    for (int e = 0; e < kSelKPT; ++e)
+      if (e == (x >> 10) && tid == (x & 1023)) kr[e] = key;
+    const uint32_t bin = key >> 20;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (tid == (int)(bin >> 2) && i == (int)(bin & 3)) hv[i] += 1u;
+  }
+  topk_decode_select(P, V, kr, hv, o);
+}
+
 // ---------------------------------------------------------------- launchers
 
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
@@ -1043,6 +1179,42 @@ int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const f
     hipLaunchKernelGGL(k_topk_select_reg, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);
   else
     hipLaunchKernelGGL(k_topk_select, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);
+  return (int)hipGetLastError();
+}
+
+bool step_fusable(const LayerParams& P, int B) {
+  return P.ratio == 4 && P.idx_fmt == CKV_BF16 && P.DI == 128 && P.HI <= 64 && P.cap <= 32768 &&
+         P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && B <= 64 && P.d <= 512;
+}
+
+int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache& c, const void* x,
+                            const void* u, const void* qI, const float* wt, const int32_t* pos, int B,
+                            float* proj, uint32_t* keys, const SelWs& sel, int32_t* topk, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const WCat wc = make_wcat(P, w);
+  const int nproj = (P.ncol / 16) * ((B + 15) / 16);
+  constexpr int RB = 256 * kScoreGroups;
+  const int nrb = (P.cap + RB - 1) / RB;
+  const int MT = (P.HI + 15) / 16;
+  dim3 grid(nproj + nrb * B);
+  const uint16_t* ix = (const uint16_t*)c.idx;
+#define CKV_SS(MTV)                                                                                       \
+  hipLaunchKernelGGL((k_step_scan<MTV, CKV_BF16>), grid, dim3(256), 0, st, P, ix, qI, wt, pos, keys, sel.hist, \
+                     (const uint16_t*)x, B, wc, proj, nproj, nrb)
+  if (MT == 1) CKV_SS(1);
+  else if (MT == 2) CKV_SS(2);
+  else if (MT == 3) CKV_SS(3);
+  else CKV_SS(4);
+#undef CKV_SS
+  if (P.kv_fmt == CKV_E4M3)
+    hipLaunchKernelGGL((k_step_select<CKV_E4M3, CKV_BF16, CKV_BF16>), dim3(B), dim3(1024), 0, st, P, w, c, u, pos,
+                       proj, B, qI, wt, keys, sel, topk);
+  else if (P.kv_fmt == CKV_BF16)
+    hipLaunchKernelGGL((k_step_select<CKV_BF16, CKV_BF16, CKV_BF16>), dim3(B), dim3(1024), 0, st, P, w, c, u, pos,
+                       proj, B, qI, wt, keys, sel, topk);
+  else
+    hipLaunchKernelGGL((k_step_select<CKV_F32, CKV_BF16, CKV_BF16>), dim3(B), dim3(1024), 0, st, P, w, c, u, pos,
+                       proj, B, qI, wt, keys, sel, topk);
   return (int)hipGetLastError();
 }
 

@@ -6,24 +6,9 @@
 // blocks are wkv | wgate | idx_wkv | idx_wgate.  The result goes to
 // part[split][m][col] in fp32; split-K partials are summed, in split order, by
 // the compress kernels that consume them.
-#include "ckv_device.h"
+#include "proj_dec.h"
 
 namespace ckv {
-
-struct WCat {
-  const void* p[4];
-  int start[5];  // column ranges of the four blocks
-};
-
-__device__ __forceinline__ const void* wcat_row(const WCat& wc, int col, int K, int esz,
-                                                int* local) {
-  int s = 0;
-#pragma unroll
-  for (int i = 1; i < 4; ++i)
-    if (col >= wc.start[i]) s = i;
-  *local = col - wc.start[s];
-  return (const char*)wc.p[s] + (size_t)(*local) * K * esz;
-}
 
 // bf16 activations x bf16 weights on MFMA.  One wave computes a 32 x 16 tile
 // (two 16-row blocks of x against 16 weight rows) over one K range.
@@ -89,40 +74,7 @@ __global__ __launch_bounds__(256) void k_proj_mfma(const uint16_t* __restrict__ 
 // y = ceil(M / 16), z = K slices; writes part[slice][m][col].
 __global__ __launch_bounds__(1024) void k_proj_dec(const uint16_t* __restrict__ X, int M, int K, WCat wc, int ncol,
                                                    float* __restrict__ part) {
-  __shared__ f32x4 red[16][64];
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15, g = lane >> 4;
-  const int col0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
-  const int ksl = K / (int)gridDim.z;   // K slice of this block (a multiple of 32)
-  int local;
-  const uint16_t* wrow = (const uint16_t*)wcat_row(wc, col0 + r, K, 2, &local) + (size_t)blockIdx.z * ksl;
-  const uint16_t* xrow = X + (size_t)min(m0 + r, M - 1) * K + (size_t)blockIdx.z * ksl;
-  const int nsteps = ksl / 32;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = wave; s0 < nsteps; s0 += 16 * 8) {
-    u32x4 a[8], b[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = 32 * min(s0 + 16 * e, nsteps - 1) + 8 * g;
-      a[e] = *(const u32x4*)(xrow + k);
-      b[e] = *(const u32x4*)(wrow + k);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (s0 + 16 * e < nsteps) acc = mfma16x16x32(as_bf16x8(a[e]), as_bf16x8(b[e]), acc);
-  }
-  red[wave][lane] = acc;
-  __syncthreads();
-  if (wave == 0) {
-    f32x4 t = red[0][lane];
-#pragma unroll
-    for (int w = 1; w < 16; ++w) t += red[w][lane];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 4 * g + i;
-      if (m < M) part[((size_t)blockIdx.z * M + m) * ncol + col0 + r] = t[i];
-    }
-  }
+  proj_tile<16>(X, M, K, wc, ncol, part, blockIdx.x * 16, blockIdx.y * 16);
 }
 
 // Any formats, vector ALU: one wave per (column, 4 rows), lanes stride K.
@@ -150,20 +102,10 @@ __global__ __launch_bounds__(64) void k_proj_vec(const void* __restrict__ X, int
 int launch_proj(const LayerParams& P, const Weights& w, const void* x, int M, float* part,
                 int splits, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  WCat wc;
-  wc.p[0] = w.wkv;
-  wc.p[1] = w.wgate;
-  wc.p[2] = w.idx_wkv;
-  wc.p[3] = w.idx_wgate;
-  wc.start[0] = 0;
-  wc.start[1] = P.d;
-  wc.start[2] = 2 * P.d;
-  wc.start[3] = P.ratio == 4 ? 2 * P.d + P.DI : 1 << 30;
-  wc.start[4] = P.ncol;
-  if (P.ratio != 4) wc.start[2] = wc.start[3] = 1 << 30;
+  const WCat wc = make_wcat(P, w);
   const int K = P.hidden;
   if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && M <= 64) {
-    dim3 grid(P.ncol / 16, (M + 15) / 16, splits);
+    dim3 grid(P.ncol / 16, (M + 15) / 16);
     hipLaunchKernelGGL(k_proj_dec, grid, dim3(1024), 0, st, (const uint16_t*)x, M, K, wc, P.ncol, part);
   } else if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16) {
     const int klen = ((K / splits) + 31) / 32 * 32;

@@ -135,6 +135,19 @@ class DeviceLayer:
         self.attn_decode(q, pos, topk if self.ratio == 4 else None, out)
         return out, (topk if self.ratio == 4 else None)
 
+    def decode_step(self, x, u, q, qI, w, pos, out=None, topk=None,
+                    B: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        """The same step as ``decode`` through the single decode-step entry
+        point (fused launches on eligible ratio-4 layers)."""
+        B = self.batch if B is None else B
+        out = self.new_out(B) if out is None else out
+        if self.ratio == 4 and topk is None:
+            topk = torch.empty((B, self.k), dtype=torch.int32, device=self.device)
+        self._check(L.decode_step(self.desc, self.weights, self.cache, x, u, q, qI, w, pos, B,
+                                  topk if self.ratio == 4 else None, out, self.ws, self.ws_bytes, self._stream()),
+                    "decode_step")
+        return out, (topk if self.ratio == 4 else None)
+
     def prefill(self, seq: int, pos0: int, x, u, q, qI=None, w=None, out=None,
                 topk=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
         """Chunked prefill of tokens pos0 .. pos0+T-1 of sequence ``seq``."""

@@ -85,7 +85,7 @@ class DeviceStack:
         for il, (dl, a) in enumerate(zip(self.layers, inputs)):
             o = outs[il] if outs is not None else None
             tk = topks[il] if topks is not None else None
-            o, _ = dl.decode(a["x"], a["u"], a["q"], a.get("qI"), a.get("w"), a["pos"], out=o, topk=tk)
+            o, _ = dl.decode_step(a["x"], a["u"], a["q"], a.get("qI"), a.get("w"), a["pos"], out=o, topk=tk)
             res.append(o)
         return res
 

@@ -278,6 +278,28 @@ int ckv_sparse_swa_attn_prefill(const ckv_layer_desc* desc, const ckv_layer_cach
                                 const int32_t* topk, void* out, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/* ---- decode_step: compress_append + indexer_topk + sparse_swa_attn of one
+ * decode token per sequence, in that order [P1 s4-s9; P4 decode path] -----------
+ *
+ * The result equals ckv_compress_append_decode, then (ratio 4)
+ * ckv_indexer_topk_decode, then ckv_sparse_swa_attn_decode, with the same
+ * arguments: x, u as for compress_append; q, out as for sparse_swa_attn;
+ * qI, iw (the indexer head weights) and topk as for indexer_topk (ratio 4;
+ * ignored and may be NULL otherwise).  topk receives the selection on ratio 4.
+ * On ratio-4 layers with bf16 activations, weights and indexer rows, D_I = 128,
+ * at most 64 indexer heads, comp_cap <= 32768 and B <= 64, the step runs as
+ * three launches: the compressor projection shares a launch with the scoring
+ * of the rows that precede this token's own row; one block per sequence then
+ * runs the compressor, scores the row this token closed (if any) and selects;
+ * then the attention.  The selection is the same; the score of the new row
+ * may differ from the separate call's in the last bits (another summation
+ * order).  Other layers run the three calls.  Error returns as for those
+ * calls; on an error nothing after the failing stage is enqueued. */
+int ckv_decode_step(const ckv_layer_desc* desc, const ckv_layer_weights* w, const ckv_layer_cache* cache,
+                    const void* x, const void* u, const void* q, const void* qI, const float* iw,
+                    const int32_t* pos, int32_t B, int32_t* topk, void* out, void* ws, size_t ws_bytes,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -120,6 +120,25 @@ def test_host_errors_before_any_enqueue():
     assert L.compress_append_prefill(d, w, cache(raw_stage=None), FAKE, FAKE, 0, 0, 16, FAKE, wp) == L.CKV_E_INVAL
     assert L.indexer_topk_prefill(d, c, FAKE, FAKE, 0, 0, 5000, FAKE, FAKE, wp) == L.CKV_E_CAPACITY
     assert L.sparse_swa_attn_prefill(d, c, FAKE, 0, 0, 16, FAKE, FAKE, FAKE, 16) == L.CKV_E_WORKSPACE
+    # the single-call decode step: same checks, all before anything is enqueued
+    st = lambda **k: L.decode_step(k.get("d", d), k.get("w", w), k.get("c", c), k.get("x", FAKE), FAKE,
+                                   k.get("q", FAKE), k.get("qI", FAKE), k.get("iw", FAKE), FAKE, k.get("B", 16),
+                                   k.get("topk", FAKE), k.get("out", FAKE), k.get("ws", FAKE), k.get("wsb", ws))
+    assert st(B=17) == L.CKV_E_CAPACITY
+    assert st(B=0) == L.CKV_E_INVAL
+    assert st(wsb=ws - 1) == L.CKV_E_WORKSPACE
+    assert st(ws=MIS) == L.CKV_E_WORKSPACE
+    assert st(topk=None) == L.CKV_E_INVAL          # ratio 4 needs the top-k output
+    assert st(qI=None) == L.CKV_E_INVAL
+    assert st(iw=MIS) == L.CKV_E_INVAL
+    assert st(out=None) == L.CKV_E_INVAL
+    assert st(q=MIS) == L.CKV_E_INVAL
+    assert st(x=None) == L.CKV_E_INVAL
+    assert st(w=weights(idx_gamma=None)) == L.CKV_E_INVAL
+    assert st(c=cache(idx=None)) == L.CKV_E_INVAL
+    assert st(d=desc(ratio=5)) == L.CKV_E_UNSUPPORTED
+    d0 = desc(ratio=0, comp_cap=0)
+    assert st(d=d0, wsb=L.workspace_bytes(d0, L.CKV_MODE_DECODE, 16), out=MIS) == L.CKV_E_INVAL
     # invalid description
     assert L.compress_append_decode(desc(ratio=5), w, c, FAKE, FAKE, FAKE, 1, FAKE, ws) == L.CKV_E_UNSUPPORTED
     assert L.lib.ckv_validate(None) == L.CKV_E_INVAL

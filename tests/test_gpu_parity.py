@@ -57,11 +57,48 @@ def run_decode_stage_checks(cfg, inp, wts, tol):
     torch.cuda.synchronize()
     assert int(dl.status.abs().sum()) == 0
     L = oracle_layer(cfg, wts)
+    raw_g, comp_g, idx_g = check_compressor(cfg, inp, dl, L)
+
+    # --- indexer on the GPU's own cache bytes
+    topk_d = None
+    bseqs = [oracle_seq_from_bytes(L, raw_g[b], None if comp_g is None else comp_g[b],
+                                   None if idx_g is None else idx_g[b], int(inp.pos[b]) + 1) for b in range(B)]
+    if cfg.ratio == 4:
+        qI, w = tie_free_queries(cfg, bseqs, inp.pos, inp.qI, inp.w)
+        topk_d = torch.empty((B, cfg.top_k), dtype=torch.int32, device="cuda")
+        dl.indexer_decode(dev(qI), dev(w), pos_d, topk_d)
+        torch.cuda.synchronize()
+        check_topk(cfg, inp, bseqs, qI, w, cpu(topk_d))
+    # --- attention with the GPU's top-k list
+    out = dl.new_out(B)
+    dl.attn_decode(q, pos_d, topk_d, out)
+    torch.cuda.synchronize()
+    check_attention(cfg, inp, bseqs, None if topk_d is None else cpu(topk_d), out, tol)
+    return dl
+
+
+def check_topk(cfg, inp, bseqs, qI, w, tk):
+    for b in range(cfg.batch):
+        ref = O.topk_select(bseqs[b].index_scores(int(inp.pos[b]), qI[b], w[b]), cfg.top_k)
+        assert sets_equal(tk[b], ref), f"top-k set differs for sequence {b}"
+        n = int((tk[b] >= 0).sum())
+        assert np.all(tk[b][:n] == np.sort(tk[b][:n])) and np.all(tk[b][n:] == -1)
+
+
+def check_attention(cfg, inp, bseqs, tk, out, tol):
+    og = out_values(out, cfg.act_fmt)
+    for b in range(cfg.batch):
+        ref = bseqs[b].attend(int(inp.pos[b]), inp.q[b], None if tk is None else tk[b])
+        assert_close(og[b], ref, tol, f"attention output b={b}")
+
+
+def check_compressor(cfg, inp, dl, L):
+    """Compressor + raw insertion of one decode step vs the oracle run from
+    the drawn state; returns the cache bytes the GPU holds."""
+    B, d = cfg.batch, cfg.head_dim
     raw_g = cpu(dl.raw)
     comp_g = cpu(dl.comp) if dl.comp is not None else None
     idx_g = cpu(dl.idx) if dl.idx is not None else None
-
-    # --- compressor + raw insertion vs the oracle run from the drawn state
     for b in range(B):
         p = int(inp.pos[b])
         seq = oracle_seq_from_init(L, inp.cache, b)
@@ -79,31 +116,54 @@ def run_decode_stage_checks(cfg, inp, wts, tol):
             kap = seq.kap[p]
             st = cpu(dl.st_kv)[b, p % W]
             assert_close(st, kap, (1e-4, 1e-5), f"state kappa b={b}")
+    return raw_g, comp_g, idx_g
 
-    # --- indexer on the GPU's own cache bytes
-    topk_d = None
+
+def run_decode_step_checks(cfg, inp, wts, tol):
+    """ckv_decode_step (one call for the whole step) vs the oracle.  The
+    indexer query is made tie-free on the cache the separate compressor call
+    leaves; the fused call then runs on a fresh copy of the drawn cache, and
+    its compressor rows, top-k set (on the bytes it wrote) and attention output
+    are checked; its top-k list must also equal the separate calls' list."""
+    B = cfg.batch
+    log(f"[decode_step] {cfg.name} B={B} p={inp.pos[:4]}")
+    L = oracle_layer(cfg, wts)
+    pos_d = dev(inp.pos)
+    x, u, q = dev(inp.x), dev(inp.u), dev(inp.q)
+    qI, w = inp.qI, inp.w
+    ref_dl = device_layer(cfg, wts, inp.cache)
+    topk_a = None
+    if cfg.ratio == 4:
+        ref_dl.compress_decode(x, u, pos_d)
+        torch.cuda.synchronize()
+        seqs_a = [oracle_seq_from_bytes(L, cpu(ref_dl.raw)[b], cpu(ref_dl.comp)[b], cpu(ref_dl.idx)[b],
+                                        int(inp.pos[b]) + 1) for b in range(B)]
+        qI, w = tie_free_queries(cfg, seqs_a, inp.pos, inp.qI, inp.w)
+        topk_a = torch.empty((B, cfg.top_k), dtype=torch.int32, device="cuda")
+        ref_dl.indexer_decode(dev(qI), dev(w), pos_d, topk_a)
+        torch.cuda.synchronize()
+    dl = device_layer(cfg, wts, inp.cache)
+    out, topk = dl.decode_step(x, u, q, dev(qI) if cfg.ratio == 4 else None,
+                               dev(w) if cfg.ratio == 4 else None, pos_d)
+    torch.cuda.synchronize()
+    assert int(dl.status.abs().sum()) == 0
+    raw_g, comp_g, idx_g = check_compressor(cfg, inp, dl, L)
     bseqs = [oracle_seq_from_bytes(L, raw_g[b], None if comp_g is None else comp_g[b],
                                    None if idx_g is None else idx_g[b], int(inp.pos[b]) + 1) for b in range(B)]
+    tk = None
     if cfg.ratio == 4:
-        qI, w = tie_free_queries(cfg, bseqs, inp.pos, inp.qI, inp.w)
-        topk_d = torch.empty((B, cfg.top_k), dtype=torch.int32, device="cuda")
-        dl.indexer_decode(dev(qI), dev(w), pos_d, topk_d)
-        torch.cuda.synchronize()
-        tk = cpu(topk_d)
+        tk = cpu(topk)
         for b in range(B):
-            ref = O.topk_select(bseqs[b].index_scores(int(inp.pos[b]), qI[b], w[b]), cfg.top_k)
-            assert sets_equal(tk[b], ref), f"top-k set differs for sequence {b}"
-            n = int((tk[b] >= 0).sum())
-            assert np.all(tk[b][:n] == np.sort(tk[b][:n])) and np.all(tk[b][n:] == -1)
-    # --- attention with the GPU's top-k list
-    out = dl.new_out(B)
-    dl.attn_decode(q, pos_d, topk_d, out)
-    torch.cuda.synchronize()
-    og = out_values(out, cfg.act_fmt)
-    for b in range(B):
-        ref = bseqs[b].attend(int(inp.pos[b]), inp.q[b], None if topk_d is None else cpu(topk_d)[b])
-        assert_close(og[b], ref, tol, f"attention output b={b}")
-    return dl
+            m = topk_margin(bseqs[b].index_scores(int(inp.pos[b]), qI[b], w[b]), cfg.top_k)
+            assert m > 1e-6, f"query {b} not tie-free on the fused call's bytes (margin {m})"
+        check_topk(cfg, inp, bseqs, qI, w, tk)
+        # where both calls stored identical indexer rows, the lists must match exactly
+        same = np.all(idx_g.reshape(B, -1) == cpu(ref_dl.idx).reshape(B, -1), axis=1)
+        log(f"  identical indexer rows in {int(same.sum())}/{B} sequences")
+        assert np.array_equal(tk[same], cpu(topk_a)[same]), "fused and separate top-k lists differ"
+        ws = dl.ws[:L_sync_bytes(dl)]
+        assert int(ws.view(torch.int32).abs().sum()) == 0, "sync region not left zero"
+    check_attention(cfg, inp, bseqs, tk, out, tol)
 
 
 def test_c2_c4a_decode_full_size():
@@ -129,6 +189,27 @@ def test_c5_c128a_and_swa_layers_decode():
     for name in ("c5_c128a", "c5_swa"):
         cfg = get_config(name)
         run_decode_stage_checks(cfg, make_decode_inputs(cfg), make_layer_weights(cfg), FP8_TOL)
+
+
+@pytest.mark.parametrize("name", ["c2", "c5", "c3", "c5_swa"])
+def test_decode_step_full_size(name):
+    """The single-call decode step at full size: fused on the c4a layers,
+    the three separate calls on c128a and sliding-window-only layers."""
+    cfg = get_config(name)
+    run_decode_step_checks(cfg, make_decode_inputs(cfg), make_layer_weights(cfg),
+                           FP8_TOL if cfg.kv_fmt == "e4m3" else BF16_TOL)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
+def test_decode_step_short_contexts(fmt):
+    """Fused step on short and ragged contexts: V <= k, the first rows,
+    positions that close a row and positions that do not."""
+    base = get_config("c2")
+    cfg = base.with_(batch=8, comp_cap=512, kv_fmt=fmt, idx_heads=8, idx_dim=128, top_k=64, seed=13,
+                     name=f"step_short_{fmt}")
+    n = np.array([1, 3, 4, 8, 259, 260, 1023, 2047], np.int64)
+    run_decode_step_checks(cfg, make_decode_inputs(cfg, n_ctx=n), make_layer_weights(cfg),
+                           FP8_TOL if fmt == "e4m3" else BF16_TOL)
 
 
 @pytest.mark.parametrize("ratio,fmt", [(4, "bf16"), (4, "e4m3"), (128, "bf16"), (0, "bf16")])
