@@ -69,12 +69,15 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
 // the reduced angle then goes through float sincos.  theta_j comes from the
 // host (LayerParams::theta, base^(-2j/n_rot) in fp64).  All RoPE tails here
 // have n_rot = 64, so pair j of every tail uses theta_j.
-__device__ __forceinline__ void rope_cs(const LayerParams& P, int j, double pos, float* c, float* s) {
-  const double a = pos * P.theta[j];
+__device__ __forceinline__ void rope_cs_theta(double theta, double pos, float* c, float* s) {
+  const double a = pos * theta;
   const double k = rint(a * 0.15915494309189535);      // a / (2 pi)
   double r = fma(-k, 6.283185307179586, a);            // 2 pi, high part
   r = fma(-k, 2.4492935982947064e-16, r);              // 2 pi, low part
   sincosf((float)r, s, c);
+}
+__device__ __forceinline__ void rope_cs(const LayerParams& P, int j, double pos, float* c, float* s) {
+  rope_cs_theta(P.theta[j], pos, c, s);
 }
 
 // ---------------------------------------------------------------- MFMA

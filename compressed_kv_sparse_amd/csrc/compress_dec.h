@@ -94,6 +94,27 @@ __device__ __forceinline__ float2 load2(const void* p, long i) {  // i even
 
 __device__ __forceinline__ float2 ld2(const float* p) { return *(const float2*)p; }
 
+namespace cmp {
+// block-wide sum and max (every thread returns the totals); red: 2 * 32 floats
+__device__ __forceinline__ float2 block_sum_max(float s, float m, float* red) {
+  s = wave_sum(s);
+  m = wave_max(m);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  lds_barrier();
+  if ((threadIdx.x & 63) == 0) {
+    red[w] = s;
+    red[32 + w] = m;
+  }
+  lds_barrier();
+  float ts = 0.f, tm = 0.f;
+  for (int i = 0; i < nw; ++i) {
+    ts += red[i];
+    tm = fmaxf(tm, red[32 + i]);
+  }
+  return make_float2(ts, tm);
+}
+}  // namespace cmp
+
 // Store one row from per-thread channel pairs (c, c+1) in format KVF.  Every
 // thread of the block calls (the E4M3 row scale is a block-wide max).
 template <int KVF>
@@ -105,7 +126,7 @@ __device__ __forceinline__ void store_row2(uint8_t* dst, float2 z, int c, bool a
     if (act) *(uint32_t*)(dst + 2 * c) = pack_bf16x2(z.x, z.y);
   } else {
     const int dn = d - n_rot;
-    const float amax = block_max(act && c < dn ? fmaxf(fabsf(z.x), fabsf(z.y)) : 0.f, red);
+    const float amax = cmp::block_sum_max(0.f, act && c < dn ? fmaxf(fabsf(z.x), fabsf(z.y)) : 0.f, red).y;
     const float s = amax > 0.f ? amax / 448.0f : 1.0f;
     if (act) {
       if (c < dn) *(uint16_t*)(dst + c) = (uint16_t)(f32_to_e4m3(z.x / s) | (f32_to_e4m3(z.y / s) << 8));
@@ -122,6 +143,13 @@ __device__ __forceinline__ float2 rope2(const LayerParams& P, float2 z, int c, i
   float cs, sn;
   rope_cs(P, (c - dn) >> 1, pos, &cs, &sn);
   return make_float2(z.x * cs - z.y * sn, z.x * sn + z.y * cs);
+}
+// The same with cos / sin of pair j taken from tables cs[j], sn[j] (LDS).
+__device__ __forceinline__ float2 rope2t(float2 z, int c, int width, int nrot, const float* cs, const float* sn) {
+  const int dn = width - nrot;
+  if (c < dn) return z;
+  const int j = (c - dn) >> 1;
+  return make_float2(z.x * cs[j] - z.y * sn[j], z.x * sn[j] + z.y * cs[j]);
 }
 
 // Pool channels (c, c+1) of row i over its window.  Token p's own values come
@@ -176,26 +204,6 @@ __device__ __forceinline__ float2 pool2(const float* skv, const float* ssc, cons
 // in rounds of 8 slots per thread.  On c4a with TPC parts, part q holds slots
 // q + TPC e: flipping by 4 maps that set onto itself (slot q + TPC e takes the
 // APE row of local index e ^ (4 / TPC)), so its loads do not depend on p.
-namespace cmp {
-// block-wide sum and max (every thread returns the totals); red: 2 * 32 floats
-__device__ __forceinline__ float2 block_sum_max(float s, float m, float* red) {
-  s = wave_sum(s);
-  m = wave_max(m);
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    red[w] = s;
-    red[32 + w] = m;
-  }
-  __syncthreads();
-  float ts = 0.f, tm = 0.f;
-  for (int i = 0; i < nw; ++i) {
-    ts += red[i];
-    tm = fmaxf(tm, red[32 + i]);
-  }
-  return make_float2(ts, tm);
-}
-}  // namespace cmp
 
 // The per-sequence body, called by every thread of a block of at least
 // TPC * d / 2 threads (threads past that take part in the reductions only).
@@ -203,12 +211,20 @@ __device__ __forceinline__ float2 block_sum_max(float s, float m, float* red) {
 // values are left in idx_row[0 .. D_I) when idx_row is non-NULL), 0 when it
 // did not, -1 for a negative position.  red: 64 floats of LDS; mrg: the
 // parts' merge area (TPC > 1): TPC * d / 2 * 6 floats, plus TPC * D_I / 2 * 6
-// on c4a.
-template <int KVF, int IDXF, int ACTF, int W, int TPC, int MAXS = 4>
+// on c4a.  rtab: 128 floats of LDS, left holding cos (rtab[j]) and sin
+// (rtab[64 + j]) of pair j at p, and at the row position i r in
+// rtab[32 + j], rtab[96 + j] (n_rot = 64).  issue() is called once every load
+// of the body has been issued and before any is waited for: a caller's own
+// loads placed there overlap the body (the vector memory counter completes in
+// issue order).  Every load of the body is issued before its first store, and
+// no barrier here waits for global memory after that, so stores stay in
+// flight while the body and the caller go on.
+template <int KVF, int IDXF, int ACTF, int W, int TPC, int MAXS = 4, typename Issue>
 __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const Weights& w, const Cache& cc,
                                                    const void* __restrict__ u, const int32_t* __restrict__ pos,
                                                    const float* __restrict__ proj, int splits, int B, int b,
-                                                   float* red, float* mrg, float* idx_row) {
+                                                   float* red, float* mrg, float* idx_row, float* rtab,
+                                                   Issue&& issue) {
   constexpr int SPT = W / TPC;                 // slots per thread
   constexpr int RND = SPT < 8 ? SPT : 8;       // slots per load round
   constexpr int r = W == 8 ? 4 : 128;
@@ -268,17 +284,16 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
       irs[e] = ld2(isc + sl * DI + ci);
       iap[e] = ld2(w.idx_ape + sl * DI + ci);
     }
-    gm = ld2(w.gamma + c);
     gmi = ld2(w.idx_gamma + ci);
   }
+  gm = ld2(w.gamma + c);
+  // compiler fences: the loads above stay above, the caller's stay in between
+  asm volatile("" ::: "memory");
+  issue();
+  asm volatile("" ::: "memory");
 
-  if (p < 0) {
-    if (tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_BAD_POS);
-    return -1;
-  }
   const bool emit = (p + 1) % r == 0;
   const int i = (p + 1) / r - 1;
-  if (emit && i >= P.cap && tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_CAPACITY);
   const bool pool = emit && i < P.cap;
   const int t0 = i * r - (W - r);
   const int cur = p & (W - 1);
@@ -377,10 +392,34 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
     }
   }
   const bool own = part == 0;   // the thread that stores this pair
+  // A negative position stores nothing.  The check sits here, after the
+  // pooling (whose arithmetic is harmless for p < 0), not before the loads:
+  // a branch there lets the compiler sink loads below it, and the wait for a
+  // late load is a wait for everything issued before it.
+  if (p < 0) {
+    if (tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_BAD_POS);
+    return -1;
+  }
+  // RoPE tables: wave 0 computes pair tid % 32 at p (lanes 0-31) and at i r
+  // (lanes 32-63); read after the barrier below
+  if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
+    // theta of pair tid % 32 selected from scalar loads of the whole table (a
+    // per-lane load would be one more vector load to wait for)
+    double theta = 0.0;
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) theta = (tid & 31) == jj ? P.theta[jj] : theta;
+    float cs, sn;
+    rope_cs_theta(theta, tid < 32 ? (double)p : (double)((p + 1) / r * r - r), &cs, &sn);
+    if (tid < 64) {
+      rtab[tid] = cs;
+      rtab[64 + tid] = sn;
+    }
+  }
+  lds_barrier();                // rtab complete
 
   // ---- raw sliding-window row: u rotated at p into slot p % swa
   {
-    const float2 z = rope2(P, uu, c, d, P.n_rot, p);
+    const float2 z = rope2t(uu, c, d, P.n_rot, rtab, rtab + 64);
     store_row2<KVF>(cc.raw + ((size_t)b * P.swa + (p & (P.swa - 1))) * P.row_bytes, z, c, own, d, P.n_rot, red);
   }
   // ---- this token's projections -> state slot p % W
@@ -394,22 +433,25 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
     *(float2*)(cc.ist_kv + o) = kia;
     *(float2*)(cc.ist_sc + o) = sia;
   }
+  // (the status atomic sits after every load of the body has been waited for:
+  // a memory operation under a branch before those waits makes the compiler
+  // wait for every outstanding load instead of the ones it needs)
+  if (emit && i >= P.cap && tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_CAPACITY);
   if (!pool) return 0;
-  if (W == 128 && TPC > 1) gm = own ? ld2(w.gamma + c) : gm;
 
   // ---- attention lane: RMSNorm, tail RoPE at i r, store row i
   {
     const float ss = cmp::block_sum_max(own ? y.x * y.x + y.y * y.y : 0.f, 0.f, red).x;
     const float inv = 1.0f / sqrtf(ss / (float)d + P.eps);
-    const float2 z = rope2(P, make_float2(gm.x * (y.x * inv), gm.y * (y.y * inv)), c, d, P.n_rot, (double)i * r);
+    const float2 z = rope2t(make_float2(gm.x * (y.x * inv), gm.y * (y.y * inv)), c, d, P.n_rot, rtab + 32, rtab + 96);
     store_row2<KVF>(cc.comp + ((size_t)b * P.cap + i) * P.row_bytes, z, c, own, d, P.n_rot, red);
   }
   if (W == 8) {  // indexer lane: its own compressor of the same form
     const float ss = cmp::block_sum_max(own && ilane ? yi.x * yi.x + yi.y * yi.y : 0.f, 0.f, red).x;
     const float inv = 1.0f / sqrtf(ss / (float)DI + P.eps);
     if (own && ilane) {
-      const float2 z = rope2(P, make_float2(gmi.x * (yi.x * inv), gmi.y * (yi.y * inv)), c, DI, P.idx_rot,
-                             (double)i * r);
+      const float2 z = rope2t(make_float2(gmi.x * (yi.x * inv), gmi.y * (yi.y * inv)), c, DI, P.idx_rot, rtab + 32,
+                              rtab + 96);
       uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * DI * (IDXF == CKV_F32 ? 4 : 2);
       if (IDXF == CKV_F32) {
         *(float2*)(dst + 4 * c) = z;
@@ -428,6 +470,193 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
     }
   }
   return 1;
+}
+
+// ------------------------------------------------------------ c4a decode
+
+// One stored-row channel c in format KVF (E4M3 codes are z / s with s the row
+// scale, written separately; the RoPE tail stays bf16).
+template <int KVF>
+__device__ __forceinline__ void put_chan(uint8_t* dst, float z, int c, int dn, float s) {
+  if constexpr (KVF == CKV_F32) {
+    ((float*)dst)[c] = z;
+  } else if constexpr (KVF == CKV_BF16) {
+    ((uint16_t*)dst)[c] = (uint16_t)f32_to_bf16(z);
+  } else {
+    if (c < dn) dst[c] = (uint8_t)f32_to_e4m3(z / s);
+    else ((uint16_t*)(dst + dn))[c - dn] = (uint16_t)f32_to_bf16(z);
+  }
+}
+
+// Rotate channel c of a row whose pairs (2j, 2j+1) sit in adjacent lanes, if c
+// is one of the last nrot channels; cs / sn: tables of pair j (LDS).  Every
+// lane calls (the partner value comes from lane ^ 1).
+__device__ __forceinline__ float rope1t(float v, int c, int width, int nrot, const float* cs, const float* sn) {
+  const float o = __shfl_xor(v, 1, 64);
+  const int dn = width - nrot;
+  if (c < dn) return v;
+  const int j = (c - dn) >> 1;
+  return (c & 1) ? fmaf(o, sn[j], v * cs[j]) : fmaf(-o, sn[j], v * cs[j]);
+}
+
+// Softmax pooling of one channel over the 8 window positions of row i
+// (window token t0 + j sits in ring slot (t0 + j) % 8 = j ^ F, F = t0 & 4),
+// two passes: the maximum of the valid scores, then exp-weighted sums.  The
+// current token's slot is taken from (kcur, scur).
+template <int F>
+__device__ __forceinline__ float pool_c4a(const float (&rk)[8], const float (&rs)[8], const float (&ap)[8],
+                                          float kcur, float scur, int t0, int cur) {
+  float e[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sl = 0; sl < 8; ++sl) {
+    const bool valid = t0 + (sl ^ F) >= 0;
+    e[sl] = valid ? (sl == cur ? scur : rs[sl]) + ap[sl ^ F] : -INFINITY;
+    mx = fmaxf(mx, e[sl]);
+  }
+  constexpr float kLog2e = 1.4426950408889634f;
+  float sw = 0.f, acc = 0.f;
+#pragma unroll
+  for (int sl = 0; sl < 8; ++sl) {
+    const float wgt = __builtin_amdgcn_exp2f((e[sl] - mx) * kLog2e);
+    sw += wgt;
+    acc = fmaf(wgt, sl == cur ? kcur : rk[sl], acc);
+  }
+  return acc / sw;
+}
+
+// The c4a per-sequence body (window 8, stride 4, with the indexer lane),
+// for a block of at least d + D_I threads.  Thread t < d owns channel t of
+// the attention row (and of the raw row); thread d + t' owns channel t' of
+// the indexer row; the rest only join the barriers.  Every thread issues the
+// same loads (idle threads at clamped addresses), and the work of idle waves
+// is skipped by wave-uniform branches.  One block reduction serves the
+// RMSNorm of both rows and the E4M3 scales of the raw and compressed rows:
+// the compressed row is (gamma y) * inv with inv > 0 a constant, so its
+// largest magnitude is inv times the largest |gamma y| (rounding is
+// monotonic).
+// Returns 1 when the token closed a row (idx_row, when non-NULL, receives the
+// indexer row's stored values), 0 when not, -1 for a negative position.
+// red: 64 floats of LDS (16-byte aligned); rtab: 128 floats of LDS (RoPE cos
+// and sin at p and at the row position, as for compress_decode_seq); issue()
+// as there.
+template <int KVF, int IDXF, int ACTF, typename Issue>
+__device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weights& w, const Cache& cc,
+                                                const void* __restrict__ u, const int32_t* __restrict__ pos,
+                                                const float* __restrict__ proj, int B, int b, float* red,
+                                                float* rtab, float* idx_row, Issue&& issue) {
+  const int d = P.d, DI = P.DI;
+  const int dn = d - P.n_rot;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nact = (d + DI + 63) / 64;   // waves holding channels
+  const bool roleA = tid < d, roleI = !roleA && tid < d + DI;
+  const int col = roleA ? tid : min(tid - d, DI - 1);
+  const int width = roleA ? d : DI;
+  float* const skv = roleA ? cc.st_kv + (size_t)b * 8 * d : cc.ist_kv + (size_t)b * 8 * DI;
+  float* const ssc = roleA ? cc.st_sc + (size_t)b * 8 * d : cc.ist_sc + (size_t)b * 8 * DI;
+  const float* ape = (roleA ? w.ape : w.idx_ape) + col;
+  const float* pj = proj + (size_t)b * P.ncol;
+
+  // one round of loads: this token's projections and raw input, the ring,
+  // the APE rows and the RMSNorm gain
+  const int p = pos[b];
+  const float ka = pj[roleA ? col : 2 * d + col];
+  const float sa = pj[roleA ? d + col : 2 * d + DI + col];
+  const float uu = load_val<ACTF>(u, (long)b * d + (roleA ? col : 0));
+  float rk[8], rs[8], ap[8];
+#pragma unroll
+  for (int sl = 0; sl < 8; ++sl) {
+    rk[sl] = skv[sl * width + col];
+    rs[sl] = ssc[sl * width + col];
+    ap[sl] = ape[sl * width];
+  }
+  const float gm = (roleA ? w.gamma : w.idx_gamma)[col];
+  asm volatile("" ::: "memory");
+  issue();
+  asm volatile("" ::: "memory");
+
+  const bool emit = p >= 0 && (p + 1) % 4 == 0;
+  const int i = (p + 1) / 4 - 1;
+  const bool pool = emit && i < P.cap;
+  const int t0 = 4 * i - 4, cur = p & 7;
+  // RoPE tables (wave 0): pair j at p and at the row position 4 i
+  if (wave == 0) {
+    double theta = 0.0;
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) theta = (tid & 31) == jj ? P.theta[jj] : theta;
+    float cs, sn;
+    rope_cs_theta(theta, tid < 32 ? (double)p : (double)(4 * i), &cs, &sn);
+    if (tid < 64) {
+      rtab[tid] = cs;
+      rtab[64 + tid] = sn;
+    }
+  }
+  float y = 0.f;
+  if (wave < nact) {
+    if (pool) y = (t0 & 4) ? pool_c4a<4>(rk, rs, ap, ka, sa, t0, cur) : pool_c4a<0>(rk, rs, ap, ka, sa, t0, cur);
+    const float gy = gm * y;
+    float v0 = roleA ? y * y : 0.f;
+    float v1 = roleI ? y * y : 0.f;
+    float v2 = roleA && col < dn ? fabsf(gy) : 0.f;
+    float v3 = roleA && col < dn ? fabsf(uu) : 0.f;
+    v0 = wave_sum(v0);
+    v1 = wave_sum(v1);
+    v2 = wave_max(v2);
+    v3 = wave_max(v3);
+    if (lane == 0) *(float4*)(red + 4 * wave) = make_float4(v0, v1, v2, v3);
+  }
+  lds_barrier();   // red, rtab
+  float sA = 0.f, sI = 0.f, mA = 0.f, mU = 0.f;
+  for (int w2 = 0; w2 < nact; ++w2) {
+    const float4 t = *(const float4*)(red + 4 * w2);
+    sA += t.x;
+    sI += t.y;
+    mA = fmaxf(mA, t.z);
+    mU = fmaxf(mU, t.w);
+  }
+  if (p < 0) {
+    if (tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_BAD_POS);
+    return -1;
+  }
+  if (emit && i >= P.cap && tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_CAPACITY);
+  if (wave < nact) {
+    // raw sliding-window row: u rotated at p, slot p % swa (attention waves)
+    const float zr = rope1t(uu, col, d, P.n_rot, rtab, rtab + 64);
+    if (roleA) {
+      uint8_t* dst = cc.raw + ((size_t)b * P.swa + (p & (P.swa - 1))) * P.row_bytes;
+      const float sc = mU > 0.f ? mU / 448.0f : 1.0f;
+      put_chan<KVF>(dst, zr, col, dn, sc);
+      if (KVF == CKV_E4M3 && tid == 0) *(float*)(dst + dn + 2 * P.n_rot) = sc;
+    }
+    if (roleA || roleI) {   // this token's projections -> state slot p % 8
+      skv[cur * width + col] = ka;
+      ssc[cur * width + col] = sa;
+    }
+    if (pool) {   // RMSNorm, tail RoPE at 4 i, row i of the attention or indexer cache
+      const float inv = 1.0f / sqrtf(roleA ? sA / (float)d + P.eps : sI / (float)DI + P.eps);
+      const float z = rope1t(gm * y * inv, col, width, roleA ? P.n_rot : P.idx_rot, rtab + 32, rtab + 96);
+      if (roleA) {
+        uint8_t* dst = cc.comp + ((size_t)b * P.cap + i) * P.row_bytes;
+        const float amax = mA * inv;
+        const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+        put_chan<KVF>(dst, z, col, dn, sc);
+        if (KVF == CKV_E4M3 && tid == 0) *(float*)(dst + dn + 2 * P.n_rot) = sc;
+      } else if (roleI) {
+        uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * DI * (IDXF == CKV_F32 ? 4 : 2);
+        float zs = z;
+        if constexpr (IDXF == CKV_F32) {
+          ((float*)dst)[col] = z;
+        } else {
+          const uint32_t h = f32_to_bf16(z);
+          ((uint16_t*)dst)[col] = (uint16_t)h;
+          zs = bf16_to_f32(h);
+        }
+        if (idx_row) idx_row[col] = zs;
+      }
+    }
+  }
+  return pool ? 1 : 0;
 }
 
 }  // namespace ckv

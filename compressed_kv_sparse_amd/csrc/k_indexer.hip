@@ -303,6 +303,9 @@ __global__ __launch_bounds__(256) void k_idx_score_vec(LayerParams P, const void
 }
 
 // ---------------------------------------------------------------- select
+// The block-wide helpers below synchronise with LDS-only barriers: their data
+// lives in registers and LDS, and a full barrier would also wait for every
+// global store the caller still has in flight.
 
 // Exclusive prefix sum over the block (1024 threads); returns the thread's
 // exclusive sum, *total receives the block total.
@@ -314,9 +317,9 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* wsum, uin
     const uint32_t y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
-  __syncthreads();
+  lds_barrier();
   if (lane == 63) wsum[wave] = x;
-  __syncthreads();
+  lds_barrier();
   uint32_t before = 0, tot = 0;
   for (int w = 0; w < nw; ++w) {
     if (w < wave) before += wsum[w];
@@ -330,12 +333,12 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* wsum) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
+  lds_barrier();
   if (lane == 0) wsum[wave] = v;
-  __syncthreads();
+  lds_barrier();
   uint32_t t = 0;
   for (int w = 0; w < nw; ++w) t += wsum[w];
-  __syncthreads();
+  lds_barrier();
   return t;
 }
 
@@ -365,7 +368,7 @@ __device__ __forceinline__ void find_bin_asc(const uint32_t* sh, int nb, uint32_
       cum += sh[b];
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Radix select over d = M - key.  count_level(shift, nbits, pfx, pmask, sh)
@@ -431,7 +434,7 @@ __device__ __forceinline__ void emit_selected(KeyAt key_at, int c0, int c1, uint
     wgt[wave] = ngt;
     weq[wave] = neq;
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t gt_before = 0, eq_before = 0;
   for (int w = 0; w < wave; ++w) {
     gt_before += wgt[w];
@@ -461,12 +464,12 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* wsum) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, 64));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
+  lds_barrier();
   if (lane == 0) wsum[wave] = v;
-  __syncthreads();
+  lds_barrier();
   uint32_t t = 0;
   for (int w = 0; w < nw; ++w) t = max(t, wsum[w]);
-  __syncthreads();
+  lds_barrier();
   return t;
 }
 
@@ -593,7 +596,7 @@ __device__ __forceinline__ void bitonic_sort_lds(uint32_t* sh, int n) {
           sh[hi] = a;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 }
@@ -623,7 +626,7 @@ __device__ __forceinline__ void find_from_top(const uint32_t (&v)[PER], uint32_t
       cum += v[i];
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // The query's histogram, 16 consecutive bins per thread -> b1 and A.
@@ -891,21 +894,46 @@ __global__ __launch_bounds__(256) void k_topk_finish(LayerParams P, const uint32
 // found by a radix select over all the keys instead.
 constexpr int kSelKPT = 32;   // keys per thread of the one-block decode selection
 
+// Key e of thread t in the one-block selection is row t + 1024 e: a wave's
+// ballot over key e covers rows 1024 e + 64 w .. +63, i.e. bitmap words
+// 32 e + 2 w and 32 e + 2 w + 1, so bitmaps come straight from ballots.
+__device__ __forceinline__ void sel_load_keys(const uint32_t* kq, int cap, int t, uint32_t (&kr)[kSelKPT]) {
+#pragma unroll
+  for (int e = 0; e < kSelKPT; ++e) kr[e] = kq[min(t + 1024 * e, cap - 1)];
+}
+
+// Lanes of this wave whose key e is a visible row (row < V), wave-uniform.
+__device__ __forceinline__ unsigned long long sel_valid(int V, int wave, int e) {
+  const int left = V - (1024 * e + 64 * wave);
+  return left >= 64 ? ~0ull : (left <= 0 ? 0ull : (~0ull >> (64 - left)));
+}
+
 // The selection itself, from keys kr (row tid + 1024 e) and histogram bins
-// hv (bins 4 tid .. 4 tid + 3) held by the 1024 threads of the block.
+// hv (bins 4 tid .. 4 tid + 3) held by the 1024 threads of the block, V > k.
+//   1. b1 = the 12-bit key bin holding the k-th largest key (histogram scan);
+//   2. the keys in b1 are appended to a candidate list (ballot counts, one
+//      block scan, no atomics) and refined by two radix levels (12 + 8 bits)
+//      to the k-th largest key T and the number of keys equal to T to take;
+//      with more candidates than the list holds, a radix select over all keys;
+//   3. bitmaps of the rows with key > T and key == T from ballots; one block
+//      scan of the words' packed popcounts gives every 32-row word its output
+//      slot, rows equal to T being taken lowest index first; rows are written
+//      ascending.
+// The per-key work is a compare or two and wave-level bit operations: with
+// one block per query the selection runs on one compute unit, so its cost is
+// the vector instructions per key.
 __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, uint32_t (&kr)[kSelKPT],
                                                    uint32_t (&hv)[4], int32_t* __restrict__ o) {
   constexpr int KPT = kSelKPT;
-  __shared__ uint32_t bm[1024];    // selected rows
-  __shared__ uint32_t eqm[1024];   // rows whose key equals the threshold
-  __shared__ uint32_t sh[kHistBins];
+  __shared__ uint32_t gtw[1024];   // rows with key > T
+  __shared__ uint32_t eqw[1024];   // rows with key == T
+  __shared__ uint32_t sh[kHistBins], sh2[256];
   __shared__ uint32_t ck[kCandCap], ci[kCandCap];
-  __shared__ uint32_t wsum[16], res[4], ncand;
-  const int tid = threadIdx.x;
+  __shared__ uint32_t wsum[16], res[4], wcnt[16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = P.topk;
-  bm[tid] = 0u;
-  eqm[tid] = 0u;
-  if (tid == 0) ncand = 0u;
+  const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   if (tid == 0) {
     res[0] = 0;
     res[1] = 0;
@@ -915,54 +943,59 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
   const uint32_t b1 = res[0], A = res[1], nb1 = res[2];
   uint32_t T, need_eq;
   if (nb1 <= (uint32_t)kCandCap) {
-    // classify: above b1 -> selected; in b1 -> candidate
+    // candidates: count per wave, then append in wave order
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) cnt += (uint32_t)__popcll(__ballot((kr[e] >> 20) == b1) & sel_valid(V, wave, e));
+    if (lane == 0) wcnt[wave] = cnt;
+#pragma unroll
+    for (int i = 0; i < kHistBins / 1024; ++i) sh[tid + 1024 * i] = 0u;
+    if (tid < 256) sh2[tid] = 0u;
+    lds_barrier();
+    uint32_t off = 0;
+    for (int w2 = 0; w2 < wave; ++w2) off += wcnt[w2];
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
-      const int x = tid + 1024 * e;
-      const uint32_t bin = kr[e] >> 20;
-      if (x < V && bin > b1) atomicOr(&bm[x >> 5], 1u << (x & 31));
-      if (x < V && bin == b1) {
-        const uint32_t sl = atomicAdd(&ncand, 1u);
-        if (sl < (uint32_t)kCandCap) {
-          ck[sl] = kr[e];
-          ci[sl] = (uint32_t)x;
+      const unsigned long long bl = __ballot((kr[e] >> 20) == b1) & sel_valid(V, wave, e);
+      if (bl) {   // wave-uniform: most key steps hold no candidate
+        const uint32_t at = off + (uint32_t)__popcll(bl & lt);
+        if (((bl >> lane) & 1ull) && at < (uint32_t)kCandCap) {
+          ck[at] = kr[e];
+          ci[at] = (uint32_t)(tid + 1024 * e);
         }
+        off += (uint32_t)__popcll(bl);
       }
     }
-    __syncthreads();
-    const int nc = (int)min(ncand, (uint32_t)kCandCap);
+    if (tid == 0) {
+      res[0] = 0;
+      res[1] = 0;
+    }
+    lds_barrier();
+    const int nc = (int)min(nb1, (uint32_t)kCandCap);
     uint32_t need = (uint32_t)k - A;
-    uint32_t prefix = b1 << 20, mask = 0xfff00000u;
-#pragma unroll 1
-    for (int lvl = 0; lvl < 2; ++lvl) {
-      const int shift = lvl == 0 ? 8 : 0;
-      const int nb = lvl == 0 ? 4096 : 256;
-      for (int e = tid; e < kHistBins; e += 1024) sh[e] = 0;
-      __syncthreads();
-      for (int c = tid; c < nc; c += 1024) {
-        const uint32_t key = ck[c];
-        if ((key & mask) == prefix) atomicAdd(&sh[(key >> shift) & (nb - 1)], 1u);
-      }
-      __syncthreads();
-      uint32_t v[4];
+    // level 0: key bits 8..19 of the candidates
+    for (int c = tid; c < nc; c += 1024) atomicAdd(&sh[(ck[c] >> 8) & 4095u], 1u);
+    lds_barrier();
+    uint32_t v[4];
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) v[i2] = (4 * tid + i2 < nb) ? sh[4 * tid + i2] : 0u;
-      if (tid == 0) {
-        res[0] = 0;
-        res[1] = 0;
-      }
-      find_from_top<4>(v, need, wsum, res);
-      prefix |= res[0] << shift;
-      mask |= (uint32_t)(nb - 1) << shift;
-      need -= res[1];
+    for (int i2 = 0; i2 < 4; ++i2) v[i2] = sh[4 * tid + i2];
+    find_from_top<4>(v, need, wsum, res);
+    const uint32_t prefix = (b1 << 20) | (res[0] << 8);
+    need -= res[1];
+    lds_barrier();   // every thread has read res
+    if (tid == 0) {
+      res[0] = 0;
+      res[1] = 0;
     }
-    T = prefix;
-    need_eq = need;
-    for (int c = tid; c < nc; c += 1024) {
-      const uint32_t key = ck[c], x = ci[c];
-      if (key > T) atomicOr(&bm[x >> 5], 1u << (x & 31));
-      else if (key == T) atomicOr(&eqm[x >> 5], 1u << (x & 31));
-    }
+    // level 1: bits 0..7 of the candidates that share bits 8..31
+    for (int c = tid; c < nc; c += 1024)
+      if ((ck[c] & 0xffffff00u) == prefix) atomicAdd(&sh2[ck[c] & 255u], 1u);
+    lds_barrier();
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) v[i2] = 4 * tid + i2 < 256 ? sh2[4 * tid + i2] : 0u;
+    find_from_top<4>(v, need, wsum, res);
+    T = prefix | res[0];
+    need_eq = need - res[1];
   } else {
     // heavily tied scores: radix select over all keys (d = M - key)
     uint32_t mloc = 0;
@@ -972,51 +1005,53 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
     auto count_level = [&](int shift, int nbits, uint32_t pfx, uint32_t pmask, uint32_t* h) {
       const uint32_t nbn = 1u << nbits;
       for (int e = tid; e < (int)nbn; e += 1024) h[e] = 0;
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int e = 0; e < KPT; ++e) {
         const uint32_t dd = M - kr[e];
         if (tid + 1024 * e < V && (dd & pmask) == pfx) atomicAdd(&h[(dd >> shift) & (nbn - 1u)], 1u);
       }
-      __syncthreads();
+      lds_barrier();
     };
     T = radix_select(M, (uint32_t)k, count_level, sh, wsum, res, &need_eq);
+  }
+  // bitmaps of key > T and key == T: lanes 0 and 1 write the low and high
+  // words of each ballot
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-      const int x = tid + 1024 * e;
-      if (x < V && kr[e] > T) atomicOr(&bm[x >> 5], 1u << (x & 31));
-      else if (x < V && kr[e] == T) atomicOr(&eqm[x >> 5], 1u << (x & 31));
+  for (int e = 0; e < KPT; ++e) {
+    const unsigned long long vm = sel_valid(V, wave, e);
+    const unsigned long long bg = __ballot(kr[e] > T) & vm, be = __ballot(kr[e] == T) & vm;
+    if (lane < 2) {
+      const int wd = 32 * e + 2 * wave + lane;
+      gtw[wd] = (uint32_t)(lane ? bg >> 32 : bg);
+      eqw[wd] = (uint32_t)(lane ? be >> 32 : be);
     }
   }
-  __syncthreads();
-  // the need_eq lowest-index rows equal to T join the selection
+  lds_barrier();
+  // word tid covers rows 32 tid .. 32 tid + 31: its slot from the counts of
+  // the words before it (key > T in the high half, key == T in the low half)
   {
-    const uint32_t ew = eqm[tid];
+    const uint32_t g = gtw[tid], q = eqw[tid];
     uint32_t tot;
-    uint32_t rank = block_exscan((uint32_t)__popc(ew), wsum, &tot);
-    uint32_t keep = 0u, bits = ew;
-    while (bits && rank < need_eq) {
+    const uint32_t before = block_exscan(((uint32_t)__popc(g) << 16) | (uint32_t)__popc(q), wsum, &tot);
+    const uint32_t gt_before = before >> 16, eq_before = before & 0xffffu;
+    uint32_t keep = 0u, bits = q, r = eq_before;
+    while (bits && r < need_eq) {
       const uint32_t lowest = bits & (~bits + 1u);
       keep |= lowest;
       bits ^= lowest;
-      ++rank;
+      ++r;
     }
-    bm[tid] |= keep;
-  }
-  __syncthreads();
-  // ascending emission: word t covers rows 32 t .. 32 t + 31
-  {
-    const uint32_t wd = bm[tid];
-    uint32_t tot;
-    uint32_t slot = block_exscan((uint32_t)__popc(wd), wsum, &tot);
-    uint32_t bits = wd;
-    while (bits) {
-      const int bpos = __ffs(bits) - 1;
-      bits &= bits - 1;
+    uint32_t sel = g | keep;
+    uint32_t slot = gt_before + min(eq_before, need_eq);
+    while (sel) {
+      const int bpos = __ffs(sel) - 1;
+      sel &= sel - 1;
       if (slot < (uint32_t)k) o[slot] = 32 * tid + bpos;
       ++slot;
     }
-    for (int j = (int)tot + tid; j < k; j += 1024) o[j] = -1;
+    const uint32_t total = (tot >> 16) + min(tot & 0xffffu, need_eq);
+    for (int j = (int)total + tid; j < k; j += 1024) o[j] = -1;
   }
 }
 
@@ -1032,8 +1067,7 @@ __global__ __launch_bounds__(1024) void k_topk_decode(LayerParams P, const uint3
   const u32x4 h4 = *(const u32x4*)(gh + 4 * tid);
   const uint32_t* kq = keys + (size_t)qn * P.cap;
   uint32_t kr[kSelKPT];
-#pragma unroll
-  for (int e = 0; e < kSelKPT; ++e) kr[e] = kq[min(tid + 1024 * e, P.cap - 1)];
+  sel_load_keys(kq, P.cap, tid, kr);
   *(u32x4*)(gh + 4 * tid) = (u32x4){0u, 0u, 0u, 0u};
   if (V <= k) {   // every visible row is taken
     for (int j = tid; j < k; j += 1024) o[j] = j < V ? j : -1;
@@ -1067,85 +1101,88 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   idx_score_block<MT, 4, QF, true>(P, idx, qI, wt, pos, 0, 0, keys, hist, i % nrb, i / nrb, true);
 }
 
-// k_step_select: one block of 1024 threads per sequence.  The query's keys
-// and histogram are loaded first; the compressor (state store, raw row,
-// pooling, RMSNorm, RoPE, cache insertion) runs on the block; when the token
-// closed a row, its indexer score is computed here (the rotated query cast to
-// the indexer format, dotted with the row's stored values, relu, weighted head
-// sum) and joins the keys and the histogram; then the selection.
+// k_step_select: one block of 1024 threads per sequence.  The indexer query
+// and the histogram are loaded first, then the compressor's inputs, then the
+// query's keys, which stay in flight while the compressor (state store, raw
+// row, pooling, RMSNorm, RoPE, cache insertion) runs on the block; when the
+// token closed a row, its indexer score is computed here (the rotated query
+// cast to the indexer format, dotted with the row's stored values, relu,
+// weighted head sum) and joins the keys and the histogram; then the selection.
 template <int KVF, int IDXF, int ACTF>
 __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, Cache cc, const void* __restrict__ u,
                                                       const int32_t* __restrict__ pos, const float* __restrict__ proj,
                                                       int B, const void* __restrict__ qI,
                                                       const float* __restrict__ wt, const uint32_t* __restrict__ keys,
                                                       SelWs S, int32_t* __restrict__ out) {
-  constexpr int TPC = 4;   // four threads per channel pair share the c4a window
-  __shared__ float red[64];
-  __shared__ float mrg[TPC * (kMaxD / 2 + kMaxDI / 2) * 6];
+  static_assert(ACTF == CKV_BF16 && IDXF == CKV_BF16, "the fused step takes bf16 activations and indexer rows");
+  constexpr int DI = 128, CPT = DI / 16;
+  __shared__ __attribute__((aligned(16))) float red[64];
   __shared__ float idx_row[kMaxDI];
   __shared__ float hsum[64];
+  __shared__ float rtab[128];
+  __shared__ __attribute__((aligned(16))) uint32_t h_lds[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t q_lds[64 * DI / 2];
   const int qn = blockIdx.x, tid = threadIdx.x;
-  const int k = P.topk;
+  const int k = P.topk, HI = P.HI;
   const IdxQuery Q = idx_query(P, pos, 0, 0, qn);
   const int V = Q.V;
   int32_t* o = out + (size_t)qn * k;
+  // this thread's 8 channels of one indexer head (heads past H_I read the
+  // last one) and histogram bins 4 tid .. 4 tid + 3
   uint32_t* gh = S.hist + (size_t)qn * kHistBins;
+  const int hh = tid >> 4, c0 = (tid & 15) * CPT;
+  const u32x4 q4 = *(const u32x4*)((const uint16_t*)qI + ((size_t)qn * HI + min(hh, HI - 1)) * DI + c0);
   const u32x4 h4 = *(const u32x4*)(gh + 4 * tid);
-  const uint32_t* kq = keys + (size_t)qn * P.cap;
+  const float wv = wt[(size_t)qn * HI + min(hh, HI - 1)];
+  // the compressor; the keys are issued after its own loads, so its waits
+  // for them do not wait for the keys (no store is issued before those
+  // waits: with loads and stores both in flight, every wait is a wait for all)
   uint32_t kr[kSelKPT];
-#pragma unroll
-  for (int e = 0; e < kSelKPT; ++e) kr[e] = kq[min(tid + 1024 * e, P.cap - 1)];
-  // this thread's share of the indexer query (head tid / 16, DI / 16 channels)
-  const int HI = P.HI, DI = P.DI, cpt = DI / 16;
-  const int hh = min(tid >> 4, max(HI - 1, 0)), c0 = (tid & 15) * cpt;
-  static_assert(ACTF == CKV_BF16, "the fused step takes bf16 activations");
-  const u32x4 qraw = *(const u32x4*)((const uint16_t*)qI + ((size_t)qn * HI + hh) * DI + c0);
-  const float wv = wt[(size_t)qn * HI + hh];
+  // (the query and the histogram, the first loads issued, are parked in LDS
+  // once the keys are on their way: registers are short while the compressor
+  // holds its window)
+  const int st = compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, B, qn, red, rtab, idx_row, [&] {
+    sel_load_keys(keys + (size_t)qn * P.cap, P.cap, tid, kr);
+    *(u32x4*)(h_lds + 4 * tid) = h4;
+    *(u32x4*)(q_lds + 4 * tid) = q4;
+  });
+  // the histogram is left zero for the next call (its load has completed)
   *(u32x4*)(gh + 4 * tid) = (u32x4){0u, 0u, 0u, 0u};
-
-  const int st = compress_decode_seq<KVF, IDXF, ACTF, 8, TPC, 1>(P, w, cc, u, pos, proj, 1, B, qn, red, mrg, idx_row);
-  if (st < 0) {
-    for (int j = tid; j < k; j += 1024) o[j] = -1;
-    return;
-  }
-  if (V <= k) {
+  if (st < 0 || V <= k) {   // bad position (V = 0), or every visible row is taken
     for (int j = tid; j < k; j += 1024) o[j] = j < V ? j : -1;
     return;
   }
-  uint32_t hv[4] = {h4[0], h4[1], h4[2], h4[3]};
-  if (st == 1 && Q.V == (Q.p + 1) / 4) {
-    // score of row V - 1: rotate the query tail at p, cast to the cache format
-    __syncthreads();   // idx_row complete
+  lds_barrier();   // idx_row complete
+  const u32x4 h4s = *(const u32x4*)(h_lds + 4 * tid);
+  uint32_t hv[4] = {h4s[0], h4s[1], h4s[2], h4s[3]};
+  if (st == 1 && V == (Q.p + 1) / 4) {
+    // score of row V - 1: query tail rotated at p, cast to bf16, dotted with the row
     const int dn = DI - P.idx_rot;
+    const u32x4 q4s = *(const u32x4*)(q_lds + 4 * tid);
     float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      if (e < cpt) {
-        float a = bf16_to_f32(qraw[e >> 1] & 0xffffu), b2 = bf16_to_f32(qraw[e >> 1] >> 16);
-        const int c = c0 + e;
-        if (c >= dn) {
-          float cs, sn;
-          rope_cs(P, (c - dn) >> 1, (double)Q.p, &cs, &sn);
-          const float x = a * cs - b2 * sn, y = a * sn + b2 * cs;
-          a = x;
-          b2 = y;
-        }
-        if (IDXF == CKV_BF16) {
-          a = bf16_to_f32(f32_to_bf16(a));
-          b2 = bf16_to_f32(f32_to_bf16(b2));
-        }
-        dot += a * idx_row[c] + b2 * idx_row[c + 1];
+    for (int i = 0; i < CPT / 2; ++i) {
+      float a = bf16_to_f32(q4s[i] & 0xffffu), b2 = bf16_to_f32(q4s[i] >> 16);
+      const int c = c0 + 2 * i;
+      if (c >= dn) {   // the query's tail at p: the same frequencies as the raw row's
+        const int j = (c - dn) >> 1;
+        const float x = a * rtab[j] - b2 * rtab[64 + j], y = a * rtab[64 + j] + b2 * rtab[j];
+        a = x;
+        b2 = y;
       }
+      a = bf16_to_f32(f32_to_bf16(a));
+      b2 = bf16_to_f32(f32_to_bf16(b2));
+      dot += a * idx_row[c] + b2 * idx_row[c + 1];
     }
 #pragma unroll
     for (int o2 = 1; o2 < 16; o2 <<= 1) dot += __shfl_xor(dot, o2, 64);
     const bool relu = !(P.flags & CKV_FLAG_IDX_NO_RELU);
-    if ((tid & 15) == 0) hsum[tid >> 4] = (tid >> 4) < HI ? wv * (relu ? fmaxf(dot, 0.f) : dot) : 0.f;
-    __syncthreads();
+    if ((tid & 15) == 0) hsum[hh] = hh < HI ? wv * (relu ? fmaxf(dot, 0.f) : dot) : 0.f;
+    lds_barrier();
     float sc = 0.f;
     for (int h = 0; h < HI; ++h) sc += hsum[h];
     const uint32_t key = float_key(sc);
-    const int x = V - 1;
+    const int x = V - 1;   // row t + 1024 e is key e of thread t
 #pragma unroll
     for (int e = 0; e < kSelKPT; ++e)
       if (e == (x >> 10) && tid == (x & 1023)) kr[e] = key;
@@ -1156,8 +1193,6 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
   }
   topk_decode_select(P, V, kr, hv, o);
 }
-
-// ---------------------------------------------------------------- launchers
 
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
                    const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, const SelWs* sel,
@@ -1184,6 +1219,7 @@ int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const f
 
 bool step_fusable(const LayerParams& P, int B) {
   return P.ratio == 4 && P.idx_fmt == CKV_BF16 && P.DI == 128 && P.HI <= 64 && P.cap <= 32768 &&
+         P.idx_rot == P.n_rot && P.n_rot == 64 &&
          P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && B <= 64 && P.d <= 512;
 }
 

@@ -200,6 +200,18 @@ def test_decode_step_full_size(name):
                            FP8_TOL if cfg.kv_fmt == "e4m3" else BF16_TOL)
 
 
+@pytest.mark.parametrize("cap,n", [(40000, (159000, 100001)), (1022, (4088, 2050))])
+def test_decode_selection_beyond_one_block(cap, n):
+    """Caches the one-block selection does not take (more than 32768 rows, or
+    a capacity that is not a multiple of 4): the chunked classify + finish
+    selection, through the stage calls and the single-call step."""
+    cfg = get_config("c5").with_(batch=2, comp_cap=cap, seed=17, name=f"cap{cap}")
+    inp = make_decode_inputs(cfg, n_ctx=np.array(n, np.int64))
+    wts = make_layer_weights(cfg)
+    run_decode_stage_checks(cfg, inp, wts, FP8_TOL)
+    run_decode_step_checks(cfg, inp, wts, FP8_TOL)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
 def test_decode_step_short_contexts(fmt):
     """Fused step on short and ragged contexts: V <= k, the first rows,
