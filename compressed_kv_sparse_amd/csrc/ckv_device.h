@@ -106,15 +106,52 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---------------------------------------------------------------- reductions
 
+// Cross-lane steps on DPP (data-parallel primitives: a lane reads another
+// lane's register within the VALU operation, no LDS round trip).  Controls:
+// quad_perm [1,0,3,2] = 0xb1, [2,3,0,1] = 0x4e, row_half_mirror = 0x141,
+// row_mirror = 0x140, row_shr:n = 0x110 + n, row_bcast:15 = 0x142 (lane 15
+// of each row to the next row), row_bcast:31 = 0x143 (lane 31 to rows 2, 3).
+// Lanes whose source is masked off or out of range receive `old`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f32(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xf,
+                                                    false));
+}
+
+// Wave-wide sum / max, returned to every lane: butterflies inside each row of
+// 16 lanes, then the row totals chained through lanes 15 and 31 up to lane 63,
+// which is read back as a scalar.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f32<0xb1>(0.f, v);
+  v += dpp_f32<0x4e>(0.f, v);
+  v += dpp_f32<0x141>(0.f, v);
+  v += dpp_f32<0x140>(0.f, v);
+  v += dpp_f32<0x142, 0xa>(0.f, v);
+  v += dpp_f32<0x143, 0xc>(0.f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f32<0xb1>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x4e>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x141>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x140>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x142, 0xa>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x143, 0xc>(-INFINITY, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// Inclusive prefix sum over the wave's lanes (lane order).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u32<0x111>(0u, x);
+  x += dpp_u32<0x112>(0u, x);
+  x += dpp_u32<0x114>(0u, x);
+  x += dpp_u32<0x118>(0u, x);
+  x += dpp_u32<0x142, 0xa>(0u, x);
+  x += dpp_u32<0x143, 0xc>(0u, x);
+  return x;
 }
 
 // Block-wide sum; `red` is LDS scratch of at least blockDim.x/64 floats.

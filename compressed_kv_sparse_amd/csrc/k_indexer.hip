@@ -311,12 +311,7 @@ __global__ __launch_bounds__(256) void k_idx_score_vec(LayerParams P, const void
 // exclusive sum, *total receives the block total.
 __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   lds_barrier();
   if (lane == 63) wsum[wave] = x;
   lds_barrier();
@@ -330,8 +325,7 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* wsum, uin
 }
 
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* wsum) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), 63);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   lds_barrier();
   if (lane == 0) wsum[wave] = v;
@@ -461,8 +455,13 @@ __device__ __forceinline__ void emit_selected(KeyAt key_at, int c0, int c1, uint
 }
 
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* wsum) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, 64));
+  v = max(v, dpp_u32<0xb1>(0u, v));
+  v = max(v, dpp_u32<0x4e>(0u, v));
+  v = max(v, dpp_u32<0x141>(0u, v));
+  v = max(v, dpp_u32<0x140>(0u, v));
+  v = max(v, dpp_u32<0x142, 0xa>(0u, v));
+  v = max(v, dpp_u32<0x143, 0xc>(0u, v));
+  v = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   lds_barrier();
   if (lane == 0) wsum[wave] = v;
@@ -902,16 +901,10 @@ __device__ __forceinline__ void sel_load_keys(const uint32_t* kq, int cap, int t
   for (int e = 0; e < kSelKPT; ++e) kr[e] = kq[min(t + 1024 * e, cap - 1)];
 }
 
-// Lanes of this wave whose key e is a visible row (row < V), wave-uniform.
-__device__ __forceinline__ unsigned long long sel_valid(int V, int wave, int e) {
-  const int left = V - (1024 * e + 64 * wave);
-  return left >= 64 ? ~0ull : (left <= 0 ? 0ull : (~0ull >> (64 - left)));
-}
-
 // The selection itself, from keys kr (row tid + 1024 e) and histogram bins
 // hv (bins 4 tid .. 4 tid + 3) held by the 1024 threads of the block, V > k.
 //   1. b1 = the 12-bit key bin holding the k-th largest key (histogram scan);
-//   2. the keys in b1 are appended to a candidate list (ballot counts, one
+//   2. the keys in b1 are appended to a candidate list (per-thread counts, one
 //      block scan, no atomics) and refined by two radix levels (12 + 8 bits)
 //      to the k-th largest key T and the number of keys equal to T to take;
 //      with more candidates than the list holds, a radix select over all keys;
@@ -919,9 +912,9 @@ __device__ __forceinline__ unsigned long long sel_valid(int V, int wave, int e) 
 //      scan of the words' packed popcounts gives every 32-row word its output
 //      slot, rows equal to T being taken lowest index first; rows are written
 //      ascending.
-// The per-key work is a compare or two and wave-level bit operations: with
-// one block per query the selection runs on one compute unit, so its cost is
-// the vector instructions per key.
+// With one block per query the selection runs on one compute unit, so its
+// cost is the instructions per key: a few vector operations, and scalar ones
+// (shared by the unit's 16 waves) only where a ballot is the product.
 __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, uint32_t (&kr)[kSelKPT],
                                                    uint32_t (&hv)[4], int32_t* __restrict__ o) {
   constexpr int KPT = kSelKPT;
@@ -929,11 +922,11 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
   __shared__ uint32_t eqw[1024];   // rows with key == T
   __shared__ uint32_t sh[kHistBins], sh2[256];
   __shared__ uint32_t ck[kCandCap], ci[kCandCap];
-  __shared__ uint32_t wsum[16], res[4], wcnt[16];
+  __shared__ uint32_t wsum[16], res[4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = P.topk;
-  const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int nv = (V - tid + 1023) >> 10;   // this thread's keys e < nv are visible rows
   if (tid == 0) {
     res[0] = 0;
     res[1] = 0;
@@ -943,27 +936,24 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
   const uint32_t b1 = res[0], A = res[1], nb1 = res[2];
   uint32_t T, need_eq;
   if (nb1 <= (uint32_t)kCandCap) {
-    // candidates: count per wave, then append in wave order
+    // candidates: per-thread counts, their block scan, then each thread
+    // appends its own at its offset
     uint32_t cnt = 0;
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) cnt += (uint32_t)__popcll(__ballot((kr[e] >> 20) == b1) & sel_valid(V, wave, e));
-    if (lane == 0) wcnt[wave] = cnt;
+    for (int e = 0; e < KPT; ++e) cnt += (e < nv && (kr[e] >> 20) == b1) ? 1u : 0u;
 #pragma unroll
     for (int i = 0; i < kHistBins / 1024; ++i) sh[tid + 1024 * i] = 0u;
     if (tid < 256) sh2[tid] = 0u;
-    lds_barrier();
-    uint32_t off = 0;
-    for (int w2 = 0; w2 < wave; ++w2) off += wcnt[w2];
+    uint32_t ctot;
+    uint32_t at = block_exscan(cnt, wsum, &ctot);
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
-      const unsigned long long bl = __ballot((kr[e] >> 20) == b1) & sel_valid(V, wave, e);
-      if (bl) {   // wave-uniform: most key steps hold no candidate
-        const uint32_t at = off + (uint32_t)__popcll(bl & lt);
-        if (((bl >> lane) & 1ull) && at < (uint32_t)kCandCap) {
+      if (e < nv && (kr[e] >> 20) == b1) {
+        if (at < (uint32_t)kCandCap) {
           ck[at] = kr[e];
           ci[at] = (uint32_t)(tid + 1024 * e);
         }
-        off += (uint32_t)__popcll(bl);
+        ++at;
       }
     }
     if (tid == 0) {
@@ -1019,8 +1009,7 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
   // words of each ballot
 #pragma unroll
   for (int e = 0; e < KPT; ++e) {
-    const unsigned long long vm = sel_valid(V, wave, e);
-    const unsigned long long bg = __ballot(kr[e] > T) & vm, be = __ballot(kr[e] == T) & vm;
+    const unsigned long long bg = __ballot(e < nv && kr[e] > T), be = __ballot(e < nv && kr[e] == T);
     if (lane < 2) {
       const int wd = 32 * e + 2 * wave + lane;
       gtw[wd] = (uint32_t)(lane ? bg >> 32 : bg);

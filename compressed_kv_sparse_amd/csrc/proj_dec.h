@@ -38,10 +38,10 @@ inline WCat make_wcat(const LayerParams& P, const Weights& w) {
 }
 
 // bf16 x bf16 on MFMA: 16 columns (col0 ..) x 16 rows (m0 ..) over all of K,
-// the NW waves of the block taking the k-steps w, w + NW, ... (eight of them
-// in flight per round, loads unconditional with the step clamped); partial
+// the NW waves of the block taking the k-steps w, w + NW, ... (SF of them in
+// flight per round, loads unconditional with the step clamped); partial
 // tiles summed through LDS in wave order.  Writes part[m][col].
-template <int NW>
+template <int NW, int SF = 8>
 __device__ __forceinline__ void proj_tile(const uint16_t* __restrict__ X, int M, int K, const WCat& wc, int ncol,
                                           float* __restrict__ part, int col0, int m0) {
   __shared__ f32x4 red[NW][64];
@@ -52,16 +52,16 @@ __device__ __forceinline__ void proj_tile(const uint16_t* __restrict__ X, int M,
   const uint16_t* xrow = X + (size_t)min(m0 + r, M - 1) * K;
   const int nsteps = K / 32;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = wave; s0 < nsteps; s0 += NW * 8) {
-    u32x4 a[8], b[8];
+  for (int s0 = wave; s0 < nsteps; s0 += NW * SF) {
+    u32x4 a[SF], b[SF];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < SF; ++e) {
       const int k = 32 * min(s0 + NW * e, nsteps - 1) + 8 * g;
       a[e] = *(const u32x4*)(xrow + k);
       b[e] = *(const u32x4*)(wrow + k);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < SF; ++e)
       if (s0 + NW * e < nsteps) acc = mfma16x16x32(as_bf16x8(a[e]), as_bf16x8(b[e]), acc);
   }
   red[wave][lane] = acc;
