@@ -106,6 +106,42 @@ def score_kernel_bytes(cfg, n):
     return tot
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic_c5.md")
+
+
+def score_kernel_source_hash():
+    """sha256 of the score kernel's source: its section of k_indexer.hip and
+    the device helpers it includes.  A recorded HBM traffic figure is valid only
+    for the source it was measured on."""
+    import hashlib
+    csrc = os.path.join(ROOT, "compressed_kv_sparse_amd", "csrc")
+    src = open(os.path.join(csrc, "k_indexer.hip")).read()
+    a = src.index("// ---------------------------------------------------------------- MFMA score")
+    b = src.index("// ---------------------------------------------------------------- vector score")
+    h = hashlib.sha256(src[a:b].encode())
+    h.update(open(os.path.join(csrc, "ckv_device.h"), "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the score kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
+    for a copy of known size), or None when the kernel's source has changed
+    since."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    kv = {}
+    for ln in lines:
+        if ln.startswith("- ") and ": " in ln:
+            k, v = ln[2:].split(": ", 1)
+            kv[k.strip()] = v.strip().strip("`")
+    if kv.get("source_sha256") != score_kernel_source_hash():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
 def prefill_flops(cfg, pos0, T):
     d, D, H, HI, DI, k = cfg.head_dim, cfg.hidden, cfg.n_heads, cfg.idx_heads, cfg.idx_dim, cfg.top_k
     f = 2.0 * T * D * 2 * (d + DI)
@@ -385,7 +421,8 @@ def main():
         log(f"[bench] {kern['name']}: {kern['avg_us']:.1f} us, {kern['gbs']:.0f} GB/s")
         roof = {"bound": "hbm", "kernel": kern["name"], "achieved": round(kern["gbs"], 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern["gbs"] / HBM_PEAK_GBS, 4),
-                "avg_us": round(kern["avg_us"], 2), "bytes_per_launch": int(kern["bytes"]), "traffic": None}
+                "avg_us": round(kern["avg_us"], 2), "bytes_per_launch": int(kern["bytes"]),
+                "traffic": recorded_traffic() if cfg.name.startswith("c5") else None}
     extra = {}
     if args.extra:
         for name in ("c2", "c3", "c5_c128a", "c5_swa"):
