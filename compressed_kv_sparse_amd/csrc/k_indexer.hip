@@ -236,6 +236,141 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   idx_score_block<MT, KS, QF, HIST>(P, idx, qI, wt, pos, seq_fixed, pos0, keys, hist, blockIdx.x, blockIdx.y, false);
 }
 
+// ---------------------------------------------------------------- prefill score GEMM
+// Chunked prefill scores every query of the chunk against every row it sees:
+// a [T x H_I, D_I] x [D_I, V] product.  One block takes 8 consecutive
+// queries (one per wave, its rotated query held as MFMA A fragments) and a run
+// of kPfTiles row tiles of 256 rows; each tile is staged once in LDS (rows
+// padded to 272 bytes, so the 16 lanes of a B-fragment read hit distinct
+// banks) and multiplied by all 8 queries, so a row is read from memory once
+// per 8 queries instead of once per query.  The next tile's loads are issued
+// before the current one is multiplied.  Rows at or past a query's V get
+// keys that are never read (the select stops at V); rows past the group's
+// last visible row re-read that row.  grid: x = row runs, y = query groups.
+// Heads are the MFMA M dimension and rows N: a lane's accumulators hold 4
+// heads of one row, so the weighted head sum is in-lane adds plus a sum over
+// the 4 lane groups (v_permlane32_swap / v_permlane16_swap, no LDS); relu is
+// one integer max on the float's bits (negative floats have negative bit
+// patterns, so max(bits, 0) is relu; a lower bound of INT_MIN keeps x), which
+// needs no NaN-quieting step in front as a float max does.
+constexpr int kPfRows = 256, kPfQ = 8, kPfTiles = 8, kPfStride = 136;   // LDS row: 128 + 8 halfwords
+
+template <int MT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_idx_score_prefill(
+    LayerParams P, const uint16_t* idx, const uint16_t* __restrict__ qI, const float* __restrict__ wt, int seq,
+    int pos0, int T, uint32_t* __restrict__ keys) {
+  constexpr int DI = 128, KS = DI / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kPfRows * kPfStride];
+  __shared__ float cs_[kPfQ][32], sn_[kPfQ][32];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.y * kPfQ;
+  const int nlast = min(n0 + kPfQ, T) - 1;
+  const int vmax = min((pos0 + nlast + 1) / 4, P.cap);   // rows the group's last query sees
+  const int row0 = blockIdx.x * kPfRows * kPfTiles;
+  if (row0 >= vmax) return;
+  const int HI = P.HI, dn = DI - P.idx_rot;
+  const int n = min(n0 + wave, T - 1);   // waves past the chunk redo its last query
+  const uint16_t* base = idx + (size_t)seq * P.cap * DI;
+  const int vlast = vmax - 1;
+
+  // tile loads: thread t takes 16-byte chunks c = t + 512 e of the 256 x 256-byte tile
+  auto load_tile = [&](u32x4(&v)[8], int rb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = tid + 512 * e;
+      v[e] = *(const u32x4*)(base + (size_t)min(rb + (c >> 4), vlast) * DI + 8 * (c & 15));
+    }
+  };
+  u32x4 pf[8];
+  load_tile(pf, row0);
+  // this lane's query fragments: head 16 mt + r, channels 32 ks + 8 g .. + 7
+  u32x4 qraw[MT][KS];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[mt][ks] = *(const u32x4*)(qI + ((size_t)n * HI + min(16 * mt + r, HI - 1)) * DI + 32 * ks + 8 * g);
+  // weights of the heads this lane's accumulators hold: head 16 mt + 4 g + i
+  float wv[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * mt + 4 * g + i;
+      wv[mt][i] = h < HI ? wt[(size_t)n * HI + min(h, HI - 1)] : 0.f;
+    }
+  if (tid < kPfQ * 32) {
+    const int qq = tid >> 5, j = tid & 31;
+    rope_cs(P, j, (double)(pos0 + min(n0 + qq, T - 1)), &cs_[qq][j], &sn_[qq][j]);
+  }
+  lds_barrier();
+  // rotated query -> bf16 A fragments (heads past H_I are zero)
+  u32x4 Qf[MT][KS];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = bf16_to_f32(qraw[mt][ks][i] & 0xffffu), b = bf16_to_f32(qraw[mt][ks][i] >> 16);
+        const int c = 32 * ks + 8 * g + 2 * i;
+        if (c >= dn) {
+          const int j = (c - dn) >> 1;
+          const float x = a * cs_[wave][j] - b * sn_[wave][j], y = a * sn_[wave][j] + b * cs_[wave][j];
+          a = x;
+          b = y;
+        }
+        Qf[mt][ks][i] = 16 * mt + r < HI ? pack_bf16x2(a, b) : 0u;
+      }
+    }
+  const int lo = (P.flags & CKV_FLAG_IDX_NO_RELU) ? INT_MIN : 0;   // relu on the bits: max(bits, lo)
+  uint32_t* kout = keys + (size_t)n * P.cap;
+
+#pragma unroll 1
+  for (int t = 0; t < kPfTiles; ++t) {
+    const int rb = row0 + t * kPfRows;
+    if (rb >= vmax) break;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = tid + 512 * e;
+      *(u32x4*)&tile[(c >> 4) * kPfStride + 8 * (c & 15)] = pf[e];
+    }
+    lds_barrier();
+    if (t + 1 < kPfTiles) load_tile(pf, rb + kPfRows);   // next tile, in flight during this one
+#pragma unroll 1
+    for (int sq = 0; sq < kPfRows / 64; ++sq) {   // 4 groups of 4 sixteen-row sub-tiles
+      float sc[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint16_t* tr = &tile[(64 * sq + 16 * u + r) * kPfStride + 8 * g];
+        u32x4 Rv[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) Rv[ks] = *(const u32x4*)(tr + 32 * ks);
+        float sv = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(as_bf16x8(Qf[mt][ks]), as_bf16x8(Rv[ks]), acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv = fmaf(wv[mt][i], __int_as_float(max(__float_as_int(acc[i]), lo)), sv);
+        }
+        // sum over the 4 lane groups (rows r of groups 0..3 hold other heads)
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sv), __float_as_uint(sv), false, false);
+        sv = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
+        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sv), __float_as_uint(sv), false, false);
+        sc[u] = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);
+      }
+      const float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
+      const int row = rb + 64 * sq + 16 * g + r;
+      *(row < P.cap ? kout + row : g_key_sink + lane) = float_key(mine);
+    }
+    lds_barrier();   // every wave is done with the tile before it is overwritten
+  }
+}
+
 // ---------------------------------------------------------------- vector score
 // Any formats.  One thread per row.  grid: x = row blocks of 256, y = queries.
 template <int IDXF, int QF>
@@ -1252,7 +1387,20 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
   const int vmax = pos ? P.cap : (vlast < P.cap ? vlast : P.cap);
   dim3 grid((unsigned)(vmax > 0 ? (vmax + 255) / 256 : 1), nq);
   const bool mf = P.idx_fmt == CKV_BF16 && P.DI == 128 && P.HI <= 64;
-  if (mf) {
+  if (mf && !pos && !hist && P.act_fmt == CKV_BF16) {
+    const uint16_t* ix = (const uint16_t*)c.idx;
+    const int MT = (P.HI + 15) / 16;
+    constexpr int RUN = kPfRows * kPfTiles;
+    dim3 pgrid((unsigned)(vmax > 0 ? (vmax + RUN - 1) / RUN : 1), (unsigned)((nq + kPfQ - 1) / kPfQ));
+#define CKV_PF(MTV)                                                                                            \
+  hipLaunchKernelGGL((k_idx_score_prefill<MTV>), pgrid, dim3(512), 0, st, P, ix, (const uint16_t*)qI, w, seq, pos0, \
+                     nq, keys)
+    if (MT == 1) CKV_PF(1);
+    else if (MT == 2) CKV_PF(2);
+    else if (MT == 3) CKV_PF(3);
+    else CKV_PF(4);
+#undef CKV_PF
+  } else if (mf) {
     const uint16_t* ix = (const uint16_t*)c.idx;
     const int MT = (P.HI + 15) / 16;
     constexpr int RB = 256 * kScoreGroups;
