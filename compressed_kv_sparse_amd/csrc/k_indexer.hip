@@ -240,27 +240,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // Chunked prefill scores every query of the chunk against every row it sees:
 // a [T x H_I, D_I] x [D_I, V] product.  One block takes 8 consecutive
 // queries (one per wave, its rotated query held as MFMA A fragments) and a run
-// of kPfTiles row tiles of 256 rows; each tile is staged once in LDS (rows
-// padded to 272 bytes, so the 16 lanes of a B-fragment read hit distinct
-// banks) and multiplied by all 8 queries, so a row is read from memory once
-// per 8 queries instead of once per query.  The next tile's loads are issued
-// before the current one is multiplied.  Rows at or past a query's V get
-// keys that are never read (the select stops at V); rows past the group's
-// last visible row re-read that row.  grid: x = row runs, y = query groups.
+// of kPfTiles row tiles of 128 rows; each tile is staged once in LDS and
+// multiplied by all 8 queries, so a row is read from memory once per 8
+// queries instead of once per query.  Rows at or past a query's V get keys
+// that are never read (the select stops at V); rows past the group's last
+// visible row re-read that row.  grid: x = row runs, y = query groups.
+//
 // Heads are the MFMA M dimension and rows N: a lane's accumulators hold 4
 // heads of one row, so the weighted head sum is in-lane adds plus a sum over
 // the 4 lane groups (v_permlane32_swap / v_permlane16_swap, no LDS); relu is
 // one integer max on the float's bits (negative floats have negative bit
 // patterns, so max(bits, 0) is relu; a lower bound of INT_MIN keeps x), which
 // needs no NaN-quieting step in front as a float max does.
-constexpr int kPfRows = 256, kPfQ = 8, kPfTiles = 8, kPfStride = 136;   // LDS row: 128 + 8 halfwords
+//
+// Tiles are double-buffered in LDS and filled by direct global-to-LDS loads
+// (no registers: two blocks of 8 waves fit a compute unit).  A wave's load
+// instruction fills 1 KB = 4 rows, lane l taking 16-byte position l % 16 of
+// row l / 16; position q of row R holds the row's chunk q ^ (R % 16), so the
+// 16 lanes of a B-fragment read (16 rows, one chunk each) hit 16 distinct
+// bank groups.  The tile reads are inline asm: the compiler would otherwise
+// wait for every direct load in flight -- including the next tile's -- before
+// any LDS read.  The kernel therefore waits for the tile loads itself (all
+// counters, then a barrier) at the top of each tile, and reads no other LDS
+// in the tile loop.
+constexpr int kPfRows = 128, kPfQ = 8, kPfTiles = 16;
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// four 16-byte LDS reads, waited for
+__device__ __forceinline__ void lds_read4_b128(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4& r0,
+                                               u32x4& r1, u32x4& r2, u32x4& r3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
 
 template <int MT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_idx_score_prefill(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_idx_score_prefill(
     LayerParams P, const uint16_t* idx, const uint16_t* __restrict__ qI, const float* __restrict__ wt, int seq,
     int pos0, int T, uint32_t* __restrict__ keys) {
   constexpr int DI = 128, KS = DI / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kPfRows * kPfStride];
+  constexpr int TB = kPfRows * DI * 2;   // bytes per tile buffer
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[2 * TB];
   __shared__ float cs_[kPfQ][32], sn_[kPfQ][32];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -270,28 +299,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int vmax = min((pos0 + nlast + 1) / 4, P.cap);   // rows the group's last query sees
   const int row0 = blockIdx.x * kPfRows * kPfTiles;
   if (row0 >= vmax) return;
+  const int ntile = min(kPfTiles, (vmax - row0 + kPfRows - 1) / kPfRows);
   const int HI = P.HI, dn = DI - P.idx_rot;
   const int n = min(n0 + wave, T - 1);   // waves past the chunk redo its last query
   const uint16_t* base = idx + (size_t)seq * P.cap * DI;
   const int vlast = vmax - 1;
 
-  // tile loads: thread t takes 16-byte chunks c = t + 512 e of the 256 x 256-byte tile
-  auto load_tile = [&](u32x4(&v)[8], int rb) {
+  // direct loads of tile rb into buffer buf: instruction e of this wave fills
+  // rows 4 (8 e + wave) .. + 3
+  auto load_tile = [&](int buf, int rb) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = tid + 512 * e;
-      v[e] = *(const u32x4*)(base + (size_t)min(rb + (c >> 4), vlast) * DI + 8 * (c & 15));
+    for (int e = 0; e < kPfRows / 32; ++e) {
+      const int R = 4 * (8 * e + wave) + (lane >> 4);
+      const int q = (lane & 15) ^ (R & 15);
+      lds_dma16(base + (size_t)min(rb + R, vlast) * DI + 8 * q, tiles + buf * TB + 1024 * (8 * e + wave));
     }
   };
-  u32x4 pf[8];
-  load_tile(pf, row0);
+  load_tile(0, row0);
   // this lane's query fragments: head 16 mt + r, channels 32 ks + 8 g .. + 7
-  u32x4 qraw[MT][KS];
+  u32x4 Qf[MT][KS];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qraw[mt][ks] = *(const u32x4*)(qI + ((size_t)n * HI + min(16 * mt + r, HI - 1)) * DI + 32 * ks + 8 * g);
+      Qf[mt][ks] = *(const u32x4*)(qI + ((size_t)n * HI + min(16 * mt + r, HI - 1)) * DI + 32 * ks + 8 * g);
   // weights of the heads this lane's accumulators hold: head 16 mt + 4 g + i
   float wv[MT][4];
 #pragma unroll
@@ -307,14 +338,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   lds_barrier();
   // rotated query -> bf16 A fragments (heads past H_I are zero)
-  u32x4 Qf[MT][KS];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float a = bf16_to_f32(qraw[mt][ks][i] & 0xffffu), b = bf16_to_f32(qraw[mt][ks][i] >> 16);
+        float a = bf16_to_f32(Qf[mt][ks][i] & 0xffffu), b = bf16_to_f32(Qf[mt][ks][i] >> 16);
         const int c = 32 * ks + 8 * g + 2 * i;
         if (c >= dn) {
           const int j = (c - dn) >> 1;
@@ -327,27 +357,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   const int lo = (P.flags & CKV_FLAG_IDX_NO_RELU) ? INT_MIN : 0;   // relu on the bits: max(bits, lo)
   uint32_t* kout = keys + (size_t)n * P.cap;
+  // this lane's B-fragment byte offsets within a buffer, k-step ks: row r of
+  // a sixteen-row sub-tile, chunk 4 ks + g at position (4 ks + g) ^ r
+  uint32_t boff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) boff[ks] = lds_addr(tiles) + r * 256 + 16 * ((4 * ks + g) ^ r);
 
 #pragma unroll 1
-  for (int t = 0; t < kPfTiles; ++t) {
+  for (int t = 0; t < ntile; ++t) {
     const int rb = row0 + t * kPfRows;
-    if (rb >= vmax) break;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = tid + 512 * e;
-      *(u32x4*)&tile[(c >> 4) * kPfStride + 8 * (c & 15)] = pf[e];
-    }
-    lds_barrier();
-    if (t + 1 < kPfTiles) load_tile(pf, rb + kPfRows);   // next tile, in flight during this one
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's share of tile t has landed
+    lds_barrier();                    // ... everyone's, and buffer (t + 1) % 2 is free
+    if (t + 1 < ntile) load_tile((t + 1) & 1, rb + kPfRows);
+    const uint32_t bt = (uint32_t)((t & 1) * TB);
 #pragma unroll 1
-    for (int sq = 0; sq < kPfRows / 64; ++sq) {   // 4 groups of 4 sixteen-row sub-tiles
+    for (int sq = 0; sq < kPfRows / 64; ++sq) {   // groups of 4 sixteen-row sub-tiles
       float sc[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint16_t* tr = &tile[(64 * sq + 16 * u + r) * kPfStride + 8 * g];
+        const uint32_t so = bt + (uint32_t)(64 * sq + 16 * u) * 256;
         u32x4 Rv[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) Rv[ks] = *(const u32x4*)(tr + 32 * ks);
+        lds_read4_b128(boff[0] + so, boff[1] + so, boff[2] + so, boff[3] + so, Rv[0], Rv[1], Rv[2], Rv[3]);
         float sv = 0.f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -367,8 +397,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int row = rb + 64 * sq + 16 * g + r;
       *(row < P.cap ? kout + row : g_key_sink + lane) = float_key(mine);
     }
-    lds_barrier();   // every wave is done with the tile before it is overwritten
   }
+  __builtin_amdgcn_s_waitcnt(0);   // no direct load outlives the block
 }
 
 // ---------------------------------------------------------------- vector score

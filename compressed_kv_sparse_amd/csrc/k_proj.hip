@@ -77,6 +77,89 @@ __global__ __launch_bounds__(1024) void k_proj_dec(const uint16_t* __restrict__ 
   proj_tile<16>(X, M, K, wc, ncol, part, blockIdx.x * 16, blockIdx.y * 16);
 }
 
+// Chunk projection (M >= 128 rows): a tiled GEMM.  A block computes a 128 x 128
+// tile of part[m][col] (128 rows of x against 128 weight rows, which all lie
+// in one of the four weight matrices when d and D_I are multiples of 128);
+// wave w takes the 64 x 64 quadrant (w / 2, w % 2) as 4 x 4 MFMA tiles.  K is
+// walked in chunks of 64: both 128 x 64 operand tiles are staged in LDS
+// (double-buffered; the next chunk's global loads are issued before the
+// current chunk is multiplied).  A tile row is 128 bytes = 8 chunks of 16; row
+// R keeps chunk c at position c ^ ((R >> 1) & 7), so the 16 rows of a fragment
+// read spread over all banks.
+constexpr int kGM = 128, kGN = 128, kGK = 64;
+
+__device__ __forceinline__ int gsw(int R, int c) { return R * 128 + 16 * (c ^ ((R >> 1) & 7)); }
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_proj_gemm(
+    const uint16_t* __restrict__ X, int M, int K, WCat wc, int ncol, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint8_t sa[2][kGM * 128], sb[2][kGN * 128];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int col0 = blockIdx.x * kGN, m0 = blockIdx.y * kGM;
+  int local;
+  const uint16_t* W = (const uint16_t*)wcat_row(wc, col0, K, 2, &local);   // row col0 of its matrix
+  // staging: thread t moves 16-byte chunks t + 256 e (e < 4) of each 128 x 64 tile: row ch >> 3, chunk ch & 7
+  u32x4 pa[4], pb[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ch = tid + 256 * e, R = ch >> 3, c = ch & 7;
+      pa[e] = *(const u32x4*)(X + (size_t)min(m0 + R, M - 1) * K + k0 + 8 * c);
+      pb[e] = *(const u32x4*)(W + (size_t)R * K + k0 + 8 * c);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ch = tid + 256 * e, R = ch >> 3, c = ch & 7;
+      *(u32x4*)&sa[buf][gsw(R, c)] = pa[e];
+      *(u32x4*)&sb[buf][gsw(R, c)] = pb[e];
+    }
+  };
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int nk = K / kGK;
+  load(0);
+  store(0);
+  lds_barrier();
+#pragma unroll 1
+  for (int kc = 0; kc < nk; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < nk) load((kc + 1) * kGK);   // in flight during this chunk
+#pragma unroll
+    for (int ks = 0; ks < kGK / 32; ++ks) {
+      u32x4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[i] = *(const u32x4*)&sa[buf][gsw(wm + 16 * i + r, 4 * ks + g)];
+        bf[i] = *(const u32x4*)&sb[buf][gsw(wn + 16 * i + r, 4 * ks + g)];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j]);
+    }
+    if (kc + 1 < nk) store(buf ^ 1);
+    lds_barrier();
+  }
+  // D[4 g + e][r] of tile (i, j): row m0 + wm + 16 i + 4 g + e, column col0 + wn + 16 j + r
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = m0 + wm + 16 * i + 4 * g + e;
+      if (m < M) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[(size_t)m * ncol + col0 + wn + 16 * j + r] = acc[i][j][e];
+      }
+    }
+}
+
 // Any formats, vector ALU: one wave per (column, 4 rows), lanes stride K.
 // grid: x = ncol, y = ceil(M / 4).  Writes split 0.
 template <int XF, int WF>
@@ -107,6 +190,10 @@ int launch_proj(const LayerParams& P, const Weights& w, const void* x, int M, fl
   if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && M <= 64) {
     dim3 grid(P.ncol / 16, (M + 15) / 16);
     hipLaunchKernelGGL(k_proj_dec, grid, dim3(1024), 0, st, (const uint16_t*)x, M, K, wc, P.ncol, part);
+  } else if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && splits == 1 && M >= kGM && P.d % kGN == 0 &&
+             (P.ratio != 4 || P.DI % kGN == 0) && K % kGK == 0) {
+    dim3 grid(P.ncol / kGN, (M + kGM - 1) / kGM);
+    hipLaunchKernelGGL(k_proj_gemm, grid, dim3(256), 0, st, (const uint16_t*)x, M, K, wc, P.ncol, part);
   } else if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16) {
     const int klen = ((K / splits) + 31) / 32 * 32;
     dim3 grid((P.ncol + 63) / 64, splits, (M + 31) / 32);
