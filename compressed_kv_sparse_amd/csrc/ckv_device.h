@@ -143,6 +143,31 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f32<0x143, 0xc>(-INFINITY, v));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// Sum over each row of 16 lanes, every lane of the row receiving it.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xb1>(0.f, v);
+  v += dpp_f32<0x4e>(0.f, v);
+  v += dpp_f32<0x141>(0.f, v);
+  v += dpp_f32<0x140>(0.f, v);
+  return v;
+}
+
+// Sum / max over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (the same lane of the
+// four 16-lane rows), every lane receiving the result: v_permlane32_swap and
+// v_permlane16_swap exchange rows in the VALU, with no LDS round trip.
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Inclusive prefix sum over the wave's lanes (lane order).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   x += dpp_u32<0x111>(0u, x);

@@ -72,9 +72,10 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
     if (prefill) {
       rps = rows;
     } else {
-      // about four splits per query, each 4 to 10 tiles of 32 rows
-      rps = (rows + 3) / 4;
-      rps = rps < 128 ? 128 : rps > 320 ? 320 : rps;
+      // about ten splits per query, each 2 to 10 tiles of 32 rows (a block's
+      // fixed cost is small next to a tile's, and more blocks fill the chip)
+      rps = (rows + 9) / 10;
+      rps = rps < 64 ? 64 : rps > 320 ? 320 : rps;
       // tuning knob: rows of the row list one decode block handles (multiple of 32)
       const char* e = getenv("CKV_ATTN_ROWS_PER_SPLIT");
       if (e && atoi(e) >= 32) rps = atoi(e);

@@ -492,7 +492,7 @@ __device__ __forceinline__ void put_chan(uint8_t* dst, float z, int c, int dn, f
 // is one of the last nrot channels; cs / sn: tables of pair j (LDS).  Every
 // lane calls (the partner value comes from lane ^ 1).
 __device__ __forceinline__ float rope1t(float v, int c, int width, int nrot, const float* cs, const float* sn) {
-  const float o = __shfl_xor(v, 1, 64);
+  const float o = dpp_f32<0xb1>(0.f, v);   // lane ^ 1
   const int dn = width - nrot;
   if (c < dn) return v;
   const int j = (c - dn) >> 1;
@@ -608,12 +608,19 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
   }
   lds_barrier();   // red, rtab
   float sA = 0.f, sI = 0.f, mA = 0.f, mU = 0.f;
-  for (int w2 = 0; w2 < nact; ++w2) {
-    const float4 t = *(const float4*)(red + 4 * w2);
-    sA += t.x;
-    sI += t.y;
-    mA = fmaxf(mA, t.z);
-    mU = fmaxf(mU, t.w);
+  {
+    float4 t[16];   // the 16 reads go out together (red holds 16 waves' entries)
+#pragma unroll
+    for (int w2 = 0; w2 < 16; ++w2) t[w2] = *(const float4*)(red + 4 * w2);
+#pragma unroll
+    for (int w2 = 0; w2 < 16; ++w2) {
+      if (w2 < nact) {
+        sA += t[w2].x;
+        sI += t[w2].y;
+        mA = fmaxf(mA, t[w2].z);
+        mU = fmaxf(mU, t[w2].w);
+      }
+    }
   }
   if (p < 0) {
     if (tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_BAD_POS);

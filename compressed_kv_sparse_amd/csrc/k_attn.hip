@@ -340,7 +340,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     lds_barrier();
     // logits of this lane's head for its 8 rows; online softmax with one
     // head per lane: the tile max and sum reduce 8 values in the lane and
-    // across the 4 lanes of the head (xor 16, xor 32).  The reference max
+    // across the 4 lanes of the head (lanes r, r + 16, r + 32, r + 48).  The reference max
     // moves only when a tile's max exceeds it by more than 8, so probabilities
     // stay below e^8 and the rescale of the accumulators is rare.
     float Sv[2][4];
@@ -357,8 +357,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
         mx = fmaxf(mx, Sv[nt][i]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = rows4_max(mx);
     const bool move = mx > m_i + 8.f;
     const float mn = move ? mx : m_i;
     const bool none = mn == -INFINITY;
@@ -372,8 +371,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
         Sv[nt][i] = pv;
         ps += pv;
       }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps = rows4_sum(ps);
     l_i = l_i * alpha + ps;
     m_i = mn;
     if (__builtin_amdgcn_readfirstlane(__ballot(alpha != 1.f) != 0ull)) {

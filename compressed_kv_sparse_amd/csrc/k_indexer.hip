@@ -54,6 +54,9 @@ __device__ __forceinline__ IdxQuery idx_query(const LayerParams& P, const int32_
 // (Measured on the 16 x 32768-row batch: 25.7 us here; 30.8 us with one
 // wave per SIMD and three buffers; 30.8 us with four waves and no prefetch.)
 constexpr int kScoreGroups = 4;
+// The decode step's scan blocks take twice as many rows, so that they and the
+// projection blocks sharing their launch are all resident from the start.
+constexpr int kStepGroups = 8;
 constexpr int kScoreBufs = 2;
 
 // Destination of the key stores of rows at or past the cache capacity (the
@@ -64,14 +67,14 @@ __device__ uint32_t g_key_sink[64];
 // old_only: the rows of the query's cache except the row its own token
 // closes (a decode step whose compressor runs concurrently scores that row
 // separately).
-template <int MT, int KS, int QF, bool HIST>
+template <int MT, int KS, int QF, bool HIST, int NG = kScoreGroups>
 __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint16_t* idx, const void* __restrict__ qI,
                                                 const float* __restrict__ wt, const int32_t* __restrict__ pos,
                                                 int seq_fixed, int pos0, uint32_t* __restrict__ keys,
                                                 uint32_t* __restrict__ hist, int bx, int qn, bool old_only) {
   constexpr int DI = KS * 32;
   constexpr int HP = MT * 16;
-  constexpr int RB = 256 * kScoreGroups;
+  constexpr int RB = 256 * NG;
   __shared__ __attribute__((aligned(16))) uint16_t qh[HP * DI];
   __shared__ float wsh[HP];
   __shared__ float cs_[32], sn_[32];
@@ -99,7 +102,7 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
   u32x4 Bq[kScoreBufs][4][KS];
   constexpr int kAhead = kScoreBufs > 1 ? kScoreBufs - 1 : 1;   // groups issued before the prologue
 #pragma unroll
-  for (int b = 0; b < kAhead && b < kScoreGroups; ++b) load(Bq[b % kScoreBufs], b);
+  for (int b = 0; b < kAhead && b < NG; ++b) load(Bq[b % kScoreBufs], b);
   // the query: MT chunks of 8 channels per thread (chunk ci = tid + 256 e is
   // head ci / (DI/8), channels 8 (ci % (DI/8)) .. +7); heads past H_I read head
   // H_I - 1 and are zeroed below
@@ -176,9 +179,7 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
 #pragma unroll
         for (int i = 0; i < 4; ++i) s += wv[mt][i] * (relu ? fmaxf(acc[i], 0.f) : acc[i]);
       }
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
-      sc[t] = s;
+      sc[t] = rows4_sum(s);
     }
     const float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
     const int row = rb0 + 256 * gi + wave * 64 + lane;
@@ -200,21 +201,21 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
       for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(Bv[t][ks]) : : "memory");
   };
 #pragma unroll
-  for (int gi = 0; gi < kScoreGroups; ++gi) {
+  for (int gi = 0; gi < NG; ++gi) {
     if constexpr (kScoreBufs > 1) {
-      if (gi + kAhead < kScoreGroups) load(Bq[(gi + kAhead) % kScoreBufs], gi + kAhead);
+      if (gi + kAhead < NG) load(Bq[(gi + kAhead) % kScoreBufs], gi + kAhead);
     }
     pin(Bq[gi % kScoreBufs]);
     score(Bq[gi % kScoreBufs], gi);
     if constexpr (kScoreBufs == 1) {
-      if (gi + 1 < kScoreGroups) load(Bq[0], gi + 1);
+      if (gi + 1 < NG) load(Bq[0], gi + 1);
     }
   }
   if constexpr (HIST) {  // this block's key histogram into the query's
     // each thread reads back the keys it wrote (kept out of the main loop,
     // whose registers are full)
 #pragma unroll
-    for (int gi = 0; gi < kScoreGroups; ++gi) {
+    for (int gi = 0; gi < NG; ++gi) {
       const int row = rb0 + 256 * gi + wave * 64 + lane;
       const uint32_t key = kout[min(row, P.cap - 1)];
       atomicAdd(&lh[key >> 20], row < Q.V ? 1u : 0u);
@@ -387,11 +388,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
           for (int i = 0; i < 4; ++i) sv = fmaf(wv[mt][i], __int_as_float(max(__float_as_int(acc[i]), lo)), sv);
         }
-        // sum over the 4 lane groups (rows r of groups 0..3 hold other heads)
-        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sv), __float_as_uint(sv), false, false);
-        sv = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
-        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sv), __float_as_uint(sv), false, false);
-        sc[u] = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);
+        sc[u] = rows4_sum(sv);   // sum over the 4 lane groups (rows r of groups 0..3 hold other heads)
       }
       const float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
       const int row = rb + 64 * sq + 16 * g + r;
@@ -474,6 +471,10 @@ __global__ __launch_bounds__(256) void k_idx_score_vec(LayerParams P, const void
 
 // Exclusive prefix sum over the block (1024 threads); returns the thread's
 // exclusive sum, *total receives the block total.
+// NW > 0: the block has exactly NW waves (wsum 16-byte aligned); the wave
+// totals are then read with a few vector reads issued together instead of a
+// loop of dependent reads.
+template <int NW = 0>
 __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const uint32_t x = wave_incl_scan(v);
@@ -481,9 +482,20 @@ __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* wsum, uin
   if (lane == 63) wsum[wave] = x;
   lds_barrier();
   uint32_t before = 0, tot = 0;
-  for (int w = 0; w < nw; ++w) {
-    if (w < wave) before += wsum[w];
-    tot += wsum[w];
+  if constexpr (NW > 0) {
+    u32x4 q[NW / 4];
+#pragma unroll
+    for (int j = 0; j < NW / 4; ++j) q[j] = *(const u32x4*)&wsum[4 * j];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      before += w < wave ? q[w >> 2][w & 3] : 0u;
+      tot += q[w >> 2][w & 3];
+    }
+  } else {
+    for (int w = 0; w < nw; ++w) {
+      if (w < wave) before += wsum[w];
+      tot += wsum[w];
+    }
   }
   *total = tot;
   return before + x - v;
@@ -769,14 +781,14 @@ __device__ __forceinline__ void bitonic_sort_lds(uint32_t* sh, int n) {
 // (thread t: bins t*per .. t*per+per-1, values v[]), find the bin where the
 // count of keys in higher bins first reaches `need`: out[0] = bin, out[1] =
 // count in bins above it, out[2] = count in the bin.  All threads.
-template <int PER>
+template <int PER, int NW = 0>
 __device__ __forceinline__ void find_from_top(const uint32_t (&v)[PER], uint32_t need, uint32_t* wsum,
                                               uint32_t* out) {
   uint32_t local = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) local += v[i];
   uint32_t tot;
-  const uint32_t before = block_exscan(local, wsum, &tot);   // bins below this thread's
+  const uint32_t before = block_exscan<NW>(local, wsum, &tot);   // bins below this thread's
   const uint32_t above = tot - before - local;                // bins above this thread's
   if (above < need && above + local >= need) {
     uint32_t cum = above;
@@ -1087,7 +1099,8 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
   __shared__ uint32_t eqw[1024];   // rows with key == T
   __shared__ uint32_t sh[kHistBins], sh2[256];
   __shared__ uint32_t ck[kCandCap], ci[kCandCap];
-  __shared__ uint32_t wsum[16], res[4];
+  __shared__ __attribute__((aligned(16))) uint32_t wsum[16];
+  __shared__ uint32_t res[4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = P.topk;
@@ -1097,7 +1110,7 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
     res[1] = 0;
     res[2] = 0;
   }
-  find_from_top<4>(hv, (uint32_t)k, wsum, res);   // ends with a barrier
+  find_from_top<4, 16>(hv, (uint32_t)k, wsum, res);   // ends with a barrier
   const uint32_t b1 = res[0], A = res[1], nb1 = res[2];
   uint32_t T, need_eq;
   if (nb1 <= (uint32_t)kCandCap) {
@@ -1110,7 +1123,7 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
     for (int i = 0; i < kHistBins / 1024; ++i) sh[tid + 1024 * i] = 0u;
     if (tid < 256) sh2[tid] = 0u;
     uint32_t ctot;
-    uint32_t at = block_exscan(cnt, wsum, &ctot);
+    uint32_t at = block_exscan<16>(cnt, wsum, &ctot);
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
       if (e < nv && (kr[e] >> 20) == b1) {
@@ -1134,7 +1147,7 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
     uint32_t v[4];
 #pragma unroll
     for (int i2 = 0; i2 < 4; ++i2) v[i2] = sh[4 * tid + i2];
-    find_from_top<4>(v, need, wsum, res);
+    find_from_top<4, 16>(v, need, wsum, res);
     const uint32_t prefix = (b1 << 20) | (res[0] << 8);
     need -= res[1];
     lds_barrier();   // every thread has read res
@@ -1148,7 +1161,7 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
     lds_barrier();
 #pragma unroll
     for (int i2 = 0; i2 < 4; ++i2) v[i2] = 4 * tid + i2 < 256 ? sh2[4 * tid + i2] : 0u;
-    find_from_top<4>(v, need, wsum, res);
+    find_from_top<4, 16>(v, need, wsum, res);
     T = prefix | res[0];
     need_eq = need - res[1];
   } else {
@@ -1187,7 +1200,7 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
   {
     const uint32_t g = gtw[tid], q = eqw[tid];
     uint32_t tot;
-    const uint32_t before = block_exscan(((uint32_t)__popc(g) << 16) | (uint32_t)__popc(q), wsum, &tot);
+    const uint32_t before = block_exscan<16>(((uint32_t)__popc(g) << 16) | (uint32_t)__popc(q), wsum, &tot);
     const uint32_t gt_before = before >> 16, eq_before = before & 0xffffu;
     uint32_t keep = 0u, bits = q, r = eq_before;
     while (bits && r < need_eq) {
@@ -1252,7 +1265,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return;
   }
   const int i = bid - nproj;
-  idx_score_block<MT, 4, QF, true>(P, idx, qI, wt, pos, 0, 0, keys, hist, i % nrb, i / nrb, true);
+  idx_score_block<MT, 4, QF, true, kStepGroups>(P, idx, qI, wt, pos, 0, 0, keys, hist, i % nrb, i / nrb, true);
 }
 
 // k_step_select: one block of 1024 threads per sequence.  The indexer query
@@ -1272,7 +1285,7 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
   constexpr int DI = 128, CPT = DI / 16;
   __shared__ __attribute__((aligned(16))) float red[64];
   __shared__ float idx_row[kMaxDI];
-  __shared__ float hsum[64];
+  __shared__ __attribute__((aligned(16))) float hsum[64];
   __shared__ float rtab[128];
   __shared__ __attribute__((aligned(16))) uint32_t h_lds[kHistBins];
   __shared__ __attribute__((aligned(16))) uint32_t q_lds[64 * DI / 2];
@@ -1328,13 +1341,16 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
       b2 = bf16_to_f32(f32_to_bf16(b2));
       dot += a * idx_row[c] + b2 * idx_row[c + 1];
     }
-#pragma unroll
-    for (int o2 = 1; o2 < 16; o2 <<= 1) dot += __shfl_xor(dot, o2, 64);
+    dot = row16_sum(dot);
     const bool relu = !(P.flags & CKV_FLAG_IDX_NO_RELU);
     if ((tid & 15) == 0) hsum[hh] = hh < HI ? wv * (relu ? fmaxf(dot, 0.f) : dot) : 0.f;
     lds_barrier();
-    float sc = 0.f;
-    for (int h = 0; h < HI; ++h) sc += hsum[h];
+    float sc = 0.f;   // heads past H_I hold 0
+#pragma unroll
+    for (int h4 = 0; h4 < 64; h4 += 4) {
+      const float4 q = *(const float4*)&hsum[h4];
+      sc += (q.x + q.y) + (q.z + q.w);
+    }
     const uint32_t key = float_key(sc);
     const int x = V - 1;   // row t + 1024 e is key e of thread t
 #pragma unroll
@@ -1383,7 +1399,7 @@ int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache&
   hipStream_t st = (hipStream_t)stream;
   const WCat wc = make_wcat(P, w);
   const int nproj = (P.ncol / 16) * ((B + 15) / 16);
-  constexpr int RB = 256 * kScoreGroups;
+  constexpr int RB = 256 * kStepGroups;
   const int nrb = (P.cap + RB - 1) / RB;
   const int MT = (P.HI + 15) / 16;
   dim3 grid(nproj + nrb * B);
