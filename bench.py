@@ -153,7 +153,13 @@ def prefill_flops(cfg, pos0, T):
 
 # --------------------------------------------------------------------------- decode
 
-def bench_decode(cfg, steps, warmup, with_kernel=True, api="step"):
+def bench_decode(cfg, steps, warmup, with_kernel=True, api="step", copies=3):
+    """Decode steps of one layer.  ``copies`` independent instances of the layer
+    (each with its own caches, all drawn from the same seed) take the steps in
+    turn, so that the caches one step reads were last touched ``copies`` steps
+    earlier: with three copies of the 128k-context layer (about 1.2 GB) nothing
+    a step reads is still in the 256 MB last-level cache from the previous one,
+    and every cache byte comes from HBM, as it does in a deep layer stack."""
     import torch
     from workloads import make_decode_inputs, make_layer_weights
     from workloads.gen import context_lengths
@@ -164,63 +170,74 @@ def bench_decode(cfg, steps, warmup, with_kernel=True, api="step"):
     wts = make_layer_weights(cfg)
     n = context_lengths(cfg)
     log(f"[bench] {cfg.name}: inputs drawn in {time.time() - t0:.1f}s")
-    dl = make_layer(cfg, wts, inp.cache)
+    layers = [make_layer(cfg, wts, inp.cache) for _ in range(max(1, copies))]
     x, u, q, pos = dev(inp.x), dev(inp.u), dev(inp.q), dev(inp.pos)
     qI = dev(inp.qI) if inp.qI is not None else None
     w = dev(inp.w) if inp.w is not None else None
     B = cfg.batch
-    out = dl.new_out(B)
+    out = layers[0].new_out(B)
     topk = torch.empty((B, cfg.top_k), dtype=torch.int32, device="cuda") if cfg.ratio == 4 else None
 
-    def step():
+    def step(dl):
         if api == "step":
             dl.decode_step(x, u, q, qI, w, pos, out=out, topk=topk)
         else:
             dl.decode(x, u, q, qI, w, pos, out=out, topk=topk)
 
-    step()
+    step(layers[0])
     torch.cuda.synchronize()
-    assert int(dl.status.abs().sum()) == 0, "device status set"
+    assert int(layers[0].status.abs().sum()) == 0, "device status set"
     ref_out = out.clone()
     ref_tk = topk.clone() if topk is not None else None
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        step()
+        for dl in layers:
+            step(dl)
     torch.cuda.current_stream().wait_stream(s)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    for _ in range(3):          # replays interleaved with eager checks
-        out.zero_()
-        g.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "graph replay differs"
-        if ref_tk is not None:
-            assert torch.equal(topk, ref_tk), "graph replay top-k differs"
-    for _ in range(warmup):
-        g.replay()
+    graphs = []
+    for dl in layers:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(dl)
+        graphs.append(g)
+    for _ in range(3):          # replays interleaved with eager checks; every copy gives the same result
+        for g in graphs:
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "graph replay differs"
+            if ref_tk is not None:
+                assert torch.equal(topk, ref_tk), "graph replay top-k differs"
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        g.replay()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
-    res = {"ms_per_step": dt * 1e3, "tok_s": B / dt, "step_bytes": decode_step_bytes(cfg, n)}
+    res = {"ms_per_step": dt * 1e3, "tok_s": B / dt, "step_bytes": decode_step_bytes(cfg, n),
+           "layer_copies": len(layers)}
     res["step_gbs"] = res["step_bytes"] / dt / 1e9
     res["step_hbm_frac"] = res["step_gbs"] / HBM_PEAK_GBS
 
     if with_kernel and cfg.ratio == 4:
-        # the dominant kernel on its own: indexer score scan, events around each launch
+        # the dominant kernel on its own: indexer score scan, the copies taking
+        # the launches in turn as above; each launch stamps a pair of HIP
+        # events at the kernel's own start and end (hipExtLaunchKernel), on
+        # the stream it runs on
         keys = torch.empty((B, cfg.comp_cap), dtype=torch.int32, device="cuda")
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:        # torch creates an event at its first record
+            a.record()
+            b.record()
         stream = torch.cuda.current_stream().cuda_stream
         for i in range(warmup + steps):
+            dl = layers[i % len(layers)]
             if i >= warmup:
-                evs[i - warmup][0].record()
+                L.time_next_score(*evs[i - warmup])
             rc = L.indexer_score_decode(dl.desc, dl.cache, qI, w, pos, B, keys, stream)
-            if i >= warmup:
-                evs[i - warmup][1].record()
             if rc:
                 raise L.CkvError(rc, "indexer_score_decode")
         torch.cuda.synchronize()
@@ -380,6 +397,9 @@ def main():
                     help="time one part alone and print its own JSON line (for kernel profiles)")
     ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--extra", action="store_true", help="also time the other decode workloads")
+    ap.add_argument("--layer-copies", type=int, default=3,
+                    help="independent layer instances taking the decode steps in turn (1: one layer re-read every "
+                         "step, partly from the last-level cache)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 3 elementwise copies (neg) of MIB MiB: a known-size reference for HBM counters")
     args = ap.parse_args()
@@ -412,7 +432,7 @@ def main():
         print(json.dumps({"part": "stack", **bench_stack(args.stack_steps, 3)}), flush=True)
         return
     cfg = get_config(args.workload)
-    r = bench_decode(cfg, args.steps, args.warmup, api=args.api)
+    r = bench_decode(cfg, args.steps, args.warmup, api=args.api, copies=args.layer_copies)
     log(f"[bench] decode {cfg.name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['tok_s']:.0f} tok/s, "
         f"step {r['step_gbs']:.0f} GB/s ({100 * r['step_hbm_frac']:.1f}% of HBM)")
     kern = r.get("kernel")
@@ -426,7 +446,7 @@ def main():
     extra = {}
     if args.extra:
         for name in ("c2", "c3", "c5_c128a", "c5_swa"):
-            e = bench_decode(get_config(name), args.steps, args.warmup, with_kernel=False)
+            e = bench_decode(get_config(name), args.steps, args.warmup, with_kernel=False, copies=args.layer_copies)
             extra[name] = {k: round(v, 4) for k, v in e.items() if not k.startswith("_") and isinstance(v, float)}
             log(f"[bench] decode {name}: {e['ms_per_step'] * 1e3:.1f} us/step, {e['tok_s']:.0f} tok/s, "
                 f"{100 * e['step_hbm_frac']:.1f}% HBM")
@@ -455,7 +475,8 @@ def main():
         "data": "synthetic (seeded draws of the workload's shapes)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "context": cfg.n_ctx, "head_dim": cfg.head_dim,
                    "heads": cfg.n_heads, "indexer": f"{cfg.idx_heads}x{cfg.idx_dim}", "top_k": cfg.top_k,
-                   "kv_cache": cfg.kv_fmt, "indexer_cache": cfg.idx_fmt, "parallelism": "1 GPU"},
+                   "kv_cache": cfg.kv_fmt, "indexer_cache": cfg.idx_fmt, "layer_copies": r["layer_copies"],
+                   "parallelism": "1 GPU"},
         "step_hbm": {"bytes": int(r["step_bytes"]), "achieved": round(r["step_gbs"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(r["step_hbm_frac"], 4)},
         "roofline": roof,

@@ -83,6 +83,8 @@ def _load() -> ctypes.CDLL:
     lib.ckv_strerror.restype = ctypes.c_char_p
     lib.ckv_last_hip_error.argtypes = []
     lib.ckv_last_hip_error.restype = ctypes.c_char_p
+    lib.ckv_time_next_score.argtypes = [VP, VP]
+    lib.ckv_time_next_score.restype = I32
     lib.ckv_workspace_bytes.argtypes = [D, I32, I32]
     lib.ckv_workspace_bytes.restype = SZ
     lib.ckv_workspace_sync_bytes.argtypes = [D, I32, I32]
@@ -110,7 +112,7 @@ EXPORTS = ("ckv_row_bytes", "ckv_validate", "ckv_strerror", "ckv_last_hip_error"
            "ckv_workspace_sync_bytes",
            "ckv_compress_append_decode", "ckv_compress_append_prefill", "ckv_indexer_topk_decode",
            "ckv_indexer_topk_prefill", "ckv_indexer_score_decode", "ckv_sparse_swa_attn_decode",
-           "ckv_sparse_swa_attn_prefill", "ckv_decode_step")
+           "ckv_sparse_swa_attn_prefill", "ckv_decode_step", "ckv_time_next_score")
 
 
 def strerror(code: int) -> str:
@@ -159,6 +161,17 @@ def compress_append_prefill(desc, weights, cache, x, u, seq, pos0, T, ws, ws_byt
 def indexer_topk_decode(desc, cache, qI, w, pos, B, topk, ws, ws_bytes, stream=None) -> int:
     return lib.ckv_indexer_topk_decode(_ref(desc), _ref(cache), _p(qI), _p(w), _p(pos), int(B), _p(topk),
                                        _p(ws), int(ws_bytes), stream)
+
+
+def time_next_score(start_event, stop_event) -> int:
+    """Arm this thread's next indexer score launch to stamp two timing events
+    (torch.cuda.Event objects, already recorded once so that they exist, or
+    raw hipEvent_t handles; None disarms)."""
+    def h(e):
+        if e is None:
+            return None
+        return int(getattr(e, "cuda_event", e))
+    return lib.ckv_time_next_score(h(start_event), h(stop_event))
 
 
 def indexer_score_decode(desc, cache, qI, w, pos, B, keys, stream=None) -> int:

@@ -277,6 +277,11 @@ extern "C" int ckv_decode_step(const ckv_layer_desc* desc, const ckv_layer_weigh
   return launched(launch_attn(P, C, q, pos, 0, 0, B, topk, out, L, wb, stream));
 }
 
+extern "C" int ckv_time_next_score(void* start_event, void* stop_event) {
+  arm_score_timing(start_event, stop_event);
+  return CKV_OK;
+}
+
 extern "C" const char* ckv_last_hip_error(void) {
   return t_last_hip ? hipGetErrorName((hipError_t)t_last_hip) : "none";
 }

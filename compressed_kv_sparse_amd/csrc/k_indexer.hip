@@ -13,10 +13,32 @@
 // piling into a few; when fewer than k keys fall in that range it widens the
 // range and counts again.  Every row above the k-th key is emitted, plus the
 // lowest-index rows equal to it, in ascending index order.
+#include <hip/hip_ext.h>
+
 #include "compress_dec.h"
 #include "proj_dec.h"
 
 namespace ckv {
+
+// Score-kernel timing: when armed, the next score launch of this thread goes
+// through hipExtLaunchKernel, which stamps the two events at the kernel's own
+// start and end (no launch gaps in between), then disarms.
+static thread_local hipEvent_t t_score_ev[2] = {nullptr, nullptr};
+
+void arm_score_timing(void* start_event, void* stop_event) {
+  t_score_ev[0] = (hipEvent_t)start_event;
+  t_score_ev[1] = (hipEvent_t)stop_event;
+}
+
+template <typename F, typename... Args>
+static void launch_score(F kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+  if (t_score_ev[0] || t_score_ev[1]) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, t_score_ev[0], t_score_ev[1], 0, args...);
+    t_score_ev[0] = t_score_ev[1] = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  }
+}
 
 struct IdxQuery {
   int seq, p, V;
@@ -649,13 +671,13 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* wsum) {
   return t;
 }
 
-// Keys of one query held in registers: wave w owns indices [2048 w, 2048 w +
-// 2048), step j of lane l holding index 2048 w + 64 j + l.  V <= 32768.  One
-// block of 1024 threads per query.
+// Keys of one query held in registers: wave w owns indices [64 KPT w,
+// 64 KPT (w + 1)), step j of lane l holding index 64 KPT w + 64 j + l.
+// V <= 1024 KPT.  One block of 1024 threads per query.
+template <int KPT>
 __global__ __launch_bounds__(1024) void k_topk_select_reg(LayerParams P, const uint32_t* __restrict__ keys,
                                                           const int32_t* __restrict__ pos, int pos0,
                                                           int32_t* __restrict__ out) {
-  constexpr int KPT = 32;
   __shared__ uint32_t sh[1024];
   __shared__ uint32_t wsum[16], wgt[16], weq[16];
   __shared__ uint32_t bc[2];
@@ -1380,8 +1402,10 @@ int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const f
     dim3 grid((unsigned)((vmax + kSelChunk - 1) / kSelChunk), nq);
     hipLaunchKernelGGL(k_topk_classify, grid, dim3(256), 0, st, P, keys, *sel, pos);
     hipLaunchKernelGGL(k_topk_finish, dim3(nq), dim3(256), 0, st, P, keys, *sel, pos, topk);
-  } else if (vmax <= 32768)
-    hipLaunchKernelGGL(k_topk_select_reg, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);
+  } else if (vmax <= 16384)
+    hipLaunchKernelGGL(k_topk_select_reg<16>, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);
+  else if (vmax <= 32768)
+    hipLaunchKernelGGL(k_topk_select_reg<32>, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);
   else
     hipLaunchKernelGGL(k_topk_select, dim3(nq), dim3(1024), 0, st, P, keys, pos, pos0, topk);
   return (int)hipGetLastError();
@@ -1438,9 +1462,8 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
     const int MT = (P.HI + 15) / 16;
     constexpr int RUN = kPfRows * kPfTiles;
     dim3 pgrid((unsigned)(vmax > 0 ? (vmax + RUN - 1) / RUN : 1), (unsigned)((nq + kPfQ - 1) / kPfQ));
-#define CKV_PF(MTV)                                                                                            \
-  hipLaunchKernelGGL((k_idx_score_prefill<MTV>), pgrid, dim3(512), 0, st, P, ix, (const uint16_t*)qI, w, seq, pos0, \
-                     nq, keys)
+#define CKV_PF(MTV) \
+  launch_score(k_idx_score_prefill<MTV>, pgrid, dim3(512), st, P, ix, (const uint16_t*)qI, w, seq, pos0, nq, keys)
     if (MT == 1) CKV_PF(1);
     else if (MT == 2) CKV_PF(2);
     else if (MT == 3) CKV_PF(3);
@@ -1451,13 +1474,13 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
     const int MT = (P.HI + 15) / 16;
     constexpr int RB = 256 * kScoreGroups;
     dim3 mgrid((unsigned)(vmax > 0 ? (vmax + RB - 1) / RB : 1), nq);
-#define CKV_IS(MTV, QF)                                                                           \
-  if (hist)                                                                                       \
-    hipLaunchKernelGGL((k_idx_score_mfma<MTV, 4, QF, true>), mgrid, dim3(256), 0, st, P, ix, qI, w, pos, \
-                       seq, pos0, keys, hist);                                                          \
-  else                                                                                            \
-    hipLaunchKernelGGL((k_idx_score_mfma<MTV, 4, QF, false>), mgrid, dim3(256), 0, st, P, ix, qI, w, pos, \
-                       seq, pos0, keys, hist)
+#define CKV_IS(MTV, QF)                                                                                     \
+  if (hist)                                                                                                 \
+    launch_score(k_idx_score_mfma<MTV, 4, QF, true>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, keys, \
+                 hist);                                                                                     \
+  else                                                                                                      \
+    launch_score(k_idx_score_mfma<MTV, 4, QF, false>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, keys, \
+                 hist)
     if (P.act_fmt == CKV_BF16) {
       if (MT == 1) CKV_IS(1, CKV_BF16);
       else if (MT == 2) CKV_IS(2, CKV_BF16);
@@ -1472,8 +1495,7 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
 #undef CKV_IS
   } else {
 #define CKV_IV(IF, QF) \
-  hipLaunchKernelGGL((k_idx_score_vec<IF, QF>), grid, dim3(256), 0, st, P, c.idx, qI, w, pos, seq, pos0, keys, \
-                     hist)
+  launch_score(k_idx_score_vec<IF, QF>, grid, dim3(256), st, P, c.idx, qI, w, pos, seq, pos0, keys, hist)
     if (P.idx_fmt == CKV_F32 && P.act_fmt == CKV_F32) CKV_IV(CKV_F32, CKV_F32);
     else if (P.idx_fmt == CKV_F32) CKV_IV(CKV_F32, CKV_BF16);
     else if (P.act_fmt == CKV_F32) CKV_IV(CKV_BF16, CKV_F32);

@@ -185,6 +185,18 @@ const char* ckv_strerror(int code);
  * ("none" if there was none).  Static string. */
 const char* ckv_last_hip_error(void);
 
+/* Kernel timing for profiling callers.  start_event / stop_event: hipEvent_t
+ * handles created by the caller (timing enabled), or NULL.  Arms the calling
+ * thread's next launch of an indexer score kernel (made by
+ * ckv_indexer_score_decode, ckv_indexer_topk_decode or
+ * ckv_indexer_topk_prefill; the fused scan launch of ckv_decode_step is not
+ * one) to stamp start_event when the kernel starts and stop_event when it
+ * ends, so
+ * that hipEventElapsedTime gives the kernel's own duration, without the
+ * launch gaps around it.  The events stay owned by the caller; the arming is
+ * consumed by that one launch; two NULLs disarm.  Returns CKV_OK. */
+int ckv_time_next_score(void* start_event, void* stop_event);
+
 /* Workspace bytes a call of `mode` with n = B (decode) or T (prefill) tokens
  * needs; the same figure serves all entry points of that mode.
  * 0 when desc is invalid.

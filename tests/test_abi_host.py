@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -153,3 +153,9 @@ def test_stack_schedule_matches_the_oracle():
         assert layer_ratio(il, "pro") == O.pro_ratio(il)
     with pytest.raises(ValueError):
         layer_ratio(0, "other")
+
+
+def test_score_timing_arms_and_disarms_without_a_device():
+    # arming only records two handles for the calling thread; no GPU call
+    assert L.time_next_score(None, None) == 0
+    assert L.lib.ckv_time_next_score(None, None) == 0
