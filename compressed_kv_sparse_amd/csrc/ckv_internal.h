@@ -110,6 +110,8 @@ int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const f
 int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const float* w,
                      const int32_t* pos, int seq, int pos0, int nq, uint32_t* keys, uint32_t* hist,
                      void* stream);
+// K slices of the decode projection (partial sums added by the compressor)
+constexpr int kProjSlices = 1;
 // events that bracket the calling thread's next launch of an indexer score
 // kernel (start, stop; either may be NULL), consumed by that launch
 void arm_score_timing(void* start_event, void* stop_event);

@@ -62,10 +62,9 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   memset(&L, 0, sizeof(L));
   const bool prefill = mode == CKV_MODE_PREFILL;
   const bool proj_mfma = P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16;
-  // the decode projection reduces its K range inside each block and writes
-  // final sums (one slice); the compressor still accepts up to 4 K slices
-  (void)proj_mfma;
-  L.proj_splits = 1;
+  // the decode projection splits K over kProjSlices blocks per tile (partial
+  // sums, added by the compressor in slice order)
+  L.proj_splits = (!prefill && proj_mfma) ? kProjSlices : 1;
   const int rows = attn_max_rows(P);
   int rps;
   if (attn_uses_tiles(P)) {

@@ -543,8 +543,8 @@ __device__ __forceinline__ float pool_c4a(const float (&rk)[8], const float (&rs
 template <int KVF, int IDXF, int ACTF, typename Issue>
 __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weights& w, const Cache& cc,
                                                 const void* __restrict__ u, const int32_t* __restrict__ pos,
-                                                const float* __restrict__ proj, int B, int b, float* red,
-                                                float* rtab, float* idx_row, Issue&& issue) {
+                                                const float* __restrict__ proj, int splits, int B, int b,
+                                                float* red, float* rtab, float* idx_row, Issue&& issue) {
   const int d = P.d, DI = P.DI;
   const int dn = d - P.n_rot;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -558,11 +558,18 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
   const float* ape = (roleA ? w.ape : w.idx_ape) + col;
   const float* pj = proj + (size_t)b * P.ncol;
 
-  // one round of loads: this token's projections and raw input, the ring,
-  // the APE rows and the RMSNorm gain
+  // one round of loads: this token's projections (the sum of up to 4 K-slice
+  // partials, in slice order; slices past `splits` re-read the last and
+  // count zero) and raw input, the ring, the APE rows and the RMSNorm gain
   const int p = pos[b];
-  const float ka = pj[roleA ? col : 2 * d + col];
-  const float sa = pj[roleA ? d + col : 2 * d + DI + col];
+  float ka = 0.f, sa = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float* pq = pj + (size_t)min(q, splits - 1) * B * P.ncol;
+    const float kq = pq[roleA ? col : 2 * d + col], sq = pq[roleA ? d + col : 2 * d + DI + col];
+    ka += q < splits ? kq : 0.f;
+    sa += q < splits ? sq : 0.f;
+  }
   const float uu = load_val<ACTF>(u, (long)b * d + (roleA ? col : 0));
   float rk[8], rs[8], ap[8];
 #pragma unroll

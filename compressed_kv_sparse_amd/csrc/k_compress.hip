@@ -28,14 +28,14 @@ __global__ __launch_bounds__(256 * TPC) void k_compress_decode(LayerParams P, We
 }
 
 // c4a: the role-split body, one block of d + D_I threads (rounded up
-// to whole waves) per sequence; one projection slice.
+// to whole waves) per sequence; up to 4 projection slices.
 template <int KVF, int IDXF, int ACTF>
 __global__ __launch_bounds__(1024) void k_compress_c4a(LayerParams P, Weights w, Cache cc, const void* __restrict__ u,
                                                        const int32_t* __restrict__ pos,
-                                                       const float* __restrict__ proj, int B) {
+                                                       const float* __restrict__ proj, int splits, int B) {
   __shared__ __attribute__((aligned(16))) float red[64];
   __shared__ float rtab[128];
-  compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, B, blockIdx.x, red, rtab, nullptr, [] {});
+  compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, splits, B, blockIdx.x, red, rtab, nullptr, [] {});
 }
 
 // Ratio 0: only the raw sliding-window row.
@@ -189,9 +189,9 @@ template <int KVF, int IDXF, int ACTF>
 static void go_decode(const LayerParams& P, const Weights& w, const Cache& c, const void* u,
                       const int32_t* pos, int B, const float* part, int splits, hipStream_t st) {
   const int np = P.d / 2;
-  if (P.ratio == 4 && splits == 1)
+  if (P.ratio == 4 && splits <= 4)
     hipLaunchKernelGGL((k_compress_c4a<KVF, IDXF, ACTF>), dim3(B), dim3((P.d + P.DI + 63) / 64 * 64), 0, st, P, w,
-                       c, u, pos, part, B);
+                       c, u, pos, part, splits, B);
   else if (P.ratio == 4)
     hipLaunchKernelGGL((k_compress_decode<KVF, IDXF, ACTF, 8, 1>), dim3(B), dim3(np), 0, st, P, w, c, u, pos,
                        part, splits, B);

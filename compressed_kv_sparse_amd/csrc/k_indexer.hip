@@ -76,9 +76,13 @@ __device__ __forceinline__ IdxQuery idx_query(const LayerParams& P, const int32_
 // (Measured on the 16 x 32768-row batch: 25.7 us here; 30.8 us with one
 // wave per SIMD and three buffers; 30.8 us with four waves and no prefetch.)
 constexpr int kScoreGroups = 4;
-// The decode step's scan blocks take twice as many rows, so that they and the
-// projection blocks sharing their launch are all resident from the start.
-constexpr int kStepGroups = 8;
+// The decode step's launch: scan blocks as above, then the projection
+// blocks, which take the compute-unit slots the scan's first blocks free
+// (placed first, they held slots the scan needed to start with), each wave
+// keeping 16 of its k-steps' loads in flight.
+constexpr int kStepGroups = 4;
+constexpr bool kStepProjLast = true;
+constexpr int kStepProjSF = 16;
 constexpr int kScoreBufs = 2;
 
 // Destination of the key stores of rows at or past the cache capacity (the
@@ -207,7 +211,9 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
     const int row = rb0 + 256 * gi + wave * 64 + lane;
     // branch-free: keys of rows in [V, cap) are written but never read; rows
     // past the capacity go to the sink; only rows below V enter the histogram
-    *(row < P.cap ? kout + row : g_key_sink + lane) = float_key(mine);
+    const uint32_t key = float_key(mine);
+    *(row < P.cap ? kout + row : g_key_sink + lane) = key;
+    if constexpr (HIST) atomicAdd(&lh[key >> 20], row < Q.V ? 1u : 0u);
   };
   // An empty asm that takes the buffer about to be multiplied as in/out
   // operands and clobbers memory: the loads issued before it cannot sink
@@ -233,16 +239,8 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
       if (gi + 1 < NG) load(Bq[0], gi + 1);
     }
   }
-  if constexpr (HIST) {  // this block's key histogram into the query's
-    // each thread reads back the keys it wrote (kept out of the main loop,
-    // whose registers are full)
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      const int row = rb0 + 256 * gi + wave * 64 + lane;
-      const uint32_t key = kout[min(row, P.cap - 1)];
-      atomicAdd(&lh[key >> 20], row < Q.V ? 1u : 0u);
-    }
-    __syncthreads();
+  if constexpr (HIST) {  // this block's key histogram (LDS, filled above) into the query's
+    lds_barrier();
     uint32_t* gh = hist + (size_t)qn * kHistBins;
     for (int e = tid; e < kHistBins; e += 256) {
       const uint32_t v = lh[e];
@@ -1272,21 +1270,26 @@ __global__ __launch_bounds__(1024) void k_topk_decode(LayerParams P, const uint3
 // (the rows the scan reads do not depend on it), and one block per sequence
 // then runs the compressor, scores the row its token closed and selects.
 //
-// k_step_scan: blocks [0, nproj) compute the projection tiles (16 columns x
-// 16 rows each, 4 waves over K); the others score the query's cache rows
-// except the row its own token closes, building the key histogram.
+// k_step_scan: the last nproj blocks compute the projection tiles (16
+// columns x 16 rows each, 4 waves over one of kProjSlices K slices); the
+// others score the query's cache rows except the row its own token closes,
+// building the key histogram.
 template <int MT, int QF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_step_scan(
     LayerParams P, const uint16_t* idx, const void* __restrict__ qI, const float* __restrict__ wt,
     const int32_t* __restrict__ pos, uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
     const uint16_t* __restrict__ X, int M, WCat wc, float* __restrict__ proj, int nproj, int nrb) {
+  const int nscan = (int)gridDim.x - nproj;
   const int bid = blockIdx.x;
-  if (bid < nproj) {
+  if (kStepProjLast ? bid >= nscan : bid < nproj) {
+    const int t = kStepProjLast ? bid - nscan : bid;
+    const int ntile = nproj / kProjSlices, tile = t % ntile;
     const int ncb = P.ncol / 16;
-    proj_tile<4>(X, M, P.hidden, wc, P.ncol, proj, 16 * (bid % ncb), 16 * (bid / ncb));
+    proj_tile<4, kStepProjSF>(X, M, P.hidden, wc, P.ncol, proj, 16 * (tile % ncb), 16 * (tile / ncb), t / ntile,
+                              kProjSlices);
     return;
   }
-  const int i = bid - nproj;
+  const int i = kStepProjLast ? bid : bid - nproj;
   idx_score_block<MT, 4, QF, true, kStepGroups>(P, idx, qI, wt, pos, 0, 0, keys, hist, i % nrb, i / nrb, true);
 }
 
@@ -1330,7 +1333,7 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
   // (the query and the histogram, the first loads issued, are parked in LDS
   // once the keys are on their way: registers are short while the compressor
   // holds its window)
-  const int st = compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, B, qn, red, rtab, idx_row, [&] {
+  const int st = compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, kProjSlices, B, qn, red, rtab, idx_row, [&] {
     sel_load_keys(keys + (size_t)qn * P.cap, P.cap, tid, kr);
     *(u32x4*)(h_lds + 4 * tid) = h4;
     *(u32x4*)(q_lds + 4 * tid) = q4;
@@ -1422,7 +1425,7 @@ int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache&
                             float* proj, uint32_t* keys, const SelWs& sel, int32_t* topk, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const WCat wc = make_wcat(P, w);
-  const int nproj = (P.ncol / 16) * ((B + 15) / 16);
+  const int nproj = (P.ncol / 16) * ((B + 15) / 16) * kProjSlices;
   constexpr int RB = 256 * kStepGroups;
   const int nrb = (P.cap + RB - 1) / RB;
   const int MT = (P.HI + 15) / 16;

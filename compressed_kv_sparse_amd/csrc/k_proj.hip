@@ -72,9 +72,10 @@ __global__ __launch_bounds__(256) void k_proj_mfma(const uint16_t* __restrict__ 
 // Splitting K over blocks puts the weight stream on more compute units (a
 // unit keeps only a limited number of misses in flight).  grid: x = ncol / 16,
 // y = ceil(M / 16), z = K slices; writes part[slice][m][col].
+constexpr int kProjDecWaves = 16;
 __global__ __launch_bounds__(1024) void k_proj_dec(const uint16_t* __restrict__ X, int M, int K, WCat wc, int ncol,
                                                    float* __restrict__ part) {
-  proj_tile<16>(X, M, K, wc, ncol, part, blockIdx.x * 16, blockIdx.y * 16);
+  proj_tile<kProjDecWaves>(X, M, K, wc, ncol, part, blockIdx.x * 16, blockIdx.y * 16, blockIdx.z, gridDim.z);
 }
 
 // Chunk projection (M >= 128 rows): a tiled GEMM.  A block computes a 128 x 128
@@ -188,8 +189,9 @@ int launch_proj(const LayerParams& P, const Weights& w, const void* x, int M, fl
   const WCat wc = make_wcat(P, w);
   const int K = P.hidden;
   if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && M <= 64) {
-    dim3 grid(P.ncol / 16, (M + 15) / 16);
-    hipLaunchKernelGGL(k_proj_dec, grid, dim3(1024), 0, st, (const uint16_t*)x, M, K, wc, P.ncol, part);
+    dim3 grid(P.ncol / 16, (M + 15) / 16, splits);
+    hipLaunchKernelGGL(k_proj_dec, grid, dim3(64 * kProjDecWaves), 0, st, (const uint16_t*)x, M, K, wc, P.ncol,
+                       part);
   } else if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && splits == 1 && M >= kGM && P.d % kGN == 0 &&
              (P.ratio != 4 || P.DI % kGN == 0) && K % kGK == 0) {
     dim3 grid(P.ncol / kGN, (M + kGM - 1) / kGM);

@@ -41,18 +41,23 @@ inline WCat make_wcat(const LayerParams& P, const Weights& w) {
 // the NW waves of the block taking the k-steps w, w + NW, ... (SF of them in
 // flight per round, loads unconditional with the step clamped); partial
 // tiles summed through LDS in wave order.  Writes part[m][col].
+// K slice `slice` of `nslice` (k-steps of 32, split evenly) when nslice > 1;
+// the result goes to part + slice * M * ncol.
 template <int NW, int SF = 8>
 __device__ __forceinline__ void proj_tile(const uint16_t* __restrict__ X, int M, int K, const WCat& wc, int ncol,
-                                          float* __restrict__ part, int col0, int m0) {
+                                          float* __restrict__ part, int col0, int m0, int slice = 0,
+                                          int nslice = 1) {
   __shared__ f32x4 red[NW][64];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   int local;
   const uint16_t* wrow = (const uint16_t*)wcat_row(wc, col0 + r, K, 2, &local);
   const uint16_t* xrow = X + (size_t)min(m0 + r, M - 1) * K;
-  const int nsteps = K / 32;
+  const int ktot = K / 32, per = (ktot + nslice - 1) / nslice;
+  const int sbeg = slice * per, nsteps = min(ktot, sbeg + per);
+  part += (size_t)slice * M * ncol;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = wave; s0 < nsteps; s0 += NW * SF) {
+  for (int s0 = sbeg + wave; s0 < nsteps; s0 += NW * SF) {
     u32x4 a[SF], b[SF];
 #pragma unroll
     for (int e = 0; e < SF; ++e) {
