@@ -108,7 +108,14 @@ __device__ __forceinline__ int topk_end(const int32_t* tk, int k, int V, int* sm
 namespace attn {
 constexpr int D = 512, DN = 448, R = 32;
 constexpr int NT = 512;     // threads per block
-constexpr int KP = D + 8;   // row-major row stride (16-bit elements)
+constexpr int KP = D + 16;  // row-major row stride (16-bit elements)
+// Element e of tile row R: row stride 528 elements (1056 bytes, 8 banks of
+// shift per row), and the 16-byte chunk e / 8 XORed with bit 2 of R.  The
+// transposed PV reads (4 rows x 32 bytes per 16 lanes) then hit 32 distinct
+// banks, and so do the 16-byte logit reads (8 lanes = rows r .. r + 7 of
+// one chunk; rows r and r + 4, 32 banks apart by the stride, differ by the
+// XOR).
+__device__ __forceinline__ int tix(int R, int e) { return R * KP + ((((e >> 3) ^ (R >> 2)) & 1) | (e >> 3 & ~1)) * 8 + (e & 7); }
 constexpr int MAXK = 4096;
 constexpr int MAXL = 128 + MAXK + 4 * R;   // row-list entries of one split (+ padding tiles)
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -264,12 +271,12 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       if (it < R * CPR) {
         const u32x4 v = S.ok[e] ? S.v[e] : (u32x4){0u, 0u, 0u, 0u};
         if (!F8) {
-          *(u32x4*)&kb[row * KP + 8 * ch] = bf16x8_to_f16(v);
+          *(u32x4*)&kb[tix(row, 8 * ch)] = bf16x8_to_f16(v);
         } else if (ch < 28) {   // 16 codes -> 16 fp16 channels
-          *(u32x4*)&kb[row * KP + 16 * ch] = e4m3x8_to_f16(v[0], v[1]);
-          *(u32x4*)&kb[row * KP + 16 * ch + 8] = e4m3x8_to_f16(v[2], v[3]);
+          *(u32x4*)&kb[tix(row, 16 * ch)] = e4m3x8_to_f16(v[0], v[1]);
+          *(u32x4*)&kb[tix(row, 16 * ch + 8)] = e4m3x8_to_f16(v[2], v[3]);
         } else {                // 8 bf16 tail channels
-          *(u32x4*)&kb[row * KP + DN + 8 * (ch - 28)] = bf16x8_to_f16(v);
+          *(u32x4*)&kb[tix(row, DN + 8 * (ch - 28))] = bf16x8_to_f16(v);
         }
       }
     }
@@ -322,11 +329,11 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       f32x4 an = {0.f, 0.f, 0.f, 0.f}, at = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 6; ++ks) {
-        const u32x4 a = *(const u32x4*)&kb[(16 * nt + r) * KP + 256 * cg + 32 * ks + 8 * g];
+        const u32x4 a = *(const u32x4*)&kb[tix(16 * nt + r, 256 * cg + 32 * ks + 8 * g)];
         an = mfma_f16(a, Bq[ks], an);
       }
-      const u32x4 a6 = *(const u32x4*)&kb[(16 * nt + r) * KP + 256 * cg + 192 + 8 * g];
-      const u32x4 a7 = *(const u32x4*)&kb[(16 * nt + r) * KP + 256 * cg + 224 + 8 * g];
+      const u32x4 a6 = *(const u32x4*)&kb[tix(16 * nt + r, 256 * cg + 192 + 8 * g)];
+      const u32x4 a7 = *(const u32x4*)&kb[tix(16 * nt + r, 256 * cg + 224 + 8 * g)];
       if (tailw) {
         at = mfma_f16(a6, Bq[6], at);
         at = mfma_f16(a7, Bq[7], at);
@@ -399,7 +406,8 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     const u32x4 bhi = tailw ? bpp : bps;
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
-      const uint16_t* tp = kb + tr_row * KP + 256 * cg + 16 * n + tr_col;
+      // rows tr_row and tr_row + 16 share bit 2, so one swizzled offset serves both
+      const uint16_t* tp = kb + tix(tr_row, 256 * cg + 16 * n + tr_col);
       const u32x2 lo4 = ds_tr16(tp), hi4 = ds_tr16(tp + 16 * KP);
       const u32x4 a = {lo4[0], lo4[1], hi4[0], hi4[1]};
       O[n] = mfma_f16(a, n < 12 ? bps : bhi, O[n]);
