@@ -471,9 +471,16 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     }
     return;
   }
+  // partial: this split's normalised output O / l in fp16 (half the bytes of
+  // fp32 to write here and to read in the merge), plus (m, l)
   const size_t pb = ((size_t)qn * nsplit + split) * H + head;
+  const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
+  uint16_t* ph = (uint16_t*)part_o;
 #pragma unroll
-  for (int n = 0; n < 16; ++n) *(f32x4*)&part_o[pb * D + 256 * cg + 16 * n + 4 * g] = O[n];
+  for (int n = 0; n < 16; ++n) {
+    const u32x2 w = {pk_f16(O[n][0] * inv, O[n][1] * inv), pk_f16(O[n][2] * inv, O[n][3] * inv)};
+    *(u32x2*)&ph[pb * D + 256 * cg + 16 * n + 4 * g] = w;
+  }
   if (g == 0 && cg == 0) {
     part_ml[pb * 2] = m_i;
     part_ml[pb * 2 + 1] = l_i;
@@ -551,8 +558,10 @@ __global__ __launch_bounds__(256) void k_attn_vec(LayerParams P, Cache cc, const
 
 // ----------------------------------------------------------------- merge
 // grid (queries, H); block d/4 threads, each four adjacent channels.  The
-// splits' (max, sum) pairs are read once into LDS.
-template <int ACTF>
+// splits' (max, sum) pairs are read once into LDS.  HALF: the partials are
+// fp16 normalised outputs O_s / l_s (tile kernel), combined with weights
+// l_s exp(m_s - M); otherwise fp32 unnormalised O_s with weights exp(m_s - M).
+template <int ACTF, bool HALF>
 __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     const int32_t* __restrict__ pos, int pos0, int nsplit,
@@ -582,7 +591,7 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
     for (int e = 0; e < 4; ++e) {
       const int sidx = threadIdx.x + 64 * e;
       const float wgt = l[e] > 0.f ? __expf(m[e] - M) : 0.f;
-      if (sidx < nsplit) wsh[sidx] = wgt;
+      if (sidx < nsplit) wsh[sidx] = HALF ? l[e] * wgt : wgt;
       L += l[e] * wgt;
     }
     L = wave_sum(L);
@@ -595,7 +604,13 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
     float4 v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      v[j] = *(const float4*)(part_o + (b0 + (size_t)min(s0 + j, nsplit - 1) * H) * d + c);
+      const size_t o = (b0 + (size_t)min(s0 + j, nsplit - 1) * H) * d + c;
+      if constexpr (HALF) {
+        const _Float16* hp = (const _Float16*)part_o + o;
+        v[j] = make_float4((float)hp[0], (float)hp[1], (float)hp[2], (float)hp[3]);
+      } else {
+        v[j] = *(const float4*)(part_o + o);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -661,10 +676,15 @@ int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32
 #undef CKV_AV
   }
   dim3 mg(nq, P.H);
-  if (P.act_fmt == CKV_F32)
-    hipLaunchKernelGGL(k_attn_merge<CKV_F32>, mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
+  const bool half = attn_uses_tiles(P);
+  if (P.act_fmt == CKV_F32 && half)
+    hipLaunchKernelGGL((k_attn_merge<CKV_F32, true>), mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
+  else if (P.act_fmt == CKV_F32)
+    hipLaunchKernelGGL((k_attn_merge<CKV_F32, false>), mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
+  else if (half)
+    hipLaunchKernelGGL((k_attn_merge<CKV_BF16, true>), mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
   else
-    hipLaunchKernelGGL(k_attn_merge<CKV_BF16>, mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
+    hipLaunchKernelGGL((k_attn_merge<CKV_BF16, false>), mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
   return (int)hipGetLastError();
 }
 
