@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // any LDS read.  The kernel therefore waits for the tile loads itself (all
 // counters, then a barrier) at the top of each tile, and reads no other LDS
 // in the tile loop.
-constexpr int kPfRows = 128, kPfQ = 8, kPfTiles = 16;
+constexpr int kPfRows = 128, kPfQ = 8, kPfTiles = 64;
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
