@@ -402,6 +402,35 @@ def test_indexer_score_stage_keys():
     assert np.all(cpu(keys_g[cfg.batch]) == 0), "keys written past the batch's rows"
 
 
+def test_score_timing_hook_brackets_one_launch():
+    """ckv_time_next_score: the armed launch gives the same keys as an unarmed
+    one, stamps both events (positive elapsed time, under a second), and the
+    arming is used up by that launch."""
+    from compressed_kv_sparse_amd import _lib as L
+    cfg = get_config("c5").with_(batch=2, comp_cap=4096, seed=33, name="score_timing")
+    inp = make_decode_inputs(cfg, n_ctx=np.array([16384, 5000]))
+    dl = device_layer(cfg, make_layer_weights(cfg), inp.cache)
+    qI, w, pos = dev(inp.qI), dev(inp.w), dev(inp.pos)
+    st = torch.cuda.current_stream().cuda_stream
+    plain = torch.zeros((cfg.batch, cfg.comp_cap), dtype=torch.int32, device="cuda")
+    timed = torch.zeros_like(plain)
+    assert L.indexer_score_decode(dl.desc, dl.cache, qI, w, pos, cfg.batch, plain, st) == 0
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()
+    torch.cuda.synchronize()
+    assert L.time_next_score(a, b) == 0
+    assert L.indexer_score_decode(dl.desc, dl.cache, qI, w, pos, cfg.batch, timed, st) == 0
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    assert 0.0 < ms < 1000.0, ms
+    assert torch.equal(plain, timed)
+    # disarmed: a further launch leaves the events where they were
+    assert L.indexer_score_decode(dl.desc, dl.cache, qI, w, pos, cfg.batch, timed, st) == 0
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) == ms
+
+
 @pytest.mark.parametrize("case", ["all_equal", "integer_ties"])
 def test_decode_topk_with_exact_ties(case):
     """Top-k under exact score ties, where the lowest-index rule decides.
