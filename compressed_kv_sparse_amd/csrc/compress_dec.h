@@ -78,6 +78,26 @@ struct PoolAcc {
       acc += w * kv;
     }
   }
+  // N entries at once: one rescale to the round's new maximum, then N
+  // weights exp(e - m) by the hardware exp2, no branch
+  template <int N>
+  __device__ __forceinline__ void add_round(const float (&e)[N], const float (&kv)[N]) {
+    constexpr float kL2e = 1.4426950408889634f;
+    float mr = e[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) mr = fmaxf(mr, e[i]);
+    const float nm = fmaxf(m, mr);
+    const float f = __builtin_amdgcn_exp2f((m - nm) * kL2e);   // m = -inf: 0, and s, acc are 0
+    s *= f;
+    acc *= f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float w = __builtin_amdgcn_exp2f((e[i] - nm) * kL2e);
+      s += w;
+      acc = fmaf(w, kv[i], acc);
+    }
+    m = nm;
+  }
   __device__ __forceinline__ float value() const { return s > 0.f ? acc / s : 0.f; }
 };
 
@@ -326,23 +346,39 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
       if (t0 & 4) pool8(std::integral_constant<int, 4>{});
       else pool8(std::integral_constant<int, 0>{});
     } else {
-      // c128a: j = slot; the window starts at t0 = 128 i >= 0
-#pragma unroll 1
-      for (int s0 = part * SPT; s0 < (part + 1) * SPT && part < TPC; s0 += RND) {
-        float2 kk[RND], ss[RND], aa[RND];
+      // c128a: j = slot; the window starts at t0 = 128 i >= 0.  The thread's
+      // SPT slots in rounds of RND, the next round's loads issued before the
+      // current round is pooled (parts past TPC re-read the last part's slots
+      // and are dropped by the merge)
+      constexpr int NR = SPT / RND;
+      const int sb = min(part, TPC - 1) * SPT;
+      float2 kk[2][RND], ss[2][RND], aa[2][RND];
+      auto load_round = [&](int rr) {
 #pragma unroll
         for (int e = 0; e < RND; ++e) {
-          kk[e] = ld2(skv + (s0 + e) * d + c);
-          ss[e] = ld2(ssc + (s0 + e) * d + c);
-          aa[e] = ld2(w.ape + (s0 + e) * d + c);
+          const int sl = sb + rr * RND + e;
+          kk[rr & 1][e] = ld2(skv + sl * d + c);
+          ss[rr & 1][e] = ld2(ssc + sl * d + c);
+          aa[rr & 1][e] = ld2(w.ape + sl * d + c);
         }
+      };
+      load_round(0);
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) {
+        if (rr + 1 < NR) load_round(rr + 1);
+        float e0[RND], e1[RND], v0[RND], v1[RND];
 #pragma unroll
         for (int e = 0; e < RND; ++e) {
-          const bool self = s0 + e == cur;
-          const float2 k2 = self ? ka : kk[e], s2 = self ? sa : ss[e];
-          a0.add(s2.x + aa[e].x, k2.x);
-          a1.add(s2.y + aa[e].y, k2.y);
+          const int sl = sb + rr * RND + e;
+          const bool self = sl == cur;
+          const float2 k2 = self ? ka : kk[rr & 1][e], s2 = self ? sa : ss[rr & 1][e];
+          e0[e] = s2.x + aa[rr & 1][e].x;
+          e1[e] = s2.y + aa[rr & 1][e].y;
+          v0[e] = k2.x;
+          v1[e] = k2.y;
         }
+        a0.add_round(e0, v0);
+        a1.add_round(e1, v1);
       }
     }
   }
