@@ -75,9 +75,6 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
       // fixed cost is small next to a tile's, and more blocks fill the chip)
       rps = (rows + 9) / 10;
       rps = rps < 64 ? 64 : rps > 320 ? 320 : rps;
-      // tuning knob: rows of the row list one decode block handles (multiple of 32)
-      const char* e = getenv("CKV_ATTN_ROWS_PER_SPLIT");
-      if (e && atoi(e) >= 32) rps = atoi(e);
     }
   } else {
     rps = 32;
