@@ -95,7 +95,7 @@ __device__ __forceinline__ int topk_end(const int32_t* tk, int k, int V, int* sm
 // inside the fp16 range).  Probabilities lie in [0, e^8].
 //
 // The block first lays out its split's row list in LDS as 64-bit row
-// addresses (bit 0 set: skipped entry, a valid dummy row stands in).  Staging
+// addresses (bit 0 set: skipped entry, an all-zero row stands in).  Staging
 // is coalesced: consecutive lanes load consecutive 16-byte chunks of one
 // stored row and convert them into the row-major tile.  The tile is
 // double-buffered: tile t is multiplied from one buffer while tile t + 1 is
@@ -154,6 +154,11 @@ __device__ __forceinline__ u32x2 ds_tr16(const uint16_t* p) {
 }
 }  // namespace attn
 
+// The row skipped list entries point at: zeros, so that a skipped row adds
+// nothing to PV (its logit is -inf through its scale slot) without a select
+// per staged value.  Written never.
+__device__ __attribute__((aligned(256))) uint8_t g_attn_zero_row[2048];
+
 template <int KVF>
 __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, const uint16_t* __restrict__ q,
                                                    const int32_t* __restrict__ pos, int seq_fixed, int pos0,
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   const int ntiles = j1 > j0 ? (j1 - j0 + R - 1) / R : 0;
   const int nent = (ntiles + 4) * R;   // table entries incl. the padding tiles the loop issues
   const int K = (P.ratio == 4 && topk) ? P.topk : 0;
-  const uint8_t* dummy = decode ? cc.raw + (size_t)A.seq * P.swa * P.row_bytes : cc.stage;
+  const uint8_t* dummy = g_attn_zero_row;
 
   // ---- the split's row list -> rtab.  The top-k list ends at its first
   // entry >= V; entries < 0 are skipped.
@@ -239,7 +244,6 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   // Thread t < 32 also loads the scale of row t.
   struct Stg {
     u32x4 v[IT];
-    bool ok[IT];
     float s;
     bool sok;
   };
@@ -249,7 +253,6 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       const int it = tid + NT * e;
       const int row = min(it / CPR, R - 1), ch = it % CPR;
       const uint64_t ra = rtab[tile * R + row];
-      S.ok[e] = !(ra & 1u) && it < R * CPR;
       const int off = !F8 ? 16 * ch : (ch < 28 ? 16 * ch : DN + 16 * (ch - 28));
       S.v[e] = *(const u32x4*)((const uint8_t*)(ra & ~(uint64_t)1) + off);
     }
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       const int it = tid + NT * e;
       const int row = it / CPR, ch = it % CPR;
       if (it < R * CPR) {
-        const u32x4 v = S.ok[e] ? S.v[e] : (u32x4){0u, 0u, 0u, 0u};
+        const u32x4 v = S.v[e];   // skipped entries read the zero row
         if (!F8) {
           *(u32x4*)&kb[tix(row, 8 * ch)] = bf16x8_to_f16(v);
         } else if (ch < 28) {   // 16 codes -> 16 fp16 channels
