@@ -240,7 +240,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   __syncthreads();
 
   // staging: item e of this thread is chunk it % CPR of tile row it / CPR,
-  // it = tid + NT e; items past the tile read a dummy row and are dropped.
+  // it = tid + NT e; items past the tile read the zero row and are dropped.
   // Thread t < 32 also loads the scale of row t.
   struct Stg {
     u32x4 v[IT];
