@@ -110,16 +110,23 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic_c5.md")
 
 
 def score_kernel_source_hash():
-    """sha256 of the score kernel's source: its section of k_indexer.hip and
-    the device helpers it includes.  A recorded HBM traffic figure is valid only
-    for the source it was measured on."""
+    """sha256 of the score kernel's code: its section of k_indexer.hip and the
+    device helpers it includes, comments and blank lines left out.  A recorded
+    HBM traffic figure is valid only for the code it was measured on."""
     import hashlib
+    import re
     csrc = os.path.join(ROOT, "compressed_kv_sparse_amd", "csrc")
+
+    def code(text):
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+        return "\n".join(ln for ln in lines if ln.strip())
+
     src = open(os.path.join(csrc, "k_indexer.hip")).read()
     a = src.index("// ---------------------------------------------------------------- MFMA score")
     b = src.index("// ---------------------------------------------------------------- vector score")
-    h = hashlib.sha256(src[a:b].encode())
-    h.update(open(os.path.join(csrc, "ckv_device.h"), "rb").read())
+    h = hashlib.sha256(code(src[a:b]).encode())
+    h.update(code(open(os.path.join(csrc, "ckv_device.h")).read()).encode())
     return h.hexdigest()
 
 

@@ -73,8 +73,10 @@ __device__ __forceinline__ IdxQuery idx_query(const LayerParams& P, const int32_
 // to its default occupancy target the compiler reuses one buffer's
 // registers for the next and every wave's loads and multiplies serialise;
 // with more blocks than fit, a second round of blocks waits for the first.
-// (Measured on the 16 x 32768-row batch: 25.7 us here; 30.8 us with one
-// wave per SIMD and three buffers; 30.8 us with four waves and no prefetch.)
+// (Measured on the 16 x 32768-row batch, rows read from HBM: 26.3 us here,
+// the time of a kernel that issues the same loads and no arithmetic; 27.7 us
+// with two groups per block (two rounds of blocks); 29-30 us with one buffer
+// at three or four waves per SIMD.)
 constexpr int kScoreGroups = 4;
 // The decode step's launch: scan blocks of 5 groups (416 for the 16 x 32768-
 // row batch), then the 80 projection blocks, each wave keeping 16 of its
