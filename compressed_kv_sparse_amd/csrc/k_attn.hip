@@ -575,26 +575,50 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
   const int c = 4 * threadIdx.x;
   const int p = pos ? pos[qn] : pos0 + qn;
   const size_t b0 = (size_t)qn * nsplit * H + h;
-  if (threadIdx.x < 64) {
+  // Loads first, all unconditional (indices clamped): the splits' (max, sum)
+  // pairs (lane l of each wave: splits l + 64 e), then this thread's four
+  // channels of the first kPF splits' partials, so that one memory round trip
+  // serves both (the weights wait only for the pairs, issued first).
+  constexpr int kPF = 16;
+  const int cl = min(c, d - 4);
+  float2 mlv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int sidx = (threadIdx.x & 63) + 64 * e;
+    mlv[e] = *(const float2*)(part_ml + (b0 + (size_t)min(sidx, nsplit - 1) * H) * 2);
+  }
+  auto load_part = [&](int sp) -> float4 {
+    const size_t o = (b0 + (size_t)min(sp, nsplit - 1) * H) * d + cl;
+    if constexpr (HALF) {
+      const _Float16* hp = (const _Float16*)part_o + o;
+      return make_float4((float)hp[0], (float)hp[1], (float)hp[2], (float)hp[3]);
+    } else {
+      return *(const float4*)(part_o + o);
+    }
+  };
+  __builtin_amdgcn_sched_barrier(0);   // (keeps the pairs' loads ahead of the partials')
+  float4 v0[kPF];
+#pragma unroll
+  for (int j = 0; j < kPF; ++j) v0[j] = load_part(j);
+  {
     // max over splits with rows, then each split's weight exp(m_s - M)
     float m[4], l[4];
     float M = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {   // clamped, unconditional loads; splits past nsplit weigh 0
-      const int sidx = threadIdx.x + 64 * e;
-      const float2 ml = *(const float2*)(part_ml + (b0 + (size_t)min(sidx, nsplit - 1) * H) * 2);
+    for (int e = 0; e < 4; ++e) {   // splits past nsplit weigh 0
+      const int sidx = (threadIdx.x & 63) + 64 * e;
       const bool in = sidx < nsplit;
-      m[e] = in ? ml.x : -INFINITY;
-      l[e] = in ? ml.y : 0.f;
+      m[e] = in ? mlv[e].x : -INFINITY;
+      l[e] = in ? mlv[e].y : 0.f;
       if (l[e] > 0.f) M = fmaxf(M, m[e]);
     }
     M = wave_max(M);
     float L = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int sidx = threadIdx.x + 64 * e;
+      const int sidx = (threadIdx.x & 63) + 64 * e;
       const float wgt = l[e] > 0.f ? __expf(m[e] - M) : 0.f;
-      if (sidx < nsplit) wsh[sidx] = HALF ? l[e] * wgt : wgt;
+      if (threadIdx.x < 64 && sidx < nsplit) wsh[sidx] = HALF ? l[e] * wgt : wgt;
       L += l[e] * wgt;
     }
     L = wave_sum(L);
@@ -603,26 +627,21 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
   __syncthreads();
   if (c >= d) return;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < nsplit; s0 += 8) {   // eight splits' loads in flight at a time
+  auto accum = [&](const float4& x, int sp) {
+    const float wgt = sp < nsplit ? wsh[sp] : 0.f;
+    a.x += x.x * wgt;
+    a.y += x.y * wgt;
+    a.z += x.z * wgt;
+    a.w += x.w * wgt;
+  };
+#pragma unroll
+  for (int j = 0; j < kPF; ++j) accum(v0[j], j);
+  for (int s0 = kPF; s0 < nsplit; s0 += 8) {   // further splits, eight loads in flight at a time
     float4 v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const size_t o = (b0 + (size_t)min(s0 + j, nsplit - 1) * H) * d + c;
-      if constexpr (HALF) {
-        const _Float16* hp = (const _Float16*)part_o + o;
-        v[j] = make_float4((float)hp[0], (float)hp[1], (float)hp[2], (float)hp[3]);
-      } else {
-        v[j] = *(const float4*)(part_o + o);
-      }
-    }
+    for (int j = 0; j < 8; ++j) v[j] = load_part(s0 + j);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float wgt = s0 + j < nsplit ? wsh[s0 + j] : 0.f;
-      a.x += v[j].x * wgt;
-      a.y += v[j].y * wgt;
-      a.z += v[j].z * wgt;
-      a.w += v[j].w * wgt;
-    }
+    for (int j = 0; j < 8; ++j) accum(v[j], s0 + j);
   }
   const float inv = Lsh > 0.f ? 1.f / Lsh : 0.f;
   float o[4] = {a.x * inv, a.y * inv, a.z * inv, a.w * inv};
