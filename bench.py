@@ -332,22 +332,28 @@ def bench_prefill(cfg, steps, warmup):
     out = dl.new_out(T)
     topk = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
     # the chunk rewrites the raw ring and the compressor state; restoring them
-    # before each run keeps every run identical (a few hundred KiB of copies)
+    # before each run keeps every run identical (a few hundred KiB of copies,
+    # outside the timed span: HIP events on the stream bracket the three
+    # prefill calls alone)
     saved = [(t, t.clone()) for t in (dl.raw, dl.st_kv, dl.st_sc, dl.ist_kv, dl.ist_sc) if t is not None]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
 
-    def run():
+    def run(ev=None):
         for t, c in saved:
             t.copy_(c)
+        if ev is not None:
+            ev[0].record()
         dl.prefill(0, inp.pos0, x, u, q, qI, w, out=out, topk=topk)
+        if ev is not None:
+            ev[1].record()
 
     for _ in range(max(1, warmup)):
         run()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        run()
+    for i in range(steps):
+        run(evs[i])
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
+    dt = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
     fl = prefill_flops(cfg, inp.pos0, T)
     return {"ms_per_chunk": dt * 1e3, "tok_s": T / dt, "tflops": fl / dt / 1e12,
             "mfma_frac": fl / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS, "flops": fl}
