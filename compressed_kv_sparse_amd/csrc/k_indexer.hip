@@ -15,6 +15,8 @@
 // lowest-index rows equal to it, in ascending index order.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "compress_dec.h"
 #include "proj_dec.h"
 
@@ -272,7 +274,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //
 // Heads are the MFMA M dimension and rows N: a lane's accumulators hold 4
 // heads of one row, so the weighted head sum is in-lane adds plus a sum over
-// the 4 lane groups (v_permlane32_swap / v_permlane16_swap, no LDS); relu is
+// the 4 lane groups, done for four sub-tiles at once as a scattered sum
+// (v_permlane32_swap / v_permlane16_swap, no LDS); relu is
 // one integer max on the float's bits (negative floats have negative bit
 // patterns, so max(bits, 0) is relu; a lower bound of INT_MIN keeps x), which
 // needs no NaN-quieting step in front as a float max does.
@@ -286,8 +289,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // wait for every direct load in flight -- including the next tile's -- before
 // any LDS read.  The kernel therefore waits for the tile loads itself (all
 // counters, then a barrier) at the top of each tile, and reads no other LDS
-// in the tile loop.
+// in the tile loop.  Sub-tiles are addressed through the read's offset field.
+//
+// Measured on MI355X (4096 queries at position 61440): a loop of the same
+// MFMA chains and epilogue with operands in registers runs at 73-80 % of
+// the bf16 peak; this kernel reaches about half of it.  Without the
+// epilogue it takes 88 % of its time, without three quarters of the LDS
+// reads 89 %, without the tile loads 97 %.  Requesting the next sub-tile's
+// fragments before the current epilogue (no spare registers for a second
+// set) and 16 queries per block were both slower.
 constexpr int kPfRows = 128, kPfQ = 8, kPfTiles = 64;
+static_assert(kPfRows % (4 * kPfQ) == 0, "each wave fills whole 4-row slices of a tile");
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
@@ -296,19 +308,33 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-// four 16-byte LDS reads, waited for
-__device__ __forceinline__ void lds_read4_b128(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4& r0,
-                                               u32x4& r1, u32x4& r2, u32x4& r3) {
+// four 16-byte LDS reads at byte offset OFF from each address, waited for
+template <int OFF>
+__device__ __forceinline__ void lds_read4_b128_at(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4& r0,
+                                                  u32x4& r1, u32x4& r2, u32x4& r3) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
   asm volatile(
-      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
+      "ds_read_b128 %0, %4 offset:%8\n\tds_read_b128 %1, %5 offset:%8\n\tds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\ts_waitcnt lgkmcnt(0)"
       : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(OFF)
       : "memory");
+}
+// Sums over the 4 lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48) of four values
+// at once, scattered: row 0 of the result holds the total of s0, row 1 of s2,
+// row 2 of s1, row 3 of s3 (three row swaps and three adds instead of four
+// full two-step sums).
+__device__ __forceinline__ float rows4_sum_scatter(float s0, float s1, float s2, float s3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
+  const float A = __uint_as_float(a[0]) + __uint_as_float(a[1]);   // rows 0-1: s0, rows 2-3: s1
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s2), __float_as_uint(s3), false, false);
+  const float B = __uint_as_float(b[0]) + __uint_as_float(b[1]);   // rows 0-1: s2, rows 2-3: s3
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(A), __float_as_uint(B), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 template <int MT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_idx_score_prefill(
+__global__ __launch_bounds__(64 * kPfQ) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_idx_score_prefill(
     LayerParams P, const uint16_t* idx, const uint16_t* __restrict__ qI, const float* __restrict__ wt, int seq,
     int pos0, int T, uint32_t* __restrict__ keys) {
   constexpr int DI = 128, KS = DI / 32;
@@ -330,13 +356,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int vlast = vmax - 1;
 
   // direct loads of tile rb into buffer buf: instruction e of this wave fills
-  // rows 4 (8 e + wave) .. + 3
+  // rows 4 (kPfQ e + wave) .. + 3
   auto load_tile = [&](int buf, int rb) {
 #pragma unroll
-    for (int e = 0; e < kPfRows / 32; ++e) {
-      const int R = 4 * (8 * e + wave) + (lane >> 4);
+    for (int e = 0; e < kPfRows / (4 * kPfQ); ++e) {
+      const int R = 4 * (kPfQ * e + wave) + (lane >> 4);
       const int q = (lane & 15) ^ (R & 15);
-      lds_dma16(base + (size_t)min(rb + R, vlast) * DI + 8 * q, tiles + buf * TB + 1024 * (8 * e + wave));
+      lds_dma16(base + (size_t)min(rb + R, vlast) * DI + 8 * q, tiles + buf * TB + 1024 * (kPfQ * e + wave));
     }
   };
   load_tile(0, row0);
@@ -393,15 +419,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     __builtin_amdgcn_s_waitcnt(0);   // this wave's share of tile t has landed
     lds_barrier();                    // ... everyone's, and buffer (t + 1) % 2 is free
     if (t + 1 < ntile) load_tile((t + 1) & 1, rb + kPfRows);
-    const uint32_t bt = (uint32_t)((t & 1) * TB);
+    uint32_t ba[KS];   // sub-tile 0 of the buffer; later sub-tiles by offset fields
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ba[ks] = boff[ks] + (uint32_t)((t & 1) * TB);
 #pragma unroll 1
     for (int sq = 0; sq < kPfRows / 64; ++sq) {   // groups of 4 sixteen-row sub-tiles
       float sc[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t so = bt + (uint32_t)(64 * sq + 16 * u) * 256;
+      auto sub = [&](auto uc) {
+        constexpr int u = decltype(uc)::value;
         u32x4 Rv[KS];
-        lds_read4_b128(boff[0] + so, boff[1] + so, boff[2] + so, boff[3] + so, Rv[0], Rv[1], Rv[2], Rv[3]);
+        lds_read4_b128_at<u * 16 * 256>(ba[0], ba[1], ba[2], ba[3], Rv[0], Rv[1], Rv[2], Rv[3]);
         float sv = 0.f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -411,11 +438,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
           for (int i = 0; i < 4; ++i) sv = fmaf(wv[mt][i], __int_as_float(max(__float_as_int(acc[i]), lo)), sv);
         }
-        sc[u] = rows4_sum(sv);   // sum over the 4 lane groups (rows r of groups 0..3 hold other heads)
-      }
-      const float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
-      const int row = rb + 64 * sq + 16 * g + r;
+        sc[u] = sv;   // this lane's heads; rows r of the other lane groups hold the rest
+      };
+      sub(std::integral_constant<int, 0>{});
+      sub(std::integral_constant<int, 1>{});
+      sub(std::integral_constant<int, 2>{});
+      sub(std::integral_constant<int, 3>{});
+      // lane group g receives the total of sub-tile (g & 1) * 2 + (g >> 1)
+      const float mine = rows4_sum_scatter(sc[0], sc[1], sc[2], sc[3]);
+      const int row = rb + 64 * sq + 16 * ((g & 1) * 2 + (g >> 1)) + r;
       *(row < P.cap ? kout + row : g_key_sink + lane) = float_key(mine);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ba[ks] += 64 * 256;
     }
   }
   __builtin_amdgcn_s_waitcnt(0);   // no direct load outlives the block
@@ -1475,7 +1509,7 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
     constexpr int RUN = kPfRows * kPfTiles;
     dim3 pgrid((unsigned)(vmax > 0 ? (vmax + RUN - 1) / RUN : 1), (unsigned)((nq + kPfQ - 1) / kPfQ));
 #define CKV_PF(MTV) \
-  launch_score(k_idx_score_prefill<MTV>, pgrid, dim3(512), st, P, ix, (const uint16_t*)qI, w, seq, pos0, nq, keys)
+  launch_score(k_idx_score_prefill<MTV>, pgrid, dim3(64 * kPfQ), st, P, ix, (const uint16_t*)qI, w, seq, pos0, nq, keys)
     if (MT == 1) CKV_PF(1);
     else if (MT == 2) CKV_PF(2);
     else if (MT == 3) CKV_PF(3);
