@@ -110,8 +110,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic_c5.md")
 
 
 def score_kernel_source_hash():
-    """sha256 of the score kernel's code: its section of k_indexer.hip and the
-    device helpers it includes, comments and blank lines left out.  A recorded
+    """sha256 of the score kernel's code: its section of k_indexer.hip (up to
+    the prefill GEMM) and the device helpers it includes, comments and blank
+    lines left out.  A recorded
     HBM traffic figure is valid only for the code it was measured on."""
     import hashlib
     import re
@@ -124,7 +125,7 @@ def score_kernel_source_hash():
 
     src = open(os.path.join(csrc, "k_indexer.hip")).read()
     a = src.index("// ---------------------------------------------------------------- MFMA score")
-    b = src.index("// ---------------------------------------------------------------- vector score")
+    b = src.index("// ---------------------------------------------------------------- prefill score GEMM")
     h = hashlib.sha256(code(src[a:b]).encode())
     h.update(code(open(os.path.join(csrc, "ckv_device.h")).read()).encode())
     return h.hexdigest()
