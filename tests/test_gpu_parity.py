@@ -478,6 +478,50 @@ def test_decode_topk_with_exact_ties(case):
     assert int(ws.view(torch.int32).abs().sum()) == 0, "sync region not left zero"
 
 
+@pytest.mark.parametrize("case", ["all_equal", "integer_ties"])
+def test_prefill_topk_with_exact_ties(case):
+    """The prefill indexer (score GEMM + per-query select) under exact ties:
+    ckv_indexer_topk_prefill on a chunk of 300 queries at 39700 over stored
+    index rows with small-integer entries, integer weights and a zero rotated
+    tail, so every score is an integer both fp32 and fp64 hold exactly
+    (all_equal: zero weights, every score 0).  Sampled queries' lists
+    against the oracle's full sort, bit-exact (lowest index first among
+    equal scores)."""
+    from compressed_kv_sparse_amd import _lib as LIB
+    cfg = get_config("c5").with_(batch=1, comp_cap=16384, kv_fmt="bf16", seed=43, name=f"pf_ties_{case}")
+    inp = make_decode_inputs(cfg, n_ctx=np.array([40000]))
+    wts = make_layer_weights(cfg)
+    rng = np.random.default_rng(11)
+    c = inp.cache
+    T, pos0 = 300, 39700
+    vals = np.array([-2.0, -1.0, 0.0, 1.0, 2.0], np.float32)
+    c.idx[:] = G.bf16_bits_of_draw(rng.choice(vals, size=c.idx.shape).astype(np.float32))
+    qI_f = rng.choice(vals, size=(T, cfg.idx_heads, cfg.idx_dim)).astype(np.float32)
+    qI_f[..., cfg.idx_dim - 64:] = 0.0
+    qI = G.bf16_bits_of_draw(qI_f)
+    if case == "all_equal":
+        w = np.zeros((T, cfg.idx_heads), np.float32)
+    else:
+        w = rng.integers(0, 3, size=(T, cfg.idx_heads)).astype(np.float32)
+    dl = device_layer(cfg, wts, c, max_chunk=T)
+    topk = torch.full((T, cfg.top_k), -7, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert LIB.indexer_topk_prefill(dl.desc, dl.cache, dev(qI), dev(w), 0, pos0, T, topk, dl.ws, dl.ws_bytes,
+                                    st) == 0
+    torch.cuda.synchronize()
+    tk = cpu(topk)
+    L = oracle_layer(cfg, wts)
+    bseq = oracle_seq_from_bytes(L, None, cpu(dl.comp)[0], cpu(dl.idx)[0], 0)
+    for n in sorted({0, 1, 63, 64, 150, 255, 256, T - 2, T - 1} | set(range(7, T, 41))):
+        p = pos0 + n
+        sc = bseq.index_scores(p, qI[n], w[n])
+        ref = np.sort(O.topk_select(sc, cfg.top_k))
+        assert np.all(sc == np.round(sc)), "scores are not exact integers"
+        kth = np.sort(sc)[::-1][cfg.top_k - 1]
+        assert int((sc == kth).sum()) > 1, "no tie at the k-th score"
+        assert np.array_equal(tk[n], ref), f"{case}: top-k of query {n} differs"
+
+
 def L_sync_bytes(dl):
     from compressed_kv_sparse_amd import _lib as L
     return L.workspace_sync_bytes(dl.desc, L.CKV_MODE_DECODE, dl.batch)
