@@ -418,8 +418,9 @@ def main():
                     help="first run 3 elementwise copies (neg) of MIB MiB: a known-size reference for HBM counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(sequences shard across GPUs with no exchange; see the design notes).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(decode batches would shard by sequence, each GPU running this path on its own sequences).",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
