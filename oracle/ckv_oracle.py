@@ -32,7 +32,10 @@ What it computes, per layer of compression ratio r (0, 4 or 128):
 Readings taken where the pages are silent (each also listed in the design
 notes): APE row = the token's slot in the window being pooled; a compressed
 row sits at position i*r; RoPE rotates adjacent channel pairs of the tail
-with theta_j = base^(-2j/n_rot); one RoPE base per layer; RMSNorm eps 1e-6;
+with theta_j = base^(-2j/n_rot); one RoPE base per layer by default, or one
+base for the raw rows and another for the compressed class (compressed and
+indexer rows), the output's two shares rotated back each in its own frame;
+RMSNorm eps 1e-6;
 logit scale 1/sqrt(d); indexer score = sum_h w_h * relu(qI_h . kI_s) with the
 rotated indexer query cast to the indexer-cache format; top-k ties go to the
 lower index, output ascending with -1 padding; an fp8 row keeps its RoPE tail
@@ -139,7 +142,11 @@ def f32_round(x: np.ndarray) -> np.ndarray:
 def stored_row_bytes(fmt: str, d: int, n_rot: int) -> int:
     """Size of one stored K=V row: f32 4d, bf16 2d; an fp8 row keeps
     d - n_rot E4M3 codes, the n_rot RoPE channels in bf16 and one fp32 scale,
-    padded to a multiple of 128 bytes."""
+    padded to a multiple of 128 bytes.  ``f64`` (8d, no rounding at all) is
+    not a cache format of the method: it lets the exact pins compare two runs
+    of the oracle to fp64 precision."""
+    if fmt == "f64":
+        return 8 * d
     if fmt == "f32":
         return 4 * d
     if fmt == "bf16":
@@ -149,6 +156,8 @@ def stored_row_bytes(fmt: str, d: int, n_rot: int) -> int:
 
 
 def decode_values(a: np.ndarray, fmt: str) -> np.ndarray:
+    if fmt == "f64":
+        return np.asarray(a, F64).copy()
     if fmt == "f32":
         return np.asarray(a, np.float32).astype(F64)
     if fmt == "bf16":
@@ -157,7 +166,9 @@ def decode_values(a: np.ndarray, fmt: str) -> np.ndarray:
 
 
 def cast_values(z: np.ndarray, fmt: str) -> np.ndarray:
-    """Value after storing ``z`` in format ``fmt`` (f32 or bf16, RNE)."""
+    """Value after storing ``z`` in format ``fmt`` (f32 or bf16, RNE; f64 keeps it)."""
+    if fmt == "f64":
+        return np.asarray(z, F64).copy()
     if fmt == "f32":
         return f32_round(z)
     if fmt == "bf16":
@@ -169,6 +180,8 @@ def decode_rows(rec: np.ndarray, fmt: str, d: int, n_rot: int) -> np.ndarray:
     """Stored row records [..., rb] uint8 -> row values [..., d] fp64."""
     rec = np.ascontiguousarray(rec, dtype=np.uint8)
     shp = rec.shape[:-1]
+    if fmt == "f64":
+        return rec[..., :8 * d].copy().view(F64).reshape(shp + (d,))
     if fmt == "f32":
         return rec[..., :4 * d].copy().view(np.float32).reshape(shp + (d,)).astype(F64)
     if fmt == "bf16":
@@ -194,6 +207,9 @@ def encode_row(z: np.ndarray, fmt: str, d: int, n_rot: int) -> Tuple[np.ndarray,
     z = np.asarray(z, F64)
     rb = stored_row_bytes(fmt, d, n_rot)
     rec = np.zeros(rb, np.uint8)
+    if fmt == "f64":
+        rec[:] = z.view(np.uint8)
+        return rec, z.copy()
     if fmt == "f32":
         v = z.astype(np.float32)
         rec[:4 * d] = v.view(np.uint8)
@@ -327,6 +343,23 @@ def attention(qhat: np.ndarray, rows: np.ndarray, scale: float) -> np.ndarray:
     return a @ rows
 
 
+def attention_two_class(q_a: np.ndarray, rows_a: np.ndarray, q_b: np.ndarray, rows_b: np.ndarray,
+                        scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One softmax over the union of two row classes whose keys carry their
+    positions in different rotation frames (raw rows and compressed rows when
+    each class has its own RoPE base): class a's logits use the query q_a,
+    class b's use q_b.  Returns the two classes' shares of o = sum_j a_j k_j,
+    so that each can be rotated back in its own frame."""
+    rows_a = np.asarray(rows_a, F64).reshape(-1, np.shape(q_a)[-1])
+    rows_b = np.asarray(rows_b, F64).reshape(-1, np.shape(q_b)[-1])
+    l = scale * np.concatenate([np.asarray(q_a, F64) @ rows_a.T, np.asarray(q_b, F64) @ rows_b.T], axis=1)
+    l = l - np.max(l, axis=1, keepdims=True)
+    a = np.exp(l)
+    a = a / np.sum(a, axis=1, keepdims=True)
+    na = rows_a.shape[0]
+    return a[:, :na] @ rows_a, a[:, na:] @ rows_b
+
+
 # ===========================================================================
 # one layer, history based
 # ===========================================================================
@@ -357,6 +390,20 @@ class OracleLayer:
     idx_ape: Optional[np.ndarray] = None
     idx_gamma: Optional[np.ndarray] = None
     relu: bool = True
+    # RoPE base of the compressed-row class (compressed rows, indexer rows and
+    # the query's rotation against them).  None: the layer's one base serves
+    # every class (per-layer reading); a value: raw rows and the query against
+    # them keep ``rope_base``, the compressed class takes this one
+    # (per-row-class reading).
+    rope_base_comp: Optional[float] = None
+
+    @property
+    def base_raw(self) -> float:
+        return self.rope_base
+
+    @property
+    def base_comp(self) -> float:
+        return self.rope_base if self.rope_base_comp is None else self.rope_base_comp
 
     @property
     def window(self) -> int:
@@ -375,7 +422,7 @@ def layer_from(cfg, weights) -> OracleLayer:
                     idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim, top_k=cfg.top_k,
                     n_rot=cfg.n_rot, swa=cfg.swa, rope_base=cfg.rope_base,
                     norm_eps=cfg.norm_eps, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt,
-                    act_fmt=cfg.act_fmt)
+                    act_fmt=cfg.act_fmt, rope_base_comp=getattr(cfg, "rope_base_comp", None))
     if weights is not None:
         L.wkv = w(weights.wkv, cfg.w_fmt)
         L.wgate = w(weights.wgate, cfg.w_fmt)
@@ -465,13 +512,13 @@ class OracleSequence:
 
     def _pool_row(self, i: int, lane: str) -> np.ndarray:
         """Pool, RMS-normalise, then rotate the tail at the row position i*r
-        (P1 s4 steps 5-7)."""
+        (P1 s4 steps 5-7) with the compressed class's base."""
         L = self.L
         y = self.pooled(i, lane)
         gamma = L.gamma if lane == "attn" else L.idx_gamma
         z = rmsnorm(y, gamma, L.norm_eps)
         n_rot = min(L.n_rot, len(z))
-        return rope_tail(z, i * L.ratio, L.rope_base, n_rot)
+        return rope_tail(z, i * L.ratio, L.base_comp, n_rot)
 
     def _row_is_computed(self, i: int) -> bool:
         """Row i is computed from history when its last window token is live."""
@@ -508,10 +555,10 @@ class OracleSequence:
     # -- raw window ----------------------------------------------------------
     def raw_row(self, t: int) -> Tuple[np.ndarray, Optional[np.ndarray], np.ndarray]:
         """(pre-cast, record, stored value) of the raw row of token t: u_t RoPE'd
-        at t (P4: the SWA rows carry their position)."""
+        at t with the raw class's base (P4: the SWA rows carry their position)."""
         L = self.L
         if self.is_live(t):
-            z = rope_tail(self.u[t], t, L.rope_base, L.n_rot)
+            z = rope_tail(self.u[t], t, L.base_raw, L.n_rot)
             rec, val = encode_row(z, L.kv_fmt, L.head_dim, L.n_rot)
             return z, rec, val
         val = decode_rows(self.raw_rec[t % L.swa], L.kv_fmt, L.head_dim, L.n_rot)
@@ -563,17 +610,22 @@ class OracleSequence:
 
     def index_scores(self, p: int, qI: np.ndarray, w: np.ndarray) -> np.ndarray:
         """Indexer scores of every visible row for query p.  The indexer query
-        gets the tail RoPE at p and is cast to the indexer-cache format."""
+        gets the tail RoPE at p (the compressed class's base: it is matched
+        against compressed rows) and is cast to the indexer-cache format."""
         L = self.L
         V = self.visible_rows(p)
-        qh = rope_tail(decode_values(qI, L.act_fmt), p, L.rope_base, min(L.n_rot, L.idx_dim))
+        qh = rope_tail(decode_values(qI, L.act_fmt), p, L.base_comp, min(L.n_rot, L.idx_dim))
         qh = cast_values(qh, L.idx_fmt)
         return indexer_scores(qh, np.asarray(w, F64), self.idx_matrix(V), relu=L.relu)
 
     def attend(self, p: int, q: np.ndarray, topk: Optional[np.ndarray]) -> np.ndarray:
-        """Output o [H, d] (pre-cast) for query p over raw window + compressed set."""
+        """Output o [H, d] (pre-cast) for query p over raw window + compressed
+        set: one softmax over both classes, the query rotated at p against
+        each class in that class's frame, and each class's share of the output
+        rotated back by -p in its own frame (inverse RoPE, P4; with one base
+        per layer the two rotations are the same and this is o rotated by -p)."""
         L = self.L
-        rows = [self.raw_row(t)[2] for t in self.raw_window(p)]
+        raw = np.stack([self.raw_row(t)[2] for t in self.raw_window(p)])
         V = self.visible_rows(p)
         sel = []
         if L.ratio == 4:
@@ -585,10 +637,13 @@ class OracleSequence:
                 sel.append(int(i))
         elif L.ratio == 128:
             sel = list(range(V))
-        allrows = np.concatenate([np.stack(rows), self.comp_matrix(sel)]) if sel else np.stack(rows)
-        qh = rope_tail(decode_values(q, L.act_fmt), p, L.rope_base, L.n_rot)
-        o = attention(qh, allrows, L.scale)
-        return rope_tail(o, -p, L.rope_base, L.n_rot)   # inverse RoPE (P4)
+        comp = self.comp_matrix(sel)
+        qv = decode_values(q, L.act_fmt).reshape(L.n_heads, L.head_dim)
+        q_raw = rope_tail(qv, p, L.base_raw, L.n_rot)
+        q_comp = rope_tail(qv, p, L.base_comp, L.n_rot)
+        o_raw, o_comp = attention_two_class(q_raw, raw, q_comp, comp, L.scale)
+        # inverse RoPE (P4), class by class
+        return rope_tail(o_raw, -p, L.base_raw, L.n_rot) + rope_tail(o_comp, -p, L.base_comp, L.n_rot)
 
     def step(self, p: int, x, u, q, qI=None, w=None, topk_override=None) -> dict:
         """One decode step at token p: make p live, then index, select, attend."""

@@ -387,24 +387,277 @@ def test_zero_query_gives_mean_of_attended_rows():
 # prefill vs decode, schedule, cache sizes
 # ---------------------------------------------------------------------------
 
-def test_prefill_equals_sequential_decode():
-    L = _small_layer(4)
-    n = 45
-    X = rng.standard_normal((n, 12)).astype(np.float32)
-    U = rng.standard_normal((n, 16)).astype(np.float32)
-    Q = rng.standard_normal((n, 3, 16)).astype(np.float32)
-    QI = rng.standard_normal((n, 2, 8)).astype(np.float32)
-    Wt = rng.uniform(0, 1, (n, 2))
-    dec = O.OracleSequence(L)
-    outs = [dec.step(p, X[p], U[p], Q[p], QI[p], Wt[p])["out_f64"] for p in range(n)]
-    chk = O.OracleSequence(L)
-    p0 = 0
-    res = {}
-    for T in (37, 1, 7):
-        res.update(O.prefill(chk, p0, X[p0:p0 + T], U[p0:p0 + T], Q[p0:p0 + T], QI[p0:p0 + T], Wt[p0:p0 + T]))
-        p0 += T
-    for p in range(n):
-        np.testing.assert_array_equal(res[p]["out_f64"], outs[p])
+# ---------------------------------------------------------------------------
+# position bookkeeping through OracleSequence
+# ---------------------------------------------------------------------------
+#
+# Each class of vector carries its position in its RoPE tail: raw row t at t,
+# compressed / indexer row i at i*r, the query at p, the output rotated back
+# by -p (vLLM page, "Shared Key and Value": the inverse rotation makes the
+# attention depend on relative positions only).  The pins below fix each of
+# these positions from outside the oracle: closed forms whose expected values
+# come from trigonometry written here, translation of a whole history, and the
+# resume of a sequence from its stored cache.
+
+
+def _softmax_out(logits, vecs):
+    """sum_j softmax(logits)_j vecs_j in plain Python floats."""
+    m = max(logits)
+    e = [math.exp(v - m) for v in logits]
+    s = sum(e)
+    out = np.zeros(len(vecs[0]))
+    for w, v in zip(e, vecs):
+        out += (w / s) * np.asarray(v, np.float64)
+    return out
+
+
+def _pin_layer(ratio, base, base_comp, d=16, D=4, DI=8, n_rot=8, top_k=4):
+    return O.OracleLayer(ratio=ratio, head_dim=d, n_heads=1, idx_heads=1 if ratio == 4 else 0,
+                         idx_dim=DI if ratio == 4 else 0, top_k=top_k if ratio == 4 else 0, n_rot=n_rot, swa=128,
+                         rope_base=base, norm_eps=1e-6, kv_fmt="f64", idx_fmt="f64", act_fmt="f64",
+                         rope_base_comp=base_comp)
+
+
+@pytest.mark.parametrize("ratio", [0, 4, 128])
+@pytest.mark.parametrize("bases", [(10000.0, None), (10000.0, 160000.0)])
+def test_positions_of_every_class_closed_form(ratio, bases):
+    """Every vector lives in tail pair 1 (channels d_n+2, d_n+3), where RoPE at
+    position s turns it by s*theta_1, theta_1 = base^(-2/n_rot).  Raw rows are
+    A*(cos t*th_r, sin t*th_r); the compressor sees a constant kappa (wgate = 0,
+    APE = 0), so every pooled row is the same unit vector, RMS-normalised to
+    amplitude c = (1/d + eps)^(-1/2) and turned by i*r*th_c; the indexer lane
+    likewise with c_I over D_I channels.  The query is Aq*e and q^I = e.  Then
+
+      raw logit        tau*Aq*A*cos((p - t) th_r)
+      compressed logit tau*Aq*c*cos((p - i r) th_c)
+      indexer score    relu(c_I cos((p - 4 i) th_c))
+
+    and the output, rotated back by -p class by class, is
+    sum a_t A (cos, sin)((t - p) th_r) + sum a_i c (cos, sin)((i r - p) th_c).
+    Rotating any class at another position (t + 1, i*r + 1, 2p, +p for the
+    inverse), or with the other class's base, moves these values."""
+    base, base_comp = bases
+    L = _pin_layer(ratio, base, base_comp)
+    d, n_rot, D, DI = L.head_dim, L.n_rot, 4, 8
+    dn = d - n_rot
+    th_r = base ** (-2.0 / n_rot)
+    th_c = (base if base_comp is None else base_comp) ** (-2.0 / n_rot)
+    A, Aq, tau = 3.0, 2.0, d ** -0.5
+    ch = dn + 2                                         # x channel of pair 1
+    if ratio:
+        W = L.window
+        L.wkv = np.zeros((d, D))
+        L.wkv[ch, 0] = 1.0
+        L.wgate = np.zeros((d, D))
+        L.ape = np.zeros((W, d))
+        L.gamma = np.ones(d)
+        if ratio == 4:
+            L.idx_wkv = np.zeros((DI, D))
+            L.idx_wkv[2, 0] = 1.0                     # D_I = n_rot: every indexer channel rotates
+            L.idx_wgate = np.zeros((DI, D))
+            L.idx_ape = np.zeros((8, DI))
+            L.idx_gamma = np.ones(DI)
+    N = 700 if ratio == 128 else 420
+    X = np.zeros((N, D))
+    X[:, 0] = 1.0
+    U = np.zeros((N, d))
+    U[:, ch] = A
+    seq = O.OracleSequence(L)
+    seq.feed(0, X, U)
+    c = (1.0 / d + 1e-6) ** -0.5
+    cI = (1.0 / DI + 1e-6) ** -0.5
+    q = np.zeros((1, d))
+    q[0, ch] = Aq
+    qI = np.zeros((1, DI))
+    qI[0, 2] = 1.0
+    for p in (5, 130, 259, 263, N - 1):
+        res = seq.query(p, q, qI if ratio == 4 else None, np.ones(1) if ratio == 4 else None)
+        logits, vecs = [], []
+        for t in range(max(0, p - 127), p + 1):
+            logits.append(tau * Aq * A * math.cos((p - t) * th_r))
+            v = np.zeros(d)
+            v[ch], v[ch + 1] = A * math.cos((t - p) * th_r), A * math.sin((t - p) * th_r)
+            vecs.append(v)
+        V = (p + 1) // ratio if ratio else 0
+        if ratio == 4:
+            sc = [max(0.0, cI * math.cos((p - 4 * i) * th_c)) for i in range(V)]
+            np.testing.assert_allclose(res["scores"], sc, rtol=1e-12, atol=1e-12)
+            order = sorted(range(V), key=lambda i: (-sc[i], i))[:L.top_k]
+            assert sorted(order) == [int(i) for i in res["topk"] if i >= 0], p
+            rows = sorted(order)
+        else:
+            rows = range(V)
+        for i in rows:
+            logits.append(tau * Aq * c * math.cos((p - i * ratio) * th_c))
+            v = np.zeros(d)
+            v[ch], v[ch + 1] = c * math.cos((i * ratio - p) * th_c), c * math.sin((i * ratio - p) * th_c)
+            vecs.append(v)
+        np.testing.assert_allclose(res["out_f64"][0], _softmax_out(logits, vecs), rtol=1e-11, atol=1e-12)
+
+
+def _rand_layer(ratio, seed, base_comp=None):
+    """Small layer with fp64 storage, channel 0 of every computed row held at
+    zero (wkv row 0 = 0); the translation pin uses that channel."""
+    r = np.random.default_rng(seed)
+    d, D, DI = 16, 12, 8
+    L = O.OracleLayer(ratio=ratio, head_dim=d, n_heads=3, idx_heads=2 if ratio == 4 else 0,
+                      idx_dim=DI if ratio == 4 else 0, top_k=4 if ratio == 4 else 0, n_rot=8, swa=128,
+                      rope_base=10000.0, norm_eps=1e-6, kv_fmt="f64", idx_fmt="f64", act_fmt="f64",
+                      rope_base_comp=base_comp)
+    if ratio:
+        W = L.window
+        L.wkv = r.standard_normal((d, D)) * 0.4
+        L.wkv[0] = 0.0
+        L.wgate = r.standard_normal((d, D)) * 0.4
+        L.ape = r.standard_normal((W, d)) * 0.3
+        L.gamma = 1.0 + 0.1 * r.standard_normal(d)
+        if ratio == 4:
+            L.idx_wkv = r.standard_normal((DI, D)) * 0.4
+            L.idx_wgate = r.standard_normal((DI, D)) * 0.4
+            L.idx_ape = r.standard_normal((8, DI)) * 0.3
+            L.idx_gamma = 1.0 + 0.1 * r.standard_normal(DI)
+    return L
+
+
+def _history(L, N, seed):
+    r = np.random.default_rng(seed)
+    X = r.standard_normal((N, 12))
+    U = r.standard_normal((N, L.head_dim))
+    U[:, 0] = 0.0
+    Q = r.standard_normal((N, L.n_heads, L.head_dim))
+    Q[..., 0] = 1.0
+    QI = r.standard_normal((N, max(L.idx_heads, 1), max(L.idx_dim, 1)))
+    Wt = r.uniform(0.0, 1.0, (N, max(L.idx_heads, 1)))
+    return X, U, Q, QI, Wt
+
+
+def _shifted_sequence(L, delta, cap):
+    """A sequence whose first live token is ``delta``, with nothing before it:
+    the pending compressor slots carry score -inf (no weight, as slots before
+    token 0 do), indexer rows before it are zero (score 0: never selected
+    while the k-th best score is positive), and each compressed row before it
+    holds -1e200 in channel 0, where every query has 1 and every live row 0,
+    so its logit is about -1e199 and its softmax weight exactly 0."""
+    d = L.head_dim
+    W = L.window
+    comp = np.zeros((cap, 8 * d), np.uint8)
+    if L.ratio:
+        for i in range(delta // L.ratio):
+            v = np.zeros(d)
+            v[0] = -1e200
+            comp[i] = v.view(np.uint8)
+    kw = {}
+    if L.ratio:
+        kw.update(st_kv=np.zeros((W, d)), st_sc=np.full((W, d), -np.inf))
+    if L.ratio == 4:
+        kw.update(ist_kv=np.zeros((8, L.idx_dim)), ist_sc=np.full((8, L.idx_dim), -np.inf))
+    return O.OracleSequence(L, raw_rec=None, comp_rec=comp, idx_vals=None, first_live=delta, **kw)
+
+
+@pytest.mark.parametrize("ratio,delta", [(4, 4 * 1237), (128, 128 * 29), (0, 3001)])
+@pytest.mark.parametrize("base_comp", [None, 160000.0])
+def test_translation_of_a_whole_history(ratio, delta, base_comp):
+    """The same un-rotated history (x, u, q, q^I, w) fed at positions 0.. and
+    at delta.., with delta a multiple of r: every query's top-k set shifts by
+    delta / r and its output is unchanged (fp64 storage; queries at p >= 127
+    so that both raw windows hold live tokens only).  This holds only when
+    raw rows, compressed rows, indexer rows, the query and the inverse
+    rotation all carry consistent positions, per class."""
+    L = _rand_layer(ratio, 7 + ratio, base_comp)
+    N = 700 if ratio == 128 else 300
+    X, U, Q, QI, Wt = _history(L, N, 99 + ratio)
+    A = O.OracleSequence(L)
+    A.feed(0, X, U)
+    B = _shifted_sequence(L, delta, (delta + N) // max(ratio, 1) + 1)
+    B.feed(delta, X, U)
+    for p in (127, 200, 263, N - 1):
+        qi, w = (QI[p], Wt[p]) if ratio == 4 else (None, None)
+        ra = A.query(p, Q[p], qi, w)
+        rb = B.query(delta + p, Q[p], qi, w)
+        if ratio == 4:
+            assert np.sort(ra["scores"])[::-1][L.top_k - 1] > 0.0
+            ta, tb = ra["topk"], rb["topk"]
+            np.testing.assert_array_equal(tb[tb >= 0], ta[ta >= 0] + delta // 4)
+        np.testing.assert_allclose(rb["out_f64"], ra["out_f64"], rtol=0, atol=1e-9)
+    if ratio:
+        # control: a shift that is not a multiple of r moves the absolute
+        # window boundaries, and the outputs change
+        B2 = _shifted_sequence(L, delta + 1, (delta + N) // ratio + 2)
+        B2.feed(delta + 1, X, U)
+        p = N - 1
+        qi, w = (QI[p], Wt[p]) if ratio == 4 else (None, None)
+        o1 = B2.query(delta + 1 + p, Q[p], qi, w)["out_f64"]
+        assert np.max(np.abs(o1 - A.query(p, Q[p], qi, w)["out_f64"])) > 1e-6
+
+
+@pytest.mark.parametrize("ratio,t0", [(4, 4 * 57 + 2), (4, 4 * 60), (128, 128 * 3 + 37), (0, 200)])
+@pytest.mark.parametrize("fmt", ["f64", "f32"])
+def test_resume_from_stored_cache_equals_full_history(ratio, t0, fmt):
+    """A sequence resumed at token t0 from the cache a full run left behind --
+    raw ring slot t % 128, compressed and indexer rows 0 .. t0//r - 1, and the
+    compressor windows' pending (kappa, sigma) in slot t % W -- continues
+    exactly as the full run does (P1 s3: chunks carry the compressor window
+    and the raw rows across their edges)."""
+    L = _rand_layer(ratio, 3 + ratio)
+    L.kv_fmt = L.idx_fmt = fmt
+    N = 700 if ratio == 128 else 320
+    X, U, Q, QI, Wt = _history(L, N, 5 + ratio)
+    A = O.OracleSequence(L)
+    A.feed(0, X, U)
+    d = L.head_dim
+    rb = O.stored_row_bytes(fmt, d, L.n_rot)
+    raw = np.zeros((128, rb), np.uint8)
+    for t in range(max(0, t0 - 127), t0):
+        raw[t % 128] = A.raw_row(t)[1]
+    kw = dict(raw_rec=raw, first_live=t0)
+    if ratio:
+        cap = N // ratio + 1
+        comp = np.zeros((cap, rb), np.uint8)
+        for i in range(t0 // ratio):
+            comp[i] = A.comp_row(i)[1]
+        W = L.window
+        st_kv, st_sc = np.zeros((W, d)), np.zeros((W, d))
+        for t in range(max(0, t0 - W), t0):
+            st_kv[t % W], st_sc[t % W] = A.kap[t], A.sig[t]
+        kw.update(comp_rec=comp, st_kv=st_kv, st_sc=st_sc)
+        if ratio == 4:
+            idx = np.zeros((cap, L.idx_dim))
+            for i in range(t0 // 4):
+                idx[i] = A.idx_row(i)[1]
+            ist_kv, ist_sc = np.zeros((8, L.idx_dim)), np.zeros((8, L.idx_dim))
+            for t in range(max(0, t0 - 8), t0):
+                ist_kv[t % 8], ist_sc[t % 8] = A.ikap[t], A.isig[t]
+            kw.update(idx_vals=idx, ist_kv=ist_kv, ist_sc=ist_sc)
+    B = O.OracleSequence(L, **kw)
+    B.feed(t0, X[t0:], U[t0:])
+    for p in sorted({t0, t0 + 1, t0 + 3, min(t0 + 130, N - 2), N - 1}):
+        qi, w = (QI[p], Wt[p]) if ratio == 4 else (None, None)
+        ra, rb_ = A.query(p, Q[p], qi, w), B.query(p, Q[p], qi, w)
+        if ratio == 4:
+            np.testing.assert_array_equal(rb_["topk"], ra["topk"])
+        np.testing.assert_allclose(rb_["out_f64"], ra["out_f64"], rtol=1e-13, atol=1e-13)
+
+
+def test_sliding_window_holds_exactly_the_last_128_tokens():
+    """Ratio 0: the output at p changes when any of the tokens p-127 .. p
+    changes (the query's own token included: it is appended before it is
+    attended) and does not change for p-128 or for any later token."""
+    L = _rand_layer(0, 1)
+    N = 400
+    X, U, Q, QI, Wt = _history(L, N, 2)
+    p = 300
+
+    def out(U2):
+        s = O.OracleSequence(L)
+        s.feed(0, X, U2)
+        return s.query(p, Q[p])["out_f64"]
+
+    base = out(U)
+    for t, moves in ((p, True), (p - 127, True), (p - 60, True), (p - 128, False), (p + 1, False),
+                     (0, False)):
+        U2 = U.copy()
+        U2[t, 1:] += 0.5
+        assert (np.max(np.abs(out(U2) - base)) > 1e-9) == moves, t
 
 
 def test_flash_schedule():

@@ -57,6 +57,9 @@ class LayerShape:
     n_rot: int = 64
     swa: int = 128
     rope_base: float = ROPE_BASE_COMPRESSED
+    # base of the compressed-row class (compressed rows, indexer rows and the
+    # query's rotation against them); None: ``rope_base`` serves every class
+    rope_base_comp: Optional[float] = None
     norm_eps: float = 1e-6
     seed: int = 1
     # distributions (standard deviations)
