@@ -3,13 +3,18 @@
 
 A step is one decode step of one c4a layer at 128k context for a batch of 16
 sequences: compress_append -> indexer_topk -> sparse_swa_attn through the C
-ABI, inputs resident in HBM (fp8 E4M3 attention cache with fp32 row scales,
-bf16 indexer cache, 64 query heads x 512, top-k 512).  The timed loop replays
-a captured HIP graph of one step.  Alongside it the script reports:
+ABI's single decode-step call, inputs resident in HBM (fp8 E4M3 attention
+cache with fp32 row scales, bf16 indexer cache, 64 query heads x 512, top-k
+512).  The timed loop replays a captured HIP graph of one step.  Alongside
+it the script reports:
 
-* roofline of the dominant kernel (the indexer score scan): algorithmic bytes
-  per launch / its average launch duration from HIP events around it;
+* roofline of the step's dominant kernel (the projection + indexer scan
+  launch): its algorithmic bytes per launch / its average duration from HIP
+  events its own dispatch stamps, and its HBM traffic from recorded counters;
 * the whole step's algorithmic bytes against HBM peak;
+* the other decode workloads (c4a at 64k for 32 sequences, c128a at up to 1M
+  tokens, the 128k c128a and window-only layers) and a context sweep of the
+  64k-workload shapes from 4k to 128k;
 * the 4096-token chunked prefill at position 61440 (tokens/s and the share of
   bf16 MFMA peak of its algorithmic flops);
 * the whole 43-layer Flash stack (2 window-only, 21 c4a, 20 c128a layers) at
@@ -48,12 +53,13 @@ def make_layer(cfg, wts, cache, max_chunk=0):
     dl = DeviceLayer(ratio=cfg.ratio, hidden=cfg.hidden, head_dim=cfg.head_dim, n_heads=cfg.n_heads,
                      batch=cfg.batch, idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim, top_k=cfg.top_k,
                      comp_cap=cfg.comp_cap, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt, act_fmt=cfg.act_fmt,
-                     w_fmt=cfg.w_fmt, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps, max_chunk=max_chunk)
+                     w_fmt=cfg.w_fmt, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps, max_chunk=max_chunk,
+                     rope_base_comp=cfg.rope_base_comp or 0.0)
     if wts is not None:
         dl.set_weights(wkv=wts.wkv, wgate=wts.wgate, ape=wts.ape, gamma=wts.gamma, idx_wkv=wts.idx_wkv,
                        idx_wgate=wts.idx_wgate, idx_ape=wts.idx_ape, idx_gamma=wts.idx_gamma)
     dl.load_cache(raw=cache.raw, comp=cache.comp, idx=cache.idx, st_kv=cache.st_kv, st_sc=cache.st_sc,
-                  ist_kv=cache.ist_kv, ist_sc=cache.ist_sc)
+                  ist_kv=cache.ist_kv, ist_sc=cache.ist_sc, n_tokens=cache.first_live)
     return dl
 
 
@@ -94,50 +100,59 @@ def decode_step_bytes(cfg, n):
     return total
 
 
-def score_kernel_bytes(cfg, n):
-    """Bytes the indexer score kernel must move: every visible indexer row, the
-    queries and head weights, and one 4-byte key written per row."""
+def step_scan_bytes(cfg, n):
+    """Algorithmic bytes of the decode step's projection + scan launch: every
+    indexer row it scores (all visible rows but the one the step's own token
+    closes, which the selection block scores), the four projection weight
+    matrices, x, q^I and the head weights.  The keys it writes are workspace,
+    not part of the method's traffic."""
     s_i = 2 if cfg.idx_fmt == "bf16" else 4
     s_a = 2 if cfg.act_fmt == "bf16" else 4
-    tot = 0.0
+    s_w = 2 if cfg.w_fmt == "bf16" else 4
+    tot = 2.0 * cfg.hidden * (cfg.head_dim + cfg.idx_dim) * s_w
     for nb in n:
         V = nb // 4
-        tot += V * cfg.idx_dim * s_i + V * 4 + cfg.idx_heads * (cfg.idx_dim * s_a + 4)
+        scanned = V - 1 if nb % 4 == 0 else V
+        tot += scanned * cfg.idx_dim * s_i + cfg.hidden * s_a + cfg.idx_heads * (cfg.idx_dim * s_a + 4)
     return tot
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic_c5.md")
+STEP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_scan_traffic_c5.md")
 
 
-def score_kernel_source_hash():
-    """sha256 of the score kernel's code: its section of k_indexer.hip (up to
-    the prefill GEMM) and the device helpers it includes, comments and blank
-    lines left out.  A recorded
-    HBM traffic figure is valid only for the code it was measured on."""
-    import hashlib
+def _code(text):
     import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
+def step_scan_source_hash():
+    """sha256 of the step scan kernel's code (comments and blank lines left
+    out): the score body and the fused-step section of k_indexer.hip, the
+    projection tile and the device helpers.  A recorded HBM traffic figure is
+    valid only for the code it was measured on."""
+    import hashlib
     csrc = os.path.join(ROOT, "compressed_kv_sparse_amd", "csrc")
-
-    def code(text):
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
-        return "\n".join(ln for ln in lines if ln.strip())
-
     src = open(os.path.join(csrc, "k_indexer.hip")).read()
-    a = src.index("// ---------------------------------------------------------------- MFMA score")
-    b = src.index("// ---------------------------------------------------------------- prefill score GEMM")
-    h = hashlib.sha256(code(src[a:b]).encode())
-    h.update(code(open(os.path.join(csrc, "ckv_device.h")).read()).encode())
+    parts = [src[src.index("// ---------------------------------------------------------------- MFMA score"):
+                 src.index("// ---------------------------------------------------------------- prefill score GEMM")],
+             src[src.index("// ---------------------------------------------------------------- fused decode step"):
+                 src.index("// k_step_select: one block")],
+             open(os.path.join(csrc, "proj_dec.h")).read(),
+             open(os.path.join(csrc, "ckv_device.h")).read()]
+    h = hashlib.sha256()
+    for part in parts:
+        h.update(_code(part).encode())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the score kernel from the committed counter
-    summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
-    for a copy of known size), or None when the kernel's source has changed
-    since."""
+def recorded_traffic(path, source_hash):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by what the counter reads for a copy of known
+    size), or None when the kernel's source has changed since."""
     try:
-        lines = open(TRAFFIC_FILE).read().splitlines()
+        lines = open(path).read().splitlines()
     except OSError:
         return None
     kv = {}
@@ -145,7 +160,7 @@ def recorded_traffic():
         if ln.startswith("- ") and ": " in ln:
             k, v = ln[2:].split(": ", 1)
             kv[k.strip()] = v.strip().strip("`")
-    if kv.get("source_sha256") != score_kernel_source_hash():
+    if kv.get("source_sha256") != source_hash:
         return None
     return int(kv["traffic_bytes_per_launch"])
 
@@ -230,32 +245,89 @@ def bench_decode(cfg, steps, warmup, with_kernel=True, api="step", copies=3):
     res["step_gbs"] = res["step_bytes"] / dt / 1e9
     res["step_hbm_frac"] = res["step_gbs"] / HBM_PEAK_GBS
 
-    if with_kernel and cfg.ratio == 4:
-        # the dominant kernel on its own: indexer score scan, the copies taking
-        # the launches in turn as above; each launch stamps a pair of HIP
-        # events at the kernel's own start and end (hipExtLaunchKernel), on
-        # the stream it runs on
-        keys = torch.empty((B, cfg.comp_cap), dtype=torch.int32, device="cuda")
+    if with_kernel and cfg.ratio == 4 and api == "step":
+        # the step's dominant kernel: the projection + indexer scan launch of
+        # the decode-step call, timed by a pair of HIP events its own dispatch
+        # stamps at the kernel's start and end (hipExtLaunchKernel), on the
+        # stream it runs on; the copies take the steps in turn as above
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for a, b in evs:        # torch creates an event at its first record
             a.record()
             b.record()
-        stream = torch.cuda.current_stream().cuda_stream
         for i in range(warmup + steps):
-            dl = layers[i % len(layers)]
             if i >= warmup:
                 L.time_next_score(*evs[i - warmup])
-            rc = L.indexer_score_decode(dl.desc, dl.cache, qI, w, pos, B, keys, stream)
-            if rc:
-                raise L.CkvError(rc, "indexer_score_decode")
+            step(layers[i % len(layers)])
         torch.cuda.synchronize()
+        assert int(layers[0].status.abs().sum()) == 0, "device status set"
         ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        kb = score_kernel_bytes(cfg, n)
-        res["kernel"] = {"name": "k_idx_score_mfma", "avg_us": ms * 1e3, "bytes": kb,
+        kb = step_scan_bytes(cfg, n)
+        res["kernel"] = {"name": "k_step_scan", "avg_us": ms * 1e3, "bytes": kb,
                          "gbs": kb / (ms * 1e-3) / 1e9}
     res["_inp"] = inp
     res["_wts"] = wts
     return res
+
+
+# --------------------------------------------------------------------------- context sweep
+
+SWEEP_CONTEXTS = (4096, 8192, 16384, 32768, 65536, 131072)
+
+
+def bench_sweep(steps, warmup, copies=3, contexts=SWEEP_CONTEXTS):
+    """Decode throughput against context length ("throughput per context
+    frontier"): the 64k workload's layer shape (c4a, 32 sequences, bf16,
+    8 x 128 indexer, top-k 512) at each context, caches filled on the device
+    as at a warm context, ``copies`` layer instances taking the steps in turn
+    so that every cache byte comes from HBM."""
+    import torch
+    from compressed_kv_sparse_amd import DeviceLayer
+    from workloads import get_config
+    from workloads.device_gen import draw_step_inputs, draw_weights, fill_layer_cache
+    from workloads.gen import context_lengths
+
+    rows = []
+    for n_ctx in contexts:
+        cfg = get_config("c2").with_(n_ctx=n_ctx, comp_cap=n_ctx // 4, name=f"c2_sweep_{n_ctx}")
+        layers = []
+        for _ in range(copies):
+            dl = DeviceLayer(ratio=4, hidden=cfg.hidden, head_dim=cfg.head_dim, n_heads=cfg.n_heads,
+                             batch=cfg.batch, idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim, top_k=cfg.top_k,
+                             comp_cap=cfg.comp_cap, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt,
+                             rope_base=cfg.rope_base, norm_eps=cfg.norm_eps)
+            fill_layer_cache(dl, cfg)
+            dl.set_weights(**draw_weights(cfg))
+            layers.append(dl)
+        a = draw_step_inputs(cfg)
+        out = layers[0].new_out(cfg.batch)
+        topk = torch.empty((cfg.batch, cfg.top_k), dtype=torch.int32, device="cuda")
+        graphs = []
+        for dl in layers:
+            dl.decode_step(a["x"], a["u"], a["q"], a["qI"], a["w"], a["pos"], out=out, topk=topk)
+        torch.cuda.synchronize()
+        assert all(int(dl.status.abs().sum()) == 0 for dl in layers), "device status set"
+        for dl in layers:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                dl.decode_step(a["x"], a["u"], a["q"], a["qI"], a["w"], a["pos"], out=out, topk=topk)
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        nb = decode_step_bytes(cfg, context_lengths(cfg))
+        rows.append({"context": n_ctx, "us_per_step": round(dt * 1e6, 2), "tok_s": round(cfg.batch / dt, 1),
+                     "hbm_frac": round(nb / dt / 1e9 / HBM_PEAK_GBS, 4)})
+        log(f"[bench] sweep {n_ctx}: {dt * 1e6:.1f} us/step, {cfg.batch / dt:.0f} tok/s, "
+            f"{100 * nb / dt / 1e9 / HBM_PEAK_GBS:.1f}% HBM")
+        del layers, graphs
+        torch.cuda.empty_cache()
+    return {"workload": "c2 shapes (c4a, B=32, bf16, indexer 8x128, top-k 512), caches filled on the device",
+            "points": rows}
 
 
 # --------------------------------------------------------------------------- layer stack
@@ -336,7 +408,8 @@ def bench_prefill(cfg, steps, warmup):
     # before each run keeps every run identical (a few hundred KiB of copies,
     # outside the timed span: HIP events on the stream bracket the three
     # prefill calls alone)
-    saved = [(t, t.clone()) for t in (dl.raw, dl.st_kv, dl.st_sc, dl.ist_kv, dl.ist_sc) if t is not None]
+    saved = [(t, t.clone()) for t in (dl.raw, dl.st_kv, dl.st_sc, dl.ist_kv, dl.ist_sc, dl.n_tokens)
+             if t is not None]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
 
     def run(ev=None):
@@ -388,9 +461,18 @@ def cpu_baseline(cfg, inp, wts, budget_s=12.0):
             break
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": model,
             "sample": f"{done} sequence decode steps of {cfg.name} (p={int(inp.pos[0])}), "
-                      f"{dt:.1f}s on the host, numpy fp64"}
+                      f"{dt:.1f}s on the host, numpy fp64 ({threads} BLAS threads of {os.cpu_count()} host CPUs)"}
 
 
 # --------------------------------------------------------------------------- main
@@ -407,10 +489,11 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-stack", action="store_true")
-    ap.add_argument("--part", choices=("all", "prefill", "stack"), default="all",
+    ap.add_argument("--part", choices=("all", "decode", "prefill", "stack"), default="all",
                     help="time one part alone and print its own JSON line (for kernel profiles)")
     ap.add_argument("--stack-steps", type=int, default=20)
-    ap.add_argument("--extra", action="store_true", help="also time the other decode workloads")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other decode workloads")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the context sweep")
     ap.add_argument("--layer-copies", type=int, default=3,
                     help="independent layer instances taking the decode steps in turn (1: one layer re-read every "
                          "step, partly from the last-level cache)")
@@ -457,14 +540,23 @@ def main():
         roof = {"bound": "hbm", "kernel": kern["name"], "achieved": round(kern["gbs"], 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern["gbs"] / HBM_PEAK_GBS, 4),
                 "avg_us": round(kern["avg_us"], 2), "bytes_per_launch": int(kern["bytes"]),
-                "traffic": recorded_traffic() if cfg.name.startswith("c5") else None}
+                "traffic": (recorded_traffic(STEP_TRAFFIC_FILE, step_scan_source_hash())
+                            if cfg.name.startswith("c5_c4a") and args.layer_copies == 3 else None)}
+    if args.part == "decode":
+        print(json.dumps({"part": "decode", "workload": cfg.name, "us_per_step": round(r["ms_per_step"] * 1e3, 2),
+                          "roofline": roof}), flush=True)
+        return
     extra = {}
-    if args.extra:
+    if not args.no_extra:
         for name in ("c2", "c3", "c5_c128a", "c5_swa"):
             e = bench_decode(get_config(name), args.steps, args.warmup, with_kernel=False, copies=args.layer_copies)
             extra[name] = {k: round(v, 4) for k, v in e.items() if not k.startswith("_") and isinstance(v, float)}
             log(f"[bench] decode {name}: {e['ms_per_step'] * 1e3:.1f} us/step, {e['tok_s']:.0f} tok/s, "
                 f"{100 * e['step_hbm_frac']:.1f}% HBM")
+            del e
+    sweep = None
+    if not args.no_sweep:
+        sweep = bench_sweep(args.steps, args.warmup, copies=args.layer_copies)
     pre = None
     if not args.no_prefill:
         p = bench_prefill(get_config("c4"), args.prefill_steps, 1)
@@ -501,6 +593,8 @@ def main():
     }
     if extra:
         line["extra"] = extra
+    if sweep:
+        line["sweep"] = sweep
     print(json.dumps(line), flush=True)
 
 

@@ -18,6 +18,7 @@ CKV_E_UNSUPPORTED = -2
 CKV_E_CAPACITY = -3
 CKV_E_WORKSPACE = -4
 CKV_E_HIP = -5
+CKV_E_SEQUENCE = -6
 
 CKV_F32, CKV_BF16, CKV_E4M3 = 0, 1, 2
 FMT = {"f32": CKV_F32, "bf16": CKV_BF16, "e4m3": CKV_E4M3}
@@ -27,6 +28,7 @@ CKV_MODE_DECODE, CKV_MODE_PREFILL = 0, 1
 CKV_MAX_CHUNK = 4096
 CKV_STATUS_BAD_POS = 1
 CKV_STATUS_CAPACITY = 2
+CKV_STATUS_SEQUENCE = 4
 
 
 class LayerDesc(ctypes.Structure):
@@ -37,7 +39,7 @@ class LayerDesc(ctypes.Structure):
         ("comp_cap", ctypes.c_int32), ("batch", ctypes.c_int32), ("kv_fmt", ctypes.c_int32),
         ("idx_fmt", ctypes.c_int32), ("act_fmt", ctypes.c_int32), ("w_fmt", ctypes.c_int32),
         ("flags", ctypes.c_uint32), ("rope_base", ctypes.c_double), ("norm_eps", ctypes.c_float),
-        ("softmax_scale", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float), ("rope_base_comp", ctypes.c_double),
     ]
 
 
@@ -51,7 +53,7 @@ class LayerCache(ctypes.Structure):
         ("raw", ctypes.c_void_p), ("comp", ctypes.c_void_p), ("idx", ctypes.c_void_p),
         ("st_kv", ctypes.c_void_p), ("st_sc", ctypes.c_void_p), ("ist_kv", ctypes.c_void_p),
         ("ist_sc", ctypes.c_void_p), ("raw_stage", ctypes.c_void_p), ("stage_rows", ctypes.c_int32),
-        ("status", ctypes.c_void_p),
+        ("status", ctypes.c_void_p), ("n_tokens", ctypes.c_void_p), ("n_tokens_host", ctypes.c_void_p),
     ]
 
 

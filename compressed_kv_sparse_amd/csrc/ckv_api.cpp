@@ -38,6 +38,7 @@ Cache to_cache(const ckv_layer_cache* c) {
   x.stage = (uint8_t*)c->raw_stage;
   x.stage_rows = c->stage_rows;
   x.status = c->status;
+  x.n_tokens = c->n_tokens;
   return x;
 }
 
@@ -49,6 +50,8 @@ int prologue(const ckv_layer_desc* d, const ckv_layer_cache* c, LayerParams* P) 
   if (!c) return CKV_E_INVAL;
   make_params(d, P);
   if (check_ptr(c->raw)) return CKV_E_INVAL;
+  if (c->n_tokens && ((uintptr_t)c->n_tokens & 3u)) return CKV_E_INVAL;
+  if (c->status && ((uintptr_t)c->status & 3u)) return CKV_E_INVAL;
   if (P->ratio) {
     if (check_ptr(c->comp) || check_ptr(c->st_kv) || check_ptr(c->st_sc)) return CKV_E_INVAL;
   }
@@ -83,6 +86,13 @@ int prefill_range_ok(const LayerParams& P, const ckv_layer_cache* c, int32_t seq
   if (P.ratio && (pos0 + T) / P.ratio > P.cap) return CKV_E_CAPACITY;
   if (!c->raw_stage || !aligned16(c->raw_stage)) return CKV_E_INVAL;
   if (c->stage_rows < T + P.swa - 1) return CKV_E_CAPACITY;
+  return CKV_OK;
+}
+
+// The host mirror of the token counts, when the caller keeps one: a chunk
+// must start at its sequence's next position.
+int prefill_sequence_ok(const ckv_layer_cache* c, int32_t seq, int32_t pos0) {
+  if (c->n_tokens_host && c->n_tokens_host[seq] != pos0) return CKV_E_SEQUENCE;
   return CKV_OK;
 }
 
@@ -133,6 +143,7 @@ extern "C" int ckv_compress_append_prefill(const ckv_layer_desc* desc, const ckv
   int rc = prologue(desc, cache, &P);
   if (rc) return rc;
   if ((rc = prefill_range_ok(P, cache, seq, pos0, T))) return rc;
+  if ((rc = prefill_sequence_ok(cache, seq, pos0))) return rc;
   if ((rc = weights_ok(P, w))) return rc;
   if (check_ptr(u) || (P.ratio && check_ptr(x))) return CKV_E_INVAL;
   WsLayout L;

@@ -76,8 +76,19 @@ __device__ __forceinline__ void rope_cs_theta(double theta, double pos, float* c
   r = fma(-k, 2.4492935982947064e-16, r);              // 2 pi, low part
   sincosf((float)r, s, c);
 }
+// Pair j at position pos in the raw rows' frame (raw rows, the query against
+// them) and in the compressed class's frame (compressed rows, indexer rows,
+// the query against them); the two coincide when the layer has one base.
 __device__ __forceinline__ void rope_cs(const LayerParams& P, int j, double pos, float* c, float* s) {
   rope_cs_theta(P.theta[j], pos, c, s);
+}
+__device__ __forceinline__ void rope_cs_c(const LayerParams& P, int j, double pos, float* c, float* s) {
+  rope_cs_theta(P.theta_c[j], pos, c, s);
+}
+// Rotation that takes a vector turned by pos in the raw frame to the same
+// vector turned by pos in the compressed frame: angle pos (theta_c - theta).
+__device__ __forceinline__ void rope_cs_switch(const LayerParams& P, int j, double pos, float* c, float* s) {
+  rope_cs_theta(P.theta_c[j] - P.theta[j], pos, c, s);
 }
 
 // ---------------------------------------------------------------- MFMA

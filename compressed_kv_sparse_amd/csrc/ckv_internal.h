@@ -14,6 +14,7 @@ constexpr int kHistBins = 4096;   // top-k histogram of the keys' top 12 bits
 constexpr int kCandCap = 4096;    // decode top-k: keys of the threshold bin resolved in LDS
 constexpr int kMaxSplits = 256;   // attention partial results merged per query
 constexpr int kMaxDI = 128;
+constexpr int kMaxTopK = 2048;    // top-k entries a query may keep (attention row table)
 
 // Layer parameters as the kernels see them (built from ckv_layer_desc after
 // validation; plain values, passed by value to every kernel).
@@ -27,7 +28,9 @@ struct LayerParams {
   int row_bytes;  // stored K=V row size
   int ncol;       // projection columns: 2d (+ 2 DI on ratio 4)
   int idx_rot;    // RoPE channels of indexer rows / queries: min(n_rot, DI)
-  double theta[32];  // RoPE frequencies base^(-2j/n_rot), j < n_rot/2
+  double theta[32];    // RoPE frequencies of the raw class: base^(-2j/n_rot), j < n_rot/2
+  double theta_c[32];  // the compressed class (compressed rows, indexer rows, indexer query)
+  int two_bases;       // theta_c differs from theta (one frame per row class)
 };
 
 struct Weights {
@@ -52,6 +55,7 @@ struct Cache {
   uint8_t* stage;
   int stage_rows;
   uint32_t* status;
+  int32_t* n_tokens;   // per-sequence token count (NULL: no sequence check)
 };
 
 // Workspace carve-up (all offsets 256-byte aligned).  The sync region comes
@@ -79,7 +83,7 @@ struct WsLayout {
   size_t proj;      // float [proj_splits][n][ncol]
   size_t keys;      // uint32 [n][cap]   indexer keys
   size_t part_o;    // float [n][splits][H][d]  attention partial outputs
-  size_t part_ml;   // float [n][splits][H][2]  attention partial (max, sum)
+  size_t part_ml;   // float [n][splits][H][4]  attention partial (max, sum, scale of the stored output, 0)
   size_t total;
   int proj_splits;
   int attn_splits;

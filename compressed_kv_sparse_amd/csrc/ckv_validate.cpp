@@ -42,8 +42,12 @@ bool make_params(const ckv_layer_desc* d, LayerParams* P) {
   P->row_bytes = (int)ckv_row_bytes(d->kv_fmt, d->head_dim, d->n_rot);
   P->ncol = d->ratio == 0 ? 0 : 2 * d->head_dim + (d->ratio == 4 ? 2 * d->idx_dim : 0);
   P->idx_rot = d->ratio == 4 ? (d->idx_dim < d->n_rot ? d->idx_dim : d->n_rot) : 0;
-  for (int j = 0; j < 32; ++j)
+  const double base_c = d->rope_base_comp > 0.0 ? d->rope_base_comp : d->rope_base;
+  for (int j = 0; j < 32; ++j) {
     P->theta[j] = 2 * j < d->n_rot ? pow(d->rope_base, -2.0 * j / (double)d->n_rot) : 0.0;
+    P->theta_c[j] = 2 * j < d->n_rot ? pow(base_c, -2.0 * j / (double)d->n_rot) : 0.0;
+  }
+  P->two_bases = base_c != d->rope_base;
   return true;
 }
 
@@ -112,7 +116,7 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   L.part_o = off;
   if (need_part) off += align256((size_t)n * L.attn_splits * P.H * P.d * sizeof(float));
   L.part_ml = off;
-  if (need_part) off += align256((size_t)n * L.attn_splits * P.H * 2 * sizeof(float));
+  if (need_part) off += align256((size_t)n * L.attn_splits * P.H * 4 * sizeof(float));
   L.total = off ? off : 256;
   return L;
 }
@@ -135,7 +139,9 @@ extern "C" size_t ckv_row_bytes(int32_t fmt, int32_t head_dim, int32_t n_rot) {
 extern "C" int ckv_validate(const ckv_layer_desc* d) {
   if (!d) return CKV_E_INVAL;
   if (d->batch <= 0 || d->hidden <= 0 || d->head_dim <= 0 || d->n_heads <= 0) return CKV_E_INVAL;
-  if (!(d->rope_base > 0.0) || !(d->norm_eps >= 0.f) || !(d->softmax_scale >= 0.f)) return CKV_E_INVAL;
+  if (!(d->rope_base > 0.0) || !(d->rope_base_comp >= 0.0) || !(d->norm_eps >= 0.f) ||
+      !(d->softmax_scale >= 0.f))
+    return CKV_E_INVAL;
   if (d->ratio != 0 && d->ratio != 4 && d->ratio != 128) return CKV_E_UNSUPPORTED;
   if (d->n_rot != 64 || d->swa != 128) return CKV_E_UNSUPPORTED;
   if (d->head_dim < 64 || d->head_dim > kMaxD || d->head_dim % 32) return CKV_E_UNSUPPORTED;
@@ -153,7 +159,7 @@ extern "C" int ckv_validate(const ckv_layer_desc* d) {
     if (!fmt_ok(d->idx_fmt, false)) return CKV_E_UNSUPPORTED;
     if (d->idx_dim != 64 && d->idx_dim != 128) return CKV_E_UNSUPPORTED;
     if (d->idx_heads < 1 || d->idx_heads > 64) return CKV_E_UNSUPPORTED;
-    if (d->top_k < 1 || d->top_k > 4096) return CKV_E_UNSUPPORTED;
+    if (d->top_k < 1 || d->top_k > kMaxTopK) return CKV_E_UNSUPPORTED;
   }
   return CKV_OK;
 }
@@ -166,6 +172,7 @@ extern "C" const char* ckv_strerror(int code) {
     case CKV_E_CAPACITY: return "capacity exceeded (batch, chunk, compressed rows or stage)";
     case CKV_E_WORKSPACE: return "workspace missing or too small";
     case CKV_E_HIP: return "HIP kernel launch failed";
+    case CKV_E_SEQUENCE: return "position is not the sequence's next token (host token count)";
     default: return "unknown error";
   }
 }

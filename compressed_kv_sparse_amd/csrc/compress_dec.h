@@ -13,13 +13,16 @@ namespace ckv {
 
 // ------------------------------------------------------------ row helpers
 
-// Rotate the last `nrot` entries of z[0..width) (LDS) at position `pos`.
+// Rotate the last `nrot` entries of z[0..width) (LDS) at position `pos`, in
+// the compressed class's frame (`comp`) or the raw rows' frame.
 // Caller synchronises before and after.
-__device__ __forceinline__ void rope_lds(const LayerParams& P, float* z, int width, int nrot, double pos) {
+__device__ __forceinline__ void rope_lds(const LayerParams& P, float* z, int width, int nrot, double pos,
+                                         bool comp) {
   const int dn = width - nrot;
   for (int j = threadIdx.x; j < nrot / 2; j += blockDim.x) {
     float c, s;
-    rope_cs(P, j, pos, &c, &s);
+    if (comp) rope_cs_c(P, j, pos, &c, &s);
+    else rope_cs(P, j, pos, &c, &s);
     const float a = z[dn + 2 * j], b = z[dn + 2 * j + 1];
     z[dn + 2 * j] = a * c - b * s;
     z[dn + 2 * j + 1] = a * s + b * c;
@@ -172,6 +175,19 @@ __device__ __forceinline__ float2 rope2t(float2 z, int c, int width, int nrot, c
   return make_float2(z.x * cs[j] - z.y * sn[j], z.x * sn[j] + z.y * cs[j]);
 }
 
+// Sequence check of a decode step (cache->n_tokens): the token at p is stored
+// when p is the sequence's next position or its last one (a re-run of that
+// step).  `nt` is n_tokens[b], read by every thread before the block's first
+// barrier; the update to p + 1 comes after a later barrier.
+__device__ __forceinline__ int seq_tokens(const Cache& cc, int b, int p) {
+  const int nt = cc.n_tokens ? cc.n_tokens[b] : p;
+  asm volatile("" : : "s"(nt) : "memory");   // the load completes here, ahead of any barrier
+  return nt;
+}
+__device__ __forceinline__ bool seq_ok(const Cache& cc, int p, int nt) {
+  return !cc.n_tokens || p == nt || p == nt - 1;
+}
+
 // Pool channels (c, c+1) of row i over its window.  Token p's own values come
 // from registers; the other W-1 tokens from the state ring.  Loads go out in
 // groups of 8 slots before the group is accumulated.
@@ -257,6 +273,7 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
 
   // this token's inputs and, on c4a, the whole ring: one round of loads
   const int p = pos[b];
+  const int nt = seq_tokens(cc, b, p);
   const float2 uu = load2<ACTF>(u, (long)b * d + c);
   // projection partials (at most MAXS K slices), summed in slice order
   float2 ka = make_float2(0.f, 0.f), sa = ka, kia = ka, sia = ka;
@@ -432,18 +449,19 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
   // pooling (whose arithmetic is harmless for p < 0), not before the loads:
   // a branch there lets the compiler sink loads below it, and the wait for a
   // late load is a wait for everything issued before it.
-  if (p < 0) {
-    if (tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_BAD_POS);
+  if (p < 0 || !seq_ok(cc, p, nt)) {
+    if (tid == 0 && cc.status) atomicOr(&cc.status[b], p < 0 ? CKV_STATUS_BAD_POS : CKV_STATUS_SEQUENCE);
     return -1;
   }
-  // RoPE tables: wave 0 computes pair tid % 32 at p (lanes 0-31) and at i r
-  // (lanes 32-63); read after the barrier below
+  // RoPE tables: wave 0 computes pair tid % 32 at p in the raw frame (lanes
+  // 0-31) and at i r in the compressed frame (lanes 32-63); read after the
+  // barrier below
   if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
-    // theta of pair tid % 32 selected from scalar loads of the whole table (a
+    // theta of pair tid % 32 selected from scalar loads of the whole tables (a
     // per-lane load would be one more vector load to wait for)
     double theta = 0.0;
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) theta = (tid & 31) == jj ? P.theta[jj] : theta;
+    for (int jj = 0; jj < 32; ++jj) theta = (tid & 31) == jj ? (tid < 32 ? P.theta[jj] : P.theta_c[jj]) : theta;
     float cs, sn;
     rope_cs_theta(theta, tid < 32 ? (double)p : (double)((p + 1) / r * r - r), &cs, &sn);
     if (tid < 64) {
@@ -452,6 +470,7 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
     }
   }
   lds_barrier();                // rtab complete
+  if (tid == 0 && cc.n_tokens) cc.n_tokens[b] = p + 1;   // every thread read it before the barrier
 
   // ---- raw sliding-window row: u rotated at p into slot p % swa
   {
@@ -576,6 +595,8 @@ __device__ __forceinline__ float pool_c4a(const float (&rk)[8], const float (&rs
 // red: 64 floats of LDS (16-byte aligned); rtab: 128 floats of LDS (RoPE cos
 // and sin at p and at the row position, as for compress_decode_seq); issue()
 // as there.
+// rtab: 192 floats (cos / sin of pair j at p raw, at 4 i compressed, at p
+// compressed: [j], [64 + j]; [32 + j], [96 + j]; [128 + j], [160 + j]).
 template <int KVF, int IDXF, int ACTF, typename Issue>
 __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weights& w, const Cache& cc,
                                                 const void* __restrict__ u, const int32_t* __restrict__ pos,
@@ -598,6 +619,7 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
   // partials, in slice order; slices past `splits` re-read the last and
   // count zero) and raw input, the ring, the APE rows and the RMSNorm gain
   const int p = pos[b];
+  const int nt = seq_tokens(cc, b, p);
   float ka = 0.f, sa = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -623,17 +645,23 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
   const int i = (p + 1) / 4 - 1;
   const bool pool = emit && i < P.cap;
   const int t0 = 4 * i - 4, cur = p & 7;
-  // RoPE tables (wave 0): pair j at p and at the row position 4 i
+  // RoPE tables (wave 0): pair j at p (raw frame) and at the row position
+  // 4 i (compressed frame)
   if (wave == 0) {
     double theta = 0.0;
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) theta = (tid & 31) == jj ? P.theta[jj] : theta;
+    for (int jj = 0; jj < 32; ++jj) theta = (tid & 31) == jj ? (tid < 32 ? P.theta[jj] : P.theta_c[jj]) : theta;
     float cs, sn;
     rope_cs_theta(theta, tid < 32 ? (double)p : (double)(4 * i), &cs, &sn);
     if (tid < 64) {
       rtab[tid] = cs;
       rtab[64 + tid] = sn;
     }
+  } else if (wave == 1 && lane < 32) {   // pair j at p in the compressed frame (the indexer query)
+    float cs, sn;
+    rope_cs_c(P, lane, (double)p, &cs, &sn);
+    rtab[128 + lane] = cs;
+    rtab[160 + lane] = sn;
   }
   float y = 0.f;
   if (wave < nact) {
@@ -665,11 +693,12 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
       }
     }
   }
-  if (p < 0) {
-    if (tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_BAD_POS);
+  if (p < 0 || !seq_ok(cc, p, nt)) {
+    if (tid == 0 && cc.status) atomicOr(&cc.status[b], p < 0 ? CKV_STATUS_BAD_POS : CKV_STATUS_SEQUENCE);
     return -1;
   }
   if (emit && i >= P.cap && tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_CAPACITY);
+  if (tid == 0 && cc.n_tokens) cc.n_tokens[b] = p + 1;   // every thread read it before the barrier above
   if (wave < nact) {
     // raw sliding-window row: u rotated at p, slot p % swa (attention waves)
     const float zr = rope1t(uu, col, d, P.n_rot, rtab, rtab + 64);

@@ -3,20 +3,32 @@
 // rows and the selected compressed rows; vLLM DeepSeek V4 page: the same
 // vector is key and value, and the output tail is rotated back by -p).
 //
-// Row list of a query at p: raw positions max(0, p-swa+1) .. p, then
+// Row list of a query at p: swa (= 128) raw slots first, slot j holding
+// position t = p - swa + 1 + j (skipped while t < 0, so that every 32-row tile
+// holds one row class only), then
 //   ratio 4   : the top-k list (entries < 0 skipped, the list ends at the first
 //               entry >= V),
 //   ratio 128 : rows 0 .. V-1,
 //   ratio 0   : nothing.
 // The list is cut into splits; each block runs the online softmax over its
 // split and either finishes the output (one split) or leaves (max, sum,
-// unnormalised output) for the merge kernel.
+// normalised output) for the merge kernel.
+//
+// Rotation frames.  Raw rows carry their position in the raw class's frame
+// (base theta), compressed rows in the compressed class's frame (theta_c;
+// the same when the layer has one base).  The query is rotated at p into the
+// frame of the split's first row class; when a split crosses from the raw
+// slots into the compressed entries, the query tail and the accumulated output
+// tail are both turned by p (theta_c - theta), which moves them into the
+// compressed frame (the output is linear in the rows, and a rotation commutes
+// with the softmax rescaling).  Each split rotates its output back by -p in
+// the frame it ended in, so the merge only adds.
 #include "ckv_device.h"
 
 namespace ckv {
 
 struct AttnQuery {
-  int seq, p, V, n_raw, n_list;
+  int seq, p, V, n_list;
 };
 
 __device__ __forceinline__ AttnQuery attn_query(const LayerParams& P, const int32_t* pos, int seq_fixed,
@@ -25,12 +37,11 @@ __device__ __forceinline__ AttnQuery attn_query(const LayerParams& P, const int3
   a.seq = pos ? qn : seq_fixed;
   a.p = pos ? pos[qn] : pos0 + qn;
   if (a.p < 0) {
-    a.V = a.n_raw = a.n_list = 0;
+    a.V = a.n_list = 0;
     return a;
   }
   a.V = P.ratio ? min((a.p + 1) / P.ratio, P.cap) : 0;
-  a.n_raw = min(P.swa, a.p + 1);
-  a.n_list = a.n_raw + (P.ratio == 4 ? P.topk : P.ratio == 128 ? a.V : 0);
+  a.n_list = P.swa + (P.ratio == 4 ? P.topk : P.ratio == 128 ? a.V : 0);
   return a;
 }
 
@@ -38,12 +49,13 @@ __device__ __forceinline__ AttnQuery attn_query(const LayerParams& P, const int3
 __device__ __forceinline__ const uint8_t* attn_row(const LayerParams& P, const Cache& c, const AttnQuery& a,
                                                    bool decode, int pos0, const int32_t* tk, int tk_end,
                                                    int j) {
-  if (j < a.n_raw) {
-    const int t = a.p - a.n_raw + 1 + j;
+  if (j < P.swa) {
+    const int t = a.p - P.swa + 1 + j;
+    if (t < 0) return nullptr;
     if (decode) return c.raw + ((size_t)a.seq * P.swa + t % P.swa) * P.row_bytes;
     return c.stage + (size_t)(t - pos0 + P.swa - 1) * P.row_bytes;
   }
-  const int jj = j - a.n_raw;
+  const int jj = j - P.swa;
   int row;
   if (P.ratio == 4) {
     if (jj >= tk_end) return nullptr;
@@ -63,6 +75,14 @@ __device__ __forceinline__ int topk_end(const int32_t* tk, int k, int V, int* sm
     if (tk[j] >= V) atomicMin(smem, j);
   __syncthreads();
   return *smem;
+}
+
+// (a, b) <- rotation of the pair by the angle whose cos / sin are (c, s);
+// s < 0 turns backwards.
+__device__ __forceinline__ void rot2(float& a, float& b, float c, float s) {
+  const float x = a * c - b * s, y = a * s + b * c;
+  a = x;
+  b = y;
 }
 
 // ----------------------------------------------------------------- MFMA
@@ -91,22 +111,30 @@ __device__ __forceinline__ int topk_end(const int32_t* tk, int k, int V, int* sm
 // fp16 (MFMA f16 x f16 -> fp32).  E4M3 codes are exact in fp16 and a row's
 // scale multiplies the non-RoPE logit part and, for PV, the probability
 // operand of the non-RoPE channels; bf16 values convert to fp16 with 2^-11
-// relative rounding (stored rows are RMS-normalised or activation-sized, far
-// inside the fp16 range).  Probabilities lie in [0, e^8].
+// relative rounding.  Probabilities lie in [0, e^8].
+// Range guard: a bf16 value at or above 65520 in magnitude has no fp16 image
+// (it becomes infinite), which makes the logits of its row non-finite.  Every
+// lane checks the logits of the rows it holds; when any logit of the split is
+// non-finite the block recomputes the split in fp32 (k_attn_tile's second
+// half), so such inputs cost time, not accuracy.  Small values need no guard:
+// below 2^-14 fp16 keeps an absolute error under 2^-25, far inside the
+// comparison's absolute tolerance.
 //
 // The block first lays out its split's row list in LDS as 64-bit row
-// addresses (bit 0 set: skipped entry, an all-zero row stands in).  Staging
-// is coalesced: consecutive lanes load consecutive 16-byte chunks of one
-// stored row and convert them into the row-major tile.  The tile is
-// double-buffered: tile t is multiplied from one buffer while tile t + 1 is
-// written into the other, two barriers per tile.  Global loads are
-// unconditional and sit outside any branch, so the compiler waits only for
-// the tile being committed; two tiles' loads are in flight while a tile is
-// multiplied.  The wave index comes from readfirstlane, so branches on the
-// wave's role (around MFMAs) are scalar branches, and the barriers inside the
-// loop order LDS only (lds_barrier).
+// addresses (bit 0 set: skipped entry, an all-zero row stands in); on ratio
+// 128 the compressed entries are computed instead (row jj at index jj), so
+// the table holds at most the raw slots and a top-k list.  Staging is
+// coalesced: consecutive lanes load consecutive 16-byte chunks of one stored
+// row and convert them into the row-major tile.  The tile is double-buffered:
+// tile t is multiplied from one buffer while tile t + 1 is written into the
+// other, two barriers per tile.  Global loads are unconditional and sit
+// outside any branch, so the compiler waits only for the tile being
+// committed; two tiles' loads are in flight while a tile is multiplied.  The
+// wave index comes from readfirstlane, so branches on the wave's role (around
+// MFMAs) are scalar branches, and the barriers inside the loop order LDS only
+// (lds_barrier).
 namespace attn {
-constexpr int D = 512, DN = 448, R = 32;
+constexpr int D = 512, DN = 448, R = 32, SWA = 128;
 constexpr int NT = 512;     // threads per block
 constexpr int KP = D + 16;  // row-major row stride (16-bit elements)
 // Element e of tile row R: row stride 528 elements (1056 bytes, 8 banks of
@@ -116,8 +144,9 @@ constexpr int KP = D + 16;  // row-major row stride (16-bit elements)
 // one chunk; rows r and r + 4, 32 banks apart by the stride, differ by the
 // XOR).
 __device__ __forceinline__ int tix(int R, int e) { return R * KP + ((((e >> 3) ^ (R >> 2)) & 1) | (e >> 3 & ~1)) * 8 + (e & 7); }
-constexpr int MAXK = 4096;
-constexpr int MAXL = 128 + MAXK + 4 * R;   // row-list entries of one split (+ padding tiles)
+constexpr int MAXK = 2048;                   // top-k entries (the layer check caps top_k here)
+constexpr int MAXL = SWA + MAXK + 4 * R;     // row-table entries of one split (+ padding tiles)
+constexpr int RAW_TILES = SWA / R;           // the raw slots fill the first four tiles
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -126,6 +155,8 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
 }
+__device__ __forceinline__ float lo_f16(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
+__device__ __forceinline__ float hi_f16(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 // 8 bf16 values -> 8 fp16 values
@@ -176,7 +207,9 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   __shared__ __attribute__((aligned(16))) float St[4][2][4][64];   // RoPE-tail logits per head group
   __shared__ uint64_t rtab[MAXL];                                  // row addresses of the split
   __shared__ __attribute__((aligned(16))) float rsc[2][R];
-  __shared__ float cs_[32], sn_[32];
+  // cos / sin tables of pair j: [0] at p in the raw frame, [1] at p in the
+  // compressed frame, [2] the frame switch (angle p (theta_c - theta))
+  __shared__ float cs_[3][32], sn_[3][32];
   __shared__ int tk_lim;
 
   const int qn = blockIdx.x / nsplit, split = blockIdx.x - qn * nsplit;
@@ -194,6 +227,11 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   const int nent = (ntiles + 4) * R;   // table entries incl. the padding tiles the loop issues
   const int K = (P.ratio == 4 && topk) ? P.topk : 0;
   const uint8_t* dummy = g_attn_zero_row;
+  const int tile0 = j0 / R;                                  // list tile of the split's first tile
+  const bool start_comp = tile0 >= RAW_TILES;
+  const bool switches = P.two_bases && !start_comp && tile0 + ntiles > RAW_TILES;
+  const bool end_comp = tile0 + ntiles > RAW_TILES;          // frame of the split's output
+  const bool inv = !(P.flags & CKV_FLAG_NO_INV_ROPE);
 
   // ---- the split's row list -> rtab.  The top-k list ends at its first
   // entry >= V; entries < 0 are skipped.
@@ -210,27 +248,32 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       if (tid + NT * e < K && tkv[e] >= A.V) first = min(first, tid + NT * e);
     if (first < K) atomicMin(&tk_lim, first);
   }
-  if (tid < 32) rope_cs(P, tid, (double)max(A.p, 0), &cs_[tid], &sn_[tid]);
+  if (tid < 96) {
+    const int j = tid & 31, f = tid >> 5;
+    float c, sn;
+    if (f == 0) rope_cs(P, j, (double)max(A.p, 0), &c, &sn);
+    else if (f == 1) rope_cs_c(P, j, (double)max(A.p, 0), &c, &sn);
+    else rope_cs_switch(P, j, (double)max(A.p, 0), &c, &sn);
+    cs_[f][j] = c;
+    sn_[f][j] = sn;
+  }
   __syncthreads();
   const int tk_end = tk_lim;
-  for (int x = tid; x < nent; x += NT) {   // raw window entries, padding
+  for (int x = tid; x < min(nent, MAXL); x += NT) {   // raw slots, padding
     const int j = j0 + x;
+    const int t = A.p - SWA + 1 + j;
     uint64_t v = (uint64_t)dummy | 1u;
-    if (j < j1 && j < A.n_raw) {
-      const int t = A.p - A.n_raw + 1 + j;
+    if (j < j1 && j < SWA && t >= 0)
       v = (uint64_t)(decode ? cc.raw + ((size_t)A.seq * P.swa + (t & (P.swa - 1))) * P.row_bytes
                             : cc.stage + (size_t)(t - pos0 + P.swa - 1) * P.row_bytes);
-    } else if (j < j1 && P.ratio == 128) {
-      v = (uint64_t)(cc.comp + ((size_t)A.seq * P.cap + (j - A.n_raw)) * P.row_bytes);
-    }
-    if (!(j < j1 && j >= A.n_raw && P.ratio == 4)) rtab[x] = v;
+    if (!(j < j1 && j >= SWA && P.ratio == 4)) rtab[x] = v;
   }
   if (K) {   // top-k entries of this split, from the registers that hold them
 #pragma unroll
     for (int e = 0; e < MAXK / NT; ++e) {
       const int jj = tid + NT * e;
-      const int x = A.n_raw + jj - j0;
-      if (jj < K && x >= 0 && A.n_raw + jj < j1) {
+      const int x = SWA + jj - j0;
+      if (jj < K && x >= 0 && SWA + jj < j1) {
         const int row = tkv[e];
         const bool ok = jj < tk_end && row >= 0 && row < A.V;
         rtab[x] = ok ? (uint64_t)(cc.comp + ((size_t)A.seq * P.cap + row) * P.row_bytes) : ((uint64_t)dummy | 1u);
@@ -238,6 +281,16 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     }
   }
   __syncthreads();
+  // address of split entry x: from the table, or (ratio 128 compressed
+  // entries) computed; both evaluated, so the caller's loads stay unconditional
+  auto addr_of = [&](int x) -> uint64_t {
+    const uint64_t tv = rtab[min(x, MAXL - 1)];
+    if (P.ratio != 128) return tv;
+    const int j = j0 + x, jj = j - SWA;
+    const uint64_t cv = (j < j1 && jj < A.V) ? (uint64_t)(cc.comp + ((size_t)A.seq * P.cap + jj) * P.row_bytes)
+                                             : ((uint64_t)dummy | 1u);
+    return j >= SWA ? cv : tv;
+  };
 
   // staging: item e of this thread is chunk it % CPR of tile row it / CPR,
   // it = tid + NT e; items past the tile read the zero row and are dropped.
@@ -252,11 +305,11 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     for (int e = 0; e < IT; ++e) {
       const int it = tid + NT * e;
       const int row = min(it / CPR, R - 1), ch = it % CPR;
-      const uint64_t ra = rtab[tile * R + row];
+      const uint64_t ra = addr_of(tile * R + row);
       const int off = !F8 ? 16 * ch : (ch < 28 ? 16 * ch : DN + 16 * (ch - 28));
       S.v[e] = *(const u32x4*)((const uint8_t*)(ra & ~(uint64_t)1) + off);
     }
-    const uint64_t rs = rtab[tile * R + (tid & 31)];
+    const uint64_t rs = addr_of(tile * R + (tid & 31));
     S.s = F8 ? *(const float*)((const uint8_t*)(rs & ~(uint64_t)1) + DN + 128) : 1.f;
     S.sok = !(rs & 1u);
   };
@@ -287,10 +340,11 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   };
 
   // rotated query of this lane's head in fp16, channels 256 cg + 32 ks + 8 g
-  // .. +7 (B operand)
+  // .. +7 (B operand), in the frame of the split's first row class
   Stg S0, S1;
   u32x4 Bq[8];
   {
+    const int f0 = start_comp ? 1 : 0;
     const uint16_t* qr = q + ((size_t)qn * H + head) * D + 256 * cg + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) Bq[ks] = *(const u32x4*)(qr + 32 * ks);
@@ -304,8 +358,9 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
         const int jb = (32 * ks + 8 * g + 256 - DN) / 2;   // first pair index of this chunk
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float a = lo_bf16(v[e]), b = hi_bf16(v[e]);
-          v[e] = pk_f16(a * cs_[jb + e] - b * sn_[jb + e], a * sn_[jb + e] + b * cs_[jb + e]);
+          float a = lo_bf16(v[e]), b = hi_bf16(v[e]);
+          rot2(a, b, cs_[f0][jb + e], sn_[f0][jb + e]);
+          v[e] = pk_f16(a, b);
         }
       } else {
         v = bf16x8_to_f16(v);
@@ -315,6 +370,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   }
 
   float m_i = -INFINITY, l_i = 0.f;
+  bool bad = false;   // a logit of a row this lane holds was not finite
   f32x4 O[16];
 #pragma unroll
   for (int n = 0; n < 16; ++n) O[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -322,6 +378,35 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   // transpose-read addresses: lane 16 g + 4 j + a reads row base + j,
   // channels ch0 + 4 a .. + 3 (base 4 g, then 16 + 4 g)
   const int tr_row = 4 * g + ((lane & 15) >> 2), tr_col = 4 * (lane & 3);
+
+  // raw slots -> compressed entries: the query tail and the output tail turn
+  // by p (theta_c - theta) (tail waves only; channels 448 + 16 (n - 12) + 4 g
+  // + i of O[n] are pairs 8 (n - 12) + 2 g + i / 2)
+  auto frame_switch = [&]() {
+    if (!tailw) return;
+#pragma unroll
+    for (int ks = 6; ks < 8; ++ks) {
+      const int jb = (32 * ks + 8 * g + 256 - DN) / 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float a = lo_f16(Bq[ks][e]), b = hi_f16(Bq[ks][e]);
+        rot2(a, b, cs_[2][jb + e], sn_[2][jb + e]);
+        Bq[ks][e] = pk_f16(a, b);
+      }
+    }
+    if (inv) {
+#pragma unroll
+      for (int n = 12; n < 16; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const int jp = 8 * (n - 12) + 2 * g + i / 2;
+          float a = O[n][i], b = O[n][i + 1];
+          rot2(a, b, cs_[2][jp], sn_[2][jp]);
+          O[n][i] = a;
+          O[n][i + 1] = b;
+        }
+    }
+  };
 
   auto tile_math = [&](int buf) {
     const uint16_t* kb = Ks[buf];
@@ -363,7 +448,9 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       const f32x4 sc = *(const f32x4*)&rsc[buf][16 * nt + 4 * g];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Sv[nt][i] = sc[i] < 0.f ? -INFINITY : ((n0[i] + n1[i]) * sc[i] + tl[i]) * scale;
+        const float lg = ((n0[i] + n1[i]) * sc[i] + tl[i]) * scale;
+        bad |= sc[i] >= 0.f && !(fabsf(lg) <= 3.4e38f);
+        Sv[nt][i] = sc[i] < 0.f ? -INFINITY : lg;
         mx = fmaxf(mx, Sv[nt][i]);
       }
     }
@@ -424,6 +511,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   // halves), and one barrier per tile publishes the next buffer.  bf16 rows
   // keep two tiles' loads in flight in registers (S0, S1); E4M3 rows one
   // (S0 only: with the conversion temporaries a second set would spill).
+  // The frame switch runs before the first compressed tile (a scalar branch).
   constexpr bool TWO = !F8;
   pin(S0);
   commit(S0, 0);
@@ -431,6 +519,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   else issue(S0, 1);
   lds_barrier();
   for (int t = 0; t < ntiles; t += 2) {
+    if (switches && tile0 + t == RAW_TILES) frame_switch();
     tile_math(0);
     if (TWO) {
       pin(S1);
@@ -442,57 +531,170 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       issue(S0, t + 2);
     }
     lds_barrier();
-    if (t + 1 < ntiles) tile_math(1);
+    if (t + 1 < ntiles) {
+      if (switches && tile0 + t + 1 == RAW_TILES) frame_switch();
+      tile_math(1);
+    }
     pin(S0);
     commit(S0, 0);
     issue(S0, TWO ? t + 4 : t + 3);
     lds_barrier();
   }
 
-  // lane (r, g) holds channels 256 cg + 16 n + 4 g + i of head `head`
+  const int fe = end_comp ? 1 : 0;   // frame the output ended in
+  if (__syncthreads_or(bad)) {
+    // ---- range guard: the split again, in fp32, from the stored rows.  Four
+    // passes of 16 heads, 32 threads per head, thread `sub` holding channels
+    // 16 sub .. +15 (subs 28..31 hold the RoPE tail, pairs 8 (sub - 28) ..).
+    const int hh = tid >> 5, sub = tid & 31, c0 = 16 * sub;
+    const bool tl = c0 >= DN;
+    const int jq = tl ? (c0 - DN) / 2 : 0;
+    const int f0 = start_comp ? 1 : 0;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int hd = blockIdx.y * 64 + 16 * pass + hh;
+      float qv[16], acc[16];
+      {
+        const u32x4* qr = (const u32x4*)(q + ((size_t)qn * H + hd) * D + c0);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const u32x4 w = qr[h2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float a = lo_bf16(w[i]), b = hi_bf16(w[i]);
+            if (tl) rot2(a, b, cs_[f0][jq + 4 * h2 + i], sn_[f0][jq + 4 * h2 + i]);
+            qv[8 * h2 + 2 * i] = a * scale;
+            qv[8 * h2 + 2 * i + 1] = b * scale;
+          }
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+      float m = -INFINITY, l = 0.f;
+      for (int x = 0; x < ntiles * R; ++x) {
+        if (switches && x == (RAW_TILES - tile0) * R && tl) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            rot2(qv[2 * e], qv[2 * e + 1], cs_[2][jq + e], sn_[2][jq + e]);
+            if (inv) rot2(acc[2 * e], acc[2 * e + 1], cs_[2][jq + e], sn_[2][jq + e]);
+          }
+        }
+        const uint64_t ra = addr_of(x);
+        if (ra & 1u) continue;
+        const uint8_t* rp = (const uint8_t*)ra;
+        float v[16];
+        if (!F8 || tl) {
+          const u32x4* src = (const u32x4*)(F8 ? rp + DN + 2 * (c0 - DN) : rp + 2 * c0);
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const u32x4 w = src[h2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[8 * h2 + 2 * i] = lo_bf16(w[i]);
+              v[8 * h2 + 2 * i + 1] = hi_bf16(w[i]);
+            }
+          }
+        } else {
+          const float sr = *(const float*)(rp + DN + 128);
+          const u32x4 w = *(const u32x4*)(rp + c0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = e4m3_to_f32((w[i >> 2] >> (8 * (i & 3))) & 0xffu) * sr;
+        }
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dot += qv[i] * v[i];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) dot += __shfl_xor(dot, o, 64);
+        const float mn = fmaxf(m, dot);
+        const float f = __expf(m - mn), pw = __expf(dot - mn);
+        l = l * f + pw;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = acc[i] * f + pw * v[i];
+        m = mn;
+      }
+      const float il = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[c] *= il;
+      if (tl && inv) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rot2(acc[2 * e], acc[2 * e + 1], cs_[fe][jq + e], -sn_[fe][jq + e]);
+      }
+      if (nsplit == 1) {
+#pragma unroll
+        for (int c = 0; c < 16; c += 2)
+          *(uint32_t*)&out[((size_t)qn * H + hd) * D + c0 + c] = pack_bf16x2(acc[c], acc[c + 1]);
+        continue;
+      }
+      // partial: the normalised output times 2^-e (e chosen so that the
+      // head's largest magnitude stays below 2^15) as two fp16 halves, the
+      // high one in the usual place and the low-order remainder in the second
+      // half of the partial buffer (about 22 significant bits: values this
+      // large can cancel in the merge); the merge multiplies by 2^e
+      float amax = 0.f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(acc[c]));
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      int ex = 0;
+      if (amax >= 16384.f) (void)frexpf(amax, &ex);
+      const float down = ldexpf(1.f, -ex);
+      const size_t pb = ((size_t)qn * nsplit + split) * H + hd;
+      const size_t lo_half = (size_t)gridDim.x * H * D;   // fp16 entries of the high halves
+      uint16_t* ph = (uint16_t*)part_o;
+#pragma unroll
+      for (int c = 0; c < 16; c += 2) {
+        const float a = acc[c] * down, b = acc[c + 1] * down;
+        const uint32_t hi = pk_f16(a, b);
+        *(uint32_t*)&ph[pb * D + c0 + c] = hi;
+        *(uint32_t*)&ph[lo_half + pb * D + c0 + c] = pk_f16(a - lo_f16(hi), b - hi_f16(hi));
+      }
+      if (sub == 0) *(float4*)(part_ml + pb * 4) = make_float4(m, l, ldexpf(1.f, ex), 1.f);
+    }
+    return;
+  }
+
+  // lane (r, g) holds channels 256 cg + 16 n + 4 g + i of head `head`;
+  // normalise and rotate the tail back by -p in the frame the split ended in
+  const float il = l_i > 0.f ? 1.f / l_i : 0.f;
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    O[n] *= il;
+    if (tailw && n >= 12 && inv) {
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const int jp = 8 * (n - 12) + 2 * g + i / 2;
+        float a = O[n][i], b = O[n][i + 1];
+        rot2(a, b, cs_[fe][jp], -sn_[fe][jp]);
+        O[n][i] = a;
+        O[n][i + 1] = b;
+      }
+    }
+  }
   if (nsplit == 1) {
-    // finish: normalise, rotate the tail back by -p, store bf16
-    const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
       const int ch = 256 * cg + 16 * n + 4 * g;
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = O[n][i] * inv;
-      if (tailw && n >= 12 && !(P.flags & CKV_FLAG_NO_INV_ROPE)) {
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const int jp = (ch + i - DN) >> 1;
-          // rotation by -p: (a, b) -> (a cos + b sin, -a sin + b cos)
-          const float x = v[i] * cs_[jp] + v[i + 1] * sn_[jp], y = -v[i] * sn_[jp] + v[i + 1] * cs_[jp];
-          v[i] = x;
-          v[i + 1] = y;
-        }
-      }
-      u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      u32x2 w = {pack_bf16x2(O[n][0], O[n][1]), pack_bf16x2(O[n][2], O[n][3])};
       *(u32x2*)&out[((size_t)qn * H + head) * D + ch] = w;
     }
     return;
   }
   // partial: this split's normalised output O / l in fp16 (half the bytes of
-  // fp32 to write here and to read in the merge), plus (m, l)
+  // fp32 to write here and to read in the merge), plus (m, l, 1)
   const size_t pb = ((size_t)qn * nsplit + split) * H + head;
-  const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
   uint16_t* ph = (uint16_t*)part_o;
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
-    const u32x2 w = {pk_f16(O[n][0] * inv, O[n][1] * inv), pk_f16(O[n][2] * inv, O[n][3] * inv)};
+    const u32x2 w = {pk_f16(O[n][0], O[n][1]), pk_f16(O[n][2], O[n][3])};
     *(u32x2*)&ph[pb * D + 256 * cg + 16 * n + 4 * g] = w;
   }
-  if (g == 0 && cg == 0) {
-    part_ml[pb * 2] = m_i;
-    part_ml[pb * 2 + 1] = l_i;
-  }
+  if (g == 0 && cg == 0) *(float4*)(part_ml + pb * 4) = make_float4(m_i, l_i, 1.f, 0.f);
 }
 
 // ----------------------------------------------------------------- vector
 // Any formats.  Block of 256 = 16 heads x 16 lanes; lane `sub` owns channels
-// [sub*dpt, (sub+1)*dpt).  grid (queries, splits, H / 16).
+// [sub*dpt, (sub+1)*dpt).  grid (queries, splits, H / 16).  Leaves the
+// split's unnormalised output, rotated back by -p in the frame it ended in,
+// and (max, sum, 1).
 template <int KVF, int ACTF>
 __global__ __launch_bounds__(256) void k_attn_vec(LayerParams P, Cache cc, const void* __restrict__ q,
                                                   const int32_t* __restrict__ pos, int seq_fixed, int pos0,
@@ -510,6 +712,10 @@ __global__ __launch_bounds__(256) void k_attn_vec(LayerParams P, Cache cc, const
   const int32_t* tk = (P.ratio == 4 && topk) ? topk + (size_t)qn * P.topk : nullptr;
   int tk_end = 0;
   if (tk) tk_end = topk_end(tk, P.topk, A.V, &tk_lim);
+  const bool start_comp = j0 >= P.swa, end_comp = j1 > P.swa;
+  const bool switches = P.two_bases && !start_comp && end_comp;
+  const bool inv = !(P.flags & CKV_FLAG_NO_INV_ROPE);
+  const double pp = (double)max(A.p, 0);
 
   float qv[32], acc[32];
   const int c0 = sub * dpt;
@@ -518,10 +724,9 @@ __global__ __launch_bounds__(256) void k_attn_vec(LayerParams P, Cache cc, const
     float a = load_val<ACTF>(q, o), b = load_val<ACTF>(q, o + 1);
     if (c0 + e >= dn) {
       float cs, sn;
-      rope_cs(P, (c0 + e - dn) / 2, (double)A.p, &cs, &sn);
-      const float x = a * cs - b * sn, y = a * sn + b * cs;
-      a = x;
-      b = y;
+      if (start_comp) rope_cs_c(P, (c0 + e - dn) / 2, pp, &cs, &sn);
+      else rope_cs(P, (c0 + e - dn) / 2, pp, &cs, &sn);
+      rot2(a, b, cs, sn);
     }
     qv[e] = a * P.scale;
     qv[e + 1] = b * P.scale;
@@ -529,6 +734,15 @@ __global__ __launch_bounds__(256) void k_attn_vec(LayerParams P, Cache cc, const
   }
   float m = -INFINITY, l = 0.f;
   for (int j = j0; j < j1; ++j) {
+    if (switches && j == P.swa) {   // raw slots -> compressed entries: change frame
+      for (int e = 0; e < dpt; e += 2) {
+        if (c0 + e < dn) continue;
+        float cs, sn;
+        rope_cs_switch(P, (c0 + e - dn) / 2, pp, &cs, &sn);
+        rot2(qv[e], qv[e + 1], cs, sn);
+        if (inv) rot2(acc[e], acc[e + 1], cs, sn);
+      }
+    }
     const uint8_t* rp = attn_row(P, cc, A, decode, pos0, tk, tk_end, j);
     if (!rp) continue;
     float rv[32];
@@ -551,41 +765,49 @@ __global__ __launch_bounds__(256) void k_attn_vec(LayerParams P, Cache cc, const
     for (int e = 0; e < dpt; ++e) acc[e] = acc[e] * f + pw * rv[e];
     m = mn;
   }
+  if (inv) {   // rotate back by -p in the frame the split ended in
+    for (int e = 0; e < dpt; e += 2) {
+      if (c0 + e < dn) continue;
+      float cs, sn;
+      if (end_comp) rope_cs_c(P, (c0 + e - dn) / 2, pp, &cs, &sn);
+      else rope_cs(P, (c0 + e - dn) / 2, pp, &cs, &sn);
+      rot2(acc[e], acc[e + 1], cs, -sn);
+    }
+  }
   const size_t pb = ((size_t)qn * nsplit + split) * H + h;
   for (int e = 0; e < dpt; ++e) part_o[pb * d + c0 + e] = acc[e];
-  if (sub == 0) {
-    part_ml[pb * 2] = m;
-    part_ml[pb * 2 + 1] = l;
-  }
+  if (sub == 0) *(float4*)(part_ml + pb * 4) = make_float4(m, l, 1.f, 0.f);
 }
 
 // ----------------------------------------------------------------- merge
 // grid (queries, H); block d/4 threads, each four adjacent channels.  The
-// splits' (max, sum) pairs are read once into LDS.  HALF: the partials are
-// fp16 normalised outputs O_s / l_s (tile kernel), combined with weights
-// l_s exp(m_s - M); otherwise fp32 unnormalised O_s with weights exp(m_s - M).
+// splits' (max, sum, scale) entries are read once into LDS.  HALF: the
+// partials are fp16 normalised outputs O_s / l_s times 1 / scale_s (tile
+// kernel), combined with weights l_s scale_s exp(m_s - M); otherwise fp32
+// unnormalised O_s with weights exp(m_s - M).  The splits have already
+// rotated their outputs back, so the merge only adds.
 template <int ACTF, bool HALF>
 __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml,
-                                                    const int32_t* __restrict__ pos, int pos0, int nsplit,
+                                                    const float* __restrict__ part_ml, int nsplit,
                                                     void* __restrict__ out) {
   __shared__ float wsh[kMaxSplits];
+  __shared__ float lsh[kMaxSplits];   // 1: the split also left a low-order half (fp16 partials)
   __shared__ float Lsh;
+  __shared__ int any_lo;
   const int qn = blockIdx.x, h = blockIdx.y, H = P.H, d = P.d;
   const int c = 4 * threadIdx.x;
-  const int p = pos ? pos[qn] : pos0 + qn;
   const size_t b0 = (size_t)qn * nsplit * H + h;
-  // Loads first, all unconditional (indices clamped): the splits' (max, sum)
-  // pairs (lane l of each wave: splits l + 64 e), then this thread's four
-  // channels of the first kPF splits' partials, so that one memory round trip
-  // serves both (the weights wait only for the pairs, issued first).
+  // Loads first, all unconditional (indices clamped): the splits' (max, sum,
+  // scale) entries (lane l of each wave: splits l + 64 e), then this thread's
+  // four channels of the first kPF splits' partials, so that one memory round
+  // trip serves both (the weights wait only for the entries, issued first).
   constexpr int kPF = 16;
   const int cl = min(c, d - 4);
-  float2 mlv[4];
+  float4 mlv[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int sidx = (threadIdx.x & 63) + 64 * e;
-    mlv[e] = *(const float2*)(part_ml + (b0 + (size_t)min(sidx, nsplit - 1) * H) * 2);
+    mlv[e] = *(const float4*)(part_ml + (b0 + (size_t)min(sidx, nsplit - 1) * H) * 4);
   }
   auto load_part = [&](int sp) -> float4 {
     const size_t o = (b0 + (size_t)min(sp, nsplit - 1) * H) * d + cl;
@@ -596,33 +818,42 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
       return *(const float4*)(part_o + o);
     }
   };
-  __builtin_amdgcn_sched_barrier(0);   // (keeps the pairs' loads ahead of the partials')
+  __builtin_amdgcn_sched_barrier(0);   // (keeps the entries' loads ahead of the partials')
   float4 v0[kPF];
 #pragma unroll
   for (int j = 0; j < kPF; ++j) v0[j] = load_part(j);
   {
     // max over splits with rows, then each split's weight exp(m_s - M)
-    float m[4], l[4];
-    float M = -INFINITY;
+    float m[4], l[4], sc[4];
+    float M = -INFINITY, lo_any = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {   // splits past nsplit weigh 0
       const int sidx = (threadIdx.x & 63) + 64 * e;
       const bool in = sidx < nsplit;
       m[e] = in ? mlv[e].x : -INFINITY;
       l[e] = in ? mlv[e].y : 0.f;
+      sc[e] = mlv[e].z;
       if (l[e] > 0.f) M = fmaxf(M, m[e]);
+      if (in) lo_any = fmaxf(lo_any, mlv[e].w);
     }
     M = wave_max(M);
+    lo_any = wave_max(lo_any);
     float L = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int sidx = (threadIdx.x & 63) + 64 * e;
       const float wgt = l[e] > 0.f ? __expf(m[e] - M) : 0.f;
-      if (threadIdx.x < 64 && sidx < nsplit) wsh[sidx] = HALF ? l[e] * wgt : wgt;
+      if (threadIdx.x < 64 && sidx < nsplit) {
+        wsh[sidx] = HALF ? l[e] * wgt * sc[e] : wgt;
+        lsh[sidx] = mlv[e].w;
+      }
       L += l[e] * wgt;
     }
     L = wave_sum(L);
-    if (threadIdx.x == 0) Lsh = L;
+    if (threadIdx.x == 0) {
+      Lsh = L;
+      any_lo = HALF && lo_any > 0.f;
+    }
   }
   __syncthreads();
   if (c >= d) return;
@@ -643,19 +874,20 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
 #pragma unroll
     for (int j = 0; j < 8; ++j) accum(v[j], s0 + j);
   }
-  const float inv = Lsh > 0.f ? 1.f / Lsh : 0.f;
-  float o[4] = {a.x * inv, a.y * inv, a.z * inv, a.w * inv};
-  const int dn = d - P.n_rot;
-  if (c >= dn && !(P.flags & CKV_FLAG_NO_INV_ROPE) && p >= 0) {
-#pragma unroll
-    for (int e = 0; e < 4; e += 2) {
-      float cs, sn;
-      rope_cs(P, (c + e - dn) / 2, (double)p, &cs, &sn);
-      const float x = o[e] * cs + o[e + 1] * sn, y = -o[e] * sn + o[e + 1] * cs;
-      o[e] = x;
-      o[e + 1] = y;
+  if (any_lo) {   // splits recomputed by the range guard: their low-order halves
+    const size_t lo_half = (size_t)gridDim.x * nsplit * H * d;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      if (lsh[sp] == 0.f) continue;
+      const _Float16* hp = (const _Float16*)part_o + lo_half + (b0 + (size_t)sp * H) * d + cl;
+      const float wgt = wsh[sp];
+      a.x += (float)hp[0] * wgt;
+      a.y += (float)hp[1] * wgt;
+      a.z += (float)hp[2] * wgt;
+      a.w += (float)hp[3] * wgt;
     }
   }
+  const float inv = Lsh > 0.f ? 1.f / Lsh : 0.f;
+  const float o[4] = {a.x * inv, a.y * inv, a.z * inv, a.w * inv};
   const size_t oo = ((size_t)qn * H + h) * d + c;
 #pragma unroll
   for (int e = 0; e < 4; ++e) store_val<ACTF>(out, oo + e, o[e]);
@@ -700,13 +932,13 @@ int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32
   dim3 mg(nq, P.H);
   const bool half = attn_uses_tiles(P);
   if (P.act_fmt == CKV_F32 && half)
-    hipLaunchKernelGGL((k_attn_merge<CKV_F32, true>), mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
+    hipLaunchKernelGGL((k_attn_merge<CKV_F32, true>), mg, dim3(128), 0, st, P, po, pml, ns, out);
   else if (P.act_fmt == CKV_F32)
-    hipLaunchKernelGGL((k_attn_merge<CKV_F32, false>), mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
+    hipLaunchKernelGGL((k_attn_merge<CKV_F32, false>), mg, dim3(128), 0, st, P, po, pml, ns, out);
   else if (half)
-    hipLaunchKernelGGL((k_attn_merge<CKV_BF16, true>), mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
+    hipLaunchKernelGGL((k_attn_merge<CKV_BF16, true>), mg, dim3(128), 0, st, P, po, pml, ns, out);
   else
-    hipLaunchKernelGGL((k_attn_merge<CKV_BF16, false>), mg, dim3(128), 0, st, P, po, pml, pos, pos0, ns, out);
+    hipLaunchKernelGGL((k_attn_merge<CKV_BF16, false>), mg, dim3(128), 0, st, P, po, pml, ns, out);
   return (int)hipGetLastError();
 }
 

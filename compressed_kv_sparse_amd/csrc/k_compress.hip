@@ -34,7 +34,7 @@ __global__ __launch_bounds__(1024) void k_compress_c4a(LayerParams P, Weights w,
                                                        const int32_t* __restrict__ pos,
                                                        const float* __restrict__ proj, int splits, int B) {
   __shared__ __attribute__((aligned(16))) float red[64];
-  __shared__ float rtab[128];
+  __shared__ float rtab[192];
   compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, splits, B, blockIdx.x, red, rtab, nullptr, [] {});
 }
 
@@ -46,13 +46,16 @@ __global__ __launch_bounds__(256) void k_raw_insert_decode(LayerParams P, Cache 
   const int b = blockIdx.x, c = 2 * threadIdx.x, d = P.d;
   const bool act = c < d;
   const int p = pos[b];
+  const int nt = seq_tokens(cc, b, p);
   const float2 uu = load2<ACTF>(u, (long)b * d + min(c, d - 2));
-  if (p < 0) {
-    if (threadIdx.x == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_BAD_POS);
+  if (p < 0 || !seq_ok(cc, p, nt)) {
+    if (threadIdx.x == 0 && cc.status) atomicOr(&cc.status[b], p < 0 ? CKV_STATUS_BAD_POS : CKV_STATUS_SEQUENCE);
     return;
   }
   const float2 z = rope2(P, uu, c, d, P.n_rot, p);
   store_row2<KVF>(cc.raw + ((size_t)b * P.swa + (p & (P.swa - 1))) * P.row_bytes, z, c, act, d, P.n_rot, red);
+  lds_barrier();
+  if (threadIdx.x == 0 && cc.n_tokens) cc.n_tokens[b] = p + 1;
 }
 
 // ------------------------------------------------------------ prefill
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(256) void k_stage_raw(LayerParams P, Cache cc, cons
   const int d = P.d;
   for (int c = threadIdx.x; c < d; c += blockDim.x) zs[c] = load_val<ACTF>(u, (long)(t - pos0) * d + c);
   __syncthreads();
-  rope_lds(P, zs, d, P.n_rot, (double)t);
+  rope_lds(P, zs, d, P.n_rot, (double)t, false);
   __syncthreads();
   store_row<KVF>(dst, zs, d, P.n_rot, red);
 }
@@ -94,6 +97,7 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
   __shared__ float red[16];
   const int i = i_first + blockIdx.x;
   const int d = P.d, r = P.ratio, W = P.W, DI = P.DI, nc = P.ncol;
+  if (cc.n_tokens && cc.n_tokens[seq] != pos0) return;   // out of sequence: the cache stays as it is
   const int t0 = i * r - (W - r);
   const float* skv = cc.st_kv + (size_t)seq * W * d;
   const float* ssc = cc.st_sc + (size_t)seq * W * d;
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
   }
   rmsnorm_lds(zs, d, w.gamma, P.eps, red);
   __syncthreads();
-  rope_lds(P, zs, d, P.n_rot, (double)i * r);
+  rope_lds(P, zs, d, P.n_rot, (double)i * r, true);
   __syncthreads();
   store_row<KVF>(cc.comp + ((size_t)seq * P.cap + i) * P.row_bytes, zs, d, P.n_rot, red);
   if (r != 4) return;
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
   }
   rmsnorm_lds(zi, DI, w.idx_gamma, P.eps, red);
   __syncthreads();
-  rope_lds(P, zi, DI, P.idx_rot, (double)i * r);
+  rope_lds(P, zi, DI, P.idx_rot, (double)i * r, true);
   __syncthreads();
   uint8_t* dst = (uint8_t*)cc.idx + ((size_t)seq * P.cap + i) * DI * (IDXF == CKV_F32 ? 4 : 2);
   store_vals<IDXF>(dst, zi, DI);
@@ -158,6 +162,7 @@ __global__ __launch_bounds__(256) void k_state_prefill(LayerParams P, Cache cc,
   const int j = blockIdx.x;
   const int d = P.d, nc = P.ncol, DI = P.DI;
   const int end = pos0 + T;
+  if (cc.n_tokens && cc.n_tokens[seq] != pos0) return;   // out of sequence: the cache stays as it is
   const int traw = end - P.swa + j;
   if (traw >= pos0) {
     const uint32_t* src = (const uint32_t*)(cc.stage + (size_t)(traw - pos0 + P.swa - 1) * P.row_bytes);
@@ -181,6 +186,13 @@ __global__ __launch_bounds__(256) void k_state_prefill(LayerParams P, Cache cc,
       cc.ist_sc[o] = pr[2 * d + DI + c];
     }
   }
+}
+
+// The chunk's sequence check and token count (cache->n_tokens): launched after
+// every kernel of the chunk has read the count.
+__global__ void k_advance_tokens(Cache cc, int seq, int pos0, int T) {
+  if (cc.n_tokens[seq] == pos0) cc.n_tokens[seq] = pos0 + T;
+  else if (cc.status) atomicOr(&cc.status[seq], CKV_STATUS_SEQUENCE);
 }
 
 // ------------------------------------------------------------ launchers
@@ -238,6 +250,7 @@ static void go_prefill(const LayerParams& P, const Weights& w, const Cache& c, c
                          c, part, seq, pos0, i_first);
   }
   hipLaunchKernelGGL(k_state_prefill, dim3(P.swa), dim3(256), 0, st, P, c, part, seq, pos0, T);
+  if (c.n_tokens) hipLaunchKernelGGL(k_advance_tokens, dim3(1), dim3(1), 0, st, c, seq, pos0, T);
 }
 
 int launch_compress_prefill(const LayerParams& P, const Weights& w, const Cache& c, const void* u,

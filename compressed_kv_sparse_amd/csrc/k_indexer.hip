@@ -152,7 +152,7 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
   }
   const float wl = wt[(size_t)qn * HI + min(tid, HI - 1)];
 
-  if (tid < nrot / 2) rope_cs(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
+  if (tid < nrot / 2) rope_cs_c(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
   if (tid < HP) wsh[tid] = tid < HI ? wl : 0.f;
   if constexpr (HIST)
     for (int e = tid; e < kHistBins; e += 256) lh[e] = 0;
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(64 * kPfQ) __attribute__((amdgpu_waves_per_eu(4, 4)
     }
   if (tid < kPfQ * 32) {
     const int qq = tid >> 5, j = tid & 31;
-    rope_cs(P, j, (double)(pos0 + min(n0 + qq, T - 1)), &cs_[qq][j], &sn_[qq][j]);
+    rope_cs_c(P, j, (double)(pos0 + min(n0 + qq, T - 1)), &cs_[qq][j], &sn_[qq][j]);
   }
   lds_barrier();
   // rotated query -> bf16 A fragments (heads past H_I are zero)
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(256) void k_idx_score_vec(LayerParams P, const void
   if (rb0 >= Q.V) return;
   const int tid = threadIdx.x;
   const int HI = P.HI, DI = P.DI, nrot = P.idx_rot, dn = DI - nrot;
-  if (tid < nrot / 2) rope_cs(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
+  if (tid < nrot / 2) rope_cs_c(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
   if (tid < HI) wsh[tid] = wt[(size_t)qn * HI + tid];
   if (hist)
     for (int e = tid; e < kHistBins; e += 256) lh[e] = 0;
@@ -1353,7 +1353,7 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
   __shared__ __attribute__((aligned(16))) float red[64];
   __shared__ float idx_row[kMaxDI];
   __shared__ __attribute__((aligned(16))) float hsum[64];
-  __shared__ float rtab[128];
+  __shared__ float rtab[192];
   __shared__ __attribute__((aligned(16))) uint32_t h_lds[kHistBins];
   __shared__ __attribute__((aligned(16))) uint32_t q_lds[64 * DI / 2];
   const int qn = blockIdx.x, tid = threadIdx.x;
@@ -1398,9 +1398,9 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
     for (int i = 0; i < CPT / 2; ++i) {
       float a = bf16_to_f32(q4s[i] & 0xffffu), b2 = bf16_to_f32(q4s[i] >> 16);
       const int c = c0 + 2 * i;
-      if (c >= dn) {   // the query's tail at p: the same frequencies as the raw row's
+      if (c >= dn) {   // the query's tail at p, in the compressed class's frame
         const int j = (c - dn) >> 1;
-        const float x = a * rtab[j] - b2 * rtab[64 + j], y = a * rtab[64 + j] + b2 * rtab[j];
+        const float x = a * rtab[128 + j] - b2 * rtab[160 + j], y = a * rtab[160 + j] + b2 * rtab[128 + j];
         a = x;
         b2 = y;
       }
@@ -1474,9 +1474,9 @@ int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache&
   const int MT = (P.HI + 15) / 16;
   dim3 grid(nproj + nrb * B);
   const uint16_t* ix = (const uint16_t*)c.idx;
-#define CKV_SS(MTV)                                                                                       \
-  hipLaunchKernelGGL((k_step_scan<MTV, CKV_BF16>), grid, dim3(256), 0, st, P, ix, qI, wt, pos, keys, sel.hist, \
-                     (const uint16_t*)x, B, wc, proj, nproj, nrb)
+#define CKV_SS(MTV)                                                                                         \
+  launch_score((k_step_scan<MTV, CKV_BF16>), grid, dim3(256), st, P, ix, qI, wt, pos, keys, sel.hist, \
+               (const uint16_t*)x, B, wc, proj, nproj, nrb)
   if (MT == 1) CKV_SS(1);
   else if (MT == 2) CKV_SS(2);
   else if (MT == 3) CKV_SS(3);

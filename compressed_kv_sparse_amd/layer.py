@@ -32,13 +32,14 @@ class DeviceLayer:
                  kv_fmt: str = "bf16", idx_fmt: str = "bf16", act_fmt: str = "bf16", w_fmt: str = "bf16",
                  rope_base: float = 160000.0, norm_eps: float = 1e-6, softmax_scale: float = 0.0,
                  flags: int = 0, n_rot: int = 64, swa: int = 128, max_chunk: int = 0,
-                 device: str = "cuda"):
+                 rope_base_comp: float = 0.0, track_tokens: bool = True, device: str = "cuda"):
         self.device = torch.device(device)
         self.desc = L.LayerDesc(ratio=ratio, hidden=hidden, head_dim=head_dim, n_rot=n_rot, n_heads=n_heads,
                                 swa=swa, idx_heads=idx_heads, idx_dim=idx_dim, top_k=top_k, comp_cap=comp_cap,
                                 batch=batch, kv_fmt=L.FMT[kv_fmt], idx_fmt=L.FMT[idx_fmt],
                                 act_fmt=L.FMT[act_fmt], w_fmt=L.FMT[w_fmt], flags=flags,
-                                rope_base=rope_base, norm_eps=norm_eps, softmax_scale=softmax_scale)
+                                rope_base=rope_base, norm_eps=norm_eps, softmax_scale=softmax_scale,
+                                rope_base_comp=rope_base_comp or 0.0)
         rc = L.validate(self.desc)
         if rc:
             raise L.CkvError(rc, "ckv_validate")
@@ -61,11 +62,16 @@ class DeviceLayer:
         self.max_chunk = max_chunk
         self.stage = z8(max_chunk + swa - 1, self.rb) if max_chunk else None
         self.status = torch.zeros(batch, dtype=torch.int32, device=dev)
+        # tokens stored per sequence (its next position); the library checks
+        # every appended position against it when tracking is on
+        self.n_tokens = torch.zeros(batch, dtype=torch.int32, device=dev)
+        self._host_tokens = None
         self.cache = L.LayerCache(
             raw=self.raw.data_ptr(), comp=self._ptr(self.comp), idx=self._ptr(self.idx),
             st_kv=self._ptr(self.st_kv), st_sc=self._ptr(self.st_sc), ist_kv=self._ptr(self.ist_kv),
             ist_sc=self._ptr(self.ist_sc), raw_stage=self._ptr(self.stage),
-            stage_rows=(max_chunk + swa - 1) if max_chunk else 0, status=self.status.data_ptr())
+            stage_rows=(max_chunk + swa - 1) if max_chunk else 0, status=self.status.data_ptr(),
+            n_tokens=self.n_tokens.data_ptr() if track_tokens else None, n_tokens_host=None)
         self.weights = None
         self._wt = {}
         nb = max(L.workspace_bytes(self.desc, L.CKV_MODE_DECODE, batch),
@@ -85,10 +91,26 @@ class DeviceLayer:
         self._wt = {k: (_dev(v, self.device) if v is not None else None) for k, v in names.items()}
         self.weights = L.LayerWeights(**{k: self._ptr(v) for k, v in self._wt.items()})
 
+    def set_host_tokens(self, counts) -> None:
+        """Give the library a host mirror of the token counts (a numpy int32
+        array the caller keeps up to date; None removes it): prefill calls whose
+        pos0 differs from it then fail with CKV_E_SEQUENCE before any work."""
+        if counts is None:
+            self._host_tokens = None
+            self.cache.n_tokens_host = None
+            return
+        arr = np.ascontiguousarray(counts, dtype=np.int32)
+        if arr.shape != (self.batch,):
+            raise ValueError(f"host token counts must have shape ({self.batch},)")
+        self._host_tokens = arr
+        self.cache.n_tokens_host = arr.ctypes.data
+
     def load_cache(self, raw=None, comp=None, idx=None, st_kv=None, st_sc=None, ist_kv=None,
-                   ist_sc=None) -> None:
+                   ist_sc=None, n_tokens=None) -> None:
         for name, a in (("raw", raw), ("comp", comp), ("idx", idx), ("st_kv", st_kv), ("st_sc", st_sc),
-                        ("ist_kv", ist_kv), ("ist_sc", ist_sc)):
+                        ("ist_kv", ist_kv), ("ist_sc", ist_sc), ("n_tokens", n_tokens)):
+            if name == "n_tokens" and a is not None:
+                a = np.asarray(a, dtype=np.int32)
             if a is None:
                 continue
             dst = getattr(self, name)

@@ -5,7 +5,9 @@
  *   [P1] "【#3】ds4.c を読み解く" (compressor s4-s5, indexer s6, mixed attention
  *        s7, tail-only RoPE s8, FP8 cache s9, prefill chunks s3), and
  *   [P4] "vLLM DeepSeek V4 サポート" (shared K=V with inverse RoPE, c4a / c128a,
- *        DSA top-k, sliding window of 128, fused cache insertion).
+ *        DSA top-k, sliding window of 128, fused cache insertion), and
+ *   [P5] "【#6】ds4.c を読み解く" (s10: KV state whose token prefix does not
+ *        match the request is refused before any layer work).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -13,21 +15,23 @@
  * - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *   Every call only enqueues work on that stream and returns; nothing
  *   synchronises.  The caller keeps every buffer alive until that work ends.
- * - The caller owns every buffer.  The library allocates no device memory,
- *   keeps no pointer after a call returns and has no mutable global state, so
- *   calls on different streams over disjoint caches may overlap.
+ * - The caller owns every buffer.  The library allocates no device memory and
+ *   keeps no pointer after a call returns, so calls on different streams over
+ *   disjoint caches may overlap.  Its only mutable state is the per-thread
+ *   arming of ckv_time_next_score (a profiling hook, off unless armed).
  * - Errors: each call returns CKV_OK (0) or a negative CKV_E_* code.  All
  *   argument, shape, capacity and workspace checks run on the host BEFORE any
  *   work is enqueued, so a failed call leaves every buffer untouched.
  *   Conditions only the device can see (a per-sequence position beyond the
- *   cache capacity, a negative position) skip that sequence and OR a bit into
+ *   cache capacity, a negative position, a position that is not the
+ *   sequence's next token) skip that sequence and OR a bit into
  *   cache->status[b] (when status is non-NULL); the caller reads it at its own
  *   synchronisation point.  No call aborts, prints or throws.
  * - A layer is described by ckv_layer_desc; ckv_validate() checks it.  The
  *   compiled kernels support: ratio 0, 4 or 128; n_rot 64; swa 128;
  *   head_dim 128 or 512 (a multiple of 64, at most 512); idx_dim 64 or 128;
  *   n_heads a multiple of 16, at most 128; idx_heads 1..64; top_k 1..2048;
- *   hidden a multiple of 64.
+ *   hidden a multiple of 64, at most 65536.
  *
  * Stored row formats (one K=V row of head_dim channels)
  * -----------------------------------------------------
@@ -58,10 +62,14 @@ extern "C" {
 #define CKV_E_CAPACITY (-3)    /* B > batch, T > chunk cap, rows beyond comp_cap, stage too small */
 #define CKV_E_WORKSPACE (-4)   /* ws NULL or ws_bytes < ckv_workspace_bytes()  */
 #define CKV_E_HIP (-5)         /* a kernel launch failed                       */
+#define CKV_E_SEQUENCE (-6)    /* pos0 is not the sequence's token count in
+                                  cache->n_tokens_host                          */
 
 /* ---- cache->status bits (device-detected, sticky) ------------------------ */
 #define CKV_STATUS_BAD_POS 1u   /* pos < 0                                      */
 #define CKV_STATUS_CAPACITY 2u  /* the row a token closes lies beyond comp_cap  */
+#define CKV_STATUS_SEQUENCE 4u  /* position is not the sequence's next token
+                                   (cache->n_tokens); the token was not stored */
 
 /* ---- formats -------------------------------------------------------------- */
 #define CKV_F32 0
@@ -96,8 +104,15 @@ extern "C" {
  *   idx_fmt     CKV_F32 / CKV_BF16 for indexer rows
  *   act_fmt     CKV_F32 / CKV_BF16 for x, u, q, qI and out
  *   w_fmt       CKV_F32 / CKV_BF16 for wkv / wgate / idx_wkv / idx_wgate
- *   rope_base   the layer's RoPE base; one base serves the query, raw rows,
- *               compressed rows and indexer of the layer [P1 s8]
+ *   rope_base   the layer's RoPE base [P1 s8]: it serves the raw rows and the
+ *               query's rotation against them, and, unless rope_base_comp is
+ *               set, everything else as well
+ *   rope_base_comp  0, or a separate base for the compressed class:
+ *               compressed rows, indexer rows and the indexer query, and the
+ *               query's rotation against compressed rows.  Attention then
+ *               takes one softmax over both classes and rotates each class's
+ *               share of the output back by -p in its own frame [P4 "Shared
+ *               Key and Value": inverse RoPE]
  *   norm_eps    RMSNorm epsilon of the compressor [P1 s4 step 6]
  *   softmax_scale  logit scale; 0 means 1/sqrt(head_dim)
  *   flags       CKV_FLAG_* */
@@ -121,6 +136,7 @@ typedef struct ckv_layer_desc {
   double rope_base;
   float norm_eps;
   float softmax_scale;
+  double rope_base_comp;
 } ckv_layer_desc;
 
 /* Compressor weights (device pointers, read only).
@@ -153,6 +169,20 @@ typedef struct ckv_layer_weights {
  *   raw_stage  [stage_rows, row_bytes]: prefill staging of the raw rows of
  *              positions pos0-swa+1 .. pos0+T-1 (stage_rows >= T + swa - 1)
  *   status     [batch] uint32 sticky device error bits, or NULL
+ *   n_tokens   [batch] int32 (device), or NULL: tokens of each sequence stored
+ *              so far, i.e. its next position [P1 s1: the engine refuses
+ *              state that does not match rather than guessing; ds4 rejects a
+ *              KV checkpoint whose prefix does not match, P5 s10].  When given,
+ *              compress_append stores a token only at position n_tokens[b]
+ *              (then sets n_tokens[b] = pos + 1) or again at n_tokens[b] - 1
+ *              (a re-run of the last step, which rewrites the same slots); any
+ *              other position sets CKV_STATUS_SEQUENCE and leaves that
+ *              sequence's cache untouched.  Prefill accepts pos0 = n_tokens[seq]
+ *              only and advances it by T.
+ *   n_tokens_host  [batch] int32 (HOST), or NULL: the caller's mirror of
+ *              n_tokens.  When given, a prefill call whose pos0 differs from
+ *              n_tokens_host[seq] returns CKV_E_SEQUENCE before any enqueue.
+ *              The library reads it and never writes it.
  * Pointers a layer does not use (comp/state for ratio 0, idx/ist_* unless
  * ratio 4, raw_stage for decode) may be NULL. */
 typedef struct ckv_layer_cache {
@@ -166,6 +196,8 @@ typedef struct ckv_layer_cache {
   void* raw_stage;
   int32_t stage_rows;
   uint32_t* status;
+  int32_t* n_tokens;
+  const int32_t* n_tokens_host;
 } ckv_layer_cache;
 
 /* ---- utilities (host only, never touch the GPU) --------------------------- */
@@ -189,12 +221,12 @@ const char* ckv_last_hip_error(void);
  * handles created by the caller (timing enabled), or NULL.  Arms the calling
  * thread's next launch of an indexer score kernel (made by
  * ckv_indexer_score_decode, ckv_indexer_topk_decode or
- * ckv_indexer_topk_prefill; the fused scan launch of ckv_decode_step is not
- * one) to stamp start_event when the kernel starts and stop_event when it
- * ends, so
- * that hipEventElapsedTime gives the kernel's own duration, without the
- * launch gaps around it.  The events stay owned by the caller; the arming is
- * consumed by that one launch; two NULLs disarm.  Returns CKV_OK. */
+ * ckv_indexer_topk_prefill, or the fused projection + scan launch of
+ * ckv_decode_step) to stamp start_event when the kernel starts and stop_event
+ * when it ends, so that hipEventElapsedTime gives the kernel's own duration,
+ * without the launch gaps around it.  The events stay owned by the caller;
+ * the arming is consumed by that one launch; two NULLs disarm.  Returns
+ * CKV_OK. */
 int ckv_time_next_score(void* start_event, void* stop_event);
 
 /* Workspace bytes a call of `mode` with n = B (decode) or T (prefill) tokens

@@ -326,8 +326,9 @@ def topk_select(scores: np.ndarray, k: int) -> np.ndarray:
     if V <= k:
         out[:V] = np.arange(V)
         return out
-    order = sorted(range(V), key=lambda s: (-float(scores[s]), s))
-    out[:] = np.sort(np.array(order[:k], np.int32))
+    sc = np.asarray(scores, F64) + 0.0               # -0 compares equal to +0
+    order = np.lexsort((np.arange(V), -sc))          # full sort: score descending, then index
+    out[:] = np.sort(order[:k]).astype(np.int32)
     return out
 
 
@@ -459,6 +460,9 @@ class OracleSequence:
         self.isig: Dict[int, np.ndarray] = {}
         self.u: Dict[int, np.ndarray] = {}
         self._row_cache: Dict[Tuple[str, int], Tuple[np.ndarray, np.ndarray, np.ndarray]] = {}
+        # memo of raw rows of live tokens and of the indexer matrix (cleared by feed)
+        self._raw_cache: Dict[int, Tuple[np.ndarray, np.ndarray, np.ndarray]] = {}
+        self._idx_mat: Optional[np.ndarray] = None
         W = L.window
         if W and st_kv is not None:
             for t in range(max(0, first_live - W), first_live):
@@ -481,9 +485,11 @@ class OracleSequence:
             has_idx = L.ratio == 4 and L.idx_wkv is not None
             if has_idx:
                 KI, SI = X @ L.idx_wkv.T, X @ L.idx_wgate.T
+        self._idx_mat = None
         for n in range(len(X)):
             t = t0 + n
             self.u[t] = U[n]
+            self._raw_cache.pop(t, None)
             if L.ratio:
                 self.kap[t], self.sig[t] = K[n], S[n]
                 if has_idx:
@@ -558,9 +564,11 @@ class OracleSequence:
         at t with the raw class's base (P4: the SWA rows carry their position)."""
         L = self.L
         if self.is_live(t):
-            z = rope_tail(self.u[t], t, L.base_raw, L.n_rot)
-            rec, val = encode_row(z, L.kv_fmt, L.head_dim, L.n_rot)
-            return z, rec, val
+            if t not in self._raw_cache:
+                z = rope_tail(self.u[t], t, L.base_raw, L.n_rot)
+                rec, val = encode_row(z, L.kv_fmt, L.head_dim, L.n_rot)
+                self._raw_cache[t] = (z, rec, val)
+            return self._raw_cache[t]
         val = decode_rows(self.raw_rec[t % L.swa], L.kv_fmt, L.head_dim, L.n_rot)
         return val, None, val
 
@@ -584,13 +592,16 @@ class OracleSequence:
         L = self.L
         if V == 0:
             return np.zeros((0, L.idx_dim))
+        if self._idx_mat is not None and len(self._idx_mat) >= V:
+            return self._idx_mat[:V].copy()
         if self.idx_vals is not None:
             rows = decode_values(self.idx_vals[:V], L.idx_fmt)
         else:
             rows = np.zeros((V, L.idx_dim))
         for i in self.computed_rows(V):
             rows[i] = self.idx_row(i)[1]
-        return rows
+        self._idx_mat = rows
+        return rows.copy()
 
     def comp_matrix(self, idx: Sequence[int]) -> np.ndarray:
         """Stored values of attention rows ``idx``."""

@@ -18,14 +18,14 @@ def device_layer(cfg: LayerShape, weights, cache: G.CacheInit = None, max_chunk:
                      batch=cfg.batch if batch is None else batch, idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim,
                      top_k=cfg.top_k, comp_cap=cfg.comp_cap, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt,
                      act_fmt=cfg.act_fmt, w_fmt=cfg.w_fmt, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps,
-                     n_rot=cfg.n_rot, swa=cfg.swa, max_chunk=max_chunk)
+                     n_rot=cfg.n_rot, swa=cfg.swa, max_chunk=max_chunk, rope_base_comp=cfg.rope_base_comp or 0.0)
     if weights is not None:
         dl.set_weights(wkv=weights.wkv, wgate=weights.wgate, ape=weights.ape, gamma=weights.gamma,
                        idx_wkv=weights.idx_wkv, idx_wgate=weights.idx_wgate, idx_ape=weights.idx_ape,
                        idx_gamma=weights.idx_gamma)
     if cache is not None:
         dl.load_cache(raw=cache.raw, comp=cache.comp, idx=cache.idx, st_kv=cache.st_kv, st_sc=cache.st_sc,
-                      ist_kv=cache.ist_kv, ist_sc=cache.ist_sc)
+                      ist_kv=cache.ist_kv, ist_sc=cache.ist_sc, n_tokens=cache.first_live)
     return dl
 
 

@@ -53,9 +53,24 @@ def test_validate_accepts_the_workload_shapes():
     (dict(act_fmt=L.CKV_E4M3), L.CKV_E_UNSUPPORTED), (dict(comp_cap=0), L.CKV_E_INVAL),
     (dict(batch=0), L.CKV_E_INVAL), (dict(rope_base=0.0), L.CKV_E_INVAL),
     (dict(flags=0x80), L.CKV_E_UNSUPPORTED), (dict(hidden=100), L.CKV_E_UNSUPPORTED),
+    (dict(top_k=2049), L.CKV_E_UNSUPPORTED), (dict(rope_base_comp=-1.0), L.CKV_E_INVAL),
 ])
 def test_validate_rejects(kw, code):
     assert L.validate(desc(**kw)) == code
+
+
+def test_validate_bounds_match_the_header():
+    """top_k 1..2048 (the header's stated range), a separate compressed-class
+    base, and c128a caches of any row count: the attention kernels compute
+    the addresses of all-visible compressed rows, so no per-split table
+    bounds them (a c128a cache of 8192 rows is the 1M-token workload's)."""
+    assert L.validate(desc(top_k=2048)) == 0
+    assert L.validate(desc(top_k=1)) == 0
+    assert L.validate(desc(rope_base=10000.0, rope_base_comp=160000.0)) == 0
+    for cap in (8192, 65536):
+        d = desc(ratio=128, comp_cap=cap, kv_fmt=L.CKV_BF16)
+        assert L.validate(d) == 0
+        assert L.workspace_bytes(d, L.CKV_MODE_PREFILL, 4096) > 0
 
 
 def test_row_bytes_and_workspace():
@@ -142,6 +157,29 @@ def test_host_errors_before_any_enqueue():
     # invalid description
     assert L.compress_append_decode(desc(ratio=5), w, c, FAKE, FAKE, FAKE, 1, FAKE, ws) == L.CKV_E_UNSUPPORTED
     assert L.lib.ckv_validate(None) == L.CKV_E_INVAL
+    # misaligned token counts / status words
+    assert L.compress_append_decode(d, w, cache(n_tokens=FAKE + 2), FAKE, FAKE, FAKE, 16, FAKE, ws) == L.CKV_E_INVAL
+    assert L.compress_append_decode(d, w, cache(status=FAKE + 1), FAKE, FAKE, FAKE, 16, FAKE, ws) == L.CKV_E_INVAL
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="fake device addresses are only passed where no GPU exists")
+def test_prefill_out_of_sequence_is_refused_on_the_host():
+    """With the host mirror of the token counts, a chunk that does not start
+    at its sequence's next position returns CKV_E_SEQUENCE before any work is
+    enqueued (the pages' engine refuses KV state whose token prefix does not
+    match).  A matching pos0 passes that check and fails later, on the
+    missing workspace, still before any enqueue."""
+    import numpy as np
+    d = desc()
+    counts = np.array([61440] + [0] * 15, np.int32)
+    c = cache(n_tokens=FAKE, n_tokens_host=counts.ctypes.data)
+    w = weights()
+    wp = L.workspace_bytes(d, L.CKV_MODE_PREFILL, 4096)
+    for pos0 in (61439, 61441, 0, 65536):
+        assert L.compress_append_prefill(d, w, c, FAKE, FAKE, 0, pos0, 4096, FAKE, wp) == L.CKV_E_SEQUENCE
+    assert L.compress_append_prefill(d, w, c, FAKE, FAKE, 0, 61440, 4096, None, wp) == L.CKV_E_WORKSPACE
+    assert L.compress_append_prefill(d, w, c, FAKE, FAKE, 3, 8, 16, FAKE, wp) == L.CKV_E_SEQUENCE
+    assert L.strerror(L.CKV_E_SEQUENCE).startswith("position")
 
 
 def test_stack_schedule_matches_the_oracle():

@@ -245,6 +245,7 @@ def test_bad_position_sets_status_and_spares_others():
     pos = inp.pos.copy()
     pos[1] = -1            # invalid position
     pos[2] = 64 * 4 + 3    # closes row 64: beyond comp_cap
+    dl.n_tokens[2] = pos[2]   # in sequence, so that the capacity check is what refuses it
     raw_before = cpu(dl.raw).copy()
     dl.compress_decode(dev(inp.x), dev(inp.u), dev(pos))
     torch.cuda.synchronize()

@@ -54,7 +54,7 @@ def test_flash_stack_decode_every_layer():
                            idx_wgate=wts.idx_wgate, idx_ape=wts.idx_ape, idx_gamma=wts.idx_gamma)
         c = inp.cache
         dl.load_cache(raw=c.raw, comp=c.comp, idx=c.idx, st_kv=c.st_kv, st_sc=c.st_sc, ist_kv=c.ist_kv,
-                      ist_sc=c.ist_sc)
+                      ist_sc=c.ist_sc, n_tokens=c.first_live)
         L = oracle_layer(cfg, wts)
         seqs = [oracle_seq_from_init(L, c, b) for b in range(B)]
         for b in range(B):

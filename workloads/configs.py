@@ -14,9 +14,12 @@ from typing import Dict, Optional, Tuple
 
 # RoPE bases.  The pages name a normal base and a separate base for
 # compressed layers ("ds4.c を読み解く (#3)", section 8) without values; the
-# values are the workload's: 10000 for uncompressed layers, 160000 for
-# compressed ones.  One base per layer (the layer's choice applies to the
-# query, the raw rows, the compressed rows and the indexer alike).
+# values are the workload's: 10000 for uncompressed layers and raw rows,
+# 160000 for compressed ones.  The layers of the 1024-token tiny workload keep
+# one base per row class (raw rows 10000, compressed and indexer rows 160000,
+# as its description states); the other workloads use one base per layer
+# (the layer's choice applies to the query, the raw rows, the compressed rows
+# and the indexer alike).
 ROPE_BASE_RAW = 10000.0
 ROPE_BASE_COMPRESSED = 160000.0
 
@@ -94,7 +97,8 @@ def _c1() -> LayerShape:
         name="c1_tiny_c4a_decode_ctx1024_f32", ratio=4, hidden=1024, head_dim=128,
         n_heads=16, idx_heads=4, idx_dim=64, top_k=32, batch=1, n_ctx=1024,
         comp_cap=256, kv_fmt="f32", idx_fmt="f32", act_fmt="f32", w_fmt="f32",
-        w_std=0.02, ape_std=0.1, seed=1)
+        w_std=0.02, ape_std=0.1, seed=1,
+        rope_base=ROPE_BASE_RAW, rope_base_comp=ROPE_BASE_COMPRESSED)
 
 
 def _c2() -> LayerShape:

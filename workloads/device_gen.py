@@ -67,8 +67,11 @@ def fill_rows(dst: torch.Tensor, fmt: str, d: int, n_rot: int, g: torch.Generato
 
 
 def fill_layer_cache(dl, cfg) -> None:
-    """Fill every cache tensor of a DeviceLayer as at a warm context (all rows drawn)."""
+    """Fill every cache tensor of a DeviceLayer as at a warm context (all rows
+    drawn); every sequence has stored n_ctx - 1 tokens, so the step's token
+    sits at position n_ctx - 1."""
     s, L = cfg.seed, cfg.layer
+    dl.n_tokens.fill_(cfg.n_ctx - 1)
     fill_rows(dl.raw, cfg.kv_fmt, cfg.head_dim, cfg.n_rot, _gen(s, "raw", L))
     if dl.comp is not None:
         fill_rows(dl.comp, cfg.kv_fmt, cfg.head_dim, cfg.n_rot, _gen(s, "comp", L))
