@@ -26,6 +26,7 @@ CKV_FLAG_NO_INV_ROPE = 1
 CKV_FLAG_IDX_NO_RELU = 2
 CKV_MODE_DECODE, CKV_MODE_PREFILL = 0, 1
 CKV_MAX_CHUNK = 4096
+CKV_STATIC_WORKSPACE_BYTES = 48 << 20
 CKV_STATUS_BAD_POS = 1
 CKV_STATUS_CAPACITY = 2
 CKV_STATUS_SEQUENCE = 4
@@ -100,6 +101,7 @@ def _load() -> ctypes.CDLL:
         "ckv_sparse_swa_attn_decode": [D, C, VP, VP, VP, I32, VP, VP, SZ, VP],
         "ckv_sparse_swa_attn_prefill": [D, C, VP, I32, I32, I32, VP, VP, VP, SZ, VP],
         "ckv_decode_step": [D, Wt, C, VP, VP, VP, VP, VP, VP, I32, VP, VP, VP, SZ, VP],
+        "ckv_decode_step_static": [D, Wt, C, VP, VP, VP, VP, VP, VP, I32, VP, VP, VP],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -114,7 +116,7 @@ EXPORTS = ("ckv_row_bytes", "ckv_validate", "ckv_strerror", "ckv_last_hip_error"
            "ckv_workspace_sync_bytes",
            "ckv_compress_append_decode", "ckv_compress_append_prefill", "ckv_indexer_topk_decode",
            "ckv_indexer_topk_prefill", "ckv_indexer_score_decode", "ckv_sparse_swa_attn_decode",
-           "ckv_sparse_swa_attn_prefill", "ckv_decode_step", "ckv_time_next_score")
+           "ckv_sparse_swa_attn_prefill", "ckv_decode_step", "ckv_time_next_score", "ckv_decode_step_static")
 
 
 def strerror(code: int) -> str:
@@ -199,3 +201,8 @@ def sparse_swa_attn_prefill(desc, cache, q, seq, pos0, T, topk, out, ws, ws_byte
 def decode_step(desc, weights, cache, x, u, q, qI, w, pos, B, topk, out, ws, ws_bytes, stream=None) -> int:
     return lib.ckv_decode_step(_ref(desc), _ref(weights), _ref(cache), _p(x), _p(u), _p(q), _p(qI), _p(w),
                                _p(pos), int(B), _p(topk), _p(out), _p(ws), int(ws_bytes), stream)
+
+
+def decode_step_static(desc, weights, cache, x, u, q, qI, w, pos, B, topk, out, stream=None) -> int:
+    return lib.ckv_decode_step_static(_ref(desc), _ref(weights), _ref(cache), _p(x), _p(u), _p(q), _p(qI), _p(w),
+                                      _p(pos), int(B), _p(topk), _p(out), stream)

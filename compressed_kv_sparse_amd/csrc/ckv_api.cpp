@@ -251,21 +251,31 @@ extern "C" int ckv_sparse_swa_attn_prefill(const ckv_layer_desc* desc, const ckv
       launch_attn(P, to_cache(cache), q, nullptr, seq, pos0, T, topk, out, L, (uint8_t*)ws, stream));
 }
 
+namespace ckv {
+int decode_step_checks(const ckv_layer_desc* desc, const ckv_layer_weights* w, const ckv_layer_cache* cache,
+                       const void* x, const void* u, const void* q, const void* qI, const float* iw,
+                       const int32_t* pos, int32_t B, int32_t* topk, void* out, void* ws, size_t ws_bytes,
+                       LayerParams* P, WsLayout* L) {
+  int rc = prologue(desc, cache, P);
+  if (rc) return rc;
+  if (B < 1) return CKV_E_INVAL;
+  if (B > P->batch) return CKV_E_CAPACITY;
+  if ((rc = weights_ok(*P, w))) return rc;
+  if (check_ptr(u) || check_ptr(q) || check_ptr(pos) || check_ptr(out) || (P->ratio && check_ptr(x)))
+    return CKV_E_INVAL;
+  if (P->ratio == 4 && (check_ptr(qI) || check_ptr(iw) || check_ptr(topk))) return CKV_E_INVAL;
+  return check_ws(*P, CKV_MODE_DECODE, B, ws, ws_bytes, L);
+}
+}  // namespace ckv
+
 extern "C" int ckv_decode_step(const ckv_layer_desc* desc, const ckv_layer_weights* w,
                                const ckv_layer_cache* cache, const void* x, const void* u, const void* q,
                                const void* qI, const float* iw, const int32_t* pos, int32_t B, int32_t* topk,
                                void* out, void* ws, size_t ws_bytes, void* stream) {
   LayerParams P;
-  int rc = prologue(desc, cache, &P);
-  if (rc) return rc;
-  if (B < 1) return CKV_E_INVAL;
-  if (B > P.batch) return CKV_E_CAPACITY;
-  if ((rc = weights_ok(P, w))) return rc;
-  if (check_ptr(u) || check_ptr(q) || check_ptr(pos) || check_ptr(out) || (P.ratio && check_ptr(x)))
-    return CKV_E_INVAL;
-  if (P.ratio == 4 && (check_ptr(qI) || check_ptr(iw) || check_ptr(topk))) return CKV_E_INVAL;
   WsLayout L;
-  if ((rc = check_ws(P, CKV_MODE_DECODE, B, ws, ws_bytes, &L))) return rc;
+  int rc = decode_step_checks(desc, w, cache, x, u, q, qI, iw, pos, B, topk, out, ws, ws_bytes, &P, &L);
+  if (rc) return rc;
   if (P.ratio != 4 || !step_fusable(P, B)) {
     if ((rc = ckv_compress_append_decode(desc, w, cache, x, u, pos, B, ws, ws_bytes, stream))) return rc;
     if (P.ratio == 4 && (rc = ckv_indexer_topk_decode(desc, cache, qI, iw, pos, B, topk, ws, ws_bytes, stream)))

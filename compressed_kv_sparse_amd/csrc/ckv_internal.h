@@ -125,6 +125,12 @@ int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32
 // fused decode step of a ratio-4 layer: projection + scan of the existing rows
 // in one launch, then per-sequence compressor + new-row score + selection
 bool step_fusable(const LayerParams& P, int B);
+// every host check of ckv_decode_step, nothing enqueued (CKV_OK or the code
+// ckv_decode_step would return)
+int decode_step_checks(const ckv_layer_desc* desc, const ckv_layer_weights* w, const ckv_layer_cache* cache,
+                       const void* x, const void* u, const void* q, const void* qI, const float* iw,
+                       const int32_t* pos, int32_t B, int32_t* topk, void* out, void* ws, size_t ws_bytes,
+                       LayerParams* P, WsLayout* L);
 int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache& c, const void* x,
                             const void* u, const void* qI, const float* wt, const int32_t* pos, int B,
                             float* proj, uint32_t* keys, const SelWs& sel, int32_t* topk, void* stream);

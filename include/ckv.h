@@ -344,6 +344,23 @@ int ckv_decode_step(const ckv_layer_desc* desc, const ckv_layer_weights* w, cons
                     const int32_t* pos, int32_t B, int32_t* topk, void* out, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* ---- decode_step without a workspace argument ------------------------------
+ * For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation).  The same step as
+ * ckv_decode_step, same arguments without ws / ws_bytes: the workspace is a
+ * device array of CKV_STATIC_WORKSPACE_BYTES inside the library, one per GPU,
+ * held until the process ends.  A layer / batch whose
+ * ckv_workspace_bytes(desc, CKV_MODE_DECODE, B) exceeds that size returns
+ * CKV_E_WORKSPACE before any work is enqueued (the 64k-context batch of 32
+ * sequences needs 44 MiB).  The call clears the array's counter region with a
+ * kernel, allocates nothing and records no memset.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (different streams,
+ * or threads) race and must not be issued. */
+#define CKV_STATIC_WORKSPACE_BYTES ((size_t)48 << 20)
+int ckv_decode_step_static(const ckv_layer_desc* desc, const ckv_layer_weights* w, const ckv_layer_cache* cache,
+                           const void* x, const void* u, const void* q, const void* qI, const float* iw,
+                           const int32_t* pos, int32_t B, int32_t* topk, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

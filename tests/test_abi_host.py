@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -160,6 +160,23 @@ def test_host_errors_before_any_enqueue():
     # misaligned token counts / status words
     assert L.compress_append_decode(d, w, cache(n_tokens=FAKE + 2), FAKE, FAKE, FAKE, 16, FAKE, ws) == L.CKV_E_INVAL
     assert L.compress_append_decode(d, w, cache(status=FAKE + 1), FAKE, FAKE, FAKE, 16, FAKE, ws) == L.CKV_E_INVAL
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="fake device addresses are only passed where no GPU exists")
+def test_static_workspace_step_refuses_what_does_not_fit():
+    """The workspace-free decode step checks everything on the host first: a
+    batch whose workspace exceeds the library's array, and the ordinary
+    argument errors, return before any GPU call."""
+    d = desc(batch=64, comp_cap=32768)
+    assert L.workspace_bytes(d, L.CKV_MODE_DECODE, 64) > L.CKV_STATIC_WORKSPACE_BYTES
+    st = lambda d, B, **k: L.decode_step_static(d, weights(), cache(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B,
+                                                k.get("topk", FAKE), FAKE)
+    assert st(d, 64) == L.CKV_E_WORKSPACE
+    assert st(desc(), 17) == L.CKV_E_CAPACITY
+    assert st(desc(), 0) == L.CKV_E_INVAL
+    assert st(desc(), 16, topk=None) == L.CKV_E_INVAL
+    assert st(desc(ratio=5), 16) == L.CKV_E_UNSUPPORTED
+    assert L.workspace_bytes(desc(), L.CKV_MODE_DECODE, 16) <= L.CKV_STATIC_WORKSPACE_BYTES
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="fake device addresses are only passed where no GPU exists")
