@@ -475,6 +475,61 @@ def cpu_baseline(cfg, inp, wts, budget_s=12.0):
                       f"{dt:.1f}s on the host, numpy fp64 ({threads} BLAS threads of {os.cpu_count()} host CPUs)"}
 
 
+def cpu_baseline_extra(budget_s=4.0):
+    """Further oracle timings on the host: the 1024-token tiny workload's
+    decode step and the 64k workload's decode step on one thread each (the
+    history fed once, then repeated steps at the last position, each
+    recomputing what a new token changes), and a sample of the 4096-token
+    prefill chunk's queries on the BLAS thread pool."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    from workloads import get_config, make_decode_inputs, make_layer_weights, make_prefill_inputs
+    from workloads import gen as G
+    out = {}
+
+    def timed_steps(seq, p, x, u, q, qI, w):
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < budget_s or n < 2:
+            seq.step(p, x, u, q, qI, w)
+            n += 1
+        return n / (time.perf_counter() - t0), n
+
+    with threadpool_limits(1):
+        cfg = get_config("c1")
+        wts = make_layer_weights(cfg)
+        x, u, q, qI, w = G.make_token_stream(cfg, cfg.n_ctx)
+        seq = O.OracleSequence(O.layer_from(cfg, wts))
+        p = cfg.n_ctx - 1
+        seq.feed(0, x[:p], u[:p])
+        v, n = timed_steps(seq, p, x[p], u[p], q[p], qI[p], w[p])
+        out["c1_decode_1thread"] = {"value": round(v, 2), "unit": "tokens/s", "steps": n}
+        cfg = get_config("c2").with_(batch=1)
+        inp = make_decode_inputs(cfg)
+        wts = make_layer_weights(cfg)
+        c = inp.cache
+        seq = O.OracleSequence(O.layer_from(cfg, wts), raw_rec=c.raw[0], comp_rec=c.comp[0], idx_vals=c.idx[0],
+                               st_kv=c.st_kv[0], st_sc=c.st_sc[0], ist_kv=c.ist_kv[0], ist_sc=c.ist_sc[0],
+                               first_live=int(c.first_live[0]))
+        v, n = timed_steps(seq, int(inp.pos[0]), inp.x[0], inp.u[0], inp.q[0], inp.qI[0], inp.w[0])
+        out["c2_decode_1thread"] = {"value": round(v, 2), "unit": "tokens/s", "steps": n}
+    cfg = get_config("c4")
+    inp = make_prefill_inputs(cfg)
+    seq = O.OracleSequence(O.layer_from(cfg, make_layer_weights(cfg)), raw_rec=inp.cache.raw[0],
+                           comp_rec=inp.cache.comp[0], idx_vals=inp.cache.idx[0], st_kv=inp.cache.st_kv[0],
+                           st_sc=inp.cache.st_sc[0], ist_kv=inp.cache.ist_kv[0], ist_sc=inp.cache.ist_sc[0],
+                           first_live=inp.pos0)
+    t0 = time.perf_counter()
+    seq.feed(inp.pos0, inp.x, inp.u)
+    n = 0
+    while time.perf_counter() - t0 < budget_s or n < 2:
+        seq.query(inp.pos0 + 8 * n, inp.q[8 * n], inp.qI[8 * n], inp.w[8 * n])
+        n += 1
+    dt = time.perf_counter() - t0
+    out["c4_prefill_sample"] = {"value": round(n / dt, 2), "unit": "tokens/s",
+                                "sample": f"the chunk's projection and {n} of its 4096 queries (every 8th)"}
+    return out
+
+
 # --------------------------------------------------------------------------- main
 
 def main():
@@ -574,6 +629,8 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, r["_inp"], r["_wts"])
         log(f"[bench] cpu oracle: {cpu['value']:.2f} tok/s on {cpu['cores']} threads")
+        cpu["others"] = cpu_baseline_extra()
+        log(f"[bench] cpu oracle, other workloads: {cpu['others']}")
     line = {
         "metric": "decode tokens/s + HBM GB/s % peak, c4a sparse attn @128k ctx; prefill tok/s",
         "value": round(r["tok_s"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -132,7 +132,8 @@ extern "C" int ckv_compress_append_decode(const ckv_layer_desc* desc, const ckv_
   if (P.ratio) {
     if ((rc = launch_proj(P, W, x, B, part, L.proj_splits, stream))) return launched(rc);
   }
-  return launched(launch_compress_decode(P, W, C, u, pos, B, part, L.proj_splits, stream));
+  return launched(launch_compress_decode(P, W, C, u, pos, B, part, L.proj_splits,
+                                        (float*)((uint8_t*)ws + L.pool), stream));
 }
 
 extern "C" int ckv_compress_append_prefill(const ckv_layer_desc* desc, const ckv_layer_weights* w,

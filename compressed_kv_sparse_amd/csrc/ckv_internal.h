@@ -82,6 +82,7 @@ struct WsLayout {
   size_t cand_idx;  // uint32 [n][kCandCap]
   size_t proj;      // float [proj_splits][n][ncol]
   size_t keys;      // uint32 [n][cap]   indexer keys
+  size_t pool;      // float [n][d] + [n][8][2]   c128a decode: pooled rows and slice sums
   size_t part_o;    // float [n][splits][H][d]  attention partial outputs
   size_t part_ml;   // float [n][splits][H][4]  attention partial (max, sum, scale of the stored output, 0)
   size_t total;
@@ -101,8 +102,12 @@ bool attn_uses_tiles(const LayerParams& P);
 // projection: part[s][m][c] for columns c of the concatenated weights
 int launch_proj(const LayerParams& P, const Weights& w, const void* x, int M, float* part,
                 int splits, void* stream);
+// c128a decode pools channel slices of 64 in parallel blocks (head_dim a
+// multiple of 64, at most 512); pool_ws: the workspace's pool region
+bool c128a_sliced(const LayerParams& P);
 int launch_compress_decode(const LayerParams& P, const Weights& w, const Cache& c, const void* u,
-                           const int32_t* pos, int B, const float* part, int splits, void* stream);
+                           const int32_t* pos, int B, const float* part, int splits, float* pool_ws,
+                           void* stream);
 int launch_compress_prefill(const LayerParams& P, const Weights& w, const Cache& c, const void* u,
                             int seq, int pos0, int T, const float* part, void* stream);
 // indexer: decode (pos != NULL, query b of sequence b) or prefill (pos == NULL,

@@ -55,6 +55,8 @@ int attn_max_rows(const LayerParams& P) {
   return P.swa + (P.ratio == 4 ? P.topk : P.ratio == 128 ? P.cap : 0);
 }
 
+bool c128a_sliced(const LayerParams& P) { return P.ratio == 128 && P.d % 64 == 0 && P.d <= kMaxD; }
+
 bool attn_uses_tiles(const LayerParams& P) {
   return P.act_fmt == CKV_BF16 && P.kv_fmt != CKV_F32 && P.H % 64 == 0 && P.d == 512 && P.n_rot == 64;
 }
@@ -68,7 +70,9 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   const bool proj_mfma = P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16;
   // the decode projection splits K over kProjSlices blocks per tile (partial
   // sums, added by the compressor in slice order)
-  L.proj_splits = (!prefill && proj_mfma) ? kProjSlices : 1;
+  // (c128a layers, whose decode projection runs on its own, use 4 slices:
+  // 4 x 64 blocks instead of 64 latency-bound ones)
+  L.proj_splits = (!prefill && proj_mfma) ? (P.ratio == 128 ? 4 : kProjSlices) : 1;
   const int rows = attn_max_rows(P);
   int rps;
   if (attn_uses_tiles(P)) {
@@ -112,6 +116,8 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   off += align256((size_t)L.proj_splits * n * P.ncol * sizeof(float));
   L.keys = off;
   if (P.ratio == 4) off += align256((size_t)n * P.cap * sizeof(uint32_t));
+  L.pool = off;
+  if (P.ratio == 128 && !prefill) off += align256((size_t)n * (P.d + 16) * sizeof(float));
   const bool need_part = !(attn_uses_tiles(P) && L.attn_splits == 1);
   L.part_o = off;
   if (need_part) off += align256((size_t)n * L.attn_splits * P.H * P.d * sizeof(float));

@@ -177,12 +177,19 @@ __device__ __forceinline__ float2 rope2t(float2 z, int c, int width, int nrot, c
 
 // Sequence check of a decode step (cache->n_tokens): the token at p is stored
 // when p is the sequence's next position or its last one (a re-run of that
-// step).  `nt` is n_tokens[b], read by every thread before the block's first
-// barrier; the update to p + 1 comes after a later barrier.
+// step).  `nt` is n_tokens[b]; every thread has read it before the barrier
+// after which thread 0 writes p + 1 (the check itself decides a return that
+// precedes that barrier, or pin_tokens holds the value there).
 __device__ __forceinline__ int seq_tokens(const Cache& cc, int b, int p) {
-  const int nt = cc.n_tokens ? cc.n_tokens[b] : p;
-  asm volatile("" : : "s"(nt) : "memory");   // the load completes here, ahead of any barrier
-  return nt;
+  return cc.n_tokens ? cc.n_tokens[b] : p;
+}
+__device__ __forceinline__ void pin_tokens(int nt) { asm volatile("" : : "s"(nt) : "memory"); }
+// After a body returned st >= 0 (the token was stored): the sequence's count
+// becomes p + 1.  Called by the kernel at its end (a store placed before the
+// body's waits would make them wait for it too); every thread read the count
+// before the body's barriers.
+__device__ __forceinline__ void advance_tokens(const Cache& cc, int b, int p, int st) {
+  if (st >= 0 && threadIdx.x == 0 && cc.n_tokens) cc.n_tokens[b] = p + 1;
 }
 __device__ __forceinline__ bool seq_ok(const Cache& cc, int p, int nt) {
   return !cc.n_tokens || p == nt || p == nt - 1;
@@ -470,7 +477,6 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
     }
   }
   lds_barrier();                // rtab complete
-  if (tid == 0 && cc.n_tokens) cc.n_tokens[b] = p + 1;   // every thread read it before the barrier
 
   // ---- raw sliding-window row: u rotated at p into slot p % swa
   {
@@ -677,6 +683,7 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
     v3 = wave_max(v3);
     if (lane == 0) *(float4*)(red + 4 * wave) = make_float4(v0, v1, v2, v3);
   }
+  pin_tokens(nt);  // read before the barrier that precedes its update
   lds_barrier();   // red, rtab
   float sA = 0.f, sI = 0.f, mA = 0.f, mU = 0.f;
   {
@@ -698,7 +705,6 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
     return -1;
   }
   if (emit && i >= P.cap && tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_CAPACITY);
-  if (tid == 0 && cc.n_tokens) cc.n_tokens[b] = p + 1;   // every thread read it before the barrier above
   if (wave < nact) {
     // raw sliding-window row: u rotated at p, slot p % swa (attention waves)
     const float zr = rope1t(uu, col, d, P.n_rot, rtab, rtab + 64);

@@ -210,7 +210,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   // cos / sin tables of pair j: [0] at p in the raw frame, [1] at p in the
   // compressed frame, [2] the frame switch (angle p (theta_c - theta))
   __shared__ float cs_[3][32], sn_[3][32];
-  __shared__ int tk_lim;
+  __shared__ int tk_lim, any_bad;
 
   const int qn = blockIdx.x / nsplit, split = blockIdx.x - qn * nsplit;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   const int j1 = min(A.n_list, j0 + rows_per_split);
   const int ntiles = j1 > j0 ? (j1 - j0 + R - 1) / R : 0;
   const int nent = (ntiles + 4) * R;   // table entries incl. the padding tiles the loop issues
-  const int K = (P.ratio == 4 && topk) ? P.topk : 0;
+  const int K = (P.ratio == 4 && topk && j1 > SWA) ? P.topk : 0;   // splits of raw slots need no list
   const uint8_t* dummy = g_attn_zero_row;
   const int tile0 = j0 / R;                                  // list tile of the split's first tile
   const bool start_comp = tile0 >= RAW_TILES;
@@ -234,14 +234,27 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   const bool inv = !(P.flags & CKV_FLAG_NO_INV_ROPE);
 
   // ---- the split's row list -> rtab.  The top-k list ends at its first
-  // entry >= V; entries < 0 are skipped.
+  // entry >= V; entries < 0 are skipped.  The list's loads go out first, then
+  // the query's (which depend on nothing), so that waiting for the list does
+  // not wait for the query; the prologue's barriers order LDS only.
   int tkv[MAXK / NT];
-  if (tid == 0) tk_lim = K;
-  __syncthreads();
+  if (tid == 0) {
+    tk_lim = K;
+    any_bad = 0;
+  }
   if (K) {
     const int32_t* tkg = topk + (size_t)qn * P.topk;
 #pragma unroll
     for (int e = 0; e < MAXK / NT; ++e) tkv[e] = tkg[min(tid + NT * e, K - 1)];
+  }
+  u32x4 Bq[8];
+  {
+    const uint16_t* qr = q + ((size_t)qn * H + head) * D + 256 * cg + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) Bq[ks] = *(const u32x4*)(qr + 32 * ks);
+  }
+  lds_barrier();
+  if (K) {
     int first = K;
 #pragma unroll
     for (int e = 0; e < MAXK / NT; ++e)
@@ -257,7 +270,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     cs_[f][j] = c;
     sn_[f][j] = sn;
   }
-  __syncthreads();
+  lds_barrier();
   const int tk_end = tk_lim;
   for (int x = tid; x < min(nent, MAXL); x += NT) {   // raw slots, padding
     const int j = j0 + x;
@@ -280,7 +293,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // address of split entry x: from the table, or (ratio 128 compressed
   // entries) computed; both evaluated, so the caller's loads stay unconditional
   auto addr_of = [&](int x) -> uint64_t {
@@ -342,12 +355,8 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   // rotated query of this lane's head in fp16, channels 256 cg + 32 ks + 8 g
   // .. +7 (B operand), in the frame of the split's first row class
   Stg S0, S1;
-  u32x4 Bq[8];
   {
     const int f0 = start_comp ? 1 : 0;
-    const uint16_t* qr = q + ((size_t)qn * H + head) * D + 256 * cg + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) Bq[ks] = *(const u32x4*)(qr + 32 * ks);
     // the first tiles' loads go out behind the query's
     issue(S0, 0);
     if (!F8) issue(S1, 1);
@@ -542,7 +551,9 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   }
 
   const int fe = end_comp ? 1 : 0;   // frame the output ended in
-  if (__syncthreads_or(bad)) {
+  if (__ballot(bad) != 0ull && lane == 0) any_bad = 1;
+  lds_barrier();
+  if (any_bad) {
     // ---- range guard: the split again, in fp32, from the stored rows.  Four
     // passes of 16 heads, 32 threads per head, thread `sub` holding channels
     // 16 sub .. +15 (subs 28..31 hold the RoPE tail, pairs 8 (sub - 28) ..).

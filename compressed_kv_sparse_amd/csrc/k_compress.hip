@@ -23,8 +23,9 @@ __global__ __launch_bounds__(256 * TPC) void k_compress_decode(LayerParams P, We
   __shared__ float red[64];
   __shared__ float mrg[TPC > 1 ? TPC * (kMaxD / 2 + (W == 8 ? kMaxDI / 2 : 0)) * 6 : 1];
   __shared__ float rtab[128];
-  compress_decode_seq<KVF, IDXF, ACTF, W, TPC>(P, w, cc, u, pos, proj, splits, B, blockIdx.x, red, mrg, nullptr,
-                                               rtab, [] {});
+  const int st = compress_decode_seq<KVF, IDXF, ACTF, W, TPC>(P, w, cc, u, pos, proj, splits, B, blockIdx.x, red,
+                                                              mrg, nullptr, rtab, [] {});
+  advance_tokens(cc, blockIdx.x, pos[blockIdx.x], st);
 }
 
 // c4a: the role-split body, one block of d + D_I threads (rounded up
@@ -35,7 +36,9 @@ __global__ __launch_bounds__(1024) void k_compress_c4a(LayerParams P, Weights w,
                                                        const float* __restrict__ proj, int splits, int B) {
   __shared__ __attribute__((aligned(16))) float red[64];
   __shared__ float rtab[192];
-  compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, splits, B, blockIdx.x, red, rtab, nullptr, [] {});
+  const int st =
+      compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, splits, B, blockIdx.x, red, rtab, nullptr, [] {});
+  advance_tokens(cc, blockIdx.x, pos[blockIdx.x], st);
 }
 
 // Ratio 0: only the raw sliding-window row.
@@ -56,6 +59,168 @@ __global__ __launch_bounds__(256) void k_raw_insert_decode(LayerParams P, Cache 
   store_row2<KVF>(cc.raw + ((size_t)b * P.swa + (p & (P.swa - 1))) * P.row_bytes, z, c, act, d, P.n_rot, red);
   lds_barrier();
   if (threadIdx.x == 0 && cc.n_tokens) cc.n_tokens[b] = p + 1;
+}
+
+// ------------------------------------------------------------ c128a decode
+// The 128-slot window of a c128a row pooled channel slice by channel slice:
+// the per-channel softmax of the pages' compressor needs no other channel, so
+// slice g (64 channels) of sequence b is one block, and only the row's
+// RMSNorm sum and the E4M3 scale need all channels -- a second, per-sequence
+// kernel takes the slices' partial sums and finishes the row.  (One block per
+// sequence would pull the whole 512 KB window state and 256 KB of APE through
+// one compute unit.)
+//
+// k_c128a_slices: grid (B, d / 64), 256 threads: thread t pools channel pair
+// 64 g + 2 (t % 32) over window slots 16 (t / 32) .. +15 (on a boundary step;
+// the 8 parts merged through LDS), writes y and the slice's (sum y^2,
+// max |gamma y| of the non-RoPE channels) to the workspace, and stores this
+// token's (kappa, sigma) of the slice in slot p % 128.  Slice 0 also stores
+// the raw row (u rotated at p).
+constexpr int kC128Parts = 8, kC128SlotsPer = 128 / kC128Parts;
+
+template <int KVF, int ACTF>
+__global__ __launch_bounds__(256) void k_c128a_slices(LayerParams P, Weights w, Cache cc, const void* __restrict__ u,
+                                                      const int32_t* __restrict__ pos, const float* __restrict__ proj,
+                                                      int splits, int B, float* __restrict__ pool_ws) {
+  __shared__ float mrg[kC128Parts][32][6];
+  __shared__ float red[64];
+  const int b = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int q = tid & 31, part = tid >> 5;
+  const int d = P.d, dn = d - P.n_rot, c = 64 * g + 2 * q;
+  const int p = pos[b];
+  const int nt = seq_tokens(cc, b, p);
+  float2 ka = make_float2(0.f, 0.f), sa = ka;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {   // this token's projections, the K slices summed in order
+    const float* pj = proj + ((size_t)min(s, splits - 1) * B + b) * P.ncol;
+    const float2 k2 = ld2(pj + c), s2 = ld2(pj + d + c);
+    if (s < splits) {
+      ka.x += k2.x; ka.y += k2.y;
+      sa.x += s2.x; sa.y += s2.y;
+    }
+  }
+  const bool ok = p >= 0 && seq_ok(cc, p, nt);
+  const bool emit = ok && (p + 1) % 128 == 0;
+  const float* skv = cc.st_kv + (size_t)b * 128 * d;
+  const float* ssc = cc.st_sc + (size_t)b * 128 * d;
+  if (emit) {   // block-uniform: the window of row (p + 1) / 128 - 1 is the whole ring, slot = position j
+    PoolAcc a0, a1;
+    float2 kv[kC128SlotsPer], sc[kC128SlotsPer], ap[kC128SlotsPer];
+#pragma unroll
+    for (int jj = 0; jj < kC128SlotsPer; ++jj) {
+      const int j = kC128SlotsPer * part + jj;
+      kv[jj] = ld2(skv + (size_t)j * d + c);
+      sc[jj] = ld2(ssc + (size_t)j * d + c);
+      ap[jj] = ld2(w.ape + (size_t)j * d + c);
+    }
+    const int jc = p & 127;   // this token's slot holds the previous window's token: take the registers
+    float e0[kC128SlotsPer], e1[kC128SlotsPer], k0[kC128SlotsPer], k1[kC128SlotsPer];
+#pragma unroll
+    for (int jj = 0; jj < kC128SlotsPer; ++jj) {
+      const bool cur = kC128SlotsPer * part + jj == jc;
+      const float2 k = cur ? ka : kv[jj], e = cur ? sa : sc[jj];
+      e0[jj] = e.x + ap[jj].x;
+      e1[jj] = e.y + ap[jj].y;
+      k0[jj] = k.x;
+      k1[jj] = k.y;
+    }
+    a0.add_round(e0, k0);
+    a1.add_round(e1, k1);
+    float* mm = mrg[part][q];
+    mm[0] = a0.m; mm[1] = a0.s; mm[2] = a0.acc;
+    mm[3] = a1.m; mm[4] = a1.s; mm[5] = a1.acc;
+    lds_barrier();
+    float ss = 0.f, mx = 0.f;
+    if (part == 0) {   // merge the parts' online-softmax states
+      float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < kC128Parts; ++r) {
+        m0 = fmaxf(m0, mrg[r][q][0]);
+        m1 = fmaxf(m1, mrg[r][q][3]);
+      }
+      float s0 = 0.f, c0 = 0.f, s1 = 0.f, c1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < kC128Parts; ++r) {
+        const float f0 = __expf(mrg[r][q][0] - m0), f1 = __expf(mrg[r][q][3] - m1);
+        s0 += mrg[r][q][1] * f0;
+        c0 += mrg[r][q][2] * f0;
+        s1 += mrg[r][q][4] * f1;
+        c1 += mrg[r][q][5] * f1;
+      }
+      const float2 y = make_float2(s0 > 0.f ? c0 / s0 : 0.f, s1 > 0.f ? c1 / s1 : 0.f);
+      *(float2*)(pool_ws + (size_t)b * d + c) = y;
+      const float2 gm = ld2(w.gamma + c);
+      ss = y.x * y.x + y.y * y.y;
+      mx = c < dn ? fmaxf(fabsf(gm.x * y.x), fabsf(gm.y * y.y)) : 0.f;
+    }
+    const float2 t = cmp::block_sum_max(ss, mx, red);
+    if (tid == 0) *(float2*)(pool_ws + (size_t)B * d + ((size_t)b * 8 + g) * 2) = t;
+  }
+  if (ok && part == 0) {   // this token's projections -> state slot p % 128
+    const size_t o = ((size_t)b * 128 + (p & 127)) * d + c;
+    *(float2*)(cc.st_kv + o) = ka;
+    *(float2*)(cc.st_sc + o) = sa;
+  }
+  if (g == 0 && ok) {      // raw sliding-window row: u rotated at p (raw frame), slot p % swa
+    const int cr = 2 * tid;
+    const float2 uu = load2<ACTF>(u, (long)b * d + min(cr, d - 2));
+    const float2 z = rope2(P, uu, cr, d, P.n_rot, p);
+    store_row2<KVF>(cc.raw + ((size_t)b * P.swa + (p & (P.swa - 1))) * P.row_bytes, z, cr, cr < d, d, P.n_rot, red);
+  }
+}
+
+// k_c128a_finish: grid (B), 256 threads (channel pair 2 t): on a boundary
+// step, RMSNorm with the slices' sums, RoPE at i * 128 (compressed frame), the
+// E4M3 scale inv * max |gamma y| (the row is (gamma y) inv with inv > 0), and
+// row i stored; the sequence's status bits and token count.
+template <int KVF>
+__global__ __launch_bounds__(256) void k_c128a_finish(LayerParams P, Weights w, Cache cc,
+                                                      const int32_t* __restrict__ pos,
+                                                      const float* __restrict__ pool_ws, int B) {
+  __shared__ float red[64];
+  const int b = blockIdx.x, tid = threadIdx.x, c = 2 * tid;
+  const int d = P.d, dn = d - P.n_rot, nsl = d / 64;
+  const int p = pos[b];
+  const int nt = seq_tokens(cc, b, p);
+  if (p < 0 || !seq_ok(cc, p, nt)) {
+    if (tid == 0 && cc.status) atomicOr(&cc.status[b], p < 0 ? CKV_STATUS_BAD_POS : CKV_STATUS_SEQUENCE);
+    return;
+  }
+  const bool emit = (p + 1) % 128 == 0;
+  const int i = (p + 1) / 128 - 1;
+  if (emit && i >= P.cap && tid == 0 && cc.status) atomicOr(&cc.status[b], CKV_STATUS_CAPACITY);
+  if (emit && i < P.cap) {
+    float ss = 0.f, mx = 0.f;
+    for (int g = 0; g < nsl; ++g) {
+      const float2 t = ld2(pool_ws + (size_t)B * d + ((size_t)b * 8 + g) * 2);
+      ss += t.x;
+      mx = fmaxf(mx, t.y);
+    }
+    const float inv = 1.0f / sqrtf(ss / (float)d + P.eps);
+    const bool act = c < d;
+    const float2 y = ld2(pool_ws + (size_t)b * d + min(c, d - 2));
+    const float2 gm = ld2(w.gamma + min(c, d - 2));
+    float2 z = make_float2(gm.x * (y.x * inv), gm.y * (y.y * inv));
+    if (c >= dn && act) {
+      float cs, sn;
+      rope_cs_c(P, (c - dn) >> 1, (double)i * 128, &cs, &sn);
+      z = make_float2(z.x * cs - z.y * sn, z.x * sn + z.y * cs);
+    }
+    uint8_t* dst = cc.comp + ((size_t)b * P.cap + i) * P.row_bytes;
+    if constexpr (KVF == CKV_E4M3) {
+      const float amax = mx * inv;
+      const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+      if (act) {
+        if (c < dn) *(uint16_t*)(dst + c) = (uint16_t)(f32_to_e4m3(z.x / sc) | (f32_to_e4m3(z.y / sc) << 8));
+        else *(uint32_t*)(dst + dn + 2 * (c - dn)) = pack_bf16x2(z.x, z.y);
+      }
+      if (tid == 0) *(float*)(dst + dn + 2 * P.n_rot) = sc;
+    } else {
+      store_row2<KVF>(dst, z, c, act, d, P.n_rot, red);
+    }
+  }
+  lds_barrier();
+  advance_tokens(cc, b, p, 0);
 }
 
 // ------------------------------------------------------------ prefill
@@ -199,9 +364,13 @@ __global__ void k_advance_tokens(Cache cc, int seq, int pos0, int T) {
 
 template <int KVF, int IDXF, int ACTF>
 static void go_decode(const LayerParams& P, const Weights& w, const Cache& c, const void* u,
-                      const int32_t* pos, int B, const float* part, int splits, hipStream_t st) {
+                      const int32_t* pos, int B, const float* part, int splits, float* pool_ws, hipStream_t st) {
   const int np = P.d / 2;
-  if (P.ratio == 4 && splits <= 4)
+  if (P.ratio == 128 && c128a_sliced(P) && splits <= 4) {
+    hipLaunchKernelGGL((k_c128a_slices<KVF, ACTF>), dim3(B, P.d / 64), dim3(256), 0, st, P, w, c, u, pos, part,
+                       splits, B, pool_ws);
+    hipLaunchKernelGGL((k_c128a_finish<KVF>), dim3(B), dim3(256), 0, st, P, w, c, pos, pool_ws, B);
+  } else if (P.ratio == 4 && splits <= 4)
     hipLaunchKernelGGL((k_compress_c4a<KVF, IDXF, ACTF>), dim3(B), dim3((P.d + P.DI + 63) / 64 * 64), 0, st, P, w,
                        c, u, pos, part, splits, B);
   else if (P.ratio == 4)
@@ -232,9 +401,10 @@ static void go_decode(const LayerParams& P, const Weights& w, const Cache& c, co
   } while (0)
 
 int launch_compress_decode(const LayerParams& P, const Weights& w, const Cache& c, const void* u,
-                           const int32_t* pos, int B, const float* part, int splits, void* stream) {
+                           const int32_t* pos, int B, const float* part, int splits, float* pool_ws,
+                           void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  CKV_DISPATCH_KV_IDX_ACT(go_decode, P, w, c, u, pos, B, part, splits, st);
+  CKV_DISPATCH_KV_IDX_ACT(go_decode, P, w, c, u, pos, B, part, splits, pool_ws, st);
   return (int)hipGetLastError();
 }
 

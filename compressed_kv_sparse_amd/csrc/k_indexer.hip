@@ -1384,6 +1384,7 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
   *(u32x4*)(gh + 4 * tid) = (u32x4){0u, 0u, 0u, 0u};
   if (st < 0 || V <= k) {   // bad position (V = 0), or every visible row is taken
     for (int j = tid; j < k; j += 1024) o[j] = j < V ? j : -1;
+    advance_tokens(cc, qn, Q.p, st);
     return;
   }
   lds_barrier();   // idx_row complete
@@ -1429,6 +1430,7 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
       if (tid == (int)(bin >> 2) && i == (int)(bin & 3)) hv[i] += 1u;
   }
   topk_decode_select(P, V, kr, hv, o);
+  advance_tokens(cc, qn, Q.p, st);
 }
 
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,
