@@ -79,9 +79,11 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
     if (prefill) {
       rps = rows;
     } else {
-      // about ten splits per query, each 2 to 10 tiles of 32 rows (a block's
-      // fixed cost is small next to a tile's, and more blocks fill the chip)
-      rps = (rows + 9) / 10;
+      // about 192 blocks over the batch, each split 2 to 10 tiles of 32 rows
+      // (measured at 128k: 16 queries x 10 splits, 32 x 5 and 8 x 26 run
+      // fastest; half or twice the blocks are 3-30 % slower)
+      const int target = (192 + n / 2) / n > 1 ? (192 + n / 2) / n : 1;
+      rps = (rows + target - 1) / target;
       rps = rps < 64 ? 64 : rps > 320 ? 320 : rps;
     }
   } else {

@@ -167,11 +167,11 @@ def test_static_workspace_step_refuses_what_does_not_fit():
     """The workspace-free decode step checks everything on the host first: a
     batch whose workspace exceeds the library's array, and the ordinary
     argument errors, return before any GPU call."""
-    d = desc(batch=64, comp_cap=32768)
-    assert L.workspace_bytes(d, L.CKV_MODE_DECODE, 64) > L.CKV_STATIC_WORKSPACE_BYTES
+    d = desc(batch=128, comp_cap=32768)
+    assert L.workspace_bytes(d, L.CKV_MODE_DECODE, 128) > L.CKV_STATIC_WORKSPACE_BYTES
     st = lambda d, B, **k: L.decode_step_static(d, weights(), cache(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B,
                                                 k.get("topk", FAKE), FAKE)
-    assert st(d, 64) == L.CKV_E_WORKSPACE
+    assert st(d, 128) == L.CKV_E_WORKSPACE
     assert st(desc(), 17) == L.CKV_E_CAPACITY
     assert st(desc(), 0) == L.CKV_E_INVAL
     assert st(desc(), 16, topk=None) == L.CKV_E_INVAL
