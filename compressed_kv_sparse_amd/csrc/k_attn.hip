@@ -111,27 +111,35 @@ __device__ __forceinline__ void rot2(float& a, float& b, float c, float s) {
 // fp16 (MFMA f16 x f16 -> fp32).  E4M3 codes are exact in fp16 and a row's
 // scale multiplies the non-RoPE logit part and, for PV, the probability
 // operand of the non-RoPE channels; bf16 values convert to fp16 with 2^-11
-// relative rounding.  Probabilities lie in [0, e^8].
+// relative rounding, and so do the rotated query tail and the probabilities
+// (bf16 probabilities, 2^-9, would be 4x coarser: visible where rows of
+// opposite sign cancel).  Logits are kept in base-2 units (times scale
+// log2 e), so that a probability is one exp2; a skipped entry's logit is -inf
+// through a per-row bias.
 // Range guard: a bf16 value at or above 65520 in magnitude has no fp16 image
-// (it becomes infinite), which makes the logits of its row non-finite.  Every
-// lane checks the logits of the rows it holds; when any logit of the split is
-// non-finite the block recomputes the split in fp32 (k_attn_tile's second
-// half), so such inputs cost time, not accuracy.  Small values need no guard:
-// below 2^-14 fp16 keeps an absolute error under 2^-25, far inside the
+// (it becomes infinite).  An infinite operand makes the split's softmax sum
+// not finite (a +inf or NaN logit), or zero although the split has rows
+// (every logit -inf), or its output not finite (inf times a zero
+// probability); the block checks these once, at the end of the split, and
+// then recomputes the split in fp32 (k_attn_tile's second half), which also
+// takes a split whose normalised output exceeds fp16's range when it leaves
+// a partial (written then as two fp16 halves under a power-of-two scale).  So
+// such inputs cost time, not accuracy.  Small values need no guard: below
+// 2^-14 fp16 keeps an absolute error under 2^-25, far inside the
 // comparison's absolute tolerance.
 //
 // The block first lays out its split's row list in LDS as 64-bit row
 // addresses (bit 0 set: skipped entry, an all-zero row stands in); on ratio
-// 128 the compressed entries are computed instead (row jj at index jj), so
-// the table holds at most the raw slots and a top-k list.  Staging is
+// 128 (CMP) the compressed entries are computed instead (row jj at index jj),
+// so the table holds at most the raw slots and a top-k list.  Staging is
 // coalesced: consecutive lanes load consecutive 16-byte chunks of one stored
-// row and convert them into the row-major tile.  The tile is double-buffered:
-// tile t is multiplied from one buffer while tile t + 1 is written into the
-// other, two barriers per tile.  Global loads are unconditional and sit
-// outside any branch, so the compiler waits only for the tile being
-// committed; two tiles' loads are in flight while a tile is multiplied.  The
-// wave index comes from readfirstlane, so branches on the wave's role (around
-// MFMAs) are scalar branches, and the barriers inside the loop order LDS only
+// row and convert them into the row-major tile.  The tile is double-buffered: tile t is
+// multiplied from one buffer while tile t + 1 is written into the other, two
+// barriers per tile.  Global loads are unconditional and sit outside any
+// branch, so the compiler waits only for the tile being committed; two
+// tiles' loads are in flight while a tile is multiplied.  The wave index comes
+// from readfirstlane, so branches on the wave's role (around MFMAs) are
+// scalar branches, and the barriers inside the loop order LDS only
 // (lds_barrier).
 namespace attn {
 constexpr int D = 512, DN = 448, R = 32, SWA = 128;
@@ -147,6 +155,8 @@ __device__ __forceinline__ int tix(int R, int e) { return R * KP + ((((e >> 3) ^
 constexpr int MAXK = 2048;                   // top-k entries (the layer check caps top_k here)
 constexpr int MAXL = SWA + MAXK + 4 * R;     // row-table entries of one split (+ padding tiles)
 constexpr int RAW_TILES = SWA / R;           // the raw slots fill the first four tiles
+constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+constexpr float MOVE2 = 8.f * LOG2E;         // the running max moves by more than e^8 only
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -183,14 +193,23 @@ __device__ __forceinline__ u32x2 ds_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                        (__attribute__((address_space(3))) i16x4_t*)(p)));
 }
+// 16 bytes from a global address held as an integer
+__device__ __forceinline__ u32x4 ldg16(uint64_t a) {
+  return *(const __attribute__((address_space(1))) u32x4*)(a);
+}
+__device__ __forceinline__ float ldg_f32(uint64_t a) {
+  return *(const __attribute__((address_space(1))) float*)(a);
+}
 }  // namespace attn
 
 // The row skipped list entries point at: zeros, so that a skipped row adds
-// nothing to PV (its logit is -inf through its scale slot) without a select
+// nothing to PV (its logit is -inf through its bias slot) without a select
 // per staged value.  Written never.
 __device__ __attribute__((aligned(256))) uint8_t g_attn_zero_row[2048];
 
-template <int KVF>
+// CMP: ratio-128 layers, whose compressed entries are computed from their
+// index instead of read from the row table.
+template <int KVF, bool CMP>
 __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, const uint16_t* __restrict__ q,
                                                    const int32_t* __restrict__ pos, int seq_fixed, int pos0,
                                                    const int32_t* __restrict__ topk, int rows_per_split,
@@ -203,14 +222,16 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   constexpr int CPR = F8 ? 36 : 64;                 // chunks per row
   constexpr int IT = (R * CPR + NT - 1) / NT;       // 4 (bf16) or 3 (E4M3)
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][R * KP];
-  __shared__ __attribute__((aligned(16))) float Sp[8][2][4][64];   // partial non-RoPE logits per wave
-  __shared__ __attribute__((aligned(16))) float St[4][2][4][64];   // RoPE-tail logits per head group
-  __shared__ uint64_t rtab[MAXL];                                  // row addresses of the split
-  __shared__ __attribute__((aligned(16))) float rsc[2][R];
+  __shared__ __attribute__((aligned(16))) float Sp[8][2][4][64];            // partial logits per wave
+  __shared__ __attribute__((aligned(16))) float St[F8 ? 4 : 1][2][4][64];   // E4M3: RoPE-tail logits per head group
+  __shared__ uint64_t rtab[MAXL];                                           // row addresses of the split
+  __shared__ __attribute__((aligned(16))) float rsc[2][R];                  // E4M3 row scales
+  __shared__ __attribute__((aligned(16))) float rbi[2][R];                  // logit bias: 0, or -inf (skipped)
   // cos / sin tables of pair j: [0] at p in the raw frame, [1] at p in the
   // compressed frame, [2] the frame switch (angle p (theta_c - theta))
   __shared__ float cs_[3][32], sn_[3][32];
-  __shared__ int tk_lim, any_bad;
+  __shared__ u32x4 qt_[4][2][64];   // the tail waves' stored query tails, for the frame switch
+  __shared__ int tk_lim, any_bad, any_row;   // any_row: the split has an entry that is not skipped
 
   const int qn = blockIdx.x / nsplit, split = blockIdx.x - qn * nsplit;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -232,6 +253,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   const bool switches = P.two_bases && !start_comp && tile0 + ntiles > RAW_TILES;
   const bool end_comp = tile0 + ntiles > RAW_TILES;          // frame of the split's output
   const bool inv = !(P.flags & CKV_FLAG_NO_INV_ROPE);
+  const float c2 = P.scale * LOG2E;                          // logit -> base-2 units
 
   // ---- the split's row list -> rtab.  The top-k list ends at its first
   // entry >= V; entries < 0 are skipped.  The list's loads go out first, then
@@ -241,6 +263,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   if (tid == 0) {
     tk_lim = K;
     any_bad = 0;
+    any_row = 0;
   }
   if (K) {
     const int32_t* tkg = topk + (size_t)qn * P.topk;
@@ -276,11 +299,14 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     const int j = j0 + x;
     const int t = A.p - SWA + 1 + j;
     uint64_t v = (uint64_t)dummy | 1u;
-    if (j < j1 && j < SWA && t >= 0)
+    if (j < j1 && j < SWA && t >= 0) {
       v = (uint64_t)(decode ? cc.raw + ((size_t)A.seq * P.swa + (t & (P.swa - 1))) * P.row_bytes
                             : cc.stage + (size_t)(t - pos0 + P.swa - 1) * P.row_bytes);
+      any_row = 1;
+    }
     if (!(j < j1 && j >= SWA && P.ratio == 4)) rtab[x] = v;
   }
+  if (CMP && tid == 0 && min(j1, SWA + A.V) > max(j0, SWA)) any_row = 1;   // computed entries
   if (K) {   // top-k entries of this split, from the registers that hold them
 #pragma unroll
     for (int e = 0; e < MAXK / NT; ++e) {
@@ -289,41 +315,48 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       if (jj < K && x >= 0 && SWA + jj < j1) {
         const int row = tkv[e];
         const bool ok = jj < tk_end && row >= 0 && row < A.V;
+        if (ok) any_row = 1;
         rtab[x] = ok ? (uint64_t)(cc.comp + ((size_t)A.seq * P.cap + row) * P.row_bytes) : ((uint64_t)dummy | 1u);
       }
     }
   }
   lds_barrier();
-  // address of split entry x: from the table, or (ratio 128 compressed
-  // entries) computed; both evaluated, so the caller's loads stay unconditional
+  // address of ratio-128 compressed entry j (list index)
+  auto comp_addr = [&](int j) -> uint64_t {
+    const int jj = j - SWA;
+    return (j < j1 && jj < A.V) ? (uint64_t)(cc.comp + ((size_t)A.seq * P.cap + jj) * P.row_bytes)
+                                : ((uint64_t)dummy | 1u);
+  };
+  // address of split entry x (any x, for the fp32 recompute)
   auto addr_of = [&](int x) -> uint64_t {
-    const uint64_t tv = rtab[min(x, MAXL - 1)];
-    if (P.ratio != 128) return tv;
-    const int j = j0 + x, jj = j - SWA;
-    const uint64_t cv = (j < j1 && jj < A.V) ? (uint64_t)(cc.comp + ((size_t)A.seq * P.cap + jj) * P.row_bytes)
-                                             : ((uint64_t)dummy | 1u);
-    return j >= SWA ? cv : tv;
+    if (CMP && j0 + x >= SWA) return comp_addr(j0 + x);
+    return rtab[min(x, MAXL - 1)];
   };
 
   // staging: item e of this thread is chunk it % CPR of tile row it / CPR,
   // it = tid + NT e; items past the tile read the zero row and are dropped.
-  // Thread t < 32 also loads the scale of row t.
+  // Thread t < 32 also loads the scale of row t (E4M3) and its skip bit.
   struct Stg {
     u32x4 v[IT];
     float s;
     bool sok;
   };
   auto issue = [&](Stg& S, int tile) {
+    // tiles hold one row class; on CMP layers a compressed tile's addresses
+    // are computed (a uniform branch)
+    const bool ctile = CMP && __builtin_amdgcn_readfirstlane(j0 + tile * R) >= SWA;
 #pragma unroll
     for (int e = 0; e < IT; ++e) {
       const int it = tid + NT * e;
       const int row = min(it / CPR, R - 1), ch = it % CPR;
-      const uint64_t ra = addr_of(tile * R + row);
+      const int x = tile * R + row;
+      const uint64_t ra = ctile ? comp_addr(j0 + x) : rtab[min(x, MAXL - 1)];
       const int off = !F8 ? 16 * ch : (ch < 28 ? 16 * ch : DN + 16 * (ch - 28));
-      S.v[e] = *(const u32x4*)((const uint8_t*)(ra & ~(uint64_t)1) + off);
+      S.v[e] = ldg16((ra & ~(uint64_t)1) + off);
     }
-    const uint64_t rs = addr_of(tile * R + (tid & 31));
-    S.s = F8 ? *(const float*)((const uint8_t*)(rs & ~(uint64_t)1) + DN + 128) : 1.f;
+    const int xs = tile * R + (tid & 31);
+    const uint64_t rs = ctile ? comp_addr(j0 + xs) : rtab[min(xs, MAXL - 1)];
+    S.s = F8 ? ldg_f32((rs & ~(uint64_t)1) + DN + 128) : 1.f;
     S.sok = !(rs & 1u);
   };
   auto pin = [&](Stg& S) {
@@ -349,11 +382,15 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
         }
       }
     }
-    if (tid < 32) rsc[buf][tid] = S.sok ? S.s : -1.f;
+    if (tid < 32) {
+      rbi[buf][tid] = S.sok ? 0.f : -INFINITY;
+      if (F8) rsc[buf][tid] = S.s;
+    }
   };
 
-  // rotated query of this lane's head in fp16, channels 256 cg + 32 ks + 8 g
-  // .. +7 (B operand), in the frame of the split's first row class
+  // query of this lane's head in fp16, channels 256 cg + 32 ks + 8 g .. +7
+  // (B operand); the tail rotated at p in the frame of the split's first row
+  // class.  LDS keeps the stored tail for the frame switch.
   Stg S0, S1;
   {
     const int f0 = start_comp ? 1 : 0;
@@ -362,44 +399,44 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     if (!F8) issue(S1, 1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      u32x4 v = Bq[ks];
+      const u32x4 v = Bq[ks];
       if (tailw && ks >= 6) {
+        if (switches) qt_[hg][ks - 6][lane] = v;
         const int jb = (32 * ks + 8 * g + 256 - DN) / 2;   // first pair index of this chunk
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float a = lo_bf16(v[e]), b = hi_bf16(v[e]);
           rot2(a, b, cs_[f0][jb + e], sn_[f0][jb + e]);
-          v[e] = pk_f16(a, b);
+          Bq[ks][e] = pk_f16(a, b);
         }
       } else {
-        v = bf16x8_to_f16(v);
+        Bq[ks] = bf16x8_to_f16(v);
       }
-      Bq[ks] = v;
     }
   }
 
-  float m_i = -INFINITY, l_i = 0.f;
-  bool bad = false;   // a logit of a row this lane holds was not finite
+  float m_i = -INFINITY, l_i = 0.f;   // running max (base-2 units) and sum of this lane's head
   f32x4 O[16];
 #pragma unroll
   for (int n = 0; n < 16; ++n) O[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const float scale = P.scale;
   // transpose-read addresses: lane 16 g + 4 j + a reads row base + j,
   // channels ch0 + 4 a .. + 3 (base 4 g, then 16 + 4 g)
   const int tr_row = 4 * g + ((lane & 15) >> 2), tr_col = 4 * (lane & 3);
 
-  // raw slots -> compressed entries: the query tail and the output tail turn
-  // by p (theta_c - theta) (tail waves only; channels 448 + 16 (n - 12) + 4 g
-  // + i of O[n] are pairs 8 (n - 12) + 2 g + i / 2)
+  // raw slots -> compressed entries: the query tail is rotated afresh in the
+  // compressed frame, and the output tail turns by p (theta_c - theta) (tail
+  // waves only; channels 448 + 16 (n - 12) + 4 g + i of O[n] are pairs
+  // 8 (n - 12) + 2 g + i / 2)
   auto frame_switch = [&]() {
     if (!tailw) return;
 #pragma unroll
     for (int ks = 6; ks < 8; ++ks) {
       const int jb = (32 * ks + 8 * g + 256 - DN) / 2;
+      const u32x4 qs = qt_[hg][ks - 6][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float a = lo_f16(Bq[ks][e]), b = hi_f16(Bq[ks][e]);
-        rot2(a, b, cs_[2][jb + e], sn_[2][jb + e]);
+        float a = lo_bf16(qs[e]), b = hi_bf16(qs[e]);
+        rot2(a, b, cs_[1][jb + e], sn_[1][jb + e]);
         Bq[ks][e] = pk_f16(a, b);
       }
     }
@@ -420,7 +457,8 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   auto tile_math = [&](int buf) {
     const uint16_t* kb = Ks[buf];
     // partial logits S^T over this wave's channel half: rows 16 nt + 4 g + i;
-    // the tail wave keeps its RoPE channels (k-steps 6, 7) apart
+    // with E4M3 rows the tail wave keeps its RoPE channels (k-steps 6, 7)
+    // apart (the row scale multiplies the code channels only)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       f32x4 an = {0.f, 0.f, 0.f, 0.f}, at = {0.f, 0.f, 0.f, 0.f};
@@ -431,10 +469,10 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       }
       const u32x4 a6 = *(const u32x4*)&kb[tix(16 * nt + r, 256 * cg + 192 + 8 * g)];
       const u32x4 a7 = *(const u32x4*)&kb[tix(16 * nt + r, 256 * cg + 224 + 8 * g)];
-      if (tailw) {
+      if (F8 && tailw) {
         at = mfma_f16(a6, Bq[6], at);
         at = mfma_f16(a7, Bq[7], at);
-        *(f32x4*)&St[hg][nt][0][4 * lane] = at;
+        *(f32x4*)&St[F8 ? hg : 0][nt][0][4 * lane] = at;
       } else {
         an = mfma_f16(a6, Bq[6], an);
         an = mfma_f16(a7, Bq[7], an);
@@ -442,38 +480,42 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       *(f32x4*)&Sp[wave][nt][0][4 * lane] = an;
     }
     lds_barrier();
-    // logits of this lane's head for its 8 rows; online softmax with one
-    // head per lane: the tile max and sum reduce 8 values in the lane and
-    // across the 4 lanes of the head (lanes r, r + 16, r + 32, r + 48).  The reference max
-    // moves only when a tile's max exceeds it by more than 8, so probabilities
-    // stay below e^8 and the rescale of the accumulators is rare.
+    // logits of this lane's head for its 8 rows, in base-2 units; online
+    // softmax with one head per lane: the tile max and sum reduce 8 values in
+    // the lane and across the 4 lanes of the head (lanes r, r + 16, r + 32,
+    // r + 48).  The reference max moves only when a tile's max exceeds it by
+    // more than e^8, so the rescale of the accumulators is rare.
     float Sv[2][4];
     float mx = -INFINITY;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const f32x4 n0 = *(const f32x4*)&Sp[hg][nt][0][4 * lane];
       const f32x4 n1 = *(const f32x4*)&Sp[hg + 4][nt][0][4 * lane];
-      const f32x4 tl = *(const f32x4*)&St[hg][nt][0][4 * lane];
-      const f32x4 sc = *(const f32x4*)&rsc[buf][16 * nt + 4 * g];
+      const f32x4 bi = *(const f32x4*)&rbi[buf][16 * nt + 4 * g];
+      f32x4 tl = {0.f, 0.f, 0.f, 0.f}, sc = {1.f, 1.f, 1.f, 1.f};
+      if (F8) {
+        tl = *(const f32x4*)&St[F8 ? hg : 0][nt][0][4 * lane];
+        sc = *(const f32x4*)&rsc[buf][16 * nt + 4 * g];
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float lg = ((n0[i] + n1[i]) * sc[i] + tl[i]) * scale;
-        bad |= sc[i] >= 0.f && !(fabsf(lg) <= 3.4e38f);
-        Sv[nt][i] = sc[i] < 0.f ? -INFINITY : lg;
+        float s = n0[i] + n1[i];
+        if (F8) s = fmaf(s, sc[i], tl[i]);
+        Sv[nt][i] = fmaf(s, c2, bi[i]);
         mx = fmaxf(mx, Sv[nt][i]);
       }
     }
     mx = rows4_max(mx);
-    const bool move = mx > m_i + 8.f;
+    const bool move = mx > m_i + MOVE2;
     const float mn = move ? mx : m_i;
-    const bool none = mn == -INFINITY;
-    const float alpha = (none || !move) ? 1.f : __expf(m_i - mn);
+    const float mref = mn == -INFINITY ? 0.f : mn;   // nothing seen yet: every logit is -inf
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_i - mn) : 1.f;
     float ps = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pv = none ? 0.f : __expf(Sv[nt][i] - mn);
+        const float pv = __builtin_amdgcn_exp2f(Sv[nt][i] - mref);
         Sv[nt][i] = pv;
         ps += pv;
       }
@@ -495,7 +537,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       bpp[e2] = pk_f16(a, b);
       if (F8) {
         const f32x2_t sc = *(const f32x2_t*)&rsc[buf][16 * nt + 4 * g + i];
-        bps[e2] = pk_f16(a * fmaxf(sc[0], 0.f), b * fmaxf(sc[1], 0.f));
+        bps[e2] = pk_f16(a * sc[0], b * sc[1]);
       } else {
         bps[e2] = bpp[e2];
       }
@@ -551,9 +593,23 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   }
 
   const int fe = end_comp ? 1 : 0;   // frame the output ended in
+  // the range guard's checks (see above): a sum that is not finite, or zero
+  // although the split has rows, an output that is not finite (the sum of its
+  // values is then inf or NaN), or a normalised output beyond the fp16
+  // partial's range, sends the split to the fp32 recompute
+  const float il = l_i > 0.f ? 1.f / l_i : 0.f;
+  float om = 0.f, os = 0.f;
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    om = fmaxf(om, fmaxf(fmaxf(fabsf(O[n][0]), fabsf(O[n][1])), fmaxf(fabsf(O[n][2]), fabsf(O[n][3]))));
+    os += (O[n][0] + O[n][1]) + (O[n][2] + O[n][3]);
+  }
+  bool bad = !(l_i < INFINITY) || (l_i == 0.f && any_row) || !(os - os == 0.f);
+  if (nsplit > 1) bad |= !(om * il < 65504.f);
   if (__ballot(bad) != 0ull && lane == 0) any_bad = 1;
   lds_barrier();
   if (any_bad) {
+    const float scale = P.scale;
     // ---- range guard: the split again, in fp32, from the stored rows.  Four
     // passes of 16 heads, 32 threads per head, thread `sub` holding channels
     // 16 sub .. +15 (subs 28..31 hold the RoPE tail, pairs 8 (sub - 28) ..).
@@ -665,7 +721,6 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
 
   // lane (r, g) holds channels 256 cg + 16 n + 4 g + i of head `head`;
   // normalise and rotate the tail back by -p in the frame the split ended in
-  const float il = l_i > 0.f ? 1.f / l_i : 0.f;
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
     O[n] *= il;
@@ -690,7 +745,8 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     return;
   }
   // partial: this split's normalised output O / l in fp16 (half the bytes of
-  // fp32 to write here and to read in the merge), plus (m, l, 1)
+  // fp32 to write here and to read in the merge), plus (m, l, 1) with m in
+  // natural-log units
   const size_t pb = ((size_t)qn * nsplit + split) * H + head;
   uint16_t* ph = (uint16_t*)part_o;
 #pragma unroll
@@ -698,7 +754,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     const u32x2 w = {pk_f16(O[n][0], O[n][1]), pk_f16(O[n][2], O[n][3])};
     *(u32x2*)&ph[pb * D + 256 * cg + 16 * n + 4 * g] = w;
   }
-  if (g == 0 && cg == 0) *(float4*)(part_ml + pb * 4) = make_float4(m_i, l_i, 1.f, 0.f);
+  if (g == 0 && cg == 0) *(float4*)(part_ml + pb * 4) = make_float4(m_i * LN2, l_i, 1.f, 0.f);
 }
 
 // ----------------------------------------------------------------- vector
@@ -917,12 +973,14 @@ int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32
     dim3 grid(nq * ns, P.H / 64);
     const uint16_t* qq = (const uint16_t*)q;
     uint16_t* oo = (uint16_t*)out;
-    if (P.kv_fmt == CKV_BF16)
-      hipLaunchKernelGGL(k_attn_tile<CKV_BF16>, grid, dim3(512), 0, st, P, c, qq, pos, seq, pos0, topk, rps, ns,
-                         po, pml, oo);
-    else
-      hipLaunchKernelGGL(k_attn_tile<CKV_E4M3>, grid, dim3(512), 0, st, P, c, qq, pos, seq, pos0, topk, rps, ns,
-                         po, pml, oo);
+#define CKV_AT(KF, CM) \
+  hipLaunchKernelGGL((k_attn_tile<KF, CM>), grid, dim3(512), 0, st, P, c, qq, pos, seq, pos0, topk, rps, ns, po, pml, oo)
+    const bool cmp = P.ratio == 128;
+    if (P.kv_fmt == CKV_BF16 && cmp) CKV_AT(CKV_BF16, true);
+    else if (P.kv_fmt == CKV_BF16) CKV_AT(CKV_BF16, false);
+    else if (cmp) CKV_AT(CKV_E4M3, true);
+    else CKV_AT(CKV_E4M3, false);
+#undef CKV_AT
     if (ns == 1) return (int)hipGetLastError();
   } else {
     dim3 grid(nq, ns, P.H / 16);
