@@ -193,6 +193,13 @@ __device__ __forceinline__ u32x2 ds_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                        (__attribute__((address_space(3))) i16x4_t*)(p)));
 }
+// Position of channel c in a split's fp16 partial row: channels
+// 256 cg + 16 n + 4 g + i sit at 256 cg + 64 g + 4 n + i, so that the lane
+// that accumulated them (lane 16 g + r of a cg wave) writes 128 contiguous
+// bytes; groups of four channels stay contiguous.
+__device__ __forceinline__ int part_pos(int c) {
+  return (c & ~255) | ((c >> 2 & 3) << 6) | ((c >> 4 & 15) << 2) | (c & 3);
+}
 // 16 bytes from a global address held as an integer
 __device__ __forceinline__ u32x4 ldg16(uint64_t a) {
   return *(const __attribute__((address_space(1))) u32x4*)(a);
@@ -241,30 +248,16 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   const int H = P.H;
   const int head = blockIdx.y * 64 + 16 * hg + r;
   const bool decode = pos != nullptr;
-  const AttnQuery A = attn_query(P, pos, seq_fixed, pos0, qn);
   const int j0 = split * rows_per_split;
-  const int j1 = min(A.n_list, j0 + rows_per_split);
-  const int ntiles = j1 > j0 ? (j1 - j0 + R - 1) / R : 0;
-  const int nent = (ntiles + 4) * R;   // table entries incl. the padding tiles the loop issues
-  const int K = (P.ratio == 4 && topk && j1 > SWA) ? P.topk : 0;   // splits of raw slots need no list
-  const uint8_t* dummy = g_attn_zero_row;
-  const int tile0 = j0 / R;                                  // list tile of the split's first tile
-  const bool start_comp = tile0 >= RAW_TILES;
-  const bool switches = P.two_bases && !start_comp && tile0 + ntiles > RAW_TILES;
-  const bool end_comp = tile0 + ntiles > RAW_TILES;          // frame of the split's output
-  const bool inv = !(P.flags & CKV_FLAG_NO_INV_ROPE);
-  const float c2 = P.scale * LOG2E;                          // logit -> base-2 units
+  // splits of raw slots need no list.  Neither this test nor the loads below
+  // involve the query's position, so they go out before its load returns.
+  const int K = (P.ratio == 4 && topk && j0 + rows_per_split > SWA) ? P.topk : 0;
 
   // ---- the split's row list -> rtab.  The top-k list ends at its first
   // entry >= V; entries < 0 are skipped.  The list's loads go out first, then
   // the query's (which depend on nothing), so that waiting for the list does
   // not wait for the query; the prologue's barriers order LDS only.
   int tkv[MAXK / NT];
-  if (tid == 0) {
-    tk_lim = K;
-    any_bad = 0;
-    any_row = 0;
-  }
   if (K) {
     const int32_t* tkg = topk + (size_t)qn * P.topk;
 #pragma unroll
@@ -276,6 +269,22 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) Bq[ks] = *(const u32x4*)(qr + 32 * ks);
   }
+  if (tid == 0) {
+    tk_lim = K;
+    any_bad = 0;
+    any_row = 0;
+  }
+  const AttnQuery A = attn_query(P, pos, seq_fixed, pos0, qn);
+  const int j1 = min(A.n_list, j0 + rows_per_split);
+  const int ntiles = j1 > j0 ? (j1 - j0 + R - 1) / R : 0;
+  const int nent = (ntiles + 4) * R;   // table entries incl. the padding tiles the loop issues
+  const uint8_t* dummy = g_attn_zero_row;
+  const int tile0 = j0 / R;                                  // list tile of the split's first tile
+  const bool start_comp = tile0 >= RAW_TILES;
+  const bool switches = P.two_bases && !start_comp && tile0 + ntiles > RAW_TILES;
+  const bool end_comp = tile0 + ntiles > RAW_TILES;          // frame of the split's output
+  const bool inv = !(P.flags & CKV_FLAG_NO_INV_ROPE);
+  const float c2 = P.scale * LOG2E;                          // logit -> base-2 units
   lds_barrier();
   if (K) {
     int first = K;
@@ -597,7 +606,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   // although the split has rows, an output that is not finite (the sum of its
   // values is then inf or NaN), or a normalised output beyond the fp16
   // partial's range, sends the split to the fp32 recompute
-  const float il = l_i > 0.f ? 1.f / l_i : 0.f;
+  const float il = l_i > 0.f ? __builtin_amdgcn_rcpf(l_i) : 0.f;
   float om = 0.f, os = 0.f;
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
@@ -711,8 +720,8 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       for (int c = 0; c < 16; c += 2) {
         const float a = acc[c] * down, b = acc[c + 1] * down;
         const uint32_t hi = pk_f16(a, b);
-        *(uint32_t*)&ph[pb * D + c0 + c] = hi;
-        *(uint32_t*)&ph[lo_half + pb * D + c0 + c] = pk_f16(a - lo_f16(hi), b - hi_f16(hi));
+        *(uint32_t*)&ph[pb * D + part_pos(c0 + c)] = hi;
+        *(uint32_t*)&ph[lo_half + pb * D + part_pos(c0 + c)] = pk_f16(a - lo_f16(hi), b - hi_f16(hi));
       }
       if (sub == 0) *(float4*)(part_ml + pb * 4) = make_float4(m, l, ldexpf(1.f, ex), 1.f);
     }
@@ -745,14 +754,16 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     return;
   }
   // partial: this split's normalised output O / l in fp16 (half the bytes of
-  // fp32 to write here and to read in the merge), plus (m, l, 1) with m in
+  // fp32 to write here and to read in the merge), in the order of part_pos
+  // (this lane's 64 channels contiguous), plus (m, l, 1) with m in
   // natural-log units
   const size_t pb = ((size_t)qn * nsplit + split) * H + head;
   uint16_t* ph = (uint16_t*)part_o;
 #pragma unroll
-  for (int n = 0; n < 16; ++n) {
-    const u32x2 w = {pk_f16(O[n][0], O[n][1]), pk_f16(O[n][2], O[n][3])};
-    *(u32x2*)&ph[pb * D + 256 * cg + 16 * n + 4 * g] = w;
+  for (int n = 0; n < 16; n += 2) {
+    const u32x4 w = {pk_f16(O[n][0], O[n][1]), pk_f16(O[n][2], O[n][3]), pk_f16(O[n + 1][0], O[n + 1][1]),
+                     pk_f16(O[n + 1][2], O[n + 1][3])};
+    *(u32x4*)&ph[pb * D + 256 * cg + 64 * g + 4 * n] = w;
   }
   if (g == 0 && cg == 0) *(float4*)(part_ml + pb * 4) = make_float4(m_i * LN2, l_i, 1.f, 0.f);
 }
@@ -876,8 +887,10 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
     const int sidx = (threadIdx.x & 63) + 64 * e;
     mlv[e] = *(const float4*)(part_ml + (b0 + (size_t)min(sidx, nsplit - 1) * H) * 4);
   }
+  // fp16 partials (the tile kernel's) hold channel c at attn::part_pos(c)
+  const int pcl = HALF ? attn::part_pos(cl) : cl;
   auto load_part = [&](int sp) -> float4 {
-    const size_t o = (b0 + (size_t)min(sp, nsplit - 1) * H) * d + cl;
+    const size_t o = (b0 + (size_t)min(sp, nsplit - 1) * H) * d + pcl;
     if constexpr (HALF) {
       const _Float16* hp = (const _Float16*)part_o + o;
       return make_float4((float)hp[0], (float)hp[1], (float)hp[2], (float)hp[3]);
@@ -945,7 +958,7 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
     const size_t lo_half = (size_t)gridDim.x * nsplit * H * d;
     for (int sp = 0; sp < nsplit; ++sp) {
       if (lsh[sp] == 0.f) continue;
-      const _Float16* hp = (const _Float16*)part_o + lo_half + (b0 + (size_t)sp * H) * d + cl;
+      const _Float16* hp = (const _Float16*)part_o + lo_half + (b0 + (size_t)sp * H) * d + pcl;
       const float wgt = wsh[sp];
       a.x += (float)hp[0] * wgt;
       a.y += (float)hp[1] * wgt;
