@@ -68,11 +68,12 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   memset(&L, 0, sizeof(L));
   const bool prefill = mode == CKV_MODE_PREFILL;
   const bool proj_mfma = P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16;
-  // the decode projection splits K over kProjSlices blocks per tile (partial
-  // sums, added by the compressor in slice order)
-  // (c128a layers, whose decode projection runs on its own, use 4 slices:
-  // 4 x 64 blocks instead of 64 latency-bound ones)
-  L.proj_splits = (!prefill && proj_mfma) ? (P.ratio == 128 ? 4 : kProjSlices) : 1;
+  // a decode projection launched on its own (c128a layers, and the
+  // separate-call c4a path) splits K over 4 blocks per tile (partial sums,
+  // added by the compressor in slice order): 4 x 64 blocks instead of 64
+  // latency-bound ones.  The single-call c4a step projects inside its scan
+  // launch with kProjSlices slices, which this region also holds.
+  L.proj_splits = (!prefill && proj_mfma) ? (kProjSlices > 4 ? kProjSlices : 4) : 1;
   const int rows = attn_max_rows(P);
   int rps;
   if (attn_uses_tiles(P)) {

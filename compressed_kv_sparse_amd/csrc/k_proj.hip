@@ -64,15 +64,18 @@ __global__ __launch_bounds__(256) void k_proj_mfma(const uint16_t* __restrict__ 
   }
 }
 
-// Decode (few rows): bf16 x bf16 on MFMA, one block of 16 waves per 16
+// Decode (few rows): bf16 x bf16 on MFMA, one block of 4 waves per 16
 // columns x 16 rows x one of gridDim.z slices of K.  Wave w takes the
-// slice's k-steps w, w + 16, ... (eight of them in flight per round, their
-// loads unconditional with the step index clamped); the 16 partial tiles are
+// slice's k-steps w, w + 4, ... (eight of them in flight per round, their
+// loads unconditional with the step index clamped); the 4 partial tiles are
 // summed through LDS in wave order, so the result is the same on every run.
 // Splitting K over blocks puts the weight stream on more compute units (a
 // unit keeps only a limited number of misses in flight).  grid: x = ncol / 16,
 // y = ceil(M / 16), z = K slices; writes part[slice][m][col].
-constexpr int kProjDecWaves = 16;
+// (Measured, c128a layer, 16 rows, K = 4096 in 4 slices: 5.1 us with 4 waves
+// of 8 k-steps each, 7.2 us with 8 waves, 10.7 us with 16 waves of 2 useful
+// k-steps and 6 clamped repeats; 2 waves 5.4 us, 8 slices 5.2-7.3 us.)
+constexpr int kProjDecWaves = 4;
 __global__ __launch_bounds__(1024) void k_proj_dec(const uint16_t* __restrict__ X, int M, int K, WCat wc, int ncol,
                                                    float* __restrict__ part) {
   proj_tile<kProjDecWaves>(X, M, K, wc, ncol, part, blockIdx.x * 16, blockIdx.y * 16, blockIdx.z, gridDim.z);
