@@ -431,6 +431,10 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   // transpose-read addresses: lane 16 g + 4 j + a reads row base + j,
   // channels ch0 + 4 a .. + 3 (base 4 g, then 16 + 4 g)
   const int tr_row = 4 * g + ((lane & 15) >> 2), tr_col = 4 * (lane & 3);
+  // per-lane tile offsets of the logit and PV reads; each access adds a
+  // compile-time offset
+  const int s_lane = tix(r, 256 * cg + 8 * g);
+  const int p_lane = tix(tr_row, 256 * cg + tr_col);
 
   // raw slots -> compressed entries: the query tail is rotated afresh in the
   // compressed frame, and the output tail turns by p (theta_c - theta) (tail
@@ -467,17 +471,20 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     const uint16_t* kb = Ks[buf];
     // partial logits S^T over this wave's channel half: rows 16 nt + 4 g + i;
     // with E4M3 rows the tail wave keeps its RoPE channels (k-steps 6, 7)
-    // apart (the row scale multiplies the code channels only)
+    // apart (the row scale multiplies the code channels only).  Element
+    // tix(16 nt + r, 256 cg + 32 ks + 8 g) is s_lane + 16 nt KP + 32 ks (the
+    // swizzle flips bit 0 of the chunk, which ks does not touch).
+    const uint16_t* ks_ = kb + s_lane;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       f32x4 an = {0.f, 0.f, 0.f, 0.f}, at = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 6; ++ks) {
-        const u32x4 a = *(const u32x4*)&kb[tix(16 * nt + r, 256 * cg + 32 * ks + 8 * g)];
+        const u32x4 a = *(const u32x4*)(ks_ + 16 * nt * KP + 32 * ks);
         an = mfma_f16(a, Bq[ks], an);
       }
-      const u32x4 a6 = *(const u32x4*)&kb[tix(16 * nt + r, 256 * cg + 192 + 8 * g)];
-      const u32x4 a7 = *(const u32x4*)&kb[tix(16 * nt + r, 256 * cg + 224 + 8 * g)];
+      const u32x4 a6 = *(const u32x4*)(ks_ + 16 * nt * KP + 192);
+      const u32x4 a7 = *(const u32x4*)(ks_ + 16 * nt * KP + 224);
       if (F8 && tailw) {
         at = mfma_f16(a6, Bq[6], at);
         at = mfma_f16(a7, Bq[7], at);
@@ -556,8 +563,9 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     const u32x4 bhi = tailw ? bpp : bps;
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
-      // rows tr_row and tr_row + 16 share bit 2, so one swizzled offset serves both
-      const uint16_t* tp = kb + tix(tr_row, 256 * cg + 16 * n + tr_col);
+      // element tix(tr_row, 256 cg + 16 n + tr_col) = p_lane + 16 n; rows
+      // tr_row and tr_row + 16 share bit 2, so one swizzled offset serves both
+      const uint16_t* tp = kb + p_lane + 16 * n;
       const u32x2 lo4 = ds_tr16(tp), hi4 = ds_tr16(tp + 16 * KP);
       const u32x4 a = {lo4[0], lo4[1], hi4[0], hi4[1]};
       O[n] = mfma_f16(a, n < 12 ? bps : bhi, O[n]);
@@ -570,8 +578,9 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   // same with the buffers swapped.  Each tile_math has its own barrier (logit
   // halves), and one barrier per tile publishes the next buffer.  bf16 rows
   // keep two tiles' loads in flight in registers (S0, S1); E4M3 rows one
-  // (S0 only: with the conversion temporaries a second set would spill).
-  // The frame switch runs before the first compressed tile (a scalar branch).
+  // (S0 only: measured slower with two, 29 -> 32 us on the window-only
+  // decode step).  The frame switch runs before the first compressed tile (a
+  // scalar branch).
   constexpr bool TWO = !F8;
   pin(S0);
   commit(S0, 0);
@@ -767,6 +776,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   }
   if (g == 0 && cg == 0) *(float4*)(part_ml + pb * 4) = make_float4(m_i * LN2, l_i, 1.f, 0.f);
 }
+
 
 // ----------------------------------------------------------------- vector
 // Any formats.  Block of 256 = 16 heads x 16 lanes; lane `sub` owns channels
@@ -986,9 +996,9 @@ int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32
     dim3 grid(nq * ns, P.H / 64);
     const uint16_t* qq = (const uint16_t*)q;
     uint16_t* oo = (uint16_t*)out;
+    const bool cmp = P.ratio == 128;
 #define CKV_AT(KF, CM) \
   hipLaunchKernelGGL((k_attn_tile<KF, CM>), grid, dim3(512), 0, st, P, c, qq, pos, seq, pos0, topk, rps, ns, po, pml, oo)
-    const bool cmp = P.ratio == 128;
     if (P.kv_fmt == CKV_BF16 && cmp) CKV_AT(CKV_BF16, true);
     else if (P.kv_fmt == CKV_BF16) CKV_AT(CKV_BF16, false);
     else if (cmp) CKV_AT(CKV_E4M3, true);
