@@ -24,6 +24,9 @@ CKV_F32, CKV_BF16, CKV_E4M3 = 0, 1, 2
 FMT = {"f32": CKV_F32, "bf16": CKV_BF16, "e4m3": CKV_E4M3}
 CKV_FLAG_NO_INV_ROPE = 1
 CKV_FLAG_IDX_NO_RELU = 2
+CKV_FLAG_SKIP_NORM = 4
+CKV_FLAG_SKIP_ROPE = 8
+CKV_FLAG_KEEP_F32 = 16
 CKV_MODE_DECODE, CKV_MODE_PREFILL = 0, 1
 CKV_MAX_CHUNK = 4096
 CKV_STATIC_WORKSPACE_BYTES = 48 << 20

@@ -43,11 +43,13 @@ bool make_params(const ckv_layer_desc* d, LayerParams* P) {
   P->ncol = d->ratio == 0 ? 0 : 2 * d->head_dim + (d->ratio == 4 ? 2 * d->idx_dim : 0);
   P->idx_rot = d->ratio == 4 ? (d->idx_dim < d->n_rot ? d->idx_dim : d->n_rot) : 0;
   const double base_c = d->rope_base_comp > 0.0 ? d->rope_base_comp : d->rope_base;
+  // CKV_FLAG_SKIP_ROPE: every frequency 0, so every rotation is the identity
+  const bool rope = !(d->flags & CKV_FLAG_SKIP_ROPE);
   for (int j = 0; j < 32; ++j) {
-    P->theta[j] = 2 * j < d->n_rot ? pow(d->rope_base, -2.0 * j / (double)d->n_rot) : 0.0;
-    P->theta_c[j] = 2 * j < d->n_rot ? pow(base_c, -2.0 * j / (double)d->n_rot) : 0.0;
+    P->theta[j] = rope && 2 * j < d->n_rot ? pow(d->rope_base, -2.0 * j / (double)d->n_rot) : 0.0;
+    P->theta_c[j] = rope && 2 * j < d->n_rot ? pow(base_c, -2.0 * j / (double)d->n_rot) : 0.0;
   }
-  P->two_bases = base_c != d->rope_base;
+  P->two_bases = rope && base_c != d->rope_base;
   return true;
 }
 
@@ -159,7 +161,12 @@ extern "C" int ckv_validate(const ckv_layer_desc* d) {
   if (!fmt_ok(d->kv_fmt, true) || !fmt_ok(d->act_fmt, false) || !fmt_ok(d->w_fmt, false))
     return CKV_E_UNSUPPORTED;
   if (d->kv_fmt == CKV_E4M3 && d->head_dim <= d->n_rot) return CKV_E_UNSUPPORTED;
-  if (d->flags & ~(CKV_FLAG_NO_INV_ROPE | CKV_FLAG_IDX_NO_RELU)) return CKV_E_UNSUPPORTED;
+  if (d->flags & ~(CKV_FLAG_NO_INV_ROPE | CKV_FLAG_IDX_NO_RELU | CKV_FLAG_SKIP_NORM | CKV_FLAG_SKIP_ROPE |
+                   CKV_FLAG_KEEP_F32))
+    return CKV_E_UNSUPPORTED;
+  if ((d->flags & CKV_FLAG_KEEP_F32) &&
+      (d->kv_fmt != CKV_F32 || d->act_fmt != CKV_F32 || d->w_fmt != CKV_F32 || (d->ratio == 4 && d->idx_fmt != CKV_F32)))
+    return CKV_E_UNSUPPORTED;
   if (d->ratio != 0) {
     if (d->comp_cap <= 0) return CKV_E_INVAL;
     if ((long long)d->comp_cap * d->ratio > (1ll << 30)) return CKV_E_UNSUPPORTED;

@@ -29,14 +29,26 @@ __device__ __forceinline__ void rope_lds(const LayerParams& P, float* z, int wid
   }
 }
 
+// 1 / rms of a row whose squares sum to ss over `width` channels, or 1 under
+// CKV_FLAG_SKIP_NORM (the gamma weight is then 1 too: norm_gamma).
+__device__ __forceinline__ float norm_inv(const LayerParams& P, float ss, int width) {
+  return (P.flags & CKV_FLAG_SKIP_NORM) ? 1.f : 1.0f / sqrtf(ss / (float)width + P.eps);
+}
+__device__ __forceinline__ float norm_gamma(const LayerParams& P, float g) {
+  return (P.flags & CKV_FLAG_SKIP_NORM) ? 1.f : g;
+}
+__device__ __forceinline__ float2 norm_gamma(const LayerParams& P, float2 g) {
+  return (P.flags & CKV_FLAG_SKIP_NORM) ? make_float2(1.f, 1.f) : g;
+}
+
 // z <- gamma * z / sqrt(mean(z^2) + eps), channels owned as c = tid + k*blockDim.
-__device__ __forceinline__ void rmsnorm_lds(float* z, int width, const float* gamma, float eps,
+__device__ __forceinline__ void rmsnorm_lds(const LayerParams& P, float* z, int width, const float* gamma,
                                             float* red) {
   float ss = 0.f;
   for (int c = threadIdx.x; c < width; c += blockDim.x) ss += z[c] * z[c];
   ss = block_sum(ss, red);
-  const float inv = 1.0f / sqrtf(ss / (float)width + eps);
-  for (int c = threadIdx.x; c < width; c += blockDim.x) z[c] = gamma[c] * (z[c] * inv);
+  const float inv = norm_inv(P, ss, width);
+  for (int c = threadIdx.x; c < width; c += blockDim.x) z[c] = norm_gamma(P, gamma[c]) * (z[c] * inv);
 }
 
 // Store z[0..d) (LDS) as one K=V row record of format KVF.  All threads call.
@@ -328,9 +340,9 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
       irs[e] = ld2(isc + sl * DI + ci);
       iap[e] = ld2(w.idx_ape + sl * DI + ci);
     }
-    gmi = ld2(w.idx_gamma + ci);
+    gmi = norm_gamma(P, ld2(w.idx_gamma + ci));
   }
-  gm = ld2(w.gamma + c);
+  gm = norm_gamma(P, ld2(w.gamma + c));
   // compiler fences: the loads above stay above, the caller's stay in between
   asm volatile("" ::: "memory");
   issue();
@@ -503,13 +515,13 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
   // ---- attention lane: RMSNorm, tail RoPE at i r, store row i
   {
     const float ss = cmp::block_sum_max(own ? y.x * y.x + y.y * y.y : 0.f, 0.f, red).x;
-    const float inv = 1.0f / sqrtf(ss / (float)d + P.eps);
+    const float inv = norm_inv(P, ss, d);
     const float2 z = rope2t(make_float2(gm.x * (y.x * inv), gm.y * (y.y * inv)), c, d, P.n_rot, rtab + 32, rtab + 96);
     store_row2<KVF>(cc.comp + ((size_t)b * P.cap + i) * P.row_bytes, z, c, own, d, P.n_rot, red);
   }
   if (W == 8) {  // indexer lane: its own compressor of the same form
     const float ss = cmp::block_sum_max(own && ilane ? yi.x * yi.x + yi.y * yi.y : 0.f, 0.f, red).x;
-    const float inv = 1.0f / sqrtf(ss / (float)DI + P.eps);
+    const float inv = norm_inv(P, ss, DI);
     if (own && ilane) {
       const float2 z = rope2t(make_float2(gmi.x * (yi.x * inv), gmi.y * (yi.y * inv)), c, DI, P.idx_rot, rtab + 32,
                               rtab + 96);
@@ -642,7 +654,7 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
     rs[sl] = ssc[sl * width + col];
     ap[sl] = ape[sl * width];
   }
-  const float gm = (roleA ? w.gamma : w.idx_gamma)[col];
+  const float gm = norm_gamma(P, (roleA ? w.gamma : w.idx_gamma)[col]);
   asm volatile("" ::: "memory");
   issue();
   asm volatile("" ::: "memory");
@@ -719,7 +731,7 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
       ssc[cur * width + col] = sa;
     }
     if (pool) {   // RMSNorm, tail RoPE at 4 i, row i of the attention or indexer cache
-      const float inv = 1.0f / sqrtf(roleA ? sA / (float)d + P.eps : sI / (float)DI + P.eps);
+      const float inv = roleA ? norm_inv(P, sA, d) : norm_inv(P, sI, DI);
       const float z = rope1t(gm * y * inv, col, width, roleA ? P.n_rot : P.idx_rot, rtab + 32, rtab + 96);
       if (roleA) {
         uint8_t* dst = cc.comp + ((size_t)b * P.cap + i) * P.row_bytes;

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void k_c128a_slices(LayerParams P, Weights w, 
       }
       const float2 y = make_float2(s0 > 0.f ? c0 / s0 : 0.f, s1 > 0.f ? c1 / s1 : 0.f);
       *(float2*)(pool_ws + (size_t)b * d + c) = y;
-      const float2 gm = ld2(w.gamma + c);
+      const float2 gm = norm_gamma(P, ld2(w.gamma + c));
       ss = y.x * y.x + y.y * y.y;
       mx = c < dn ? fmaxf(fabsf(gm.x * y.x), fabsf(gm.y * y.y)) : 0.f;
     }
@@ -196,10 +196,10 @@ __global__ __launch_bounds__(256) void k_c128a_finish(LayerParams P, Weights w, 
       ss += t.x;
       mx = fmaxf(mx, t.y);
     }
-    const float inv = 1.0f / sqrtf(ss / (float)d + P.eps);
+    const float inv = norm_inv(P, ss, d);
     const bool act = c < d;
     const float2 y = ld2(pool_ws + (size_t)b * d + min(c, d - 2));
-    const float2 gm = ld2(w.gamma + min(c, d - 2));
+    const float2 gm = norm_gamma(P, ld2(w.gamma + min(c, d - 2)));
     float2 z = make_float2(gm.x * (y.x * inv), gm.y * (y.y * inv));
     if (c >= dn && act) {
       float cs, sn;
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
     }
     zs[c] = pa.value();
   }
-  rmsnorm_lds(zs, d, w.gamma, P.eps, red);
+  rmsnorm_lds(P, zs, d, w.gamma, red);
   __syncthreads();
   rope_lds(P, zs, d, P.n_rot, (double)i * r, true);
   __syncthreads();
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
     }
     zi[c] = pa.value();
   }
-  rmsnorm_lds(zi, DI, w.idx_gamma, P.eps, red);
+  rmsnorm_lds(P, zi, DI, w.idx_gamma, red);
   __syncthreads();
   rope_lds(P, zi, DI, P.idx_rot, (double)i * r, true);
   __syncthreads();

@@ -79,6 +79,17 @@ extern "C" {
 /* ---- desc.flags ------------------------------------------------------------ */
 #define CKV_FLAG_NO_INV_ROPE 1u  /* skip the inverse RoPE on the output [P4]   */
 #define CKV_FLAG_IDX_NO_RELU 2u  /* indexer sums raw dots instead of relu(dots) */
+/* Debug stage skips, for tests that isolate one stage of the compressor or
+ * the attention [P1 s4 steps 6-8]:
+ *   SKIP_NORM  compressed rows of both lanes are stored without RMSNorm
+ *              (neither the 1/rms factor nor the gamma weight);
+ *   SKIP_ROPE  no tail rotation anywhere: raw, compressed and indexer rows,
+ *              both queries and the output (every angle is zero);
+ *   KEEP_F32   every cast is the identity: accepted only with f32 caches,
+ *              activations and weights (else CKV_E_UNSUPPORTED). */
+#define CKV_FLAG_SKIP_NORM 4u
+#define CKV_FLAG_SKIP_ROPE 8u
+#define CKV_FLAG_KEEP_F32 16u
 
 /* ---- modes for ckv_workspace_bytes ---------------------------------------- */
 #define CKV_MODE_DECODE 0

@@ -397,6 +397,15 @@ class OracleLayer:
     # them keep ``rope_base``, the compressed class takes this one
     # (per-row-class reading).
     rope_base_comp: Optional[float] = None
+    # Debug stage skips of the library's layer description (used to isolate a
+    # stage in tests): no RMSNorm (neither 1/rms nor gamma) on compressed rows;
+    # no tail rotation anywhere (every angle zero).
+    skip_norm: bool = False
+    skip_rope: bool = False
+
+    def rope(self, x, pos, base: float, n_rot: int) -> np.ndarray:
+        """rope_tail, or the identity when the layer skips RoPE."""
+        return np.asarray(x, F64) if self.skip_rope else rope_tail(x, pos, base, n_rot)
 
     @property
     def base_raw(self) -> float:
@@ -522,9 +531,9 @@ class OracleSequence:
         L = self.L
         y = self.pooled(i, lane)
         gamma = L.gamma if lane == "attn" else L.idx_gamma
-        z = rmsnorm(y, gamma, L.norm_eps)
+        z = y if L.skip_norm else rmsnorm(y, gamma, L.norm_eps)
         n_rot = min(L.n_rot, len(z))
-        return rope_tail(z, i * L.ratio, L.base_comp, n_rot)
+        return L.rope(z, i * L.ratio, L.base_comp, n_rot)
 
     def _row_is_computed(self, i: int) -> bool:
         """Row i is computed from history when its last window token is live."""
@@ -565,7 +574,7 @@ class OracleSequence:
         L = self.L
         if self.is_live(t):
             if t not in self._raw_cache:
-                z = rope_tail(self.u[t], t, L.base_raw, L.n_rot)
+                z = L.rope(self.u[t], t, L.base_raw, L.n_rot)
                 rec, val = encode_row(z, L.kv_fmt, L.head_dim, L.n_rot)
                 self._raw_cache[t] = (z, rec, val)
             return self._raw_cache[t]
@@ -625,7 +634,7 @@ class OracleSequence:
         against compressed rows) and is cast to the indexer-cache format."""
         L = self.L
         V = self.visible_rows(p)
-        qh = rope_tail(decode_values(qI, L.act_fmt), p, L.base_comp, min(L.n_rot, L.idx_dim))
+        qh = L.rope(decode_values(qI, L.act_fmt), p, L.base_comp, min(L.n_rot, L.idx_dim))
         qh = cast_values(qh, L.idx_fmt)
         return indexer_scores(qh, np.asarray(w, F64), self.idx_matrix(V), relu=L.relu)
 
@@ -650,11 +659,11 @@ class OracleSequence:
             sel = list(range(V))
         comp = self.comp_matrix(sel)
         qv = decode_values(q, L.act_fmt).reshape(L.n_heads, L.head_dim)
-        q_raw = rope_tail(qv, p, L.base_raw, L.n_rot)
-        q_comp = rope_tail(qv, p, L.base_comp, L.n_rot)
+        q_raw = L.rope(qv, p, L.base_raw, L.n_rot)
+        q_comp = L.rope(qv, p, L.base_comp, L.n_rot)
         o_raw, o_comp = attention_two_class(q_raw, raw, q_comp, comp, L.scale)
         # inverse RoPE (P4), class by class
-        return rope_tail(o_raw, -p, L.base_raw, L.n_rot) + rope_tail(o_comp, -p, L.base_comp, L.n_rot)
+        return L.rope(o_raw, -p, L.base_raw, L.n_rot) + L.rope(o_comp, -p, L.base_comp, L.n_rot)
 
     def step(self, p: int, x, u, q, qI=None, w=None, topk_override=None) -> dict:
         """One decode step at token p: make p live, then index, select, attend."""

@@ -12,13 +12,14 @@ BF16_TOL = (2e-2, 1e-3)   # (rtol, atol) for bf16 / fp32 outputs
 FP8_TOL = (5e-2, 1e-3)    # when the K=V cache is fp8
 
 
-def device_layer(cfg: LayerShape, weights, cache: G.CacheInit = None, max_chunk: int = 0, batch=None):
+def device_layer(cfg: LayerShape, weights, cache: G.CacheInit = None, max_chunk: int = 0, batch=None, flags=0):
     from compressed_kv_sparse_amd import DeviceLayer
     dl = DeviceLayer(ratio=cfg.ratio, hidden=cfg.hidden, head_dim=cfg.head_dim, n_heads=cfg.n_heads,
                      batch=cfg.batch if batch is None else batch, idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim,
                      top_k=cfg.top_k, comp_cap=cfg.comp_cap, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt,
                      act_fmt=cfg.act_fmt, w_fmt=cfg.w_fmt, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps,
-                     n_rot=cfg.n_rot, swa=cfg.swa, max_chunk=max_chunk, rope_base_comp=cfg.rope_base_comp or 0.0)
+                     n_rot=cfg.n_rot, swa=cfg.swa, max_chunk=max_chunk, rope_base_comp=cfg.rope_base_comp or 0.0,
+                     flags=flags)
     if weights is not None:
         dl.set_weights(wkv=weights.wkv, wgate=weights.wgate, ape=weights.ape, gamma=weights.gamma,
                        idx_wkv=weights.idx_wkv, idx_wgate=weights.idx_wgate, idx_ape=weights.idx_ape,

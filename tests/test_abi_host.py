@@ -52,11 +52,26 @@ def test_validate_accepts_the_workload_shapes():
     (dict(top_k=0), L.CKV_E_UNSUPPORTED), (dict(kv_fmt=7), L.CKV_E_UNSUPPORTED),
     (dict(act_fmt=L.CKV_E4M3), L.CKV_E_UNSUPPORTED), (dict(comp_cap=0), L.CKV_E_INVAL),
     (dict(batch=0), L.CKV_E_INVAL), (dict(rope_base=0.0), L.CKV_E_INVAL),
-    (dict(flags=0x80), L.CKV_E_UNSUPPORTED), (dict(hidden=100), L.CKV_E_UNSUPPORTED),
+    (dict(flags=0x80), L.CKV_E_UNSUPPORTED), (dict(flags=0x20), L.CKV_E_UNSUPPORTED), (dict(hidden=100), L.CKV_E_UNSUPPORTED),
     (dict(top_k=2049), L.CKV_E_UNSUPPORTED), (dict(rope_base_comp=-1.0), L.CKV_E_INVAL),
 ])
 def test_validate_rejects(kw, code):
     assert L.validate(desc(**kw)) == code
+
+
+def test_debug_stage_flags():
+    """The header's debug stage skips are accepted (SKIP_NORM, SKIP_ROPE on any
+    formats; KEEP_F32 only with f32 caches, activations and weights); other
+    bits are not."""
+    both = L.CKV_FLAG_SKIP_NORM | L.CKV_FLAG_SKIP_ROPE
+    assert L.validate(desc(flags=both)) == 0
+    assert L.validate(desc(flags=both | L.CKV_FLAG_NO_INV_ROPE | L.CKV_FLAG_IDX_NO_RELU)) == 0
+    assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32)) == L.CKV_E_UNSUPPORTED
+    f32 = dict(kv_fmt=L.CKV_F32, idx_fmt=L.CKV_F32, act_fmt=L.CKV_F32, w_fmt=L.CKV_F32)
+    assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, **f32)) == 0
+    assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, **dict(f32, idx_fmt=L.CKV_BF16))) == L.CKV_E_UNSUPPORTED
+    assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, ratio=0, comp_cap=0, **dict(f32, idx_fmt=L.CKV_BF16))) == 0
+    assert L.validate(desc(flags=32)) == L.CKV_E_UNSUPPORTED
 
 
 def test_validate_bounds_match_the_header():

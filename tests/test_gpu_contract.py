@@ -306,3 +306,101 @@ def test_attention_range_guard_prefill():
     for n_ in (0, 4, 5, 6, 39, 40, 41, 95):
         ref = seq.attend(pos0 + n_, inp.q[n_], None)
         assert_close(og[n_], ref, BF16_TOL, f"guarded prefill output {n_}")
+
+
+# ---------------------------------------------------------------------------
+# debug stage skips (desc.flags)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("which", ["norm", "rope", "both"])
+def test_debug_stage_skips_decode_and_prefill(which):
+    """C1 (f32) with the boundary's SKIP_NORM / SKIP_ROPE against the oracle
+    with the same skips: 300 compress_append steps from token 0 (every stored
+    row compared), index + attend at the last token; then the same tokens
+    prefilled in chunks of 150 + 150 on a fresh layer, with top-k sets and
+    outputs of sampled queries compared."""
+    from harness import compare_rows, tie_free_queries
+    from compressed_kv_sparse_amd import _lib as L
+    fl = {"norm": L.CKV_FLAG_SKIP_NORM, "rope": L.CKV_FLAG_SKIP_ROPE,
+          "both": L.CKV_FLAG_SKIP_NORM | L.CKV_FLAG_SKIP_ROPE}[which]
+    cfg = get_config("c1")
+    wts = make_layer_weights(cfg)
+    T = 300
+    x, u, q, qI, w = G.make_token_stream(cfg, T)
+    Lo = oracle_layer(cfg, wts)
+    Lo.skip_norm = bool(fl & L.CKV_FLAG_SKIP_NORM)
+    Lo.skip_rope = bool(fl & L.CKV_FLAG_SKIP_ROPE)
+    seq = O.OracleSequence(Lo)
+    seq.feed(0, x, u)
+    dl = device_layer(cfg, wts, flags=fl)
+    xd, ud = dev(x), dev(u)
+    for p in range(T):
+        dl.compress_decode(xd[p:p + 1], ud[p:p + 1], dev(np.array([p], np.int32)), B=1)
+    torch.cuda.synchronize()
+    comp_g, idx_g, raw_g = cpu(dl.comp)[0], cpu(dl.idx)[0], cpu(dl.raw)[0]
+    for i in range(T // 4):
+        compare_rows(comp_g[i], seq.comp_row(i)[0], "f32", cfg.head_dim, cfg.n_rot, f"[{which}] comp row {i}")
+        assert_close(idx_g[i], seq.idx_row(i)[0], BF16_TOL, f"[{which}] idx row {i}")
+    for t in range(T - 128, T):
+        compare_rows(raw_g[t % 128], seq.raw_row(t)[0], "f32", cfg.head_dim, cfg.n_rot, f"[{which}] raw {t}")
+    p = T - 1
+    qI1, w1 = tie_free_queries(cfg, [seq], [p], qI[p:p + 1], w[p:p + 1])
+    pos_d = dev(np.array([p], np.int32))
+    topk_d = torch.empty((1, cfg.top_k), dtype=torch.int32, device="cuda")
+    dl.indexer_decode(dev(qI1), dev(w1), pos_d, topk_d, B=1)
+    out = dl.new_out(1)
+    dl.attn_decode(dev(q[p:p + 1]), pos_d, topk_d, out, B=1)
+    torch.cuda.synchronize()
+    ref = seq.query(p, q[p], qI1[0], w1[0])
+    assert sets_equal(cpu(topk_d)[0], ref["topk"])
+    assert_close(cpu(out)[0], ref["out_f64"], BF16_TOL, f"[{which}] decode output")
+    log(f"[skips {which}] decode rows, top-k and output match")
+
+    qI2, w2 = qI.copy(), w.copy()
+    want = [0, 1, 3, 99, 149, 150, 151, 203, 255, 299]
+    for n in want:
+        for a in range(40):
+            if topk_margin(seq.index_scores(n, qI2[n], w2[n]), cfg.top_k) > 1e-4:
+                break
+            nq, nw = G.draw_query_index(cfg, 1, sub=7000 + n, attempt=a + 1)
+            qI2[n], w2[n] = nq[0], nw[0]
+    dp = device_layer(cfg, wts, max_chunk=150, flags=fl)
+    for p0 in (0, 150):
+        sl = slice(p0, p0 + 150)
+        o, tk = dp.prefill(0, p0, dev(x[sl]), dev(u[sl]), dev(q[sl]), dev(qI2[sl]), dev(w2[sl]))
+        torch.cuda.synchronize()
+        og, tkg = cpu(o), cpu(tk)
+        for n in want:
+            if not p0 <= n < p0 + 150:
+                continue
+            r = seq.query(n, q[n], qI2[n], w2[n])
+            assert sets_equal(tkg[n - p0], r["topk"]), f"[{which}] prefill top-k of query {n}"
+            assert_close(og[n - p0], r["out_f64"], BF16_TOL, f"[{which}] prefill output {n}")
+    log(f"[skips {which}] prefill matches")
+
+
+def test_keep_f32_changes_nothing_on_f32_layers():
+    """KEEP_F32 declares that every cast is the identity; on an f32 layer
+    (C1) it is accepted and the stored bytes and outputs are those of the
+    same calls without it."""
+    from compressed_kv_sparse_amd import _lib as L
+    cfg = get_config("c1")
+    wts = make_layer_weights(cfg)
+    T = 160
+    x, u, q, qI, w = G.make_token_stream(cfg, T)
+    res = []
+    for fl in (0, L.CKV_FLAG_KEEP_F32):
+        dl = device_layer(cfg, wts, flags=fl)
+        xd, ud = dev(x), dev(u)
+        for p in range(T):
+            dl.compress_decode(xd[p:p + 1], ud[p:p + 1], dev(np.array([p], np.int32)), B=1)
+        p = T - 1
+        pos_d = dev(np.array([p], np.int32))
+        topk_d = torch.empty((1, cfg.top_k), dtype=torch.int32, device="cuda")
+        dl.indexer_decode(dev(qI[p:p + 1]), dev(w[p:p + 1]), pos_d, topk_d, B=1)
+        out = dl.new_out(1)
+        dl.attn_decode(dev(q[p:p + 1]), pos_d, topk_d, out, B=1)
+        torch.cuda.synchronize()
+        res.append((cpu(dl.comp), cpu(dl.idx), cpu(dl.raw), cpu(topk_d), cpu(out)))
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))

@@ -687,3 +687,60 @@ def test_workload_row_counts():
     assert get_config("c2").comp_cap == 16384
     assert get_config("c5").comp_cap == 32768 and get_config("c5_c128a").comp_cap == 1024
     assert get_config("c3").comp_cap == 8192
+
+
+# ---------------------------------------------------------------- debug stage skips
+# The boundary's SKIP_NORM / SKIP_ROPE flags turn the RMSNorm (with its gamma)
+# and every tail rotation off.  With both off and wgate = APE = 0 every
+# compressor score is equal, so each stored row is the plain mean of
+# kappa_t = W_kv x_t over its window's live tokens (P1 s4 steps 3-5 with the
+# scores uniform), the raw row of token t is u_t, and the output is the plain
+# softmax average of the attended rows with the query as given.
+
+
+@pytest.mark.parametrize("ratio", [4, 128])
+def test_debug_skips_leave_window_means_and_plain_attention(ratio):
+    rng = np.random.default_rng(11 + ratio)
+    L = _pin_layer(ratio, 10000.0, 160000.0)
+    L.skip_norm = L.skip_rope = True
+    d, D, W = L.head_dim, 4, L.window
+    L.wkv = rng.standard_normal((d, D))
+    L.wgate = np.zeros((d, D))
+    L.ape = np.zeros((W, d))
+    L.gamma = rng.uniform(0.5, 1.5, d)           # ignored under SKIP_NORM
+    if ratio == 4:
+        DI = L.idx_dim
+        L.idx_wkv = rng.standard_normal((DI, D))
+        L.idx_wgate = np.zeros((DI, D))
+        L.idx_ape = np.zeros((8, DI))
+        L.idx_gamma = rng.uniform(0.5, 1.5, DI)
+    N = 300 if ratio == 4 else 700
+    X = rng.standard_normal((N, D))
+    U = rng.standard_normal((N, d))
+    seq = O.OracleSequence(L)
+    seq.feed(0, X, U)
+    kap = X @ L.wkv.T
+    rows = []
+    for i in range(N // ratio):
+        toks = [t for t in range(i * ratio - (W - ratio), i * ratio + ratio) if 0 <= t < N]
+        want = kap[toks].mean(axis=0)
+        np.testing.assert_allclose(seq.comp_row(i)[0], want, rtol=1e-12, atol=1e-12)
+        rows.append(want)
+        if ratio == 4:
+            iw = (X[toks] @ L.idx_wkv.T).mean(axis=0)
+            np.testing.assert_allclose(seq.idx_row(i)[0], iw, rtol=1e-12, atol=1e-12)
+    p = N - 1
+    for t in range(p - 127, p + 1):
+        np.testing.assert_array_equal(seq.raw_row(t)[0], U[t])
+    q = rng.standard_normal((1, d))
+    V = seq.visible_rows(p)
+    sel = [0, 5, 17, V - 1] if ratio == 4 else list(range(V))
+    topk = np.array(sel, np.int32) if ratio == 4 else None
+    vecs = [U[t] for t in range(p - 127, p + 1)] + [rows[i] for i in sel]
+    logits = [float(q[0] @ v) * d ** -0.5 for v in vecs]
+    np.testing.assert_allclose(seq.attend(p, q, topk)[0], _softmax_out(logits, vecs), rtol=1e-12, atol=1e-12)
+    # the same layer with RoPE on moves the output (the skip is not vacuous)
+    L.skip_rope = False
+    seq2 = O.OracleSequence(L)
+    seq2.feed(0, X, U)
+    assert np.max(np.abs(seq2.attend(p, q, topk)[0] - _softmax_out(logits, vecs))) > 1e-3
