@@ -39,7 +39,10 @@ RMSNorm eps 1e-6;
 logit scale 1/sqrt(d); indexer score = sum_h w_h * relu(qI_h . kI_s) with the
 rotated indexer query cast to the indexer-cache format; top-k ties go to the
 lower index, output ascending with -1 padding; an fp8 row keeps its RoPE tail
-in bf16 and scales its other channels by max|z|/448.
+in bf16 and scales its other channels by max|z|/448; an fp4 indexer cache is
+the QAT round trip of P1 s9 read as orthonormal Hadamard-128 then OCP MXFP4
+(E2M1 in blocks of 32 with a power-of-two block scale), applied alike to the
+rotated indexer query.
 
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
@@ -136,6 +139,114 @@ def f32_round(x: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# indexer QAT: Hadamard-128 and FP4 (P1 s9: the indexer's compressed rows and
+# its query pass through a Hadamard transform of width 128 and an FP4
+# activation-quantisation round trip; P4 "DeepSeek V4 attention
+# architecture": the indexer cache may be fp4).  The pages name neither the
+# FP4 element format nor its scaling; the reading taken here is OCP MXFP4:
+# E2M1 elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) in blocks of 32
+# consecutive channels, each block sharing a power-of-two scale 2^e with
+# e = floor(log2 max|x|) - 2 (2 = the largest E2M1 exponent), elements rounded
+# to nearest with ties to the even code and saturated at 6.  The Hadamard
+# transform is the orthonormal one (Sylvester order, H / sqrt(n), symmetric),
+# applied to the 128 channels after the tail RoPE.
+# ---------------------------------------------------------------------------
+
+FP4_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])   # E2M1 magnitude of codes 0..7
+FP4_BLOCK = 32
+
+
+def hadamard(x: np.ndarray) -> np.ndarray:
+    """Orthonormal Walsh-Hadamard transform along the last axis (length a
+    power of two): x @ H_n / sqrt(n), H_n the Sylvester matrix."""
+    from scipy.linalg import hadamard as sylvester
+    x = np.asarray(x, F64)
+    n = x.shape[-1]
+    return x @ (sylvester(n).astype(F64) / math.sqrt(n))
+
+
+def fp4_decode(codes: np.ndarray) -> np.ndarray:
+    """E2M1 codes (bit 3 = sign) -> values."""
+    c = np.asarray(codes, np.int64)
+    mag = FP4_GRID[c & 7]
+    return np.where(c & 8, -mag, mag)
+
+
+def fp4_encode(v: np.ndarray) -> np.ndarray:
+    """Values (already divided by their block scale) -> E2M1 codes: nearest
+    grid magnitude, a tie going to the even code, saturated at 6; the sign bit
+    is set for negative values (zero keeps code 0)."""
+    v = np.asarray(v, F64)
+    a = np.minimum(np.abs(v), FP4_GRID[-1])
+    dist = np.abs(a[..., None] - FP4_GRID)                     # [..., 8]
+    best = dist.min(axis=-1, keepdims=True)
+    cand = np.isclose(dist, best, rtol=0.0, atol=0.0) | (dist == best)
+    # among equally near codes (at most two, adjacent) take the even one
+    even = cand & ((np.arange(8) & 1) == 0)
+    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    return (code | np.where((v < 0) & (code > 0), 8, 0)).astype(np.uint8)
+
+
+def mxfp4_encode(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Blocks of 32 along the last axis -> (E2M1 codes [..., n], block
+    exponents e [..., n/32] as ints).  e = floor(log2 max|x|) - 2, clamped to
+    [-127, 127]; an all-zero block takes e = -127."""
+    x = np.asarray(x, F64)
+    shp = x.shape
+    blk = x.reshape(shp[:-1] + (shp[-1] // FP4_BLOCK, FP4_BLOCK))
+    amax = np.max(np.abs(blk), axis=-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    codes = fp4_encode(blk / np.ldexp(1.0, e)[..., None])
+    return codes.reshape(shp), e
+
+
+def mxfp4_decode(codes: np.ndarray, e: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes)
+    shp = c.shape
+    blk = fp4_decode(c).reshape(shp[:-1] + (shp[-1] // FP4_BLOCK, FP4_BLOCK))
+    return (blk * np.ldexp(1.0, np.asarray(e, np.int64))[..., None]).reshape(shp)
+
+
+def mxfp4_round_trip(x: np.ndarray) -> np.ndarray:
+    return mxfp4_decode(*mxfp4_encode(x))
+
+
+def fp4_row_bytes(n: int) -> int:
+    """One stored fp4 indexer row: n/2 bytes of codes (channel 2j in the low
+    nibble of byte j, 2j + 1 in the high one), then n/32 E8M0 bytes (e + 127)."""
+    return n // 2 + n // FP4_BLOCK
+
+
+def fp4_encode_rows(x: np.ndarray) -> np.ndarray:
+    """Rows [..., n] (already in the Hadamard domain) -> records [..., n/2 + n/32] uint8."""
+    codes, e = mxfp4_encode(x)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return np.concatenate([packed, (e + 127).astype(np.uint8)], axis=-1)
+
+
+def fp4_decode_rows(rec: np.ndarray, n: int) -> np.ndarray:
+    rec = np.asarray(rec, np.uint8)
+    packed = rec[..., :n // 2]
+    codes = np.empty(rec.shape[:-1] + (n,), np.uint8)
+    codes[..., 0::2] = packed & 15
+    codes[..., 1::2] = packed >> 4
+    e = rec[..., n // 2:n // 2 + n // FP4_BLOCK].astype(np.int64) - 127
+    return mxfp4_decode(codes, e)
+
+
+def idx_quantise(z: np.ndarray, fmt: str) -> Tuple[np.ndarray, np.ndarray]:
+    """An indexer vector (a row after its RoPE, or the rotated query) as it
+    enters the scores: (value before rounding, value after).  fp4 is the QAT
+    round trip, Hadamard then MXFP4 (P1 s9); f32 / bf16 a plain cast."""
+    if fmt == "fp4":
+        h = hadamard(z)
+        return h, mxfp4_round_trip(h)
+    return np.asarray(z, F64), cast_values(z, fmt)
+
+
+# ---------------------------------------------------------------------------
 # stored-row formats
 # ---------------------------------------------------------------------------
 
@@ -156,6 +267,12 @@ def stored_row_bytes(fmt: str, d: int, n_rot: int) -> int:
 
 
 def decode_values(a: np.ndarray, fmt: str) -> np.ndarray:
+    """Stored values -> fp64.  fp4 takes indexer-row records [..., n/2 + n/32]
+    (values in the Hadamard domain)."""
+    if fmt == "fp4":
+        a = np.asarray(a, np.uint8)
+        n = a.shape[-1] * 32 // 17
+        return fp4_decode_rows(a, n)
     if fmt == "f64":
         return np.asarray(a, F64).copy()
     if fmt == "f32":
@@ -555,13 +672,15 @@ class OracleSequence:
         return self._row_cache[key]
 
     def idx_row(self, i: int) -> Tuple[np.ndarray, np.ndarray]:
-        """(pre-cast value, stored value) of indexer row i."""
+        """(pre-cast value, stored value) of indexer row i (for an fp4 cache
+        both in the Hadamard domain: before and after the MXFP4 round trip)."""
         key = ("idx", i)
         if key not in self._row_cache:
             L = self.L
             if self._row_is_computed(i):
                 z = self._pool_row(i, "idx")
-                self._row_cache[key] = (z, cast_values(z, L.idx_fmt), None)
+                pre, val = idx_quantise(z, L.idx_fmt)
+                self._row_cache[key] = (pre, val, None)
             else:
                 v = decode_values(self.idx_vals[i], L.idx_fmt)
                 self._row_cache[key] = (v, v, None)
@@ -631,11 +750,12 @@ class OracleSequence:
     def index_scores(self, p: int, qI: np.ndarray, w: np.ndarray) -> np.ndarray:
         """Indexer scores of every visible row for query p.  The indexer query
         gets the tail RoPE at p (the compressed class's base: it is matched
-        against compressed rows) and is cast to the indexer-cache format."""
+        against compressed rows) and is cast to the indexer-cache format (for
+        fp4: the Hadamard + MXFP4 round trip of its rows, P1 s9)."""
         L = self.L
         V = self.visible_rows(p)
         qh = L.rope(decode_values(qI, L.act_fmt), p, L.base_comp, min(L.n_rot, L.idx_dim))
-        qh = cast_values(qh, L.idx_fmt)
+        qh = idx_quantise(qh, L.idx_fmt)[1]
         return indexer_scores(qh, np.asarray(w, F64), self.idx_matrix(V), relu=L.relu)
 
     def attend(self, p: int, q: np.ndarray, topk: Optional[np.ndarray]) -> np.ndarray:

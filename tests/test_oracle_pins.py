@@ -744,3 +744,142 @@ def test_debug_skips_leave_window_means_and_plain_attention(ratio):
     seq2 = O.OracleSequence(L)
     seq2.feed(0, X, U)
     assert np.max(np.abs(seq2.attend(p, q, topk)[0] - _softmax_out(logits, vecs))) > 1e-3
+
+
+# ---------------------------------------------------------------- indexer QAT (fp4)
+# P1 s9: the indexer's rows and query pass through Hadamard-128 and an FP4
+# round trip.  Readings (the pages give no format): orthonormal Sylvester
+# Hadamard; OCP MXFP4 (E2M1 elements, blocks of 32, power-of-two scale
+# 2^(floor(log2 max|x|) - 2), round to nearest even, saturate at 6).  The pins
+# below rebuild each piece independently: H from Kronecker products, the E2M1
+# values from the bit layout (1 sign, 2 exponent bits with bias 1, 1 mantissa
+# bit), rounding by brute force over the representable values.
+
+
+def _kron_hadamard(n):
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), h)
+    return h / math.sqrt(n)
+
+
+def _e2m1_value(code):
+    s = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    return s * (m * 0.5 if e == 0 else (1.0 + 0.5 * m) * 2.0 ** (e - 1))
+
+
+def _fp4_brute(v):
+    """Nearest E2M1 value of v (already scaled): ties to the even mantissa bit,
+    |v| above 6 saturates."""
+    a = min(abs(v), 6.0)
+    best, code = None, None
+    for c in range(8):
+        val = _e2m1_value(c)
+        dist = abs(a - val)
+        if best is None or dist < best - 1e-15 or (abs(dist - best) <= 1e-15 and (c & 1) == 0):
+            best, code = dist, c
+    out = _e2m1_value(code)
+    return -out if v < 0 else out
+
+
+def test_hadamard_is_orthonormal_and_keeps_dot_products():
+    H = _kron_hadamard(128)
+    np.testing.assert_allclose(O.hadamard(np.eye(128)), H, atol=1e-15)
+    np.testing.assert_allclose(H @ H, np.eye(128), atol=1e-12)      # symmetric and orthonormal
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal((5, 128)), rng.standard_normal((7, 128))
+    np.testing.assert_allclose(O.hadamard(q) @ O.hadamard(k).T, q @ k.T, rtol=1e-12, atol=1e-12)
+    # without the FP4 step the indexer scores are those of the plain vectors
+    w = rng.uniform(0, 1, 5)
+    np.testing.assert_allclose(O.indexer_scores(O.hadamard(q), w, O.hadamard(k)), O.indexer_scores(q, w, k),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_e2m1_codes_from_the_bit_layout():
+    for c in range(16):
+        assert O.fp4_decode(np.array([c]))[0] == _e2m1_value(c), c
+
+
+def test_fp4_rounding_by_brute_force():
+    rng = np.random.default_rng(4)
+    vals = list(rng.uniform(-8, 8, 4000)) + [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -2.5, -5.0, 6.0, 6.5,
+                                             -7.9, 0.0, 1e-9, -1e-9]
+    got = O.fp4_decode(O.fp4_encode(np.array(vals)))
+    for v, g in zip(vals, got):
+        assert g == _fp4_brute(v), (v, g, _fp4_brute(v))
+
+
+def test_mxfp4_block_scale_and_error_bound():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, 128)) * 10.0 ** rng.uniform(-4, 4, (64, 1))
+    codes, e = O.mxfp4_encode(x)
+    blk = x.reshape(64, 4, 32)
+    amax = np.abs(blk).max(axis=-1)
+    ratio = amax / np.ldexp(1.0, e)
+    assert np.all((ratio >= 4.0) & (ratio < 8.0))                   # e = floor(log2 amax) - 2
+    rt = O.mxfp4_round_trip(x)
+    err = np.abs(rt - x).reshape(64, 4, 32)
+    step = np.ldexp(1.0, e)[..., None]
+    assert np.all(err <= 2 * step)                                   # saturation above 6 * 2^e
+    unsat = np.abs(blk) <= 6 * step
+    assert np.all(err[unsat] <= step.repeat(32, -1)[unsat])         # largest half-gap (between 4 and 6)
+    np.testing.assert_array_equal(O.mxfp4_round_trip(rt), rt)       # the grid is a fixed point
+    # exact block values survive, a zero block stays zero
+    exact = np.zeros((1, 32))
+    exact[0, :8] = [6, -4, 3, 1.5, 0.5, 0, 2, -6]
+    np.testing.assert_array_equal(O.mxfp4_round_trip(exact * 2.0 ** -5), exact * 2.0 ** -5)
+    np.testing.assert_array_equal(O.mxfp4_round_trip(np.zeros((1, 32))), np.zeros((1, 32)))
+
+
+def test_fp4_row_record_layout():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((3, 128))
+    rec = O.fp4_encode_rows(x)
+    assert rec.shape == (3, 68) and O.fp4_row_bytes(128) == 68
+    codes, e = O.mxfp4_encode(x)
+    np.testing.assert_array_equal(rec[:, :64] & 15, codes[:, 0::2])
+    np.testing.assert_array_equal(rec[:, :64] >> 4, codes[:, 1::2])
+    np.testing.assert_array_equal(rec[:, 64:].astype(np.int64) - 127, e)
+    np.testing.assert_array_equal(O.decode_values(rec, "fp4"), O.mxfp4_round_trip(x))
+
+
+def test_fp4_indexer_scores_by_brute_force():
+    """An fp4 layer's indexer: rows and query rounded in the Hadamard domain;
+    scores against a brute-force rebuild (Kronecker H, per-element nearest
+    E2M1 value with the block scale from max |x|)."""
+    rng = np.random.default_rng(7)
+    L = _pin_layer(4, 10000.0, None, d=16, D=4, DI=128, n_rot=8, top_k=4)
+    L.idx_fmt = "fp4"
+    L.idx_heads = 2
+    L.wkv = rng.standard_normal((16, 4))
+    L.wgate = rng.standard_normal((16, 4))
+    L.ape = rng.standard_normal((8, 16)) * 0.1
+    L.gamma = np.ones(16)
+    L.idx_wkv = rng.standard_normal((128, 4))
+    L.idx_wgate = rng.standard_normal((128, 4))
+    L.idx_ape = rng.standard_normal((8, 128)) * 0.1
+    L.idx_gamma = rng.uniform(0.5, 1.5, 128)
+    N = 60
+    seq = O.OracleSequence(L)
+    seq.feed(0, rng.standard_normal((N, 4)), rng.standard_normal((N, 16)))
+    H = _kron_hadamard(128)
+
+    def brute_rt(v):
+        out = np.empty_like(v)
+        for b in range(0, 128, 32):
+            blk = v[b:b + 32]
+            amax = np.max(np.abs(blk))
+            sc = 2.0 ** (math.floor(math.log2(amax)) - 2) if amax > 0 else 0.0
+            out[b:b + 32] = [(_fp4_brute(t / sc) * sc if sc else 0.0) for t in blk]
+        return out
+
+    p = N - 1
+    qI = rng.standard_normal((2, 128))
+    w = rng.uniform(0, 1, 2)
+    qr = L.rope(qI, p, L.base_comp, 8)
+    qt = np.stack([brute_rt(H @ qr[h]) for h in range(2)])
+    V = seq.visible_rows(p)
+    rows = np.stack([brute_rt(H @ seq._pool_row(i, "idx")) for i in range(V)])
+    want = np.array([sum(w[h] * max(float(qt[h] @ rows[i]), 0.0) for h in range(2)) for i in range(V)])
+    np.testing.assert_allclose(seq.index_scores(p, qI, w), want, rtol=1e-12, atol=1e-12)
