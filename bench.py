@@ -73,11 +73,18 @@ def dev(a):
 
 # --------------------------------------------------------------------------- algorithmic work
 
+def idx_row_bytes(cfg):
+    """Bytes of one stored indexer row: f32 / bf16 values, or the fp4 record
+    (codes at 4 bits plus one scale byte per 32 channels)."""
+    DI = cfg.idx_dim
+    return {"f32": 4 * DI, "bf16": 2 * DI, "fp4": DI // 2 + DI // 32}[cfg.idx_fmt]
+
+
 def decode_step_bytes(cfg, n):
     """Bytes one decode step must move (reads + writes), per the method."""
     d, D, H, HI, DI, k, r = cfg.head_dim, cfg.hidden, cfg.n_heads, cfg.idx_heads, cfg.idx_dim, cfg.top_k, cfg.ratio
     rho = ALGO_ROW_BYTES[cfg.kv_fmt](d)
-    s_i = 2 if cfg.idx_fmt == "bf16" else 4
+    rho_i = idx_row_bytes(cfg) if r == 4 else 0
     s_a = 2 if cfg.act_fmt == "bf16" else 4
     s_w = 2 if cfg.w_fmt == "bf16" else 4
     W = cfg.window
@@ -88,12 +95,12 @@ def decode_step_bytes(cfg, n):
         C = min(k, V) if r == 4 else (V if r == 128 else 0)
         b = 0.0
         if r == 4:
-            b += V * DI * s_i + HI * (DI * s_a + 4) + 8 * k
+            b += V * rho_i + HI * (DI * s_a + 4) + 8 * k
         b += (min(nb, 128) + C) * rho + H * d * 2 * s_a + d * s_a + rho
         if r:
             b += D * s_a + 8 * (d + (DI if r == 4 else 0))
             if (p + 1) % r == 0:
-                b += W * 8 * (d + (DI if r == 4 else 0)) + rho + (DI * s_i if r == 4 else 0)
+                b += W * 8 * (d + (DI if r == 4 else 0)) + rho + rho_i
         total += b
     if r:
         total += 2 * D * (d + (DI if r == 4 else 0)) * s_w + W * 4 * (d + (DI if r == 4 else 0))
@@ -106,14 +113,14 @@ def step_scan_bytes(cfg, n):
     closes, which the selection block scores), the four projection weight
     matrices, x, q^I and the head weights.  The keys it writes are workspace,
     not part of the method's traffic."""
-    s_i = 2 if cfg.idx_fmt == "bf16" else 4
+    rho_i = idx_row_bytes(cfg)
     s_a = 2 if cfg.act_fmt == "bf16" else 4
     s_w = 2 if cfg.w_fmt == "bf16" else 4
     tot = 2.0 * cfg.hidden * (cfg.head_dim + cfg.idx_dim) * s_w
     for nb in n:
         V = nb // 4
         scanned = V - 1 if nb % 4 == 0 else V
-        tot += scanned * cfg.idx_dim * s_i + cfg.hidden * s_a + cfg.idx_heads * (cfg.idx_dim * s_a + 4)
+        tot += scanned * rho_i + cfg.hidden * s_a + cfg.idx_heads * (cfg.idx_dim * s_a + 4)
     return tot
 
 
@@ -603,9 +610,14 @@ def main():
         return
     extra = {}
     if not args.no_extra:
-        for name in ("c2", "c3", "c5_c128a", "c5_swa"):
-            e = bench_decode(get_config(name), args.steps, args.warmup, with_kernel=False, copies=args.layer_copies)
+        for name in ("c2", "c3", "c5_c128a", "c5_swa", "c5_fp4idx"):
+            e = bench_decode(get_config(name), args.steps, args.warmup, with_kernel=name == "c5_fp4idx",
+                             copies=args.layer_copies)
             extra[name] = {k: round(v, 4) for k, v in e.items() if not k.startswith("_") and isinstance(v, float)}
+            if "kernel" in e:   # the fp4 indexer's projection + scan launch
+                kk = e["kernel"]
+                extra[name]["scan_us"] = round(kk["avg_us"], 2)
+                extra[name]["scan_hbm_frac"] = round(kk["gbs"] / HBM_PEAK_GBS, 4)
             log(f"[bench] decode {name}: {e['ms_per_step'] * 1e3:.1f} us/step, {e['tok_s']:.0f} tok/s, "
                 f"{100 * e['step_hbm_frac']:.1f}% HBM")
             del e
@@ -620,6 +632,12 @@ def main():
                "mfma_frac": round(p["mfma_frac"], 4)}
         log(f"[bench] prefill: {p['ms_per_chunk']:.2f} ms/chunk, {p['tok_s']:.0f} tok/s, "
             f"{p['tflops']:.1f} TFLOP/s ({100 * p['mfma_frac']:.1f}% of bf16 MFMA)")
+        if not args.no_extra:   # the same chunk with the fp4 indexer cache
+            c4f = get_config("c4_fp4idx")
+            pf = bench_prefill(c4f, args.prefill_steps, 1)
+            pre["fp4_indexer"] = {"workload": c4f.name, "tok_s": round(pf["tok_s"], 1),
+                                  "ms_per_chunk": round(pf["ms_per_chunk"], 3)}
+            log(f"[bench] prefill (fp4 indexer): {pf['ms_per_chunk']:.2f} ms/chunk, {pf['tok_s']:.0f} tok/s")
     stack = None
     if not args.no_stack:
         stack = bench_stack(args.stack_steps, 3)

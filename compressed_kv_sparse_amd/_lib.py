@@ -20,8 +20,8 @@ CKV_E_WORKSPACE = -4
 CKV_E_HIP = -5
 CKV_E_SEQUENCE = -6
 
-CKV_F32, CKV_BF16, CKV_E4M3 = 0, 1, 2
-FMT = {"f32": CKV_F32, "bf16": CKV_BF16, "e4m3": CKV_E4M3}
+CKV_F32, CKV_BF16, CKV_E4M3, CKV_FP4 = 0, 1, 2, 3
+FMT = {"f32": CKV_F32, "bf16": CKV_BF16, "e4m3": CKV_E4M3, "fp4": CKV_FP4}
 CKV_FLAG_NO_INV_ROPE = 1
 CKV_FLAG_IDX_NO_RELU = 2
 CKV_FLAG_SKIP_NORM = 4
@@ -83,6 +83,8 @@ def _load() -> ctypes.CDLL:
     D, Wt, C = P(LayerDesc), P(LayerWeights), P(LayerCache)
     lib.ckv_row_bytes.argtypes = [I32, I32, I32]
     lib.ckv_row_bytes.restype = SZ
+    lib.ckv_idx_row_bytes.argtypes = [I32, I32]
+    lib.ckv_idx_row_bytes.restype = SZ
     lib.ckv_validate.argtypes = [D]
     lib.ckv_validate.restype = ctypes.c_int
     lib.ckv_strerror.argtypes = [ctypes.c_int]
@@ -115,7 +117,7 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 
-EXPORTS = ("ckv_row_bytes", "ckv_validate", "ckv_strerror", "ckv_last_hip_error", "ckv_workspace_bytes",
+EXPORTS = ("ckv_row_bytes", "ckv_idx_row_bytes", "ckv_validate", "ckv_strerror", "ckv_last_hip_error", "ckv_workspace_bytes",
            "ckv_workspace_sync_bytes",
            "ckv_compress_append_decode", "ckv_compress_append_prefill", "ckv_indexer_topk_decode",
            "ckv_indexer_topk_prefill", "ckv_indexer_score_decode", "ckv_sparse_swa_attn_decode",
@@ -128,6 +130,10 @@ def strerror(code: int) -> str:
 
 def row_bytes(fmt: int, head_dim: int, n_rot: int = 64) -> int:
     return int(lib.ckv_row_bytes(fmt, head_dim, n_rot))
+
+
+def idx_row_bytes(fmt: int, idx_dim: int) -> int:
+    return int(lib.ckv_idx_row_bytes(fmt, idx_dim))
 
 
 def validate(desc: LayerDesc) -> int:

@@ -28,6 +28,7 @@ struct LayerParams {
   int row_bytes;  // stored K=V row size
   int ncol;       // projection columns: 2d (+ 2 DI on ratio 4)
   int idx_rot;    // RoPE channels of indexer rows / queries: min(n_rot, DI)
+  int idx_row_bytes;   // stored indexer row size (ckv_idx_row_bytes)
   double theta[32];    // RoPE frequencies of the raw class: base^(-2j/n_rot), j < n_rot/2
   double theta_c[32];  // the compressed class (compressed rows, indexer rows, indexer query)
   int two_bases;       // theta_c differs from theta (one frame per row class)

@@ -42,6 +42,7 @@ bool make_params(const ckv_layer_desc* d, LayerParams* P) {
   P->row_bytes = (int)ckv_row_bytes(d->kv_fmt, d->head_dim, d->n_rot);
   P->ncol = d->ratio == 0 ? 0 : 2 * d->head_dim + (d->ratio == 4 ? 2 * d->idx_dim : 0);
   P->idx_rot = d->ratio == 4 ? (d->idx_dim < d->n_rot ? d->idx_dim : d->n_rot) : 0;
+  P->idx_row_bytes = d->ratio == 4 ? (int)ckv_idx_row_bytes(d->idx_fmt, d->idx_dim) : 0;
   const double base_c = d->rope_base_comp > 0.0 ? d->rope_base_comp : d->rope_base;
   // CKV_FLAG_SKIP_ROPE: every frequency 0, so every rotation is the identity
   const bool rope = !(d->flags & CKV_FLAG_SKIP_ROPE);
@@ -147,6 +148,14 @@ extern "C" size_t ckv_row_bytes(int32_t fmt, int32_t head_dim, int32_t n_rot) {
   return 0;
 }
 
+extern "C" size_t ckv_idx_row_bytes(int32_t fmt, int32_t idx_dim) {
+  if (idx_dim <= 0) return 0;
+  if (fmt == CKV_F32) return (size_t)4 * idx_dim;
+  if (fmt == CKV_BF16) return (size_t)2 * idx_dim;
+  if (fmt == CKV_FP4 && idx_dim % 32 == 0) return (size_t)idx_dim / 2 + (size_t)idx_dim / 32;
+  return 0;
+}
+
 extern "C" int ckv_validate(const ckv_layer_desc* d) {
   if (!d) return CKV_E_INVAL;
   if (d->batch <= 0 || d->hidden <= 0 || d->head_dim <= 0 || d->n_heads <= 0) return CKV_E_INVAL;
@@ -172,8 +181,10 @@ extern "C" int ckv_validate(const ckv_layer_desc* d) {
     if ((long long)d->comp_cap * d->ratio > (1ll << 30)) return CKV_E_UNSUPPORTED;
   }
   if (d->ratio == 4) {
-    if (!fmt_ok(d->idx_fmt, false)) return CKV_E_UNSUPPORTED;
+    if (!fmt_ok(d->idx_fmt, false) && d->idx_fmt != CKV_FP4) return CKV_E_UNSUPPORTED;
     if (d->idx_dim != 64 && d->idx_dim != 128) return CKV_E_UNSUPPORTED;
+    // fp4 rows: one 16 x 16 x 128 scaled MFMA per head tile and row tile
+    if (d->idx_fmt == CKV_FP4 && (d->idx_dim != 128 || d->act_fmt != CKV_BF16)) return CKV_E_UNSUPPORTED;
     if (d->idx_heads < 1 || d->idx_heads > 64) return CKV_E_UNSUPPORTED;
     if (d->top_k < 1 || d->top_k > kMaxTopK) return CKV_E_UNSUPPORTED;
   }

@@ -8,6 +8,7 @@
 #include <type_traits>
 
 #include "ckv_device.h"
+#include "idx_fp4.h"
 
 namespace ckv {
 
@@ -280,6 +281,7 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
                                                    const float* __restrict__ proj, int splits, int B, int b,
                                                    float* red, float* mrg, float* idx_row, float* rtab,
                                                    Issue&& issue) {
+  static_assert(IDXF != CKV_FP4, "fp4 indexer rows are written by compress_c4a_seq");
   constexpr int SPT = W / TPC;                 // slots per thread
   constexpr int RND = SPT < 8 ? SPT : 8;       // slots per load round
   constexpr int r = W == 8 ? 4 : 128;
@@ -525,7 +527,7 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
     if (own && ilane) {
       const float2 z = rope2t(make_float2(gmi.x * (yi.x * inv), gmi.y * (yi.y * inv)), c, DI, P.idx_rot, rtab + 32,
                               rtab + 96);
-      uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * DI * (IDXF == CKV_F32 ? 4 : 2);
+      uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * P.idx_row_bytes;
       if (IDXF == CKV_F32) {
         *(float2*)(dst + 4 * c) = z;
         if (idx_row) {
@@ -740,17 +742,29 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
         put_chan<KVF>(dst, z, col, dn, sc);
         if (KVF == CKV_E4M3 && tid == 0) *(float*)(dst + dn + 2 * P.n_rot) = sc;
       } else if (roleI) {
-        uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * DI * (IDXF == CKV_F32 ? 4 : 2);
-        float zs = z;
-        if constexpr (IDXF == CKV_F32) {
-          ((float*)dst)[col] = z;
+        if constexpr (IDXF == CKV_FP4) {
+          idx_row[col] = z;   // encoded below
         } else {
-          const uint32_t h = f32_to_bf16(z);
-          ((uint16_t*)dst)[col] = (uint16_t)h;
-          zs = bf16_to_f32(h);
+          uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * P.idx_row_bytes;
+          float zs = z;
+          if constexpr (IDXF == CKV_F32) {
+            ((float*)dst)[col] = z;
+          } else {
+            const uint32_t h = f32_to_bf16(z);
+            ((uint16_t*)dst)[col] = (uint16_t)h;
+            zs = bf16_to_f32(h);
+          }
+          if (idx_row) idx_row[col] = zs;
         }
-        if (idx_row) idx_row[col] = zs;
       }
+    }
+  }
+  if constexpr (IDXF == CKV_FP4) {
+    // fp4 indexer row: Hadamard + MXFP4 by wave 0 from the RoPE'd row in LDS;
+    // idx_row then holds the stored (decoded) values
+    if (pool) {
+      lds_barrier();
+      if (wave == 0) fp4_store_row(idx_row, (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * kFp4RowBytes, idx_row);
     }
   }
   return pool ? 1 : 0;

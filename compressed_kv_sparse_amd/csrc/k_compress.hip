@@ -36,8 +36,9 @@ __global__ __launch_bounds__(1024) void k_compress_c4a(LayerParams P, Weights w,
                                                        const float* __restrict__ proj, int splits, int B) {
   __shared__ __attribute__((aligned(16))) float red[64];
   __shared__ float rtab[192];
-  const int st =
-      compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, splits, B, blockIdx.x, red, rtab, nullptr, [] {});
+  __shared__ __attribute__((aligned(16))) float idx_lds[IDXF == CKV_FP4 ? kMaxDI : 1];   // fp4 row staging
+  const int st = compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, splits, B, blockIdx.x, red, rtab,
+                                                   IDXF == CKV_FP4 ? idx_lds : nullptr, [] {});
   advance_tokens(cc, blockIdx.x, pos[blockIdx.x], st);
 }
 
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
                                                       const float* __restrict__ part, int seq,
                                                       int pos0, int i_first) {
   __shared__ float zs[kMaxD];
-  __shared__ float zi[kMaxDI];
+  __shared__ __attribute__((aligned(16))) float zi[kMaxDI];
   __shared__ float red[16];
   const int i = i_first + blockIdx.x;
   const int d = P.d, r = P.ratio, W = P.W, DI = P.DI, nc = P.ncol;
@@ -314,8 +315,12 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
   __syncthreads();
   rope_lds(P, zi, DI, P.idx_rot, (double)i * r, true);
   __syncthreads();
-  uint8_t* dst = (uint8_t*)cc.idx + ((size_t)seq * P.cap + i) * DI * (IDXF == CKV_F32 ? 4 : 2);
-  store_vals<IDXF>(dst, zi, DI);
+  uint8_t* dst = (uint8_t*)cc.idx + ((size_t)seq * P.cap + i) * P.idx_row_bytes;
+  if constexpr (IDXF == CKV_FP4) {
+    if (threadIdx.x < 64) fp4_store_row(zi, dst, nullptr);
+  } else {
+    store_vals<IDXF>(dst, zi, DI);
+  }
 }
 
 // After the chunk: the last W tokens' projections go to the state rings and
@@ -370,9 +375,11 @@ static void go_decode(const LayerParams& P, const Weights& w, const Cache& c, co
     hipLaunchKernelGGL((k_c128a_slices<KVF, ACTF>), dim3(B, P.d / 64), dim3(256), 0, st, P, w, c, u, pos, part,
                        splits, B, pool_ws);
     hipLaunchKernelGGL((k_c128a_finish<KVF>), dim3(B), dim3(256), 0, st, P, w, c, pos, pool_ws, B);
-  } else if (P.ratio == 4 && splits <= 4)
+  } else if (P.ratio == 4 && (splits <= 4 || IDXF == CKV_FP4))   // (fp4: splits is at most 4)
     hipLaunchKernelGGL((k_compress_c4a<KVF, IDXF, ACTF>), dim3(B), dim3((P.d + P.DI + 63) / 64 * 64), 0, st, P, w,
                        c, u, pos, part, splits, B);
+  else if constexpr (IDXF == CKV_FP4)
+    return;   // fp4 indexer rows are ratio 4 only
   else if (P.ratio == 4)
     hipLaunchKernelGGL((k_compress_decode<KVF, IDXF, ACTF, 8, 1>), dim3(B), dim3(np), 0, st, P, w, c, u, pos,
                        part, splits, B);
@@ -386,7 +393,11 @@ static void go_decode(const LayerParams& P, const Weights& w, const Cache& c, co
 #define CKV_DISPATCH_KV_IDX_ACT(FN, ...)                                               \
   do {                                                                                 \
     const bool idx32 = P.idx_fmt == CKV_F32, act32 = P.act_fmt == CKV_F32;            \
-    if (P.kv_fmt == CKV_F32) {                                                         \
+    if (P.idx_fmt == CKV_FP4) {   /* validated: bf16 activations */                  \
+      if (P.kv_fmt == CKV_F32) FN<CKV_F32, CKV_FP4, CKV_BF16>(__VA_ARGS__);            \
+      else if (P.kv_fmt == CKV_BF16) FN<CKV_BF16, CKV_FP4, CKV_BF16>(__VA_ARGS__);     \
+      else FN<CKV_E4M3, CKV_FP4, CKV_BF16>(__VA_ARGS__);                               \
+    } else if (P.kv_fmt == CKV_F32) {                                                  \
       if (idx32 && act32) FN<CKV_F32, CKV_F32, CKV_F32>(__VA_ARGS__);                  \
       else if (act32) FN<CKV_F32, CKV_BF16, CKV_F32>(__VA_ARGS__);                     \
       else FN<CKV_F32, CKV_BF16, CKV_BF16>(__VA_ARGS__);                               \

@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "compress_dec.h"
+#include "idx_fp4.h"
 #include "proj_dec.h"
 
 namespace ckv {
@@ -252,6 +253,159 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
       if (v) atomicAdd(&gh[e], v);
     }
   }
+}
+
+// ---------------------------------------------------------------- fp4 MFMA score
+// fp4 indexer rows (68-byte MXFP4 records of the Hadamard-rotated rows, D_I =
+// 128): one scaled fp4 MFMA (16 heads x 16 rows x all 128 channels) per head
+// tile and row tile, 4x fewer bytes per row than bf16.  Same grid, groups and
+// load pipeline as the bf16 block above.  Lane (r, g)'s share of a 16-row
+// tile is the 16-byte code block g of row r and the row's scale dword (byte g
+// is its block scale), both at 4-byte aligned addresses; a tile is 1088
+// contiguous bytes.  The query: wave mt loads head tile mt (lane (r, g):
+// head 16 mt + r, channels 32 g .. 32 g + 31), rotates its tail, applies the
+// Hadamard transform and the MXFP4 rounding in registers and leaves the
+// codes and scales in LDS in MFMA operand order; every wave then reads the
+// MT tiles back.  The query's loads go out before the rows', so waiting for
+// them does not wait for the rows (loads complete in order).
+constexpr int kFp4Bufs = 4;
+
+template <int MT, bool HIST, int NG = kScoreGroups>
+__device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const uint8_t* idx,
+                                                    const void* __restrict__ qI, const float* __restrict__ wt,
+                                                    const int32_t* __restrict__ pos, int seq_fixed, int pos0,
+                                                    uint32_t* __restrict__ keys, uint32_t* __restrict__ hist, int bx,
+                                                    int qn, bool old_only) {
+  constexpr int HP = MT * 16;
+  constexpr int RB = 256 * NG;
+  constexpr int BUFS = kFp4Bufs;
+  __shared__ __attribute__((aligned(16))) u32x4 qc[MT * 64];
+  __shared__ uint32_t qs[MT * 64];
+  __shared__ float wsh[HP];
+  __shared__ float cs_[32], sn_[32];
+  __shared__ uint32_t lh[kHistBins];
+  IdxQuery Q = idx_query(P, pos, seq_fixed, pos0, qn);
+  if (old_only && Q.p >= 0 && (Q.p + 1) % 4 == 0 && (Q.p + 1) / 4 <= P.cap) Q.V -= 1;
+  const int rb0 = bx * RB;
+  if (rb0 >= Q.V) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int HI = P.HI;
+  const uint8_t* base = idx + (size_t)Q.seq * P.cap * kFp4RowBytes;
+  const int vlast = Q.V - 1;
+
+  // the query first: head tile (wave % MT), 32 channels per lane; heads past
+  // H_I read head H_I - 1 and are zeroed below
+  const int qh = 16 * (wave % MT) + r;
+  u32x4 qraw[4];
+  {
+    const uint16_t* qp = (const uint16_t*)qI + ((size_t)qn * HI + min(qh, HI - 1)) * 128 + 32 * g;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qraw[k] = *(const u32x4*)(qp + 8 * k);
+  }
+  const float wl = wt[(size_t)qn * HI + min(tid, HI - 1)];
+
+  auto load = [&](u32x4(&Bc)[4], uint32_t(&Bs)[4], int gi) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = min(rb0 + 256 * gi + wave * 64 + 16 * t + r, vlast);
+      const uint8_t* rp = base + (size_t)row * kFp4RowBytes;
+      Bc[t] = *(const u32x4_a4*)(rp + 16 * g);
+      Bs[t] = *(const uint32_t*)(rp + 64);
+    }
+  };
+  u32x4 Bc[BUFS][4];
+  uint32_t Bs[BUFS][4];
+  constexpr int kAhead = BUFS > 1 ? BUFS - 1 : 1;
+#pragma unroll
+  for (int b = 0; b < kAhead && b < NG; ++b) load(Bc[b % BUFS], Bs[b % BUFS], b);
+
+  if (tid < P.idx_rot / 2) rope_cs_c(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
+  if (tid < HP) wsh[tid] = tid < HI ? wl : 0.f;
+  if constexpr (HIST)
+    for (int e = tid; e < kHistBins; e += 256) lh[e] = 0;
+  lds_barrier();   // cs_, sn_, wsh, lh
+  {
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      v[i] = bf16_to_f32((qraw[i >> 3][(i >> 1) & 3] >> (16 * (i & 1))) & 0xffffu);
+      if (qh >= HI) v[i] = 0.f;
+    }
+    rope_block32(v, g, 128 - P.idx_rot, cs_, sn_);
+    fwht128(v);
+    uint32_t sb;
+    const u32x4 codes = mxfp4_block<false>(v, sb);
+    if (wave < MT) {
+      qc[wave * 64 + lane] = codes;
+      qs[wave * 64 + lane] = sb;
+    }
+  }
+  lds_barrier();   // qc, qs
+  u32x4 A[MT];
+  uint32_t sa[MT];
+  float wv[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    A[mt] = qc[mt * 64 + lane];
+    sa[mt] = qs[mt * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[mt][i] = wsh[16 * mt + 4 * g + i];
+  }
+  const bool relu = !(P.flags & CKV_FLAG_IDX_NO_RELU);
+  uint32_t* kout = keys + (size_t)qn * P.cap;
+
+  auto score = [&](const u32x4(&Bc)[4], const uint32_t(&Bs)[4], int gi) {
+    float sc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float s = 0.f;
+      const uint32_t sb = Bs[t] >> (8 * g);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const f32x4 acc = mfma_fp4(A[mt], sa[mt], Bc[t], sb, (f32x4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += wv[mt][i] * (relu ? fmaxf(acc[i], 0.f) : acc[i]);
+      }
+      sc[t] = rows4_sum(s);
+    }
+    const float mine = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
+    const int row = rb0 + 256 * gi + wave * 64 + lane;
+    const uint32_t key = float_key(mine);
+    *(row < P.cap ? kout + row : g_key_sink + lane) = key;
+    if constexpr (HIST) atomicAdd(&lh[key >> 20], row < Q.V ? 1u : 0u);
+  };
+  // keeps each group's loads above the previous group's multiplies (as in
+  // the bf16 block)
+  auto pin = [&](u32x4(&Bc)[4], uint32_t(&Bs)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      asm volatile("" : "+v"(Bc[t]) : : "memory");
+      asm volatile("" : "+v"(Bs[t]) : : "memory");
+    }
+  };
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    if (gi + kAhead < NG) load(Bc[(gi + kAhead) % BUFS], Bs[(gi + kAhead) % BUFS], gi + kAhead);
+    pin(Bc[gi % BUFS], Bs[gi % BUFS]);
+    score(Bc[gi % BUFS], Bs[gi % BUFS], gi);
+  }
+  if constexpr (HIST) {
+    lds_barrier();
+    uint32_t* gh = hist + (size_t)qn * kHistBins;
+    for (int e = tid; e < kHistBins; e += 256) {
+      const uint32_t v = lh[e];
+      if (v) atomicAdd(&gh[e], v);
+    }
+  }
+}
+
+template <int MT, bool HIST>
+__global__ __launch_bounds__(256) void k_idx_score_fp4(LayerParams P, const uint8_t* idx, const void* __restrict__ qI,
+                                                       const float* __restrict__ wt, const int32_t* __restrict__ pos,
+                                                       int seq_fixed, int pos0, uint32_t* __restrict__ keys,
+                                                       uint32_t* __restrict__ hist) {
+  idx_score_block_fp4<MT, HIST>(P, idx, qI, wt, pos, seq_fixed, pos0, keys, hist, blockIdx.x, blockIdx.y, false);
 }
 
 template <int MT, int KS, int QF, bool HIST>
@@ -1316,9 +1470,9 @@ __global__ __launch_bounds__(1024) void k_topk_decode(LayerParams P, const uint3
 // columns x 16 rows each, 4 waves over one of kProjSlices K slices); the
 // others score the query's cache rows except the row its own token closes,
 // building the key histogram.
-template <int MT, int QF>
+template <int MT, int QF, int IDXF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_step_scan(
-    LayerParams P, const uint16_t* idx, const void* __restrict__ qI, const float* __restrict__ wt,
+    LayerParams P, const void* idx, const void* __restrict__ qI, const float* __restrict__ wt,
     const int32_t* __restrict__ pos, uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
     const uint16_t* __restrict__ X, int M, WCat wc, float* __restrict__ proj, int nproj, int nrb) {
   const int nscan = (int)gridDim.x - nproj;
@@ -1332,7 +1486,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return;
   }
   const int i = kStepProjLast ? bid : bid - nproj;
-  idx_score_block<MT, 4, QF, true, kStepGroups>(P, idx, qI, wt, pos, 0, 0, keys, hist, i % nrb, i / nrb, true);
+  if constexpr (IDXF == CKV_FP4)
+    idx_score_block_fp4<MT, true, kStepGroups>(P, (const uint8_t*)idx, qI, wt, pos, 0, 0, keys, hist, i % nrb,
+                                               i / nrb, true);
+  else
+    idx_score_block<MT, 4, QF, true, kStepGroups>(P, (const uint16_t*)idx, qI, wt, pos, 0, 0, keys, hist, i % nrb,
+                                                  i / nrb, true);
 }
 
 // k_step_select: one block of 1024 threads per sequence.  The indexer query
@@ -1348,10 +1507,11 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
                                                       int B, const void* __restrict__ qI,
                                                       const float* __restrict__ wt, const uint32_t* __restrict__ keys,
                                                       SelWs S, int32_t* __restrict__ out) {
-  static_assert(ACTF == CKV_BF16 && IDXF == CKV_BF16, "the fused step takes bf16 activations and indexer rows");
+  static_assert(ACTF == CKV_BF16 && (IDXF == CKV_BF16 || IDXF == CKV_FP4),
+                "the fused step takes bf16 activations and bf16 or fp4 indexer rows");
   constexpr int DI = 128, CPT = DI / 16;
   __shared__ __attribute__((aligned(16))) float red[64];
-  __shared__ float idx_row[kMaxDI];
+  __shared__ __attribute__((aligned(16))) float idx_row[kMaxDI];
   __shared__ __attribute__((aligned(16))) float hsum[64];
   __shared__ float rtab[192];
   __shared__ __attribute__((aligned(16))) uint32_t h_lds[kHistBins];
@@ -1391,25 +1551,53 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
   const u32x4 h4s = *(const u32x4*)(h_lds + 4 * tid);
   uint32_t hv[4] = {h4s[0], h4s[1], h4s[2], h4s[3]};
   if (st == 1 && V == (Q.p + 1) / 4) {
-    // score of row V - 1: query tail rotated at p, cast to bf16, dotted with the row
+    // score of row V - 1: query tail rotated at p, cast to the indexer
+    // format, dotted with the row's stored values
     const int dn = DI - P.idx_rot;
-    const u32x4 q4s = *(const u32x4*)(q_lds + 4 * tid);
     float dot = 0.f;
+    if constexpr (IDXF == CKV_FP4) {
+      // this thread's 8 channels of head hh: RoPE, Hadamard and the MXFP4
+      // round trip of the query (bit-identical to the scan's 32-channel
+      // form), dotted with the row's stored values
+      const u32x4 q4s = *(const u32x4*)(q_lds + 4 * tid);
+      float v[8];
 #pragma unroll
-    for (int i = 0; i < CPT / 2; ++i) {
-      float a = bf16_to_f32(q4s[i] & 0xffffu), b2 = bf16_to_f32(q4s[i] >> 16);
-      const int c = c0 + 2 * i;
-      if (c >= dn) {   // the query's tail at p, in the compressed class's frame
-        const int j = (c - dn) >> 1;
-        const float x = a * rtab[128 + j] - b2 * rtab[160 + j], y = a * rtab[160 + j] + b2 * rtab[128 + j];
-        a = x;
-        b2 = y;
+      for (int i = 0; i < 8; i += 2) {
+        float a = bf16_to_f32(q4s[i >> 1] & 0xffffu), b2 = bf16_to_f32(q4s[i >> 1] >> 16);
+        const int c = c0 + i;
+        if (c >= dn) {
+          const int j = (c - dn) >> 1;
+          const float2 r = rope_pair(a, b2, rtab[128 + j], rtab[160 + j]);
+          a = r.x;
+          b2 = r.y;
+        }
+        v[i] = a;
+        v[i + 1] = b2;
       }
-      a = bf16_to_f32(f32_to_bf16(a));
-      b2 = bf16_to_f32(f32_to_bf16(b2));
-      dot += a * idx_row[c] + b2 * idx_row[c + 1];
+      fwht128_x8(v);
+      uint32_t sb;
+      (void)mxfp4_x8<true>(v, sb);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot += v[i] * idx_row[c0 + i];
+      dot = row16_sum(dot);
+    } else {
+      const u32x4 q4s = *(const u32x4*)(q_lds + 4 * tid);
+#pragma unroll
+      for (int i = 0; i < CPT / 2; ++i) {
+        float a = bf16_to_f32(q4s[i] & 0xffffu), b2 = bf16_to_f32(q4s[i] >> 16);
+        const int c = c0 + 2 * i;
+        if (c >= dn) {   // the query's tail at p, in the compressed class's frame
+          const int j = (c - dn) >> 1;
+          const float x = a * rtab[128 + j] - b2 * rtab[160 + j], y = a * rtab[160 + j] + b2 * rtab[128 + j];
+          a = x;
+          b2 = y;
+        }
+        a = bf16_to_f32(f32_to_bf16(a));
+        b2 = bf16_to_f32(f32_to_bf16(b2));
+        dot += a * idx_row[c] + b2 * idx_row[c + 1];
+      }
+      dot = row16_sum(dot);
     }
-    dot = row16_sum(dot);
     const bool relu = !(P.flags & CKV_FLAG_IDX_NO_RELU);
     if ((tid & 15) == 0) hsum[hh] = hh < HI ? wv * (relu ? fmaxf(dot, 0.f) : dot) : 0.f;
     lds_barrier();
@@ -1460,7 +1648,8 @@ int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const f
 }
 
 bool step_fusable(const LayerParams& P, int B) {
-  return P.ratio == 4 && P.idx_fmt == CKV_BF16 && P.DI == 128 && P.HI <= 64 && P.cap <= 32768 &&
+  return P.ratio == 4 && (P.idx_fmt == CKV_BF16 || P.idx_fmt == CKV_FP4) && P.DI == 128 && P.HI <= 64 &&
+         P.cap <= 32768 &&
          P.idx_rot == P.n_rot && P.n_rot == 64 &&
          P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && B <= 64 && P.d <= 512;
 }
@@ -1475,24 +1664,33 @@ int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache&
   const int nrb = (P.cap + RB - 1) / RB;
   const int MT = (P.HI + 15) / 16;
   dim3 grid(nproj + nrb * B);
-  const uint16_t* ix = (const uint16_t*)c.idx;
-#define CKV_SS(MTV)                                                                                         \
-  launch_score((k_step_scan<MTV, CKV_BF16>), grid, dim3(256), st, P, ix, qI, wt, pos, keys, sel.hist, \
-               (const uint16_t*)x, B, wc, proj, nproj, nrb)
-  if (MT == 1) CKV_SS(1);
-  else if (MT == 2) CKV_SS(2);
-  else if (MT == 3) CKV_SS(3);
-  else CKV_SS(4);
+  const bool fp4 = P.idx_fmt == CKV_FP4;
+#define CKV_SS(MTV, IF)                                                                                        \
+  launch_score((k_step_scan<MTV, CKV_BF16, IF>), grid, dim3(256), st, P, (const void*)c.idx, qI, wt, pos, keys, \
+               sel.hist, (const uint16_t*)x, B, wc, proj, nproj, nrb)
+#define CKV_SS_MT(IF)      \
+  if (MT == 1) CKV_SS(1, IF); \
+  else if (MT == 2) CKV_SS(2, IF); \
+  else if (MT == 3) CKV_SS(3, IF); \
+  else CKV_SS(4, IF)
+  if (fp4) CKV_SS_MT(CKV_FP4);
+  else CKV_SS_MT(CKV_BF16);
+#undef CKV_SS_MT
 #undef CKV_SS
-  if (P.kv_fmt == CKV_E4M3)
-    hipLaunchKernelGGL((k_step_select<CKV_E4M3, CKV_BF16, CKV_BF16>), dim3(B), dim3(1024), 0, st, P, w, c, u, pos,
-                       proj, B, qI, wt, keys, sel, topk);
-  else if (P.kv_fmt == CKV_BF16)
-    hipLaunchKernelGGL((k_step_select<CKV_BF16, CKV_BF16, CKV_BF16>), dim3(B), dim3(1024), 0, st, P, w, c, u, pos,
-                       proj, B, qI, wt, keys, sel, topk);
-  else
-    hipLaunchKernelGGL((k_step_select<CKV_F32, CKV_BF16, CKV_BF16>), dim3(B), dim3(1024), 0, st, P, w, c, u, pos,
-                       proj, B, qI, wt, keys, sel, topk);
+#define CKV_SEL(KF, IF)                                                                                        \
+  hipLaunchKernelGGL((k_step_select<KF, IF, CKV_BF16>), dim3(B), dim3(1024), 0, st, P, w, c, u, pos, proj, B, qI, \
+                     wt, keys, sel, topk)
+  if (P.kv_fmt == CKV_E4M3) {
+    if (fp4) CKV_SEL(CKV_E4M3, CKV_FP4);
+    else CKV_SEL(CKV_E4M3, CKV_BF16);
+  } else if (P.kv_fmt == CKV_BF16) {
+    if (fp4) CKV_SEL(CKV_BF16, CKV_FP4);
+    else CKV_SEL(CKV_BF16, CKV_BF16);
+  } else {
+    if (fp4) CKV_SEL(CKV_F32, CKV_FP4);
+    else CKV_SEL(CKV_F32, CKV_BF16);
+  }
+#undef CKV_SEL
   return (int)hipGetLastError();
 }
 
@@ -1505,7 +1703,22 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
   const int vmax = pos ? P.cap : (vlast < P.cap ? vlast : P.cap);
   dim3 grid((unsigned)(vmax > 0 ? (vmax + 255) / 256 : 1), nq);
   const bool mf = P.idx_fmt == CKV_BF16 && P.DI == 128 && P.HI <= 64;
-  if (mf && !pos && !hist && P.act_fmt == CKV_BF16) {
+  if (P.idx_fmt == CKV_FP4) {   // validated: D_I 128, H_I <= 64, bf16 queries
+    const uint8_t* ix = (const uint8_t*)c.idx;
+    const int MT = (P.HI + 15) / 16;
+    constexpr int RB = 256 * kScoreGroups;
+    dim3 mgrid((unsigned)(vmax > 0 ? (vmax + RB - 1) / RB : 1), nq);
+#define CKV_F4(MTV)                                                                                              \
+  if (hist)                                                                                                      \
+    launch_score(k_idx_score_fp4<MTV, true>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, keys, hist);  \
+  else                                                                                                           \
+    launch_score(k_idx_score_fp4<MTV, false>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, keys, hist)
+    if (MT == 1) CKV_F4(1);
+    else if (MT == 2) CKV_F4(2);
+    else if (MT == 3) CKV_F4(3);
+    else CKV_F4(4);
+#undef CKV_F4
+  } else if (mf && !pos && !hist && P.act_fmt == CKV_BF16) {
     const uint16_t* ix = (const uint16_t*)c.idx;
     const int MT = (P.HI + 15) / 16;
     constexpr int RUN = kPfRows * kPfTiles;

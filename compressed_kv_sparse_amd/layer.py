@@ -55,8 +55,11 @@ class DeviceLayer:
         self.comp = z8(batch, comp_cap, self.rb) if ratio else None
         self.st_kv = zf(batch, W, head_dim) if ratio else None
         self.st_sc = zf(batch, W, head_dim) if ratio else None
-        idt = torch.float32 if idx_fmt == "f32" else torch.int16
-        self.idx = torch.zeros((batch, comp_cap, idx_dim), dtype=idt, device=dev) if ratio == 4 else None
+        if ratio == 4 and idx_fmt == "fp4":   # 68-byte MXFP4 records
+            self.idx = z8(batch, comp_cap, L.idx_row_bytes(L.CKV_FP4, idx_dim))
+        else:
+            idt = torch.float32 if idx_fmt == "f32" else torch.int16
+            self.idx = torch.zeros((batch, comp_cap, idx_dim), dtype=idt, device=dev) if ratio == 4 else None
         self.ist_kv = zf(batch, 8, idx_dim) if ratio == 4 else None
         self.ist_sc = zf(batch, 8, idx_dim) if ratio == 4 else None
         self.max_chunk = max_chunk

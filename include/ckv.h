@@ -42,8 +42,30 @@
  *              s = max|z_c|/448 over the non-RoPE channels (1 if all zero),
  *              padded to a multiple of 128 bytes (640 bytes at head_dim 512).
  *              The FP8 round trip covers the non-RoPE part only [P1 s9].
- * ckv_row_bytes() returns the size.  Indexer rows are idx_dim values in
- * idx_fmt (F32 or BF16).
+ * ckv_row_bytes() returns the size.
+ *
+ * Indexer rows (idx_fmt; ckv_idx_row_bytes() returns the size)
+ * ------------------------------------------------------------
+ *   CKV_F32  : idx_dim float32
+ *   CKV_BF16 : idx_dim bfloat16
+ *   CKV_FP4  : the indexer's quantisation-aware form [P1 s9]: the row, after
+ *              its tail RoPE, multiplied by the orthonormal Walsh-Hadamard
+ *              matrix of order idx_dim (Sylvester order, entries
+ *              +-1/sqrt(idx_dim)), then stored as OCP MXFP4: per block of 32
+ *              consecutive channels one E8M0 scale 2^e, e = floor(log2 of the
+ *              block's max |x|) - 2 clamped to [-127, 127] (-127 for an
+ *              all-zero block), and 32 E2M1 codes of x / 2^e (grid 0, 0.5, 1,
+ *              1.5, 2, 3, 4, 6; nearest, ties to the even code, saturated at
+ *              6; bit 3 the sign, kept only for a nonzero magnitude).  Record:
+ *              idx_dim/2 code bytes (channel 2j in the low nibble of byte j,
+ *              2j+1 in the high one), then idx_dim/32 bytes e + 127 -- 68
+ *              bytes at idx_dim 128.  The indexer query gets the same
+ *              transform (RoPE, Hadamard, MXFP4 round trip) before the dot
+ *              products, so scores are exact products of the two fp4 vectors.
+ *              The pages name the transform and the 4-bit width but not the
+ *              block size, scale rule or bit layout: these are the OCP
+ *              microscaling format's.  Built for ratio 4, idx_dim 128,
+ *              idx_heads <= 64 and act_fmt BF16.
  */
 #ifndef CKV_H
 #define CKV_H
@@ -75,6 +97,7 @@ extern "C" {
 #define CKV_F32 0
 #define CKV_BF16 1
 #define CKV_E4M3 2
+#define CKV_FP4 3   /* indexer rows only */
 
 /* ---- desc.flags ------------------------------------------------------------ */
 #define CKV_FLAG_NO_INV_ROPE 1u  /* skip the inverse RoPE on the output [P4]   */
@@ -112,7 +135,7 @@ extern "C" {
  *   comp_cap    compressed rows per sequence the cache holds
  *   batch       sequences the cache holds
  *   kv_fmt      CKV_F32 / CKV_BF16 / CKV_E4M3 for raw and compressed rows
- *   idx_fmt     CKV_F32 / CKV_BF16 for indexer rows
+ *   idx_fmt     CKV_F32 / CKV_BF16 / CKV_FP4 for indexer rows
  *   act_fmt     CKV_F32 / CKV_BF16 for x, u, q, qI and out
  *   w_fmt       CKV_F32 / CKV_BF16 for wkv / wgate / idx_wkv / idx_wgate
  *   rope_base   the layer's RoPE base [P1 s8]: it serves the raw rows and the
@@ -216,6 +239,12 @@ typedef struct ckv_layer_cache {
 /* Bytes of one stored K=V row in format fmt; 0 for an unknown format. */
 size_t ckv_row_bytes(int32_t fmt, int32_t head_dim, int32_t n_rot);
 
+/* Bytes of one stored indexer row of idx_dim channels in format fmt
+ * (CKV_F32 4 idx_dim, CKV_BF16 2 idx_dim, CKV_FP4 idx_dim/2 + idx_dim/32 for a
+ * multiple of 32); 0 for an unknown format or a size the format cannot hold.
+ * The indexer cache is [batch][comp_cap] such rows, back to back. */
+size_t ckv_idx_row_bytes(int32_t fmt, int32_t idx_dim);
+
 /* Fail-fast check of a layer description against what the library is built
  * for [P1 s1: the engine refuses a layout it was not built for rather than
  * guessing].  Returns CKV_OK, CKV_E_INVAL or CKV_E_UNSUPPORTED. */
@@ -287,7 +316,8 @@ int ckv_compress_append_prefill(const ckv_layer_desc* desc, const ckv_layer_weig
  * [P1 s6; P4 DSA] (ratio 4 only, else CKV_E_UNSUPPORTED) ------------------------
  *
  * For query position p, V = (p+1)/4 rows are visible.  The indexer query
- * qI[h] is RoPE'd at p (tail) and cast to idx_fmt; row s scores
+ * qI[h] is RoPE'd at p (tail) and cast to idx_fmt (for CKV_FP4: Hadamard,
+ * then the MXFP4 round trip); row s scores
  * I(s) = sum_h w[h] * relu(qI[h] . idx[s]).  topk[0..k) receives the k best
  * rows (ties to the lower index) in ascending index order, -1 padded; when
  * V <= k it receives 0..V-1 then -1s.

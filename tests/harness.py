@@ -109,6 +109,69 @@ def compare_rows(gpu_rec, ref_z, fmt, d, n_rot, what):
         assert_close(gt, ref_z[n, dn:], BF16_TOL, f"{what} row {n} tail")
 
 
+FP4_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])   # E2M1 rounding boundaries
+FP4_T_MARGIN = 2e-5    # distance (in units of the block scale) taken as a possible rounding flip
+FP4_E_MARGIN = 1e-5    # relative distance of a block max from a power of two
+
+
+def fp4_ordinal(codes):
+    c = np.asarray(codes).astype(np.int64)
+    return np.where(c & 8, -(c & 7), c & 7)
+
+
+def fp4_unpack(rec, n):
+    rec = np.asarray(rec, np.uint8)
+    codes = np.empty(rec.shape[:-1] + (n,), np.uint8)
+    codes[..., 0::2] = rec[..., :n // 2] & 15
+    codes[..., 1::2] = rec[..., :n // 2] >> 4
+    return codes, rec[..., n // 2:n // 2 + n // 32].astype(np.int64) - 127
+
+
+def fp4_fragile(h):
+    """Per value of Hadamard-domain vectors h [..., n]: True where a float32
+    computation of h could round to another MXFP4 code than fp64 does (the
+    scaled value lies within FP4_T_MARGIN of a rounding boundary, or its
+    block's max lies within FP4_E_MARGIN of a power of two)."""
+    h = np.asarray(h, np.float64)
+    blk = h.reshape(h.shape[:-1] + (h.shape[-1] // 32, 32))
+    amax = np.abs(blk).max(-1)
+    with np.errstate(divide="ignore"):
+        lg = np.log2(np.where(amax > 0, amax, 1.0))
+    near_pow2 = (amax > 0) & (np.abs(lg - np.round(lg)) < FP4_E_MARGIN)
+    e = np.where(amax > 0, np.floor(lg) - 2, -127)
+    t = np.abs(blk) / np.ldexp(1.0, e.astype(np.int64))[..., None]
+    near_mid = np.min(np.abs(t[..., None] - FP4_MIDPOINTS), axis=-1) < FP4_T_MARGIN
+    return (near_mid | near_pow2[..., None]).reshape(h.shape)
+
+
+def compare_fp4_rows(gpu_rec, pre, what):
+    """GPU fp4 indexer records vs the oracle's pre-rounding (Hadamard-domain)
+    values: block scales and codes equal to the oracle's own encoding, except
+    where fp4_fragile marks the value, where the neighbouring code (and for a
+    block max at a power of two, the neighbouring scale) is accepted."""
+    pre = np.atleast_2d(np.asarray(pre, np.float64))
+    n = pre.shape[-1]
+    gpu_rec = np.asarray(gpu_rec, np.uint8).reshape(pre.shape[0], -1)
+    ref_rec = O.fp4_encode_rows(pre)
+    cg, eg = fp4_unpack(gpu_rec, n)
+    cr, er = fp4_unpack(ref_rec, n)
+    frag = fp4_fragile(pre)
+    blk_frag = frag.reshape(pre.shape[0], n // 32, 32).any(-1)
+    bad_e = (eg != er) & ~((np.abs(eg - er) == 1) & blk_frag)
+    assert not bad_e.any(), f"{what}: block scale differs at {np.argwhere(bad_e)[:5].tolist()}"
+    same_e = np.repeat(eg == er, 32, axis=-1)
+    dist = np.abs(fp4_ordinal(cg) - fp4_ordinal(cr))
+    bad = same_e & (dist > 0) & ~((dist == 1) & frag)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} fp4 codes differ (first {np.argwhere(bad)[:5].tolist()})")
+
+
+def fp4_query_fragile(L, p, qI):
+    """True when the indexer query's MXFP4 codes at position p could differ
+    between a float32 and an fp64 computation (see fp4_fragile)."""
+    qh = L.rope(O.decode_values(qI, L.act_fmt), p, L.base_comp, min(L.n_rot, L.idx_dim))
+    return bool(fp4_fragile(O.hadamard(qh)).any())
+
+
 def topk_margin(scores: np.ndarray, k: int) -> float:
     """Gap between the k-th and (k+1)-th largest score, relative to max|s|
     (inf when every row is selected)."""
@@ -124,13 +187,15 @@ def sets_equal(gpu_topk: np.ndarray, ref_topk: np.ndarray) -> bool:
 
 def tie_free_queries(cfg, seqs, pos, qI, w, attempts=40, margin=1e-4):
     """Redraw q^I / w of any query whose oracle score gap at the k boundary is
-    below ``margin`` (same generator, sub-seed per query and attempt)."""
+    below ``margin``, or (fp4 indexer) whose MXFP4 codes are fragile (same
+    generator, sub-seed per query and attempt)."""
     qI, w = qI.copy(), w.copy()
     for b, seq in enumerate(seqs):
         for a in range(attempts):
-            sc = seq.index_scores(int(pos[b]), qI[b], w[b])
-            if topk_margin(sc, cfg.top_k) > margin:
-                break
+            if not (cfg.idx_fmt == "fp4" and fp4_query_fragile(seq.L, int(pos[b]), qI[b])):
+                sc = seq.index_scores(int(pos[b]), qI[b], w[b])
+                if topk_margin(sc, cfg.top_k) > margin:
+                    break
             nq, nw = G.draw_query_index(cfg, 1, sub=b, attempt=a + 1)
             qI[b], w[b] = nq[0], nw[0]
         else:

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -86,6 +86,29 @@ def test_validate_bounds_match_the_header():
         d = desc(ratio=128, comp_cap=cap, kv_fmt=L.CKV_BF16)
         assert L.validate(d) == 0
         assert L.workspace_bytes(d, L.CKV_MODE_PREFILL, 4096) > 0
+
+
+def test_fp4_indexer_rows():
+    """CKV_FP4 indexer rows: 68-byte records at idx_dim 128, accepted on ratio-4
+    layers with idx_dim 128 and bf16 activations only; KEEP_F32 excludes it."""
+    assert L.idx_row_bytes(L.CKV_FP4, 128) == 68
+    assert L.idx_row_bytes(L.CKV_FP4, 64) == 34
+    assert L.idx_row_bytes(L.CKV_FP4, 100) == 0
+    assert L.idx_row_bytes(L.CKV_BF16, 128) == 256
+    assert L.idx_row_bytes(L.CKV_F32, 64) == 256
+    assert L.idx_row_bytes(L.CKV_E4M3, 128) == 0
+    assert L.row_bytes(L.CKV_FP4, 512) == 0            # not a K=V row format
+    assert L.validate(desc(idx_fmt=L.CKV_FP4)) == 0
+    assert L.validate(desc(idx_fmt=L.CKV_FP4, kv_fmt=L.CKV_BF16, idx_heads=8)) == 0
+    assert L.validate(desc(idx_fmt=L.CKV_FP4, idx_dim=64)) == L.CKV_E_UNSUPPORTED
+    assert L.validate(desc(idx_fmt=L.CKV_FP4, act_fmt=L.CKV_F32)) == L.CKV_E_UNSUPPORTED
+    assert L.validate(desc(kv_fmt=L.CKV_FP4)) == L.CKV_E_UNSUPPORTED
+    assert L.validate(desc(idx_fmt=4)) == L.CKV_E_UNSUPPORTED
+    f32 = dict(kv_fmt=L.CKV_F32, act_fmt=L.CKV_F32, w_fmt=L.CKV_F32)
+    assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, idx_fmt=L.CKV_FP4, **f32)) == L.CKV_E_UNSUPPORTED
+    d4, d16 = desc(idx_fmt=L.CKV_FP4), desc()
+    for mode, n in ((L.CKV_MODE_DECODE, 16), (L.CKV_MODE_PREFILL, 4096)):
+        assert L.workspace_bytes(d4, mode, n) == L.workspace_bytes(d16, mode, n)
 
 
 def test_row_bytes_and_workspace():

@@ -11,8 +11,9 @@ import numpy as np
 import pytest
 
 import oracle as O
-from harness import (BF16_TOL, FP8_TOL, assert_close, compare_rows, dev, device_layer, oracle_layer,
-                     oracle_seq_from_bytes, oracle_seq_from_init, sets_equal, tie_free_queries, topk_margin)
+from harness import (BF16_TOL, FP8_TOL, assert_close, compare_fp4_rows, compare_rows, dev, device_layer,
+                     fp4_query_fragile, oracle_layer, oracle_seq_from_bytes, oracle_seq_from_init, sets_equal,
+                     tie_free_queries, topk_margin)
 from workloads import get_config, make_decode_inputs, make_layer_weights, make_prefill_inputs
 from workloads import gen as G
 
@@ -92,6 +93,14 @@ def check_attention(cfg, inp, bseqs, tk, out, tol):
         assert_close(og[b], ref, tol, f"attention output b={b}")
 
 
+def check_idx_row(cfg, rec, pre, what):
+    """A stored indexer row vs the oracle's value before the format's rounding."""
+    if cfg.idx_fmt == "fp4":
+        compare_fp4_rows(rec, pre, what)
+    else:
+        assert_close(O.decode_values(rec, cfg.idx_fmt), pre, BF16_TOL, what)
+
+
 def check_compressor(cfg, inp, dl, L):
     """Compressor + raw insertion of one decode step vs the oracle run from
     the drawn state; returns the cache bytes the GPU holds."""
@@ -109,8 +118,7 @@ def check_compressor(cfg, inp, dl, L):
             i = (p + 1) // cfg.ratio - 1
             compare_rows(comp_g[b, i], seq.comp_row(i)[0], cfg.kv_fmt, d, cfg.n_rot, f"comp row {i} b={b}")
             if cfg.ratio == 4:
-                gi = O.decode_values(idx_g[b, i], cfg.idx_fmt)
-                assert_close(gi, seq.idx_row(i)[0], BF16_TOL, f"idx row {i} b={b}")
+                check_idx_row(cfg, idx_g[b, i], seq.idx_row(i)[0], f"idx row {i} b={b}")
         if cfg.ratio:
             W = cfg.window
             kap = seq.kap[p]
@@ -166,6 +174,14 @@ def run_decode_step_checks(cfg, inp, wts, tol):
     check_attention(cfg, inp, bseqs, tk, out, tol)
 
 
+def test_c5_c4a_fp4_indexer_decode_full_size():
+    """The 16 x 131072-token c4a decode with the fp4 indexer cache, stage by
+    stage: compressor rows (fp4 records against the oracle's encoding), top-k
+    on the stored records, attention."""
+    cfg = get_config("c5_fp4idx")
+    run_decode_stage_checks(cfg, make_decode_inputs(cfg), make_layer_weights(cfg), FP8_TOL)
+
+
 def test_c2_c4a_decode_full_size():
     cfg = get_config("c2")
     run_decode_stage_checks(cfg, make_decode_inputs(cfg), make_layer_weights(cfg), BF16_TOL)
@@ -191,7 +207,7 @@ def test_c5_c128a_and_swa_layers_decode():
         run_decode_stage_checks(cfg, make_decode_inputs(cfg), make_layer_weights(cfg), FP8_TOL)
 
 
-@pytest.mark.parametrize("name", ["c2", "c5", "c3", "c5_swa"])
+@pytest.mark.parametrize("name", ["c2", "c5", "c3", "c5_swa", "c5_fp4idx"])
 def test_decode_step_full_size(name):
     """The single-call decode step at full size: fused on the c4a layers,
     the three separate calls on c128a and sliding-window-only layers."""
@@ -212,26 +228,27 @@ def test_decode_selection_beyond_one_block(cap, n):
     run_decode_step_checks(cfg, inp, wts, FP8_TOL)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
-def test_decode_step_short_contexts(fmt):
+@pytest.mark.parametrize("fmt,idx_fmt", [("bf16", "bf16"), ("e4m3", "bf16"), ("e4m3", "fp4")])
+def test_decode_step_short_contexts(fmt, idx_fmt):
     """Fused step on short and ragged contexts: V <= k, the first rows,
     positions that close a row and positions that do not."""
     base = get_config("c2")
-    cfg = base.with_(batch=8, comp_cap=512, kv_fmt=fmt, idx_heads=8, idx_dim=128, top_k=64, seed=13,
-                     name=f"step_short_{fmt}")
+    cfg = base.with_(batch=8, comp_cap=512, kv_fmt=fmt, idx_fmt=idx_fmt, idx_heads=8, idx_dim=128, top_k=64,
+                     seed=13, name=f"step_short_{fmt}_{idx_fmt}")
     n = np.array([1, 3, 4, 8, 259, 260, 1023, 2047], np.int64)
     run_decode_step_checks(cfg, make_decode_inputs(cfg, n_ctx=n), make_layer_weights(cfg),
                            FP8_TOL if fmt == "e4m3" else BF16_TOL)
 
 
-@pytest.mark.parametrize("ratio,fmt", [(4, "bf16"), (4, "e4m3"), (128, "bf16"), (0, "bf16")])
-def test_short_contexts_and_ragged_batch(ratio, fmt):
+@pytest.mark.parametrize("ratio,fmt,idx_fmt", [(4, "bf16", "bf16"), (4, "e4m3", "bf16"), (4, "bf16", "fp4"),
+                                                (128, "bf16", "bf16"), (0, "bf16", "bf16")])
+def test_short_contexts_and_ragged_batch(ratio, fmt, idx_fmt):
     """Positions below the window and the top-k size (V <= k, raw window < 128,
     row 0's empty slots), mixed per sequence."""
     base = get_config("c2")
-    cfg = base.with_(ratio=ratio, batch=8, comp_cap={4: 512, 128: 64, 0: 0}[ratio], kv_fmt=fmt,
+    cfg = base.with_(ratio=ratio, batch=8, comp_cap={4: 512, 128: 64, 0: 0}[ratio], kv_fmt=fmt, idx_fmt=idx_fmt,
                      idx_heads=8 if ratio == 4 else 0, idx_dim=128 if ratio == 4 else 0,
-                     top_k=64 if ratio == 4 else 0, seed=11, name=f"short_r{ratio}_{fmt}")
+                     top_k=64 if ratio == 4 else 0, seed=11, name=f"short_r{ratio}_{fmt}_{idx_fmt}")
     n = np.array([1, 4, 8, 100, 129, 260, 1024, 2047 if ratio != 128 else 8192], np.int64)
     run_decode_stage_checks(cfg, make_decode_inputs(cfg, n_ctx=n), make_layer_weights(cfg),
                             FP8_TOL if fmt == "e4m3" else BF16_TOL)
@@ -336,10 +353,11 @@ def test_c1_prefill_chunks_equal_sequential_decode(chunks):
         assert_close(outs[p], ref["out_f64"], BF16_TOL, f"output of query {p}")
 
 
-def test_c4_prefill_chunk_sampled():
+@pytest.mark.parametrize("name", ["c4", "c4_fp4idx"])
+def test_c4_prefill_chunk_sampled(name):
     """4096-token chunk at 61440 (compressor windows straddle the chunk edge):
     every emitted row, and sampled queries' top-k and outputs."""
-    cfg = get_config("c4")
+    cfg = get_config(name)
     wts = make_layer_weights(cfg)
     inp = make_prefill_inputs(cfg)
     L = oracle_layer(cfg, wts)
@@ -350,7 +368,8 @@ def test_c4_prefill_chunk_sampled():
     qI, w = inp.qI.copy(), inp.w.copy()
     for n in sample:
         for a in range(40):
-            if topk_margin(seq.index_scores(p0 + n, qI[n], w[n]), cfg.top_k) > MARGIN:
+            if not (cfg.idx_fmt == "fp4" and fp4_query_fragile(L, p0 + n, qI[n])) and \
+                    topk_margin(seq.index_scores(p0 + n, qI[n], w[n]), cfg.top_k) > MARGIN:
                 break
             nq, nw = G.draw_query_index(cfg, 1, sub=9000 + n, attempt=a + 1)
             qI[n], w[n] = nq[0], nw[0]
@@ -361,7 +380,7 @@ def test_c4_prefill_chunk_sampled():
     comp_g, idx_g = cpu(dl.comp)[0], cpu(dl.idx)[0]
     for i in range(p0 // 4, (p0 + T) // 4, 37):
         compare_rows(comp_g[i], seq.comp_row(i)[0], cfg.kv_fmt, cfg.head_dim, cfg.n_rot, f"comp row {i}")
-        assert_close(O.decode_values(idx_g[i], cfg.idx_fmt), seq.idx_row(i)[0], BF16_TOL, f"idx row {i}")
+        check_idx_row(cfg, idx_g[i], seq.idx_row(i)[0], f"idx row {i}")
     i = p0 // 4   # the row whose window straddles the chunk edge
     compare_rows(comp_g[i], seq.comp_row(i)[0], cfg.kv_fmt, cfg.head_dim, cfg.n_rot, "edge row")
     og, tkg = out_values(out, cfg.act_fmt), cpu(tk)
@@ -375,22 +394,31 @@ def test_c4_prefill_chunk_sampled():
         assert_close(og[n], ref, BF16_TOL, f"output of query {n}")
 
 
-def test_indexer_score_stage_keys():
+@pytest.mark.parametrize("idx_fmt", ["bf16", "fp4"])
+def test_indexer_score_stage_keys(idx_fmt):
     """ckv_indexer_score_decode alone: keys decode to the oracle's scores."""
     from compressed_kv_sparse_amd import _lib as L
-    cfg = get_config("c5").with_(batch=4, comp_cap=4096, seed=31, name="score_stage")
+    cfg = get_config("c5").with_(batch=4, comp_cap=4096, seed=31, idx_fmt=idx_fmt, name=f"score_stage_{idx_fmt}")
     inp = make_decode_inputs(cfg, n_ctx=np.array([16384, 9001, 4100, 333]))
     wts = make_layer_weights(cfg)
+    Lo = oracle_layer(cfg, wts)
+    qI, w = inp.qI.copy(), inp.w.copy()
+    for b in range(cfg.batch):   # fp4: queries whose MXFP4 codes cannot flip between fp32 and fp64
+        a = 0
+        while idx_fmt == "fp4" and fp4_query_fragile(Lo, int(inp.pos[b]), qI[b]):
+            a += 1
+            assert a < 40, f"no robust fp4 query for sequence {b}"
+            nq, nw = G.draw_query_index(cfg, 1, sub=b, attempt=a)
+            qI[b], w[b] = nq[0], nw[0]
     dl = device_layer(cfg, wts, inp.cache)
     # one guard row after the batch's [B, comp_cap] keys must stay untouched
     keys_g = torch.zeros((cfg.batch + 1, cfg.comp_cap), dtype=torch.int32, device="cuda")
     keys = keys_g[:cfg.batch]
-    rc = L.indexer_score_decode(dl.desc, dl.cache, dev(inp.qI), dev(inp.w), dev(inp.pos), cfg.batch, keys,
+    rc = L.indexer_score_decode(dl.desc, dl.cache, dev(qI), dev(w), dev(inp.pos), cfg.batch, keys,
                                 torch.cuda.current_stream().cuda_stream)
     assert rc == 0
     torch.cuda.synchronize()
     kg = cpu(keys).view(np.uint32)
-    Lo = oracle_layer(cfg, wts)
     for b in range(cfg.batch):
         p = int(inp.pos[b])
         V = (p + 1) // 4
@@ -398,7 +426,7 @@ def test_indexer_score_stage_keys():
         bits = np.where(k & 0x80000000, k & 0x7FFFFFFF, ~k).astype(np.uint32)
         sc = bits.view(np.float32).astype(np.float64)
         seq = oracle_seq_from_bytes(Lo, cpu(dl.raw)[b], cpu(dl.comp)[b], cpu(dl.idx)[b], p + 1)
-        ref = seq.index_scores(p, inp.qI[b], inp.w[b])
+        ref = seq.index_scores(p, qI[b], w[b])
         assert np.max(np.abs(sc - ref)) <= 1e-4 * np.max(np.abs(ref)), f"scores b={b}"
     assert np.all(cpu(keys_g[cfg.batch]) == 0), "keys written past the batch's rows"
 

@@ -54,7 +54,7 @@ class LayerShape:
     n_ctx: int                 # tokens seen including the query (decode)
     comp_cap: int              # compressed rows per sequence the cache holds
     kv_fmt: str = "bf16"       # f32 | bf16 | e4m3
-    idx_fmt: str = "bf16"      # f32 | bf16
+    idx_fmt: str = "bf16"      # f32 | bf16 | fp4 (Hadamard + MXFP4 records)
     act_fmt: str = "bf16"      # f32 | bf16
     w_fmt: str = "bf16"        # f32 | bf16
     n_rot: int = 64
@@ -142,6 +142,11 @@ for _f in (_c1, _c2, _c3, _c4):
 for _r, _l in ((4, 2), (128, 3), (0, 0)):
     _c = _c5(_r, _l)
     CONFIGS[_c.name] = _c
+# the same c4a decode and prefill workloads with the indexer cache in the
+# quantisation-aware fp4 form (Hadamard-128 + MXFP4 records of 68 bytes)
+for _c in (_c5(4, 2).with_(name="c5_c4a_decode_b16_ctx131072_fp8_fp4idx", idx_fmt="fp4"),
+           _c4().with_(name="c4_c4a_prefill_T4096_at61440_bf16_fp4idx", idx_fmt="fp4")):
+    CONFIGS[_c.name] = _c
 
 # short aliases
 ALIASES = {
@@ -152,6 +157,8 @@ ALIASES = {
     "c5": "c5_c4a_decode_b16_ctx131072_fp8",
     "c5_c128a": "c5_c128a_decode_b16_ctx131072_fp8",
     "c5_swa": "c5_swa_decode_b16_ctx131072_fp8",
+    "c5_fp4idx": "c5_c4a_decode_b16_ctx131072_fp8_fp4idx",
+    "c4_fp4idx": "c4_c4a_prefill_T4096_at61440_bf16_fp4idx",
 }
 
 

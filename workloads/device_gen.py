@@ -22,7 +22,7 @@ import zlib
 
 import torch
 
-from .gen import e4m3_row_offsets
+from .gen import FP4_SCALE_BYTES, e4m3_row_offsets
 
 
 def _gen(seed: int, name: str, layer: int) -> torch.Generator:
@@ -66,6 +66,16 @@ def fill_rows(dst: torch.Tensor, fmt: str, d: int, n_rot: int, g: torch.Generato
     dst[..., soff:soff + 4] = sc.view(torch.uint8).reshape(shape + (4,))
 
 
+def fill_fp4_records(dst: torch.Tensor, dim: int, g) -> None:
+    """fp4 indexer records as gen.draw_fp4_records lays them out: uniform
+    4-bit codes, block-scale bytes uniform in FP4_SCALE_BYTES."""
+    lo, hi = FP4_SCALE_BYTES
+    dst[..., :dim // 2].copy_(torch.randint(0, 256, tuple(dst.shape[:-1]) + (dim // 2,), generator=g,
+                                            device="cuda", dtype=torch.int32).to(torch.uint8))
+    dst[..., dim // 2:].copy_(torch.randint(lo, hi + 1, tuple(dst.shape[:-1]) + (dim // 32,), generator=g,
+                                            device="cuda", dtype=torch.int32).to(torch.uint8))
+
+
 def fill_layer_cache(dl, cfg) -> None:
     """Fill every cache tensor of a DeviceLayer as at a warm context (all rows
     drawn); every sequence has stored n_ctx - 1 tokens, so the step's token
@@ -80,6 +90,8 @@ def fill_layer_cache(dl, cfg) -> None:
     if dl.idx is not None:
         if cfg.idx_fmt == "bf16":
             dl.idx.copy_(bf16_draw(tuple(dl.idx.shape), _gen(s, "idx", L)))
+        elif cfg.idx_fmt == "fp4":
+            fill_fp4_records(dl.idx, cfg.idx_dim, _gen(s, "idx", L))
         else:
             dl.idx.normal_(generator=_gen(s, "idx", L))
         dl.ist_kv.normal_(generator=_gen(s, "ist_kv", L))

@@ -10,6 +10,8 @@ values.  Values are returned as the exact stored bit patterns:
   rounding step of the method)
 * ``e4m3`` -> uint8 row records (see :func:`row_bytes`) whose fp8 codes are
   drawn directly as sign / exponent / mantissa fields.
+* ``fp4`` (indexer rows) -> uint8 records (see :func:`idx_row_bytes`) whose
+  4-bit codes and block-scale bytes are drawn directly.
 
 Nothing here projects, pools, normalises, rotates, scores, selects or
 attends.
@@ -46,6 +48,19 @@ def row_bytes(fmt: str, d: int, n_rot: int = 64) -> int:
     if fmt == "e4m3":
         raw = (d - n_rot) + 2 * n_rot + 4
         return (raw + ROW_ALIGN - 1) // ROW_ALIGN * ROW_ALIGN
+    raise ValueError(fmt)
+
+
+def idx_row_bytes(fmt: str, dim: int) -> int:
+    """Bytes one stored indexer row occupies: f32 4 dim, bf16 2 dim; ``fp4``
+    records hold dim/2 bytes of 4-bit codes (two channels a byte, the even
+    channel in the low nibble) and then dim/32 one-byte block scales."""
+    if fmt == "f32":
+        return 4 * dim
+    if fmt == "bf16":
+        return 2 * dim
+    if fmt == "fp4":
+        return dim // 2 + dim // 32
     raise ValueError(fmt)
 
 
@@ -118,7 +133,23 @@ def draw_rows(rng, n_rows_shape, fmt: str, d: int, n_rot: int = 64) -> np.ndarra
     return out
 
 
+FP4_SCALE_BYTES = (125, 127)   # block scales 2^-2 .. 2^0 (E8M0 bytes e + 127)
+
+
+def draw_fp4_records(rng, shape, dim: int) -> np.ndarray:
+    """fp4 indexer records with every 4-bit code uniform over its 16 values and
+    block-scale bytes uniform in FP4_SCALE_BYTES (inclusive)."""
+    shape = tuple(shape)
+    out = np.empty(shape + (idx_row_bytes("fp4", dim),), np.uint8)
+    out[..., :dim // 2] = rng.integers(0, 256, size=shape + (dim // 2,), dtype=np.uint8)
+    lo, hi = FP4_SCALE_BYTES
+    out[..., dim // 2:] = rng.integers(lo, hi + 1, size=shape + (dim // 32,), dtype=np.uint8)
+    return out
+
+
 def draw_idx_rows(rng, shape, fmt: str, dim: int) -> np.ndarray:
+    if fmt == "fp4":
+        return draw_fp4_records(rng, shape, dim)
     return draw_values(rng, tuple(shape) + (dim,), fmt)
 
 
@@ -227,7 +258,10 @@ def _draw_cache(cfg: LayerShape, first_live: np.ndarray, empty: bool) -> CacheIn
         st_sc = np.zeros((B, W, d), np.float32)
     if r == 4:
         DI = cfg.idx_dim
-        idx = np.zeros((B, cap, DI), np.float32 if cfg.idx_fmt == "f32" else np.uint16)
+        if cfg.idx_fmt == "fp4":
+            idx = np.zeros((B, cap, idx_row_bytes("fp4", DI)), np.uint8)
+        else:
+            idx = np.zeros((B, cap, DI), np.float32 if cfg.idx_fmt == "f32" else np.uint16)
         ist_kv = np.zeros((B, 8, DI), np.float32)
         ist_sc = np.zeros((B, 8, DI), np.float32)
     if empty:
