@@ -179,6 +179,7 @@ extern "C" int ckv_indexer_topk_decode(const ckv_layer_desc* desc, const ckv_lay
   sel.sure = (uint32_t*)(wb + L.sure);
   sel.cand_key = (uint32_t*)(wb + L.cand_key);
   sel.cand_idx = (uint32_t*)(wb + L.cand_idx);
+  sel.qf4 = wb + L.qf4;
   return launched(launch_indexer(P, to_cache(cache), qI, w, pos, 0, 0, B, (uint32_t*)(wb + L.keys), &sel,
                                  topk, stream));
 }
@@ -292,6 +293,7 @@ extern "C" int ckv_decode_step(const ckv_layer_desc* desc, const ckv_layer_weigh
   sel.sure = (uint32_t*)(wb + L.sure);
   sel.cand_key = (uint32_t*)(wb + L.cand_key);
   sel.cand_idx = (uint32_t*)(wb + L.cand_idx);
+  sel.qf4 = wb + L.qf4;
   const Cache C = to_cache(cache);
   if ((rc = launch_step_scan_select(P, to_weights(w), C, x, u, qI, iw, pos, B, (float*)(wb + L.proj),
                                     (uint32_t*)(wb + L.keys), sel, topk, stream)))

@@ -71,6 +71,7 @@ struct SelWs {
   uint32_t* sure;
   uint32_t* cand_key;
   uint32_t* cand_idx;
+  uint8_t* qf4;   // fp4 indexer: each query's rotated, transformed query as [n][64 heads] 68-byte records
 };
 
 struct WsLayout {
@@ -81,6 +82,7 @@ struct WsLayout {
   size_t sure;      // uint32 [n][top_k]
   size_t cand_key;  // uint32 [n][kCandCap]
   size_t cand_idx;  // uint32 [n][kCandCap]
+  size_t qf4;       // uint8 [n][64][68]   fp4 indexer decode: the queries in fp4 record form
   size_t proj;      // float [proj_splits][n][ncol]
   size_t keys;      // uint32 [n][cap]   indexer keys
   size_t pool;      // float [n][d] + [n][8][2]   c128a decode: pooled rows and slice sums

@@ -118,6 +118,8 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
     L.cand_idx = off;
     off += align256((size_t)n * kCandCap * sizeof(uint32_t));
   }
+  L.qf4 = off;
+  if (P.ratio == 4 && !prefill && P.idx_fmt == CKV_FP4) off += align256((size_t)n * 64 * 68);
   L.proj = off;
   off += align256((size_t)L.proj_splits * n * P.ncol * sizeof(float));
   L.keys = off;

@@ -36,16 +36,16 @@ typedef u32x4 u32x4_a4 __attribute__((aligned(4)));
 
 // Butterfly on the lane bit that permlane swap S exchanges: the lane with the
 // bit clear receives a + b, the other a - b (a from the lane with the bit clear).
-__device__ __forceinline__ float hbfly32(float v, bool hi) {
+// neg: 0x80000000 on the lanes with the bit set, else 0 (a + (-b) is a - b
+// exactly).
+__device__ __forceinline__ float hbfly32(float v, uint32_t neg) {
   const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   // s[0]: the value of the lane with bit 5 clear, s[1]: with bit 5 set
-  const float a = __uint_as_float(s[0]), b = __uint_as_float(s[1]);
-  return hi ? a - b : a + b;
+  return __uint_as_float(s[0]) + __uint_as_float(s[1] ^ neg);
 }
-__device__ __forceinline__ float hbfly16(float v, bool hi) {
+__device__ __forceinline__ float hbfly16(float v, uint32_t neg) {
   const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float a = __uint_as_float(s[0]), b = __uint_as_float(s[1]);
-  return hi ? a - b : a + b;
+  return __uint_as_float(s[0]) + __uint_as_float(s[1] ^ neg);
 }
 
 // Orthonormal 128-point Walsh-Hadamard transform of the vector held by lanes
@@ -65,47 +65,60 @@ __device__ __forceinline__ void fwht128(float (&v)[32]) {
     }
   }
   const int lane = threadIdx.x & 63;
+  const uint32_t n16 = (lane & 16) ? 0x80000000u : 0u, n32 = (lane & 32) ? 0x80000000u : 0u;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = hbfly16(v[i], lane & 16);
+  for (int i = 0; i < 32; ++i) v[i] = hbfly16(v[i], n16);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = hbfly32(v[i], lane & 32) * 0.08838834764831845f;   // 1 / sqrt(128)
+  for (int i = 0; i < 32; ++i) v[i] = hbfly32(v[i], n32) * 0.08838834764831845f;   // 1 / sqrt(128)
 }
 
-// E2M1 magnitude code of a >= 0 (a value already divided by its block scale):
-// nearest grid point, ties to the even code, 6 and above -> 7.
-__device__ __forceinline__ uint32_t e2m1_mag(float a) {
-  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
-         (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-}
+// E2M1 magnitude of code m (0..7)
 __device__ __forceinline__ float e2m1_value(uint32_t m) {
   return m < 4 ? 0.5f * (float)m : m == 4 ? 2.f : m == 5 ? 3.f : m == 6 ? 4.f : 6.f;
 }
 
+// Block exponent of a block whose largest magnitude is am: e = floor(log2 am)
+// - 2 (frexp's exponent is floor(log2 am) + 1), -127 for am = 0 or below
+// 2^-125; at most 125 for any finite float.
+__device__ __forceinline__ int mxfp4_exponent(float am) {
+  return am > 0.f ? max(__builtin_amdgcn_frexp_expf(am) - 3, -127) : -127;
+}
+
+// E2M1 codes of 8 values divided by 2^e (value i at nibble i), by the gfx950
+// conversion v_cvt_scalef32_pk_fp4_f32, which divides by its scale operand
+// and rounds to the nearest grid point, ties to the even code, saturating at
+// 6 -- measured against the rounding rule on MI355X for values around every
+// boundary and tie and for scales 2^-100 .. 2^10.  It keeps the sign of a
+// negative value that rounds to zero (code 8); the stored form has code 0
+// there, so those sign bits are cleared.  The scale 2^-127 is not a normal
+// float: that case divides 2 x by 2^-126 instead (both exact).
+__device__ __forceinline__ uint32_t fp4_codes8(float v0, float v1, float v2, float v3, float v4, float v5, float v6,
+                                               float v7, int e) {
+  const float s = __uint_as_float((uint32_t)(127 + max(e, -126)) << 23);
+  const float pre = e == -127 ? 2.f : 1.f;
+  uint32_t r = 0u;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v0 * pre, v1 * pre, s, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v2 * pre, v3 * pre, s, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v4 * pre, v5 * pre, s, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v6 * pre, v7 * pre, s, 3);
+  const uint32_t m = r & 0x77777777u;
+  const uint32_t nz = (m | (m >> 1) | (m >> 2)) & 0x11111111u;   // bit 0 of each nibble: magnitude != 0
+  return r & (0x77777777u | (nz << 3));
+}
+
 // MXFP4 encoding of this lane's block of 32 values: the codes (channel j at
-// nibble j % 8 of dword j / 8) and the scale byte e + 127 are returned; with
-// ROUND_TRIP, v is replaced by the decoded values.
-template <bool ROUND_TRIP>
-__device__ __forceinline__ u32x4 mxfp4_block(float (&v)[32], uint32_t& scale_byte) {
+// nibble j % 8 of dword j / 8) are returned, the scale byte e + 127 in
+// scale_byte.
+__device__ __forceinline__ u32x4 mxfp4_block(const float (&v)[32], uint32_t& scale_byte) {
   float am = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
-  // floor(log2 am) = frexp exponent - 1; e <= 125 for any finite float
-  const int e = am > 0.f ? max(__builtin_amdgcn_frexp_expf(am) - 3, -127) : -127;
-  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, a normal float
-  const float sc = __uint_as_float((uint32_t)(127 + max(e, -126)) << 23);
-  u32x4 codes = {0u, 0u, 0u, 0u};
+  const int e = mxfp4_exponent(am);
+  u32x4 codes;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float x = v[i] * inv;   // exact: a power-of-two scaling
-    const uint32_t m = e2m1_mag(fabsf(x));
-    const uint32_t c = m | (x < 0.f && m ? 8u : 0u);
-    codes[i >> 3] |= c << (4 * (i & 7));
-    if constexpr (ROUND_TRIP) {
-      // 2^e: for e = -127 (sc holds 2^-126) the extra halving is exact
-      const float mag = e2m1_value(m) * sc * (e == -127 ? 0.5f : 1.f);
-      v[i] = x < 0.f ? -mag : mag;
-    }
-  }
+  for (int q = 0; q < 4; ++q)
+    codes[q] = fp4_codes8(v[8 * q], v[8 * q + 1], v[8 * q + 2], v[8 * q + 3], v[8 * q + 4], v[8 * q + 5],
+                          v[8 * q + 6], v[8 * q + 7], e);
   scale_byte = (uint32_t)(e + 127);
   return codes;
 }
@@ -119,27 +132,43 @@ __device__ __forceinline__ f32x4 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32_
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
-// One RoPE pair (a, b) rotated by the angle with cosine c and sine s, written
-// with explicit fmas so that every kernel rotating an indexer query rounds
-// alike (the decode step's scan and its selection block must derive the same
-// fp4 query).
+// Decoded values of 8 stored codes (channel i at nibble i) of a block with
+// E8M0 scale byte sb.
+__device__ __forceinline__ void fp4_decode8(uint32_t codes, uint32_t sb, float (&v)[8]) {
+  const int e = (int)(sb & 255u) - 127;
+  const float sc = __uint_as_float((uint32_t)(127 + min(max(e, -126), 127)) << 23) * (e == -127 ? 0.5f : 1.f);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = (codes >> (4 * i)) & 15u;
+    const float mag = e2m1_value(c & 7u) * sc;
+    v[i] = (c & 8u) ? -mag : mag;
+  }
+}
+
+// One RoPE pair (a, b) rotated by the angle with cosine c and sine s, with
+// explicit fmas (the rounding does not depend on the compiler's contraction
+// choices).
 __device__ __forceinline__ float2 rope_pair(float a, float b, float c, float s) {
   return make_float2(fmaf(a, c, -(b * s)), fmaf(a, s, b * c));
 }
 
-// Tail RoPE of this lane's block of an indexer vector (channels 32 g .. +31;
-// the tail is channels DI - n_rot .. DI - 1, pair j = channels dn + 2 j,
-// dn + 2 j + 1), with cos / sin of pair j at cs[j], sn[j].
-__device__ __forceinline__ void rope_block32(float (&v)[32], int g, int dn, const float* cs, const float* sn) {
+// RoPE of this lane's block of an indexer vector (channels 32 g .. 32 g + 31,
+// pairs 16 g .. 16 g + 15 of the 128 channels), cos / sin of its pairs at
+// cs[0..15], sn[0..15] (16-byte aligned): every pair is rotated, the pairs
+// before the tail with cos 1, sin 0, which leaves them exactly as they are.
+__device__ __forceinline__ void rope_block32(float (&v)[32], const float* cs, const float* sn) {
+  float c[16], s[16];
 #pragma unroll
-  for (int i = 0; i < 32; i += 2) {
-    const int c = 32 * g + i;
-    if (c >= dn) {
-      const int j = (c - dn) >> 1;
-      const float2 r = rope_pair(v[i], v[i + 1], cs[j], sn[j]);
-      v[i] = r.x;
-      v[i + 1] = r.y;
-    }
+  for (int q = 0; q < 4; ++q) {
+    const float4 a = *(const float4*)(cs + 4 * q), b = *(const float4*)(sn + 4 * q);
+    c[4 * q] = a.x; c[4 * q + 1] = a.y; c[4 * q + 2] = a.z; c[4 * q + 3] = a.w;
+    s[4 * q] = b.x; s[4 * q + 1] = b.y; s[4 * q + 2] = b.z; s[4 * q + 3] = b.w;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float2 r = rope_pair(v[2 * j], v[2 * j + 1], c[j], s[j]);
+    v[2 * j] = r.x;
+    v[2 * j + 1] = r.y;
   }
 }
 
@@ -159,6 +188,7 @@ __device__ __forceinline__ float xor16(float v) {
   else return dpp_f32<0x128>(0.f, v);                                         // row_ror:8
 }
 
+// butterfly on lane bit M: the bit-clear lane keeps a + b, the other a - b
 template <int M>
 __device__ __forceinline__ void bfly16(float (&v)[8], bool hi) {
 #pragma unroll
@@ -190,31 +220,16 @@ __device__ __forceinline__ void fwht128_x8(float (&v)[8]) {
 }
 
 // MXFP4 of the block of 4 lanes (s / 4): this lane's 8 codes (channel 8 s + i
-// at nibble i) are returned, the block's scale byte in scale_byte; with
-// ROUND_TRIP v receives the decoded values.
-template <bool ROUND_TRIP>
-__device__ __forceinline__ uint32_t mxfp4_x8(float (&v)[8], uint32_t& scale_byte) {
+// at nibble i) are returned, the block's scale byte in scale_byte.
+__device__ __forceinline__ uint32_t mxfp4_x8(const float (&v)[8], uint32_t& scale_byte) {
   float am = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
   am = fmaxf(am, xor16<1>(am));
   am = fmaxf(am, xor16<2>(am));
-  const int e = am > 0.f ? max(__builtin_amdgcn_frexp_expf(am) - 3, -127) : -127;
-  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
-  const float sc = __uint_as_float((uint32_t)(127 + max(e, -126)) << 23);
-  uint32_t codes = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float x = v[i] * inv;
-    const uint32_t m = e2m1_mag(fabsf(x));
-    codes |= (m | (x < 0.f && m ? 8u : 0u)) << (4 * i);
-    if constexpr (ROUND_TRIP) {
-      const float mag = e2m1_value(m) * sc * (e == -127 ? 0.5f : 1.f);
-      v[i] = x < 0.f ? -mag : mag;
-    }
-  }
+  const int e = mxfp4_exponent(am);
   scale_byte = (uint32_t)(e + 127);
-  return codes;
+  return fp4_codes8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], e);
 }
 
 // Encode one indexer row held in LDS (z[0..127], after its RoPE) and store
@@ -227,7 +242,8 @@ __device__ __forceinline__ void fp4_store_row(const float* z, uint8_t* dst, floa
   float v[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
   fwht128_x8(v);
   uint32_t sb;
-  const uint32_t codes = mxfp4_x8<true>(v, sb);
+  const uint32_t codes = mxfp4_x8(v, sb);
+  if (rt) fp4_decode8(codes, sb, v);
   if (lane < 16) {
     *(uint32_t*)(dst + 4 * s) = codes;
     if ((s & 3) == 0) dst[64 + (s >> 2)] = (uint8_t)sb;

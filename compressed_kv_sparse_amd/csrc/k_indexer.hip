@@ -87,6 +87,11 @@ constexpr int kScoreGroups = 4;
 // from the start.  (Measured step scan: 34.4 us; 37.1 us with 4 groups, where
 // the projection blocks wait for scan blocks to finish; 37.4 us with 6.)
 constexpr int kStepGroups = 5;
+// fp4 rows: groups per block of the score kernel and of the step scan, and
+// groups in flight per wave
+constexpr int kFp4Groups = 4;
+constexpr int kFp4StepGroups = 5;
+constexpr int kFp4Bufs = 8;
 constexpr bool kStepProjLast = true;
 constexpr int kStepProjSF = 16;
 constexpr int kScoreBufs = 2;
@@ -268,21 +273,19 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
 // codes and scales in LDS in MFMA operand order; every wave then reads the
 // MT tiles back.  The query's loads go out before the rows', so waiting for
 // them does not wait for the rows (loads complete in order).
-constexpr int kFp4Bufs = 4;
 
 template <int MT, bool HIST, int NG = kScoreGroups>
 __device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const uint8_t* idx,
                                                     const void* __restrict__ qI, const float* __restrict__ wt,
                                                     const int32_t* __restrict__ pos, int seq_fixed, int pos0,
                                                     uint32_t* __restrict__ keys, uint32_t* __restrict__ hist, int bx,
-                                                    int qn, bool old_only) {
+                                                    int qn, bool old_only, uint8_t* __restrict__ qout) {
   constexpr int HP = MT * 16;
   constexpr int RB = 256 * NG;
-  constexpr int BUFS = kFp4Bufs;
   __shared__ __attribute__((aligned(16))) u32x4 qc[MT * 64];
   __shared__ uint32_t qs[MT * 64];
-  __shared__ float wsh[HP];
-  __shared__ float cs_[32], sn_[32];
+  __shared__ float wsh[256];
+  __shared__ __attribute__((aligned(16))) float cs_[64], sn_[64];   // per channel pair; 1, 0 before the tail
   __shared__ uint32_t lh[kHistBins];
   IdxQuery Q = idx_query(P, pos, seq_fixed, pos0, qn);
   if (old_only && Q.p >= 0 && (Q.p + 1) % 4 == 0 && (Q.p + 1) / 4 <= P.cap) Q.V -= 1;
@@ -304,6 +307,9 @@ __device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const 
     for (int k = 0; k < 4; ++k) qraw[k] = *(const u32x4*)(qp + 8 * k);
   }
   const float wl = wt[(size_t)qn * HI + min(tid, HI - 1)];
+  // (the query and head weights stay ahead of the rows in the load queue:
+  // waiting for them then does not wait for the rows)
+  asm volatile("" ::: "memory");
 
   auto load = [&](u32x4(&Bc)[4], uint32_t(&Bs)[4], int gi) {
 #pragma unroll
@@ -314,14 +320,22 @@ __device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const 
       Bs[t] = *(const uint32_t*)(rp + 64);
     }
   };
+  // the first BUFS groups' loads go out before the prologue (20 registers a
+  // group); each later group is issued into the buffer the scores just freed
+  constexpr int BUFS = NG < kFp4Bufs ? NG : kFp4Bufs;
   u32x4 Bc[BUFS][4];
   uint32_t Bs[BUFS][4];
-  constexpr int kAhead = BUFS > 1 ? BUFS - 1 : 1;
 #pragma unroll
-  for (int b = 0; b < kAhead && b < NG; ++b) load(Bc[b % BUFS], Bs[b % BUFS], b);
+  for (int b = 0; b < BUFS; ++b) load(Bc[b], Bs[b], b);
 
-  if (tid < P.idx_rot / 2) rope_cs_c(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
-  if (tid < HP) wsh[tid] = tid < HI ? wl : 0.f;
+  if (tid < 64) {   // pair tid of the 128 channels: the tail's pairs rotate, the others keep (1, 0)
+    const int j = tid - (64 - P.idx_rot / 2);
+    float c = 1.f, sn = 0.f;
+    if (j >= 0) rope_cs_theta(theta_c_sel(P, j), (double)Q.p, &c, &sn);
+    cs_[tid] = c;
+    sn_[tid] = sn;
+  }
+  wsh[tid] = tid < HI ? wl : 0.f;   // (unconditional: the load stays where it is issued)
   if constexpr (HIST)
     for (int e = tid; e < kHistBins; e += 256) lh[e] = 0;
   lds_barrier();   // cs_, sn_, wsh, lh
@@ -332,10 +346,10 @@ __device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const 
       v[i] = bf16_to_f32((qraw[i >> 3][(i >> 1) & 3] >> (16 * (i & 1))) & 0xffffu);
       if (qh >= HI) v[i] = 0.f;
     }
-    rope_block32(v, g, 128 - P.idx_rot, cs_, sn_);
+    rope_block32(v, cs_ + 16 * g, sn_ + 16 * g);
     fwht128(v);
     uint32_t sb;
-    const u32x4 codes = mxfp4_block<false>(v, sb);
+    const u32x4 codes = mxfp4_block(v, sb);
     if (wave < MT) {
       qc[wave * 64 + lane] = codes;
       qs[wave * 64 + lane] = sb;
@@ -375,8 +389,7 @@ __device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const 
     *(row < P.cap ? kout + row : g_key_sink + lane) = key;
     if constexpr (HIST) atomicAdd(&lh[key >> 20], row < Q.V ? 1u : 0u);
   };
-  // keeps each group's loads above the previous group's multiplies (as in
-  // the bf16 block)
+  // keeps the loads above the multiplies (as in the bf16 block)
   auto pin = [&](u32x4(&Bc)[4], uint32_t(&Bs)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -386,9 +399,21 @@ __device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const 
   };
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    if (gi + kAhead < NG) load(Bc[(gi + kAhead) % BUFS], Bs[(gi + kAhead) % BUFS], gi + kAhead);
     pin(Bc[gi % BUFS], Bs[gi % BUFS]);
     score(Bc[gi % BUFS], Bs[gi % BUFS], gi);
+    if (gi + BUFS < NG) load(Bc[gi % BUFS], Bs[gi % BUFS], gi + BUFS);
+  }
+  // the query's fp4 form for the selection block (record layout: head h at
+  // qout + 68 (64 qn + h)), by the first row block, after its loads
+  if (qout && bx == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt == wave) {
+        uint8_t* rec = qout + (size_t)(64 * qn + 16 * mt + r) * kFp4RowBytes;
+        *(u32x4_a4*)(rec + 16 * g) = A[mt];
+        rec[64 + g] = (uint8_t)sa[mt];
+      }
+    }
   }
   if constexpr (HIST) {
     lds_barrier();
@@ -401,11 +426,12 @@ __device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const 
 }
 
 template <int MT, bool HIST>
-__global__ __launch_bounds__(256) void k_idx_score_fp4(LayerParams P, const uint8_t* idx, const void* __restrict__ qI,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_idx_score_fp4(LayerParams P, const uint8_t* idx, const void* __restrict__ qI,
                                                        const float* __restrict__ wt, const int32_t* __restrict__ pos,
                                                        int seq_fixed, int pos0, uint32_t* __restrict__ keys,
                                                        uint32_t* __restrict__ hist) {
-  idx_score_block_fp4<MT, HIST>(P, idx, qI, wt, pos, seq_fixed, pos0, keys, hist, blockIdx.x, blockIdx.y, false);
+  idx_score_block_fp4<MT, HIST, kFp4Groups>(P, idx, qI, wt, pos, seq_fixed, pos0, keys, hist, blockIdx.x, blockIdx.y,
+                                            false, nullptr);
 }
 
 template <int MT, int KS, int QF, bool HIST>
@@ -1474,7 +1500,8 @@ template <int MT, int QF, int IDXF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_step_scan(
     LayerParams P, const void* idx, const void* __restrict__ qI, const float* __restrict__ wt,
     const int32_t* __restrict__ pos, uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
-    const uint16_t* __restrict__ X, int M, WCat wc, float* __restrict__ proj, int nproj, int nrb) {
+    const uint16_t* __restrict__ X, int M, WCat wc, float* __restrict__ proj, int nproj, int nrb,
+    uint8_t* __restrict__ qf4) {
   const int nscan = (int)gridDim.x - nproj;
   const int bid = blockIdx.x;
   if (kStepProjLast ? bid >= nscan : bid < nproj) {
@@ -1487,8 +1514,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const int i = kStepProjLast ? bid : bid - nproj;
   if constexpr (IDXF == CKV_FP4)
-    idx_score_block_fp4<MT, true, kStepGroups>(P, (const uint8_t*)idx, qI, wt, pos, 0, 0, keys, hist, i % nrb,
-                                               i / nrb, true);
+    idx_score_block_fp4<MT, true, kFp4StepGroups>(P, (const uint8_t*)idx, qI, wt, pos, 0, 0, keys, hist, i % nrb,
+                                                  i / nrb, true, qf4);
   else
     idx_score_block<MT, 4, QF, true, kStepGroups>(P, (const uint16_t*)idx, qI, wt, pos, 0, 0, keys, hist, i % nrb,
                                                   i / nrb, true);
@@ -1501,6 +1528,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // token closed a row, its indexer score is computed here (the rotated query
 // cast to the indexer format, dotted with the row's stored values, relu,
 // weighted head sum) and joins the keys and the histogram; then the selection.
+// With fp4 indexer rows the scan has already rotated and transformed the
+// query (Hadamard, MXFP4) and left it in S.qf4: the block reads those codes
+// instead of the bf16 query, so both kernels score with the same fp4 query.
 template <int KVF, int IDXF, int ACTF>
 __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, Cache cc, const void* __restrict__ u,
                                                       const int32_t* __restrict__ pos, const float* __restrict__ proj,
@@ -1525,7 +1555,14 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
   // last one) and histogram bins 4 tid .. 4 tid + 3
   uint32_t* gh = S.hist + (size_t)qn * kHistBins;
   const int hh = tid >> 4, c0 = (tid & 15) * CPT;
-  const u32x4 q4 = *(const u32x4*)((const uint16_t*)qI + ((size_t)qn * HI + min(hh, HI - 1)) * DI + c0);
+  u32x4 q4;
+  if constexpr (IDXF == CKV_FP4) {
+    // the scan's fp4 form of the query: this thread's 8 codes and their block scale
+    const uint8_t* rec = S.qf4 + (size_t)(64 * qn + min(hh, HI - 1)) * kFp4RowBytes;
+    q4 = (u32x4){*(const uint32_t*)(rec + 4 * (tid & 15)), (uint32_t)rec[64 + ((tid & 15) >> 2)], 0u, 0u};
+  } else {
+    q4 = *(const u32x4*)((const uint16_t*)qI + ((size_t)qn * HI + min(hh, HI - 1)) * DI + c0);
+  }
   const u32x4 h4 = *(const u32x4*)(gh + 4 * tid);
   const float wv = wt[(size_t)qn * HI + min(hh, HI - 1)];
   // the compressor; the keys are issued after its own loads, so its waits
@@ -1553,34 +1590,18 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
   if (st == 1 && V == (Q.p + 1) / 4) {
     // score of row V - 1: query tail rotated at p, cast to the indexer
     // format, dotted with the row's stored values
-    const int dn = DI - P.idx_rot;
     float dot = 0.f;
     if constexpr (IDXF == CKV_FP4) {
-      // this thread's 8 channels of head hh: RoPE, Hadamard and the MXFP4
-      // round trip of the query (bit-identical to the scan's 32-channel
-      // form), dotted with the row's stored values
+      // the query's fp4 values (left by the scan, which rotated and
+      // transformed it) dotted with the row's stored values
       const u32x4 q4s = *(const u32x4*)(q_lds + 4 * tid);
       float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        float a = bf16_to_f32(q4s[i >> 1] & 0xffffu), b2 = bf16_to_f32(q4s[i >> 1] >> 16);
-        const int c = c0 + i;
-        if (c >= dn) {
-          const int j = (c - dn) >> 1;
-          const float2 r = rope_pair(a, b2, rtab[128 + j], rtab[160 + j]);
-          a = r.x;
-          b2 = r.y;
-        }
-        v[i] = a;
-        v[i + 1] = b2;
-      }
-      fwht128_x8(v);
-      uint32_t sb;
-      (void)mxfp4_x8<true>(v, sb);
+      fp4_decode8(q4s[0], q4s[1], v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) dot += v[i] * idx_row[c0 + i];
       dot = row16_sum(dot);
     } else {
+      const int dn = DI - P.idx_rot;
       const u32x4 q4s = *(const u32x4*)(q_lds + 4 * tid);
 #pragma unroll
       for (int i = 0; i < CPT / 2; ++i) {
@@ -1660,14 +1681,14 @@ int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache&
   hipStream_t st = (hipStream_t)stream;
   const WCat wc = make_wcat(P, w);
   const int nproj = (P.ncol / 16) * ((B + 15) / 16) * kProjSlices;
-  constexpr int RB = 256 * kStepGroups;
+  const int RB = 256 * (P.idx_fmt == CKV_FP4 ? kFp4StepGroups : kStepGroups);
   const int nrb = (P.cap + RB - 1) / RB;
   const int MT = (P.HI + 15) / 16;
   dim3 grid(nproj + nrb * B);
   const bool fp4 = P.idx_fmt == CKV_FP4;
 #define CKV_SS(MTV, IF)                                                                                        \
   launch_score((k_step_scan<MTV, CKV_BF16, IF>), grid, dim3(256), st, P, (const void*)c.idx, qI, wt, pos, keys, \
-               sel.hist, (const uint16_t*)x, B, wc, proj, nproj, nrb)
+               sel.hist, (const uint16_t*)x, B, wc, proj, nproj, nrb, sel.qf4)
 #define CKV_SS_MT(IF)      \
   if (MT == 1) CKV_SS(1, IF); \
   else if (MT == 2) CKV_SS(2, IF); \
@@ -1706,7 +1727,7 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
   if (P.idx_fmt == CKV_FP4) {   // validated: D_I 128, H_I <= 64, bf16 queries
     const uint8_t* ix = (const uint8_t*)c.idx;
     const int MT = (P.HI + 15) / 16;
-    constexpr int RB = 256 * kScoreGroups;
+    constexpr int RB = 256 * kFp4Groups;
     dim3 mgrid((unsigned)(vmax > 0 ? (vmax + RB - 1) / RB : 1), nq);
 #define CKV_F4(MTV)                                                                                              \
   if (hist)                                                                                                      \

@@ -106,9 +106,10 @@ def test_fp4_indexer_rows():
     assert L.validate(desc(idx_fmt=4)) == L.CKV_E_UNSUPPORTED
     f32 = dict(kv_fmt=L.CKV_F32, act_fmt=L.CKV_F32, w_fmt=L.CKV_F32)
     assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, idx_fmt=L.CKV_FP4, **f32)) == L.CKV_E_UNSUPPORTED
+    # the decode workspace also holds each query's fp4 form (64 heads x 68 bytes)
     d4, d16 = desc(idx_fmt=L.CKV_FP4), desc()
-    for mode, n in ((L.CKV_MODE_DECODE, 16), (L.CKV_MODE_PREFILL, 4096)):
-        assert L.workspace_bytes(d4, mode, n) == L.workspace_bytes(d16, mode, n)
+    assert L.workspace_bytes(d4, L.CKV_MODE_DECODE, 16) == L.workspace_bytes(d16, L.CKV_MODE_DECODE, 16) + 16 * 64 * 68
+    assert L.workspace_bytes(d4, L.CKV_MODE_PREFILL, 4096) == L.workspace_bytes(d16, L.CKV_MODE_PREFILL, 4096)
 
 
 def test_row_bytes_and_workspace():
