@@ -85,7 +85,7 @@ __device__ __forceinline__ void rope_cs(const LayerParams& P, int j, double pos,
 __device__ __forceinline__ void rope_cs_c(const LayerParams& P, int j, double pos, float* c, float* s) {
   rope_cs_theta(P.theta_c[j], pos, c, s);
 }
-// theta_c[j] for a lane-dependent j, chosen among the 32 entries read as
+// theta_c[j] (theta[j]) for a lane-dependent j, chosen among the 32 entries read as
 // scalars: indexing the kernel-argument array with a per-lane j compiles to a
 // vector load from the argument segment, which a kernel that has issued its
 // own vector loads first then waits for behind all of them.
@@ -93,6 +93,12 @@ __device__ __forceinline__ double theta_c_sel(const LayerParams& P, int j) {
   double t = 0.0;
 #pragma unroll
   for (int jj = 0; jj < 32; ++jj) t = j == jj ? P.theta_c[jj] : t;
+  return t;
+}
+__device__ __forceinline__ double theta_sel(const LayerParams& P, int j) {
+  double t = 0.0;
+#pragma unroll
+  for (int jj = 0; jj < 32; ++jj) t = j == jj ? P.theta[jj] : t;
   return t;
 }
 // Rotation that takes a vector turned by pos in the raw frame to the same

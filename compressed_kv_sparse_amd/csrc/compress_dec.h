@@ -657,6 +657,13 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
     ap[sl] = ape[sl * width];
   }
   const float gm = norm_gamma(P, (roleA ? w.gamma : w.idx_gamma)[col]);
+  // this lane's RoPE frequency for the tables below (wave 0: the raw frame in
+  // lanes 0-31, the compressed frame in lanes 32-63; wave 1: the compressed
+  // frame): a per-lane index into the kernel-argument arrays is a vector
+  // load, so it is waited for here, before the caller's loads -- waited for
+  // after them, the wait would cover them all
+  double th_lane = wave == 0 && lane < 32 ? P.theta[lane & 31] : P.theta_c[lane & 31];
+  asm volatile("" : "+v"(th_lane));
   asm volatile("" ::: "memory");
   issue();
   asm volatile("" ::: "memory");
@@ -668,18 +675,13 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
   // RoPE tables (wave 0): pair j at p (raw frame) and at the row position
   // 4 i (compressed frame)
   if (wave == 0) {
-    double theta = 0.0;
-#pragma unroll
-    for (int jj = 0; jj < 32; ++jj) theta = (tid & 31) == jj ? (tid < 32 ? P.theta[jj] : P.theta_c[jj]) : theta;
     float cs, sn;
-    rope_cs_theta(theta, tid < 32 ? (double)p : (double)(4 * i), &cs, &sn);
-    if (tid < 64) {
-      rtab[tid] = cs;
-      rtab[64 + tid] = sn;
-    }
+    rope_cs_theta(th_lane, tid < 32 ? (double)p : (double)(4 * i), &cs, &sn);
+    rtab[tid] = cs;
+    rtab[64 + tid] = sn;
   } else if (wave == 1 && lane < 32) {   // pair j at p in the compressed frame (the indexer query)
     float cs, sn;
-    rope_cs_c(P, lane, (double)p, &cs, &sn);
+    rope_cs_theta(th_lane, (double)p, &cs, &sn);
     rtab[128 + lane] = cs;
     rtab[160 + lane] = sn;
   }

@@ -113,7 +113,7 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
   constexpr int HP = MT * 16;
   constexpr int RB = 256 * NG;
   __shared__ __attribute__((aligned(16))) uint16_t qh[HP * DI];
-  __shared__ float wsh[HP];
+  __shared__ float wsh[256];
   __shared__ float cs_[32], sn_[32];
   __shared__ uint32_t lh[kHistBins];
   IdxQuery Q = idx_query(P, pos, seq_fixed, pos0, qn);
@@ -126,20 +126,6 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
   const uint16_t* base = idx + (size_t)Q.seq * P.cap * DI;
   const int vlast = Q.V - 1;
 
-  // rows of group gi for this wave -> B operands; rows past V re-read row V-1
-  auto load = [&](u32x4(&Bv)[4][KS], int gi) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int row = min(rb0 + 256 * gi + wave * 64 + 16 * t + r, vlast);
-      const uint16_t* rp = base + (size_t)row * DI + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) Bv[t][ks] = *(const u32x4*)(rp + 32 * ks);
-    }
-  };
-  u32x4 Bq[kScoreBufs][4][KS];
-  constexpr int kAhead = kScoreBufs > 1 ? kScoreBufs - 1 : 1;   // groups issued before the prologue
-#pragma unroll
-  for (int b = 0; b < kAhead && b < NG; ++b) load(Bq[b % kScoreBufs], b);
   // the query: MT chunks of 8 channels per thread (chunk ci = tid + 256 e is
   // head ci / (DI/8), channels 8 (ci % (DI/8)) .. +7); heads past H_I read head
   // H_I - 1 and are zeroed below
@@ -157,12 +143,30 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
     }
   }
   const float wl = wt[(size_t)qn * HI + min(tid, HI - 1)];
+  // (the query and head weights stay ahead of the rows in the load queue:
+  // waiting for them then does not wait for the rows)
+  asm volatile("" ::: "memory");
 
-  if (tid < nrot / 2) rope_cs_c(P, tid, (double)Q.p, &cs_[tid], &sn_[tid]);
-  if (tid < HP) wsh[tid] = tid < HI ? wl : 0.f;
+  // rows of group gi for this wave -> B operands; rows past V re-read row V-1
+  auto load = [&](u32x4(&Bv)[4][KS], int gi) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = min(rb0 + 256 * gi + wave * 64 + 16 * t + r, vlast);
+      const uint16_t* rp = base + (size_t)row * DI + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) Bv[t][ks] = *(const u32x4*)(rp + 32 * ks);
+    }
+  };
+  u32x4 Bq[kScoreBufs][4][KS];
+  constexpr int kAhead = kScoreBufs > 1 ? kScoreBufs - 1 : 1;   // groups issued before the prologue
+#pragma unroll
+  for (int b = 0; b < kAhead && b < NG; ++b) load(Bq[b % kScoreBufs], b);
+
+  if (tid < nrot / 2) rope_cs_theta(theta_c_sel(P, tid), (double)Q.p, &cs_[tid], &sn_[tid]);
+  wsh[tid] = tid < HI ? wl : 0.f;   // (unconditional: the load stays where it is issued)
   if constexpr (HIST)
     for (int e = tid; e < kHistBins; e += 256) lh[e] = 0;
-  __syncthreads();
+  lds_barrier();   // cs_, sn_, wsh, lh (no wait for the rows in flight)
   // rotated query -> bf16 in LDS
 #pragma unroll
   for (int e = 0; e < MT; ++e) {
@@ -189,7 +193,7 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
     }
     *(u32x4*)&qh[h * DI + c] = packed;
   }
-  __syncthreads();
+  lds_barrier();   // qh
 
   u32x4 A[MT][KS];
   float wv[MT][4];
