@@ -1324,6 +1324,51 @@ __device__ __forceinline__ void sel_load_keys(const uint32_t* kq, int cap, int t
   for (int e = 0; e < kSelKPT; ++e) kr[e] = kq[min(t + 1024 * e, cap - 1)];
 }
 
+// One wave: in the LDS histogram h[0..64 PER) (lane l owns bins PER l ..
+// PER l + PER - 1, PER 1 or a multiple of 4), the bin where the count of
+// keys in higher bins first reaches need (1 <= need <= the total): returns
+// the bin; *above = the count in higher bins, *cnt = the count in the bin.
+// Every lane of the wave receives the results; no block barrier.
+template <int PER>
+__device__ __forceinline__ uint32_t wave_find_from_top(const uint32_t* h, uint32_t need, uint32_t* above,
+                                                       uint32_t* cnt) {
+  const int lane = threadIdx.x & 63;
+  uint32_t v[PER];
+  if constexpr (PER == 1) {
+    v[0] = h[lane];
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+      const u32x4 t = *(const u32x4*)(h + PER * lane + i);
+      v[i] = t[0];
+      v[i + 1] = t[1];
+      v[i + 2] = t[2];
+      v[i + 3] = t[3];
+    }
+  }
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) local += v[i];
+  const uint32_t incl = wave_incl_scan(local);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  const uint32_t abv = total - incl;   // bins of higher lanes
+  const bool mine = abv < need && abv + local >= need;
+  const int owner = (int)__builtin_ctzll(__ballot(mine));
+  uint32_t bin = 0, ab = 0, c = 0, cum = abv;
+#pragma unroll
+  for (int i = PER - 1; i >= 0; --i) {
+    if (cum < need && cum + v[i] >= need) {
+      bin = (uint32_t)(PER * lane + i);
+      ab = cum;
+      c = v[i];
+    }
+    cum += v[i];
+  }
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)ab, owner);
+  *cnt = (uint32_t)__builtin_amdgcn_readlane((int)c, owner);
+  return (uint32_t)__builtin_amdgcn_readlane((int)bin, owner);
+}
+
 // The selection itself, from keys kr (row tid + 1024 e) and histogram bins
 // hv (bins 4 tid .. 4 tid + 3) held by the 1024 threads of the block, V > k.
 //   1. b1 = the 12-bit key bin holding the k-th largest key (histogram scan);
@@ -1343,7 +1388,8 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
   constexpr int KPT = kSelKPT;
   __shared__ uint32_t gtw[1024];   // rows with key > T
   __shared__ uint32_t eqw[1024];   // rows with key == T
-  __shared__ uint32_t sh[kHistBins], sh2[256];
+  __shared__ uint32_t sh[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hl0[256], hl1[256], hl2[64];   // candidate radix levels
   __shared__ uint32_t ck[kCandCap], ci[kCandCap];
   __shared__ __attribute__((aligned(16))) uint32_t wsum[16];
   __shared__ uint32_t res[4];
@@ -1355,61 +1401,66 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
     res[0] = 0;
     res[1] = 0;
     res[2] = 0;
+    res[3] = 0;
   }
   find_from_top<4, 16>(hv, (uint32_t)k, wsum, res);   // ends with a barrier
   const uint32_t b1 = res[0], A = res[1], nb1 = res[2];
-  uint32_t T, need_eq;
+  uint32_t T, need_eq, n_eq = 0u;
   if (nb1 <= (uint32_t)kCandCap) {
-    // candidates: per-thread counts, their block scan, then each thread
-    // appends its own at its offset
+    // candidates: the keys of bin b1, appended at offsets from a wave scan of
+    // the per-thread counts and one LDS atomic per wave (their order does not
+    // matter: each carries its row)
+    if (tid < 256) hl0[tid] = 0u;
+    else if (tid < 512) hl1[tid - 256] = 0u;
+    else if (tid < 576) hl2[tid - 512] = 0u;
     uint32_t cnt = 0;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) cnt += (e < nv && (kr[e] >> 20) == b1) ? 1u : 0u;
+    {
+      const uint32_t incl = wave_incl_scan(cnt);
+      const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      uint32_t wbase = 0u;
+      if (lane == 0 && wtot) wbase = atomicAdd(&res[3], wtot);
+      uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 0) + incl - cnt;
 #pragma unroll
-    for (int i = 0; i < kHistBins / 1024; ++i) sh[tid + 1024 * i] = 0u;
-    if (tid < 256) sh2[tid] = 0u;
-    uint32_t ctot;
-    uint32_t at = block_exscan<16>(cnt, wsum, &ctot);
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-      if (e < nv && (kr[e] >> 20) == b1) {
-        if (at < (uint32_t)kCandCap) {
-          ck[at] = kr[e];
-          ci[at] = (uint32_t)(tid + 1024 * e);
+      for (int e = 0; e < KPT; ++e) {
+        if (e < nv && (kr[e] >> 20) == b1) {
+          if (at < (uint32_t)kCandCap) {
+            ck[at] = kr[e];
+            ci[at] = (uint32_t)(tid + 1024 * e);
+          }
+          ++at;
         }
-        ++at;
       }
     }
-    if (tid == 0) {
-      res[0] = 0;
-      res[1] = 0;
+    lds_barrier();
+    // wave 0 resolves the k-th key among them with three radix levels of
+    // the candidates' low 20 bits (8, 8 and 4 bits), no block barrier
+    if (wave == 0) {
+      const int nc = (int)min(nb1, (uint32_t)kCandCap);
+      uint32_t need = (uint32_t)k - A, ab, cn;
+      for (int c = lane; c < nc; c += 64) atomicAdd(&hl0[(ck[c] >> 12) & 255u], 1u);
+      const uint32_t d0 = wave_find_from_top<4>(hl0, need, &ab, &cn);
+      need -= ab;
+      const uint32_t p0 = (b1 << 20) | (d0 << 12);
+      for (int c = lane; c < nc; c += 64)
+        if ((ck[c] & 0xfffff000u) == p0) atomicAdd(&hl1[(ck[c] >> 4) & 255u], 1u);
+      const uint32_t d1 = wave_find_from_top<4>(hl1, need, &ab, &cn);
+      need -= ab;
+      const uint32_t p1 = p0 | (d1 << 4);
+      for (int c = lane; c < nc; c += 64)
+        if ((ck[c] & 0xfffffff0u) == p1) atomicAdd(&hl2[ck[c] & 15u], 1u);
+      const uint32_t d2 = wave_find_from_top<1>(hl2, need, &ab, &cn);
+      if (lane == 0) {
+        res[0] = p1 | d2;
+        res[1] = need - ab;   // keys equal to T taken
+        res[2] = cn;          // keys equal to T
+      }
     }
     lds_barrier();
-    const int nc = (int)min(nb1, (uint32_t)kCandCap);
-    uint32_t need = (uint32_t)k - A;
-    // level 0: key bits 8..19 of the candidates
-    for (int c = tid; c < nc; c += 1024) atomicAdd(&sh[(ck[c] >> 8) & 4095u], 1u);
-    lds_barrier();
-    uint32_t v[4];
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) v[i2] = sh[4 * tid + i2];
-    find_from_top<4, 16>(v, need, wsum, res);
-    const uint32_t prefix = (b1 << 20) | (res[0] << 8);
-    need -= res[1];
-    lds_barrier();   // every thread has read res
-    if (tid == 0) {
-      res[0] = 0;
-      res[1] = 0;
-    }
-    // level 1: bits 0..7 of the candidates that share bits 8..31
-    for (int c = tid; c < nc; c += 1024)
-      if ((ck[c] & 0xffffff00u) == prefix) atomicAdd(&sh2[ck[c] & 255u], 1u);
-    lds_barrier();
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) v[i2] = 4 * tid + i2 < 256 ? sh2[4 * tid + i2] : 0u;
-    find_from_top<4, 16>(v, need, wsum, res);
-    T = prefix | res[0];
-    need_eq = need - res[1];
+    T = res[0];
+    need_eq = res[1];
+    n_eq = res[2];
   } else {
     // heavily tied scores: radix select over all keys (d = M - key)
     uint32_t mloc = 0;
@@ -1429,22 +1480,32 @@ __device__ __forceinline__ void topk_decode_select(const LayerParams& P, int V, 
     };
     T = radix_select(M, (uint32_t)k, count_level, sh, wsum, res, &need_eq);
   }
-  // bitmaps of key > T and key == T: lanes 0 and 1 write the low and high
-  // words of each ballot
+  // bitmaps of key > T (gtw) and key == T (eqw); when every key equal to T
+  // is taken (no tie at the k-th place) one bitmap of key >= T (gtw) does.
+  // Lanes 0 and 1 write the low and high words of each ballot.
+  const bool all_eq = n_eq == need_eq;
+  if (all_eq) {
 #pragma unroll
-  for (int e = 0; e < KPT; ++e) {
-    const unsigned long long bg = __ballot(e < nv && kr[e] > T), be = __ballot(e < nv && kr[e] == T);
-    if (lane < 2) {
-      const int wd = 32 * e + 2 * wave + lane;
-      gtw[wd] = (uint32_t)(lane ? bg >> 32 : bg);
-      eqw[wd] = (uint32_t)(lane ? be >> 32 : be);
+    for (int e = 0; e < KPT; ++e) {
+      const unsigned long long bg = __ballot(e < nv && kr[e] >= T);
+      if (lane < 2) gtw[32 * e + 2 * wave + lane] = (uint32_t)(lane ? bg >> 32 : bg);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+      const unsigned long long bg = __ballot(e < nv && kr[e] > T), be = __ballot(e < nv && kr[e] == T);
+      if (lane < 2) {
+        const int wd = 32 * e + 2 * wave + lane;
+        gtw[wd] = (uint32_t)(lane ? bg >> 32 : bg);
+        eqw[wd] = (uint32_t)(lane ? be >> 32 : be);
+      }
     }
   }
   lds_barrier();
   // word tid covers rows 32 tid .. 32 tid + 31: its slot from the counts of
   // the words before it (key > T in the high half, key == T in the low half)
   {
-    const uint32_t g = gtw[tid], q = eqw[tid];
+    const uint32_t g = gtw[tid], q = all_eq ? 0u : eqw[tid];
     uint32_t tot;
     const uint32_t before = block_exscan<16>(((uint32_t)__popc(g) << 16) | (uint32_t)__popc(q), wsum, &tot);
     const uint32_t gt_before = before >> 16, eq_before = before & 0xffffu;
