@@ -584,8 +584,9 @@ def main():
         torch.cuda.synchronize()
         del a, b
     if args.part == "prefill":
-        p = bench_prefill(get_config("c4"), args.prefill_steps, 1)
-        print(json.dumps({"part": "prefill", "workload": get_config("c4").name,
+        pcfg = get_config(args.workload if args.workload.startswith("c4") else "c4")
+        p = bench_prefill(pcfg, args.prefill_steps, 1)
+        print(json.dumps({"part": "prefill", "workload": pcfg.name,
                           **{k: round(v, 4) for k, v in p.items()}}), flush=True)
         return
     if args.part == "stack":
