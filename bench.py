@@ -440,6 +440,49 @@ def bench_prefill(cfg, steps, warmup):
             "mfma_frac": fl / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS, "flops": fl}
 
 
+# --------------------------------------------------------------------------- Hyper-Connection mixer
+
+def bench_hc(T, D=4096, steps=20, copies=3):
+    """The Hyper-Connection mixer around the attention block (split + Sinkhorn +
+    pre mix, then the post mix) for T tokens of hidden D, bf16 streams; copies
+    of the buffers taken in turn (the T = 4096 streams, 134 MB a copy, then come
+    from HBM).  Algorithmic bytes: pre reads the mixer row and four streams and
+    writes the block input and the split; post reads the split, four streams and
+    the block output and writes four streams."""
+    import torch
+    from compressed_kv_sparse_amd import HCMixer
+    g = torch.Generator(device="cuda")
+    g.manual_seed(T)
+    m = HCMixer(D, act_fmt="bf16")
+    bufs = []
+    for _ in range(copies):
+        mix = torch.randn((T, 24), generator=g, device="cuda")
+        h = torch.randn((T, 4, D), generator=g, device="cuda").to(torch.bfloat16)
+        y = torch.randn((T, D), generator=g, device="cuda").to(torch.bfloat16)
+        x = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+        coef = torch.empty((T, 24), dtype=torch.float32, device="cuda")
+        out = torch.empty_like(h)
+        bufs.append((mix, h, y, x, coef, out))
+
+    def run(b):
+        mix, h, y, x, coef, out = b
+        m.pre(mix, h, x=x, coef=coef)
+        m.post(coef, h, y, out=out)
+
+    for i in range(3):
+        run(bufs[i % copies])
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        run(bufs[i % copies])
+        b.record()
+    torch.cuda.synchronize()
+    dt = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e-3
+    nbytes = T * (96 + 8 * D + 2 * D + 96) + T * (96 + 8 * D + 2 * D + 8 * D)
+    return {"T": T, "hidden": D, "us": round(dt * 1e6, 2), "bytes": nbytes,
+            "gbs": round(nbytes / dt / 1e9, 1), "hbm_frac": round(nbytes / dt / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 # --------------------------------------------------------------------------- CPU oracle
 
 def cpu_baseline(cfg, inp, wts, budget_s=12.0):
@@ -551,7 +594,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-stack", action="store_true")
-    ap.add_argument("--part", choices=("all", "decode", "prefill", "stack"), default="all",
+    ap.add_argument("--part", choices=("all", "decode", "prefill", "stack", "hc"), default="all",
                     help="time one part alone and print its own JSON line (for kernel profiles)")
     ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the other decode workloads")
@@ -589,6 +632,10 @@ def main():
         print(json.dumps({"part": "prefill", "workload": pcfg.name,
                           **{k: round(v, 4) for k, v in p.items()}}), flush=True)
         return
+    if args.part == "hc":
+        for T in (16, 4096):
+            print(json.dumps({"part": "hc", **bench_hc(T)}), flush=True)
+        return
     if args.part == "stack":
         print(json.dumps({"part": "stack", **bench_stack(args.stack_steps, 3)}), flush=True)
         return
@@ -622,6 +669,11 @@ def main():
             log(f"[bench] decode {name}: {e['ms_per_step'] * 1e3:.1f} us/step, {e['tok_s']:.0f} tok/s, "
                 f"{100 * e['step_hbm_frac']:.1f}% HBM")
             del e
+    if not args.no_extra:   # the Hyper-Connection mixer around the block (decode and prefill token counts)
+        for T in (16, 4096):
+            e = bench_hc(T)
+            extra[f"hc_T{T}"] = {k: v for k, v in e.items() if k in ("us", "gbs", "hbm_frac")}
+            log(f"[bench] hc mixer T={T}: {e['us']:.1f} us, {e['gbs']:.0f} GB/s ({100 * e['hbm_frac']:.1f}% of HBM)")
     sweep = None
     if not args.no_sweep:
         sweep = bench_sweep(args.steps, args.warmup, copies=args.layer_copies)

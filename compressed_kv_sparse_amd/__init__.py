@@ -10,4 +10,5 @@ from ._lib import (  # noqa: F401
     indexer_topk_decode, indexer_topk_prefill, row_bytes, sparse_swa_attn_decode, sparse_swa_attn_prefill,
     strerror, validate, workspace_bytes,
 )
+from .hc import HCMixer  # noqa: F401
 from .layer import DeviceLayer  # noqa: F401

@@ -61,6 +61,11 @@ class LayerCache(ctypes.Structure):
     ]
 
 
+class HcDesc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_hc", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("act_fmt", ctypes.c_int32)]
+
+
 class CkvError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -107,6 +112,9 @@ def _load() -> ctypes.CDLL:
         "ckv_sparse_swa_attn_prefill": [D, C, VP, I32, I32, I32, VP, VP, VP, SZ, VP],
         "ckv_decode_step": [D, Wt, C, VP, VP, VP, VP, VP, VP, I32, VP, VP, VP, SZ, VP],
         "ckv_decode_step_static": [D, Wt, C, VP, VP, VP, VP, VP, VP, I32, VP, VP, VP],
+        "ckv_hc_validate": [P(HcDesc)],
+        "ckv_hc_pre": [P(HcDesc), VP, VP, I32, VP, VP, VP],
+        "ckv_hc_post": [P(HcDesc), VP, VP, VP, I32, VP, VP],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -121,7 +129,8 @@ EXPORTS = ("ckv_row_bytes", "ckv_idx_row_bytes", "ckv_validate", "ckv_strerror",
            "ckv_workspace_sync_bytes",
            "ckv_compress_append_decode", "ckv_compress_append_prefill", "ckv_indexer_topk_decode",
            "ckv_indexer_topk_prefill", "ckv_indexer_score_decode", "ckv_sparse_swa_attn_decode",
-           "ckv_sparse_swa_attn_prefill", "ckv_decode_step", "ckv_time_next_score", "ckv_decode_step_static")
+           "ckv_sparse_swa_attn_prefill", "ckv_decode_step", "ckv_time_next_score", "ckv_decode_step_static",
+           "ckv_hc_validate", "ckv_hc_pre", "ckv_hc_post")
 
 
 def strerror(code: int) -> str:
@@ -215,3 +224,15 @@ def decode_step(desc, weights, cache, x, u, q, qI, w, pos, B, topk, out, ws, ws_
 def decode_step_static(desc, weights, cache, x, u, q, qI, w, pos, B, topk, out, stream=None) -> int:
     return lib.ckv_decode_step_static(_ref(desc), _ref(weights), _ref(cache), _p(x), _p(u), _p(q), _p(qI), _p(w),
                                       _p(pos), int(B), _p(topk), _p(out), stream)
+
+
+def hc_validate(desc: HcDesc) -> int:
+    return int(lib.ckv_hc_validate(ctypes.byref(desc)))
+
+
+def hc_pre(desc: HcDesc, mix: int, h: int, T: int, x: int, coef: int, stream) -> int:
+    return int(lib.ckv_hc_pre(ctypes.byref(desc), mix, h, T, x, coef, stream))
+
+
+def hc_post(desc: HcDesc, coef: int, h: int, y: int, T: int, h_out: int, stream) -> int:
+    return int(lib.ckv_hc_post(ctypes.byref(desc), coef, h, y, T, h_out, stream))

@@ -309,3 +309,42 @@ extern "C" int ckv_time_next_score(void* start_event, void* stop_event) {
 extern "C" const char* ckv_last_hip_error(void) {
   return t_last_hip ? hipGetErrorName((hipError_t)t_last_hip) : "none";
 }
+
+// ---- Hyper-Connection mixer -------------------------------------------------
+
+static HcParams hc_params(const ckv_hc_desc* d) {
+  HcParams Hp;
+  Hp.hidden = d->hidden;
+  Hp.iters = d->sinkhorn_iters;
+  Hp.eps = d->eps;
+  Hp.act_fmt = d->act_fmt;
+  return Hp;
+}
+
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+extern "C" int ckv_hc_pre(const ckv_hc_desc* d, const float* mix, const void* h, int32_t T, void* x, float* coef,
+                          void* stream) {
+  int rc = ckv_hc_validate(d);
+  if (rc) return rc;
+  if (T < 1 || check_ptr(mix) || check_ptr(h) || check_ptr(x) || check_ptr(coef)) return CKV_E_INVAL;
+  const size_t es = d->act_fmt == CKV_F32 ? 4 : 2;
+  if (overlap(x, (size_t)T * d->hidden * es, h, (size_t)T * 4 * d->hidden * es)) return CKV_E_INVAL;
+  clear_stale();
+  return launched(launch_hc_pre(hc_params(d), mix, h, T, x, coef, stream));
+}
+
+extern "C" int ckv_hc_post(const ckv_hc_desc* d, const float* coef, const void* h, const void* y, int32_t T,
+                           void* h_out, void* stream) {
+  int rc = ckv_hc_validate(d);
+  if (rc) return rc;
+  if (T < 1 || check_ptr(coef) || check_ptr(h) || check_ptr(y) || check_ptr(h_out)) return CKV_E_INVAL;
+  const size_t es = d->act_fmt == CKV_F32 ? 4 : 2;
+  const size_t nh = (size_t)T * 4 * d->hidden * es;
+  if (overlap(h_out, nh, h, nh) || overlap(h_out, nh, y, (size_t)T * d->hidden * es)) return CKV_E_INVAL;
+  clear_stale();
+  return launched(launch_hc_post(hc_params(d), coef, h, y, T, h_out, stream));
+}

@@ -94,6 +94,12 @@ struct WsLayout {
   int attn_rows_per_split;
 };
 
+// Hyper-Connection mixer parameters (validated ckv_hc_desc)
+struct HcParams {
+  int hidden, iters, act_fmt;
+  float eps;
+};
+
 bool make_params(const ckv_layer_desc* desc, LayerParams* P);
 WsLayout ws_layout(const LayerParams& P, int mode, int n);
 int attn_max_rows(const LayerParams& P);
@@ -139,6 +145,10 @@ int decode_step_checks(const ckv_layer_desc* desc, const ckv_layer_weights* w, c
                        const void* x, const void* u, const void* q, const void* qI, const float* iw,
                        const int32_t* pos, int32_t B, int32_t* topk, void* out, void* ws, size_t ws_bytes,
                        LayerParams* P, WsLayout* L);
+// Hyper-Connection mixer: split + Sinkhorn + pre mix, and the post mix
+int launch_hc_pre(const HcParams& Hp, const float* mix, const void* h, int T, void* x, float* coef, void* stream);
+int launch_hc_post(const HcParams& Hp, const float* coef, const void* h, const void* y, int T, void* hout,
+                   void* stream);
 int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache& c, const void* x,
                             const void* u, const void* qI, const float* wt, const int32_t* pos, int B,
                             float* proj, uint32_t* keys, const SelWs& sel, int32_t* topk, void* stream);

@@ -221,3 +221,13 @@ extern "C" size_t ckv_workspace_bytes(const ckv_layer_desc* d, int32_t mode, int
   make_params(d, &P);
   return ws_layout(P, mode, n).total;
 }
+
+extern "C" int ckv_hc_validate(const ckv_hc_desc* d) {
+  if (!d) return CKV_E_INVAL;
+  if (d->n_hc != 4) return CKV_E_UNSUPPORTED;
+  if (d->hidden <= 0 || d->hidden % 8 || d->hidden > 65536) return CKV_E_UNSUPPORTED;
+  if (d->sinkhorn_iters < 1 || d->sinkhorn_iters > 100) return CKV_E_UNSUPPORTED;
+  if (!(d->eps >= 0.f) || !(d->eps < 1e30f)) return CKV_E_UNSUPPORTED;
+  if (d->act_fmt != CKV_F32 && d->act_fmt != CKV_BF16) return CKV_E_UNSUPPORTED;
+  return CKV_OK;
+}

@@ -402,6 +402,44 @@ int ckv_decode_step_static(const ckv_layer_desc* desc, const ckv_layer_weights* 
                            const void* x, const void* u, const void* q, const void* qI, const float* iw,
                            const int32_t* pos, int32_t B, int32_t* topk, void* out, void* stream);
 
+/* ---- Hyper-Connection mixer around the attention block [P1 s10] ------------
+ *
+ * The hidden state is carried as n_hc = 4 residual streams h_0..h_3 of
+ * `hidden` channels.  A per-token mixer row of 24 float32 values
+ * m = [pre (4) | post (4) | coupling (16, row-major)] is split into
+ *   pre_i  = sigmoid(m[i]),  post_j = sigmoid(m[4 + j]),
+ *   C      = Sinkhorn(m[8..23]): a softmax along each row, a column
+ *            normalisation, then (sinkhorn_iters - 1) times a row and a column
+ *            normalisation, each dividing by (sum + eps)  (C rows j, columns i);
+ * the block reads x = sum_i pre_i h_i, and after it (output y) the streams
+ * become h'_j = sum_i C[j][i] h_i + post_j y.  The page fixes n_hc, the
+ * iteration count (20 at the Flash shape), the split and the alternating
+ * normalisation with eps; the row layout, the logistic gates and the first
+ * iteration's form are this library's reading.  Arithmetic in float32. */
+typedef struct ckv_hc_desc {
+  int32_t hidden;          /* channels per stream: a multiple of 8, at most 65536 */
+  int32_t n_hc;            /* streams: 4 */
+  int32_t sinkhorn_iters;  /* 1..100 (20 at the Flash shape) */
+  float eps;               /* Sinkhorn eps, >= 0 and finite (1e-6) */
+  int32_t act_fmt;         /* CKV_F32 / CKV_BF16 for h, x, y and h_out */
+} ckv_hc_desc;
+
+/* CKV_OK, CKV_E_INVAL (NULL) or CKV_E_UNSUPPORTED. */
+int ckv_hc_validate(const ckv_hc_desc* desc);
+
+/* Split + Sinkhorn + pre mix of T tokens (T >= 1): mix [T, 24] float32,
+ * h [T, 4, hidden] act_fmt -> x [T, hidden] act_fmt and coef [T, 24] float32
+ * (pre 4, post 4, C 16 row-major), the input of ckv_hc_post.  Every pointer
+ * 16-byte aligned (else CKV_E_INVAL); x must not overlap h. */
+int ckv_hc_pre(const ckv_hc_desc* desc, const float* mix, const void* h, int32_t T, void* x, float* coef,
+               void* stream);
+
+/* Post mix: coef [T, 24] from ckv_hc_pre, h [T, 4, hidden], y [T, hidden]
+ * (the block output) -> h_out [T, 4, hidden], all act_fmt but coef; h_out
+ * must not overlap h or y. */
+int ckv_hc_post(const ckv_hc_desc* desc, const float* coef, const void* h, const void* y, int32_t T,
+                void* h_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 20, names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -253,3 +253,24 @@ def test_score_timing_arms_and_disarms_without_a_device():
     # arming only records two handles for the calling thread; no GPU call
     assert L.time_next_score(None, None) == 0
     assert L.lib.ckv_time_next_score(None, None) == 0
+
+
+def test_hc_validate():
+    """The Hyper-Connection mixer's description: 4 streams, hidden a multiple of
+    8 up to 65536, 1..100 Sinkhorn iterations, finite eps >= 0, f32 / bf16."""
+    good = dict(hidden=4096, n_hc=4, sinkhorn_iters=20, eps=1e-6, act_fmt=L.CKV_BF16)
+    assert L.hc_validate(L.HcDesc(**good)) == 0
+    assert L.hc_validate(L.HcDesc(**dict(good, act_fmt=L.CKV_F32, hidden=8, sinkhorn_iters=1, eps=0.0))) == 0
+    for kw in (dict(n_hc=2), dict(hidden=100), dict(hidden=65544), dict(hidden=0), dict(sinkhorn_iters=0),
+               dict(sinkhorn_iters=101), dict(eps=-1.0), dict(eps=float("inf")), dict(eps=float("nan")),
+               dict(act_fmt=L.CKV_E4M3)):
+        assert L.hc_validate(L.HcDesc(**dict(good, **kw))) == L.CKV_E_UNSUPPORTED, kw
+    d = L.HcDesc(**good)
+    # NULL or misaligned pointers and T < 1 fail before any enqueue (no device needed)
+    assert L.hc_pre(d, 0, FAKE, 4, FAKE, FAKE, None) == L.CKV_E_INVAL
+    assert L.hc_pre(d, FAKE, FAKE, 4, MIS, FAKE, None) == L.CKV_E_INVAL
+    assert L.hc_pre(d, FAKE, FAKE, 0, FAKE + (1 << 30), FAKE, None) == L.CKV_E_INVAL
+    assert L.hc_post(d, FAKE, FAKE, FAKE, 4, 0, None) == L.CKV_E_INVAL
+    # outputs overlapping their inputs
+    assert L.hc_pre(d, FAKE, FAKE, 4, FAKE + 16, FAKE + (1 << 30), None) == L.CKV_E_INVAL
+    assert L.hc_post(d, FAKE + (1 << 30), FAKE, FAKE + (1 << 31), 4, FAKE + 4096, None) == L.CKV_E_INVAL
