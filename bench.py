@@ -54,7 +54,7 @@ def make_layer(cfg, wts, cache, max_chunk=0):
                      batch=cfg.batch, idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim, top_k=cfg.top_k,
                      comp_cap=cfg.comp_cap, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt, act_fmt=cfg.act_fmt,
                      w_fmt=cfg.w_fmt, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps, max_chunk=max_chunk,
-                     rope_base_comp=cfg.rope_base_comp or 0.0)
+                     rope_base_comp=cfg.rope_base_comp or 0.0, flags=cfg.flags)
     if wts is not None:
         dl.set_weights(wkv=wts.wkv, wgate=wts.wgate, ape=wts.ape, gamma=wts.gamma, idx_wkv=wts.idx_wkv,
                        idx_wgate=wts.idx_wgate, idx_ape=wts.idx_ape, idx_gamma=wts.idx_gamma)
@@ -96,7 +96,8 @@ def decode_step_bytes(cfg, n):
         b = 0.0
         if r == 4:
             b += V * rho_i + HI * (DI * s_a + 4) + 8 * k
-        b += (min(nb, 128) + C) * rho + H * d * 2 * s_a + d * s_a + rho
+        out_b = H * (d + 4 * (d // 128)) if cfg.flags & 32 else H * d * s_a   # fp8 output records
+        b += (min(nb, 128) + C) * rho + H * d * s_a + out_b + d * s_a + rho
         if r:
             b += D * s_a + 8 * (d + (DI if r == 4 else 0))
             if (p + 1) % r == 0:
@@ -658,7 +659,7 @@ def main():
         return
     extra = {}
     if not args.no_extra:
-        for name in ("c2", "c3", "c5_c128a", "c5_swa", "c5_fp4idx"):
+        for name in ("c2", "c3", "c5_c128a", "c5_swa", "c5_fp4idx", "c5_out8"):
             e = bench_decode(get_config(name), args.steps, args.warmup, with_kernel=name == "c5_fp4idx",
                              copies=args.layer_copies)
             extra[name] = {k: round(v, 4) for k, v in e.items() if not k.startswith("_") and isinstance(v, float)}

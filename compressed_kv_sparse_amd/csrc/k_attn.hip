@@ -207,6 +207,12 @@ __device__ __forceinline__ u32x4 ldg16(uint64_t a) {
 __device__ __forceinline__ float ldg_f32(uint64_t a) {
   return *(const __attribute__((address_space(1))) float*)(a);
 }
+// fp8 output records (CKV_FLAG_OUT_FP8): a row's d E4M3 codes, then one fp32
+// scale per group of 128 channels
+__device__ __forceinline__ int out8_bytes(int d) { return d + 4 * (d >> 7); }
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float e) {
+  return f32_to_e4m3(a) | (f32_to_e4m3(b) << 8) | (f32_to_e4m3(c) << 16) | (f32_to_e4m3(e) << 24);
+}
 }  // namespace attn
 
 // The row skipped list entries point at: zeros, so that a skipped row adds
@@ -704,6 +710,22 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
         for (int e = 0; e < 8; ++e) rot2(acc[2 * e], acc[2 * e + 1], cs_[fe][jq + e], -sn_[fe][jq + e]);
       }
       if (nsplit == 1) {
+        if (P.flags & CKV_FLAG_OUT_FP8) {   // fp8 record: group sub / 8 = 8 lanes
+          float am = 0.f;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) am = fmaxf(am, fabsf(acc[c]));
+#pragma unroll
+          for (int o = 1; o < 8; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+          const float sc = am > 0.f ? am / 448.f : 1.f;
+          uint8_t* rec = (uint8_t*)out + ((size_t)qn * H + hd) * out8_bytes(D);
+          const u32x4 w = {e4m3x4(acc[0] / sc, acc[1] / sc, acc[2] / sc, acc[3] / sc),
+                           e4m3x4(acc[4] / sc, acc[5] / sc, acc[6] / sc, acc[7] / sc),
+                           e4m3x4(acc[8] / sc, acc[9] / sc, acc[10] / sc, acc[11] / sc),
+                           e4m3x4(acc[12] / sc, acc[13] / sc, acc[14] / sc, acc[15] / sc)};
+          *(u32x4*)(rec + c0) = w;
+          if ((sub & 7) == 0) *(float*)(rec + D + 4 * (sub >> 3)) = sc;
+          continue;
+        }
 #pragma unroll
         for (int c = 0; c < 16; c += 2)
           *(uint32_t*)&out[((size_t)qn * H + hd) * D + c0 + c] = pack_bf16x2(acc[c], acc[c + 1]);
@@ -754,6 +776,29 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
     }
   }
   if (nsplit == 1) {
+    if (P.flags & CKV_FLAG_OUT_FP8) {
+      // fp8 record: this wave's channels are groups 2 cg (n < 8) and 2 cg + 1,
+      // each spread over the head's four lanes (l ^ 16, l ^ 32)
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const float m = fmaxf(fmaxf(fabsf(O[n][0]), fabsf(O[n][1])), fmaxf(fabsf(O[n][2]), fabsf(O[n][3])));
+        if (n < 8) a0 = fmaxf(a0, m);
+        else a1 = fmaxf(a1, m);
+      }
+      a0 = rows4_max(a0);
+      a1 = rows4_max(a1);
+      const float s0 = a0 > 0.f ? a0 / 448.f : 1.f, s1 = a1 > 0.f ? a1 / 448.f : 1.f;
+      uint8_t* rec = (uint8_t*)out + ((size_t)qn * H + head) * out8_bytes(D);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const float sc = n < 8 ? s0 : s1;
+        *(uint32_t*)(rec + 256 * cg + 16 * n + 4 * g) =
+            e4m3x4(O[n][0] / sc, O[n][1] / sc, O[n][2] / sc, O[n][3] / sc);
+      }
+      if (g == 0) *(float2*)(rec + D + 8 * cg) = make_float2(s0, s1);
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
       const int ch = 256 * cg + 16 * n + 4 * g;
@@ -874,7 +919,7 @@ __global__ __launch_bounds__(256) void k_attn_vec(LayerParams P, Cache cc, const
 // kernel), combined with weights l_s scale_s exp(m_s - M); otherwise fp32
 // unnormalised O_s with weights exp(m_s - M).  The splits have already
 // rotated their outputs back, so the merge only adds.
-template <int ACTF, bool HALF>
+template <int ACTF, bool HALF, bool OUT8 = false>
 __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml, int nsplit,
                                                     void* __restrict__ out) {
@@ -978,9 +1023,21 @@ __global__ __launch_bounds__(128) void k_attn_merge(LayerParams P, const float* 
   }
   const float inv = Lsh > 0.f ? 1.f / Lsh : 0.f;
   const float o[4] = {a.x * inv, a.y * inv, a.z * inv, a.w * inv};
-  const size_t oo = ((size_t)qn * H + h) * d + c;
+  if constexpr (OUT8) {
+    // fp8 record of this (query, head): group c / 128 = the 32 lanes of this
+    // half-wave; its scale max|o| / 448, written by the group's first lane
+    float am = fmaxf(fmaxf(fabsf(o[0]), fabsf(o[1])), fmaxf(fabsf(o[2]), fabsf(o[3])));
 #pragma unroll
-  for (int e = 0; e < 4; ++e) store_val<ACTF>(out, oo + e, o[e]);
+    for (int m = 1; m < 32; m <<= 1) am = fmaxf(am, __shfl_xor(am, m, 64));
+    const float sc = am > 0.f ? am / 448.f : 1.f;
+    uint8_t* rec = (uint8_t*)out + ((size_t)qn * H + h) * attn::out8_bytes(d);
+    *(uint32_t*)(rec + c) = attn::e4m3x4(o[0] / sc, o[1] / sc, o[2] / sc, o[3] / sc);
+    if ((c & 127) == 0) *(float*)(rec + d + 4 * (c >> 7)) = sc;
+  } else {
+    const size_t oo = ((size_t)qn * H + h) * d + c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_val<ACTF>(out, oo + e, o[e]);
+  }
 }
 
 // ----------------------------------------------------------------- launcher
@@ -1023,7 +1080,9 @@ int launch_attn(const LayerParams& P, const Cache& c, const void* q, const int32
   }
   dim3 mg(nq, P.H);
   const bool half = attn_uses_tiles(P);
-  if (P.act_fmt == CKV_F32 && half)
+  if (P.flags & CKV_FLAG_OUT_FP8)   // (validated: the tiled path, bf16 activations)
+    hipLaunchKernelGGL((k_attn_merge<CKV_BF16, true, true>), mg, dim3(128), 0, st, P, po, pml, ns, out);
+  else if (P.act_fmt == CKV_F32 && half)
     hipLaunchKernelGGL((k_attn_merge<CKV_F32, true>), mg, dim3(128), 0, st, P, po, pml, ns, out);
   else if (P.act_fmt == CKV_F32)
     hipLaunchKernelGGL((k_attn_merge<CKV_F32, false>), mg, dim3(128), 0, st, P, po, pml, ns, out);

@@ -129,6 +129,10 @@ class DeviceLayer:
             raise L.CkvError(rc, where)
 
     def new_out(self, n: int) -> torch.Tensor:
+        """An attention output buffer: [n, H, d] in act_fmt, or with
+        CKV_FLAG_OUT_FP8 [n, H, d + 4 d/128] bytes of fp8 records."""
+        if self.desc.flags & L.CKV_FLAG_OUT_FP8:
+            return torch.empty((n, self.H, self.d + 4 * (self.d // 128)), dtype=torch.uint8, device=self.device)
         dt = torch.float32 if self.act_fmt == "f32" else torch.bfloat16
         return torch.empty((n, self.H, self.d), dtype=dt, device=self.device)
 

@@ -113,6 +113,17 @@ extern "C" {
 #define CKV_FLAG_SKIP_NORM 4u
 #define CKV_FLAG_SKIP_ROPE 8u
 #define CKV_FLAG_KEEP_F32 16u
+/* Attention output in fp8, fused with its inverse RoPE [P4 "GPU compute
+ * saturation": inverse RoPE + fp8 quantisation of the attention output]:
+ * every (query, head) row of `out` is a record of head_dim OCP E4M3FN codes,
+ * then head_dim/128 float32 scales, one per group of 128 consecutive channels
+ * (s = max|o| / 448 over the group, 1 when all zero; code = RNE(o / s),
+ * saturated) -- 528 bytes at head_dim 512; out is [n, n_heads, 528] bytes.
+ * The page names the fusion, not the format: the group size and scale rule
+ * are this library's reading.  Built for the tiled attention (bf16
+ * activations, bf16 or E4M3 caches, head_dim 512, n_heads a multiple of 64),
+ * else CKV_E_UNSUPPORTED. */
+#define CKV_FLAG_OUT_FP8 32u
 
 /* ---- modes for ckv_workspace_bytes ---------------------------------------- */
 #define CKV_MODE_DECODE 0
@@ -349,7 +360,8 @@ int ckv_indexer_topk_prefill(const ckv_layer_desc* desc, const ckv_layer_cache* 
  * max(0, p-swa+1)..p, plus topk rows (ratio 4; entries < 0 skipped, entries
  * >= V end the list) or rows 0..V-1 (ratio 128) or none (ratio 0);
  * l_j = scale * q.row_j, o = sum_j softmax(l)_j row_j, then the output tail is
- * rotated by -p, and o is cast to act_fmt.
+ * rotated by -p, and o is cast to act_fmt (with CKV_FLAG_OUT_FP8: written as
+ * the fp8 records described there).
  * Decode: q [B, n_heads, head_dim], pos [B] device, topk [B, top_k] (ratio 4,
  *         else NULL), out [B, n_heads, head_dim].
  * Prefill: q [T, ...], topk [T, top_k] or NULL, out [T, ...] for queries

@@ -352,6 +352,44 @@ def encode_row(z: np.ndarray, fmt: str, d: int, n_rot: int) -> Tuple[np.ndarray,
 # ===========================================================================
 
 
+# ---------------------------------------------------------------------------
+# attention output in fp8 (P4 "GPU compute saturation": the inverse RoPE of the
+# attention output is fused with its fp8 quantisation).  The page names the
+# fusion, not the format; the reading taken here: E4M3 codes of the output
+# (after the inverse RoPE) in groups of 128 consecutive channels of a head,
+# each group scaled by s = max|o| / 448 over the group (1 when all zero), s
+# kept as fp32; a head's record is its d codes then its d/128 scales.
+
+OUT_FP8_GROUP = 128
+
+
+def out_fp8_record_bytes(d: int) -> int:
+    return d + 4 * (d // OUT_FP8_GROUP)
+
+
+def encode_out_fp8(o: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Output rows o [..., d] -> (records [..., d + 4 d/128] uint8, decoded
+    values [..., d])."""
+    o = np.asarray(o, F64)
+    d = o.shape[-1]
+    g = o.reshape(o.shape[:-1] + (d // OUT_FP8_GROUP, OUT_FP8_GROUP))
+    amax = np.abs(g).max(axis=-1)
+    s = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
+    codes = e4m3_encode(g / s.astype(F64)[..., None])
+    rec = np.concatenate([codes.reshape(o.shape[:-1] + (d,)),
+                          np.ascontiguousarray(s).view(np.uint8).reshape(o.shape[:-1] + (4 * (d // OUT_FP8_GROUP),))],
+                         axis=-1)
+    return rec, decode_out_fp8(rec, d)
+
+
+def decode_out_fp8(rec: np.ndarray, d: int) -> np.ndarray:
+    rec = np.asarray(rec, np.uint8)
+    ng = d // OUT_FP8_GROUP
+    s = np.ascontiguousarray(rec[..., d:d + 4 * ng]).view(np.float32).astype(F64)
+    v = e4m3_decode(rec[..., :d]).reshape(rec.shape[:-1] + (ng, OUT_FP8_GROUP))
+    return (v * s[..., None]).reshape(rec.shape[:-1] + (d,))
+
+
 def rope_theta(base: float, n_rot: int) -> np.ndarray:
     """theta_j = base^(-2j/n_rot), j = 0 .. n_rot/2 - 1."""
     j = np.arange(n_rot // 2, dtype=F64)

@@ -12,14 +12,14 @@ BF16_TOL = (2e-2, 1e-3)   # (rtol, atol) for bf16 / fp32 outputs
 FP8_TOL = (5e-2, 1e-3)    # when the K=V cache is fp8
 
 
-def device_layer(cfg: LayerShape, weights, cache: G.CacheInit = None, max_chunk: int = 0, batch=None, flags=0):
+def device_layer(cfg: LayerShape, weights, cache: G.CacheInit = None, max_chunk: int = 0, batch=None, flags=None):
     from compressed_kv_sparse_amd import DeviceLayer
     dl = DeviceLayer(ratio=cfg.ratio, hidden=cfg.hidden, head_dim=cfg.head_dim, n_heads=cfg.n_heads,
                      batch=cfg.batch if batch is None else batch, idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim,
                      top_k=cfg.top_k, comp_cap=cfg.comp_cap, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt,
                      act_fmt=cfg.act_fmt, w_fmt=cfg.w_fmt, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps,
                      n_rot=cfg.n_rot, swa=cfg.swa, max_chunk=max_chunk, rope_base_comp=cfg.rope_base_comp or 0.0,
-                     flags=flags)
+                     flags=cfg.flags if flags is None else flags)
     if weights is not None:
         dl.set_weights(wkv=weights.wkv, wgate=weights.wgate, ape=weights.ape, gamma=weights.gamma,
                        idx_wkv=weights.idx_wkv, idx_wgate=weights.idx_wgate, idx_ape=weights.idx_ape,
@@ -201,3 +201,28 @@ def tie_free_queries(cfg, seqs, pos, qI, w, attempts=40, margin=1e-4):
         else:
             raise AssertionError(f"no tie-free indexer query for sequence {b}")
     return qI, w
+
+
+def compare_out_fp8(rec_gpu, o_ref, rtol, what, atol=1e-3):
+    """fp8 attention-output records (CKV_FLAG_OUT_FP8) [H, d + 4 d/128] vs the
+    oracle's output o_ref [H, d] (pre-cast): every group's scale within rtol of
+    the oracle's max|o| / 448 and its largest code at 448 (or an all-zero
+    group with scale 1); decoded values within the attention tolerance plus
+    half an E4M3 step (2^-4 relative, 2^-10 of the scale below the normal
+    range)."""
+    o_ref = np.atleast_2d(np.asarray(o_ref, np.float64))
+    H, d = o_ref.shape
+    ng = d // 128
+    rec = np.asarray(rec_gpu, np.uint8).reshape(H, d + 4 * ng)
+    ref_rec, _ = O.encode_out_fp8(o_ref)
+    sg = rec[:, d:].copy().view(np.float32).reshape(H, ng).astype(np.float64)
+    sr = ref_rec[:, d:].copy().view(np.float32).reshape(H, ng).astype(np.float64)
+    assert np.all(np.abs(sg - sr) <= rtol * sr + atol / 448.0), f"{what}: group scales {sg.ravel()[:4]} vs {sr.ravel()[:4]}"
+    mag = (rec[:, :d] & 0x7F).reshape(H, ng, 128).max(axis=-1)
+    assert np.all((mag == 0x7E) | ((mag == 0) & (sg == 1.0))), f"{what}: a group's largest code is not 448"
+    deq = O.decode_out_fp8(rec, d)
+    bound = (atol + (rtol + 2.0 ** -4 * (1 + rtol)) * np.abs(o_ref)
+             + np.repeat(2.0 ** -10 * sg, 128, axis=1)) * 1.01
+    bad = np.abs(deq - o_ref) > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} fp8 outputs outside; first {np.argwhere(bad)[:3].tolist()} "
+                           f"gpu {deq[bad][:3]} ref {o_ref[bad][:3]}")

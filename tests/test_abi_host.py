@@ -52,7 +52,7 @@ def test_validate_accepts_the_workload_shapes():
     (dict(top_k=0), L.CKV_E_UNSUPPORTED), (dict(kv_fmt=7), L.CKV_E_UNSUPPORTED),
     (dict(act_fmt=L.CKV_E4M3), L.CKV_E_UNSUPPORTED), (dict(comp_cap=0), L.CKV_E_INVAL),
     (dict(batch=0), L.CKV_E_INVAL), (dict(rope_base=0.0), L.CKV_E_INVAL),
-    (dict(flags=0x80), L.CKV_E_UNSUPPORTED), (dict(flags=0x20), L.CKV_E_UNSUPPORTED), (dict(hidden=100), L.CKV_E_UNSUPPORTED),
+    (dict(flags=0x80), L.CKV_E_UNSUPPORTED), (dict(flags=0x40), L.CKV_E_UNSUPPORTED), (dict(hidden=100), L.CKV_E_UNSUPPORTED),
     (dict(top_k=2049), L.CKV_E_UNSUPPORTED), (dict(rope_base_comp=-1.0), L.CKV_E_INVAL),
 ])
 def test_validate_rejects(kw, code):
@@ -71,7 +71,7 @@ def test_debug_stage_flags():
     assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, **f32)) == 0
     assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, **dict(f32, idx_fmt=L.CKV_BF16))) == L.CKV_E_UNSUPPORTED
     assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, ratio=0, comp_cap=0, **dict(f32, idx_fmt=L.CKV_BF16))) == 0
-    assert L.validate(desc(flags=32)) == L.CKV_E_UNSUPPORTED
+    assert L.validate(desc(flags=64)) == L.CKV_E_UNSUPPORTED
 
 
 def test_validate_bounds_match_the_header():
@@ -274,3 +274,14 @@ def test_hc_validate():
     # outputs overlapping their inputs
     assert L.hc_pre(d, FAKE, FAKE, 4, FAKE + 16, FAKE + (1 << 30), None) == L.CKV_E_INVAL
     assert L.hc_post(d, FAKE + (1 << 30), FAKE, FAKE + (1 << 31), 4, FAKE + 4096, None) == L.CKV_E_INVAL
+
+
+def test_out_fp8_flag():
+    """CKV_FLAG_OUT_FP8 (attention output as E4M3 records with group scales) is
+    accepted on the tiled attention's shapes only."""
+    f = L.CKV_FLAG_OUT_FP8
+    assert L.validate(desc(flags=f)) == 0
+    assert L.validate(desc(flags=f, kv_fmt=L.CKV_BF16, ratio=128, comp_cap=8192)) == 0
+    assert L.validate(desc(flags=f, ratio=0, comp_cap=0)) == 0
+    for kw in (dict(act_fmt=L.CKV_F32), dict(kv_fmt=L.CKV_F32), dict(head_dim=256), dict(n_heads=32)):
+        assert L.validate(desc(flags=f, **kw)) == L.CKV_E_UNSUPPORTED, kw

@@ -883,3 +883,30 @@ def test_fp4_indexer_scores_by_brute_force():
     rows = np.stack([brute_rt(H @ seq._pool_row(i, "idx")) for i in range(V)])
     want = np.array([sum(w[h] * max(float(qt[h] @ rows[i]), 0.0) for h in range(2)) for i in range(V)])
     np.testing.assert_allclose(seq.index_scores(p, qI, w), want, rtol=1e-12, atol=1e-12)
+
+
+def test_out_fp8_scale_rule_and_error_bound():
+    """Attention output in fp8 (group-of-128 E4M3 with an fp32 scale
+    max|o|/448): each group's largest element takes the largest code (448),
+    a zero group keeps scale 1 and zero codes, the record holds d codes then
+    d/128 scales, and the round trip is within half an E4M3 step of its group
+    (2^-4 relative above 2^-6 s, 2^-10 s below)."""
+    rng = np.random.default_rng(1234)
+    o = rng.standard_normal((3, 512)) * np.array([[1.0], [1e-3], [50.0]])
+    o[1, 128:256] = 0.0
+    rec, val = O.encode_out_fp8(o)
+    assert rec.shape == (3, 512 + 16) and O.out_fp8_record_bytes(512) == 528
+    s = rec[:, 512:].copy().view(np.float32).reshape(3, 4).astype(np.float64)
+    g = o.reshape(3, 4, 128)
+    for r in range(3):
+        for k in range(4):
+            codes = rec[r, 128 * k:128 * (k + 1)]
+            if not np.any(g[r, k]):
+                assert s[r, k] == 1.0 and not np.any(codes & 0x7F)
+                continue
+            assert s[r, k] == np.float32(np.abs(g[r, k]).max() / 448.0)
+            assert (codes & 0x7F).max() == 0x7E          # 448 = exponent 15, mantissa 6
+            err = np.abs(val[r, 128 * k:128 * (k + 1)] - g[r, k])
+            bound = np.maximum(2.0 ** -4 * np.abs(g[r, k]), 2.0 ** -10 * s[r, k]) * (1 + 1e-6)
+            assert np.all(err <= bound)
+    assert np.allclose(O.decode_out_fp8(rec, 512), val)

@@ -75,6 +75,7 @@ class LayerShape:
     # variable context lengths per sequence (inclusive range); None -> all n_ctx
     ctx_range: Optional[Tuple[int, int]] = None
     layer: int = 0
+    flags: int = 0                    # ckv_layer_desc.flags (e.g. 32: attention output as fp8 records)
 
     @property
     def window(self) -> int:
@@ -147,6 +148,10 @@ for _r, _l in ((4, 2), (128, 3), (0, 0)):
 for _c in (_c5(4, 2).with_(name="c5_c4a_decode_b16_ctx131072_fp8_fp4idx", idx_fmt="fp4"),
            _c4().with_(name="c4_c4a_prefill_T4096_at61440_bf16_fp4idx", idx_fmt="fp4")):
     CONFIGS[_c.name] = _c
+# the C5 c4a decode with the attention output written as fp8 records (the
+# inverse RoPE fused with the output's E4M3 quantisation)
+_c = _c5(4, 2).with_(name="c5_c4a_decode_b16_ctx131072_fp8_out8", flags=32)
+CONFIGS[_c.name] = _c
 
 # short aliases
 ALIASES = {
@@ -159,6 +164,7 @@ ALIASES = {
     "c5_swa": "c5_swa_decode_b16_ctx131072_fp8",
     "c5_fp4idx": "c5_c4a_decode_b16_ctx131072_fp8_fp4idx",
     "c4_fp4idx": "c4_c4a_prefill_T4096_at61440_bf16_fp4idx",
+    "c5_out8": "c5_c4a_decode_b16_ctx131072_fp8_out8",
 }
 
 
