@@ -42,7 +42,9 @@ lower index, output ascending with -1 padding; an fp8 row keeps its RoPE tail
 in bf16 and scales its other channels by max|z|/448; an fp4 indexer cache is
 the QAT round trip of P1 s9 read as orthonormal Hadamard-128 then OCP MXFP4
 (E2M1 in blocks of 32 with a power-of-two block scale), applied alike to the
-rotated indexer query.
+rotated indexer query; the optional query norm (P4 "GPU compute
+saturation") divides each head's query by its RMS, with no learned weight,
+before the RoPE.
 
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
@@ -424,6 +426,19 @@ def rmsnorm(y: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
     return np.asarray(gamma, F64) * y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
 
 
+def query_rms_norm(q: np.ndarray, eps: float) -> np.ndarray:
+    """Each head's query divided by its RMS: q_h / sqrt(mean(q_h^2) + eps).
+
+    P4 "GPU compute saturation" lists a query norm among the steps fused with
+    the raw keys' RoPE and insertion, without its form.  Reading: an RMS
+    normalisation over each head's head_dim channels with no learned weight,
+    eps = the layer's RMSNorm eps, applied before the query's RoPE (a rotation
+    of channel pairs keeps every pair's sum of squares, so the order does not
+    change the result)."""
+    q = np.asarray(q, F64)
+    return q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + eps)
+
+
 def window_positions(i: int, ratio: int) -> np.ndarray:
     """Token position held by each slot j of compressed row i's window.
 
@@ -557,6 +572,9 @@ class OracleLayer:
     # no tail rotation anywhere (every angle zero).
     skip_norm: bool = False
     skip_rope: bool = False
+    # query norm of the layer description's flags: each head's attention
+    # query RMS-normalised (query_rms_norm) before its RoPE
+    q_norm: bool = False
 
     def rope(self, x, pos, base: float, n_rot: int) -> np.ndarray:
         """rope_tail, or the identity when the layer skips RoPE."""
@@ -817,6 +835,8 @@ class OracleSequence:
             sel = list(range(V))
         comp = self.comp_matrix(sel)
         qv = decode_values(q, L.act_fmt).reshape(L.n_heads, L.head_dim)
+        if L.q_norm:
+            qv = query_rms_norm(qv, L.norm_eps)
         q_raw = L.rope(qv, p, L.base_raw, L.n_rot)
         q_comp = L.rope(qv, p, L.base_comp, L.n_rot)
         o_raw, o_comp = attention_two_class(q_raw, raw, q_comp, comp, L.scale)

@@ -910,3 +910,61 @@ def test_out_fp8_scale_rule_and_error_bound():
             bound = np.maximum(2.0 ** -4 * np.abs(g[r, k]), 2.0 ** -10 * s[r, k]) * (1 + 1e-6)
             assert np.all(err <= bound)
     assert np.allclose(O.decode_out_fp8(rec, 512), val)
+
+
+# ---------------------------------------------------------------- query norm
+# P4 "GPU compute saturation" names a query norm fused with the raw keys'
+# RoPE and insertion.  Reading: each head's query divided by its RMS over the
+# head's channels (no learned weight, eps = the layer's RMSNorm eps), before
+# the RoPE.
+
+
+def test_query_norm_closed_forms():
+    # one head (3, 4): mean square 12.5
+    got = O.query_rms_norm(np.array([[3.0, 4.0]]), 0.0)
+    np.testing.assert_allclose(got, [[3.0 / math.sqrt(12.5), 4.0 / math.sqrt(12.5)]], rtol=1e-15)
+    # with eps the output's mean square is ms / (ms + eps), head by head:
+    # heads of very different size are each brought to RMS ~1 (not one
+    # norm over all heads)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((4, 64)) * np.array([[1e-3], [1.0], [30.0], [1e3]])
+    eps = 1e-6
+    out = O.query_rms_norm(q, eps)
+    ms = np.mean(q * q, axis=-1)
+    np.testing.assert_allclose(np.mean(out * out, axis=-1), ms / (ms + eps), rtol=1e-12)
+    # scale invariance at eps = 0 (a negative factor flips the sign)
+    np.testing.assert_allclose(O.query_rms_norm(-7.5 * q, 0.0), -O.query_rms_norm(q, 0.0), rtol=1e-13)
+    # a head whose entries are all +-1 is already at RMS 1
+    pm = np.where(rng.standard_normal((2, 32)) > 0, 1.0, -1.0)
+    np.testing.assert_array_equal(O.query_rms_norm(pm, 0.0), pm)
+
+
+@pytest.mark.parametrize("ratio", [4, 128])
+def test_query_norm_in_attention_is_per_head_and_before_rope(ratio):
+    """With the query norm on and eps = 0, a query whose head h holds
+    c_h * (+-1) entries attends exactly like the +-1 query without the norm
+    (each head rescaled by its own factor, the tail still rotated at p); and
+    the norm commutes with the RoPE: normalising the rotated query gives the
+    rotated normalised query."""
+    L = _rand_layer(ratio, seed=40 + ratio)
+    L.norm_eps = 0.0
+    X, U, Q, QI, Wt = _history(L, 260, seed=41)
+    seq = O.OracleSequence(L)
+    seq.feed(0, X, U)
+    p = 259
+    topk = O.topk_select(seq.index_scores(p, QI[p], Wt[p]), L.top_k) if ratio == 4 else None
+    rng = np.random.default_rng(42)
+    pm = np.where(rng.standard_normal((L.n_heads, L.head_dim)) > 0, 1.0, -1.0)
+    c = np.array([0.01, 3.0, 250.0])[:, None]
+    plain = seq.attend(p, pm, topk)
+    L.q_norm = True
+    np.testing.assert_allclose(seq.attend(p, c * pm, topk), plain, rtol=1e-12, atol=1e-13)
+    # the norm is not vacuous: a random query moves
+    qr = rng.standard_normal((L.n_heads, L.head_dim)) * 4.0
+    on = seq.attend(p, qr, topk)
+    L.q_norm = False
+    assert np.max(np.abs(on - seq.attend(p, qr, topk))) > 1e-3
+    # RoPE keeps each pair's sum of squares, so norm and rotation commute
+    rot = O.rope_tail(qr, p, L.base_raw, L.n_rot)
+    np.testing.assert_allclose(O.query_rms_norm(rot, 1e-6),
+                               O.rope_tail(O.query_rms_norm(qr, 1e-6), p, L.base_raw, L.n_rot), rtol=1e-12)
