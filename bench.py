@@ -659,7 +659,7 @@ def main():
         return
     extra = {}
     if not args.no_extra:
-        for name in ("c2", "c3", "c5_c128a", "c5_swa", "c5_fp4idx", "c5_out8"):
+        for name in ("c2", "c3", "c5_c128a", "c5_swa", "c5_fp4idx", "c5_out8", "c5_qnorm"):
             e = bench_decode(get_config(name), args.steps, args.warmup, with_kernel=name == "c5_fp4idx",
                              copies=args.layer_copies)
             extra[name] = {k: round(v, 4) for k, v in e.items() if not k.startswith("_") and isinstance(v, float)}

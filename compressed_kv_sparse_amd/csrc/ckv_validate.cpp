@@ -173,7 +173,7 @@ extern "C" int ckv_validate(const ckv_layer_desc* d) {
     return CKV_E_UNSUPPORTED;
   if (d->kv_fmt == CKV_E4M3 && d->head_dim <= d->n_rot) return CKV_E_UNSUPPORTED;
   if (d->flags & ~(CKV_FLAG_NO_INV_ROPE | CKV_FLAG_IDX_NO_RELU | CKV_FLAG_SKIP_NORM | CKV_FLAG_SKIP_ROPE |
-                   CKV_FLAG_KEEP_F32 | CKV_FLAG_OUT_FP8))
+                   CKV_FLAG_KEEP_F32 | CKV_FLAG_OUT_FP8 | CKV_FLAG_Q_NORM))
     return CKV_E_UNSUPPORTED;
   // fp8 output: the tiled attention's epilogues only
   if ((d->flags & CKV_FLAG_OUT_FP8) && !(d->act_fmt == CKV_BF16 && d->kv_fmt != CKV_F32 && d->n_heads % 64 == 0 &&

@@ -244,6 +244,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   // compressed frame, [2] the frame switch (angle p (theta_c - theta))
   __shared__ float cs_[3][32], sn_[3][32];
   __shared__ u32x4 qt_[4][2][64];   // the tail waves' stored query tails, for the frame switch
+  __shared__ float qss[2][64];      // query norm: each channel half's sum of squares per head
   __shared__ int tk_lim, any_bad, any_row;   // any_row: the split has an entry that is not skipped
 
   const int qn = blockIdx.x / nsplit, split = blockIdx.x - qn * nsplit;
@@ -335,7 +336,25 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       }
     }
   }
+  // query norm: this lane's 64 channels' squares, summed over the head's four
+  // lanes here and over the two channel halves through LDS
+  const bool qnorm = P.flags & CKV_FLAG_Q_NORM;
+  if (qnorm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = lo_bf16(Bq[ks][e]), b = hi_bf16(Bq[ks][e]);
+        ss = fmaf(a, a, fmaf(b, b, ss));
+      }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    if (g == 0) qss[cg][16 * hg + r] = ss;
+  }
   lds_barrier();
+  // 1 without the norm (an exact multiply)
+  const float qsc = qnorm ? 1.f / sqrtf((qss[0][16 * hg + r] + qss[1][16 * hg + r]) * (1.f / D) + P.eps) : 1.f;
   // address of ratio-128 compressed entry j (list index)
   auto comp_addr = [&](int j) -> uint64_t {
     const int jj = j - SWA;
@@ -420,12 +439,13 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
         const int jb = (32 * ks + 8 * g + 256 - DN) / 2;   // first pair index of this chunk
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float a = lo_bf16(v[e]), b = hi_bf16(v[e]);
+          float a = lo_bf16(v[e]) * qsc, b = hi_bf16(v[e]) * qsc;
           rot2(a, b, cs_[f0][jb + e], sn_[f0][jb + e]);
           Bq[ks][e] = pk_f16(a, b);
         }
       } else {
-        Bq[ks] = bf16x8_to_f16(v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bq[ks][e] = pk_f16(lo_bf16(v[e]) * qsc, hi_bf16(v[e]) * qsc);
       }
     }
   }
@@ -454,7 +474,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       const u32x4 qs = qt_[hg][ks - 6][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float a = lo_bf16(qs[e]), b = hi_bf16(qs[e]);
+        float a = lo_bf16(qs[e]) * qsc, b = hi_bf16(qs[e]) * qsc;
         rot2(a, b, cs_[1][jb + e], sn_[1][jb + e]);
         Bq[ks][e] = pk_f16(a, b);
       }
@@ -646,12 +666,25 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
       float qv[16], acc[16];
       {
         const u32x4* qr = (const u32x4*)(q + ((size_t)qn * H + hd) * D + c0);
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const u32x4 w = qr[h2];
+        const u32x4 w0 = qr[0], w1 = qr[1];
+        float gsc = 1.f;   // query norm over the head's 32 threads
+        if (qnorm) {
+          float ss = 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float a = lo_bf16(w[i]), b = hi_bf16(w[i]);
+            const float a0 = lo_bf16(w0[i]), b0 = hi_bf16(w0[i]), a1 = lo_bf16(w1[i]), b1 = hi_bf16(w1[i]);
+            ss = fmaf(a0, a0, fmaf(b0, b0, fmaf(a1, a1, fmaf(b1, b1, ss))));
+          }
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o, 64);
+          gsc = 1.f / sqrtf(ss * (1.f / D) + P.eps);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const u32x4 w = h2 ? w1 : w0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float a = lo_bf16(w[i]) * gsc, b = hi_bf16(w[i]) * gsc;
             if (tl) rot2(a, b, cs_[f0][jq + 4 * h2 + i], sn_[f0][jq + 4 * h2 + i]);
             qv[8 * h2 + 2 * i] = a * scale;
             qv[8 * h2 + 2 * i + 1] = b * scale;
@@ -852,9 +885,20 @@ __global__ __launch_bounds__(256) void k_attn_vec(LayerParams P, Cache cc, const
 
   float qv[32], acc[32];
   const int c0 = sub * dpt;
+  float qsc = 1.f;   // query norm: the head's sum of squares over its 16 lanes
+  if (P.flags & CKV_FLAG_Q_NORM) {
+    float ss = 0.f;
+    for (int e = 0; e < dpt; ++e) {
+      const float a = load_val<ACTF>(q, ((size_t)qn * H + h) * d + c0 + e);
+      ss = fmaf(a, a, ss);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    qsc = 1.f / sqrtf(ss / (float)d + P.eps);
+  }
   for (int e = 0; e < dpt; e += 2) {
     const size_t o = ((size_t)qn * H + h) * d + c0 + e;
-    float a = load_val<ACTF>(q, o), b = load_val<ACTF>(q, o + 1);
+    float a = load_val<ACTF>(q, o) * qsc, b = load_val<ACTF>(q, o + 1) * qsc;
     if (c0 + e >= dn) {
       float cs, sn;
       if (start_comp) rope_cs_c(P, (c0 + e - dn) / 2, pp, &cs, &sn);

@@ -124,6 +124,15 @@ extern "C" {
  * activations, bf16 or E4M3 caches, head_dim 512, n_heads a multiple of 64),
  * else CKV_E_UNSUPPORTED. */
 #define CKV_FLAG_OUT_FP8 32u
+/* Query norm inside the attention [P4 "GPU compute saturation": the query
+ * norm fused with the raw keys' RoPE and insertion]: before its RoPE, each
+ * head's attention query is divided by its RMS over head_dim channels,
+ * q_h / sqrt(mean(q_h^2) + norm_eps), in float32 with no learned weight (the
+ * page names the step, not its form: this is the library's reading).  The
+ * attention kernels apply it as they load the query, so the normalised query
+ * is never stored.  Any layer shape; affects sparse_swa_attn (and the decode
+ * step's attention) only, not the indexer query. */
+#define CKV_FLAG_Q_NORM 64u
 
 /* ---- modes for ckv_workspace_bytes ---------------------------------------- */
 #define CKV_MODE_DECODE 0

@@ -10,6 +10,7 @@ from workloads.configs import LayerShape
 
 BF16_TOL = (2e-2, 1e-3)   # (rtol, atol) for bf16 / fp32 outputs
 FP8_TOL = (5e-2, 1e-3)    # when the K=V cache is fp8
+Q_NORM_FLAG = 64          # ckv_layer_desc.flags bit of the query norm
 
 
 def device_layer(cfg: LayerShape, weights, cache: G.CacheInit = None, max_chunk: int = 0, batch=None, flags=None):
@@ -39,7 +40,9 @@ def dev(a, device="cuda"):
 
 
 def oracle_layer(cfg, weights):
-    return O.layer_from(cfg, weights)
+    L = O.layer_from(cfg, weights)
+    L.q_norm = bool(cfg.flags & Q_NORM_FLAG)
+    return L
 
 
 def oracle_seq_from_init(L, cache: G.CacheInit, b: int) -> O.OracleSequence:

@@ -52,7 +52,7 @@ def test_validate_accepts_the_workload_shapes():
     (dict(top_k=0), L.CKV_E_UNSUPPORTED), (dict(kv_fmt=7), L.CKV_E_UNSUPPORTED),
     (dict(act_fmt=L.CKV_E4M3), L.CKV_E_UNSUPPORTED), (dict(comp_cap=0), L.CKV_E_INVAL),
     (dict(batch=0), L.CKV_E_INVAL), (dict(rope_base=0.0), L.CKV_E_INVAL),
-    (dict(flags=0x80), L.CKV_E_UNSUPPORTED), (dict(flags=0x40), L.CKV_E_UNSUPPORTED), (dict(hidden=100), L.CKV_E_UNSUPPORTED),
+    (dict(flags=0x80), L.CKV_E_UNSUPPORTED), (dict(flags=0x100), L.CKV_E_UNSUPPORTED), (dict(hidden=100), L.CKV_E_UNSUPPORTED),
     (dict(top_k=2049), L.CKV_E_UNSUPPORTED), (dict(rope_base_comp=-1.0), L.CKV_E_INVAL),
 ])
 def test_validate_rejects(kw, code):
@@ -71,7 +71,7 @@ def test_debug_stage_flags():
     assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, **f32)) == 0
     assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, **dict(f32, idx_fmt=L.CKV_BF16))) == L.CKV_E_UNSUPPORTED
     assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, ratio=0, comp_cap=0, **dict(f32, idx_fmt=L.CKV_BF16))) == 0
-    assert L.validate(desc(flags=64)) == L.CKV_E_UNSUPPORTED
+    assert L.validate(desc(flags=128)) == L.CKV_E_UNSUPPORTED
 
 
 def test_validate_bounds_match_the_header():
@@ -285,3 +285,16 @@ def test_out_fp8_flag():
     assert L.validate(desc(flags=f, ratio=0, comp_cap=0)) == 0
     for kw in (dict(act_fmt=L.CKV_F32), dict(kv_fmt=L.CKV_F32), dict(head_dim=256), dict(n_heads=32)):
         assert L.validate(desc(flags=f, **kw)) == L.CKV_E_UNSUPPORTED, kw
+
+
+def test_q_norm_flag():
+    """CKV_FLAG_Q_NORM (each head's query RMS-normalised in the attention) is
+    accepted on every layer shape and combines with the other flags; its value
+    is the one the test harness gives the oracle."""
+    from harness import Q_NORM_FLAG
+    f = L.CKV_FLAG_Q_NORM
+    assert f == Q_NORM_FLAG == 64
+    for kw in (dict(), dict(act_fmt=L.CKV_F32, kv_fmt=L.CKV_F32, w_fmt=L.CKV_F32, idx_fmt=L.CKV_F32),
+               dict(head_dim=256), dict(n_heads=32), dict(ratio=0, comp_cap=0)):
+        assert L.validate(desc(flags=f, **kw)) == 0, kw
+    assert L.validate(desc(flags=f | L.CKV_FLAG_OUT_FP8 | L.CKV_FLAG_NO_INV_ROPE)) == 0

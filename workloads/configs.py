@@ -152,6 +152,9 @@ for _c in (_c5(4, 2).with_(name="c5_c4a_decode_b16_ctx131072_fp8_fp4idx", idx_fm
 # inverse RoPE fused with the output's E4M3 quantisation)
 _c = _c5(4, 2).with_(name="c5_c4a_decode_b16_ctx131072_fp8_out8", flags=32)
 CONFIGS[_c.name] = _c
+# ... and with each head's query RMS-normalised inside the attention
+_c = _c5(4, 2).with_(name="c5_c4a_decode_b16_ctx131072_fp8_qnorm", flags=64)
+CONFIGS[_c.name] = _c
 
 # short aliases
 ALIASES = {
@@ -165,6 +168,7 @@ ALIASES = {
     "c5_fp4idx": "c5_c4a_decode_b16_ctx131072_fp8_fp4idx",
     "c4_fp4idx": "c4_c4a_prefill_T4096_at61440_bf16_fp4idx",
     "c5_out8": "c5_c4a_decode_b16_ctx131072_fp8_out8",
+    "c5_qnorm": "c5_c4a_decode_b16_ctx131072_fp8_qnorm",
 }
 
 
