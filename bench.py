@@ -401,7 +401,9 @@ def bench_stack(steps, warmup):
 
 # --------------------------------------------------------------------------- prefill
 
-def bench_prefill(cfg, steps, warmup):
+def bench_prefill(cfg, steps, warmup, side=False):
+    """One chunk per run: the three prefill calls, or (side) one
+    ckv_prefill_chunk call with the indexer branch on a second stream."""
     import torch
     from workloads import make_layer_weights, make_prefill_inputs
 
@@ -419,13 +421,17 @@ def bench_prefill(cfg, steps, warmup):
     saved = [(t, t.clone()) for t in (dl.raw, dl.st_kv, dl.st_sc, dl.ist_kv, dl.ist_sc, dl.n_tokens)
              if t is not None]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    side_st = torch.cuda.Stream() if side else None
 
     def run(ev=None):
         for t, c in saved:
             t.copy_(c)
         if ev is not None:
             ev[0].record()
-        dl.prefill(0, inp.pos0, x, u, q, qI, w, out=out, topk=topk)
+        if side_st is None:
+            dl.prefill(0, inp.pos0, x, u, q, qI, w, out=out, topk=topk)
+        else:
+            dl.prefill_chunk(0, inp.pos0, x, u, q, qI, w, out=out, topk=topk, side_stream=side_st)
         if ev is not None:
             ev[1].record()
 
@@ -594,6 +600,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--side-stream", action="store_true",
+                    help="--part prefill: one ckv_prefill_chunk call with the indexer branch on a second stream")
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--part", choices=("all", "decode", "prefill", "stack", "hc"), default="all",
                     help="time one part alone and print its own JSON line (for kernel profiles)")
@@ -629,8 +637,8 @@ def main():
         del a, b
     if args.part == "prefill":
         pcfg = get_config(args.workload if args.workload.startswith("c4") else "c4")
-        p = bench_prefill(pcfg, args.prefill_steps, 1)
-        print(json.dumps({"part": "prefill", "workload": pcfg.name,
+        p = bench_prefill(pcfg, args.prefill_steps, 1, side=args.side_stream)
+        print(json.dumps({"part": "prefill", "workload": pcfg.name, "side_stream": args.side_stream,
                           **{k: round(v, 4) for k, v in p.items()}}), flush=True)
         return
     if args.part == "hc":
@@ -686,6 +694,12 @@ def main():
                "mfma_frac": round(p["mfma_frac"], 4)}
         log(f"[bench] prefill: {p['ms_per_chunk']:.2f} ms/chunk, {p['tok_s']:.0f} tok/s, "
             f"{p['tflops']:.1f} TFLOP/s ({100 * p['mfma_frac']:.1f}% of bf16 MFMA)")
+        if not args.no_extra:   # one call, the indexer on a second stream
+            pp = bench_prefill(get_config("c4"), args.prefill_steps, 1, side=True)
+            pre["side_stream"] = {"ms_per_chunk": round(pp["ms_per_chunk"], 3), "tok_s": round(pp["tok_s"], 1),
+                                  "mfma_frac": round(pp["mfma_frac"], 4)}
+            log(f"[bench] prefill (indexer on a second stream): {pp['ms_per_chunk']:.2f} ms/chunk, "
+                f"{pp['tok_s']:.0f} tok/s")
         if not args.no_extra:   # the same chunk with the fp4 indexer cache
             c4f = get_config("c4_fp4idx")
             pf = bench_prefill(c4f, args.prefill_steps, 1)

@@ -114,6 +114,7 @@ def _load() -> ctypes.CDLL:
         "ckv_sparse_swa_attn_prefill": [D, C, VP, I32, I32, I32, VP, VP, VP, SZ, VP],
         "ckv_decode_step": [D, Wt, C, VP, VP, VP, VP, VP, VP, I32, VP, VP, VP, SZ, VP],
         "ckv_decode_step_static": [D, Wt, C, VP, VP, VP, VP, VP, VP, I32, VP, VP, VP],
+        "ckv_prefill_chunk": [D, Wt, C, VP, VP, VP, VP, VP, I32, I32, I32, VP, VP, VP, SZ, VP, VP],
         "ckv_hc_validate": [P(HcDesc)],
         "ckv_hc_pre": [P(HcDesc), VP, VP, I32, VP, VP, VP],
         "ckv_hc_post": [P(HcDesc), VP, VP, VP, I32, VP, VP],
@@ -132,7 +133,7 @@ EXPORTS = ("ckv_row_bytes", "ckv_idx_row_bytes", "ckv_validate", "ckv_strerror",
            "ckv_compress_append_decode", "ckv_compress_append_prefill", "ckv_indexer_topk_decode",
            "ckv_indexer_topk_prefill", "ckv_indexer_score_decode", "ckv_sparse_swa_attn_decode",
            "ckv_sparse_swa_attn_prefill", "ckv_decode_step", "ckv_time_next_score", "ckv_decode_step_static",
-           "ckv_hc_validate", "ckv_hc_pre", "ckv_hc_post")
+           "ckv_hc_validate", "ckv_hc_pre", "ckv_hc_post", "ckv_prefill_chunk")
 
 
 def strerror(code: int) -> str:
@@ -226,6 +227,13 @@ def decode_step(desc, weights, cache, x, u, q, qI, w, pos, B, topk, out, ws, ws_
 def decode_step_static(desc, weights, cache, x, u, q, qI, w, pos, B, topk, out, stream=None) -> int:
     return lib.ckv_decode_step_static(_ref(desc), _ref(weights), _ref(cache), _p(x), _p(u), _p(q), _p(qI), _p(w),
                                       _p(pos), int(B), _p(topk), _p(out), stream)
+
+
+def prefill_chunk(desc, weights, cache, x, u, q, qI, w, seq, pos0, T, topk, out, ws, ws_bytes, stream=None,
+                  side_stream=None) -> int:
+    return lib.ckv_prefill_chunk(_ref(desc), _ref(weights), _ref(cache), _p(x), _p(u), _p(q), _p(qI), _p(w),
+                                 int(seq), int(pos0), int(T), _p(topk), _p(out), _p(ws), int(ws_bytes), stream,
+                                 side_stream)
 
 
 def hc_validate(desc: HcDesc) -> int:

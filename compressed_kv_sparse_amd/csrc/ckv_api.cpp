@@ -301,6 +301,82 @@ extern "C" int ckv_decode_step(const ckv_layer_desc* desc, const ckv_layer_weigh
   return launched(launch_attn(P, C, q, pos, 0, 0, B, topk, out, L, wb, stream));
 }
 
+// ---- prefill chunk with the indexer on a second stream ----------------------
+
+namespace {
+// events of one call: created here, destroyed once enqueued (the runtime
+// releases an event that is still pending when its work completes)
+struct Events {
+  hipEvent_t e[3] = {};
+  int n = 0;
+  int get(hipEvent_t* ev) {   // a hipError_t
+    const hipError_t r = hipEventCreateWithFlags(&e[n], hipEventDisableTiming);
+    if (r == hipSuccess) *ev = e[n++];
+    return (int)r;
+  }
+  ~Events() {
+    for (int i = 0; i < n; ++i) (void)hipEventDestroy(e[i]);
+  }
+};
+}  // namespace
+
+extern "C" int ckv_prefill_chunk(const ckv_layer_desc* desc, const ckv_layer_weights* w,
+                                 const ckv_layer_cache* cache, const void* x, const void* u, const void* q,
+                                 const void* qI, const float* iw, int32_t seq, int32_t pos0, int32_t T,
+                                 int32_t* topk, void* out, void* ws, size_t ws_bytes, void* stream,
+                                 void* side_stream) {
+  LayerParams P;
+  int rc = prologue(desc, cache, &P);
+  if (rc) return rc;
+  if ((rc = prefill_range_ok(P, cache, seq, pos0, T))) return rc;
+  if ((rc = prefill_sequence_ok(cache, seq, pos0))) return rc;
+  if ((rc = weights_ok(P, w))) return rc;
+  if (check_ptr(u) || check_ptr(q) || check_ptr(out) || (P.ratio && check_ptr(x))) return CKV_E_INVAL;
+  if (P.ratio == 4 && (check_ptr(qI) || check_ptr(iw) || check_ptr(topk) || !aligned16(topk))) return CKV_E_INVAL;
+  WsLayout L;
+  if ((rc = check_ws(P, CKV_MODE_PREFILL, T, ws, ws_bytes, &L))) return rc;
+  clear_stale();
+  const Weights W = P.ratio ? to_weights(w) : Weights{};
+  const Cache C = to_cache(cache);
+  uint8_t* wb = (uint8_t*)ws;
+  float* part = (float*)(wb + L.proj);
+  uint32_t* keys = (uint32_t*)(wb + L.keys);
+  int32_t* tk = P.ratio == 4 ? topk : nullptr;
+  if (P.ratio != 4 || !side_stream || side_stream == stream) {
+    if (P.ratio && (rc = launch_proj(P, W, x, T, part, 1, stream))) return launched(rc);
+    if ((rc = launch_compress_prefill(P, W, C, u, seq, pos0, T, part, stream))) return launched(rc);
+    if (P.ratio == 4 && (rc = launch_indexer(P, C, qI, iw, nullptr, seq, pos0, T, keys, nullptr, topk, stream)))
+      return launched(rc);
+    return launched(launch_attn(P, C, q, nullptr, seq, pos0, T, tk, out, L, wb, stream));
+  }
+  // Two streams.  Main: the attention lane's projection columns, the raw
+  // staging and the attention rows.  Side: the indexer lane's projection
+  // columns and rows (event `pooled`), then the scores and the selection
+  // (event `selected`).  Main then moves the state rings and the token count
+  // (which the indexer rows' pooling reads: after `pooled`) and runs the
+  // attention after `selected`.
+  hipStream_t main_st = (hipStream_t)stream, side = (hipStream_t)side_stream;
+  const int ca = 2 * P.d;   // attention-lane columns [0, 2d), indexer lane [2d, ncol)
+  Events ev;
+  hipEvent_t fork, pooled, selected;
+  if ((rc = ev.get(&fork)) || (rc = ev.get(&pooled)) || (rc = ev.get(&selected))) return launched(rc);
+  if ((rc = (int)hipEventRecord(fork, main_st)) || (rc = (int)hipStreamWaitEvent(side, fork, 0)))
+    return launched(rc);
+  if ((rc = launch_proj(P, W, x, T, part, 1, side, ca, P.ncol)) ||
+      (rc = launch_compress_prefill(P, W, C, u, seq, pos0, T, part, side, kPfPoolIdx)) ||
+      (rc = (int)hipEventRecord(pooled, side)) ||
+      (rc = launch_indexer(P, C, qI, iw, nullptr, seq, pos0, T, keys, nullptr, topk, side)) ||
+      (rc = (int)hipEventRecord(selected, side)))
+    return launched(rc);
+  if ((rc = launch_proj(P, W, x, T, part, 1, main_st, 0, ca)) ||
+      (rc = launch_compress_prefill(P, W, C, u, seq, pos0, T, part, main_st, kPfStage | kPfPoolAttn)) ||
+      (rc = (int)hipStreamWaitEvent(main_st, pooled, 0)) ||
+      (rc = launch_compress_prefill(P, W, C, u, seq, pos0, T, part, main_st, kPfState)) ||
+      (rc = (int)hipStreamWaitEvent(main_st, selected, 0)))
+    return launched(rc);
+  return launched(launch_attn(P, C, q, nullptr, seq, pos0, T, tk, out, L, wb, stream));
+}
+
 extern "C" int ckv_time_next_score(void* start_event, void* stop_event) {
   arm_score_timing(start_event, stop_event);
   return CKV_OK;

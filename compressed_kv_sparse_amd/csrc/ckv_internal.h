@@ -108,17 +108,22 @@ int attn_max_rows(const LayerParams& P);
 bool attn_uses_tiles(const LayerParams& P);
 
 // ---- launchers (return 0 or a hipError_t value) ----------------------------
-// projection: part[s][m][c] for columns c of the concatenated weights
+// projection: part[s][m][c] for columns c_begin <= c < c_end (-1: ncol) of
+// the concatenated weights
 int launch_proj(const LayerParams& P, const Weights& w, const void* x, int M, float* part,
-                int splits, void* stream);
+                int splits, void* stream, int c_begin = 0, int c_end = -1);
 // c128a decode pools channel slices of 64 in parallel blocks (head_dim a
 // multiple of 64, at most 512); pool_ws: the workspace's pool region
 bool c128a_sliced(const LayerParams& P);
 int launch_compress_decode(const LayerParams& P, const Weights& w, const Cache& c, const void* u,
                            const int32_t* pos, int B, const float* part, int splits, float* pool_ws,
                            void* stream);
+// the chunk's compressor pieces: raw staging, attention-lane rows,
+// indexer-lane rows, then the state rings and the token count (in that order
+// when several are asked for)
+constexpr int kPfStage = 1, kPfPoolAttn = 2, kPfPoolIdx = 4, kPfState = 8, kPfAll = 15;
 int launch_compress_prefill(const LayerParams& P, const Weights& w, const Cache& c, const void* u,
-                            int seq, int pos0, int T, const float* part, void* stream);
+                            int seq, int pos0, int T, const float* part, void* stream, int parts = kPfAll);
 // indexer: decode (pos != NULL, query b of sequence b) or prefill (pos == NULL,
 // query n of sequence seq at position pos0 + n)
 int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const float* w,

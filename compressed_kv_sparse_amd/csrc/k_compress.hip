@@ -253,11 +253,12 @@ __global__ __launch_bounds__(256) void k_stage_raw(LayerParams P, Cache cc, cons
 
 // Pool every row whose window closes inside the chunk.  Window tokens before
 // pos0 come from the state ring, chunk tokens from the projection part[n][col].
-// One block per emitted row i = i_first + blockIdx.x.
+// One block per emitted row i = i_first + blockIdx.x; lanes: bit 0 the
+// attention row, bit 1 the indexer row (ratio 4).
 template <int KVF, int IDXF>
 __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, Cache cc,
                                                       const float* __restrict__ part, int seq,
-                                                      int pos0, int i_first) {
+                                                      int pos0, int i_first, int lanes) {
   __shared__ float zs[kMaxD];
   __shared__ __attribute__((aligned(16))) float zi[kMaxDI];
   __shared__ float red[16];
@@ -267,30 +268,32 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
   const int t0 = i * r - (W - r);
   const float* skv = cc.st_kv + (size_t)seq * W * d;
   const float* ssc = cc.st_sc + (size_t)seq * W * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    PoolAcc pa;
-    for (int j = 0; j < W; ++j) {
-      const int t = t0 + j;
-      if (t < 0) continue;
-      float kv, sc;
-      if (t >= pos0) {
-        const float* pr = part + (size_t)(t - pos0) * nc;
-        kv = pr[c];
-        sc = pr[d + c];
-      } else {
-        kv = skv[(t % W) * d + c];
-        sc = ssc[(t % W) * d + c];
+  if (lanes & 1) {
+    for (int c = threadIdx.x; c < d; c += blockDim.x) {
+      PoolAcc pa;
+      for (int j = 0; j < W; ++j) {
+        const int t = t0 + j;
+        if (t < 0) continue;
+        float kv, sc;
+        if (t >= pos0) {
+          const float* pr = part + (size_t)(t - pos0) * nc;
+          kv = pr[c];
+          sc = pr[d + c];
+        } else {
+          kv = skv[(t % W) * d + c];
+          sc = ssc[(t % W) * d + c];
+        }
+        pa.add(sc + w.ape[j * d + c], kv);
       }
-      pa.add(sc + w.ape[j * d + c], kv);
+      zs[c] = pa.value();
     }
-    zs[c] = pa.value();
+    rmsnorm_lds(P, zs, d, w.gamma, red);
+    __syncthreads();
+    rope_lds(P, zs, d, P.n_rot, (double)i * r, true);
+    __syncthreads();
+    store_row<KVF>(cc.comp + ((size_t)seq * P.cap + i) * P.row_bytes, zs, d, P.n_rot, red);
   }
-  rmsnorm_lds(P, zs, d, w.gamma, red);
-  __syncthreads();
-  rope_lds(P, zs, d, P.n_rot, (double)i * r, true);
-  __syncthreads();
-  store_row<KVF>(cc.comp + ((size_t)seq * P.cap + i) * P.row_bytes, zs, d, P.n_rot, red);
-  if (r != 4) return;
+  if (r != 4 || !(lanes & 2)) return;
   const float* ikv = cc.ist_kv + (size_t)seq * 8 * DI;
   const float* isc = cc.ist_sc + (size_t)seq * 8 * DI;
   for (int c = threadIdx.x; c < DI; c += blockDim.x) {
@@ -421,23 +424,26 @@ int launch_compress_decode(const LayerParams& P, const Weights& w, const Cache& 
 
 template <int KVF, int IDXF, int ACTF>
 static void go_prefill(const LayerParams& P, const Weights& w, const Cache& c, const void* u,
-                       int seq, int pos0, int T, const float* part, hipStream_t st) {
-  hipLaunchKernelGGL((k_stage_raw<KVF, ACTF>), dim3(T + P.swa - 1), dim3(256), 0, st, P, c, u, seq,
-                     pos0);
-  if (P.ratio) {
+                       int seq, int pos0, int T, const float* part, hipStream_t st, int parts) {
+  if (parts & kPfStage)
+    hipLaunchKernelGGL((k_stage_raw<KVF, ACTF>), dim3(T + P.swa - 1), dim3(256), 0, st, P, c, u, seq, pos0);
+  const int lanes = ((parts & kPfPoolAttn) ? 1 : 0) | ((parts & kPfPoolIdx) && P.ratio == 4 ? 2 : 0);
+  if (P.ratio && lanes) {
     const int i_first = pos0 / P.ratio, i_end = (pos0 + T) / P.ratio;
     if (i_end > i_first)
       hipLaunchKernelGGL((k_pool_prefill<KVF, IDXF>), dim3(i_end - i_first), dim3(256), 0, st, P, w,
-                         c, part, seq, pos0, i_first);
+                         c, part, seq, pos0, i_first, lanes);
   }
-  hipLaunchKernelGGL(k_state_prefill, dim3(P.swa), dim3(256), 0, st, P, c, part, seq, pos0, T);
-  if (c.n_tokens) hipLaunchKernelGGL(k_advance_tokens, dim3(1), dim3(1), 0, st, c, seq, pos0, T);
+  if (parts & kPfState) {
+    hipLaunchKernelGGL(k_state_prefill, dim3(P.swa), dim3(256), 0, st, P, c, part, seq, pos0, T);
+    if (c.n_tokens) hipLaunchKernelGGL(k_advance_tokens, dim3(1), dim3(1), 0, st, c, seq, pos0, T);
+  }
 }
 
 int launch_compress_prefill(const LayerParams& P, const Weights& w, const Cache& c, const void* u,
-                            int seq, int pos0, int T, const float* part, void* stream) {
+                            int seq, int pos0, int T, const float* part, void* stream, int parts) {
   hipStream_t st = (hipStream_t)stream;
-  CKV_DISPATCH_KV_IDX_ACT(go_prefill, P, w, c, u, seq, pos0, T, part, st);
+  CKV_DISPATCH_KV_IDX_ACT(go_prefill, P, w, c, u, seq, pos0, T, part, st, parts);
   return (int)hipGetLastError();
 }
 

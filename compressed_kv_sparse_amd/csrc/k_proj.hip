@@ -12,13 +12,14 @@ namespace ckv {
 
 // bf16 activations x bf16 weights on MFMA.  One wave computes a 32 x 16 tile
 // (two 16-row blocks of x against 16 weight rows) over one K range.
-// grid: x = ncol / 64 (4 waves of 16 columns), y = splits, z = ceil(M / 32).
+// grid: x = (cend - cbase) / 64 (4 waves of 16 columns), y = splits,
+// z = ceil(M / 32); part rows have stride ncol.
 __global__ __launch_bounds__(256) void k_proj_mfma(const uint16_t* __restrict__ X, int M, int K,
                                                    WCat wc, int ncol, int klen,
-                                                   float* __restrict__ part) {
+                                                   float* __restrict__ part, int cbase, int cend) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col0 = blockIdx.x * 64 + wave * 16;
-  if (col0 >= ncol) return;
+  const int col0 = cbase + blockIdx.x * 64 + wave * 16;
+  if (col0 >= cend) return;
   const int m0 = blockIdx.z * 32;
   const int k0 = blockIdx.y * klen, k1 = min(K, k0 + klen);
   const int r = lane & 15, g = lane >> 4;
@@ -77,8 +78,9 @@ __global__ __launch_bounds__(256) void k_proj_mfma(const uint16_t* __restrict__ 
 // k-steps and 6 clamped repeats; 2 waves 5.4 us, 8 slices 5.2-7.3 us.)
 constexpr int kProjDecWaves = 4;
 __global__ __launch_bounds__(1024) void k_proj_dec(const uint16_t* __restrict__ X, int M, int K, WCat wc, int ncol,
-                                                   float* __restrict__ part) {
-  proj_tile<kProjDecWaves>(X, M, K, wc, ncol, part, blockIdx.x * 16, blockIdx.y * 16, blockIdx.z, gridDim.z);
+                                                   float* __restrict__ part, int cbase) {
+  proj_tile<kProjDecWaves>(X, M, K, wc, ncol, part, cbase + blockIdx.x * 16, blockIdx.y * 16, blockIdx.z,
+                           gridDim.z);
 }
 
 // Chunk projection (M >= 128 rows): a tiled GEMM.  A block computes a 128 x 128
@@ -95,12 +97,12 @@ constexpr int kGM = 128, kGN = 128, kGK = 64;
 __device__ __forceinline__ int gsw(int R, int c) { return R * 128 + 16 * (c ^ ((R >> 1) & 7)); }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_proj_gemm(
-    const uint16_t* __restrict__ X, int M, int K, WCat wc, int ncol, float* __restrict__ part) {
+    const uint16_t* __restrict__ X, int M, int K, WCat wc, int ncol, float* __restrict__ part, int cbase) {
   __shared__ __attribute__((aligned(16))) uint8_t sa[2][kGM * 128], sb[2][kGN * 128];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int col0 = blockIdx.x * kGN, m0 = blockIdx.y * kGM;
+  const int col0 = cbase + blockIdx.x * kGN, m0 = blockIdx.y * kGM;
   int local;
   const uint16_t* W = (const uint16_t*)wcat_row(wc, col0, K, 2, &local);   // row col0 of its matrix
   // staging: thread t moves 16-byte chunks t + 256 e (e < 4) of each 128 x 64 tile: row ch >> 3, chunk ch & 7
@@ -168,8 +170,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // grid: x = ncol, y = ceil(M / 4).  Writes split 0.
 template <int XF, int WF>
 __global__ __launch_bounds__(64) void k_proj_vec(const void* __restrict__ X, int M, int K, WCat wc,
-                                                 int ncol, float* __restrict__ part) {
-  const int col = blockIdx.x, m0 = blockIdx.y * 4, lane = threadIdx.x;
+                                                 int ncol, float* __restrict__ part, int cbase) {
+  const int col = cbase + blockIdx.x, m0 = blockIdx.y * 4, lane = threadIdx.x;
   int local;
   const void* wrow = wcat_row(wc, col, K, WF == CKV_F32 ? 4 : 2, &local);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -187,30 +189,33 @@ __global__ __launch_bounds__(64) void k_proj_vec(const void* __restrict__ X, int
 }
 
 int launch_proj(const LayerParams& P, const Weights& w, const void* x, int M, float* part,
-                int splits, void* stream) {
+                int splits, void* stream, int c_begin, int c_end) {
   hipStream_t st = (hipStream_t)stream;
   const WCat wc = make_wcat(P, w);
   const int K = P.hidden;
-  if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && M <= 64) {
-    dim3 grid(P.ncol / 16, (M + 15) / 16, splits);
+  if (c_end < 0) c_end = P.ncol;
+  const int nc = c_end - c_begin;   // columns of this launch; part rows keep stride ncol
+  if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && M <= 64 && c_begin % 16 == 0 && nc % 16 == 0) {
+    dim3 grid(nc / 16, (M + 15) / 16, splits);
     hipLaunchKernelGGL(k_proj_dec, grid, dim3(64 * kProjDecWaves), 0, st, (const uint16_t*)x, M, K, wc, P.ncol,
-                       part);
+                       part, c_begin);
   } else if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && splits == 1 && M >= kGM && P.d % kGN == 0 &&
-             (P.ratio != 4 || P.DI % kGN == 0) && K % kGK == 0) {
-    dim3 grid(P.ncol / kGN, (M + kGM - 1) / kGM);
-    hipLaunchKernelGGL(k_proj_gemm, grid, dim3(256), 0, st, (const uint16_t*)x, M, K, wc, P.ncol, part);
-  } else if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16) {
+             (P.ratio != 4 || P.DI % kGN == 0) && K % kGK == 0 && c_begin % kGN == 0 && nc % kGN == 0) {
+    dim3 grid(nc / kGN, (M + kGM - 1) / kGM);
+    hipLaunchKernelGGL(k_proj_gemm, grid, dim3(256), 0, st, (const uint16_t*)x, M, K, wc, P.ncol, part, c_begin);
+  } else if (P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && c_begin % 64 == 0) {
     const int klen = ((K / splits) + 31) / 32 * 32;
-    dim3 grid((P.ncol + 63) / 64, splits, (M + 31) / 32);
-    hipLaunchKernelGGL(k_proj_mfma, grid, dim3(256), 0, st, (const uint16_t*)x, M, K, wc, P.ncol,
-                       klen, part);
+    dim3 grid((nc + 63) / 64, splits, (M + 31) / 32);
+    hipLaunchKernelGGL(k_proj_mfma, grid, dim3(256), 0, st, (const uint16_t*)x, M, K, wc, P.ncol, klen, part,
+                       c_begin, c_end);
   } else {
-    dim3 grid(P.ncol, (M + 3) / 4);
-#define CKV_PV(XF, WF)                                                                     \
-  hipLaunchKernelGGL((k_proj_vec<XF, WF>), grid, dim3(64), 0, st, x, M, K, wc, P.ncol, part)
+    dim3 grid(nc, (M + 3) / 4);
+#define CKV_PV(XF, WF)                                                                          \
+  hipLaunchKernelGGL((k_proj_vec<XF, WF>), grid, dim3(64), 0, st, x, M, K, wc, P.ncol, part, c_begin)
     if (P.act_fmt == CKV_F32 && P.w_fmt == CKV_F32) CKV_PV(CKV_F32, CKV_F32);
     else if (P.act_fmt == CKV_F32) CKV_PV(CKV_F32, CKV_BF16);
-    else CKV_PV(CKV_BF16, CKV_F32);
+    else if (P.w_fmt == CKV_F32) CKV_PV(CKV_BF16, CKV_F32);
+    else CKV_PV(CKV_BF16, CKV_BF16);
 #undef CKV_PV
   }
   return (int)hipGetLastError();

@@ -194,3 +194,18 @@ class DeviceLayer:
                                               topk if self.ratio == 4 else None, out, self.ws, self.ws_bytes,
                                               st), "sparse_swa_attn_prefill")
         return out, (topk if self.ratio == 4 else None)
+
+    def prefill_chunk(self, seq: int, pos0: int, x, u, q, qI=None, w=None, out=None, topk=None,
+                      side_stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        """The same chunk as :meth:`prefill` in one call (ckv_prefill_chunk); with
+        ``side_stream`` (a torch stream) the indexer branch runs there beside
+        the attention lane's compression and the raw staging."""
+        T = u.shape[0]
+        out = self.new_out(T) if out is None else out
+        if self.ratio == 4 and topk is None:
+            topk = torch.empty((T, self.k), dtype=torch.int32, device=self.device)
+        side = None if side_stream is None else side_stream.cuda_stream
+        self._check(L.prefill_chunk(self.desc, self.weights, self.cache, x, u, q, qI, w, seq, pos0, T,
+                                    topk if self.ratio == 4 else None, out, self.ws, self.ws_bytes, self._stream(),
+                                    side), "prefill_chunk")
+        return out, (topk if self.ratio == 4 else None)

@@ -406,6 +406,31 @@ int ckv_decode_step(const ckv_layer_desc* desc, const ckv_layer_weights* w, cons
                     const int32_t* pos, int32_t B, int32_t* topk, void* out, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* ---- prefill_chunk: the three prefill calls of one chunk, the indexer
+ * branch on a second stream [P4 "GPU compute saturation": the indexer
+ * pipeline on its own stream beside the main KV compression and the SWA
+ * token insertion] -----------------------------------------------------------
+ *
+ * The result equals ckv_compress_append_prefill, then (ratio 4)
+ * ckv_indexer_topk_prefill, then ckv_sparse_swa_attn_prefill with the same
+ * arguments (x, u as for compress_append; q, out as for sparse_swa_attn; qI,
+ * iw and topk as for indexer_topk, ratio 4 only, else ignored and may be
+ * NULL), bit for bit.  With side_stream NULL or equal to stream, or on a
+ * layer without an indexer, everything runs in that order on `stream`.
+ * Otherwise the side stream (after the work already on `stream`) projects
+ * and pools the indexer lane, then scores and selects, while `stream`
+ * projects and pools the attention lane and stages the raw rows; `stream`
+ * then updates the compressor state and the token count and runs the
+ * attention once the selection is done.  When the call returns, every piece
+ * of the chunk is ordered before later work on `stream`.  The side stream
+ * must not be used to reuse this workspace or cache before `stream` has
+ * passed this call.  The call creates its three ordering events itself (no
+ * device memory).  Error returns as for the three calls. */
+int ckv_prefill_chunk(const ckv_layer_desc* desc, const ckv_layer_weights* w, const ckv_layer_cache* cache,
+                      const void* x, const void* u, const void* q, const void* qI, const float* iw, int32_t seq,
+                      int32_t pos0, int32_t T, int32_t* topk, void* out, void* ws, size_t ws_bytes, void* stream,
+                      void* side_stream);
+
 /* ---- decode_step without a workspace argument ------------------------------
  * For callers that cannot allocate device memory (code under stream capture,
  * tight serving loops, harnesses that forbid allocation).  The same step as

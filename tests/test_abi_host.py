@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -174,6 +174,19 @@ def test_host_errors_before_any_enqueue():
     assert L.compress_append_prefill(d, w, cache(raw_stage=None), FAKE, FAKE, 0, 0, 16, FAKE, wp) == L.CKV_E_INVAL
     assert L.indexer_topk_prefill(d, c, FAKE, FAKE, 0, 0, 5000, FAKE, FAKE, wp) == L.CKV_E_CAPACITY
     assert L.sparse_swa_attn_prefill(d, c, FAKE, 0, 0, 16, FAKE, FAKE, FAKE, 16) == L.CKV_E_WORKSPACE
+    # the single-call prefill chunk: the three calls' checks
+    pc = lambda **k: L.prefill_chunk(k.get("d", d), k.get("w", w), k.get("c", c), k.get("x", FAKE), FAKE,
+                                     k.get("q", FAKE), k.get("qI", FAKE), k.get("iw", FAKE), 0, k.get("pos0", 0),
+                                     k.get("T", 16), k.get("topk", FAKE), k.get("out", FAKE), FAKE, k.get("wsb", wp),
+                                     None, k.get("side", FAKE))
+    assert pc(T=4097) == L.CKV_E_CAPACITY
+    assert pc(pos0=-1) == L.CKV_E_INVAL
+    assert pc(wsb=16) == L.CKV_E_WORKSPACE
+    assert pc(topk=None) == L.CKV_E_INVAL and pc(topk=MIS) == L.CKV_E_INVAL
+    assert pc(qI=None) == L.CKV_E_INVAL and pc(iw=None) == L.CKV_E_INVAL
+    assert pc(x=None) == L.CKV_E_INVAL and pc(out=None) == L.CKV_E_INVAL
+    assert pc(c=cache(stage_rows=100)) == L.CKV_E_CAPACITY
+    assert pc(w=weights(idx_gamma=None)) == L.CKV_E_INVAL
     # the single-call decode step: same checks, all before anything is enqueued
     st = lambda **k: L.decode_step(k.get("d", d), k.get("w", w), k.get("c", c), k.get("x", FAKE), FAKE,
                                    k.get("q", FAKE), k.get("qI", FAKE), k.get("iw", FAKE), FAKE, k.get("B", 16),
