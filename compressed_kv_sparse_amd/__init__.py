@@ -12,3 +12,4 @@ from ._lib import (  # noqa: F401
 )
 from .hc import HCMixer  # noqa: F401
 from .layer import DeviceLayer  # noqa: F401
+from .paged import BlockTable, FreeList, PagePools, rows_per_block  # noqa: F401

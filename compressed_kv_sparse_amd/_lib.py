@@ -35,6 +35,7 @@ CKV_STATIC_WORKSPACE_BYTES = 48 << 20
 CKV_STATUS_BAD_POS = 1
 CKV_STATUS_CAPACITY = 2
 CKV_STATUS_SEQUENCE = 4
+CKV_STATUS_PAGE = 8
 
 
 class LayerDesc(ctypes.Structure):
@@ -60,6 +61,7 @@ class LayerCache(ctypes.Structure):
         ("st_kv", ctypes.c_void_p), ("st_sc", ctypes.c_void_p), ("ist_kv", ctypes.c_void_p),
         ("ist_sc", ctypes.c_void_p), ("raw_stage", ctypes.c_void_p), ("stage_rows", ctypes.c_int32),
         ("status", ctypes.c_void_p), ("n_tokens", ctypes.c_void_p), ("n_tokens_host", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("n_pages", ctypes.c_int32),
     ]
 
 

@@ -58,6 +58,16 @@ int prologue(const ckv_layer_desc* d, const ckv_layer_cache* c, LayerParams* P) 
   if (P->ratio == 4) {
     if (check_ptr(c->idx) || check_ptr(c->ist_kv) || check_ptr(c->ist_sc)) return CKV_E_INVAL;
   }
+  P->blocks = nullptr;
+  if (P->ratio && c->block_table) {   // paged: 256 token positions a block
+    const int rpb = 256 / P->ratio;
+    if ((uintptr_t)c->block_table & 3u || c->n_pages < 1) return CKV_E_INVAL;
+    if (P->cap % rpb) return CKV_E_UNSUPPORTED;
+    P->blocks = c->block_table;
+    P->n_pages = c->n_pages;
+    P->max_blocks = P->cap / rpb;
+    P->rpb_shift = P->ratio == 4 ? 6 : 1;
+  }
   return CKV_OK;
 }
 

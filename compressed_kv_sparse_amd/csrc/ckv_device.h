@@ -231,6 +231,32 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 
 // ---------------------------------------------------------------- format IO
 
+// ---- row slots of the compressed caches -------------------------------------
+// Compressed row i of sequence b sits at slot b * cap + i of a contiguous
+// cache.  A paged cache ("vLLM DeepSeek V4", KV cache memory management: one
+// logical block of 256 token positions for every compressed layer) keeps it
+// at slot page * rpb + i % rpb of its page pools, rpb = 256 / ratio rows a
+// page, page = blocks[b * max_blocks + i / rpb]; the K=V and the indexer rows
+// of a c4a layer share the page index.  An entry outside the pool gives -1.
+__device__ __forceinline__ long long row_slot(const LayerParams& P, int b, int i) {
+  if (!P.blocks) return (long long)b * P.cap + i;
+  const int pg = P.blocks[(size_t)b * P.max_blocks + (i >> P.rpb_shift)];
+  const int m = (1 << P.rpb_shift) - 1;
+  return (pg >= 0 && pg < P.n_pages) ? ((long long)pg << P.rpb_shift) + (i & m) : -1;
+}
+// the slot a read takes: a bad entry reads page 0 (the write that stored the
+// row reported it)
+__device__ __forceinline__ long long row_slot_rd(const LayerParams& P, int b, int i) {
+  const long long s = row_slot(P, b, i);
+  return s >= 0 ? s : (long long)(i & ((1 << P.rpb_shift) - 1));
+}
+// the slot a store takes, or -1 after flagging the sequence
+__device__ __forceinline__ long long row_slot_wr(const LayerParams& P, uint32_t* status, int b, int i) {
+  const long long s = row_slot(P, b, i);
+  if (s < 0 && status) atomicOr(&status[b], CKV_STATUS_PAGE);
+  return s;
+}
+
 template <int FMT>
 __device__ __forceinline__ float load_val(const void* p, long i) {
   if constexpr (FMT == CKV_F32) return ((const float*)p)[i];

@@ -32,6 +32,11 @@ struct LayerParams {
   double theta[32];    // RoPE frequencies of the raw class: base^(-2j/n_rot), j < n_rot/2
   double theta_c[32];  // the compressed class (compressed rows, indexer rows, indexer query)
   int two_bases;       // theta_c differs from theta (one frame per row class)
+  // paged layout (cache->block_table): page table, pages per pool, table
+  // columns per sequence, log2 of the compressed rows a page holds; blocks
+  // NULL: contiguous [batch, cap] rows
+  const int32_t* blocks;
+  int n_pages, max_blocks, rpb_shift;
 };
 
 struct Weights {

@@ -519,7 +519,8 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
     const float ss = cmp::block_sum_max(own ? y.x * y.x + y.y * y.y : 0.f, 0.f, red).x;
     const float inv = norm_inv(P, ss, d);
     const float2 z = rope2t(make_float2(gm.x * (y.x * inv), gm.y * (y.y * inv)), c, d, P.n_rot, rtab + 32, rtab + 96);
-    store_row2<KVF>(cc.comp + ((size_t)b * P.cap + i) * P.row_bytes, z, c, own, d, P.n_rot, red);
+    const long long slot = row_slot_wr(P, tid == 0 ? cc.status : nullptr, b, i);
+    if (slot >= 0) store_row2<KVF>(cc.comp + slot * P.row_bytes, z, c, own, d, P.n_rot, red);
   }
   if (W == 8) {  // indexer lane: its own compressor of the same form
     const float ss = cmp::block_sum_max(own && ilane ? yi.x * yi.x + yi.y * yi.y : 0.f, 0.f, red).x;
@@ -527,8 +528,11 @@ __device__ __forceinline__ int compress_decode_seq(const LayerParams& P, const W
     if (own && ilane) {
       const float2 z = rope2t(make_float2(gmi.x * (yi.x * inv), gmi.y * (yi.y * inv)), c, DI, P.idx_rot, rtab + 32,
                               rtab + 96);
-      uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * P.idx_row_bytes;
-      if (IDXF == CKV_F32) {
+      const long long slot = row_slot_wr(P, c == 0 ? cc.status : nullptr, b, i);
+      uint8_t* dst = (uint8_t*)cc.idx + (slot < 0 ? 0 : slot) * P.idx_row_bytes;
+      if (slot < 0) {
+        // (a block-table entry outside the pool: the row is not stored)
+      } else if (IDXF == CKV_F32) {
         *(float2*)(dst + 4 * c) = z;
         if (idx_row) {
           idx_row[c] = z.x;
@@ -738,23 +742,29 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
       const float inv = roleA ? norm_inv(P, sA, d) : norm_inv(P, sI, DI);
       const float z = rope1t(gm * y * inv, col, width, roleA ? P.n_rot : P.idx_rot, rtab + 32, rtab + 96);
       if (roleA) {
-        uint8_t* dst = cc.comp + ((size_t)b * P.cap + i) * P.row_bytes;
+        const long long slot = row_slot_wr(P, tid == 0 ? cc.status : nullptr, b, i);
         const float amax = mA * inv;
         const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-        put_chan<KVF>(dst, z, col, dn, sc);
-        if (KVF == CKV_E4M3 && tid == 0) *(float*)(dst + dn + 2 * P.n_rot) = sc;
+        if (slot >= 0) {
+          uint8_t* dst = cc.comp + slot * P.row_bytes;
+          put_chan<KVF>(dst, z, col, dn, sc);
+          if (KVF == CKV_E4M3 && tid == 0) *(float*)(dst + dn + 2 * P.n_rot) = sc;
+        }
       } else if (roleI) {
         if constexpr (IDXF == CKV_FP4) {
           idx_row[col] = z;   // encoded below
         } else {
-          uint8_t* dst = (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * P.idx_row_bytes;
+          const long long slot = row_slot(P, b, i);   // (the attention role reports a bad entry)
           float zs = z;
           if constexpr (IDXF == CKV_F32) {
-            ((float*)dst)[col] = z;
+            zs = z;
           } else {
-            const uint32_t h = f32_to_bf16(z);
-            ((uint16_t*)dst)[col] = (uint16_t)h;
-            zs = bf16_to_f32(h);
+            zs = bf16_to_f32(f32_to_bf16(z));
+          }
+          if (slot >= 0) {
+            uint8_t* dst = (uint8_t*)cc.idx + slot * P.idx_row_bytes;
+            if constexpr (IDXF == CKV_F32) ((float*)dst)[col] = z;
+            else ((uint16_t*)dst)[col] = (uint16_t)f32_to_bf16(z);
           }
           if (idx_row) idx_row[col] = zs;
         }
@@ -766,7 +776,9 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
     // idx_row then holds the stored (decoded) values
     if (pool) {
       lds_barrier();
-      if (wave == 0) fp4_store_row(idx_row, (uint8_t*)cc.idx + ((size_t)b * P.cap + i) * kFp4RowBytes, idx_row);
+      const long long slot = row_slot(P, b, i);
+      if (wave == 0) fp4_store_row(idx_row, (uint8_t*)cc.idx + (slot < 0 ? 0 : slot) * kFp4RowBytes, idx_row,
+                                   slot >= 0);
     }
   }
   return pool ? 1 : 0;

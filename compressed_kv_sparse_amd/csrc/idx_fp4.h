@@ -234,9 +234,10 @@ __device__ __forceinline__ uint32_t mxfp4_x8(const float (&v)[8], uint32_t& scal
 
 // Encode one indexer row held in LDS (z[0..127], after its RoPE) and store
 // the 68-byte record at dst; called by a whole wave (every 16-lane row
-// computes the row; lanes 0-15 store it).  With rt != NULL the decoded values
-// (Hadamard domain) are written to rt[0..127] by the same lanes (rt may be z).
-__device__ __forceinline__ void fp4_store_row(const float* z, uint8_t* dst, float* rt) {
+// computes the row; lanes 0-15 store it, unless store is false).  With rt !=
+// NULL the decoded values (Hadamard domain) are written to rt[0..127] by the
+// same lanes (rt may be z).
+__device__ __forceinline__ void fp4_store_row(const float* z, uint8_t* dst, float* rt, bool store = true) {
   const int lane = threadIdx.x & 63, s = lane & 15;
   const float4 t0 = *(const float4*)(z + 8 * s), t1 = *(const float4*)(z + 8 * s + 4);
   float v[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
@@ -245,8 +246,10 @@ __device__ __forceinline__ void fp4_store_row(const float* z, uint8_t* dst, floa
   const uint32_t codes = mxfp4_x8(v, sb);
   if (rt) fp4_decode8(codes, sb, v);
   if (lane < 16) {
-    *(uint32_t*)(dst + 4 * s) = codes;
-    if ((s & 3) == 0) dst[64 + (s >> 2)] = (uint8_t)sb;
+    if (store) {
+      *(uint32_t*)(dst + 4 * s) = codes;
+      if ((s & 3) == 0) dst[64 + (s >> 2)] = (uint8_t)sb;
+    }
     if (rt) {
       *(float4*)(rt + 8 * s) = make_float4(v[0], v[1], v[2], v[3]);
       *(float4*)(rt + 8 * s + 4) = make_float4(v[4], v[5], v[6], v[7]);

@@ -64,7 +64,7 @@ __device__ __forceinline__ const uint8_t* attn_row(const LayerParams& P, const C
   } else {
     row = jj;
   }
-  return c.comp + ((size_t)a.seq * P.cap + row) * P.row_bytes;
+  return c.comp + row_slot_rd(P, a.seq, row) * P.row_bytes;
 }
 
 // First index of the top-k list holding a row >= V (the list ends there).
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
         const int row = tkv[e];
         const bool ok = jj < tk_end && row >= 0 && row < A.V;
         if (ok) any_row = 1;
-        rtab[x] = ok ? (uint64_t)(cc.comp + ((size_t)A.seq * P.cap + row) * P.row_bytes) : ((uint64_t)dummy | 1u);
+        rtab[x] = ok ? (uint64_t)(cc.comp + row_slot_rd(P, A.seq, row) * P.row_bytes) : ((uint64_t)dummy | 1u);
       }
     }
   }
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
   // address of ratio-128 compressed entry j (list index)
   auto comp_addr = [&](int j) -> uint64_t {
     const int jj = j - SWA;
-    return (j < j1 && jj < A.V) ? (uint64_t)(cc.comp + ((size_t)A.seq * P.cap + jj) * P.row_bytes)
+    return (j < j1 && jj < A.V) ? (uint64_t)(cc.comp + row_slot_rd(P, A.seq, jj) * P.row_bytes)
                                 : ((uint64_t)dummy | 1u);
   };
   // address of split entry x (any x, for the fp32 recompute)

@@ -207,8 +207,11 @@ __global__ __launch_bounds__(256) void k_c128a_finish(LayerParams P, Weights w, 
       rope_cs_c(P, (c - dn) >> 1, (double)i * 128, &cs, &sn);
       z = make_float2(z.x * cs - z.y * sn, z.x * sn + z.y * cs);
     }
-    uint8_t* dst = cc.comp + ((size_t)b * P.cap + i) * P.row_bytes;
-    if constexpr (KVF == CKV_E4M3) {
+    const long long slot = row_slot_wr(P, tid == 0 ? cc.status : nullptr, b, i);
+    uint8_t* dst = cc.comp + (slot < 0 ? 0 : slot) * P.row_bytes;
+    if (slot < 0) {
+      // (a block-table entry outside the pool: the row is not stored)
+    } else if constexpr (KVF == CKV_E4M3) {
       const float amax = mx * inv;
       const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
       if (act) {
@@ -291,7 +294,8 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
     __syncthreads();
     rope_lds(P, zs, d, P.n_rot, (double)i * r, true);
     __syncthreads();
-    store_row<KVF>(cc.comp + ((size_t)seq * P.cap + i) * P.row_bytes, zs, d, P.n_rot, red);
+    const long long slot = row_slot_wr(P, threadIdx.x == 0 ? cc.status : nullptr, seq, i);
+    if (slot >= 0) store_row<KVF>(cc.comp + slot * P.row_bytes, zs, d, P.n_rot, red);
   }
   if (r != 4 || !(lanes & 2)) return;
   const float* ikv = cc.ist_kv + (size_t)seq * 8 * DI;
@@ -318,7 +322,9 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
   __syncthreads();
   rope_lds(P, zi, DI, P.idx_rot, (double)i * r, true);
   __syncthreads();
-  uint8_t* dst = (uint8_t*)cc.idx + ((size_t)seq * P.cap + i) * P.idx_row_bytes;
+  const long long slot = row_slot_wr(P, threadIdx.x == 0 ? cc.status : nullptr, seq, i);
+  if (slot < 0) return;
+  uint8_t* dst = (uint8_t*)cc.idx + slot * P.idx_row_bytes;
   if constexpr (IDXF == CKV_FP4) {
     if (threadIdx.x < 64) fp4_store_row(zi, dst, nullptr);
   } else {

@@ -100,11 +100,64 @@ constexpr int kScoreBufs = 2;
 // last row block of a query can run past it); written, never read.
 __device__ uint32_t g_key_sink[64];
 
+// Rows of a scan block: rows rb0 + 64 j + q (rb0 a multiple of 64, q < 64)
+// of sequence seq, rows past V - 1 clamped to it (their keys are never read).
+// Contiguous caches: the sequence's rows in order.  Paged caches (PAGED: 64
+// indexer rows a page, NT * 64 pages a block): lane l keeps the addresses of
+// pages l, 64 + l, .. of the block as the table names them (an entry outside
+// the pool reads page 0), loaded once before any row; a wave takes a page's
+// address from that lane with a lane read, so the row loads need no table
+// access of their own.  j is the same in the whole wave.
+template <bool PAGED, int NT = 1>
+struct ScanRows;
+
+template <int NT>
+struct ScanRows<false, NT> {
+  const uint8_t* base;
+  int rb0, vlast;
+  __device__ __forceinline__ ScanRows(const LayerParams& P, const void* idx, int seq, int rb0_, int vlast_,
+                                      int row_bytes)
+      : base((const uint8_t*)idx + (size_t)seq * P.cap * row_bytes), rb0(rb0_), vlast(vlast_) {}
+  __device__ __forceinline__ const uint8_t* row(int j, int q, int row_bytes) const {
+    return base + (size_t)min(rb0 + 64 * j + q, vlast) * row_bytes;
+  }
+};
+
+template <int NT>
+struct ScanRows<true, NT> {
+  uint64_t pb[NT];   // this lane's page addresses
+  int jlast, vin;    // page and in-page index of the last visible row (V - 1)
+  __device__ __forceinline__ ScanRows(const LayerParams& P, const void* idx, int seq, int rb0, int vlast,
+                                      int row_bytes) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int blk = min((rb0 >> 6) + 64 * t + (int)(threadIdx.x & 63), P.max_blocks - 1);
+      int pg = P.blocks[(size_t)seq * P.max_blocks + blk];
+      pg = (pg >= 0 && pg < P.n_pages) ? pg : 0;
+      pb[t] = (uint64_t)((const uint8_t*)idx + (size_t)pg * 64 * row_bytes);
+    }
+    jlast = (vlast >> 6) - (rb0 >> 6);
+    vin = vlast & 63;
+  }
+  __device__ __forceinline__ const uint8_t* row(int j, int q, int row_bytes) const {
+    const int jj = __builtin_amdgcn_readfirstlane(min(j, jlast));
+    uint64_t a = pb[0];
+#pragma unroll
+    for (int t = 1; t < NT; ++t)
+      if (jj >= 64 * t) a = pb[t];
+    const int l = jj & 63;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)a, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(a >> 32), l);
+    const int qq = jj == jlast ? min(q, vin) : q;
+    return (const uint8_t*)(((uint64_t)hi << 32) | lo) + (size_t)qq * row_bytes;
+  }
+};
+
 // The body as a device function: block (bx, qn) of the grid above.
 // old_only: the rows of the query's cache except the row its own token
 // closes (a decode step whose compressor runs concurrently scores that row
 // separately).
-template <int MT, int KS, int QF, bool HIST, int NG = kScoreGroups>
+template <int MT, int KS, int QF, bool HIST, int NG = kScoreGroups, bool PAGED = false>
 __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint16_t* idx, const void* __restrict__ qI,
                                                 const float* __restrict__ wt, const int32_t* __restrict__ pos,
                                                 int seq_fixed, int pos0, uint32_t* __restrict__ keys,
@@ -123,8 +176,8 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int HI = P.HI, nrot = P.idx_rot, dn = DI - nrot;
-  const uint16_t* base = idx + (size_t)Q.seq * P.cap * DI;
   const int vlast = Q.V - 1;
+  const ScanRows<PAGED> rows(P, idx, Q.seq, rb0, vlast, 2 * DI);
 
   // the query: MT chunks of 8 channels per thread (chunk ci = tid + 256 e is
   // head ci / (DI/8), channels 8 (ci % (DI/8)) .. +7); heads past H_I read head
@@ -151,8 +204,7 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
   auto load = [&](u32x4(&Bv)[4][KS], int gi) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int row = min(rb0 + 256 * gi + wave * 64 + 16 * t + r, vlast);
-      const uint16_t* rp = base + (size_t)row * DI + 8 * g;
+      const uint16_t* rp = (const uint16_t*)rows.row(4 * gi + wave, 16 * t + r, 2 * DI) + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) Bv[t][ks] = *(const u32x4*)(rp + 32 * ks);
     }
@@ -278,7 +330,7 @@ __device__ __forceinline__ void idx_score_block(const LayerParams& P, const uint
 // MT tiles back.  The query's loads go out before the rows', so waiting for
 // them does not wait for the rows (loads complete in order).
 
-template <int MT, bool HIST, int NG = kScoreGroups>
+template <int MT, bool HIST, int NG = kScoreGroups, bool PAGED = false>
 __device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const uint8_t* idx,
                                                     const void* __restrict__ qI, const float* __restrict__ wt,
                                                     const int32_t* __restrict__ pos, int seq_fixed, int pos0,
@@ -298,8 +350,8 @@ __device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int HI = P.HI;
-  const uint8_t* base = idx + (size_t)Q.seq * P.cap * kFp4RowBytes;
   const int vlast = Q.V - 1;
+  const ScanRows<PAGED> rows(P, idx, Q.seq, rb0, vlast, kFp4RowBytes);
 
   // the query first: head tile (wave % MT), 32 channels per lane; heads past
   // H_I read head H_I - 1 and are zeroed below
@@ -318,8 +370,7 @@ __device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const 
   auto load = [&](u32x4(&Bc)[4], uint32_t(&Bs)[4], int gi) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int row = min(rb0 + 256 * gi + wave * 64 + 16 * t + r, vlast);
-      const uint8_t* rp = base + (size_t)row * kFp4RowBytes;
+      const uint8_t* rp = rows.row(4 * gi + wave, 16 * t + r, kFp4RowBytes);
       Bc[t] = *(const u32x4_a4*)(rp + 16 * g);
       Bs[t] = *(const uint32_t*)(rp + 64);
     }
@@ -429,21 +480,22 @@ __device__ __forceinline__ void idx_score_block_fp4(const LayerParams& P, const 
   }
 }
 
-template <int MT, bool HIST>
+template <int MT, bool HIST, bool PAGED = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_idx_score_fp4(LayerParams P, const uint8_t* idx, const void* __restrict__ qI,
                                                        const float* __restrict__ wt, const int32_t* __restrict__ pos,
                                                        int seq_fixed, int pos0, uint32_t* __restrict__ keys,
                                                        uint32_t* __restrict__ hist) {
-  idx_score_block_fp4<MT, HIST, kFp4Groups>(P, idx, qI, wt, pos, seq_fixed, pos0, keys, hist, blockIdx.x, blockIdx.y,
-                                            false, nullptr);
+  idx_score_block_fp4<MT, HIST, kFp4Groups, PAGED>(P, idx, qI, wt, pos, seq_fixed, pos0, keys, hist, blockIdx.x,
+                                                   blockIdx.y, false, nullptr);
 }
 
-template <int MT, int KS, int QF, bool HIST>
+template <int MT, int KS, int QF, bool HIST, bool PAGED = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_idx_score_mfma(
     LayerParams P, const uint16_t* idx, const void* __restrict__ qI, const float* __restrict__ wt,
     const int32_t* __restrict__ pos, int seq_fixed, int pos0, uint32_t* __restrict__ keys,
     uint32_t* __restrict__ hist) {
-  idx_score_block<MT, KS, QF, HIST>(P, idx, qI, wt, pos, seq_fixed, pos0, keys, hist, blockIdx.x, blockIdx.y, false);
+  idx_score_block<MT, KS, QF, HIST, kScoreGroups, PAGED>(P, idx, qI, wt, pos, seq_fixed, pos0, keys, hist, blockIdx.x,
+                                                         blockIdx.y, false);
 }
 
 // ---------------------------------------------------------------- prefill score GEMM
@@ -517,7 +569,7 @@ __device__ __forceinline__ float rows4_sum_scatter(float s0, float s1, float s2,
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-template <int MT>
+template <int MT, bool PAGED = false>
 __global__ __launch_bounds__(64 * kPfQ) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_idx_score_prefill(
     LayerParams P, const uint16_t* idx, const uint16_t* __restrict__ qI, const float* __restrict__ wt, int seq,
     int pos0, int T, uint32_t* __restrict__ keys) {
@@ -536,17 +588,21 @@ __global__ __launch_bounds__(64 * kPfQ) __attribute__((amdgpu_waves_per_eu(4, 4)
   const int ntile = min(kPfTiles, (vmax - row0 + kPfRows - 1) / kPfRows);
   const int HI = P.HI, dn = DI - P.idx_rot;
   const int n = min(n0 + wave, T - 1);   // waves past the chunk redo its last query
-  const uint16_t* base = idx + (size_t)seq * P.cap * DI;
   const int vlast = vmax - 1;
+  // the run's rows: 128 pages of 64 (two a tile)
+  static_assert(kPfRows * kPfTiles == 128 * 64 && kPfRows == 128, "two lane tables of 64 pages");
+  const ScanRows<PAGED, 2> rows(P, idx, seq, row0, vlast, 2 * DI);
 
   // direct loads of tile rb into buffer buf: instruction e of this wave fills
-  // rows 4 (kPfQ e + wave) .. + 3
+  // rows 4 (kPfQ e + wave) .. + 3, which lie in the tile's page e / 2 (a page
+  // the whole wave shares)
   auto load_tile = [&](int buf, int rb) {
 #pragma unroll
     for (int e = 0; e < kPfRows / (4 * kPfQ); ++e) {
       const int R = 4 * (kPfQ * e + wave) + (lane >> 4);
       const int q = (lane & 15) ^ (R & 15);
-      lds_dma16(base + (size_t)min(rb + R, vlast) * DI + 8 * q, tiles + buf * TB + 1024 * (kPfQ * e + wave));
+      const uint8_t* rp = rows.row(((rb - row0) >> 6) + (e >> 1), R & 63, 2 * DI);
+      lds_dma16(rp + 16 * q, tiles + buf * TB + 1024 * (kPfQ * e + wave));
     }
   };
   load_tile(0, row0);
@@ -684,7 +740,7 @@ __global__ __launch_bounds__(256) void k_idx_score_vec(LayerParams P, const void
   const bool relu = !(P.flags & CKV_FLAG_IDX_NO_RELU);
   const int row = rb0 + tid;
   if (row < Q.V) {
-    const size_t ro = ((size_t)Q.seq * P.cap + row) * DI;
+    const size_t ro = (size_t)row_slot_rd(P, Q.seq, row) * DI;
     float s = 0.f;
     for (int h = 0; h < HI; ++h) {
       float dot = 0.f;
@@ -1561,7 +1617,7 @@ __global__ __launch_bounds__(1024) void k_topk_decode(LayerParams P, const uint3
 // columns x 16 rows each, 4 waves over one of kProjSlices K slices); the
 // others score the query's cache rows except the row its own token closes,
 // building the key histogram.
-template <int MT, int QF, int IDXF>
+template <int MT, int QF, int IDXF, bool PAGED = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_step_scan(
     LayerParams P, const void* idx, const void* __restrict__ qI, const float* __restrict__ wt,
     const int32_t* __restrict__ pos, uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
@@ -1579,11 +1635,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const int i = kStepProjLast ? bid : bid - nproj;
   if constexpr (IDXF == CKV_FP4)
-    idx_score_block_fp4<MT, true, kFp4StepGroups>(P, (const uint8_t*)idx, qI, wt, pos, 0, 0, keys, hist, i % nrb,
-                                                  i / nrb, true, qf4);
+    idx_score_block_fp4<MT, true, kFp4StepGroups, PAGED>(P, (const uint8_t*)idx, qI, wt, pos, 0, 0, keys, hist,
+                                                         i % nrb, i / nrb, true, qf4);
   else
-    idx_score_block<MT, 4, QF, true, kStepGroups>(P, (const uint16_t*)idx, qI, wt, pos, 0, 0, keys, hist, i % nrb,
-                                                  i / nrb, true);
+    idx_score_block<MT, 4, QF, true, kStepGroups, PAGED>(P, (const uint16_t*)idx, qI, wt, pos, 0, 0, keys, hist,
+                                                         i % nrb, i / nrb, true);
 }
 
 // k_step_select: one block of 1024 threads per sequence.  The indexer query
@@ -1751,9 +1807,13 @@ int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache&
   const int MT = (P.HI + 15) / 16;
   dim3 grid(nproj + nrb * B);
   const bool fp4 = P.idx_fmt == CKV_FP4;
-#define CKV_SS(MTV, IF)                                                                                        \
-  launch_score((k_step_scan<MTV, CKV_BF16, IF>), grid, dim3(256), st, P, (const void*)c.idx, qI, wt, pos, keys, \
-               sel.hist, (const uint16_t*)x, B, wc, proj, nproj, nrb, sel.qf4)
+#define CKV_SS(MTV, IF)                                                                                          \
+  if (P.blocks)                                                                                                   \
+    launch_score((k_step_scan<MTV, CKV_BF16, IF, true>), grid, dim3(256), st, P, (const void*)c.idx, qI, wt, pos, \
+                 keys, sel.hist, (const uint16_t*)x, B, wc, proj, nproj, nrb, sel.qf4);                           \
+  else                                                                                                            \
+    launch_score((k_step_scan<MTV, CKV_BF16, IF>), grid, dim3(256), st, P, (const void*)c.idx, qI, wt, pos, keys, \
+                 sel.hist, (const uint16_t*)x, B, wc, proj, nproj, nrb, sel.qf4)
 #define CKV_SS_MT(IF)      \
   if (MT == 1) CKV_SS(1, IF); \
   else if (MT == 2) CKV_SS(2, IF); \
@@ -1794,23 +1854,37 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
     const int MT = (P.HI + 15) / 16;
     constexpr int RB = 256 * kFp4Groups;
     dim3 mgrid((unsigned)(vmax > 0 ? (vmax + RB - 1) / RB : 1), nq);
-#define CKV_F4(MTV)                                                                                              \
-  if (hist)                                                                                                      \
-    launch_score(k_idx_score_fp4<MTV, true>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, keys, hist);  \
-  else                                                                                                           \
-    launch_score(k_idx_score_fp4<MTV, false>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, keys, hist)
+#define CKV_F4P(MTV, PG)                                                                                          \
+  if (hist)                                                                                                       \
+    launch_score(k_idx_score_fp4<MTV, true, PG>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, keys, hist); \
+  else                                                                                                            \
+    launch_score(k_idx_score_fp4<MTV, false, PG>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, keys, hist)
+#define CKV_F4(MTV)         \
+  do {                      \
+    if (P.blocks) {         \
+      CKV_F4P(MTV, true);   \
+    } else {                \
+      CKV_F4P(MTV, false);  \
+    }                       \
+  } while (0)
     if (MT == 1) CKV_F4(1);
     else if (MT == 2) CKV_F4(2);
     else if (MT == 3) CKV_F4(3);
     else CKV_F4(4);
 #undef CKV_F4
+#undef CKV_F4P
   } else if (mf && !pos && !hist && P.act_fmt == CKV_BF16) {
     const uint16_t* ix = (const uint16_t*)c.idx;
     const int MT = (P.HI + 15) / 16;
     constexpr int RUN = kPfRows * kPfTiles;
     dim3 pgrid((unsigned)(vmax > 0 ? (vmax + RUN - 1) / RUN : 1), (unsigned)((nq + kPfQ - 1) / kPfQ));
-#define CKV_PF(MTV) \
-  launch_score(k_idx_score_prefill<MTV>, pgrid, dim3(64 * kPfQ), st, P, ix, (const uint16_t*)qI, w, seq, pos0, nq, keys)
+#define CKV_PF(MTV)                                                                                              \
+  if (P.blocks)                                                                                                   \
+    launch_score(k_idx_score_prefill<MTV, true>, pgrid, dim3(64 * kPfQ), st, P, ix, (const uint16_t*)qI, w, seq,  \
+                 pos0, nq, keys);                                                                                 \
+  else                                                                                                            \
+    launch_score(k_idx_score_prefill<MTV>, pgrid, dim3(64 * kPfQ), st, P, ix, (const uint16_t*)qI, w, seq, pos0, \
+                 nq, keys)
     if (MT == 1) CKV_PF(1);
     else if (MT == 2) CKV_PF(2);
     else if (MT == 3) CKV_PF(3);
@@ -1821,13 +1895,21 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
     const int MT = (P.HI + 15) / 16;
     constexpr int RB = 256 * kScoreGroups;
     dim3 mgrid((unsigned)(vmax > 0 ? (vmax + RB - 1) / RB : 1), nq);
-#define CKV_IS(MTV, QF)                                                                                     \
-  if (hist)                                                                                                 \
-    launch_score(k_idx_score_mfma<MTV, 4, QF, true>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, keys, \
-                 hist);                                                                                     \
-  else                                                                                                      \
-    launch_score(k_idx_score_mfma<MTV, 4, QF, false>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, keys, \
-                 hist)
+#define CKV_ISP(MTV, QF, PG)                                                                                  \
+  if (hist)                                                                                                   \
+    launch_score(k_idx_score_mfma<MTV, 4, QF, true, PG>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, \
+                 keys, hist);                                                                                 \
+  else                                                                                                        \
+    launch_score(k_idx_score_mfma<MTV, 4, QF, false, PG>, mgrid, dim3(256), st, P, ix, qI, w, pos, seq, pos0, \
+                 keys, hist)
+#define CKV_IS(MTV, QF)         \
+  do {                          \
+    if (P.blocks) {             \
+      CKV_ISP(MTV, QF, true);   \
+    } else {                    \
+      CKV_ISP(MTV, QF, false);  \
+    }                           \
+  } while (0)
     if (P.act_fmt == CKV_BF16) {
       if (MT == 1) CKV_IS(1, CKV_BF16);
       else if (MT == 2) CKV_IS(2, CKV_BF16);
@@ -1840,6 +1922,7 @@ int launch_idx_score(const LayerParams& P, const Cache& c, const void* qI, const
       else CKV_IS(4, CKV_F32);
     }
 #undef CKV_IS
+#undef CKV_ISP
   } else {
 #define CKV_IV(IF, QF) \
   launch_score(k_idx_score_vec<IF, QF>, grid, dim3(256), st, P, c.idx, qI, w, pos, seq, pos0, keys, hist)

@@ -14,6 +14,7 @@ import numpy as np
 import torch
 
 from . import _lib as L
+from .paged import BlockTable, PagePools, rows_per_block
 
 
 def _dev(a, device) -> torch.Tensor:
@@ -32,7 +33,11 @@ class DeviceLayer:
                  kv_fmt: str = "bf16", idx_fmt: str = "bf16", act_fmt: str = "bf16", w_fmt: str = "bf16",
                  rope_base: float = 160000.0, norm_eps: float = 1e-6, softmax_scale: float = 0.0,
                  flags: int = 0, n_rot: int = 64, swa: int = 128, max_chunk: int = 0,
-                 rope_base_comp: float = 0.0, track_tokens: bool = True, device: str = "cuda"):
+                 rope_base_comp: float = 0.0, track_tokens: bool = True, pages: Optional[PagePools] = None,
+                 device: str = "cuda"):
+        """pages: page pools for a paged compressed cache (256-position
+        blocks through a block table; ratio 4 / 128 only), else contiguous
+        [batch, comp_cap] rows."""
         self.device = torch.device(device)
         self.desc = L.LayerDesc(ratio=ratio, hidden=hidden, head_dim=head_dim, n_rot=n_rot, n_heads=n_heads,
                                 swa=swa, idx_heads=idx_heads, idx_dim=idx_dim, top_k=top_k, comp_cap=comp_cap,
@@ -52,14 +57,25 @@ class DeviceLayer:
         z8 = lambda *s: torch.zeros(s, dtype=torch.uint8, device=dev)
         zf = lambda *s: torch.zeros(s, dtype=torch.float32, device=dev)
         self.raw = z8(batch, swa, self.rb)
-        self.comp = z8(batch, comp_cap, self.rb) if ratio else None
+        self.irb = L.idx_row_bytes(L.FMT[idx_fmt], idx_dim) if ratio == 4 else 0
+        self.paged = pages is not None and ratio != 0
+        self.table = None
+        if self.paged:   # page pools shared with other layers; rows reach them through the block table
+            if pages.kv_row_bytes != self.rb or (ratio == 4 and pages.idx_row_bytes != self.irb):
+                raise ValueError("the page pools' row sizes do not match this layer")
+            self.rpb = rows_per_block(ratio)
+            self.comp = pages.kv_pool(ratio)
+            self.idx = pages.idx_pool() if ratio == 4 else None
+            self.table = BlockTable(pages.free[ratio], batch, comp_cap // self.rpb, device=dev)
+        else:
+            self.comp = z8(batch, comp_cap, self.rb) if ratio else None
+            if ratio == 4 and idx_fmt == "fp4":   # 68-byte MXFP4 records
+                self.idx = z8(batch, comp_cap, self.irb)
+            else:
+                idt = torch.float32 if idx_fmt == "f32" else torch.int16
+                self.idx = torch.zeros((batch, comp_cap, idx_dim), dtype=idt, device=dev) if ratio == 4 else None
         self.st_kv = zf(batch, W, head_dim) if ratio else None
         self.st_sc = zf(batch, W, head_dim) if ratio else None
-        if ratio == 4 and idx_fmt == "fp4":   # 68-byte MXFP4 records
-            self.idx = z8(batch, comp_cap, L.idx_row_bytes(L.CKV_FP4, idx_dim))
-        else:
-            idt = torch.float32 if idx_fmt == "f32" else torch.int16
-            self.idx = torch.zeros((batch, comp_cap, idx_dim), dtype=idt, device=dev) if ratio == 4 else None
         self.ist_kv = zf(batch, 8, idx_dim) if ratio == 4 else None
         self.ist_sc = zf(batch, 8, idx_dim) if ratio == 4 else None
         self.max_chunk = max_chunk
@@ -74,7 +90,9 @@ class DeviceLayer:
             st_kv=self._ptr(self.st_kv), st_sc=self._ptr(self.st_sc), ist_kv=self._ptr(self.ist_kv),
             ist_sc=self._ptr(self.ist_sc), raw_stage=self._ptr(self.stage),
             stage_rows=(max_chunk + swa - 1) if max_chunk else 0, status=self.status.data_ptr(),
-            n_tokens=self.n_tokens.data_ptr() if track_tokens else None, n_tokens_host=None)
+            n_tokens=self.n_tokens.data_ptr() if track_tokens else None, n_tokens_host=None,
+            block_table=self.table.dev.data_ptr() if self.paged else None,
+            n_pages=pages.n_pages(ratio) if self.paged else 0)
         self.weights = None
         self._wt = {}
         nb = max(L.workspace_bytes(self.desc, L.CKV_MODE_DECODE, batch),
@@ -110,15 +128,64 @@ class DeviceLayer:
 
     def load_cache(self, raw=None, comp=None, idx=None, st_kv=None, st_sc=None, ist_kv=None,
                    ist_sc=None, n_tokens=None) -> None:
+        """Copy cache contents in; comp / idx in the contiguous [batch,
+        comp_cap, ...] shape (a paged layer maps every block first and
+        scatters the rows into its pages)."""
         for name, a in (("raw", raw), ("comp", comp), ("idx", idx), ("st_kv", st_kv), ("st_sc", st_sc),
                         ("ist_kv", ist_kv), ("ist_sc", ist_sc), ("n_tokens", n_tokens)):
             if name == "n_tokens" and a is not None:
                 a = np.asarray(a, dtype=np.int32)
             if a is None:
                 continue
+            if self.paged and name in ("comp", "idx"):
+                self._scatter_rows(getattr(self, name), _dev(a, self.device))
+                continue
             dst = getattr(self, name)
             src = _dev(a, self.device)
             dst.view(-1).copy_(src.reshape(-1).view(dst.dtype))
+
+    # -------------------------------------------------------------- paged rows
+    def map_rows(self, b: int, n_rows: int, order=None) -> None:
+        """Paged layers: give sequence b pages for compressed rows 0 ..
+        n_rows - 1 (the blocks of positions 0 .. 256 ceil(n_rows / rpb) - 1)."""
+        self.table.map_blocks(b, -(-n_rows // self.rpb), order)
+
+    def release_sequence(self, b: int) -> None:
+        """Paged layers: return sequence b's pages to the pool."""
+        self.table.release(b)
+
+    def _scatter_rows(self, pool: torch.Tensor, rows: torch.Tensor) -> None:
+        nb = self.cap // self.rpb
+        for b in range(self.batch):
+            self.map_rows(b, self.cap)
+            pages = self.table.dev[b].long()
+            src = rows[b].reshape(nb, -1).view(torch.uint8)
+            pool.view(pool.shape[0], -1).index_copy_(0, pages, src.reshape(nb, -1))
+
+    def _gather_rows(self, pool: torch.Tensor, row_elems: int, dtype) -> torch.Tensor:
+        nb = self.cap // self.rpb
+        out = torch.zeros((self.batch, nb, pool[0].numel()), dtype=torch.uint8, device=self.device)
+        for b in range(self.batch):
+            pg = self.table.dev[b].long()
+            ok = (pg >= 0) & (pg < pool.shape[0])
+            out[b][ok] = pool.view(pool.shape[0], -1)[pg[ok]]
+        return out.view(self.batch, self.cap, -1).view(dtype).view(self.batch, self.cap, row_elems)
+
+    def comp_rows(self) -> torch.Tensor:
+        """The K=V rows as [batch, comp_cap, row_bytes] (paged: gathered from
+        the pages, zeros where a block has no page in the pool)."""
+        if not self.paged:
+            return self.comp
+        return self._gather_rows(self.comp, self.rb, torch.uint8)
+
+    def idx_rows(self) -> torch.Tensor:
+        """The indexer rows in the contiguous layout's shape and type."""
+        if not self.paged:
+            return self.idx
+        if self.idx_fmt == "fp4":
+            return self._gather_rows(self.idx, self.irb, torch.uint8)
+        dt = torch.float32 if self.idx_fmt == "f32" else torch.int16
+        return self._gather_rows(self.idx, self.DI, dt)
 
     # -------------------------------------------------------------- steps
     def _stream(self):

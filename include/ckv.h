@@ -92,6 +92,9 @@ extern "C" {
 #define CKV_STATUS_CAPACITY 2u  /* the row a token closes lies beyond comp_cap  */
 #define CKV_STATUS_SEQUENCE 4u  /* position is not the sequence's next token
                                    (cache->n_tokens); the token was not stored */
+#define CKV_STATUS_PAGE 8u      /* a compressed row's block-table entry lies
+                                   outside the page pool; the row was not
+                                   stored                                      */
 
 /* ---- formats -------------------------------------------------------------- */
 #define CKV_F32 0
@@ -216,7 +219,9 @@ typedef struct ckv_layer_weights {
  *   raw        [batch, swa, row_bytes]      raw rows, token t in slot t % swa,
  *                                           stored RoPE'd at t      [P1 s2, s7]
  *   comp       [batch, comp_cap, row_bytes] compressed row i at index i
- *   idx        [batch, comp_cap, idx_dim]   indexer rows (ratio 4)
+ *              (paged: see block_table)
+ *   idx        [batch, comp_cap, idx row]   indexer rows (ratio 4; paged: see
+ *                                           block_table)
  *   st_kv, st_sc   [batch, W, head_dim] float32: compressor window state,
  *                  token t's (kappa, sigma) in slot t % W          [P1 s5; P4]
  *   ist_kv, ist_sc [batch, 8, idx_dim] float32: indexer compressor state
@@ -237,6 +242,22 @@ typedef struct ckv_layer_weights {
  *              n_tokens.  When given, a prefill call whose pos0 differs from
  *              n_tokens_host[seq] returns CKV_E_SEQUENCE before any enqueue.
  *              The library reads it and never writes it.
+ *   block_table  [batch, comp_cap / rpb] int32 (device), or NULL: the paged
+ *              layout [P4 "KV cache memory management": one logical block
+ *              of 256 token positions for every compressed layer, so rpb =
+ *              256 / ratio rows a block -- 64 on c4a, 2 on c128a].  With a
+ *              table, comp and idx are page pools, comp [n_pages, rpb,
+ *              row_bytes] and idx [n_pages, 64, idx row] (ratio 4: the
+ *              indexer rows use the same page index as the K=V rows), and
+ *              compressed row i of sequence b lives in page block_table[b *
+ *              comp_cap / rpb + i / rpb], slot i % rpb.  comp_cap must be a
+ *              multiple of rpb.  A store to a row whose entry lies outside
+ *              [0, n_pages) is dropped and sets CKV_STATUS_PAGE; a read through
+ *              such an entry reads page 0.  Pages are the caller's to hand out
+ *              (a block needs its page before a call stores or reads its rows);
+ *              the raw window and the compressor state stay per-sequence rings
+ *              keyed by position (the page's sliding-window form of them).
+ *   n_pages    pages in each pool (>= 1 with a table, else ignored).
  * Pointers a layer does not use (comp/state for ratio 0, idx/ist_* unless
  * ratio 4, raw_stage for decode) may be NULL. */
 typedef struct ckv_layer_cache {
@@ -252,6 +273,8 @@ typedef struct ckv_layer_cache {
   uint32_t* status;
   int32_t* n_tokens;
   const int32_t* n_tokens_host;
+  const int32_t* block_table;
+  int32_t n_pages;
 } ckv_layer_cache;
 
 /* ---- utilities (host only, never touch the GPU) --------------------------- */
