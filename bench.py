@@ -49,12 +49,28 @@ def log(*a):
 # --------------------------------------------------------------------------- setup
 
 def make_layer(cfg, wts, cache, max_chunk=0):
-    from compressed_kv_sparse_amd import DeviceLayer
+    """A DeviceLayer holding the drawn cache.  A paged workload gets a pool of
+    its own with every block's page drawn from a seeded permutation (the
+    pages of a sequence scattered over the pool, as after many allocations)."""
+    from compressed_kv_sparse_amd import DeviceLayer, PagePools
+    from compressed_kv_sparse_amd import _lib as L
+    pools = None
+    if cfg.paged and cfg.ratio:
+        nb = cfg.comp_cap // (256 // cfg.ratio)
+        rb = L.row_bytes(L.FMT[cfg.kv_fmt], cfg.head_dim, cfg.n_rot)
+        irb = L.idx_row_bytes(L.FMT[cfg.idx_fmt], cfg.idx_dim) if cfg.ratio == 4 else 0
+        npg = cfg.batch * nb
+        pools = PagePools(kv_row_bytes=rb, idx_row_bytes=irb, pages_c4a=npg if cfg.ratio == 4 else 0,
+                          pages_c128a=npg if cfg.ratio == 128 else 0)
     dl = DeviceLayer(ratio=cfg.ratio, hidden=cfg.hidden, head_dim=cfg.head_dim, n_heads=cfg.n_heads,
                      batch=cfg.batch, idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim, top_k=cfg.top_k,
                      comp_cap=cfg.comp_cap, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt, act_fmt=cfg.act_fmt,
                      w_fmt=cfg.w_fmt, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps, max_chunk=max_chunk,
-                     rope_base_comp=cfg.rope_base_comp or 0.0, flags=cfg.flags)
+                     rope_base_comp=cfg.rope_base_comp or 0.0, flags=cfg.flags, pages=pools)
+    if pools is not None:
+        perm = np.random.default_rng(cfg.seed).permutation(npg)
+        for b in range(cfg.batch):
+            dl.map_rows(b, cfg.comp_cap, order=perm[b * nb:(b + 1) * nb])
     if wts is not None:
         dl.set_weights(wkv=wts.wkv, wgate=wts.wgate, ape=wts.ape, gamma=wts.gamma, idx_wkv=wts.idx_wkv,
                        idx_wgate=wts.idx_wgate, idx_ape=wts.idx_ape, idx_gamma=wts.idx_gamma)
@@ -340,10 +356,11 @@ def bench_sweep(steps, warmup, copies=3, contexts=SWEEP_CONTEXTS):
 
 # --------------------------------------------------------------------------- layer stack
 
-def bench_stack(steps, warmup):
+def bench_stack(steps, warmup, paged=False):
     """The 43-layer Flash stack at 128k context, batch 16: one decode step of
     every layer (window-only, c4a and c128a per the schedule), replayed as one
-    captured HIP graph.  Caches, weights and inputs are seeded device-side draws."""
+    captured HIP graph.  Caches, weights and inputs are seeded device-side draws.
+    paged: the compressed rows in page pools all layers share."""
     import torch
     from compressed_kv_sparse_amd.stack import DeviceStack, StackShape
     from workloads.configs import stack_layer
@@ -351,7 +368,7 @@ def bench_stack(steps, warmup):
     from workloads.gen import context_lengths
 
     t0 = time.time()
-    stk = DeviceStack(StackShape())
+    stk = DeviceStack(StackShape(paged=paged))
     inputs, nbytes = [], 0.0
     for il, dl in enumerate(stk.layers):
         cfg = stack_layer(il)
@@ -394,7 +411,7 @@ def bench_stack(steps, warmup):
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
     B = stk.shape.batch
-    return {"workload": "c5_flash_stack_43L_b16_ctx131072_fp8", "layers": len(stk),
+    return {"workload": "c5_flash_stack_43L_b16_ctx131072_fp8" + ("_paged" if paged else ""), "layers": len(stk),
             "ms_per_step": round(dt * 1e3, 4), "tok_s": round(B / dt, 1), "bytes": int(nbytes),
             "achieved_gbs": round(nbytes / dt / 1e9, 1), "frac": round(nbytes / dt / 1e9 / HBM_PEAK_GBS, 4)}
 
@@ -647,6 +664,8 @@ def main():
         return
     if args.part == "stack":
         print(json.dumps({"part": "stack", **bench_stack(args.stack_steps, 3)}), flush=True)
+        if not args.no_extra:
+            print(json.dumps({"part": "stack", **bench_stack(args.stack_steps, 3, paged=True)}), flush=True)
         return
     cfg = get_config(args.workload)
     r = bench_decode(cfg, args.steps, args.warmup, api=args.api, copies=args.layer_copies)
@@ -667,7 +686,7 @@ def main():
         return
     extra = {}
     if not args.no_extra:
-        for name in ("c2", "c3", "c5_c128a", "c5_swa", "c5_fp4idx", "c5_out8", "c5_qnorm"):
+        for name in ("c2", "c3", "c5_c128a", "c5_swa", "c5_fp4idx", "c5_out8", "c5_qnorm", "c5_paged"):
             e = bench_decode(get_config(name), args.steps, args.warmup, with_kernel=name == "c5_fp4idx",
                              copies=args.layer_copies)
             extra[name] = {k: round(v, 4) for k, v in e.items() if not k.startswith("_") and isinstance(v, float)}
@@ -711,6 +730,10 @@ def main():
         stack = bench_stack(args.stack_steps, 3)
         log(f"[bench] stack {stack['layers']} layers: {stack['ms_per_step']:.3f} ms/step, {stack['tok_s']:.0f} tok/s, "
             f"{100 * stack['frac']:.1f}% of HBM")
+        if not args.no_extra:   # the same stack with every compressed row in shared page pools
+            sp = bench_stack(args.stack_steps, 3, paged=True)
+            stack["paged"] = {k: sp[k] for k in ("workload", "ms_per_step", "tok_s", "frac")}
+            log(f"[bench] stack (paged): {sp['ms_per_step']:.3f} ms/step, {sp['tok_s']:.0f} tok/s")
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, r["_inp"], r["_wts"])

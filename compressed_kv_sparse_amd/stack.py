@@ -14,6 +14,12 @@ order on the current stream, so the whole stack can be captured as one HIP
 graph.  No work is shared between layers: the stack is 43 independent
 single-layer steps, as the attention layers of the model are between their
 (absent) feed-forward blocks.
+
+With ``paged`` the compressed rows of every layer live in pages of pools that
+all layers share, one pool per page size ("vLLM DeepSeek V4", KV cache memory
+management: three page sizes for the whole stack -- c4a K=V pages, c4a indexer
+pages, c128a K=V pages), each layer reaching its pages through its own block
+table.
 """
 from __future__ import annotations
 
@@ -22,7 +28,9 @@ from typing import Dict, List, Optional
 
 import torch
 
+from . import _lib as L
 from .layer import DeviceLayer
+from .paged import BLOCK_TOKENS, PagePools
 
 SCHEDULES = ("flash", "pro")
 
@@ -53,6 +61,7 @@ class StackShape:
     rope_base_raw: float = 10000.0
     rope_base_comp: float = 160000.0
     norm_eps: float = 1e-6
+    paged: bool = False            # compressed rows in shared page pools (block tables)
 
 
 class DeviceStack:
@@ -62,6 +71,14 @@ class DeviceStack:
         self.shape = s = shape
         self.ratios = [layer_ratio(il, s.schedule) for il in range(s.n_layers)]
         self.layers: List[DeviceLayer] = []
+        self.pools = None
+        if s.paged:   # every layer's whole capacity, in pages of the shared pools
+            per_seq = s.n_ctx // BLOCK_TOKENS
+            self.pools = PagePools(
+                kv_row_bytes=L.row_bytes(L.FMT[s.kv_fmt], s.head_dim, 64),
+                idx_row_bytes=L.idx_row_bytes(L.FMT[s.idx_fmt], s.idx_dim),
+                pages_c4a=self.ratios.count(4) * s.batch * per_seq,
+                pages_c128a=self.ratios.count(128) * s.batch * per_seq, device=device)
         for r in self.ratios:
             ci = r == 4
             self.layers.append(DeviceLayer(
@@ -69,7 +86,7 @@ class DeviceStack:
                 idx_heads=s.idx_heads if ci else 0, idx_dim=s.idx_dim if ci else 0,
                 top_k=s.top_k if ci else 0, comp_cap=(s.n_ctx // r) if r else 0, kv_fmt=s.kv_fmt,
                 idx_fmt=s.idx_fmt, rope_base=s.rope_base_comp if r else s.rope_base_raw,
-                norm_eps=s.norm_eps, device=device))
+                norm_eps=s.norm_eps, pages=self.pools, device=device))
 
     def __len__(self) -> int:
         return len(self.layers)

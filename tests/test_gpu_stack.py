@@ -34,11 +34,14 @@ def cpu(t):
     return t.numpy()
 
 
-def test_flash_stack_decode_every_layer():
+@pytest.mark.parametrize("paged", [False, True])
+def test_flash_stack_decode_every_layer(paged):
+    """paged: every layer's compressed rows in pages of pools the 43 layers
+    share (three page sizes), through per-layer block tables."""
     from compressed_kv_sparse_amd.stack import DeviceStack, StackShape
 
     B, n = 2, 4096 + 4          # p = 4099: c4a boundary (row 1024 emitted), c128a mid-window
-    shape = StackShape(batch=B, n_ctx=8192)
+    shape = StackShape(batch=B, n_ctx=8192, paged=paged)
     stk = DeviceStack(shape)
     assert len(stk) == 43
     assert stk.ratios == [O.flash_ratio(il) for il in range(43)]
@@ -68,14 +71,16 @@ def test_flash_stack_decode_every_layer():
     outs, topks = stk.buffers()
     stk.decode(inputs, outs, topks)
     torch.cuda.synchronize()
-    print(f"[stack] 43 layers stepped at p={n - 1}", flush=True)
+    print(f"[stack] 43 layers stepped at p={n - 1} (paged: {paged})", flush=True)
+    if paged:
+        assert len(stk.pools.page_sizes()) == 3
 
     for il, (dl, (cfg, L, inp, seqs, qI, w)) in enumerate(zip(stk.layers, cases)):
         assert int(np.abs(cpu(dl.status)).sum()) == 0, f"layer {il}: status set"
         d, r = cfg.head_dim, cfg.ratio
         raw_g = cpu(dl.raw)
-        comp_g = cpu(dl.comp) if dl.comp is not None else None
-        idx_g = cpu(dl.idx) if dl.idx is not None else None
+        comp_g = cpu(dl.comp_rows()) if dl.comp is not None else None
+        idx_g = cpu(dl.idx_rows()) if dl.idx is not None else None
         for b in range(B):
             p = int(inp.pos[b])
             compare_rows(raw_g[b, p % cfg.swa], seqs[b].raw_row(p)[0], cfg.kv_fmt, d, cfg.n_rot,

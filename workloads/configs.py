@@ -76,6 +76,7 @@ class LayerShape:
     ctx_range: Optional[Tuple[int, int]] = None
     layer: int = 0
     flags: int = 0                    # ckv_layer_desc.flags (e.g. 32: attention output as fp8 records)
+    paged: bool = False               # compressed rows in scattered 256-position pages (block table)
 
     @property
     def window(self) -> int:
@@ -155,6 +156,9 @@ CONFIGS[_c.name] = _c
 # ... and with each head's query RMS-normalised inside the attention
 _c = _c5(4, 2).with_(name="c5_c4a_decode_b16_ctx131072_fp8_qnorm", flags=64)
 CONFIGS[_c.name] = _c
+# ... and with the compressed and indexer rows in scattered pages of a pool
+_c = _c5(4, 2).with_(name="c5_c4a_decode_b16_ctx131072_fp8_paged", paged=True)
+CONFIGS[_c.name] = _c
 
 # short aliases
 ALIASES = {
@@ -169,6 +173,7 @@ ALIASES = {
     "c4_fp4idx": "c4_c4a_prefill_T4096_at61440_bf16_fp4idx",
     "c5_out8": "c5_c4a_decode_b16_ctx131072_fp8_out8",
     "c5_qnorm": "c5_c4a_decode_b16_ctx131072_fp8_qnorm",
+    "c5_paged": "c5_c4a_decode_b16_ctx131072_fp8_paged",
 }
 
 

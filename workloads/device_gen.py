@@ -83,17 +83,24 @@ def fill_layer_cache(dl, cfg) -> None:
     s, L = cfg.seed, cfg.layer
     dl.n_tokens.fill_(cfg.n_ctx - 1)
     fill_rows(dl.raw, cfg.kv_fmt, cfg.head_dim, cfg.n_rot, _gen(s, "raw", L))
+    paged = getattr(dl, "paged", False)   # rows drawn in the contiguous shape, then scattered into pages
     if dl.comp is not None:
-        fill_rows(dl.comp, cfg.kv_fmt, cfg.head_dim, cfg.n_rot, _gen(s, "comp", L))
+        comp = torch.empty((dl.batch, dl.cap, dl.rb), dtype=torch.uint8, device="cuda") if paged else dl.comp
+        fill_rows(comp, cfg.kv_fmt, cfg.head_dim, cfg.n_rot, _gen(s, "comp", L))
+        if paged:
+            dl.load_cache(comp=comp)
         dl.st_kv.normal_(generator=_gen(s, "st_kv", L))
         dl.st_sc.normal_(generator=_gen(s, "st_sc", L))
     if dl.idx is not None:
+        idx = torch.empty_like(dl.idx_rows()) if paged else dl.idx
         if cfg.idx_fmt == "bf16":
-            dl.idx.copy_(bf16_draw(tuple(dl.idx.shape), _gen(s, "idx", L)))
+            idx.copy_(bf16_draw(tuple(idx.shape), _gen(s, "idx", L)))
         elif cfg.idx_fmt == "fp4":
-            fill_fp4_records(dl.idx, cfg.idx_dim, _gen(s, "idx", L))
+            fill_fp4_records(idx, cfg.idx_dim, _gen(s, "idx", L))
         else:
-            dl.idx.normal_(generator=_gen(s, "idx", L))
+            idx.normal_(generator=_gen(s, "idx", L))
+        if paged:
+            dl.load_cache(idx=idx)
         dl.ist_kv.normal_(generator=_gen(s, "ist_kv", L))
         dl.ist_sc.normal_(generator=_gen(s, "ist_sc", L))
 
