@@ -44,7 +44,10 @@ the QAT round trip of P1 s9 read as orthonormal Hadamard-128 then OCP MXFP4
 (E2M1 in blocks of 32 with a power-of-two block scale), applied alike to the
 rotated indexer query; the optional query norm (P4 "GPU compute
 saturation") divides each head's query by its RMS, with no learned weight,
-before the RoPE.
+before the RoPE.  Optionally (two_lane) a ratio-4 compressor is
+two lanes wide: lane A of a token serves the window its block ends, lane B
+the window of its own row (P1 s5, the alternative reading of its lane
+comment).
 
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
@@ -575,6 +578,13 @@ class OracleLayer:
     # query norm of the layer description's flags: each head's attention
     # query RMS-normalised (query_rms_norm) before its RoPE
     q_norm: bool = False
+    # two-lane c4a compressor (P1 s5: a ratio-4 compressor is twice as wide
+    # as its rows): every token projects to two lanes (wkv, wgate [2 w, D]),
+    # lane A serving the window it ends (slots 0-3 of the next row), lane B the
+    # window of its own row (slots 4-7); APE [4, 2 w] holds lane A's slot s in
+    # row s, channels :w, and lane B's in channels w:.  Both compressors of a
+    # ratio-4 layer take it (the indexer's at width D_I).
+    two_lane: bool = False
 
     def rope(self, x, pos, base: float, n_rot: int) -> np.ndarray:
         """rope_tail, or the identity when the layer skips RoPE."""
@@ -605,7 +615,8 @@ def layer_from(cfg, weights) -> OracleLayer:
                     idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim, top_k=cfg.top_k,
                     n_rot=cfg.n_rot, swa=cfg.swa, rope_base=cfg.rope_base,
                     norm_eps=cfg.norm_eps, kv_fmt=cfg.kv_fmt, idx_fmt=cfg.idx_fmt,
-                    act_fmt=cfg.act_fmt, rope_base_comp=getattr(cfg, "rope_base_comp", None))
+                    act_fmt=cfg.act_fmt, rope_base_comp=getattr(cfg, "rope_base_comp", None),
+                    two_lane=bool(getattr(cfg, "two_lane", False)) and cfg.ratio == 4)
     if weights is not None:
         L.wkv = w(weights.wkv, cfg.w_fmt)
         L.wgate = w(weights.wgate, cfg.w_fmt)
@@ -688,14 +699,22 @@ class OracleSequence:
         L = self.L
         ts = window_positions(i, L.ratio)
         kap, sig = (self.kap, self.sig) if lane == "attn" else (self.ikap, self.isig)
-        ape = L.ape if lane == "attn" else L.idx_ape
+        ape = np.asarray(L.ape if lane == "attn" else L.idx_ape, F64)
+        two = L.two_lane and L.ratio == 4
+        if two:   # slot j < 4: lane A (first half), slot j >= 4: lane B (second half)
+            width = ape.shape[1] // 2
+            ape = np.concatenate([ape[:, :width], ape[:, width:]])
         width = ape.shape[1]
         valid = ts >= 0
         kw = np.zeros((len(ts), width))
         sw = np.zeros((len(ts), width))
         for j, t in enumerate(ts):
             if t >= 0:
-                kw[j], sw[j] = kap[int(t)], sig[int(t)]
+                k, sg = kap[int(t)], sig[int(t)]
+                if two:
+                    h = slice(0, width) if j < 4 else slice(width, 2 * width)
+                    k, sg = k[h], sg[h]
+                kw[j], sw[j] = k, sg
         return pool_window(kw, sw, ape, valid)
 
     def _pool_row(self, i: int, lane: str) -> np.ndarray:

@@ -968,3 +968,84 @@ def test_query_norm_in_attention_is_per_head_and_before_rope(ratio):
     rot = O.rope_tail(qr, p, L.base_raw, L.n_rot)
     np.testing.assert_allclose(O.query_rms_norm(rot, 1e-6),
                                O.rope_tail(O.query_rms_norm(qr, 1e-6), p, L.base_raw, L.n_rot), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- two-lane c4a compressor
+# P1 s5: a ratio-4 compressor is twice as wide as its rows.  Reading (the
+# alternative to one lane): each token projects to lanes A and B; a row's
+# window takes lane A of the previous block's four tokens (slots 0-3) and lane
+# B of its own block's (slots 4-7); APE [4, 2 w] holds lane A's slot s in
+# row s, channels :w, lane B's in channels w:.
+
+
+def _two_lane_from(L1):
+    """The two-lane layer whose lanes are both the one-lane layer's weights."""
+    import copy
+    L2 = copy.copy(L1)
+    L2.two_lane = True
+    L2.wkv, L2.wgate = np.vstack([L1.wkv, L1.wkv]), np.vstack([L1.wgate, L1.wgate])
+    L2.ape = np.hstack([L1.ape[:4], L1.ape[4:]])
+    L2.idx_wkv, L2.idx_wgate = np.vstack([L1.idx_wkv, L1.idx_wkv]), np.vstack([L1.idx_wgate, L1.idx_wgate])
+    L2.idx_ape = np.hstack([L1.idx_ape[:4], L1.idx_ape[4:]])
+    return L2
+
+
+def test_two_lane_with_tied_lanes_is_the_one_lane_compressor():
+    L1 = _rand_layer(4, seed=61)
+    L2 = _two_lane_from(L1)
+    X, U, Q, QI, Wt = _history(L1, 300, seed=62)
+    s1, s2 = O.OracleSequence(L1), O.OracleSequence(L2)
+    s1.feed(0, X, U)
+    s2.feed(0, X, U)
+    for i in range(75):
+        np.testing.assert_allclose(s2.comp_row(i)[0], s1.comp_row(i)[0], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(s2.idx_row(i)[0], s1.idx_row(i)[0], rtol=1e-13, atol=1e-13)
+    p = 299
+    np.testing.assert_allclose(s2.query(p, Q[p], QI[p], Wt[p])["out_f64"], s1.query(p, Q[p], QI[p], Wt[p])["out_f64"],
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_two_lane_windows_take_each_lane_once():
+    """Lane B of token t enters row t // 4 only, lane A row t // 4 + 1 only
+    (perturbation of one token's projection, attention and indexer lanes)."""
+    rng = np.random.default_rng(63)
+    L = _two_lane_from(_rand_layer(4, seed=64))
+    L.wkv = L.wkv + 0.3 * rng.standard_normal(L.wkv.shape)        # untie the lanes
+    L.idx_wkv = L.idx_wkv + 0.3 * rng.standard_normal(L.idx_wkv.shape)
+    X, U, *_ = _history(L, 120, seed=65)
+    d, DI = L.head_dim, L.idx_dim
+    t = 53                                                         # row 13, slot 5 of its window
+    for lane, half in (("B", slice(d, 2 * d)), ("A", slice(0, d))):
+        for kind in ("attn", "idx"):
+            base, moved = O.OracleSequence(L), O.OracleSequence(L)
+            base.feed(0, X, U)
+            moved.feed(0, X, U)
+            h = half if kind == "attn" else slice(half.start // d * DI, half.start // d * DI + DI)
+            tab = moved.kap if kind == "attn" else moved.ikap
+            tab[t] = tab[t].copy()
+            tab[t][h] += 5.0
+            moved._row_cache.clear()
+            get = (lambda s, i: s.comp_row(i)[0]) if kind == "attn" else (lambda s, i: s.idx_row(i)[0])
+            own, nxt = t // 4, t // 4 + 1
+            changed = {i for i in range(own - 2, own + 4) if not np.allclose(get(base, i), get(moved, i))}
+            assert changed == ({own} if lane == "B" else {nxt}), (lane, kind, changed)
+
+
+def test_two_lane_ape_slots():
+    """A dominant APE entry picks one token's lane: lane A's slot s is token
+    4 i - 4 + s, lane B's slot s token 4 i + s (one channel, no norm / RoPE)."""
+    L = _two_lane_from(_rand_layer(4, seed=66))
+    L.skip_norm = L.skip_rope = True
+    rng = np.random.default_rng(67)
+    L.wkv = rng.standard_normal(L.wkv.shape)
+    X, U, *_ = _history(L, 80, seed=68)
+    d = L.head_dim
+    i, c = 10, 3
+    for lane, s in (("A", 1), ("B", 2), ("A", 3), ("B", 0)):
+        L.ape = np.zeros((4, 2 * d))
+        L.ape[s, c + (d if lane == "B" else 0)] = 80.0
+        seq = O.OracleSequence(L)
+        seq.feed(0, X, U)
+        t = 4 * i - 4 + s if lane == "A" else 4 * i + s
+        want = seq.kap[t][c + (d if lane == "B" else 0)]
+        assert seq.comp_row(i)[0][c] == pytest.approx(want, rel=1e-12, abs=1e-12), (lane, s)

@@ -77,6 +77,11 @@ class LayerShape:
     layer: int = 0
     flags: int = 0                    # ckv_layer_desc.flags (e.g. 32: attention output as fp8 records)
     paged: bool = False               # compressed rows in scattered 256-position pages (block table)
+    two_lane: bool = False            # ratio 4: two-lane compressors (projections 2 d / 2 D_I, APE [4, 2 w])
+
+    @property
+    def lanes(self) -> int:
+        return 2 if self.two_lane and self.ratio == 4 else 1
 
     @property
     def window(self) -> int:

@@ -176,19 +176,20 @@ def make_layer_weights(cfg: LayerShape) -> Optional[LayerWeights]:
     d, D, W = cfg.head_dim, cfg.hidden, cfg.window
     w_std = cfg.w_std if cfg.w_std is not None else D ** -0.5
     ape_std = cfg.ape_std if cfg.ape_std is not None else d ** -0.5
+    nl = cfg.lanes   # two-lane c4a: projections of 2 d rows, APE [4, 2 d]
     lw = LayerWeights(
-        wkv=draw_values(_rng(s, "wkv", L), (d, D), cfg.w_fmt, w_std),
-        wgate=draw_values(_rng(s, "wgate", L), (d, D), cfg.w_fmt, w_std),
-        ape=_normal32(_rng(s, "ape", L), (W, d), ape_std),
+        wkv=draw_values(_rng(s, "wkv", L), (nl * d, D), cfg.w_fmt, w_std),
+        wgate=draw_values(_rng(s, "wgate", L), (nl * d, D), cfg.w_fmt, w_std),
+        ape=_normal32(_rng(s, "ape", L), (W // nl, nl * d), ape_std),
         gamma=(1.0 + _normal32(_rng(s, "gamma", L), (d,), cfg.gamma_std)).astype(np.float32)
         if cfg.gamma_std else np.ones(d, np.float32),
     )
     if cfg.ratio == 4:
         DI = cfg.idx_dim
         iape_std = cfg.ape_std if cfg.ape_std is not None else DI ** -0.5
-        lw.idx_wkv = draw_values(_rng(s, "idx_wkv", L), (DI, D), cfg.w_fmt, w_std)
-        lw.idx_wgate = draw_values(_rng(s, "idx_wgate", L), (DI, D), cfg.w_fmt, w_std)
-        lw.idx_ape = _normal32(_rng(s, "idx_ape", L), (8, DI), iape_std)
+        lw.idx_wkv = draw_values(_rng(s, "idx_wkv", L), (nl * DI, D), cfg.w_fmt, w_std)
+        lw.idx_wgate = draw_values(_rng(s, "idx_wgate", L), (nl * DI, D), cfg.w_fmt, w_std)
+        lw.idx_ape = _normal32(_rng(s, "idx_ape", L), (8 // nl, nl * DI), iape_std)
         lw.idx_gamma = ((1.0 + _normal32(_rng(s, "idx_gamma", L), (DI,), cfg.gamma_std))
                         .astype(np.float32) if cfg.gamma_std else np.ones(DI, np.float32))
     return lw
@@ -252,18 +253,19 @@ def _draw_cache(cfg: LayerShape, first_live: np.ndarray, empty: bool) -> CacheIn
     comp = idx = st_kv = st_sc = ist_kv = ist_sc = None
     r, W, cap = cfg.ratio, cfg.window, cfg.comp_cap
     n_drawn = np.zeros(B, np.int64)
+    nl = cfg.lanes   # a two-lane state slot holds both lanes of its token
     if r:
         comp = np.zeros((B, cap, rb), np.uint8)
-        st_kv = np.zeros((B, W, d), np.float32)
-        st_sc = np.zeros((B, W, d), np.float32)
+        st_kv = np.zeros((B, W, nl * d), np.float32)
+        st_sc = np.zeros((B, W, nl * d), np.float32)
     if r == 4:
         DI = cfg.idx_dim
         if cfg.idx_fmt == "fp4":
             idx = np.zeros((B, cap, idx_row_bytes("fp4", DI)), np.uint8)
         else:
             idx = np.zeros((B, cap, DI), np.float32 if cfg.idx_fmt == "f32" else np.uint16)
-        ist_kv = np.zeros((B, 8, DI), np.float32)
-        ist_sc = np.zeros((B, 8, DI), np.float32)
+        ist_kv = np.zeros((B, 8, nl * DI), np.float32)
+        ist_sc = np.zeros((B, 8, nl * DI), np.float32)
     if empty:
         return CacheInit(raw, comp, idx, st_kv, st_sc, ist_kv, ist_sc, n_drawn, first_live)
     for b in range(B):
@@ -286,12 +288,12 @@ def _draw_cache(cfg: LayerShape, first_live: np.ndarray, empty: bool) -> CacheIn
         # pending compressor state: tokens [t0 - W, t0) that are >= 0
         ts = np.arange(max(0, t0 - W), t0)
         if len(ts):
-            st_kv[b, ts % W] = _normal32(_rng(s, "st_kv", L, b), (len(ts), d), 1.0)
-            st_sc[b, ts % W] = _normal32(_rng(s, "st_sc", L, b), (len(ts), d), 1.0)
+            st_kv[b, ts % W] = _normal32(_rng(s, "st_kv", L, b), (len(ts), nl * d), 1.0)
+            st_sc[b, ts % W] = _normal32(_rng(s, "st_sc", L, b), (len(ts), nl * d), 1.0)
             if r == 4:
                 ts8 = ts[ts >= t0 - 8]
-                ist_kv[b, ts8 % 8] = _normal32(_rng(s, "ist_kv", L, b), (len(ts8), cfg.idx_dim), 1.0)
-                ist_sc[b, ts8 % 8] = _normal32(_rng(s, "ist_sc", L, b), (len(ts8), cfg.idx_dim), 1.0)
+                ist_kv[b, ts8 % 8] = _normal32(_rng(s, "ist_kv", L, b), (len(ts8), nl * cfg.idx_dim), 1.0)
+                ist_sc[b, ts8 % 8] = _normal32(_rng(s, "ist_sc", L, b), (len(ts8), nl * cfg.idx_dim), 1.0)
     return CacheInit(raw, comp, idx, st_kv, st_sc, ist_kv, ist_sc, n_drawn, first_live)
 
 
