@@ -104,6 +104,7 @@ def decode_step_bytes(cfg, n):
     s_a = 2 if cfg.act_fmt == "bf16" else 4
     s_w = 2 if cfg.w_fmt == "bf16" else 4
     W = cfg.window
+    nl = cfg.lanes   # two-lane compressors: twice the projection and state bytes
     total = 0.0
     for nb in n:
         p = nb - 1
@@ -115,12 +116,12 @@ def decode_step_bytes(cfg, n):
         out_b = H * (d + 4 * (d // 128)) if cfg.flags & 32 else H * d * s_a   # fp8 output records
         b += (min(nb, 128) + C) * rho + H * d * s_a + out_b + d * s_a + rho
         if r:
-            b += D * s_a + 8 * (d + (DI if r == 4 else 0))
+            b += D * s_a + 8 * nl * (d + (DI if r == 4 else 0))
             if (p + 1) % r == 0:
-                b += W * 8 * (d + (DI if r == 4 else 0)) + rho + rho_i
+                b += W * 8 * nl * (d + (DI if r == 4 else 0)) + rho + rho_i
         total += b
     if r:
-        total += 2 * D * (d + (DI if r == 4 else 0)) * s_w + W * 4 * (d + (DI if r == 4 else 0))
+        total += nl * (2 * D * (d + (DI if r == 4 else 0)) * s_w + W * 4 * (d + (DI if r == 4 else 0)))
     return total
 
 
@@ -191,7 +192,7 @@ def recorded_traffic(path, source_hash):
 
 def prefill_flops(cfg, pos0, T):
     d, D, H, HI, DI, k = cfg.head_dim, cfg.hidden, cfg.n_heads, cfg.idx_heads, cfg.idx_dim, cfg.top_k
-    f = 2.0 * T * D * 2 * (d + DI)
+    f = 2.0 * T * D * 2 * (d + DI) * cfg.lanes   # the projections (two-lane compressors: both lanes)
     for p in range(pos0, pos0 + T):
         V = (p + 1) // 4
         f += 2.0 * HI * DI * V + 4.0 * H * d * (min(128, p + 1) + min(k, V))
@@ -686,7 +687,7 @@ def main():
         return
     extra = {}
     if not args.no_extra:
-        for name in ("c2", "c3", "c5_c128a", "c5_swa", "c5_fp4idx", "c5_out8", "c5_qnorm", "c5_paged"):
+        for name in ("c2", "c3", "c5_c128a", "c5_swa", "c5_fp4idx", "c5_out8", "c5_qnorm", "c5_paged", "c5_two_lane"):
             e = bench_decode(get_config(name), args.steps, args.warmup, with_kernel=name == "c5_fp4idx",
                              copies=args.layer_copies)
             extra[name] = {k: round(v, 4) for k, v in e.items() if not k.startswith("_") and isinstance(v, float)}

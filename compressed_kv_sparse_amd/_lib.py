@@ -29,6 +29,7 @@ CKV_FLAG_SKIP_ROPE = 8
 CKV_FLAG_KEEP_F32 = 16
 CKV_FLAG_OUT_FP8 = 32
 CKV_FLAG_Q_NORM = 64
+CKV_FLAG_TWO_LANE = 128
 CKV_MODE_DECODE, CKV_MODE_PREFILL = 0, 1
 CKV_MAX_CHUNK = 4096
 CKV_STATIC_WORKSPACE_BYTES = 48 << 20

@@ -366,7 +366,7 @@ extern "C" int ckv_prefill_chunk(const ckv_layer_desc* desc, const ckv_layer_wei
   // (which the indexer rows' pooling reads: after `pooled`) and runs the
   // attention after `selected`.
   hipStream_t main_st = (hipStream_t)stream, side = (hipStream_t)side_stream;
-  const int ca = 2 * P.d;   // attention-lane columns [0, 2d), indexer lane [2d, ncol)
+  const int ca = 2 * P.lanes * P.d;   // attention compressor's columns [0, ca), the indexer's [ca, ncol)
   Events ev;
   hipEvent_t fork, pooled, selected;
   if ((rc = ev.get(&fork)) || (rc = ev.get(&pooled)) || (rc = ev.get(&selected))) return launched(rc);

@@ -37,6 +37,7 @@ struct LayerParams {
   // NULL: contiguous [batch, cap] rows
   const int32_t* blocks;
   int n_pages, max_blocks, rpb_shift;
+  int lanes;   // compressor lanes: 2 on two-lane c4a layers (CKV_FLAG_TWO_LANE), else 1
 };
 
 struct Weights {

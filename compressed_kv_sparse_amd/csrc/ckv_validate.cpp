@@ -40,7 +40,8 @@ bool make_params(const ckv_layer_desc* d, LayerParams* P) {
   P->scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / sqrt((double)d->head_dim));
   P->W = d->ratio == 4 ? 8 : d->ratio == 128 ? 128 : 0;
   P->row_bytes = (int)ckv_row_bytes(d->kv_fmt, d->head_dim, d->n_rot);
-  P->ncol = d->ratio == 0 ? 0 : 2 * d->head_dim + (d->ratio == 4 ? 2 * d->idx_dim : 0);
+  P->lanes = d->ratio == 4 && (d->flags & CKV_FLAG_TWO_LANE) ? 2 : 1;
+  P->ncol = d->ratio == 0 ? 0 : P->lanes * (2 * d->head_dim + (d->ratio == 4 ? 2 * d->idx_dim : 0));
   P->idx_rot = d->ratio == 4 ? (d->idx_dim < d->n_rot ? d->idx_dim : d->n_rot) : 0;
   P->idx_row_bytes = d->ratio == 4 ? (int)ckv_idx_row_bytes(d->idx_fmt, d->idx_dim) : 0;
   const double base_c = d->rope_base_comp > 0.0 ? d->rope_base_comp : d->rope_base;
@@ -173,8 +174,9 @@ extern "C" int ckv_validate(const ckv_layer_desc* d) {
     return CKV_E_UNSUPPORTED;
   if (d->kv_fmt == CKV_E4M3 && d->head_dim <= d->n_rot) return CKV_E_UNSUPPORTED;
   if (d->flags & ~(CKV_FLAG_NO_INV_ROPE | CKV_FLAG_IDX_NO_RELU | CKV_FLAG_SKIP_NORM | CKV_FLAG_SKIP_ROPE |
-                   CKV_FLAG_KEEP_F32 | CKV_FLAG_OUT_FP8 | CKV_FLAG_Q_NORM))
+                   CKV_FLAG_KEEP_F32 | CKV_FLAG_OUT_FP8 | CKV_FLAG_Q_NORM | CKV_FLAG_TWO_LANE))
     return CKV_E_UNSUPPORTED;
+  if ((d->flags & CKV_FLAG_TWO_LANE) && d->ratio != 4) return CKV_E_UNSUPPORTED;
   // fp8 output: the tiled attention's epilogues only
   if ((d->flags & CKV_FLAG_OUT_FP8) && !(d->act_fmt == CKV_BF16 && d->kv_fmt != CKV_F32 && d->n_heads % 64 == 0 &&
                                           d->head_dim == 512 && d->n_rot == 64))

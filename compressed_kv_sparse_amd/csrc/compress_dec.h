@@ -581,16 +581,21 @@ __device__ __forceinline__ float rope1t(float v, int c, int width, int nrot, con
 // Softmax pooling of one channel over the 8 window positions of row i
 // (window token t0 + j sits in ring slot (t0 + j) % 8 = j ^ F, F = t0 & 4),
 // two passes: the maximum of the valid scores, then exp-weighted sums.  The
-// current token's slot is taken from (kcur, scur).
+// current token's slot is taken from (kcur, scur).  Window positions 0-3 take
+// the ring values (rkA, rsA), positions 4-7 (rkB, rsB): the same arrays for a
+// one-lane compressor, lane A and lane B for a two-lane one (the current
+// token, position 7, is lane B).
 template <int F>
-__device__ __forceinline__ float pool_c4a(const float (&rk)[8], const float (&rs)[8], const float (&ap)[8],
-                                          float kcur, float scur, int t0, int cur) {
+__device__ __forceinline__ float pool_c4a(const float (&rkA)[8], const float (&rsA)[8], const float (&rkB)[8],
+                                          const float (&rsB)[8], const float (&ap)[8], float kcur, float scur,
+                                          int t0, int cur) {
   float e[8];
   float mx = -INFINITY;
 #pragma unroll
   for (int sl = 0; sl < 8; ++sl) {
     const bool valid = t0 + (sl ^ F) >= 0;
-    e[sl] = valid ? (sl == cur ? scur : rs[sl]) + ap[sl ^ F] : -INFINITY;
+    const float rs = (sl ^ F) < 4 ? rsA[sl] : rsB[sl];
+    e[sl] = valid ? (sl == cur ? scur : rs) + ap[sl ^ F] : -INFINITY;
     mx = fmaxf(mx, e[sl]);
   }
   constexpr float kLog2e = 1.4426950408889634f;
@@ -599,7 +604,8 @@ __device__ __forceinline__ float pool_c4a(const float (&rk)[8], const float (&rs
   for (int sl = 0; sl < 8; ++sl) {
     const float wgt = __builtin_amdgcn_exp2f((e[sl] - mx) * kLog2e);
     sw += wgt;
-    acc = fmaf(wgt, sl == cur ? kcur : rk[sl], acc);
+    const float rk = (sl ^ F) < 4 ? rkA[sl] : rkB[sl];
+    acc = fmaf(wgt, sl == cur ? kcur : rk, acc);
   }
   return acc / sw;
 }
@@ -621,7 +627,10 @@ __device__ __forceinline__ float pool_c4a(const float (&rk)[8], const float (&rs
 // as there.
 // rtab: 192 floats (cos / sin of pair j at p raw, at 4 i compressed, at p
 // compressed: [j], [64 + j]; [32 + j], [96 + j]; [128 + j], [160 + j]).
-template <int KVF, int IDXF, int ACTF, typename Issue>
+// NL: compressor lanes (2: CKV_FLAG_TWO_LANE, each token's projections and
+// ring slot hold lane A then lane B, ape row s holds lane A's slot s then lane
+// B's slot 4 + s).
+template <int KVF, int IDXF, int ACTF, int NL = 1, typename Issue>
 __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weights& w, const Cache& cc,
                                                 const void* __restrict__ u, const int32_t* __restrict__ pos,
                                                 const float* __restrict__ proj, int splits, int B, int b,
@@ -634,31 +643,45 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
   const bool roleA = tid < d, roleI = !roleA && tid < d + DI;
   const int col = roleA ? tid : min(tid - d, DI - 1);
   const int width = roleA ? d : DI;
-  float* const skv = roleA ? cc.st_kv + (size_t)b * 8 * d : cc.ist_kv + (size_t)b * 8 * DI;
-  float* const ssc = roleA ? cc.st_sc + (size_t)b * 8 * d : cc.ist_sc + (size_t)b * 8 * DI;
+  const int sw = NL * width;   // ring slot (and APE row) stride
+  float* const skv = roleA ? cc.st_kv + (size_t)b * 8 * NL * d : cc.ist_kv + (size_t)b * 8 * NL * DI;
+  float* const ssc = roleA ? cc.st_sc + (size_t)b * 8 * NL * d : cc.ist_sc + (size_t)b * 8 * NL * DI;
   const float* ape = (roleA ? w.ape : w.idx_ape) + col;
   const float* pj = proj + (size_t)b * P.ncol;
+  const int kb = roleA ? 0 : 2 * NL * d;   // this compressor's kappa columns; sigma from kb + NL * width
 
   // one round of loads: this token's projections (the sum of up to 4 K-slice
   // partials, in slice order; slices past `splits` re-read the last and
   // count zero) and raw input, the ring, the APE rows and the RMSNorm gain
   const int p = pos[b];
   const int nt = seq_tokens(cc, b, p);
-  float ka = 0.f, sa = 0.f;
+  float ka = 0.f, sa = 0.f, kb2 = 0.f, sb2 = 0.f;   // lane A (the only lane at NL = 1), lane B
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float* pq = pj + (size_t)min(q, splits - 1) * B * P.ncol;
-    const float kq = pq[roleA ? col : 2 * d + col], sq = pq[roleA ? d + col : 2 * d + DI + col];
+    const float kq = pq[kb + col], sq = pq[kb + sw + col];
     ka += q < splits ? kq : 0.f;
     sa += q < splits ? sq : 0.f;
+    if constexpr (NL == 2) {
+      const float kq2 = pq[kb + width + col], sq2 = pq[kb + sw + width + col];
+      kb2 += q < splits ? kq2 : 0.f;
+      sb2 += q < splits ? sq2 : 0.f;
+    }
   }
   const float uu = load_val<ACTF>(u, (long)b * d + (roleA ? col : 0));
   float rk[8], rs[8], ap[8];
+  float rkB[NL == 2 ? 8 : 1], rsB[NL == 2 ? 8 : 1];
 #pragma unroll
   for (int sl = 0; sl < 8; ++sl) {
-    rk[sl] = skv[sl * width + col];
-    rs[sl] = ssc[sl * width + col];
-    ap[sl] = ape[sl * width];
+    rk[sl] = skv[sl * sw + col];
+    rs[sl] = ssc[sl * sw + col];
+    if constexpr (NL == 2) {
+      rkB[sl] = skv[sl * sw + width + col];
+      rsB[sl] = ssc[sl * sw + width + col];
+      ap[sl] = ape[(sl & 3) * sw + (sl < 4 ? 0 : width)];   // window position sl
+    } else {
+      ap[sl] = ape[sl * width];
+    }
   }
   const float gm = norm_gamma(P, (roleA ? w.gamma : w.idx_gamma)[col]);
   // this lane's RoPE frequency for the tables below (wave 0: the raw frame in
@@ -691,7 +714,13 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
   }
   float y = 0.f;
   if (wave < nact) {
-    if (pool) y = (t0 & 4) ? pool_c4a<4>(rk, rs, ap, ka, sa, t0, cur) : pool_c4a<0>(rk, rs, ap, ka, sa, t0, cur);
+    if (pool) {
+      if constexpr (NL == 2)
+        y = (t0 & 4) ? pool_c4a<4>(rk, rs, rkB, rsB, ap, kb2, sb2, t0, cur)
+                     : pool_c4a<0>(rk, rs, rkB, rsB, ap, kb2, sb2, t0, cur);
+      else
+        y = (t0 & 4) ? pool_c4a<4>(rk, rs, rk, rs, ap, ka, sa, t0, cur) : pool_c4a<0>(rk, rs, rk, rs, ap, ka, sa, t0, cur);
+    }
     const float gy = gm * y;
     float v0 = roleA ? y * y : 0.f;
     float v1 = roleI ? y * y : 0.f;
@@ -735,8 +764,12 @@ __device__ __forceinline__ int compress_c4a_seq(const LayerParams& P, const Weig
       if (KVF == CKV_E4M3 && tid == 0) *(float*)(dst + dn + 2 * P.n_rot) = sc;
     }
     if (roleA || roleI) {   // this token's projections -> state slot p % 8
-      skv[cur * width + col] = ka;
-      ssc[cur * width + col] = sa;
+      skv[cur * sw + col] = ka;
+      ssc[cur * sw + col] = sa;
+      if constexpr (NL == 2) {
+        skv[cur * sw + width + col] = kb2;
+        ssc[cur * sw + width + col] = sb2;
+      }
     }
     if (pool) {   // RMSNorm, tail RoPE at 4 i, row i of the attention or indexer cache
       const float inv = roleA ? norm_inv(P, sA, d) : norm_inv(P, sI, DI);

@@ -29,16 +29,16 @@ __global__ __launch_bounds__(256 * TPC) void k_compress_decode(LayerParams P, We
 }
 
 // c4a: the role-split body, one block of d + D_I threads (rounded up
-// to whole waves) per sequence; up to 4 projection slices.
-template <int KVF, int IDXF, int ACTF>
+// to whole waves) per sequence; up to 4 projection slices; NL compressor lanes.
+template <int KVF, int IDXF, int ACTF, int NL = 1>
 __global__ __launch_bounds__(1024) void k_compress_c4a(LayerParams P, Weights w, Cache cc, const void* __restrict__ u,
                                                        const int32_t* __restrict__ pos,
                                                        const float* __restrict__ proj, int splits, int B) {
   __shared__ __attribute__((aligned(16))) float red[64];
   __shared__ float rtab[192];
   __shared__ __attribute__((aligned(16))) float idx_lds[IDXF == CKV_FP4 ? kMaxDI : 1];   // fp4 row staging
-  const int st = compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, splits, B, blockIdx.x, red, rtab,
-                                                   IDXF == CKV_FP4 ? idx_lds : nullptr, [] {});
+  const int st = compress_c4a_seq<KVF, IDXF, ACTF, NL>(P, w, cc, u, pos, proj, splits, B, blockIdx.x, red, rtab,
+                                                       IDXF == CKV_FP4 ? idx_lds : nullptr, [] {});
   advance_tokens(cc, blockIdx.x, pos[blockIdx.x], st);
 }
 
@@ -266,27 +266,31 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
   __shared__ __attribute__((aligned(16))) float zi[kMaxDI];
   __shared__ float red[16];
   const int i = i_first + blockIdx.x;
-  const int d = P.d, r = P.ratio, W = P.W, DI = P.DI, nc = P.ncol;
+  const int d = P.d, r = P.ratio, W = P.W, DI = P.DI, nc = P.ncol, NL = P.lanes;
   if (cc.n_tokens && cc.n_tokens[seq] != pos0) return;   // out of sequence: the cache stays as it is
   const int t0 = i * r - (W - r);
-  const float* skv = cc.st_kv + (size_t)seq * W * d;
-  const float* ssc = cc.st_sc + (size_t)seq * W * d;
+  // two lanes (ratio 4): window positions 0-3 take lane A (offset 0) of
+  // their token's projections / ring slot / APE row j, positions 4-7 lane B
+  // (offset w) of APE row j - 4; one lane: APE row j
+  const float* skv = cc.st_kv + (size_t)seq * W * NL * d;
+  const float* ssc = cc.st_sc + (size_t)seq * W * NL * d;
   if (lanes & 1) {
     for (int c = threadIdx.x; c < d; c += blockDim.x) {
       PoolAcc pa;
       for (int j = 0; j < W; ++j) {
         const int t = t0 + j;
         if (t < 0) continue;
+        const int lo = NL == 2 && j >= 4 ? d : 0;   // lane offset
         float kv, sc;
         if (t >= pos0) {
           const float* pr = part + (size_t)(t - pos0) * nc;
-          kv = pr[c];
-          sc = pr[d + c];
+          kv = pr[lo + c];
+          sc = pr[NL * d + lo + c];
         } else {
-          kv = skv[(t % W) * d + c];
-          sc = ssc[(t % W) * d + c];
+          kv = skv[(t % W) * NL * d + lo + c];
+          sc = ssc[(t % W) * NL * d + lo + c];
         }
-        pa.add(sc + w.ape[j * d + c], kv);
+        pa.add(sc + w.ape[(NL == 2 ? (j & 3) * 2 * d : j * d) + lo + c], kv);
       }
       zs[c] = pa.value();
     }
@@ -298,23 +302,24 @@ __global__ __launch_bounds__(256) void k_pool_prefill(LayerParams P, Weights w, 
     if (slot >= 0) store_row<KVF>(cc.comp + slot * P.row_bytes, zs, d, P.n_rot, red);
   }
   if (r != 4 || !(lanes & 2)) return;
-  const float* ikv = cc.ist_kv + (size_t)seq * 8 * DI;
-  const float* isc = cc.ist_sc + (size_t)seq * 8 * DI;
+  const float* ikv = cc.ist_kv + (size_t)seq * 8 * NL * DI;
+  const float* isc = cc.ist_sc + (size_t)seq * 8 * NL * DI;
   for (int c = threadIdx.x; c < DI; c += blockDim.x) {
     PoolAcc pa;
     for (int j = 0; j < 8; ++j) {
       const int t = t0 + j;
       if (t < 0) continue;
+      const int lo = NL == 2 && j >= 4 ? DI : 0;
       float kv, sc;
       if (t >= pos0) {
-        const float* pr = part + (size_t)(t - pos0) * nc;
-        kv = pr[2 * d + c];
-        sc = pr[2 * d + DI + c];
+        const float* pr = part + (size_t)(t - pos0) * nc + 2 * NL * d;
+        kv = pr[lo + c];
+        sc = pr[NL * DI + lo + c];
       } else {
-        kv = ikv[(t % 8) * DI + c];
-        sc = isc[(t % 8) * DI + c];
+        kv = ikv[(t % 8) * NL * DI + lo + c];
+        sc = isc[(t % 8) * NL * DI + lo + c];
       }
-      pa.add(sc + w.idx_ape[j * DI + c], kv);
+      pa.add(sc + w.idx_ape[(NL == 2 ? (j & 3) * 2 * DI : j * DI) + lo + c], kv);
     }
     zi[c] = pa.value();
   }
@@ -353,16 +358,17 @@ __global__ __launch_bounds__(256) void k_state_prefill(LayerParams P, Cache cc,
   const int t = end - W + j;
   if (t < pos0) return;
   const float* pr = part + (size_t)(t - pos0) * nc;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    const size_t o = ((size_t)seq * W + t % W) * d + c;
+  const int wa = P.lanes * d, wi = P.lanes * DI;   // a ring slot holds every lane of its token
+  for (int c = threadIdx.x; c < wa; c += blockDim.x) {
+    const size_t o = ((size_t)seq * W + t % W) * wa + c;
     cc.st_kv[o] = pr[c];
-    cc.st_sc[o] = pr[d + c];
+    cc.st_sc[o] = pr[wa + c];
   }
   if (P.ratio == 4) {
-    for (int c = threadIdx.x; c < DI; c += blockDim.x) {
-      const size_t o = ((size_t)seq * 8 + t % 8) * DI + c;
-      cc.ist_kv[o] = pr[2 * d + c];
-      cc.ist_sc[o] = pr[2 * d + DI + c];
+    for (int c = threadIdx.x; c < wi; c += blockDim.x) {
+      const size_t o = ((size_t)seq * 8 + t % 8) * wi + c;
+      cc.ist_kv[o] = pr[2 * wa + c];
+      cc.ist_sc[o] = pr[2 * wa + wi + c];
     }
   }
 }
@@ -384,6 +390,9 @@ static void go_decode(const LayerParams& P, const Weights& w, const Cache& c, co
     hipLaunchKernelGGL((k_c128a_slices<KVF, ACTF>), dim3(B, P.d / 64), dim3(256), 0, st, P, w, c, u, pos, part,
                        splits, B, pool_ws);
     hipLaunchKernelGGL((k_c128a_finish<KVF>), dim3(B), dim3(256), 0, st, P, w, c, pos, pool_ws, B);
+  } else if (P.ratio == 4 && P.lanes == 2) {   // (decode projections have at most 4 slices)
+    hipLaunchKernelGGL((k_compress_c4a<KVF, IDXF, ACTF, 2>), dim3(B), dim3((P.d + P.DI + 63) / 64 * 64), 0, st, P,
+                       w, c, u, pos, part, splits, B);
   } else if (P.ratio == 4 && (splits <= 4 || IDXF == CKV_FP4))   // (fp4: splits is at most 4)
     hipLaunchKernelGGL((k_compress_c4a<KVF, IDXF, ACTF>), dim3(B), dim3((P.d + P.DI + 63) / 64 * 64), 0, st, P, w,
                        c, u, pos, part, splits, B);

@@ -1790,7 +1790,8 @@ int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const f
 }
 
 bool step_fusable(const LayerParams& P, int B) {
-  return P.ratio == 4 && (P.idx_fmt == CKV_BF16 || P.idx_fmt == CKV_FP4) && P.DI == 128 && P.HI <= 64 &&
+  return P.ratio == 4 && P.lanes == 1 && (P.idx_fmt == CKV_BF16 || P.idx_fmt == CKV_FP4) && P.DI == 128 &&
+         P.HI <= 64 &&
          P.cap <= 32768 &&
          P.idx_rot == P.n_rot && P.n_rot == 64 &&
          P.act_fmt == CKV_BF16 && P.w_fmt == CKV_BF16 && B <= 64 && P.d <= 512;

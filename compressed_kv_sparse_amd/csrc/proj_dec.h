@@ -29,10 +29,11 @@ inline WCat make_wcat(const LayerParams& P, const Weights& w) {
   wc.p[1] = w.wgate;
   wc.p[2] = w.idx_wkv;
   wc.p[3] = w.idx_wgate;
+  // (two-lane c4a: each matrix has both lanes' rows, lane A first)
   wc.start[0] = 0;
-  wc.start[1] = P.d;
-  wc.start[2] = P.ratio == 4 ? 2 * P.d : 1 << 30;
-  wc.start[3] = P.ratio == 4 ? 2 * P.d + P.DI : 1 << 30;
+  wc.start[1] = P.lanes * P.d;
+  wc.start[2] = P.ratio == 4 ? 2 * P.lanes * P.d : 1 << 30;
+  wc.start[3] = P.ratio == 4 ? P.lanes * (2 * P.d + P.DI) : 1 << 30;
   wc.start[4] = P.ncol;
   return wc;
 }

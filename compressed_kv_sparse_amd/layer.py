@@ -74,10 +74,12 @@ class DeviceLayer:
             else:
                 idt = torch.float32 if idx_fmt == "f32" else torch.int16
                 self.idx = torch.zeros((batch, comp_cap, idx_dim), dtype=idt, device=dev) if ratio == 4 else None
-        self.st_kv = zf(batch, W, head_dim) if ratio else None
-        self.st_sc = zf(batch, W, head_dim) if ratio else None
-        self.ist_kv = zf(batch, 8, idx_dim) if ratio == 4 else None
-        self.ist_sc = zf(batch, 8, idx_dim) if ratio == 4 else None
+        # a ring slot holds every compressor lane of its token (two on two-lane c4a layers)
+        self.lanes = 2 if ratio == 4 and flags & L.CKV_FLAG_TWO_LANE else 1
+        self.st_kv = zf(batch, W, self.lanes * head_dim) if ratio else None
+        self.st_sc = zf(batch, W, self.lanes * head_dim) if ratio else None
+        self.ist_kv = zf(batch, 8, self.lanes * idx_dim) if ratio == 4 else None
+        self.ist_sc = zf(batch, 8, self.lanes * idx_dim) if ratio == 4 else None
         self.max_chunk = max_chunk
         self.stage = z8(max_chunk + swa - 1, self.rb) if max_chunk else None
         self.status = torch.zeros(batch, dtype=torch.int32, device=dev)

@@ -136,6 +136,19 @@ extern "C" {
  * is never stored.  Any layer shape; affects sparse_swa_attn (and the decode
  * step's attention) only, not the indexer query. */
 #define CKV_FLAG_Q_NORM 64u
+/* Two-lane c4a compressors [P1 s5: a ratio-4 compressor's state is twice as
+ * wide as its rows, a first and a second half]: ratio-4 layers only (else
+ * CKV_E_UNSUPPORTED).  Every token projects to two lanes of width w (w = d for
+ * the attention compressor, D_I for the indexer's): wkv, wgate [2d, hidden]
+ * and idx_wkv, idx_wgate [2 D_I, hidden], lane A the first w rows.  Row i
+ * pools lane A of tokens 4i-4 .. 4i-1 (window slots 0-3) and lane B of tokens
+ * 4i .. 4i+3 (slots 4-7); ape [4, 2d] (idx_ape [4, 2 D_I]) holds lane A's
+ * bias of slot s in row s, columns 0..w-1, and lane B's (slot 4 + s) in
+ * columns w..2w-1.  The state rings keep both lanes of each token: st_kv,
+ * st_sc [batch, 8, 2d], ist_kv, ist_sc [batch, 8, 2 D_I].  The page names the
+ * two lanes, not what each holds: this is the library's reading (without the
+ * flag one lane serves both windows). */
+#define CKV_FLAG_TWO_LANE 128u
 
 /* ---- modes for ckv_workspace_bytes ---------------------------------------- */
 #define CKV_MODE_DECODE 0
@@ -198,6 +211,8 @@ typedef struct ckv_layer_desc {
 
 /* Compressor weights (device pointers, read only).
  *   wkv, wgate          [head_dim, hidden] row-major, w_fmt   [P1 s4 steps 1-2]
+ *                       (CKV_FLAG_TWO_LANE: [2 head_dim, hidden]; the indexer's
+ *                       and both APEs change alike, see there)
  *   ape                 [W, head_dim] float32, W = 8 (r=4) / 128 (r=128): the
  *                       learned position bias added to the score of window slot j
  *   gamma               [head_dim] float32 RMSNorm weight
@@ -224,7 +239,9 @@ typedef struct ckv_layer_weights {
  *                                           block_table)
  *   st_kv, st_sc   [batch, W, head_dim] float32: compressor window state,
  *                  token t's (kappa, sigma) in slot t % W          [P1 s5; P4]
+ *                  (CKV_FLAG_TWO_LANE: [batch, 8, 2 head_dim], lane A then B)
  *   ist_kv, ist_sc [batch, 8, idx_dim] float32: indexer compressor state
+ *                  (CKV_FLAG_TWO_LANE: [batch, 8, 2 idx_dim])
  *   raw_stage  [stage_rows, row_bytes]: prefill staging of the raw rows of
  *              positions pos0-swa+1 .. pos0+T-1 (stage_rows >= T + swa - 1)
  *   status     [batch] uint32 sticky device error bits, or NULL

@@ -52,7 +52,7 @@ def test_validate_accepts_the_workload_shapes():
     (dict(top_k=0), L.CKV_E_UNSUPPORTED), (dict(kv_fmt=7), L.CKV_E_UNSUPPORTED),
     (dict(act_fmt=L.CKV_E4M3), L.CKV_E_UNSUPPORTED), (dict(comp_cap=0), L.CKV_E_INVAL),
     (dict(batch=0), L.CKV_E_INVAL), (dict(rope_base=0.0), L.CKV_E_INVAL),
-    (dict(flags=0x80), L.CKV_E_UNSUPPORTED), (dict(flags=0x100), L.CKV_E_UNSUPPORTED), (dict(hidden=100), L.CKV_E_UNSUPPORTED),
+    (dict(flags=0x200), L.CKV_E_UNSUPPORTED), (dict(flags=0x100), L.CKV_E_UNSUPPORTED), (dict(hidden=100), L.CKV_E_UNSUPPORTED),
     (dict(top_k=2049), L.CKV_E_UNSUPPORTED), (dict(rope_base_comp=-1.0), L.CKV_E_INVAL),
 ])
 def test_validate_rejects(kw, code):
@@ -71,7 +71,7 @@ def test_debug_stage_flags():
     assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, **f32)) == 0
     assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, **dict(f32, idx_fmt=L.CKV_BF16))) == L.CKV_E_UNSUPPORTED
     assert L.validate(desc(flags=L.CKV_FLAG_KEEP_F32, ratio=0, comp_cap=0, **dict(f32, idx_fmt=L.CKV_BF16))) == 0
-    assert L.validate(desc(flags=128)) == L.CKV_E_UNSUPPORTED
+    assert L.validate(desc(flags=256)) == L.CKV_E_UNSUPPORTED
 
 
 def test_validate_bounds_match_the_header():
@@ -311,3 +311,17 @@ def test_q_norm_flag():
                dict(head_dim=256), dict(n_heads=32), dict(ratio=0, comp_cap=0)):
         assert L.validate(desc(flags=f, **kw)) == 0, kw
     assert L.validate(desc(flags=f | L.CKV_FLAG_OUT_FP8 | L.CKV_FLAG_NO_INV_ROPE)) == 0
+
+
+def test_two_lane_flag():
+    """CKV_FLAG_TWO_LANE: ratio-4 layers only; the projection doubles (the
+    prefill workspace's projection region grows with it)."""
+    f = L.CKV_FLAG_TWO_LANE
+    assert f == 128
+    assert L.validate(desc(flags=f)) == 0
+    assert L.validate(desc(flags=f, idx_fmt=L.CKV_FP4)) == 0
+    assert L.validate(desc(flags=f, ratio=128, comp_cap=8192)) == L.CKV_E_UNSUPPORTED
+    assert L.validate(desc(flags=f, ratio=0, comp_cap=0)) == L.CKV_E_UNSUPPORTED
+    one, two = desc(), desc(flags=f)
+    grow = L.workspace_bytes(two, L.CKV_MODE_PREFILL, 4096) - L.workspace_bytes(one, L.CKV_MODE_PREFILL, 4096)
+    assert grow >= 4096 * (2 * 512 + 2 * 128) * 4 - 256

@@ -16,6 +16,7 @@ from harness import (BF16_TOL, FP8_TOL, assert_close, compare_fp4_rows, compare_
                      tie_free_queries, topk_margin)
 from workloads import get_config, make_decode_inputs, make_layer_weights, make_prefill_inputs
 from workloads import gen as G
+from workloads.configs import TWO_LANE_FLAG
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -192,6 +193,25 @@ def test_c5_c4a_fp8_decode_full_size():
     run_decode_stage_checks(cfg, make_decode_inputs(cfg), make_layer_weights(cfg), FP8_TOL)
 
 
+@pytest.mark.parametrize("name", ["c2_small", "c5_two_lane"])
+def test_two_lane_decode(name):
+    """Two-lane compressors (CKV_FLAG_TWO_LANE): the separate calls' stages
+    against the oracle, then the single-call step (which runs the separate
+    calls on such layers)."""
+    if name == "c2_small":
+        cfg = get_config("c2").with_(batch=3, comp_cap=1024, top_k=128, seed=87, flags=TWO_LANE_FLAG,
+                                     name="two_lane_c2_small")
+        inp = make_decode_inputs(cfg, n_ctx=np.array([4000, 2501, 130], np.int64))
+    else:
+        cfg = get_config(name)
+        inp = make_decode_inputs(cfg)
+    wts = make_layer_weights(cfg)
+    assert cfg.two_lane and wts.wkv.shape[0] == 2 * cfg.head_dim and wts.ape.shape == (4, 2 * cfg.head_dim)
+    tol = FP8_TOL if cfg.kv_fmt == "e4m3" else BF16_TOL
+    run_decode_stage_checks(cfg, inp, wts, tol)
+    run_decode_step_checks(cfg, inp, wts, tol)
+
+
 def test_c3_c128a_decode_full_size():
     cfg = get_config("c3")
     # force a few sequences onto a c128a boundary so the step emits a row
@@ -274,10 +294,12 @@ def test_bad_position_sets_status_and_spares_others():
     assert not np.array_equal(raw_after[0], raw_before[0])
 
 
-def test_c1_full_history_decode_chain():
+@pytest.mark.parametrize("flags", [0, TWO_LANE_FLAG])
+def test_c1_full_history_decode_chain(flags):
     """C1 from token 0: 1024 compress_append steps, then index + attend at 1023;
-    every stored row and the output compared with the oracle's history run."""
-    cfg = get_config("c1")
+    every stored row and the output compared with the oracle's history run
+    (one-lane and two-lane compressors)."""
+    cfg = get_config("c1").with_(flags=flags)
     wts = make_layer_weights(cfg)
     T = cfg.n_ctx
     x, u, q, qI, w = G.make_token_stream(cfg, T)
@@ -309,11 +331,12 @@ def test_c1_full_history_decode_chain():
     assert_close(cpu(out)[0], ref["out_f64"], BF16_TOL, "c1 output")
 
 
-@pytest.mark.parametrize("chunks", [(1024,), (37, 1, 500, 486)])
-def test_c1_prefill_chunks_equal_sequential_decode(chunks):
+@pytest.mark.parametrize("chunks,flags", [((1024,), 0), ((37, 1, 500, 486), 0), ((37, 1, 500, 486), TWO_LANE_FLAG)])
+def test_c1_prefill_chunks_equal_sequential_decode(chunks, flags):
     """Chunked prefill from token 0 in chunks of varying size: stored rows and
-    every query's output against the oracle (prefill = sequential decode)."""
-    cfg = get_config("c1")
+    every query's output against the oracle (prefill = sequential decode);
+    one-lane and two-lane compressors."""
+    cfg = get_config("c1").with_(flags=flags)
     wts = make_layer_weights(cfg)
     T = sum(chunks)
     x, u, q, qI, w = G.make_token_stream(cfg, T)
@@ -353,7 +376,7 @@ def test_c1_prefill_chunks_equal_sequential_decode(chunks):
         assert_close(outs[p], ref["out_f64"], BF16_TOL, f"output of query {p}")
 
 
-@pytest.mark.parametrize("name", ["c4", "c4_fp4idx"])
+@pytest.mark.parametrize("name", ["c4", "c4_fp4idx", "c4_two_lane"])
 def test_c4_prefill_chunk_sampled(name):
     """4096-token chunk at 61440 (compressor windows straddle the chunk edge):
     every emitted row, and sampled queries' top-k and outputs."""

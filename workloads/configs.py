@@ -40,6 +40,10 @@ def window_of(ratio: int) -> int:
     return {4: 8, 128: 128}.get(ratio, 0)
 
 
+# ckv_layer_desc.flags bit of the two-lane c4a compressors
+TWO_LANE_FLAG = 128
+
+
 @dataclass(frozen=True)
 class LayerShape:
     name: str
@@ -77,11 +81,15 @@ class LayerShape:
     layer: int = 0
     flags: int = 0                    # ckv_layer_desc.flags (e.g. 32: attention output as fp8 records)
     paged: bool = False               # compressed rows in scattered 256-position pages (block table)
-    two_lane: bool = False            # ratio 4: two-lane compressors (projections 2 d / 2 D_I, APE [4, 2 w])
+
+    @property
+    def two_lane(self) -> bool:
+        """Ratio 4 with two-lane compressors (projections 2 d / 2 D_I, APE [4, 2 w])."""
+        return bool(self.flags & TWO_LANE_FLAG) and self.ratio == 4
 
     @property
     def lanes(self) -> int:
-        return 2 if self.two_lane and self.ratio == 4 else 1
+        return 2 if self.two_lane else 1
 
     @property
     def window(self) -> int:
@@ -161,6 +169,10 @@ CONFIGS[_c.name] = _c
 # ... and with each head's query RMS-normalised inside the attention
 _c = _c5(4, 2).with_(name="c5_c4a_decode_b16_ctx131072_fp8_qnorm", flags=64)
 CONFIGS[_c.name] = _c
+# the C5 c4a decode and the C4 chunk with two-lane compressors
+for _c in (_c5(4, 2).with_(name="c5_c4a_decode_b16_ctx131072_fp8_two_lane", flags=TWO_LANE_FLAG),
+           _c4().with_(name="c4_c4a_prefill_T4096_at61440_bf16_two_lane", flags=TWO_LANE_FLAG)):
+    CONFIGS[_c.name] = _c
 # ... and with the compressed and indexer rows in scattered pages of a pool
 _c = _c5(4, 2).with_(name="c5_c4a_decode_b16_ctx131072_fp8_paged", paged=True)
 CONFIGS[_c.name] = _c
@@ -179,6 +191,8 @@ ALIASES = {
     "c5_out8": "c5_c4a_decode_b16_ctx131072_fp8_out8",
     "c5_qnorm": "c5_c4a_decode_b16_ctx131072_fp8_qnorm",
     "c5_paged": "c5_c4a_decode_b16_ctx131072_fp8_paged",
+    "c5_two_lane": "c5_c4a_decode_b16_ctx131072_fp8_two_lane",
+    "c4_two_lane": "c4_c4a_prefill_T4096_at61440_bf16_two_lane",
 }
 
 
