@@ -81,7 +81,9 @@ WsLayout ws_layout(const LayerParams& P, int mode, int n) {
   const int rows = attn_max_rows(P);
   int rps;
   if (attn_uses_tiles(P)) {
-    if (prefill) {
+    if (prefill || P.ratio == 0) {
+      // (a window-only layer's 128 rows: one split per query -- four tiles in
+      // one block, then the output, instead of two blocks and the merge launch)
       rps = rows;
     } else {
       // about 192 blocks over the batch, each split 2 to 10 tiles of 32 rows
