@@ -775,7 +775,10 @@ __global__ __launch_bounds__(512) void k_attn_tile(LayerParams P, Cache cc, cons
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
       int ex = 0;
-      if (amax >= 16384.f) (void)frexpf(amax, &ex);
+      if (amax >= 16384.f) {   // amax = m 2^f, m in [0.5, 1): scaled to m 2^14
+        (void)frexpf(amax, &ex);
+        ex -= 14;
+      }
       const float down = ldexpf(1.f, -ex);
       const size_t pb = ((size_t)qn * nsplit + split) * H + hd;
       const size_t lo_half = (size_t)gridDim.x * H * D;   // fp16 entries of the high halves
