@@ -227,6 +227,63 @@ def test_c5_c128a_and_swa_layers_decode():
         run_decode_stage_checks(cfg, make_decode_inputs(cfg), make_layer_weights(cfg), FP8_TOL)
 
 
+def test_c5_decode_step_oracle_own_rows():
+    """The C5 c4a step at full size with the oracle on its own rows: it runs
+    this step's compressor itself from the drawn state (raw row, compressed
+    row, indexer row) and scores, selects and attends over its own bytes; no
+    GPU byte enters its scores or outputs.
+
+    * top-k: the GPU's set must contain every row whose oracle score is above
+      the oracle's k-th by more than 2 delta and only rows within 2 delta
+      below it, delta being the largest score change the GPU's stored rows
+      make (plus fp32 key rounding); where no score lies within that band of
+      the k-th the set is unique and must be equal;
+    * outputs: the oracle's attention with its own rows over the GPU's list,
+      within the fp8 tolerance widened, element by element, by the change the
+      GPU's stored rows make to that attention (the rows this step computes
+      may differ by one E4M3 code: up to 1/8 of an element)."""
+    cfg = get_config("c5")
+    inp = make_decode_inputs(cfg)
+    wts = make_layer_weights(cfg)
+    L = oracle_layer(cfg, wts)
+    B, k = cfg.batch, cfg.top_k
+    own = []
+    for b in range(B):
+        sq = oracle_seq_from_init(L, inp.cache, b)
+        sq.feed(int(inp.pos[b]), inp.x[b][None], inp.u[b][None])
+        own.append(sq)
+    dl = device_layer(cfg, wts, inp.cache)
+    out, topk = dl.decode_step(dev(inp.x), dev(inp.u), dev(inp.q), dev(inp.qI), dev(inp.w), dev(inp.pos))
+    torch.cuda.synchronize()
+    assert int(dl.status.abs().sum()) == 0
+    raw_g, comp_g, idx_g = cpu(dl.raw), cpu(dl.comp), cpu(dl.idx)
+    tkg, og = cpu(topk), out_values(out, cfg.act_fmt)
+    unique = equal = 0
+    for b in range(B):
+        p = int(inp.pos[b])
+        s_own = own[b].index_scores(p, inp.qI[b], inp.w[b])
+        on_gpu_rows = oracle_seq_from_bytes(L, raw_g[b], comp_g[b], idx_g[b], p + 1)
+        s_gpu = on_gpu_rows.index_scores(p, inp.qI[b], inp.w[b])
+        smax = float(np.max(np.abs(s_own)))
+        delta = float(np.max(np.abs(s_own - s_gpu))) + 1e-5 * smax
+        kth = np.sort(s_own)[::-1][k - 1]
+        g = tkg[b][tkg[b] >= 0]
+        assert len(g) == k and len(set(g.tolist())) == k, f"sequence {b}: not {k} distinct rows"
+        assert np.all(np.isin(np.nonzero(s_own > kth + 2 * delta)[0], g)), f"sequence {b}: a clear top-k row missing"
+        assert np.all(s_own[g] >= kth - 2 * delta), f"sequence {b}: a row clearly outside the top-k selected"
+        ref_set = O.topk_select(s_own, k)
+        equal += int(np.array_equal(np.sort(g), ref_set))
+        if int(np.sum(np.abs(s_own - kth) <= 2 * delta)) == 1:
+            unique += 1
+            assert np.array_equal(np.sort(g), ref_set), f"sequence {b}: unique top-k set differs"
+        ref = own[b].attend(p, inp.q[b], tkg[b])
+        row_change = np.abs(on_gpu_rows.attend(p, inp.q[b], tkg[b]) - ref)
+        bad = np.abs(og[b] - ref) > FP8_TOL[1] + FP8_TOL[0] * np.abs(ref) + row_change
+        assert not bad.any(), (f"c5 own-rows output b={b}: {int(bad.sum())} outside the band; "
+                               f"first {np.argwhere(bad)[:3].tolist()}")
+    log(f"[c5 own rows] sets equal to the oracle's in {equal}/{B} sequences ({unique} unique by the band rule)")
+
+
 @pytest.mark.parametrize("name", ["c2", "c5", "c3", "c5_swa", "c5_fp4idx"])
 def test_decode_step_full_size(name):
     """The single-call decode step at full size: fused on the c4a layers,
