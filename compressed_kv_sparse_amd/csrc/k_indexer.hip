@@ -1617,7 +1617,7 @@ __global__ __launch_bounds__(1024) void k_topk_decode(LayerParams P, const uint3
 // columns x 16 rows each, 4 waves over one of kProjSlices K slices); the
 // others score the query's cache rows except the row its own token closes,
 // building the key histogram.
-template <int MT, int QF, int IDXF, bool PAGED = false>
+template <int MT, int QF, int IDXF, bool PAGED = false, int NG = kStepGroups>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_step_scan(
     LayerParams P, const void* idx, const void* __restrict__ qI, const float* __restrict__ wt,
     const int32_t* __restrict__ pos, uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
@@ -1635,11 +1635,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const int i = kStepProjLast ? bid : bid - nproj;
   if constexpr (IDXF == CKV_FP4)
-    idx_score_block_fp4<MT, true, kFp4StepGroups, PAGED>(P, (const uint8_t*)idx, qI, wt, pos, 0, 0, keys, hist,
-                                                         i % nrb, i / nrb, true, qf4);
+    idx_score_block_fp4<MT, true, NG, PAGED>(P, (const uint8_t*)idx, qI, wt, pos, 0, 0, keys, hist, i % nrb,
+                                             i / nrb, true, qf4);
   else
-    idx_score_block<MT, 4, QF, true, kStepGroups, PAGED>(P, (const uint16_t*)idx, qI, wt, pos, 0, 0, keys, hist,
-                                                         i % nrb, i / nrb, true);
+    idx_score_block<MT, 4, QF, true, NG, PAGED>(P, (const uint16_t*)idx, qI, wt, pos, 0, 0, keys, hist, i % nrb,
+                                                i / nrb, true);
 }
 
 // k_step_select: one block of 1024 threads per sequence.  The indexer query
@@ -1652,7 +1652,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // With fp4 indexer rows the scan has already rotated and transformed the
 // query (Hadamard, MXFP4) and left it in S.qf4: the block reads those codes
 // instead of the bf16 query, so both kernels score with the same fp4 query.
-template <int KVF, int IDXF, int ACTF>
+template <int KVF, int IDXF, int ACTF, int NL = 1>
 __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, Cache cc, const void* __restrict__ u,
                                                       const int32_t* __restrict__ pos, const float* __restrict__ proj,
                                                       int B, const void* __restrict__ qI,
@@ -1693,7 +1693,7 @@ __global__ __launch_bounds__(1024) void k_step_select(LayerParams P, Weights w, 
   // (the query and the histogram, the first loads issued, are parked in LDS
   // once the keys are on their way: registers are short while the compressor
   // holds its window)
-  const int st = compress_c4a_seq<KVF, IDXF, ACTF>(P, w, cc, u, pos, proj, kProjSlices, B, qn, red, rtab, idx_row, [&] {
+  const int st = compress_c4a_seq<KVF, IDXF, ACTF, NL>(P, w, cc, u, pos, proj, kProjSlices, B, qn, red, rtab, idx_row, [&] {
     sel_load_keys(keys + (size_t)qn * P.cap, P.cap, tid, kr);
     *(u32x4*)(h_lds + 4 * tid) = h4;
     *(u32x4*)(q_lds + 4 * tid) = q4;
@@ -1790,7 +1790,8 @@ int launch_indexer(const LayerParams& P, const Cache& c, const void* qI, const f
 }
 
 bool step_fusable(const LayerParams& P, int B) {
-  return P.ratio == 4 && P.lanes == 1 && (P.idx_fmt == CKV_BF16 || P.idx_fmt == CKV_FP4) && P.DI == 128 &&
+  return P.ratio == 4 && (P.lanes == 1 || P.lanes == 2) && (P.idx_fmt == CKV_BF16 || P.idx_fmt == CKV_FP4) &&
+         P.DI == 128 &&
          P.HI <= 64 &&
          P.cap <= 32768 &&
          P.idx_rot == P.n_rot && P.n_rot == 64 &&
@@ -1803,18 +1804,26 @@ int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache&
   hipStream_t st = (hipStream_t)stream;
   const WCat wc = make_wcat(P, w);
   const int nproj = (P.ncol / 16) * ((B + 15) / 16) * kProjSlices;
-  const int RB = 256 * (P.idx_fmt == CKV_FP4 ? kFp4StepGroups : kStepGroups);
+  // two-lane layers have twice the projection blocks: their scan blocks take
+  // one row group more, so that every block is resident from the start
+  constexpr int kTwoLaneGroups = kStepGroups + 1;
+  static_assert(kFp4StepGroups == kStepGroups, "one group count for both indexer formats");
+  const bool wide = P.lanes == 2;
+  const int RB = 256 * (wide ? kTwoLaneGroups : kStepGroups);
   const int nrb = (P.cap + RB - 1) / RB;
   const int MT = (P.HI + 15) / 16;
   dim3 grid(nproj + nrb * B);
   const bool fp4 = P.idx_fmt == CKV_FP4;
-#define CKV_SS(MTV, IF)                                                                                          \
+#define CKV_SS_NG(MTV, IF, NGV)                                                                                  \
   if (P.blocks)                                                                                                   \
-    launch_score((k_step_scan<MTV, CKV_BF16, IF, true>), grid, dim3(256), st, P, (const void*)c.idx, qI, wt, pos, \
-                 keys, sel.hist, (const uint16_t*)x, B, wc, proj, nproj, nrb, sel.qf4);                           \
+    launch_score((k_step_scan<MTV, CKV_BF16, IF, true, NGV>), grid, dim3(256), st, P, (const void*)c.idx, qI, wt, \
+                 pos, keys, sel.hist, (const uint16_t*)x, B, wc, proj, nproj, nrb, sel.qf4);                      \
   else                                                                                                            \
-    launch_score((k_step_scan<MTV, CKV_BF16, IF>), grid, dim3(256), st, P, (const void*)c.idx, qI, wt, pos, keys, \
-                 sel.hist, (const uint16_t*)x, B, wc, proj, nproj, nrb, sel.qf4)
+    launch_score((k_step_scan<MTV, CKV_BF16, IF, false, NGV>), grid, dim3(256), st, P, (const void*)c.idx, qI,    \
+                 wt, pos, keys, sel.hist, (const uint16_t*)x, B, wc, proj, nproj, nrb, sel.qf4)
+#define CKV_SS(MTV, IF)                        \
+  if (wide) CKV_SS_NG(MTV, IF, kTwoLaneGroups); \
+  else CKV_SS_NG(MTV, IF, kStepGroups)
 #define CKV_SS_MT(IF)      \
   if (MT == 1) CKV_SS(1, IF); \
   else if (MT == 2) CKV_SS(2, IF); \
@@ -1824,9 +1833,14 @@ int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache&
   else CKV_SS_MT(CKV_BF16);
 #undef CKV_SS_MT
 #undef CKV_SS
-#define CKV_SEL(KF, IF)                                                                                        \
-  hipLaunchKernelGGL((k_step_select<KF, IF, CKV_BF16>), dim3(B), dim3(1024), 0, st, P, w, c, u, pos, proj, B, qI, \
-                     wt, keys, sel, topk)
+#undef CKV_SS_NG
+#define CKV_SEL(KF, IF)                                                                                         \
+  if (P.lanes == 2)                                                                                              \
+    hipLaunchKernelGGL((k_step_select<KF, IF, CKV_BF16, 2>), dim3(B), dim3(1024), 0, st, P, w, c, u, pos, proj, B, \
+                       qI, wt, keys, sel, topk);                                                                 \
+  else                                                                                                           \
+    hipLaunchKernelGGL((k_step_select<KF, IF, CKV_BF16>), dim3(B), dim3(1024), 0, st, P, w, c, u, pos, proj, B, qI, \
+                       wt, keys, sel, topk)
   if (P.kv_fmt == CKV_E4M3) {
     if (fp4) CKV_SEL(CKV_E4M3, CKV_FP4);
     else CKV_SEL(CKV_E4M3, CKV_BF16);

@@ -432,8 +432,9 @@ int ckv_sparse_swa_attn_prefill(const ckv_layer_desc* desc, const ckv_layer_cach
  * arguments: x, u as for compress_append; q, out as for sparse_swa_attn;
  * qI, iw (the indexer head weights) and topk as for indexer_topk (ratio 4;
  * ignored and may be NULL otherwise).  topk receives the selection on ratio 4.
- * On ratio-4 layers with bf16 activations, weights and indexer rows, D_I = 128,
- * at most 64 indexer heads, comp_cap <= 32768 and B <= 64, the step runs as
+ * On ratio-4 layers with bf16 activations and weights, bf16 or fp4 indexer
+ * rows, one or two compressor lanes, D_I = 128, at most 64 indexer heads,
+ * comp_cap <= 32768 and B <= 64, the step runs as
  * three launches: the compressor projection shares a launch with the scoring
  * of the rows that precede this token's own row; one block per sequence then
  * runs the compressor, scores the row this token closed (if any) and selects;

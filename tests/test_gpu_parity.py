@@ -196,8 +196,9 @@ def test_c5_c4a_fp8_decode_full_size():
 @pytest.mark.parametrize("name", ["c2_small", "c5_two_lane"])
 def test_two_lane_decode(name):
     """Two-lane compressors (CKV_FLAG_TWO_LANE): the separate calls' stages
-    against the oracle, then the single-call step (which runs the separate
-    calls on such layers)."""
+    against the oracle, then the single-call step (fused: both lanes'
+    projection columns in the scan launch, the two-lane compressor in the
+    selection block), whose top-k list must equal the separate calls'."""
     if name == "c2_small":
         cfg = get_config("c2").with_(batch=3, comp_cap=1024, top_k=128, seed=87, flags=TWO_LANE_FLAG,
                                      name="two_lane_c2_small")
