@@ -1807,13 +1807,12 @@ int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache&
   // two-lane layers have twice the projection blocks: their scan blocks take
   // one row group more, so that every block is resident from the start
   constexpr int kTwoLaneGroups = kStepGroups + 1;
-  static_assert(kFp4StepGroups == kStepGroups, "one group count for both indexer formats");
   const bool wide = P.lanes == 2;
-  const int RB = 256 * (wide ? kTwoLaneGroups : kStepGroups);
+  const bool fp4 = P.idx_fmt == CKV_FP4;
+  const int RB = 256 * (wide ? kTwoLaneGroups : fp4 ? kFp4StepGroups : kStepGroups);
   const int nrb = (P.cap + RB - 1) / RB;
   const int MT = (P.HI + 15) / 16;
   dim3 grid(nproj + nrb * B);
-  const bool fp4 = P.idx_fmt == CKV_FP4;
 #define CKV_SS_NG(MTV, IF, NGV)                                                                                  \
   if (P.blocks)                                                                                                   \
     launch_score((k_step_scan<MTV, CKV_BF16, IF, true, NGV>), grid, dim3(256), st, P, (const void*)c.idx, qI, wt, \
@@ -1821,9 +1820,9 @@ int launch_step_scan_select(const LayerParams& P, const Weights& w, const Cache&
   else                                                                                                            \
     launch_score((k_step_scan<MTV, CKV_BF16, IF, false, NGV>), grid, dim3(256), st, P, (const void*)c.idx, qI,    \
                  wt, pos, keys, sel.hist, (const uint16_t*)x, B, wc, proj, nproj, nrb, sel.qf4)
-#define CKV_SS(MTV, IF)                        \
-  if (wide) CKV_SS_NG(MTV, IF, kTwoLaneGroups); \
-  else CKV_SS_NG(MTV, IF, kStepGroups)
+#define CKV_SS(MTV, IF)                                              \
+  if (wide) CKV_SS_NG(MTV, IF, kTwoLaneGroups);                       \
+  else CKV_SS_NG(MTV, IF, (IF == CKV_FP4 ? kFp4StepGroups : kStepGroups))
 #define CKV_SS_MT(IF)      \
   if (MT == 1) CKV_SS(1, IF); \
   else if (MT == 2) CKV_SS(2, IF); \
