@@ -27,10 +27,11 @@ def _bytes(t):
     return t.numpy().copy()
 
 
-@pytest.mark.parametrize("name", ["c5", "c5_c128a"])
+@pytest.mark.parametrize("name", ["c5", "c5_c128a", "c5_two_lane"])
 def test_static_workspace_step_equals_workspace_step(name):
     from compressed_kv_sparse_amd import _lib as L
-    cfg = get_config(name).with_(batch=8, comp_cap=8192 if name == "c5" else 512, seed=101, name=f"static_{name}")
+    cfg = get_config(name).with_(batch=8, comp_cap=512 if name == "c5_c128a" else 8192, seed=101,
+                                 name=f"static_{name}")
     r = cfg.ratio
     n = np.array([32768, 20001, 4100, 131, 9, 30000, 12345, 65536][:cfg.batch], np.int64)
     n = np.minimum(n, cfg.comp_cap * r)
